@@ -1,0 +1,199 @@
+#!/usr/bin/env python3
+"""Benchmark: batched speculative-sampling verification on one MI355X.
+
+A step is one call of the whole verification (row statistics of every draft
+row i < gamma and target row i <= gamma, the accept tests, the first
+rejection, the residual / Saguaro / bonus draw, the outputs) over one batch of
+synthetic logits already resident in HBM.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--mode residual]
+
+Prints one JSON line.  value = verified draft positions per second,
+B * gamma / (seconds per call).  The roofline block prices the whole call
+(its algorithmic bytes over its event-timed duration) against the MI355X HBM
+peak of 8 TB/s; cpu_baseline times the fp64 oracle on a bounded sample of
+the same workload on this host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+DEFAULT_WORKLOAD = "B256_g8_V152064_bf16"
+METRIC = "verified draft positions/sec and achieved HBM GB/s (% of peak) at B,gamma,V"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--mode", choices=("residual", "saguaro"), default="residual")
+    ap.add_argument("--eps", type=float, default=0.0)
+    ap.add_argument("--sets", type=int, default=0,
+                    help="input sets to rotate through (0: enough for > 1 GB)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="wall-clock budget of the CPU oracle sample")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only run a plain device copy of this many bytes (counter calibration)")
+    return ap.parse_args()
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "rejection_sampling_verify_12_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_record(workload: str, mode: str):
+    """HBM bytes per call from committed rocprofv3 counter runs, if they were
+    taken on the current kernel sources; None otherwise."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}_{mode}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_digest") != source_digest():
+        return None
+    return rec.get("bytes_per_call")
+
+
+def cpu_baseline(batch, mode: str, eps: float, budget_s: float) -> dict:
+    """The fp64 oracle on the first sequences of the same workload, one thread."""
+    import oracle as O
+    import workloads as W
+    t0 = time.perf_counter()
+    n = 0
+    while n < batch.B:
+        O.verify_one(W.decode_f64(batch.draft[n], batch.dtype), W.decode_f64(batch.target[n], batch.dtype),
+                     batch.draft_tokens[n], batch.u_accept[n], batch.u_sample[n], batch.T, mode, eps)
+        n += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": n * batch.gamma / dt, "unit": "positions/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {n} of {batch.B} sequences of {batch.name}, fp64 numpy, one thread, "
+                      f"{dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU: --gpus {args.gpus} is not supported (sequences are "
+              "independent; a multi-GPU run would shard B with no communication).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import rejection_sampling_verify_12_amd as R
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    if args.copy_bytes:
+        src = torch.empty(args.copy_bytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": args.copy_bytes, "launches": args.steps}))
+        return
+
+    t0 = time.perf_counter()
+    batch = W.make_workload(args.workload, workers=min(16, os.cpu_count() or 1))
+    print(f"[bench] generated {args.workload} in {time.perf_counter() - t0:.1f} s", file=sys.stderr,
+          flush=True)
+    B, g, V = batch.B, batch.gamma, batch.V
+    dt_code = R.SPEC_BF16 if batch.dtype == "bf16" else R.SPEC_F32
+    bytes_alg = R.bytes_algorithmic(B, g, V, dt_code)
+    nsets = args.sets or max(1, -(-(1 << 30) // max(bytes_alg, 1)) + (1 if bytes_alg < (1 << 30) else 0))
+
+    def dev_logits(a):
+        if batch.dtype == "bf16":
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    base_d, base_t = dev_logits(batch.draft), dev_logits(batch.target)
+    sets = [(base_d, base_t)]
+    for s in range(1, nsets):   # extra copies so that successive calls miss the 256 MB cache
+        sets.append((base_d.clone(), base_t.clone()))
+    tok = torch.from_numpy(batch.draft_tokens).to(dev)
+    ua = torch.from_numpy(batch.u_accept).to(dev)
+    us = torch.from_numpy(batch.u_sample).to(dev)
+    out = R.alloc_outputs(B, g, dev)
+    ws = R.new_workspace(R.spec_workspace_bytes(B, g, V, dt_code), dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def call(i):
+        d, t = sets[i % nsets]
+        if args.mode == "residual":
+            R.spec_verify(d, t, tok, ua, us, batch.T, out=out, workspace=ws, stream=stream)
+        else:
+            R.spec_verify_saguaro(d, t, tok, ua, us, batch.T, out=out, workspace=ws, stream=stream,
+                                  eps=args.eps)
+
+    for i in range(args.warmup):
+        call(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        call(args.warmup + i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    per_call_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    ms_step = wall * 1e3 / args.steps
+    ev_ms = float(per_call_ms.mean())
+    acc = out.accepted.cpu().numpy()
+
+    achieved = bytes_alg / (ev_ms * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": B * g / (ms_step * 1e-3),
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "B": B, "gamma": g, "V": V, "T": batch.T,
+                   "logits": batch.dtype, "mode": args.mode, "eps": args.eps,
+                   "input_sets": nsets, "alpha_target": [float(batch.alpha_target.min()),
+                                                         float(batch.alpha_target.max())],
+                   "mean_accepted": float(acc.mean())},
+        "event_ms": {"mean": ev_ms, "p10": float(np.percentile(per_call_ms, 10)),
+                     "p50": float(np.percentile(per_call_ms, 50)),
+                     "p90": float(np.percentile(per_call_ms, 90))},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic_record(args.workload, args.mode),
+                     "kernel": "spec_verify call (all kernels)", "bytes_alg": bytes_alg},
+        "source_digest": source_digest(),
+    }
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(batch, args.mode, args.eps, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,168 @@
+/*
+ * spec_verify.h - batched speculative-sampling verification on MI355X (gfx950).
+ *
+ * What is computed.  For each of B sequences the caller supplies draft logits
+ * and target logits at gamma+1 positions over a V-token vocabulary, the gamma
+ * draft tokens x_0..x_{gamma-1}, a temperature T and uniforms.  With
+ * p_i = softmax(draft_i / T) and q_i = softmax(target_i / T):
+ *
+ *   - position i is accepted iff u_accept[b][i] < min(1, q_i(x_i) / p_i(x_i))
+ *     ("Speculative Decoding: small model guesses, large model verifies",
+ *      section 3: the acceptance rule; section 5.4: same T on both sides);
+ *   - k = the first rejected position, or gamma if none (section 3: stop at
+ *     the first rejection; section 2: 1..gamma+1 tokens per round);
+ *   - if k < gamma a token y is drawn from the residual (q_k - p_k)+ / sum(q_k - p_k)+
+ *     (section 3), or with spec_verify_saguaro from
+ *     sqrt(p_k * max(r, eps)) / sum, r = the normalised residual
+ *     ("Speculative Speculative Decoding (Saguaro)", section 3.2);
+ *   - if k == gamma the bonus token y is drawn from q_gamma (section 2: the
+ *     target scores gamma+1 positions);
+ *   - every draw takes the first token id j whose running probability sum in
+ *     token-id order exceeds u_sample[b][k] (section 3, the choice helper);
+ *   - the committed length is in_len + k + 1 (SSD summary, AMD MI300X part:
+ *     on rejection only the valid-length pointer of the KV cache moves).
+ *
+ * Conventions for every entry point.
+ *   - All array pointers are DEVICE pointers; `stream` is a hipStream_t passed
+ *     as void* (NULL = the default stream).  Calls only enqueue work on that
+ *     stream and return; nothing is synchronised.
+ *   - The caller owns every buffer.  The library never allocates or frees
+ *     device memory and keeps no global state; concurrent calls need distinct
+ *     workspaces.
+ *   - Logits are row-major [B][gamma+1][V], contiguous, float32 (SPEC_F32) or
+ *     bfloat16 (SPEC_BF16).  Row i of sequence b starts at element
+ *     (b*(gamma+1)+i)*V.  The verification reads draft rows 0..gamma-1 and
+ *     target rows 0..gamma; draft row gamma is read only by outcome prediction.
+ *   - Host-checkable errors return a negative status before anything is
+ *     enqueued: B < 0, gamma outside [1, 63], V < 1, T not finite or <= 0,
+ *     eps not finite or < 0, a NULL required pointer, an unknown dtype, a
+ *     workspace smaller than spec_workspace_bytes().  B == 0 is a no-op.
+ *   - Data errors found on the device mark only their sequence: a draft token
+ *     outside [0, V), or a row read by the rule that holds a NaN or +inf
+ *     logit (or only -inf logits).  Such a sequence gets accepted = -1, every
+ *     token -1, first_reject = -1, mask = 0, out_len = in_len.
+ *   - A launch failure returns SPEC_ELAUNCH.  No exception crosses the ABI.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum spec_status {
+  SPEC_OK = 0,
+  SPEC_EINVAL = -1,     /* bad size, temperature, eps or NULL pointer */
+  SPEC_EDTYPE = -2,     /* dtype is neither SPEC_F32 nor SPEC_BF16 */
+  SPEC_EWORKSPACE = -3, /* workspace NULL or smaller than required */
+  SPEC_ELAUNCH = -4     /* a kernel launch failed */
+};
+
+enum spec_dtype { SPEC_F32 = 0, SPEC_BF16 = 1 };
+
+/*
+ * Optional diagnostics (pass NULL in production).  Each field is an optional
+ * device pointer; NULL fields are skipped.  Values are those the device used.
+ *   row_max, row_logZ: [B][2*gamma+1], draft rows 0..gamma-1 then target rows
+ *     0..gamma: max_j l_j / T and log sum_j exp(l_j / T).
+ *   px, qx: [B][gamma] p_i(x_i), q_i(x_i).
+ *   resid_mass: [B] sum_j (q_k - p_k)+ (0 when k == gamma).
+ *   token_prob: [B] probability of y under the distribution it was drawn from.
+ *   cdf_lo, cdf_hi: [B] the running sums C_{y-1} and C_y of that distribution.
+ * Invalid sequences leave their entries unwritten.
+ */
+typedef struct spec_diag {
+  double* row_max;
+  double* row_logZ;
+  double* px;
+  double* qx;
+  double* resid_mass;
+  double* token_prob;
+  double* cdf_lo;
+  double* cdf_hi;
+} spec_diag;
+
+/*
+ * Bytes of device workspace spec_verify / spec_verify_saguaro need for these
+ * sizes (0 when B == 0).  Returns 0 for arguments spec_verify would reject.
+ * The workspace must be zero-filled before its first use; each call that
+ * completes leaves it ready for the next one, so a workspace is allocated and
+ * cleared once and then reused by calls on one stream.
+ */
+size_t spec_workspace_bytes(int B, int gamma, int V, int dtype);
+
+/*
+ * Verification with residual resampling.
+ *   draft_logits, target_logits: [B][gamma+1][V] of `dtype`.
+ *   draft_tokens: [B][gamma] int32.
+ *   u_accept: [B][gamma] float, u_sample: [B][gamma+1] float, values in [0, 1).
+ *   temperature: T > 0, applied to both models.
+ *   in_len: [B] int32 committed lengths before the round; NULL = zeros.
+ * Outputs ([B] unless stated):
+ *   out_tokens: [B][gamma+1] int32: x_0..x_{k-1}, y, then -1.
+ *   out_accepted: k (number of accepted draft tokens).
+ *   out_first_reject: k if k < gamma else -1 (nullable).
+ *   out_accept_mask: bit i = decision at position i for all i < gamma (nullable).
+ *   out_len: in_len + k + 1 (nullable).
+ *   diag: NULL or a host pointer to a spec_diag of optional device pointers.
+ */
+int spec_verify(const void* draft_logits, const void* target_logits, int dtype,
+                const int32_t* draft_tokens, const float* u_accept, const float* u_sample,
+                int B, int gamma, int V, float temperature, const int32_t* in_len,
+                int32_t* out_tokens, int32_t* out_accepted, int32_t* out_first_reject,
+                uint64_t* out_accept_mask, int32_t* out_len, const spec_diag* diag,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * As spec_verify, but a rejection at k draws from the Saguaro distribution
+ * proportional to sqrt(p_k(j) * max(r_j, eps)), r = (q_k - p_k)+ / sum(q_k - p_k)+
+ * ("Speculative Speculative Decoding (Saguaro)", section 3.2).  eps = 0 is the
+ * section's formula; eps = 1e-8 reproduces the clamp in its code.  The bonus
+ * draw (k == gamma) is unchanged.
+ */
+int spec_verify_saguaro(const void* draft_logits, const void* target_logits, int dtype,
+                        const int32_t* draft_tokens, const float* u_accept,
+                        const float* u_sample, int B, int gamma, int V, float temperature,
+                        const int32_t* in_len, int32_t* out_tokens, int32_t* out_accepted,
+                        int32_t* out_first_reject, uint64_t* out_accept_mask, int32_t* out_len,
+                        const spec_diag* diag, void* workspace, size_t workspace_bytes,
+                        void* stream, float eps);
+
+/*
+ * Bytes of device workspace spec_predict_outcomes needs (same zero-on-entry
+ * rule as spec_workspace_bytes).
+ */
+size_t spec_predict_workspace_bytes(int B, int gamma, int V, int dtype);
+
+/*
+ * Outcome prediction for speculative speculative decoding
+ * ("Speculative Speculative Decoding (Saguaro)", section 3.1: an outcome is
+ * (k accepted, bonus token); the bonus is predicted from the draft logits'
+ * top-3).  For every sequence b and every k in 0..gamma, cand[b][k][0..2]
+ * are the token ids of the three largest draft logits at position k,
+ * descending, equal logits ordered by lower id (+0.0 and -0.0 are equal); a
+ * row holding a NaN gives -1 candidates.  3*(gamma+1) candidates per sequence.
+ *   draft_logits: [B][gamma+1][V] of dtype (all gamma+1 rows are read).
+ *   accepted, out_tokens: a verification's out_accepted [B] and out_tokens
+ *     [B][gamma+1], or both NULL to compute candidates only.
+ *   cand: [B][gamma+1][3] int32.
+ *   hit: [B] int32 (nullable): 1 iff out_tokens[b][k] is one of cand[b][k],
+ *     k = accepted[b]; 0 for an invalid sequence (accepted < 0).
+ *   cand_idx: [B] int32 (nullable): 3k + rank of the matching candidate, or -1.
+ */
+int spec_predict_outcomes(const void* draft_logits, int dtype, int B, int gamma, int V,
+                          const int32_t* accepted, const int32_t* out_tokens, int32_t* cand,
+                          int32_t* hit, int32_t* cand_idx, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* A static, human-readable description of a status code. */
+const char* spec_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

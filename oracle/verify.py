@@ -38,7 +38,8 @@ notes with its justification):
   running sum never exceeds u (rounding only).
 * Saguaro: pi proportional to sqrt(p_k * max(w / S, eps)), w = (q_k - p_k)+,
   S = sum w; eps = 0 is the formula, eps = 1e-8 the page's code.  Used only on
-  a rejection; the bonus stays q_gamma.
+  a rejection; the bonus stays q_gamma.  A zero normaliser (residual only
+  where p_k = 0) falls back to the residual.
 * A sequence whose rows read by the rule hold a NaN or +inf logit, or are all
   -inf, or whose draft token lies outside [0, V), is invalid: accepted = -1,
   tokens -1, mask 0, first_reject -1, out_len = in_len.
@@ -110,10 +111,15 @@ def residual_weights(p_k: np.ndarray, q_k: np.ndarray) -> np.ndarray:
 
 
 def saguaro_distribution(p_k: np.ndarray, w: np.ndarray, eps: float) -> np.ndarray:
-    """pi proportional to sqrt(p_D * max(w / sum w, eps)) ([SSD] section 3.2)."""
+    """pi proportional to sqrt(p_D * max(w / sum w, eps)) ([SSD] section 3.2).
+
+    If every product is zero (the residual lives only where p_D = 0 and
+    eps = 0) the formula is 0/0; the normalised residual is returned instead.
+    """
     r = w / w.sum()
     s = np.sqrt(p_k * np.maximum(r, eps))
-    return s / s.sum()
+    tot = s.sum()
+    return s / tot if tot > 0 else r
 
 
 # ---------------------------------------------------------------------------

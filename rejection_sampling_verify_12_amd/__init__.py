@@ -1,0 +1,217 @@
+"""Python binding of libspecverify (batched speculative-sampling verification, gfx950).
+
+Argument marshalling only: every step of the verification runs in the HIP
+kernels of ``libspecverify.so``; torch provides device memory and streams.
+The names follow the C ABI in include/spec_verify.h.  Importing works
+without a GPU; calling a compute entry point needs the built library and a
+device, and fails loudly otherwise (there is no CPU fallback).
+"""
+from __future__ import annotations
+
+import collections
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libspecverify.so")
+
+SPEC_OK, SPEC_EINVAL, SPEC_EDTYPE, SPEC_EWORKSPACE, SPEC_ELAUNCH = 0, -1, -2, -3, -4
+SPEC_F32, SPEC_BF16 = 0, 1
+
+EXPORTED = ("spec_workspace_bytes", "spec_verify", "spec_verify_saguaro",
+            "spec_predict_workspace_bytes", "spec_predict_outcomes", "spec_status_str")
+
+
+class SpecDiag(ctypes.Structure):
+    """struct spec_diag: optional device pointers (0 = not requested)."""
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("row_max", "row_logZ", "px", "qx", "resid_mass", "token_prob", "cdf_lo", "cdf_hi")]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libspecverify.so and declare its signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m rejection_sampling_verify_12_amd.build` (no CPU fallback)")
+    lib = ctypes.CDLL(path)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    verify_args = [vp, vp, i32, vp, vp, vp, i32, i32, i32, f32, vp, vp, vp, vp, vp, vp,
+                   ctypes.POINTER(SpecDiag), vp, sz, vp]
+    lib.spec_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.spec_workspace_bytes.restype = sz
+    lib.spec_verify.argtypes = verify_args
+    lib.spec_verify.restype = i32
+    lib.spec_verify_saguaro.argtypes = verify_args + [f32]
+    lib.spec_verify_saguaro.restype = i32
+    lib.spec_predict_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.spec_predict_workspace_bytes.restype = sz
+    lib.spec_predict_outcomes.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.spec_predict_outcomes.restype = i32
+    lib.spec_status_str.argtypes = [i32]
+    lib.spec_status_str.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+class SpecError(RuntimeError):
+    def __init__(self, status: int):
+        super().__init__(f"spec status {status}: {spec_status_str(status)}")
+        self.status = status
+
+
+def spec_status_str(status: int) -> str:
+    return load_library().spec_status_str(int(status)).decode()
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return SPEC_BF16
+    if t.dtype == torch.float32:
+        return SPEC_F32
+    raise TypeError(f"logits must be float32 or bfloat16, got {t.dtype}")
+
+
+def spec_workspace_bytes(B: int, gamma: int, V: int, dtype: int) -> int:
+    return int(load_library().spec_workspace_bytes(B, gamma, V, dtype))
+
+
+def spec_predict_workspace_bytes(B: int, gamma: int, V: int, dtype: int) -> int:
+    return int(load_library().spec_predict_workspace_bytes(B, gamma, V, dtype))
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream_handle(stream, device):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream
+
+
+def _check_dev(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("every tensor must be a contiguous device tensor")
+
+
+def new_workspace(nbytes: int, device):
+    """A zero-filled workspace (the library leaves it zeroed after each call)."""
+    import torch
+    return torch.zeros(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+VerifyOut = collections.namedtuple(
+    "VerifyOut", "tokens accepted first_reject accept_mask out_len diag")
+
+DIAG_FIELDS = ("row_max", "row_logZ", "px", "qx", "resid_mass", "token_prob", "cdf_lo", "cdf_hi")
+
+
+def alloc_outputs(B: int, gamma: int, device, diag: bool = False) -> VerifyOut:
+    import torch
+    i32 = dict(dtype=torch.int32, device=device)
+    d = None
+    if diag:
+        R = 2 * gamma + 1
+        shapes = dict(row_max=(B, R), row_logZ=(B, R), px=(B, gamma), qx=(B, gamma),
+                      resid_mass=(B,), token_prob=(B,), cdf_lo=(B,), cdf_hi=(B,))
+        d = {k: torch.full(shapes[k], float("nan"), dtype=torch.float64, device=device)
+             for k in DIAG_FIELDS}
+    return VerifyOut(torch.empty((B, gamma + 1), **i32), torch.empty((B,), **i32),
+                     torch.empty((B,), **i32), torch.empty((B,), dtype=torch.int64, device=device),
+                     torch.empty((B,), **i32), d)
+
+
+def _verify_call(saguaro: bool, draft_logits, target_logits, draft_tokens, u_accept, u_sample,
+                 temperature: float, in_len=None, out: VerifyOut | None = None, diag: bool = False,
+                 workspace=None, stream=None, eps: float = 0.0) -> VerifyOut:
+    lib = load_library()
+    B, G1, V = draft_logits.shape
+    gamma = G1 - 1
+    if target_logits.shape != draft_logits.shape or target_logits.dtype != draft_logits.dtype:
+        raise ValueError("draft and target logits must share shape and dtype")
+    _check_dev(draft_logits, target_logits, draft_tokens, u_accept, u_sample, in_len)
+    dt = _dtype_code(draft_logits)
+    dev = draft_logits.device
+    if out is None:
+        out = alloc_outputs(B, gamma, dev, diag)
+    need = spec_workspace_bytes(B, gamma, V, dt)
+    if workspace is None:
+        workspace = new_workspace(need, dev)
+    dg = None
+    if out.diag is not None:
+        dg = SpecDiag(*[out.diag[k].data_ptr() for k in DIAG_FIELDS])
+    args = [draft_logits.data_ptr(), target_logits.data_ptr(), dt, draft_tokens.data_ptr(),
+            u_accept.data_ptr(), u_sample.data_ptr(), B, gamma, V, float(temperature),
+            _ptr(in_len), out.tokens.data_ptr(), out.accepted.data_ptr(),
+            out.first_reject.data_ptr(), out.accept_mask.data_ptr(), out.out_len.data_ptr(),
+            ctypes.byref(dg) if dg is not None else None, workspace.data_ptr(),
+            workspace.numel(), _stream_handle(stream, dev)]
+    if saguaro:
+        st = lib.spec_verify_saguaro(*args, float(eps))
+    else:
+        st = lib.spec_verify(*args)
+    if st != SPEC_OK:
+        raise SpecError(st)
+    return out
+
+
+def spec_verify(draft_logits, target_logits, draft_tokens, u_accept, u_sample, temperature,
+                in_len=None, out=None, diag=False, workspace=None, stream=None) -> VerifyOut:
+    """Residual-mode verification of a [B, gamma+1, V] batch (see spec_verify.h)."""
+    return _verify_call(False, draft_logits, target_logits, draft_tokens, u_accept, u_sample,
+                        temperature, in_len, out, diag, workspace, stream)
+
+
+def spec_verify_saguaro(draft_logits, target_logits, draft_tokens, u_accept, u_sample,
+                        temperature, in_len=None, out=None, diag=False, workspace=None,
+                        stream=None, eps: float = 0.0) -> VerifyOut:
+    """Saguaro-mode verification (see spec_verify.h)."""
+    return _verify_call(True, draft_logits, target_logits, draft_tokens, u_accept, u_sample,
+                        temperature, in_len, out, diag, workspace, stream, eps)
+
+
+PredictOut = collections.namedtuple("PredictOut", "cand hit cand_idx")
+
+
+def spec_predict_outcomes(draft_logits, accepted=None, out_tokens=None, out=None,
+                          workspace=None, stream=None) -> PredictOut:
+    """Top-3 outcome candidates per position and, given a verification's
+    outputs, the hit flag and candidate index (see spec_verify.h)."""
+    import torch
+    lib = load_library()
+    B, G1, V = draft_logits.shape
+    gamma = G1 - 1
+    _check_dev(draft_logits, accepted, out_tokens)
+    dt = _dtype_code(draft_logits)
+    dev = draft_logits.device
+    if out is None:
+        i32 = dict(dtype=torch.int32, device=dev)
+        out = PredictOut(torch.empty((B, G1, 3), **i32), torch.empty((B,), **i32),
+                         torch.empty((B,), **i32))
+    need = spec_predict_workspace_bytes(B, gamma, V, dt)
+    if workspace is None:
+        workspace = new_workspace(need, dev)
+    st = lib.spec_predict_outcomes(draft_logits.data_ptr(), dt, B, gamma, V, _ptr(accepted),
+                                   _ptr(out_tokens), out.cand.data_ptr(), _ptr(out.hit),
+                                   _ptr(out.cand_idx), workspace.data_ptr(), workspace.numel(),
+                                   _stream_handle(stream, dev))
+    if st != SPEC_OK:
+        raise SpecError(st)
+    return out
+
+
+def bytes_algorithmic(B: int, gamma: int, V: int, dtype: int) -> int:
+    """Bytes the method must move once per call: draft rows i < gamma and target
+    rows i <= gamma, draft tokens, uniforms, lengths, and the outputs."""
+    es = 2 if dtype == SPEC_BF16 else 4
+    return ((B * gamma + B * (gamma + 1)) * V * es + B * gamma * 4 + B * gamma * 4
+            + B * (gamma + 1) * 4 + B * 4 + B * (gamma + 1) * 4 + B * (4 + 4 + 8 + 4))

@@ -1,0 +1,201 @@
+// Device helpers shared by the verification and outcome-prediction kernels.
+// gfx950 (CDNA4): 64-lane wavefronts, 256-thread work-groups (4 waves).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sv {
+
+constexpr int kThreads = 256;               // every kernel runs 256-thread work-groups
+constexpr int kWaves = kThreads / 64;
+constexpr int kUnit = 8;                    // logits per thread per load unit (16 B of bf16)
+constexpr int kTile = kThreads * kUnit;     // 2048 logits: granularity of the sampling scan
+constexpr int kChunk = 16384;               // logits of one row per statistics work-group
+constexpr float kNegSentinel = -1.0e30f;    // "no finite logit seen yet"
+
+enum : int { kF32 = 0, kBF16 = 1 };
+
+// ---------------------------------------------------------------------------
+// Logit loads.  A row is `const void*`; element j is float32 or bfloat16.
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+template <int DT>
+__device__ __forceinline__ float load_one(const void* row, int64_t j) {
+  if constexpr (DT == kBF16) {
+    return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(row)[j]) << 16);
+  } else {
+    return static_cast<const float*>(row)[j];
+  }
+}
+
+// Eight consecutive logits starting at j0.  VEC: j0 + 8 <= n and 16-byte
+// aligned rows (one or two 16-byte loads).  Otherwise per-element loads with
+// positions >= n read as -inf.
+template <int DT, bool VEC>
+__device__ __forceinline__ void load8(const void* row, int64_t j0, int64_t n, float (&v)[8]) {
+  if constexpr (VEC) {
+    if constexpr (DT == kBF16) {
+      const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(row) + j0);
+      v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x);
+      v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
+      v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z);
+      v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
+    } else {
+      const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(row) + j0);
+      const float4 a = p[0], b = p[1];
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+      v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (j0 + e < n) ? load_one<DT>(row, j0 + e) : -INFINITY;
+  }
+}
+
+// Hardware base-2 exponential (v_exp_f32).
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------------------
+// Cross-work-group hand-off without cache-wide maintenance.  A producer
+// writes its payload with device-coherent (agent-scope) stores, waits until
+// they have completed, then bumps an arrival counter with a relaxed atomic;
+// the consumer reads payloads with device-coherent loads.  (An agent-scope
+// fence would write back and invalidate the whole L2 of the XCD instead.)
+
+__device__ __forceinline__ void st_dev(double* p, double v) {
+  __hip_atomic_store(reinterpret_cast<unsigned long long*>(p),
+                     (unsigned long long)__double_as_longlong(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ double ld_dev(const double* p) {
+  return __longlong_as_double((long long)__hip_atomic_load(
+      reinterpret_cast<const unsigned long long*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ __forceinline__ void st_dev_u64(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(reinterpret_cast<unsigned long long*>(p), (unsigned long long)v,
+                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_dev_u64(const uint64_t* p) {
+  return (uint64_t)__hip_atomic_load(reinterpret_cast<const unsigned long long*>(p),
+                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait for every outstanding memory operation of this wave (s_waitcnt 0).
+__device__ __forceinline__ void wait_mem() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// ---------------------------------------------------------------------------
+// Work-group reductions and scans (256 threads, 4 waves).  `lds` must hold
+// kWaves entries of the reduced type; each call ends with a barrier so the
+// scratch can be reused.
+
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ int wave_min_int(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ double block_sum(double v, double* lds) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  __syncthreads();
+  if (l == 0) lds[w] = v;
+  __syncthreads();
+  double t = 0.0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) t += lds[i];
+  __syncthreads();
+  return t;
+}
+
+// N sums at once (one barrier pair); lds holds kWaves * N doubles.
+template <int N>
+__device__ __forceinline__ void block_sum_n(double (&v)[N], double* lds) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = wave_sum(v[i]);
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  __syncthreads();
+  if (l == 0) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) lds[w * N + i] = v[i];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    double t = 0.0;
+#pragma unroll
+    for (int j = 0; j < kWaves; ++j) t += lds[j * N + i];
+    v[i] = t;
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ float block_max(float v, float* lds) {
+  v = wave_max(v);
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  __syncthreads();
+  if (l == 0) lds[w] = v;
+  __syncthreads();
+  float t = lds[0];
+#pragma unroll
+  for (int i = 1; i < kWaves; ++i) t = fmaxf(t, lds[i]);
+  __syncthreads();
+  return t;
+}
+
+__device__ __forceinline__ int block_min_int(int v, int* lds) {
+  v = wave_min_int(v);
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  __syncthreads();
+  if (l == 0) lds[w] = v;
+  __syncthreads();
+  int t = lds[0];
+#pragma unroll
+  for (int i = 1; i < kWaves; ++i) t = min(t, lds[i]);
+  __syncthreads();
+  return t;
+}
+
+// Exclusive prefix sum over the work-group in thread order; returns this
+// thread's offset and writes the total.
+__device__ __forceinline__ double block_exclusive_scan(double v, double* lds, double& total) {
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  double incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const double t = __shfl_up(incl, o, 64);
+    if (l >= o) incl += t;
+  }
+  __syncthreads();
+  if (l == 63) lds[w] = incl;
+  __syncthreads();
+  double before = 0.0, all = 0.0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) {
+    if (i < w) before += lds[i];
+    all += lds[i];
+  }
+  __syncthreads();
+  total = all;
+  const double excl = __shfl_up(incl, 1, 64);
+  return before + (l == 0 ? 0.0 : excl);
+}
+
+}  // namespace sv

@@ -1,0 +1,122 @@
+"""Host-side checks of the C ABI (no GPU): the library loads, exports every
+function include/spec_verify.h declares, sizes its workspace, and rejects bad
+arguments with the documented status before anything is enqueued."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import rejection_sampling_verify_12_amd as R
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "spec_verify.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(spec_\w+)\s*\(", src, re.M)))
+
+
+def test_header_declares_the_abi():
+    names = declared_functions()
+    assert names == sorted(R.EXPORTED), names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = R.load_library()
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for st in (R.SPEC_OK, R.SPEC_EINVAL, R.SPEC_EDTYPE, R.SPEC_EWORKSPACE, R.SPEC_ELAUNCH):
+        assert R.spec_status_str(st) and R.spec_status_str(st) != "unknown status"
+    assert R.spec_status_str(123) == "unknown status"
+
+
+def test_workspace_bytes():
+    assert R.spec_workspace_bytes(0, 4, 1000, R.SPEC_BF16) == 0
+    assert R.spec_workspace_bytes(-1, 4, 1000, R.SPEC_BF16) == 0
+    assert R.spec_workspace_bytes(2, 0, 1000, R.SPEC_BF16) == 0
+    assert R.spec_workspace_bytes(2, 64, 1000, R.SPEC_BF16) == 0
+    assert R.spec_workspace_bytes(2, 4, 0, R.SPEC_BF16) == 0
+    assert R.spec_workspace_bytes(2, 4, 1000, 7) == 0
+    a = R.spec_workspace_bytes(256, 8, 152064, R.SPEC_BF16)
+    b = R.spec_workspace_bytes(512, 8, 152064, R.SPEC_BF16)
+    assert 0 < a < b and a % 256 == 0
+    # modest: far below the logits it verifies
+    assert a < 0.01 * 256 * 17 * 152064 * 2
+    assert R.spec_predict_workspace_bytes(128, 4, 128256, R.SPEC_BF16) > 0
+    assert R.spec_predict_workspace_bytes(0, 4, 128256, R.SPEC_BF16) == 0
+
+
+FAKE = 4096   # never dereferenced: every call below fails validation first
+
+
+def _verify(saguaro=False, eps=0.0, **kw):
+    lib = R.load_library()
+    a = dict(draft=FAKE, target=FAKE, dtype=R.SPEC_BF16, tokens=FAKE, ua=FAKE, us=FAKE, B=4,
+             gamma=3, V=1000, T=1.0, in_len=None, out_tokens=FAKE, out_acc=FAKE, out_fr=None,
+             out_mask=None, out_len=None, diag=None, ws=FAKE, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    args = list(a.values())
+    return lib.spec_verify_saguaro(*args, eps) if saguaro else lib.spec_verify(*args)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=-1), R.SPEC_EINVAL),
+    (dict(gamma=0), R.SPEC_EINVAL),
+    (dict(gamma=64), R.SPEC_EINVAL),
+    (dict(V=0), R.SPEC_EINVAL),
+    (dict(T=0.0), R.SPEC_EINVAL),
+    (dict(T=-1.0), R.SPEC_EINVAL),
+    (dict(T=math.nan), R.SPEC_EINVAL),
+    (dict(T=math.inf), R.SPEC_EINVAL),
+    (dict(dtype=2), R.SPEC_EDTYPE),
+    (dict(draft=None), R.SPEC_EINVAL),
+    (dict(target=None), R.SPEC_EINVAL),
+    (dict(tokens=None), R.SPEC_EINVAL),
+    (dict(ua=None), R.SPEC_EINVAL),
+    (dict(us=None), R.SPEC_EINVAL),
+    (dict(out_tokens=None), R.SPEC_EINVAL),
+    (dict(out_acc=None), R.SPEC_EINVAL),
+    (dict(ws=None), R.SPEC_EWORKSPACE),
+    (dict(ws_bytes=16), R.SPEC_EWORKSPACE),
+    (dict(B=0, draft=None, ws=None), R.SPEC_OK),
+])
+def test_verify_rejects_bad_arguments(kw, status):
+    assert _verify(**kw) == status
+    assert _verify(saguaro=True, **kw) == status
+
+
+@pytest.mark.parametrize("eps", [-1e-8, math.nan, math.inf])
+def test_saguaro_rejects_bad_eps(eps):
+    assert _verify(saguaro=True, eps=eps) == R.SPEC_EINVAL
+
+
+def test_predict_rejects_bad_arguments():
+    lib = R.load_library()
+
+    def call(**kw):
+        a = dict(draft=FAKE, dtype=R.SPEC_BF16, B=4, gamma=3, V=1000, acc=None, tok=None,
+                 cand=FAKE, hit=None, idx=None, ws=FAKE, ws_bytes=1 << 30, stream=None)
+        a.update(kw)
+        return lib.spec_predict_outcomes(*a.values())
+
+    assert call(B=-1) == R.SPEC_EINVAL
+    assert call(gamma=64) == R.SPEC_EINVAL
+    assert call(dtype=9) == R.SPEC_EDTYPE
+    assert call(draft=None) == R.SPEC_EINVAL
+    assert call(cand=None) == R.SPEC_EINVAL
+    assert call(acc=FAKE) == R.SPEC_EINVAL          # accepted without out_tokens
+    assert call(ws_bytes=8) == R.SPEC_EWORKSPACE
+    assert call(B=0, draft=None) == R.SPEC_OK
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    monkeypatch.setattr(R, "_lib", None)
+    with pytest.raises(RuntimeError, match="no CPU fallback"):
+        R.load_library(str(tmp_path / "absent.so"))

@@ -1,0 +1,246 @@
+"""GPU parity: the HIP library (through its C ABI) against the fp64 oracle.
+
+Every case prints its name, shapes and seed before touching the GPU.
+"""
+import functools
+
+import numpy as np
+import pytest
+import scipy.stats
+
+import oracle as O
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+H = pytest.importorskip("gpu_harness")
+
+
+@functools.lru_cache(maxsize=None)
+def workload(name):
+    H.say(f"[gen] {name}")
+    return W.make_workload(name)
+
+
+def random_batch(B, gamma, V, dtype, T, seed, scale=3.0, sigma=0.7):
+    """Gaussian logits (draft) and a noisy copy (target); tokens ~ p by Gumbel-max."""
+    rng = W.philox(seed, 7)
+    d64 = rng.standard_normal((B, gamma + 1, V)) * scale
+    t64 = d64 + sigma * rng.standard_normal((B, gamma + 1, V))
+    draft, target = W.encode(d64, dtype), W.encode(t64, dtype)
+    tokens = W.gumbel_argmax(W.decode_f64(draft, dtype)[:, :gamma], T, W.philox(seed, 8))
+    return W.Batch(name=f"rand_B{B}_g{gamma}_V{V}_{dtype}", B=B, gamma=gamma, V=V, T=T,
+                   dtype=dtype, draft=draft, target=target, draft_tokens=tokens,
+                   u_accept=W.uniforms24(W.philox(seed, 9), (B, gamma)),
+                   u_sample=W.uniforms24(W.philox(seed, 10), (B, gamma + 1)),
+                   in_len=np.arange(B, dtype=np.int32) * 3, seed=seed)
+
+
+# --------------------------------------------------------------------------- configured workloads
+
+@pytest.mark.parametrize("name", list(W.WORKLOADS))
+def test_workload_residual(name):
+    rep = H.parity(workload(name), "residual")
+    rep.check()
+
+
+@pytest.mark.parametrize("eps", [0.0, 1e-8])
+def test_workload_saguaro(eps):
+    rep = H.parity(workload("B256_g8_V152064_bf16"), "saguaro", eps)
+    rep.check()
+
+
+def test_alpha_spread_realised():
+    """The B=256 workload's realised acceptance tracks its alpha ramp."""
+    batch = workload("B256_g8_V152064_bf16")
+    gpu = H.run_gpu(batch, diag=True)
+    px, qx = gpu["diag"]["px"], gpu["diag"]["qx"]
+    acc = np.minimum(1.0, qx / px).mean(1)   # E[accept | x] averaged over positions
+    lo, hi = acc[:64].mean(), acc[-64:].mean()
+    H.say(f"[alpha] mean a first quarter {lo:.3f} last quarter {hi:.3f}")
+    assert hi > lo + 0.2
+
+
+# --------------------------------------------------------------------------- toy (V = 7)
+
+def test_toy_generation_64_tokens():
+    """A 64-token toy generation, one B=1 call per round, GPU and oracle in lockstep."""
+    out_g, out_o, prev, rnd = [0], [0], 0, 0
+    while len(out_g) < 64:
+        batch = W.toy_batch([prev], seed=1201, round_index=rnd)
+        gpu = H.run_gpu(batch, diag=False)
+        ref = H.run_oracle(batch)
+        rep = H.compare(batch, gpu, ref, check_diag=False)
+        assert rep.excused == 0
+        rep.check()
+        k = int(gpu["accepted"][0])
+        out_g += gpu["tokens"][0][: k + 1].tolist()
+        out_o += ref[0].tokens[: k + 1].tolist()
+        prev = out_g[-1]
+        rnd += 1
+    assert out_g == out_o
+    H.say(f"[toy64] rounds={rnd} tokens={out_g[:64]}")
+
+
+def test_toy_200k_rounds():
+    """200k independent toy rounds in one call: oracle parity on a slice, and the
+    output law equals the target tables (speculative-decoding blog, section 3)."""
+    n = 200_000
+    prev = np.arange(n) % 2
+    batch = W.toy_batch(prev, seed=1201)
+    gpu = H.run_gpu(batch, diag=False)
+    ref = H.run_oracle(batch, seqs=range(20_000))
+    rep = H.compare(batch, gpu, ref, check_diag=False)
+    H.say(f"[toy200k] {rep}")
+    rep.check()
+    trans = np.zeros((2, 7))
+    for b in range(n):
+        k = int(gpu["accepted"][b])
+        seq = [int(prev[b])] + gpu["tokens"][b][: k + 1].tolist()
+        for u, v in zip(seq[:-1], seq[1:]):
+            trans[int(u != 0), v] += 1
+    for s in (0, 1):
+        exp = W.TOY_TARGET[s] * trans[s].sum()
+        p = scipy.stats.chisquare(trans[s], exp).pvalue
+        H.say(f"[toy200k] state {s} chi2 p={p:.3g} max dev "
+              f"{np.abs(trans[s] / trans[s].sum() - W.TOY_TARGET[s]).max():.4f}")
+        assert p > 1e-3
+
+
+# --------------------------------------------------------------------------- shapes and edges
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("V,gamma,B", [(1, 3, 4), (5, 2, 9), (7, 4, 33), (2048 * 3 + 5, 3, 17),
+                                      (16384 * 2 + 8, 2, 5), (4096, 63, 3), (50000, 1, 7),
+                                      (65536, 6, 12)])
+def test_shapes(dtype, V, gamma, B):
+    batch = random_batch(B, gamma, V, dtype, 1.0, seed=V + gamma)
+    H.parity(batch, "residual").check()
+    H.parity(batch, "saguaro", 0.0).check()
+
+
+@pytest.mark.parametrize("T", [0.25, 0.8, 2.0])
+def test_temperatures(T):
+    batch = random_batch(16, 4, 20000, "bf16", T, seed=77)
+    H.parity(batch, "residual").check()
+
+
+def test_forced_paths():
+    """u = 0 accepts everything (bonus path); p == q accepts everything; q(x) = 0
+    forces the rejection at a chosen position; p(x) = 0 with q(x) > 0 accepts."""
+    B, g, V = 8, 5, 3000
+    base = random_batch(B, g, V, "f32", 1.0, seed=5)
+    b1 = W.Batch(**{**base.__dict__, "u_accept": np.zeros((B, g), np.float32), "name": "u0"})
+    H.parity(b1, "residual").check()
+    assert (H.run_gpu(b1, diag=False)["accepted"] == g).all()
+    b2 = W.Batch(**{**base.__dict__, "target": base.draft.copy(), "name": "p_eq_q",
+                    "u_accept": np.full((B, g), 1 - 2 ** -24, np.float32)})
+    H.parity(b2, "residual").check()
+    assert (H.run_gpu(b2, diag=False)["accepted"] == g).all()
+    t3 = base.target.copy()
+    for b in range(B):
+        t3[b, b % g, base.draft_tokens[b, b % g]] = -np.inf
+    b3 = W.Batch(**{**base.__dict__, "target": t3, "u_accept": np.zeros((B, g), np.float32),
+                    "name": "q0"})
+    H.parity(b3, "residual").check()
+    gk = H.run_gpu(b3, diag=False)["accepted"]
+    assert gk.tolist() == [b % g for b in range(B)]
+    d4 = base.draft.copy()
+    for b in range(B):
+        d4[b, 0, base.draft_tokens[b, 0]] = -np.inf
+    b4 = W.Batch(**{**base.__dict__, "draft": d4, "name": "p0"})
+    H.parity(b4, "residual").check()
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_invalid_sequences(dtype):
+    B, g, V = 10, 3, 5000
+    base = random_batch(B, g, V, dtype, 1.0, seed=6)
+    d, t, x = base.draft.copy(), base.target.copy(), base.draft_tokens.copy()
+    nan = np.uint16(0x7FC0) if dtype == "bf16" else np.float32(np.nan)
+    inf = np.uint16(0x7F80) if dtype == "bf16" else np.float32(np.inf)
+    ninf = np.uint16(0xFF80) if dtype == "bf16" else np.float32(-np.inf)
+    t[1, g, 17] = nan            # bonus row
+    d[2, 0, 4999] = inf          # draft row 0
+    t[3, 1, :] = ninf            # target row 1 all -inf
+    x[4, 2] = V                  # token out of range
+    x[5, 0] = -1
+    d[6, g, 3] = nan             # draft row gamma: not read by the rule -> valid
+    bad = W.Batch(**{**base.__dict__, "draft": d, "target": t, "draft_tokens": x, "name": "bad"})
+    rep = H.parity(bad, "residual")
+    rep.check()
+    gpu = H.run_gpu(bad, diag=False)
+    assert gpu["accepted"][[1, 2, 3, 4, 5]].tolist() == [-1] * 5
+    assert gpu["accepted"][6] >= 0
+
+
+def test_empty_batch_is_noop():
+    import rejection_sampling_verify_12_amd as R
+    z = torch.zeros((0, 5, 100), dtype=torch.bfloat16, device="cuda")
+    i = torch.zeros((0, 4), dtype=torch.int32, device="cuda")
+    u = torch.zeros((0, 4), dtype=torch.float32, device="cuda")
+    us = torch.zeros((0, 5), dtype=torch.float32, device="cuda")
+    out = R.spec_verify(z, z, i, u, us, 1.0)
+    assert out.tokens.shape == (0, 5)
+
+
+def test_deterministic_replay():
+    """Identical inputs give bit-identical outputs (including diagnostics)."""
+    batch = workload("B64_g5_V128256_bf16")
+    db = H.to_device(batch)
+    first = H.run_gpu(batch, db=db)
+    for _ in range(20):
+        again = H.run_gpu(batch, db=db)
+        for k in ("tokens", "accepted", "mask", "out_len"):
+            assert np.array_equal(first[k], again[k])
+        for k, v in first["diag"].items():
+            assert np.array_equal(v, again["diag"][k], equal_nan=True), k
+
+
+# --------------------------------------------------------------------------- outcome prediction
+
+def _predict(batch, gpu=None):
+    import rejection_sampling_verify_12_amd as R
+    db = H.to_device(batch)
+    acc = tok = None
+    if gpu is not None:
+        acc = torch.from_numpy(gpu["accepted"]).cuda()
+        tok = torch.from_numpy(gpu["tokens"]).cuda()
+    out = R.spec_predict_outcomes(db.draft, acc, tok)
+    torch.cuda.synchronize()
+    return out.cand.cpu().numpy(), out.hit.cpu().numpy(), out.cand_idx.cpu().numpy()
+
+
+def test_predict_outcomes_workload():
+    batch = workload("B128_g4_V128256_bf16")
+    gpu = H.run_gpu(batch, diag=False)
+    cand, hit, idx = _predict(batch, gpu)
+    ref_cand = O.predict_outcomes(batch.draft64())
+    np.testing.assert_array_equal(cand, ref_cand)
+    ref_hit, ref_idx = O.predict_hits(ref_cand, gpu["accepted"], gpu["tokens"])
+    np.testing.assert_array_equal(hit, ref_hit)
+    np.testing.assert_array_equal(idx, ref_idx)
+    H.say(f"[predict] hit rate {hit.mean():.3f} over {len(hit)} sequences")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_predict_edges(dtype):
+    B, g, V = 6, 2, 20000
+    rng = np.random.default_rng(3)
+    d64 = np.round(rng.normal(size=(B, g + 1, V)), 1)   # many ties
+    d64[0, 0, :] = 0.0
+    d64[0, 0, 5] = -0.0
+    d64[2, 2, 19999] = 50.0                               # max at the last id
+    draft = W.encode(d64, dtype)
+    draft[1, 1, 100] = np.uint16(0x7FC0) if dtype == "bf16" else np.float32(np.nan)
+    batch = W.Batch(name="pred_edges", B=B, gamma=g, V=V, T=1.0, dtype=dtype, draft=draft,
+                    target=draft, draft_tokens=np.zeros((B, g), np.int32),
+                    u_accept=np.zeros((B, g), np.float32), u_sample=np.zeros((B, g + 1), np.float32),
+                    in_len=np.zeros(B, np.int32))
+    cand, _, _ = _predict(batch)
+    np.testing.assert_array_equal(cand, O.predict_outcomes(W.decode_f64(draft, dtype)))
+    small = W.Batch(**{**batch.__dict__, "V": 2, "draft": draft[:, :, :2].copy(),
+                       "target": draft[:, :, :2].copy()})
+    cand2, _, _ = _predict(small)
+    np.testing.assert_array_equal(cand2, O.predict_outcomes(W.decode_f64(small.draft, dtype)))

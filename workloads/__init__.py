@@ -64,9 +64,11 @@ def uniforms24(rng: np.random.Generator, shape) -> np.ndarray:
 
 def f32_to_bf16_bits(x) -> np.ndarray:
     """Round float32 values to bfloat16 (round to nearest even); return the bits."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    bias = ((u >> 16) & 1) + 0x7FFF
-    return ((u + bias) >> 16).astype(np.uint16)
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    if np.isnan(x).any():
+        raise ValueError("NaN logits are planted as raw bits, not rounded")
+    u = u + (((u >> 16) & 1) + np.uint32(0x7FFF))   # no overflow for finite or inf values
+    return (u >> 16).astype(np.uint16)
 
 
 def bf16_bits_to_f64(bits) -> np.ndarray:
@@ -94,8 +96,7 @@ def encode(x64: np.ndarray, dtype: str) -> np.ndarray:
 # Gumbel-max draws (draft-token sampling for the input recipe).
 
 def gumbel(rng: np.random.Generator, shape) -> np.ndarray:
-    u = (rng.integers(0, 1 << 53, size=shape, dtype=np.int64).astype(np.float64) + 0.5) * (2.0 ** -53)
-    return -np.log(-np.log(u))
+    return rng.gumbel(size=shape)
 
 
 def gumbel_argmax(logits64: np.ndarray, T: float, rng: np.random.Generator) -> np.ndarray:
@@ -273,6 +274,24 @@ def workload_alpha(name: str) -> np.ndarray:
     return np.full(B, float(alpha))
 
 
-def make_workload(name: str, seqs=None, table: dict | None = None) -> Batch:
+def _make_part(args):
+    name, seqs = args
+    return make_workload(name, seqs=seqs)
+
+
+def make_workload(name: str, seqs=None, table: dict | None = None, workers: int = 1) -> Batch:
+    """A named workload (optionally a subset of its sequences).  ``workers`` > 1
+    generates sequence blocks in worker processes; the result is identical."""
     B, gamma, V, T, dtype, _, seed = WORKLOADS[name]
+    seqs = np.arange(B) if seqs is None else np.asarray(seqs)
+    if workers > 1 and len(seqs) > 1:
+        import concurrent.futures as cf
+        import multiprocessing as mp
+        blocks = [b for b in np.array_split(seqs, min(workers, len(seqs))) if len(b)]
+        with cf.ProcessPoolExecutor(len(blocks), mp_context=mp.get_context("fork")) as ex:
+            parts = list(ex.map(_make_part, [(name, b) for b in blocks]))
+        cat = {f: np.concatenate([getattr(p, f) for p in parts])
+               for f in ("draft", "target", "draft_tokens", "u_accept", "u_sample", "in_len",
+                         "alpha_target")}
+        return dataclasses.replace(parts[0], B=len(seqs), **cat)
     return zipf_batch(name, B, gamma, V, T, dtype, workload_alpha(name), seed, seqs=seqs, table=table)
