@@ -187,7 +187,8 @@ def main():
                      "p90": float(np.percentile(per_call_ms, 90))},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic_record(args.workload, args.mode),
-                     "kernel": "spec_verify call (all kernels)", "bytes_alg": bytes_alg},
+                     "kernel": "one spec_verify call (every kernel it launches), event-timed on its stream",
+                     "bytes_alg": bytes_alg},
         "source_digest": source_digest(),
     }
     if not args.no_cpu:

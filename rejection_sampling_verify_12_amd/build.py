@@ -36,17 +36,18 @@ def command(out: str = LIB, extra=()) -> list[str]:
             "-I", INCLUDE, "-I", CSRC, *extra, "-o", out, *srcs]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile the library; returns its path.  Always recompiles."""
-    tmp = LIB + ".tmp"
-    cmd = command(tmp)
+def build(verbose: bool = False, out: str = LIB, defines: dict | None = None) -> str:
+    """Compile the library; returns its path.  Always recompiles.  ``defines``
+    sets tuning macros (SV_CHUNK, SV_STREAM_UNROLL, SV_TILES_PER_ITEM, ...)."""
+    tmp = out + ".tmp"
+    cmd = command(tmp, [f"-D{k}={v}" for k, v in (defines or {}).items()])
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

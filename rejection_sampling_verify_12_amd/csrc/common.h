@@ -11,7 +11,10 @@ constexpr int kThreads = 256;               // every kernel runs 256-thread work
 constexpr int kWaves = kThreads / 64;
 constexpr int kUnit = 8;                    // logits per thread per load unit (16 B of bf16)
 constexpr int kTile = kThreads * kUnit;     // 2048 logits: granularity of the sampling scan
-constexpr int kChunk = 16384;               // logits of one row per statistics work-group
+#ifndef SV_CHUNK
+#define SV_CHUNK 32768
+#endif
+constexpr int kChunk = SV_CHUNK;            // logits of one row per statistics work-group (target)
 constexpr float kNegSentinel = -1.0e30f;    // "no finite logit seen yet"
 
 enum : int { kF32 = 0, kBF16 = 1 };
@@ -52,6 +55,46 @@ __device__ __forceinline__ void load8(const void* row, int64_t j0, int64_t n, fl
   } else {
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = (j0 + e < n) ? load_one<DT>(row, j0 + e) : -INFINITY;
+  }
+}
+
+// Eight logits as loaded: the raw 16-byte word for aligned bf16 rows (unpacked
+// when used, so a batch of loads in flight costs 4 VGPRs per eight logits),
+// floats otherwise.
+template <int DT, bool VEC>
+struct Raw8 {
+  float v[8];
+};
+template <>
+struct Raw8<kBF16, true> {
+  uint4 w;
+};
+
+template <int DT, bool VEC>
+__device__ __forceinline__ void load_raw(const void* row, int64_t j0, int64_t n, Raw8<DT, VEC>& r) {
+  if constexpr (DT == kBF16 && VEC) {
+    if (j0 < n) r.w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(row) + j0);
+    else r.w = make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u);   // -inf
+  } else {
+    if (j0 < n) {
+      load8<DT, VEC>(row, j0, n, r.v);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) r.v[e] = -INFINITY;
+    }
+  }
+}
+
+template <int DT, bool VEC>
+__device__ __forceinline__ void unpack(const Raw8<DT, VEC>& r, float (&v)[8]) {
+  if constexpr (DT == kBF16 && VEC) {
+    v[0] = bf16_lo(r.w.x); v[1] = bf16_hi(r.w.x);
+    v[2] = bf16_lo(r.w.y); v[3] = bf16_hi(r.w.y);
+    v[4] = bf16_lo(r.w.z); v[5] = bf16_hi(r.w.z);
+    v[6] = bf16_lo(r.w.w); v[7] = bf16_hi(r.w.w);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = r.v[e];
   }
 }
 

@@ -31,6 +31,8 @@
 
 #include <cmath>
 #include <limits.h>
+#include <algorithm>
+#include <type_traits>
 
 namespace sv {
 
@@ -59,7 +61,30 @@ __device__ __forceinline__ Partial load_partial(const Partial* p) {
 
 enum : int { kModeTarget = 0, kModeResidual = 1, kModeSaguaro = 2, kModeSaguaroEps = 3 };
 
-constexpr int kTilesPerItem = 4;
+#ifndef SV_TILES_PER_ITEM
+#define SV_TILES_PER_ITEM 4
+#endif
+#ifndef SV_STREAM_UNROLL
+#define SV_STREAM_UNROLL 4
+#endif
+// 1: one persistent cooperative kernel runs every phase (the default);
+// 0: separate stream, decision and sampling kernels.
+#ifndef SV_FUSED
+#define SV_FUSED 0
+#endif
+// Sampling items of a sequence run this many rounds of the persistent grid
+// after its stream items (x1000).
+// Waves per SIMD the fused kernel is compiled for (registers are capped to
+// fit; the rare decision and refine paths may spill).
+#ifndef SV_FUSED_WAVES
+#define SV_FUSED_WAVES 8
+#endif
+#ifndef SV_LAG_MILLIROUNDS
+#define SV_LAG_MILLIROUNDS 1500
+#endif
+constexpr int kTilesPerItem = SV_TILES_PER_ITEM;
+static_assert(kChunk % (SV_STREAM_UNROLL * kThreads * kUnit) == 0,
+              "a stream chunk must hold whole batches");
 
 // A sequence's decision, written by its last stream item.
 struct SeqRec {
@@ -75,12 +100,35 @@ struct SeqRec {
   double pad1;
 };
 
-// Arrival counters of one sequence, one 128-byte line each.
+static_assert(sizeof(SeqRec) % 8 == 0, "SeqRec is moved as 64-bit words");
+constexpr int kRecWords = sizeof(SeqRec) / 8;
+
+// A decision record written and read with device-coherent 64-bit accesses.
+__device__ __forceinline__ void store_rec(SeqRec* p, const SeqRec& r) {
+  const uint64_t* w = reinterpret_cast<const uint64_t*>(&r);
+#pragma unroll
+  for (int i = 0; i < kRecWords; ++i) st_dev_u64(reinterpret_cast<uint64_t*>(p) + i, w[i]);
+}
+__device__ __forceinline__ SeqRec load_rec(const SeqRec* p) {
+  SeqRec r;
+  uint64_t* w = reinterpret_cast<uint64_t*>(&r);
+#pragma unroll
+  for (int i = 0; i < kRecWords; ++i) w[i] = ld_dev_u64(reinterpret_cast<const uint64_t*>(p) + i);
+  return r;
+}
+// epsS and pad0 share the fifth word.
+__device__ __forceinline__ void store_rec_eps(SeqRec* p, float epsS) {
+  st_dev_u64(reinterpret_cast<uint64_t*>(p) + 4, (uint64_t)__float_as_uint(epsS));
+}
+
+// Arrival counters and ready flags of one sequence, one 128-byte line each.
 struct SeqCtr {
-  unsigned stream_done;
-  unsigned a_done;
-  unsigned b_done;
-  unsigned pad[29];
+  unsigned stream_done;  // stream items finished
+  unsigned a_done;       // residual-mass items finished (Saguaro eps > 0)
+  unsigned b_done;       // sampling items finished
+  unsigned decided;      // 1 once the decision record is written
+  unsigned a_ready;      // 1 once eps * residual mass is written
+  unsigned pad[27];
 };
 
 struct VerifyArgs {
@@ -96,6 +144,8 @@ struct VerifyArgs {
   uint64_t* out_mask;
   int32_t* out_len;
   spec_diag diag;
+  unsigned* err;     // nonzero if a bounded wait timed out (co-residency lost)
+  unsigned* next;    // item counter of the fused kernel (zero between calls)
   Partial* part;     // [B][2*gamma+1][nc]
   SeqRec* seq;       // [B]
   SeqCtr* ctr;       // [B]
@@ -142,6 +192,35 @@ __device__ __forceinline__ bool arrive(unsigned* counter, unsigned total, int* l
 // ---------------------------------------------------------------------------
 // Stream item: one chunk of one row -> Partial.
 
+// One batch of N units (8 logits each) of a lane: raise the lane's integer
+// offset if the batch holds a larger logit (rescaling the running sum by an
+// exact power of two), then add the batch's terms 2^(l c_T - mref), tree-summed
+// in fp32, to the fp64 running sum.
+template <int DT, bool VEC, int N>
+__device__ __forceinline__ void stream_batch(const Raw8<DT, VEC> (&raw)[N], float ch, float cl,
+                                             float& mref, float& mraw, double& s) {
+  float v[N * 8];
+#pragma unroll
+  for (int u = 0; u < N; ++u) unpack<DT, VEC>(raw[u], *reinterpret_cast<float(*)[8]>(v + u * 8));
+  float bm = v[0];
+#pragma unroll
+  for (int e = 1; e < N * 8; ++e) bm = fmaxf(bm, v[e]);
+  mraw = fmaxf(mraw, bm);
+  const float bl = bm * ch;
+  if (bl > mref) {
+    const float nref = ceilf(fminf(bl, 1.0e30f));
+    if (s != 0.0) s = ldexp(s, (int)fmaxf(mref - nref, -2000.f));
+    mref = nref;
+  }
+#pragma unroll
+  for (int e = 0; e < N * 8; ++e) v[e] = exp2_fast(fmaf(v[e], cl, fmaf(v[e], ch, -mref)));
+#pragma unroll
+  for (int w = N * 4; w >= 1; w >>= 1)   // pairwise sum in fp32
+#pragma unroll
+    for (int e = 0; e < w; ++e) v[e] += v[e + w];
+  s += (double)v[0];
+}
+
 template <int DT, bool VEC, int U>
 __device__ __forceinline__ void stream_item(const VerifyArgs& a, int b, int r, int c, float* lds_f,
                                             double* lds_d) {
@@ -154,47 +233,47 @@ __device__ __forceinline__ void stream_item(const VerifyArgs& a, int b, int r, i
   float mref = kNegSentinel, mraw = -INFINITY;
   double s = 0.0;
   constexpr int64_t kStep = (int64_t)kThreads * kUnit;
-  for (int64_t j = begin + (int64_t)threadIdx.x * kUnit; j < end; j += kStep * U) {
-    float v[U * 8];
+  int64_t j = begin + (int64_t)threadIdx.x * kUnit;
+  // Full batches: U units, all in range, loads issued back to back.
+  for (; j + (U - 1) * kStep + kUnit <= end; j += U * kStep) {
+    Raw8<DT, VEC> raw[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t ju = j + u * kStep;
-      float(&vu)[8] = *reinterpret_cast<float(*)[8]>(v + u * 8);
-      if (ju < end) {
-        load8<DT, VEC>(row, ju, end, vu);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) vu[e] = -INFINITY;
-      }
-    }
-    float bm = v[0];
-#pragma unroll
-    for (int e = 1; e < U * 8; ++e) bm = fmaxf(bm, v[e]);
-    mraw = fmaxf(mraw, bm);
-    const float bl = bm * ch;
-    if (bl > mref) {   // new offset: rescale the running sum by an exact power of two
-      const float nref = ceilf(fminf(bl, 1.0e30f));
-      if (s != 0.0) s = ldexp(s, (int)fmaxf(mref - nref, -2000.f));
-      mref = nref;
-    }
-#pragma unroll
-    for (int e = 0; e < U * 8; ++e) v[e] = exp2_fast(fmaf(v[e], cl, fmaf(v[e], ch, -mref)));
-#pragma unroll
-    for (int w = U * 4; w >= 1; w >>= 1)   // pairwise sum of the batch in fp32
-#pragma unroll
-      for (int e = 0; e < w; ++e) v[e] += v[e + w];
-    s += (double)v[0];
+    for (int u = 0; u < U; ++u) load_raw<DT, VEC>(row, j + u * kStep, end, raw[u]);
+    stream_batch<DT, VEC, U>(raw, ch, cl, mref, mraw, s);
   }
-  const float mb = block_max(mref, lds_f);
-  const float mr = block_max(mraw, lds_f);
-  const double sd = (s != 0.0) ? ldexp(s, (int)fmaxf(mref - mb, -2000.f)) : 0.0;
-  const double sb = block_sum(sd, lds_d);
-  if (threadIdx.x == 0)
+  // Remaining units of this lane (fewer than U; the last may be partial).
+  for (; j < end; j += kStep) {
+    Raw8<DT, VEC> raw[1];
+    load_raw<DT, VEC>(row, j, end, raw[0]);
+    stream_batch<DT, VEC, 1>(raw, ch, cl, mref, mraw, s);
+  }
+  // Merge the lanes: wave shuffles, then one barrier; thread 0 stores the piece.
+  const float wm = wave_max(mref);
+  const float wr = wave_max(mraw);
+  double sd = (s != 0.0) ? ldexp(s, (int)fmaxf(mref - wm, -2000.f)) : 0.0;
+  sd = wave_sum(sd);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    lds_f[wave] = wm;
+    lds_f[kWaves + wave] = wr;
+    lds_d[wave] = sd;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float mb = lds_f[0], mr = lds_f[kWaves];
+    for (int i = 1; i < kWaves; ++i) {
+      mb = fmaxf(mb, lds_f[i]);
+      mr = fmaxf(mr, lds_f[kWaves + i]);
+    }
+    double sb = 0.0;
+    for (int i = 0; i < kWaves; ++i)
+      if (lds_d[i] != 0.0) sb += ldexp(lds_d[i], (int)fmaxf(lds_f[i] - mb, -2000.f));
     store_partial(a.part + ((int64_t)b * (2 * a.gamma + 1) + r) * a.nc + c, mb, mr, sb);
+  }
 }
 
 // ---------------------------------------------------------------------------
-// Decision of one sequence (run by its last stream item).
+// Decision of one sequence.
 
 struct DecideLds {
   float M[128];
@@ -204,34 +283,52 @@ struct DecideLds {
   int k, valid;
 };
 
+// Merge the chunk pieces of every row (16 lanes per row, 16 rows per pass;
+// fp64), then run the accept test at every draft position (wave 0, lane i =
+// position i; fp64) and record the sequence's decision.
 template <int DT>
 __device__ void decide_seq(const VerifyArgs& a, int b, DecideLds& sh) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = a.gamma, R = 2 * g + 1;
   const double cTd = a.cTd;
   const Partial* P0 = a.part + (int64_t)b * R * a.nc;
-
-  // 1. Merge each row's chunk pieces (one wave per row, lanes over chunks; fp64).
-  for (int r = wave; r < R; r += kWaves) {
-    const Partial* P = P0 + (int64_t)r * a.nc;
+  const int sub = lane & 15;
+  for (int r0 = 0; r0 < R; r0 += 16) {
+    const int r = r0 + wave * 4 + (lane >> 4);
     float M = kNegSentinel, mr = -INFINITY;
-    // lanes hold their chunks' pieces (nc <= 64 in one pass; more loop)
-    for (int c0 = 0; c0 < a.nc; c0 += 64) {
-      const int c = c0 + lane;
-      const Partial p = c < a.nc ? load_partial(P + c) : Partial{kNegSentinel, -INFINITY, 0.0};
-      M = fmaxf(M, p.mc);
-      mr = fmaxf(mr, p.mraw);
-    }
-    M = wave_max(M);
-    mr = wave_max(mr);
     double z = 0.0;
-    for (int c0 = 0; c0 < a.nc; c0 += 64) {
-      const int c = c0 + lane;
-      const Partial p = c < a.nc ? load_partial(P + c) : Partial{kNegSentinel, -INFINITY, 0.0};
-      if (p.s != 0.0) z += ldexp(p.s, (int)fmaxf(p.mc - M, -2000.f));
+    if (r < R) {
+      const Partial* P = P0 + (int64_t)r * a.nc;
+      if (a.nc <= 16) {   // one piece per lane, kept in registers
+        const Partial p = sub < a.nc ? load_partial(P + sub) : Partial{kNegSentinel, -INFINITY, 0.0};
+        M = p.mc;
+        mr = p.mraw;
+#pragma unroll
+        for (int o = 8; o > 0; o >>= 1) {
+          M = fmaxf(M, __shfl_xor(M, o, 16));
+          mr = fmaxf(mr, __shfl_xor(mr, o, 16));
+        }
+        if (p.s != 0.0) z = ldexp(p.s, (int)fmaxf(p.mc - M, -2000.f));
+      } else {
+        for (int c = sub; c < a.nc; c += 16) {
+          const Partial p = load_partial(P + c);
+          M = fmaxf(M, p.mc);
+          mr = fmaxf(mr, p.mraw);
+        }
+#pragma unroll
+        for (int o = 8; o > 0; o >>= 1) {
+          M = fmaxf(M, __shfl_xor(M, o, 16));
+          mr = fmaxf(mr, __shfl_xor(mr, o, 16));
+        }
+        for (int c = sub; c < a.nc; c += 16) {
+          const Partial p = load_partial(P + c);
+          if (p.s != 0.0) z += ldexp(p.s, (int)fmaxf(p.mc - M, -2000.f));
+        }
+      }
     }
-    z = wave_sum(z);
-    if (lane == 0) {
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) z += __shfl_xor(z, o, 16);
+    if (r < R && sub == 0) {
       const int ok = (z > 0.0) && isfinite(z) && isfinite(M);
       sh.M[r] = M;
       sh.Z[r] = z;
@@ -243,7 +340,6 @@ __device__ void decide_seq(const VerifyArgs& a, int b, DecideLds& sh) {
   }
   __syncthreads();
 
-  // 2. Accept test at every draft position (wave 0, lane i = position i).
   if (wave == 0) {
     int rows_bad = 0;
     for (int r = lane; r < R; r += 64) rows_bad |= sh.bad[r];
@@ -301,7 +397,7 @@ __device__ void decide_seq(const VerifyArgs& a, int b, DecideLds& sh) {
     rec.pad0 = 0.f;
     rec.Zt = sh.Z[g + k];
     rec.pad1 = 0.0;
-    a.seq[b] = rec;
+    store_rec(a.seq + b, rec);
   }
 }
 
@@ -325,69 +421,99 @@ __device__ __forceinline__ SampleCoef coef_of(const VerifyArgs& a, const SeqRec&
 
 constexpr float kLn2f = 0.69314718055994530942f;
 
-// 1 - 2^d for d in (-1, 0]: -expm1(d ln 2) by its Taylor series (degree 9,
-// truncation below 1e-8 relative); 1 - 2^d directly for d <= -1.
+// 1 - 2^d.  PRECISE: for d in (-1, 0], -expm1(d ln 2) by its Taylor series
+// (degree 9, truncation below 1e-8 relative), so a small residual keeps its
+// relative precision; otherwise (and for d <= -1) 1 - 2^d from the rounded
+// exponential, whose error is a few ulp of 1 (of q_j, not of the residual).
+template <bool PRECISE>
 __device__ __forceinline__ float one_minus_exp2(float d, float ex) {
-  const float x = d * kLn2f;
-  float p = 1.f / 362880.f;
-  p = fmaf(p, x, 1.f / 40320.f);
-  p = fmaf(p, x, 1.f / 5040.f);
-  p = fmaf(p, x, 1.f / 720.f);
-  p = fmaf(p, x, 1.f / 120.f);
-  p = fmaf(p, x, 1.f / 24.f);
-  p = fmaf(p, x, 1.f / 6.f);
-  p = fmaf(p, x, 0.5f);
-  p = fmaf(p, x, 1.f);
-  return d > -1.f ? -x * p : 1.f - ex;
+  if constexpr (!PRECISE) {
+    return 1.f - ex;
+  } else {
+    const float x = d * kLn2f;
+    float p = 1.f / 362880.f;
+    p = fmaf(p, x, 1.f / 40320.f);
+    p = fmaf(p, x, 1.f / 5040.f);
+    p = fmaf(p, x, 1.f / 720.f);
+    p = fmaf(p, x, 1.f / 120.f);
+    p = fmaf(p, x, 1.f / 24.f);
+    p = fmaf(p, x, 1.f / 6.f);
+    p = fmaf(p, x, 0.5f);
+    p = fmaf(p, x, 1.f);
+    return d > -1.f ? -x * p : 1.f - ex;
+  }
 }
 
-// Sampling weights of eight logits, each proportional (one factor per
-// sequence) to the probability of the distribution drawn from:
+// Sampling weight of one logit pair, proportional (one factor per sequence)
+// to the probability of the distribution drawn from:
 //   target row:  q_j                      (eq_j = 2^(lt_j c_T - Mt))
 //   residual:    (q_j - p_j)+             (eq_j (1 - 2^delta_j) where delta_j < 0)
 //   Saguaro:     sqrt(p_j (q_j - p_j)+)   (eq_j sqrt(2^delta_j (1 - 2^delta_j)))
 //   Saguaro eps: sqrt(p_j max(r_j, eps))  (sqrt(eq_j 2^delta_j max(res_j, eps sum res)))
-// with delta_j = log2(p_j / q_j) = (ld_j - lt_j) c_T + K.  The residual is
-// formed from delta_j (exact logit difference for bf16, a two-sum for
-// float32), so its relative error stays at a few ulp where q_j and p_j nearly
-// cancel.  r = the residual weight.
-template <int DT>
-__device__ __forceinline__ void sample_weights(int mode, const float (&ld)[8], const float (&lt)[8],
-                                               const SampleCoef& c, float (&w)[8], float (&r)[8]) {
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float eq = exp2_fast(fmaf(lt[e], c.c_lo, fmaf(lt[e], c.c_hi, -c.Mt)));
-    if (mode == kModeTarget) {
-      w[e] = eq;
-      r[e] = 0.f;
-      continue;
-    }
-    const float dl = ld[e] - lt[e];
+// with delta_j = log2(p_j / q_j) = (ld_j - lt_j) c_T + K (exact logit
+// difference for bf16, a two-sum for float32).  r = the residual weight.
+template <int DT, int MODE, bool PRECISE>
+__device__ __forceinline__ float weight_one(float ld, float lt, const SampleCoef& c, float& r) {
+  const float eq = exp2_fast(fmaf(lt, c.c_lo, fmaf(lt, c.c_hi, -c.Mt)));
+  if constexpr (MODE == kModeTarget) {
+    r = 0.f;
+    return eq;
+  } else {
+    const float dl = ld - lt;
     float d;
     if constexpr (DT == kBF16) {
       d = fmaf(dl, c.c_hi, c.K_hi) + fmaf(dl, c.c_lo, c.K_lo);   // dl is exact
     } else {
-      const float bb = dl - ld[e];
-      const float err = (ld[e] - (dl - bb)) - (lt[e] + bb);       // ld - lt = dl + err
+      const float bb = dl - ld;
+      const float err = (ld - (dl - bb)) - (lt + bb);             // ld - lt = dl + err
       d = fmaf(dl, c.c_hi, c.K_hi) + fmaf(err, c.c_hi, fmaf(dl, c.c_lo, c.K_lo));
     }
     const float ex = exp2_fast(d);          // p_j / q_j
-    const float em1 = one_minus_exp2(d, ex);
+    const float em1 = one_minus_exp2<PRECISE>(d, ex);
     const bool pos = (eq > 0.f) && (d < 0.f);
     const float res = pos ? eq * em1 : 0.f;
-    r[e] = res;
-    if (mode == kModeResidual) w[e] = res;
-    else if (mode == kModeSaguaro) w[e] = pos ? eq * sqrtf(ex * em1) : 0.f;
-    else w[e] = (eq > 0.f) ? sqrtf(eq * ex * fmaxf(res, c.epsS)) : 0.f;
+    r = res;
+    if constexpr (MODE == kModeResidual) return res;
+    else if constexpr (MODE == kModeSaguaro) return pos ? eq * sqrtf(ex * em1) : 0.f;
+    else return (eq > 0.f) ? sqrtf(eq * ex * fmaxf(res, c.epsS)) : 0.f;
   }
 }
 
-template <int DT, bool VEC>
-__device__ __forceinline__ void load_pair(int mode, const void* drow, const void* trow, int64_t j0,
-                                          int64_t V, float (&ld)[8], float (&lt)[8]) {
+template <int DT, int MODE, bool PRECISE>
+__device__ __forceinline__ void sample_weights(const float (&ld)[8], const float (&lt)[8],
+                                               const SampleCoef& c, float (&w)[8], float (&r)[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) w[e] = weight_one<DT, MODE, PRECISE>(ld[e], lt[e], c, r[e]);
+}
+
+// Mode chosen at run time (scalar paths: pi(y), degenerate fallbacks).
+template <int DT, bool PRECISE>
+__device__ __noinline__ float weight_rt(int mode, float ld, float lt, const SampleCoef& c, float& r) {
+  switch (mode) {
+    case kModeTarget: return weight_one<DT, kModeTarget, PRECISE>(ld, lt, c, r);
+    case kModeResidual: return weight_one<DT, kModeResidual, PRECISE>(ld, lt, c, r);
+    case kModeSaguaro: return weight_one<DT, kModeSaguaro, PRECISE>(ld, lt, c, r);
+    default: return weight_one<DT, kModeSaguaroEps, PRECISE>(ld, lt, c, r);
+  }
+}
+
+// Call f with the weight mode as a compile-time constant.
+template <class F>
+__device__ __forceinline__ void with_mode(int mode, F&& f) {
+  switch (mode) {
+    case kModeTarget: f(std::integral_constant<int, kModeTarget>{}); break;
+    case kModeResidual: f(std::integral_constant<int, kModeResidual>{}); break;
+    case kModeSaguaro: f(std::integral_constant<int, kModeSaguaro>{}); break;
+    default: f(std::integral_constant<int, kModeSaguaroEps>{}); break;
+  }
+}
+
+template <int DT, bool VEC, int MODE>
+__device__ __forceinline__ void load_pair(const void* drow, const void* trow, int64_t j0, int64_t V,
+                                          float (&ld)[8], float (&lt)[8]) {
   if (j0 < V) {
     load8<DT, VEC>(trow, j0, V, lt);
-    if (mode != kModeTarget) load8<DT, VEC>(drow, j0, V, ld);
+    if constexpr (MODE != kModeTarget) load8<DT, VEC>(drow, j0, V, ld);
   } else {
 #pragma unroll
     for (int e = 0; e < 8; ++e) lt[e] = ld[e] = -INFINITY;
@@ -402,27 +528,29 @@ __device__ __forceinline__ void draw_rows(const VerifyArgs& a, int b, int k, con
   trow = row_ptr<DT>(a, b, a.gamma + k);
 }
 
-// Tile sums of the weights of `mode` over tiles [t0, t0 + kTilesPerItem) (clipped
-// to ntile): tw[i] (fp64, identical in every thread) and the residual total.
-template <int DT, bool VEC>
-__device__ __forceinline__ void tile_sums(const VerifyArgs& a, int b, int mode, const SampleCoef& cf,
-                                          int k, int t0, double (&tw)[kTilesPerItem + 1],
-                                          double* lds_d) {
+// Tile sums of the weights over tiles [t0, t0 + kTilesPerItem) (clipped to
+// ntile): tw[i] (fp64, identical in every thread) and, last, the residual total.
+template <int DT, bool VEC, int MODE>
+__device__ __forceinline__ void tile_sums(const VerifyArgs& a, int b, const SampleCoef& cf, int k,
+                                          int t0, double (&tw)[kTilesPerItem + 1], double* lds_d) {
   const void *drow, *trow;
   draw_rows<DT>(a, b, k, drow, trow);
   const int64_t lane_off = (int64_t)threadIdx.x * kUnit;
-  float ld[kTilesPerItem][8], lt[kTilesPerItem][8];
+  Raw8<DT, VEC> rd[kTilesPerItem], rt[kTilesPerItem];
 #pragma unroll
   for (int i = 0; i < kTilesPerItem; ++i) {
     const int t = t0 + i;
     const int64_t j0 = t < a.ntile ? (int64_t)t * kTile + lane_off : (int64_t)a.V;
-    load_pair<DT, VEC>(mode, drow, trow, j0, a.V, ld[i], lt[i]);
+    load_raw<DT, VEC>(trow, j0, a.V, rt[i]);
+    if constexpr (MODE != kModeTarget) load_raw<DT, VEC>(drow, j0, a.V, rd[i]);
   }
   float rs = 0.f;
 #pragma unroll
   for (int i = 0; i < kTilesPerItem; ++i) {
-    float w[8], r[8];
-    sample_weights<DT>(mode, ld[i], lt[i], cf, w, r);
+    float ld[8], lt[8], w[8], r[8];
+    unpack<DT, VEC>(rt[i], lt);
+    if constexpr (MODE != kModeTarget) unpack<DT, VEC>(rd[i], ld);
+    sample_weights<DT, MODE, false>(ld, lt, cf, w, r);
     float ws = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -441,10 +569,10 @@ __device__ __forceinline__ void tile_sums(const VerifyArgs& a, int b, int mode, 
 // Residual mass for the Saguaro clamp (pass A).
 template <int DT, bool VEC>
 __device__ void sample_item_a(const VerifyArgs& a, int b, int s, double* lds_d) {
-  const SeqRec rec = a.seq[b];
-  double tw[kTilesPerItem + 1] = {0, 0, 0, 0, 0};
+  const SeqRec rec = load_rec(a.seq + b);
+  double tw[kTilesPerItem + 1] = {};
   if (rec.valid && rec.mode == kModeSaguaroEps)
-    tile_sums<DT, VEC>(a, b, kModeResidual, coef_of(a, rec), rec.k, s * kTilesPerItem, tw, lds_d);
+    tile_sums<DT, VEC, kModeResidual>(a, b, coef_of(a, rec), rec.k, s * kTilesPerItem, tw, lds_d);
   if (threadIdx.x == 0) st_dev(a.itemsum + (int64_t)b * a.nt + s, tw[kTilesPerItem]);
 }
 
@@ -453,23 +581,26 @@ __device__ void finish_a(const VerifyArgs& a, int b, double* lds_d) {
   double v = 0.0;
   for (int i = threadIdx.x; i < a.nt; i += kThreads) v += ld_dev(a.itemsum + (int64_t)b * a.nt + i);
   v = block_sum(v, lds_d);
-  if (threadIdx.x == 0) a.seq[b].epsS = (float)(v * (double)a.eps);
+  if (threadIdx.x == 0) store_rec_eps(a.seq + b, (float)(v * (double)a.eps));
 }
 
 // Tile sums of the sampling weights (pass B).
 template <int DT, bool VEC>
 __device__ void sample_item_b(const VerifyArgs& a, int b, int s, double* lds_d) {
-  const SeqRec rec = a.seq[b];
+  const SeqRec rec = load_rec(a.seq + b);
   if (!rec.valid) return;
-  double tw[kTilesPerItem + 1];
   const int t0 = s * kTilesPerItem;
-  tile_sums<DT, VEC>(a, b, rec.mode, coef_of(a, rec), rec.k, t0, tw, lds_d);
-  if (threadIdx.x == 0) {
+  const SampleCoef cf = coef_of(a, rec);
+  with_mode(rec.mode, [&](auto m) {
+    double tw[kTilesPerItem + 1];
+    tile_sums<DT, VEC, decltype(m)::value>(a, b, cf, rec.k, t0, tw, lds_d);
+    if (threadIdx.x == 0) {
 #pragma unroll
-    for (int i = 0; i < kTilesPerItem; ++i)
-      if (t0 + i < a.ntile) st_dev(a.tiles + (int64_t)b * a.ntile + t0 + i, tw[i]);
-    st_dev(a.itemsum + (int64_t)b * a.nt + s, tw[kTilesPerItem]);
-  }
+      for (int i = 0; i < kTilesPerItem; ++i)
+        if (t0 + i < a.ntile) st_dev(a.tiles + (int64_t)b * a.ntile + t0 + i, tw[i]);
+      st_dev(a.itemsum + (int64_t)b * a.nt + s, tw[kTilesPerItem]);
+    }
+  });
 }
 
 struct RefineLds {
@@ -479,89 +610,81 @@ struct RefineLds {
   double off, lo, hi, w;
 };
 
-// Locate, rescan and write the outputs (run by the last pass-B item).
-template <int DT, bool VEC>
-__device__ void refine_seq(const VerifyArgs& a, int b, RefineLds& sh) {
+// Locate the tile holding u * S (S = sum of the tile sums) by an fp64 scan
+// over the tile sums in token order; returns S, sets sh.tile and sh.off.
+__device__ double locate_tile(const double* tiles, int ntile, double u, RefineLds& sh, double& target) {
   const int tid = threadIdx.x;
-  const SeqRec rec = a.seq[b];
-  if (!rec.valid) return;   // outputs were written by the decision
-  const int g = a.gamma, k = rec.k;
-  const int64_t orow = (int64_t)b * (g + 1);
-  double* tiles = a.tiles + (int64_t)b * a.ntile;
-  SampleCoef cf = coef_of(a, rec);
-  int mode = rec.mode;
-
-  double rtot = 0.0;
-  for (int i = tid; i < a.nt; i += kThreads) rtot += ld_dev(a.itemsum + (int64_t)b * a.nt + i);
-  rtot = block_sum(rtot, sh.lds_d);
-  if (mode == kModeTarget) rtot = 0.0;
-
   double S = 0.0;
-  for (;;) {
-    double v = 0.0;
-    for (int i = tid; i < a.ntile; i += kThreads) v += ld_dev(tiles + i);
-    S = block_sum(v, sh.lds_d);
-    if (S > 0.0 || mode == kModeTarget) break;
-    // A zero Saguaro normaliser falls back to the residual, a zero residual
-    // mass to q_k: recompute every tile sum here (degenerate inputs only).
-    mode = mode == kModeResidual ? kModeTarget : kModeResidual;
-    if (mode == kModeTarget) rtot = 0.0;
-    for (int t0 = 0; t0 < a.ntile; t0 += kTilesPerItem) {
-      double tw[kTilesPerItem + 1];
-      tile_sums<DT, VEC>(a, b, mode, cf, k, t0, tw, sh.lds_d);
-      if (tid == 0)
-        for (int i = 0; i < kTilesPerItem; ++i)
-          if (t0 + i < a.ntile) st_dev(tiles + t0 + i, tw[i]);
-    }
-    if (tid == 0) wait_mem();
-    __syncthreads();
-  }
-
-  // Tile holding u * S: fp64 exclusive scan over the tile sums in token order.
-  const double target = (double)a.u_smp[orow + k] * S;
-  if (tid == 0) sh.tile = -1;
-  __syncthreads();
-  double carry = 0.0;
-  for (int base = 0; base < a.ntile; base += kThreads) {
-    const int t = base + tid;
-    const double v = t < a.ntile ? ld_dev(tiles + t) : 0.0;
+  if (ntile <= kThreads) {   // one tile sum per thread, loaded once
+    const double v = tid < ntile ? ld_dev(tiles + tid) : 0.0;
     double tot;
-    const double off = carry + block_exclusive_scan(v, sh.lds_d, tot);
-    // Intervals of nonzero tiles are disjoint up to rounding: take the first.
-    const int hit = (t < a.ntile && off <= target && target < off + v) ? t : INT_MAX;
+    const double off = block_exclusive_scan(v, sh.lds_d, tot);
+    S = tot;
+    target = u * S;
+    const int hit = (tid < ntile && off <= target && target < off + v) ? tid : INT_MAX;
     const int first = block_min_int(hit, sh.lds_i);
-    if (first != INT_MAX) {
-      if (t == first) {
-        sh.tile = t;
-        sh.off = off;
-      }
-      __syncthreads();
-      break;
+    if (first != INT_MAX && tid == first) {
+      sh.tile = tid;
+      sh.off = off;
     }
-    carry += tot;
+  } else {
+    double v = 0.0;
+    for (int i = tid; i < ntile; i += kThreads) v += ld_dev(tiles + i);
+    S = block_sum(v, sh.lds_d);
+    target = u * S;
+    double carry = 0.0;
+    for (int base = 0; base < ntile; base += kThreads) {
+      const int t = base + tid;
+      const double x = t < ntile ? ld_dev(tiles + t) : 0.0;
+      double tot;
+      const double off = carry + block_exclusive_scan(x, sh.lds_d, tot);
+      const int hit = (t < ntile && off <= target && target < off + x) ? t : INT_MAX;
+      const int first = block_min_int(hit, sh.lds_i);
+      if (first != INT_MAX) {
+        if (t == first) {
+          sh.tile = t;
+          sh.off = off;
+        }
+        break;
+      }
+      carry += tot;
+    }
   }
+  __syncthreads();
   if (sh.tile < 0) {   // u * S at or past the last running sum (rounding): last nonzero tile
     int last = -1;
-    for (int t = tid; t < a.ntile; t += kThreads)
+    for (int t = tid; t < ntile; t += kThreads)
       if (ld_dev(tiles + t) > 0.0) last = t;
     last = -block_min_int(-last, sh.lds_i);
     if (tid == 0) {
-      sh.tile = last;
+      sh.tile = max(last, 0);
       double off = 0.0;
       for (int t = 0; t < last; ++t) off += ld_dev(tiles + t);
       sh.off = off;
     }
     __syncthreads();
   }
+  return S;
+}
 
-  // Rescan the tile: the same per-lane fp32 sums, fp64 prefix.
-  const int tsel = max(sh.tile, 0);
+// Rescan the chosen tile: the same weights and per-lane fp32 sums as its tile
+// sum, fp64 prefix.  Writes y, C_{y-1} and C_y (unnormalised) and pi(y)'s
+// weight recomputed with the precise residual.
+template <int DT, bool VEC, int MODE>
+__device__ int rescan_tile(const VerifyArgs& a, int b, int k, const SampleCoef& cf, double target,
+                           RefineLds& sh) {
+  const int tid = threadIdx.x;
+  const int tsel = sh.tile;
   const void *drow, *trow;
   draw_rows<DT>(a, b, k, drow, trow);
   const int64_t j0 = (int64_t)tsel * kTile + (int64_t)tid * kUnit;
+  Raw8<DT, VEC> rd, rt;
+  load_raw<DT, VEC>(trow, j0, a.V, rt);
+  if constexpr (MODE != kModeTarget) load_raw<DT, VEC>(drow, j0, a.V, rd);
   float ld[8], lt[8], w[8], r[8];
-  load_pair<DT, VEC>(mode, drow, trow, j0, a.V, ld, lt);
-  sample_weights<DT>(mode, ld, lt, cf, w, r);
+  unpack<DT, VEC>(rt, lt);
+  if constexpr (MODE != kModeTarget) unpack<DT, VEC>(rd, ld);
+  sample_weights<DT, MODE, false>(ld, lt, cf, w, r);
   float ws = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ws += w[e];
@@ -571,11 +694,13 @@ __device__ void refine_seq(const VerifyArgs& a, int b, RefineLds& sh) {
   int cand = INT_MAX;
   if (off <= tgt && tgt < off + (double)ws) {
     double run = off;
+    bool found = false;
+#pragma unroll
     for (int e = 0; e < 8; ++e) {
       const double nx = run + (double)w[e];
-      if (w[e] > 0.f && tgt < nx) {
+      if (!found && w[e] > 0.f && tgt < nx) {
         cand = (int)(j0 + e);
-        break;
+        found = true;
       }
       run = nx;
     }
@@ -590,13 +715,77 @@ __device__ void refine_seq(const VerifyArgs& a, int b, RefineLds& sh) {
     if (y < 0) y = (int)min<int64_t>(a.V - 1, (int64_t)tsel * kTile + kTile - 1);
   }
   if (y >= j0 && y < j0 + 8) {   // the owner of y reports C_{y-1}, C_y and pi(y)
-    double run = sh.off + off;
-    for (int e = 0; e < (int)(y - j0); ++e) run += (double)w[e];
+    const int idx = (int)(y - j0);
+    double run = sh.off + off, wy = 0.0;
+    float ldy = 0.f, lty = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if (e < idx) run += (double)w[e];
+      if (e == idx) {
+        wy = (double)w[e];
+        ldy = ld[e];
+        lty = lt[e];
+      }
+    }
     sh.lo = run;
-    sh.w = (double)w[y - j0];
-    sh.hi = run + (double)w[y - j0];
+    sh.hi = run + wy;
+    float rr;
+    sh.w = (double)weight_rt<DT, true>(MODE, ldy, lty, cf, rr);
   }
   __syncthreads();
+  return y;
+}
+
+// Locate, rescan and write the outputs (run by the last pass-B item).
+template <int DT, bool VEC>
+__device__ void refine_seq(const VerifyArgs& a, int b, RefineLds& sh) {
+  const int tid = threadIdx.x;
+  const SeqRec rec = load_rec(a.seq + b);
+  if (!rec.valid) return;   // outputs were written by the decision
+  const int g = a.gamma, k = rec.k;
+  const int64_t orow = (int64_t)b * (g + 1);
+  double* tiles = a.tiles + (int64_t)b * a.ntile;
+  const SampleCoef cf = coef_of(a, rec);
+  int mode = rec.mode;
+  if (tid == 0) sh.tile = -1;
+
+  double rtot = 0.0;
+  for (int i = tid; i < a.nt; i += kThreads) rtot += ld_dev(a.itemsum + (int64_t)b * a.nt + i);
+  rtot = block_sum(rtot, sh.lds_d);
+  if (mode == kModeTarget) rtot = 0.0;
+
+  const double u = (double)a.u_smp[orow + k];
+  double target = 0.0;
+  double S = locate_tile(tiles, a.ntile, u, sh, target);
+  while (!(S > 0.0) && mode != kModeTarget) {
+    // A zero Saguaro normaliser falls back to the residual, a zero residual
+    // mass to q_k: recompute every tile sum here (degenerate inputs only).
+    mode = mode == kModeResidual ? kModeTarget : kModeResidual;
+    if (mode == kModeTarget) rtot = 0.0;
+    const void *drow, *trow;
+    draw_rows<DT>(a, b, k, drow, trow);
+    for (int t = 0; t < a.ntile; ++t) {
+      float ws = 0.f;
+#pragma unroll 1
+      for (int e = 0; e < kUnit; ++e) {
+        const int64_t j = (int64_t)t * kTile + (int64_t)tid * kUnit + e;
+        float rr;
+        if (j < a.V)
+          ws += weight_rt<DT, false>(mode, load_one<DT>(drow, j), load_one<DT>(trow, j), cf, rr);
+      }
+      const double tw = block_sum((double)ws, sh.lds_d);
+      if (tid == 0) st_dev(tiles + t, tw);
+    }
+    if (tid == 0) {
+      wait_mem();
+      sh.tile = -1;
+    }
+    __syncthreads();
+    S = locate_tile(tiles, a.ntile, u, sh, target);
+  }
+
+  int y = 0;
+  with_mode(mode, [&](auto m) { y = rescan_tile<DT, VEC, decltype(m)::value>(a, b, k, cf, target, sh); });
 
   if (tid <= g) {
     int tok = -1;
@@ -619,12 +808,10 @@ __device__ void refine_seq(const VerifyArgs& a, int b, RefineLds& sh) {
 // ---------------------------------------------------------------------------
 // Kernels.
 
-template <int DT, bool VEC, int U>
+template <int DT, bool VEC, int U, bool DECIDE>
 __global__ __launch_bounds__(kThreads) void stream_kernel(VerifyArgs a) {
-  __shared__ float lds_f[kWaves];
+  __shared__ float lds_f[2 * kWaves];
   __shared__ double lds_d[kWaves];
-  __shared__ int flag;
-  __shared__ DecideLds dsh;
   const int R = 2 * a.gamma + 1;
   const int64_t id = blockIdx.x;
   const int per_seq = R * a.nc;
@@ -632,7 +819,17 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(VerifyArgs a) {
   const int rem = (int)(id - (int64_t)b * per_seq);
   const int r = rem / a.nc, c = rem - r * a.nc;
   stream_item<DT, VEC, U>(a, b, r, c, lds_f, lds_d);
-  if (arrive(&a.ctr[b].stream_done, (unsigned)per_seq, &flag)) decide_seq<DT>(a, b, dsh);
+  if constexpr (DECIDE) {
+    __shared__ int flag;
+    __shared__ DecideLds dsh;
+    if (arrive(&a.ctr[b].stream_done, (unsigned)per_seq, &flag)) decide_seq<DT>(a, b, dsh);
+  }
+}
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void decide_kernel(VerifyArgs a) {
+  __shared__ DecideLds dsh;
+  decide_seq<DT>(a, blockIdx.x, dsh);
 }
 
 template <int DT, bool VEC>
@@ -654,13 +851,160 @@ __global__ __launch_bounds__(kThreads) void sample_b_kernel(VerifyArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Fused persistent kernel.
+//
+// Items are numbered in steps: step t holds the stream items of sequence t,
+// then the residual-mass items (Saguaro eps > 0) of sequence t - LA, then the
+// sampling items of sequence t - LB.  Work-groups take item numbers in
+// increasing order from a global counter (one item ahead, so the atomic's
+// latency overlaps the current item), so items run nearly in order and a
+// sequence's sampling items start about LB steps after its rows were
+// streamed, re-reading them from the 256 MB last-level cache.  A sampling
+// item waits (bounded spin) for its sequence's decision, which the last of
+// the sequence's stream items makes.  An item waits only on items with
+// smaller numbers, all of them already taken by resident work-groups (the
+// launch is cooperative), so the smallest unfinished item can always run.
+
+struct Sched {
+  int B, NS, NA, NB, LA, LB;
+  int64_t total;
+};
+
+__host__ __device__ inline int64_t sched_offset(const Sched& s, int t) {
+  const int ns = t < s.B ? t : s.B;
+  int na = t - s.LA, nb = t - s.LB;
+  na = na < 0 ? 0 : (na > s.B ? s.B : na);
+  nb = nb < 0 ? 0 : (nb > s.B ? s.B : nb);
+  return (int64_t)ns * s.NS + (int64_t)na * s.NA + (int64_t)nb * s.NB;
+}
+
+enum : int { kItemStream = 0, kItemA = 1, kItemB = 2 };
+
+__device__ __forceinline__ void sched_decode(const Sched& s, int64_t j, int& kind, int& b, int& sub) {
+  int lo = 0, hi = s.B + s.LB;   // offset(lo) <= j < offset(hi) = total
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (sched_offset(s, mid) <= j) lo = mid;
+    else hi = mid;
+  }
+  int64_t w = j - sched_offset(s, lo);
+  if (lo < s.B) {
+    if (w < s.NS) {
+      kind = kItemStream;
+      b = lo;
+      sub = (int)w;
+      return;
+    }
+    w -= s.NS;
+  }
+  const int ba = lo - s.LA;
+  if (s.NA > 0 && ba >= 0 && ba < s.B) {
+    if (w < s.NA) {
+      kind = kItemA;
+      b = ba;
+      sub = (int)w;
+      return;
+    }
+    w -= s.NA;
+  }
+  kind = kItemB;
+  b = lo - s.LB;
+  sub = (int)w;
+}
+
+// Bounded spin until *flag is nonzero (thread 0 polls; the work-group follows).
+// A timeout records an error instead of hanging.
+__device__ __forceinline__ void wait_flag(const VerifyArgs& a, unsigned* flag, int* lds_flag) {
+  if (threadIdx.x == 0) {
+    unsigned polls = 0;
+    while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+      __builtin_amdgcn_s_sleep(2);
+      if (++polls > (1u << 23)) {   // about half a second
+        __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+    }
+    *lds_flag = 0;
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ void set_flag(unsigned* flag) {
+  if (threadIdx.x == 0) {
+    wait_mem();
+    __hip_atomic_store(flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+template <int DT, bool VEC, int U>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(SV_FUSED_WAVES, SV_FUSED_WAVES)))
+void fused_kernel(VerifyArgs a, Sched sc) {
+  __shared__ union {
+    DecideLds d;
+    RefineLds r;
+  } sh;
+  __shared__ float lds_f[2 * kWaves];
+  __shared__ double lds_d[kWaves * (kTilesPerItem + 1)];
+  __shared__ int flag;
+  __shared__ unsigned item;
+  const bool eps_mode = a.saguaro && a.eps > 0.f;
+  const unsigned grabs = (unsigned)sc.total + gridDim.x;   // every work-group over-takes once
+  unsigned ahead = 0;
+  if (threadIdx.x == 0)
+    ahead = __hip_atomic_fetch_add(a.next, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (;;) {
+    if (threadIdx.x == 0) {
+      item = ahead;
+      if (ahead == grabs - 1)   // the last take of the call: leave the counter zeroed
+        __hip_atomic_store(a.next, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else if (ahead < sc.total)
+        ahead = __hip_atomic_fetch_add(a.next, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    const int64_t j = item;
+    if (j >= sc.total) break;
+    int kind, b, sub;
+    sched_decode(sc, j, kind, b, sub);
+    SeqCtr& ctr = a.ctr[b];
+    if (kind == kItemStream) {
+      const int r = sub / a.nc, c = sub - r * a.nc;
+      stream_item<DT, VEC, U>(a, b, r, c, lds_f, lds_d);
+      if (arrive(&ctr.stream_done, (unsigned)sc.NS, &flag)) {
+        decide_seq<DT>(a, b, sh.d);
+        __syncthreads();
+        set_flag(&ctr.decided);
+      }
+    } else if (kind == kItemA) {
+      wait_flag(a, &ctr.decided, &flag);
+      sample_item_a<DT, VEC>(a, b, sub, lds_d);
+      if (arrive(&ctr.a_done, (unsigned)a.nt, &flag)) {
+        finish_a(a, b, lds_d);
+        __syncthreads();
+        set_flag(&ctr.a_ready);
+      }
+    } else {
+      wait_flag(a, eps_mode ? &ctr.a_ready : &ctr.decided, &flag);
+      sample_item_b<DT, VEC>(a, b, sub, lds_d);
+      if (arrive(&ctr.b_done, (unsigned)a.nt, &flag)) {
+        refine_seq<DT, VEC>(a, b, sh.r);
+        if (threadIdx.x == 0) {   // every reader of the flags has passed them
+          __hip_atomic_store(&ctr.decided, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(&ctr.a_ready, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Host side.
 
 static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
   int nc, chunk, ntile, nt;
-  size_t part_off, seq_off, ctr_off, tiles_off, item_off, total;
+  size_t err_off, part_off, seq_off, ctr_off, tiles_off, item_off, total;
 };
 
 static bool sizes_ok(int B, int gamma, int V) {
@@ -669,13 +1013,16 @@ static bool sizes_ok(int B, int gamma, int V) {
 
 static Layout layout(int B, int gamma, int V) {
   Layout L;
-  const int nc0 = (V + kChunk - 1) / kChunk;
-  L.chunk = (int)((((int64_t)V + nc0 - 1) / nc0 + 7) / 8 * 8);   // balanced, a multiple of 8
+  // Chunks are a multiple of the batch stride (SV_STREAM_UNROLL * 2048 logits),
+  // so only a row's last chunk has a partial batch.
+  L.chunk = kChunk;
   L.nc = (int)(((int64_t)V + L.chunk - 1) / L.chunk);
   L.ntile = (V + kTile - 1) / kTile;
   L.nt = (L.ntile + kTilesPerItem - 1) / kTilesPerItem;
   const size_t R = 2 * (size_t)gamma + 1;
   size_t off = 0;
+  L.err_off = off;
+  off += 256;
   L.part_off = off;
   off += align256((size_t)B * R * L.nc * sizeof(Partial));
   L.seq_off = off;
@@ -691,14 +1038,43 @@ static Layout layout(int B, int gamma, int V) {
 }
 
 template <int DT, bool VEC>
-static void launch_all(const VerifyArgs& a, hipStream_t st) {
+static hipError_t launch_all(const VerifyArgs& a, hipStream_t st) {
   const int R = 2 * a.gamma + 1;
+  if (SV_FUSED) {
+    auto kern = fused_kernel<DT, VEC, SV_STREAM_UNROLL>;
+    int dev = 0, ncu = 0, per_cu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess)
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kern),
+                                                       kThreads, 0);
+    if (e != hipSuccess) return e;
+    Sched sc;
+    sc.B = a.B;
+    sc.NS = R * a.nc;
+    sc.NA = (a.saguaro && a.eps > 0.f) ? a.nt : 0;
+    sc.NB = a.nt;
+    const int64_t all = (int64_t)a.B * (sc.NS + sc.NA + sc.NB);
+    const int64_t G = std::max<int64_t>(1, std::min<int64_t>((int64_t)per_cu * ncu, all));
+    const int64_t per_step = sc.NS + sc.NA + sc.NB;
+    const int L = (int)std::max<int64_t>(1, (G * SV_LAG_MILLIROUNDS / 1000 + per_step - 1) / per_step);
+    sc.LA = L;
+    sc.LB = sc.NA > 0 ? 2 * L : L;
+    sc.total = all;
+    VerifyArgs args = a;
+    void* params[] = {&args, &sc};
+    return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kern), dim3((unsigned)G),
+                                      dim3(kThreads), params, 0, st);
+  }
   const unsigned nstream = (unsigned)((int64_t)a.B * R * a.nc);
   const unsigned nsample = (unsigned)((int64_t)a.B * a.nt);
-  hipLaunchKernelGGL((stream_kernel<DT, VEC, 4>), dim3(nstream), dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL((stream_kernel<DT, VEC, SV_STREAM_UNROLL, false>), dim3(nstream), dim3(kThreads),
+                     0, st, a);
+  hipLaunchKernelGGL((decide_kernel<DT>), dim3((unsigned)a.B), dim3(kThreads), 0, st, a);
   if (a.saguaro && a.eps > 0.f)
     hipLaunchKernelGGL((sample_a_kernel<DT, VEC>), dim3(nsample), dim3(kThreads), 0, st, a);
   hipLaunchKernelGGL((sample_b_kernel<DT, VEC>), dim3(nsample), dim3(kThreads), 0, st, a);
+  return hipGetLastError();
 }
 
 static int verify_impl(const void* draft, const void* target, int dtype, const int32_t* tokens,
@@ -718,6 +1094,8 @@ static int verify_impl(const void* draft, const void* target, int dtype, const i
   // Grid limit: at most 2^32 - 1 work-items per launch dimension.
   if ((int64_t)B * (2 * gamma + 1) * L.nc * kThreads > (int64_t)UINT_MAX) return SPEC_EINVAL;
   if ((int64_t)B * L.nt * kThreads > (int64_t)UINT_MAX) return SPEC_EINVAL;
+  // Fused item numbers (plus one extra take per work-group) fit in 32 bits.
+  if ((int64_t)B * ((2 * gamma + 1) * L.nc + 2 * L.nt) > (int64_t)INT_MAX / 2) return SPEC_EINVAL;
   if (!ws || ws_bytes < L.total) return SPEC_EWORKSPACE;
 
   VerifyArgs a;
@@ -735,6 +1113,8 @@ static int verify_impl(const void* draft, const void* target, int dtype, const i
   if (diag) a.diag = *diag;
   else a.diag = spec_diag{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
   char* w = static_cast<char*>(ws);
+  a.err = reinterpret_cast<unsigned*>(w + L.err_off);
+  a.next = reinterpret_cast<unsigned*>(w + L.err_off + 8);
   a.part = reinterpret_cast<Partial*>(w + L.part_off);
   a.seq = reinterpret_cast<SeqRec*>(w + L.seq_off);
   a.ctr = reinterpret_cast<SeqCtr*>(w + L.ctr_off);
@@ -765,14 +1145,10 @@ static int verify_impl(const void* draft, const void* target, int dtype, const i
   const bool vec = (V % 8 == 0) && ((uintptr_t)draft % 16 == 0) && ((uintptr_t)target % 16 == 0);
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  if (dtype == SPEC_BF16) {
-    if (vec) launch_all<kBF16, true>(a, st);
-    else launch_all<kBF16, false>(a, st);
-  } else {
-    if (vec) launch_all<kF32, true>(a, st);
-    else launch_all<kF32, false>(a, st);
-  }
-  return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ELAUNCH;
+  hipError_t e;
+  if (dtype == SPEC_BF16) e = vec ? launch_all<kBF16, true>(a, st) : launch_all<kBF16, false>(a, st);
+  else e = vec ? launch_all<kF32, true>(a, st) : launch_all<kF32, false>(a, st);
+  return e == hipSuccess ? SPEC_OK : SPEC_ELAUNCH;
 }
 
 }  // namespace sv

@@ -62,13 +62,17 @@ def to_device(batch: W.Batch, dev="cuda") -> DeviceBatch:
 
 def run_gpu(batch: W.Batch, mode="residual", eps=0.0, diag=True, db: DeviceBatch | None = None):
     db = db or to_device(batch)
+    dt = R.SPEC_BF16 if batch.dtype == "bf16" else R.SPEC_F32
+    ws = R.new_workspace(R.spec_workspace_bytes(batch.B, batch.gamma, batch.V, dt), db.draft.device)
     if mode == "residual":
         out = R.spec_verify(db.draft, db.target, db.tokens, db.u_accept, db.u_sample, batch.T,
-                            in_len=db.in_len, diag=diag)
+                            in_len=db.in_len, diag=diag, workspace=ws)
     else:
         out = R.spec_verify_saguaro(db.draft, db.target, db.tokens, db.u_accept, db.u_sample,
-                                    batch.T, in_len=db.in_len, diag=diag, eps=eps)
+                                    batch.T, in_len=db.in_len, diag=diag, eps=eps, workspace=ws)
     torch.cuda.synchronize()
+    # The workspace's first word records a timed-out wait; it must stay zero.
+    assert batch.B == 0 or int(ws[:4].view(torch.int32).item()) == 0, "bounded wait timed out"
     host = {
         "tokens": out.tokens.cpu().numpy(), "accepted": out.accepted.cpu().numpy(),
         "first_reject": out.first_reject.cpu().numpy(),
