@@ -27,8 +27,9 @@
  *     as void* (NULL = the default stream).  Calls only enqueue work on that
  *     stream and return; nothing is synchronised.
  *   - The caller owns every buffer.  The library never allocates or frees
- *     device memory and keeps no global state; concurrent calls need distinct
- *     workspaces.
+ *     device memory; its only global state is a per-device cache of how many
+ *     work-groups the GPU holds at once (queried on the first call).
+ *     Concurrent calls need distinct workspaces.
  *   - Logits are row-major [B][gamma+1][V], contiguous, float32 (SPEC_F32) or
  *     bfloat16 (SPEC_BF16).  Row i of sequence b starts at element
  *     (b*(gamma+1)+i)*V.  The verification reads draft rows 0..gamma-1 and
@@ -90,7 +91,11 @@ typedef struct spec_diag {
  * sizes (0 when B == 0).  Returns 0 for arguments spec_verify would reject.
  * The workspace must be zero-filled before its first use; each call that
  * completes leaves it ready for the next one, so a workspace is allocated and
- * cleared once and then reused by calls on one stream.
+ * cleared once and then reused by calls on one stream.  Its first 32-bit word
+ * is an error flag: the kernels hand partial results between work-groups
+ * through the workspace and wait for them with bounded polls; a poll that
+ * times out (never expected) sets the word to 1 and the call's outputs are
+ * then unreliable.  After that, zero the whole workspace before reusing it.
  */
 size_t spec_workspace_bytes(int B, int gamma, int V, int dtype);
 

@@ -70,11 +70,31 @@ struct Raw8<kBF16, true> {
   uint4 w;
 };
 
-template <int DT, bool VEC>
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// NT: a nontemporal load (data read once: streamed through the caches
+// without being kept; reads noticeably faster from HBM on gfx950).
+template <int DT, bool VEC, bool NT = false>
 __device__ __forceinline__ void load_raw(const void* row, int64_t j0, int64_t n, Raw8<DT, VEC>& r) {
   if constexpr (DT == kBF16 && VEC) {
-    if (j0 < n) r.w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(row) + j0);
-    else r.w = make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u);   // -inf
+    if (j0 < n) {
+      const u32x4* p = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(row) + j0);
+      const u32x4 t = NT ? __builtin_nontemporal_load(p) : *p;
+      r.w = make_uint4(t.x, t.y, t.z, t.w);
+    } else {
+      r.w = make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u);   // -inf
+    }
+  } else if constexpr (DT == kF32 && VEC && NT) {
+    if (j0 < n) {
+      const f32x4* p = reinterpret_cast<const f32x4*>(static_cast<const float*>(row) + j0);
+      const f32x4 a = __builtin_nontemporal_load(p), b = __builtin_nontemporal_load(p + 1);
+      r.v[0] = a.x; r.v[1] = a.y; r.v[2] = a.z; r.v[3] = a.w;
+      r.v[4] = b.x; r.v[5] = b.y; r.v[6] = b.z; r.v[7] = b.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) r.v[e] = -INFINITY;
+    }
   } else {
     if (j0 < n) {
       load8<DT, VEC>(row, j0, n, r.v);
@@ -96,6 +116,21 @@ __device__ __forceinline__ void unpack(const Raw8<DT, VEC>& r, float (&v)[8]) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = r.v[e];
   }
+}
+
+// A value equal in every lane, moved to a scalar register (frees vector
+// registers on long paths).
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ float uni(float x) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+}
+__device__ __forceinline__ uint64_t uni(uint64_t x) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)x);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(x >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ double uni(double x) {
+  return __longlong_as_double((long long)uni((uint64_t)__double_as_longlong(x)));
 }
 
 // Hardware base-2 exponential (v_exp_f32).

@@ -8,24 +8,38 @@
 // (section 3.2: proportional to sqrt(p_D * p_residual)).
 //
 // Work items (each one 256-thread work-group's job):
-//   stream item (b, r, c): stream chunk c of row r of sequence b once from
-//     HBM and reduce it to a piece of the tempered-softmax normaliser,
-//     (mc, s) with s = sum_j 2^(l_j * c_T - mc), c_T = log2(e) / T.  c_T is
-//     an unevaluated float pair (two FMAs per logit) so the temperature is
-//     exact; mc is an integer, so rescaling a sum is an exact ldexp.  Each
-//     batch of a lane's logits is tree-summed in fp32 and accumulated in fp64.
-//     The last item of a sequence to finish (arrival counter) merges the
-//     pieces in fp64, runs the accept test at every draft position (fp64,
-//     wave ballot -> first rejection k) and writes the sequence's decision.
-//   sample item (b, s): per-tile (2048-logit) sums of the sampling weights
-//     over its tiles of row pair k (or target row gamma).  The last item of a
-//     sequence locates the tile holding u * total (fp64 scan over the tile
-//     sums), rescans that tile (fp64 prefix over the same per-lane fp32 sums)
-//     and writes the outputs.  Saguaro with eps > 0 runs one more set of
-//     items first to get the residual mass the clamp is relative to.
+//   stream (b, r, c): stream chunk c of row r of sequence b once from HBM and
+//     reduce it to a piece of the row's tempered-softmax log-normaliser,
+//     v = log2 sum_j 2^(l_j c_T), c_T = log2(e) / T.  c_T is an unevaluated
+//     float pair (two FMAs per logit) so the temperature is exact; each lane
+//     keeps an integer offset, so every rescale is an exact ldexp, tree-sums
+//     each batch of its logits in fp32 and accumulates in fp64.
+//   decide (b): merge the pieces of every row (fp64), run the accept test at
+//     every draft position (fp64, wave ballot -> first rejection k) and write
+//     the sequence's decision record.
+//   residual mass (b, s), Saguaro with eps > 0 only: the residual weight sum
+//     over a few 2048-logit tiles of row pair k, which the eps clamp needs.
+//   sample (b, s): per-tile sums of the sampling weights over a few tiles of
+//     row pair k (or target row gamma after a full acceptance).
+//   refine (b): locate the tile holding u * total (fp64 scan over the tile
+//     sums, token order), rescan it (fp64 prefix over the same per-lane fp32
+//     sums) and write the outputs.
 //
-// Workspace counters are zero between calls; the last arriver of each phase
-// resets its counter.
+// Hand-off between work-groups uses 64-bit slots that are 0 when empty: a
+// producer stores ~bits(value) with one device-coherent store, a consumer
+// polls (bounded) until the slot is nonzero and clears it after use, so the
+// workspace is all zero again when a call ends (decision records aside).
+// No item waits for anything but items of the same sequence that come
+// earlier in the launch order.
+//
+// Default launch: one kernel whose blocks run the items in steps, step t
+// holding the stream items of sequence t, then the decision of sequence
+// t - LD, the sampling items of t - LB and the refine item of t - LR.  A
+// sequence's later items thus start while other sequences stream, and its
+// re-read of row pair k comes from the 256 MB last-level cache.  Work-groups
+// are dispatched in block order, so the smallest unfinished block has every
+// item it waits for finished and can always run; a wait that still times out
+// sets the error word and gives up instead of hanging.
 #include "common.h"
 #include "spec_verify.h"
 
@@ -36,29 +50,6 @@
 
 namespace sv {
 
-// One (row, chunk) piece of a row's normaliser: s = sum 2^(l*c_T - mc), mc an
-// integer (log2 units); mraw = the chunk's largest raw logit.
-struct Partial {
-  float mc;
-  float mraw;
-  double s;
-};
-
-__device__ __forceinline__ void store_partial(Partial* p, float mc, float mraw, double s) {
-  const uint64_t w = (uint64_t)__float_as_uint(mc) | ((uint64_t)__float_as_uint(mraw) << 32);
-  st_dev_u64(reinterpret_cast<uint64_t*>(p), w);
-  st_dev(&p->s, s);
-}
-
-__device__ __forceinline__ Partial load_partial(const Partial* p) {
-  const uint64_t w = ld_dev_u64(reinterpret_cast<const uint64_t*>(p));
-  Partial r;
-  r.mc = __uint_as_float((uint32_t)w);
-  r.mraw = __uint_as_float((uint32_t)(w >> 32));
-  r.s = ld_dev(&p->s);
-  return r;
-}
-
 enum : int { kModeTarget = 0, kModeResidual = 1, kModeSaguaro = 2, kModeSaguaroEps = 3 };
 
 #ifndef SV_TILES_PER_ITEM
@@ -67,69 +58,88 @@ enum : int { kModeTarget = 0, kModeResidual = 1, kModeSaguaro = 2, kModeSaguaroE
 #ifndef SV_STREAM_UNROLL
 #define SV_STREAM_UNROLL 4
 #endif
-// 1: one persistent cooperative kernel runs every phase (the default);
-// 0: separate stream, decision and sampling kernels.
+// 1: every item in one kernel (the default); 0: one kernel per item kind.
 #ifndef SV_FUSED
-#define SV_FUSED 0
+#define SV_FUSED 1
 #endif
-// Sampling items of a sequence run this many rounds of the persistent grid
-// after its stream items (x1000).
-// Waves per SIMD the fused kernel is compiled for (registers are capped to
-// fit; the rare decision and refine paths may spill).
-#ifndef SV_FUSED_WAVES
-#define SV_FUSED_WAVES 8
+// Lags of the decision, residual-mass, sampling and refine items behind their
+// sequence's stream items, in thousandths of a round (one round = as many
+// stream items as the GPU holds at once); each is added to the one before.
+#ifndef SV_LAG_DECIDE
+#define SV_LAG_DECIDE 1400
 #endif
-#ifndef SV_LAG_MILLIROUNDS
-#define SV_LAG_MILLIROUNDS 1500
+#ifndef SV_LAG_MASS
+#define SV_LAG_MASS 1000
+#endif
+#ifndef SV_LAG_SAMPLE
+#define SV_LAG_SAMPLE 1000
+#endif
+#ifndef SV_LAG_REFINE
+#define SV_LAG_REFINE 800
+#endif
+// 1: the stream loop keeps the next batch's loads in flight (two buffers).
+#ifndef SV_PIPE
+#define SV_PIPE 0
+#endif
+#ifndef SV_SAMPLE_NT
+#define SV_SAMPLE_NT 0
 #endif
 constexpr int kTilesPerItem = SV_TILES_PER_ITEM;
+constexpr bool kSampleNT = SV_SAMPLE_NT != 0;   // nontemporal loads in the sampling items
 static_assert(kChunk % (SV_STREAM_UNROLL * kThreads * kUnit) == 0,
               "a stream chunk must hold whole batches");
+constexpr unsigned kMaxPolls = 1u << 22;   // bounded waits: about a quarter of a second
 
-// A sequence's decision, written by its last stream item.
+// ---------------------------------------------------------------------------
+// Slots.
+
+__device__ __forceinline__ uint64_t slot_word(double x) {
+  uint64_t b = (uint64_t)__double_as_longlong(x);
+  if (b == ~0ull) b = 0x7FF8000000000000ull;   // keep the empty word 0 unreachable
+  return ~b;
+}
+__device__ __forceinline__ double slot_value(uint64_t w) { return __longlong_as_double((long long)~w); }
+__device__ __forceinline__ void slot_put(uint64_t* p, double x) { st_dev_u64(p, slot_word(x)); }
+__device__ __forceinline__ void slot_clear(uint64_t* p) { st_dev_u64(p, 0ull); }
+__device__ __forceinline__ void slot_put32(unsigned* p, float x) {
+  uint32_t b = __float_as_uint(x);
+  if (b == ~0u) b = 0x7FC00000u;
+  __hip_atomic_store(p, ~b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void slot_clear32(unsigned* p) {
+  __hip_atomic_store(p, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// A sequence's decision, written by its decision item before its flag.
 struct SeqRec {
   uint64_t mask;
   int k;
   int valid;
   int mode;         // weights of the draw
-  float Mt;         // offset of the row drawn from (target row k)
+  float Mt;         // integer offset of the row drawn from (target row k)
   float K_hi, K_lo; // log2(p_j/q_j) = (ld_j - lt_j) * c_T + K
-  float epsS;       // eps * sum of residual weights (Saguaro eps > 0)
-  float pad0;
-  double Zt;        // normaliser of target row k (offset Mt)
-  double pad1;
+  double Zt;        // sum_j 2^(lt_j c_T - Mt) over target row k
 };
-
 static_assert(sizeof(SeqRec) % 8 == 0, "SeqRec is moved as 64-bit words");
 constexpr int kRecWords = sizeof(SeqRec) / 8;
 
-// A decision record written and read with device-coherent 64-bit accesses.
 __device__ __forceinline__ void store_rec(SeqRec* p, const SeqRec& r) {
   const uint64_t* w = reinterpret_cast<const uint64_t*>(&r);
 #pragma unroll
   for (int i = 0; i < kRecWords; ++i) st_dev_u64(reinterpret_cast<uint64_t*>(p) + i, w[i]);
 }
+// Read by every thread of a work-group; the fields are kept in scalar registers.
 __device__ __forceinline__ SeqRec load_rec(const SeqRec* p) {
   SeqRec r;
   uint64_t* w = reinterpret_cast<uint64_t*>(&r);
 #pragma unroll
-  for (int i = 0; i < kRecWords; ++i) w[i] = ld_dev_u64(reinterpret_cast<const uint64_t*>(p) + i);
+  for (int i = 0; i < kRecWords; ++i) w[i] = uni(ld_dev_u64(reinterpret_cast<const uint64_t*>(p) + i));
   return r;
 }
-// epsS and pad0 share the fifth word.
-__device__ __forceinline__ void store_rec_eps(SeqRec* p, float epsS) {
-  st_dev_u64(reinterpret_cast<uint64_t*>(p) + 4, (uint64_t)__float_as_uint(epsS));
-}
 
-// Arrival counters and ready flags of one sequence, one 128-byte line each.
-struct SeqCtr {
-  unsigned stream_done;  // stream items finished
-  unsigned a_done;       // residual-mass items finished (Saguaro eps > 0)
-  unsigned b_done;       // sampling items finished
-  unsigned decided;      // 1 once the decision record is written
-  unsigned a_ready;      // 1 once eps * residual mass is written
-  unsigned pad[27];
-};
+// One 128-byte line per sequence: [0] = 1 once the decision record is
+// written; [1] = residual-mass and sampling items past their wait for it.
+constexpr int kFlagStride = 32;
 
 struct VerifyArgs {
   const void* draft;
@@ -144,16 +154,17 @@ struct VerifyArgs {
   uint64_t* out_mask;
   int32_t* out_len;
   spec_diag diag;
-  unsigned* err;     // nonzero if a bounded wait timed out (co-residency lost)
-  unsigned* next;    // item counter of the fused kernel (zero between calls)
-  Partial* part;     // [B][2*gamma+1][nc]
+  unsigned* err;     // nonzero once a bounded wait timed out
+  uint64_t* part;    // [B][2*gamma+1][nc] slots: chunk log2-normalisers
+  unsigned* mraw;    // [B][2*gamma+1][nc] 32-bit slots: chunk maxima of the raw logits
   SeqRec* seq;       // [B]
-  SeqCtr* ctr;       // [B]
-  double* tiles;     // [B][ntile] tile sums of the sampling weights
-  double* itemsum;   // [B][nt] residual-weight sum of each sample item
+  unsigned* flag;    // [B * kFlagStride]: decision flag and pass count
+  uint64_t* tiles;   // [B][ntile] slots: tile sums of the sampling weights
+  uint64_t* mass;    // [B][nt] slots: residual sums of the residual-mass items (eps > 0)
+  uint64_t* rsum;    // [B][nt] slots: residual sums of the sampling items (Saguaro)
   int B, gamma, V;
   int nc, chunk;     // stream chunks per row and their length
-  int ntile, nt;     // sampling tiles per row; sample items per sequence
+  int ntile, nt;     // sampling tiles per row; sampling items per sequence
   float c_hi, c_lo;  // log2(e) / T as an unevaluated float pair, c_lo > 0
   double cTd;        // c_hi + c_lo
   double invT;
@@ -171,26 +182,44 @@ __device__ __forceinline__ const void* row_ptr(const VerifyArgs& a, int b, int r
   return base + idx * a.V * es;
 }
 
-// Thread 0 (which wrote this work-group's payload with device-coherent
-// stores) waits for them to complete and counts the arrival.  Returns true in
-// every thread of the work-group that completes the count; that work-group
-// reads the other arrivers' payloads with device-coherent loads.
-__device__ __forceinline__ bool arrive(unsigned* counter, unsigned total, int* lds_flag) {
-  __syncthreads();
+// Bounded polls.  A timeout (or an error already recorded by another
+// work-group) records the error and returns whatever the word holds.
+__device__ __forceinline__ bool give_up(const VerifyArgs& a, unsigned& polls) {
+  ++polls;
+  if ((polls & 63u) == 0u &&
+      (polls > kMaxPolls || __hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))) {
+    __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return true;
+  }
+  __builtin_amdgcn_s_sleep(2);
+  return false;
+}
+__device__ __forceinline__ uint64_t poll(const VerifyArgs& a, const uint64_t* p) {
+  uint64_t w = ld_dev_u64(p);
+  unsigned polls = 0;
+  while (w == 0ull && !give_up(a, polls)) w = ld_dev_u64(p);
+  return w;
+}
+__device__ __forceinline__ unsigned poll32(const VerifyArgs& a, const unsigned* p) {
+  unsigned w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  unsigned polls = 0;
+  while (w == 0u && !give_up(a, polls)) w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return w;
+}
+// Thread 0 waits for the sequence's decision flag (COUNT: and counts this
+// item as past it); the work-group follows.
+template <bool COUNT>
+__device__ __forceinline__ void wait_decided(const VerifyArgs& a, int b) {
   if (threadIdx.x == 0) {
-    wait_mem();
-    const unsigned old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int last = (old == total - 1);
-    if (last)   // nobody else touches it again in this call
-      __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *lds_flag = last;
+    unsigned* f = a.flag + (int64_t)b * kFlagStride;
+    (void)poll32(a, f);
+    if (COUNT) __hip_atomic_fetch_add(f + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
-  return *lds_flag != 0;
 }
 
 // ---------------------------------------------------------------------------
-// Stream item: one chunk of one row -> Partial.
+// Stream item: one chunk of one row -> its log2-normaliser piece.
 
 // One batch of N units (8 logits each) of a lane: raise the lane's integer
 // offset if the batch holds a larger logit (rescaling the running sum by an
@@ -221,9 +250,13 @@ __device__ __forceinline__ void stream_batch(const Raw8<DT, VEC> (&raw)[N], floa
   s += (double)v[0];
 }
 
+struct StreamLds {
+  float f[2 * kWaves];
+  double d[kWaves];
+};
+
 template <int DT, bool VEC, int U>
-__device__ __forceinline__ void stream_item(const VerifyArgs& a, int b, int r, int c, float* lds_f,
-                                            double* lds_d) {
+__device__ __forceinline__ void stream_item(const VerifyArgs& a, int b, int r, int c, StreamLds& sh) {
   const void* row = row_ptr<DT>(a, b, r);
   const int64_t begin = (int64_t)c * a.chunk;
   const int64_t end = min<int64_t>(begin + a.chunk, a.V);
@@ -234,41 +267,73 @@ __device__ __forceinline__ void stream_item(const VerifyArgs& a, int b, int r, i
   double s = 0.0;
   constexpr int64_t kStep = (int64_t)kThreads * kUnit;
   int64_t j = begin + (int64_t)threadIdx.x * kUnit;
+  constexpr int64_t kBatch = U * kStep;
+#if SV_PIPE
+  // Full batches (the same count in every lane), two buffers: the loads of
+  // the next batch are in flight while this one is reduced.
+  const int nb = (int)((end - begin) / kBatch);
+  if (nb > 0) {
+    Raw8<DT, VEC> A[U], Bf[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) load_raw<DT, VEC, true>(row, j + u * kStep, end, A[u]);
+    for (int i = 0;; i += 2) {
+      if (i + 1 < nb) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) load_raw<DT, VEC, true>(row, j + kBatch + u * kStep, end, Bf[u]);
+      }
+      stream_batch<DT, VEC, U>(A, ch, cl, mref, mraw, s);
+      j += kBatch;
+      if (i + 1 >= nb) break;
+      if (i + 2 < nb) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) load_raw<DT, VEC, true>(row, j + kBatch + u * kStep, end, A[u]);
+      }
+      stream_batch<DT, VEC, U>(Bf, ch, cl, mref, mraw, s);
+      j += kBatch;
+      if (i + 2 >= nb) break;
+    }
+  }
+#else
   // Full batches: U units, all in range, loads issued back to back.
-  for (; j + (U - 1) * kStep + kUnit <= end; j += U * kStep) {
+  for (; j + (U - 1) * kStep + kUnit <= end; j += kBatch) {
     Raw8<DT, VEC> raw[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) load_raw<DT, VEC>(row, j + u * kStep, end, raw[u]);
+    for (int u = 0; u < U; ++u) load_raw<DT, VEC, true>(row, j + u * kStep, end, raw[u]);
     stream_batch<DT, VEC, U>(raw, ch, cl, mref, mraw, s);
   }
+#endif
   // Remaining units of this lane (fewer than U; the last may be partial).
   for (; j < end; j += kStep) {
     Raw8<DT, VEC> raw[1];
-    load_raw<DT, VEC>(row, j, end, raw[0]);
+    load_raw<DT, VEC, true>(row, j, end, raw[0]);
     stream_batch<DT, VEC, 1>(raw, ch, cl, mref, mraw, s);
   }
-  // Merge the lanes: wave shuffles, then one barrier; thread 0 stores the piece.
+  // Merge the lanes: wave shuffles, then one barrier; thread 0 publishes.
   const float wm = wave_max(mref);
   const float wr = wave_max(mraw);
   double sd = (s != 0.0) ? ldexp(s, (int)fmaxf(mref - wm, -2000.f)) : 0.0;
   sd = wave_sum(sd);
   const int wave = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) {
-    lds_f[wave] = wm;
-    lds_f[kWaves + wave] = wr;
-    lds_d[wave] = sd;
+    sh.f[wave] = wm;
+    sh.f[kWaves + wave] = wr;
+    sh.d[wave] = sd;
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    float mb = lds_f[0], mr = lds_f[kWaves];
+    float mb = sh.f[0], mr = sh.f[kWaves];
     for (int i = 1; i < kWaves; ++i) {
-      mb = fmaxf(mb, lds_f[i]);
-      mr = fmaxf(mr, lds_f[kWaves + i]);
+      mb = fmaxf(mb, sh.f[i]);
+      mr = fmaxf(mr, sh.f[kWaves + i]);
     }
     double sb = 0.0;
     for (int i = 0; i < kWaves; ++i)
-      if (lds_d[i] != 0.0) sb += ldexp(lds_d[i], (int)fmaxf(lds_f[i] - mb, -2000.f));
-    store_partial(a.part + ((int64_t)b * (2 * a.gamma + 1) + r) * a.nc + c, mb, mr, sb);
+      if (sh.d[i] != 0.0) sb += ldexp(sh.d[i], (int)fmaxf(sh.f[i] - mb, -2000.f));
+    // log2 of the chunk's normaliser; -inf for an all -inf chunk.
+    const double v = sb > 0.0 ? (double)mb + log2(sb) : (sb == 0.0 ? -INFINITY : sb);
+    const int64_t idx = ((int64_t)b * (2 * a.gamma + 1) + r) * a.nc + c;
+    slot_put32(a.mraw + idx, mr);
+    slot_put(a.part + idx, v);
   }
 }
 
@@ -276,69 +341,67 @@ __device__ __forceinline__ void stream_item(const VerifyArgs& a, int b, int r, i
 // Decision of one sequence.
 
 struct DecideLds {
-  float M[128];
-  double Z[128];
+  double M[128];   // row offsets (integers, log2 units)
+  double Z[128];   // row normalisers: sum_j 2^(l_j c_T - M)
   int bad[128];
   uint64_t mask;
   int k, valid;
 };
 
 // Merge the chunk pieces of every row (16 lanes per row, 16 rows per pass;
-// fp64), then run the accept test at every draft position (wave 0, lane i =
-// position i; fp64) and record the sequence's decision.
+// fp64): Z = sum_c 2^(v_c - M), M = the integer ceiling of max_c v_c.  Then the accept test
+// at every draft position (wave 0, lane i = position i; fp64), the decision
+// record and its flag.  Every piece slot is cleared once read.
 template <int DT>
-__device__ void decide_seq(const VerifyArgs& a, int b, DecideLds& sh) {
+__device__ void decide_item(const VerifyArgs& a, int b, DecideLds& sh) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = a.gamma, R = 2 * g + 1;
-  const double cTd = a.cTd;
-  const Partial* P0 = a.part + (int64_t)b * R * a.nc;
+  const int64_t base = (int64_t)b * R * a.nc;
   const int sub = lane & 15;
   for (int r0 = 0; r0 < R; r0 += 16) {
     const int r = r0 + wave * 4 + (lane >> 4);
-    float M = kNegSentinel, mr = -INFINITY;
-    double z = 0.0;
+    double M = -INFINITY, z = 0.0;
+    float mr = -INFINITY;
     if (r < R) {
-      const Partial* P = P0 + (int64_t)r * a.nc;
-      if (a.nc <= 16) {   // one piece per lane, kept in registers
-        const Partial p = sub < a.nc ? load_partial(P + sub) : Partial{kNegSentinel, -INFINITY, 0.0};
-        M = p.mc;
-        mr = p.mraw;
+      // Pieces c = sub, sub + 16, ...: wait for each, take the maximum; the
+      // first stays in a register, later ones are read again for the sum.
+      const int64_t p0 = base + (int64_t)r * a.nc;
+      double v0 = -INFINITY;
+      for (int c = sub; c < a.nc; c += 16) {
+        const double v = slot_value(poll(a, a.part + p0 + c));
+        mr = fmaxf(mr, __uint_as_float(~poll32(a, a.mraw + p0 + c)));
+        if (c == sub) v0 = v;
+        M = fmax(M, v);
+      }
 #pragma unroll
-        for (int o = 8; o > 0; o >>= 1) {
-          M = fmaxf(M, __shfl_xor(M, o, 16));
-          mr = fmaxf(mr, __shfl_xor(mr, o, 16));
-        }
-        if (p.s != 0.0) z = ldexp(p.s, (int)fmaxf(p.mc - M, -2000.f));
-      } else {
-        for (int c = sub; c < a.nc; c += 16) {
-          const Partial p = load_partial(P + c);
-          M = fmaxf(M, p.mc);
-          mr = fmaxf(mr, p.mraw);
-        }
-#pragma unroll
-        for (int o = 8; o > 0; o >>= 1) {
-          M = fmaxf(M, __shfl_xor(M, o, 16));
-          mr = fmaxf(mr, __shfl_xor(mr, o, 16));
-        }
-        for (int c = sub; c < a.nc; c += 16) {
-          const Partial p = load_partial(P + c);
-          if (p.s != 0.0) z += ldexp(p.s, (int)fmaxf(p.mc - M, -2000.f));
-        }
+      for (int o = 8; o > 0; o >>= 1) {
+        M = fmax(M, __shfl_xor(M, o, 16));
+        mr = fmaxf(mr, __shfl_xor(mr, o, 16));
+      }
+      M = ceil(M);
+      for (int c = sub; c < a.nc; c += 16) {
+        const double v = c == sub ? v0 : slot_value(ld_dev_u64(a.part + p0 + c));
+        if (v != -INFINITY) z += exp2(v - M);   // a NaN piece stays NaN
+        slot_clear(a.part + p0 + c);
+        slot_clear32(a.mraw + p0 + c);
       }
     }
 #pragma unroll
     for (int o = 8; o > 0; o >>= 1) z += __shfl_xor(z, o, 16);
     if (r < R && sub == 0) {
+      // An all -inf row (M = -inf), a +inf logit (M = +inf) or a NaN logit
+      // (z = NaN) is bad.
       const int ok = (z > 0.0) && isfinite(z) && isfinite(M);
       sh.M[r] = M;
       sh.Z[r] = z;
       sh.bad[r] = !ok;
       if (ok && a.diag.row_max) a.diag.row_max[(int64_t)b * R + r] = (double)mr * a.invT;
-      if (ok && a.diag.row_logZ)
-        a.diag.row_logZ[(int64_t)b * R + r] = (double)M * 0.69314718055994530942 + log(z);
     }
   }
   __syncthreads();
+  if (a.diag.row_logZ)
+    for (int r = tid; r < R; r += kThreads)
+      if (!sh.bad[r]) a.diag.row_logZ[(int64_t)b * R + r] = sh.M[r] * 0.69314718055994530942 + log(sh.Z[r]);
 
   if (wave == 0) {
     int rows_bad = 0;
@@ -351,8 +414,8 @@ __device__ void decide_seq(const VerifyArgs& a, int b, DecideLds& sh) {
       if (!bad && !rows_bad) {
         const float ld = load_one<DT>(row_ptr<DT>(a, b, lane), x);
         const float lt = load_one<DT>(row_ptr<DT>(a, b, g + lane), x);
-        const double px = exp2((double)ld * cTd - (double)sh.M[lane]) / sh.Z[lane];
-        const double qx = exp2((double)lt * cTd - (double)sh.M[g + lane]) / sh.Z[g + lane];
+        const double px = exp2((double)ld * a.cTd - sh.M[lane]) / sh.Z[lane];
+        const double qx = exp2((double)lt * a.cTd - sh.M[g + lane]) / sh.Z[g + lane];
         double ratio;
         if (px > 0.0) ratio = fmin(1.0, qx / px);
         else ratio = qx > 0.0 ? 1.0 : 0.0;
@@ -389,15 +452,20 @@ __device__ void decide_seq(const VerifyArgs& a, int b, DecideLds& sh) {
     rec.valid = sh.valid;
     rec.mode = k == g ? kModeTarget
                       : (!a.saguaro ? kModeResidual : (a.eps > 0.f ? kModeSaguaroEps : kModeSaguaro));
-    rec.Mt = sh.M[g + k];
-    const double K = k < g ? ((double)sh.M[g + k] - (double)sh.M[k]) + log2(sh.Z[g + k] / sh.Z[k]) : 0.0;
-    rec.K_hi = (float)K;
-    rec.K_lo = (float)(K - (double)rec.K_hi);
-    rec.epsS = 0.f;
-    rec.pad0 = 0.f;
-    rec.Zt = sh.Z[g + k];
-    rec.pad1 = 0.0;
+    rec.Mt = 0.f;
+    rec.K_hi = rec.K_lo = 0.f;
+    rec.Zt = 1.0;
+    if (sh.valid) {
+      const double Mt = sh.M[g + k];
+      rec.Mt = (float)Mt;   // exact below 2^24; otherwise Zt absorbs the rounding
+      rec.Zt = ldexp(sh.Z[g + k], (int)fmin(fmax(Mt - (double)rec.Mt, -2000.0), 2000.0));
+      const double K = k < g ? (Mt - sh.M[k]) + log2(sh.Z[g + k] / sh.Z[k]) : 0.0;
+      rec.K_hi = (float)K;
+      rec.K_lo = (float)(K - (double)rec.K_hi);
+    }
     store_rec(a.seq + b, rec);
+    wait_mem();
+    __hip_atomic_store(a.flag + (int64_t)b * kFlagStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -408,14 +476,14 @@ struct SampleCoef {
   float c_hi, c_lo, Mt, K_hi, K_lo, epsS;
 };
 
-__device__ __forceinline__ SampleCoef coef_of(const VerifyArgs& a, const SeqRec& rec) {
+__device__ __forceinline__ SampleCoef coef_of(const VerifyArgs& a, const SeqRec& rec, float epsS) {
   SampleCoef c;
   c.c_hi = a.c_hi;
   c.c_lo = a.c_lo;
   c.Mt = rec.Mt;
   c.K_hi = rec.K_hi;
   c.K_lo = rec.K_lo;
-  c.epsS = rec.epsS;
+  c.epsS = epsS;
   return c;
 }
 
@@ -486,17 +554,6 @@ __device__ __forceinline__ void sample_weights(const float (&ld)[8], const float
   for (int e = 0; e < 8; ++e) w[e] = weight_one<DT, MODE, PRECISE>(ld[e], lt[e], c, r[e]);
 }
 
-// Mode chosen at run time (scalar paths: pi(y), degenerate fallbacks).
-template <int DT, bool PRECISE>
-__device__ __noinline__ float weight_rt(int mode, float ld, float lt, const SampleCoef& c, float& r) {
-  switch (mode) {
-    case kModeTarget: return weight_one<DT, kModeTarget, PRECISE>(ld, lt, c, r);
-    case kModeResidual: return weight_one<DT, kModeResidual, PRECISE>(ld, lt, c, r);
-    case kModeSaguaro: return weight_one<DT, kModeSaguaro, PRECISE>(ld, lt, c, r);
-    default: return weight_one<DT, kModeSaguaroEps, PRECISE>(ld, lt, c, r);
-  }
-}
-
 // Call f with the weight mode as a compile-time constant.
 template <class F>
 __device__ __forceinline__ void with_mode(int mode, F&& f) {
@@ -508,18 +565,6 @@ __device__ __forceinline__ void with_mode(int mode, F&& f) {
   }
 }
 
-template <int DT, bool VEC, int MODE>
-__device__ __forceinline__ void load_pair(const void* drow, const void* trow, int64_t j0, int64_t V,
-                                          float (&ld)[8], float (&lt)[8]) {
-  if (j0 < V) {
-    load8<DT, VEC>(trow, j0, V, lt);
-    if constexpr (MODE != kModeTarget) load8<DT, VEC>(drow, j0, V, ld);
-  } else {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) lt[e] = ld[e] = -INFINITY;
-  }
-}
-
 // Rows of the draw: target row k and (on a rejection) draft row k.
 template <int DT>
 __device__ __forceinline__ void draw_rows(const VerifyArgs& a, int b, int k, const void*& drow,
@@ -528,95 +573,116 @@ __device__ __forceinline__ void draw_rows(const VerifyArgs& a, int b, int k, con
   trow = row_ptr<DT>(a, b, a.gamma + k);
 }
 
-// Tile sums of the weights over tiles [t0, t0 + kTilesPerItem) (clipped to
-// ntile): tw[i] (fp64, identical in every thread) and, last, the residual total.
-template <int DT, bool VEC, int MODE>
+// Tile sums of the weights over tiles [t0, t0 + N) (clipped to ntile): tw[i]
+// (fp64, identical in every thread) and, last, the residual total.  The loads
+// of G tiles are in flight together (all N for packed bf16 rows, whose raw
+// words take half the registers of floats).
+template <int DT, bool VEC, int MODE, int N = kTilesPerItem>
 __device__ __forceinline__ void tile_sums(const VerifyArgs& a, int b, const SampleCoef& cf, int k,
-                                          int t0, double (&tw)[kTilesPerItem + 1], double* lds_d) {
+                                          int t0, double (&tw)[N + 1], double* lds_d) {
+  constexpr int G = (DT == kBF16 && VEC) ? N : (N >= 2 ? 2 : 1);
+  static_assert(N % G == 0, "tile groups must divide the item");
   const void *drow, *trow;
   draw_rows<DT>(a, b, k, drow, trow);
   const int64_t lane_off = (int64_t)threadIdx.x * kUnit;
-  Raw8<DT, VEC> rd[kTilesPerItem], rt[kTilesPerItem];
-#pragma unroll
-  for (int i = 0; i < kTilesPerItem; ++i) {
-    const int t = t0 + i;
-    const int64_t j0 = t < a.ntile ? (int64_t)t * kTile + lane_off : (int64_t)a.V;
-    load_raw<DT, VEC>(trow, j0, a.V, rt[i]);
-    if constexpr (MODE != kModeTarget) load_raw<DT, VEC>(drow, j0, a.V, rd[i]);
-  }
   float rs = 0.f;
 #pragma unroll
-  for (int i = 0; i < kTilesPerItem; ++i) {
-    float ld[8], lt[8], w[8], r[8];
-    unpack<DT, VEC>(rt[i], lt);
-    if constexpr (MODE != kModeTarget) unpack<DT, VEC>(rd[i], ld);
-    sample_weights<DT, MODE, false>(ld, lt, cf, w, r);
-    float ws = 0.f;
+  for (int g0 = 0; g0 < N; g0 += G) {
+    Raw8<DT, VEC> rd[G], rt[G];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      ws += w[e];
-      rs += r[e];
+    for (int i = 0; i < G; ++i) {
+      const int t = t0 + g0 + i;
+      const int64_t j0 = t < a.ntile ? (int64_t)t * kTile + lane_off : (int64_t)a.V;
+      load_raw<DT, VEC, kSampleNT>(trow, j0, a.V, rt[i]);
+      if constexpr (MODE != kModeTarget) load_raw<DT, VEC, kSampleNT>(drow, j0, a.V, rd[i]);
     }
-    tw[i] = (double)ws;
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      float ld[8], lt[8], w[8], r[8];
+      unpack<DT, VEC>(rt[i], lt);
+      if constexpr (MODE != kModeTarget) unpack<DT, VEC>(rd[i], ld);
+      sample_weights<DT, MODE, false>(ld, lt, cf, w, r);
+      float ws = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        ws += w[e];
+        rs += r[e];
+      }
+      tw[g0 + i] = (double)ws;
+    }
+    if constexpr (G < N) __builtin_amdgcn_sched_barrier(0);   // keep the groups apart
   }
-  tw[kTilesPerItem] = (double)rs;
-  block_sum_n<kTilesPerItem + 1>(tw, lds_d);
+  tw[N] = (double)rs;
+  block_sum_n<N + 1>(tw, lds_d);
+}
+
+// eps * (residual mass) for Saguaro eps > 0, from the residual-mass items'
+// slots (waited for), summed in the same order by every reader.
+__device__ float eps_clamp(const VerifyArgs& a, int b, double* lds_d) {
+  double v = 0.0;
+  for (int i = threadIdx.x; i < a.nt; i += kThreads) v += slot_value(poll(a, a.mass + (int64_t)b * a.nt + i));
+  v = block_sum(v, lds_d);
+  return uni((float)(v * (double)a.eps));
 }
 
 // ---------------------------------------------------------------------------
-// Sample items.
+// Residual-mass and sampling items.
 
-// Residual mass for the Saguaro clamp (pass A).
 template <int DT, bool VEC>
-__device__ void sample_item_a(const VerifyArgs& a, int b, int s, double* lds_d) {
+__device__ void mass_item(const VerifyArgs& a, int b, int s, double* lds_d) {
+  wait_decided<true>(a, b);
   const SeqRec rec = load_rec(a.seq + b);
-  double tw[kTilesPerItem + 1] = {};
-  if (rec.valid && rec.mode == kModeSaguaroEps)
-    tile_sums<DT, VEC, kModeResidual>(a, b, coef_of(a, rec), rec.k, s * kTilesPerItem, tw, lds_d);
-  if (threadIdx.x == 0) st_dev(a.itemsum + (int64_t)b * a.nt + s, tw[kTilesPerItem]);
+  if (!rec.valid || rec.mode != kModeSaguaroEps) return;
+  double tw[kTilesPerItem + 1];
+  tile_sums<DT, VEC, kModeResidual>(a, b, coef_of(a, rec, 0.f), rec.k, s * kTilesPerItem, tw, lds_d);
+  if (threadIdx.x == 0) slot_put(a.mass + (int64_t)b * a.nt + s, tw[kTilesPerItem]);
 }
 
-// eps * residual mass, by the last pass-A item of a sequence.
-__device__ void finish_a(const VerifyArgs& a, int b, double* lds_d) {
-  double v = 0.0;
-  for (int i = threadIdx.x; i < a.nt; i += kThreads) v += ld_dev(a.itemsum + (int64_t)b * a.nt + i);
-  v = block_sum(v, lds_d);
-  if (threadIdx.x == 0) store_rec_eps(a.seq + b, (float)(v * (double)a.eps));
-}
-
-// Tile sums of the sampling weights (pass B).
 template <int DT, bool VEC>
-__device__ void sample_item_b(const VerifyArgs& a, int b, int s, double* lds_d) {
+__device__ void sample_item(const VerifyArgs& a, int b, int s, double* lds_d) {
+  wait_decided<true>(a, b);
   const SeqRec rec = load_rec(a.seq + b);
   if (!rec.valid) return;
   const int t0 = s * kTilesPerItem;
-  const SampleCoef cf = coef_of(a, rec);
+  const float epsS = rec.mode == kModeSaguaroEps ? eps_clamp(a, b, lds_d) : 0.f;
+  const SampleCoef cf = coef_of(a, rec, epsS);
   with_mode(rec.mode, [&](auto m) {
+    constexpr int MODE = decltype(m)::value;
     double tw[kTilesPerItem + 1];
-    tile_sums<DT, VEC, decltype(m)::value>(a, b, cf, rec.k, t0, tw, lds_d);
+    tile_sums<DT, VEC, MODE>(a, b, cf, rec.k, t0, tw, lds_d);
     if (threadIdx.x == 0) {
 #pragma unroll
       for (int i = 0; i < kTilesPerItem; ++i)
-        if (t0 + i < a.ntile) st_dev(a.tiles + (int64_t)b * a.ntile + t0 + i, tw[i]);
-      st_dev(a.itemsum + (int64_t)b * a.nt + s, tw[kTilesPerItem]);
+        if (t0 + i < a.ntile) slot_put(a.tiles + (int64_t)b * a.ntile + t0 + i, tw[i]);
+      if (MODE == kModeSaguaro) slot_put(a.rsum + (int64_t)b * a.nt + s, tw[kTilesPerItem]);
     }
   });
 }
 
+// ---------------------------------------------------------------------------
+// Refine item.
+
 struct RefineLds {
   double lds_d[kWaves * (kTilesPerItem + 1)];
   int lds_i[kWaves];
-  int tile;
-  double off, lo, hi, w;
+  int tile, owner;
+  double off, lane_off, lo, hi, w;
+  float w8[kUnit];
+  int y;
 };
+
+__device__ __forceinline__ double tile_value(const uint64_t* tiles, int t) {
+  return slot_value(ld_dev_u64(tiles + t));
+}
 
 // Locate the tile holding u * S (S = sum of the tile sums) by an fp64 scan
 // over the tile sums in token order; returns S, sets sh.tile and sh.off.
-__device__ double locate_tile(const double* tiles, int ntile, double u, RefineLds& sh, double& target) {
+__device__ double locate_tile(const uint64_t* tiles, int ntile, double u, RefineLds& sh, double& target) {
   const int tid = threadIdx.x;
+  if (tid == 0) sh.tile = -1;
   double S = 0.0;
   if (ntile <= kThreads) {   // one tile sum per thread, loaded once
-    const double v = tid < ntile ? ld_dev(tiles + tid) : 0.0;
+    const double v = tid < ntile ? tile_value(tiles, tid) : 0.0;
     double tot;
     const double off = block_exclusive_scan(v, sh.lds_d, tot);
     S = tot;
@@ -629,13 +695,13 @@ __device__ double locate_tile(const double* tiles, int ntile, double u, RefineLd
     }
   } else {
     double v = 0.0;
-    for (int i = tid; i < ntile; i += kThreads) v += ld_dev(tiles + i);
+    for (int i = tid; i < ntile; i += kThreads) v += tile_value(tiles, i);
     S = block_sum(v, sh.lds_d);
     target = u * S;
     double carry = 0.0;
     for (int base = 0; base < ntile; base += kThreads) {
       const int t = base + tid;
-      const double x = t < ntile ? ld_dev(tiles + t) : 0.0;
+      const double x = t < ntile ? tile_value(tiles, t) : 0.0;
       double tot;
       const double off = carry + block_exclusive_scan(x, sh.lds_d, tot);
       const int hit = (t < ntile && off <= target && target < off + x) ? t : INT_MAX;
@@ -654,12 +720,12 @@ __device__ double locate_tile(const double* tiles, int ntile, double u, RefineLd
   if (sh.tile < 0) {   // u * S at or past the last running sum (rounding): last nonzero tile
     int last = -1;
     for (int t = tid; t < ntile; t += kThreads)
-      if (ld_dev(tiles + t) > 0.0) last = t;
+      if (tile_value(tiles, t) > 0.0) last = t;
     last = -block_min_int(-last, sh.lds_i);
     if (tid == 0) {
       sh.tile = max(last, 0);
       double off = 0.0;
-      for (int t = 0; t < last; ++t) off += ld_dev(tiles + t);
+      for (int t = 0; t < last; ++t) off += tile_value(tiles, t);
       sh.off = off;
     }
     __syncthreads();
@@ -668,333 +734,297 @@ __device__ double locate_tile(const double* tiles, int ntile, double u, RefineLd
 }
 
 // Rescan the chosen tile: the same weights and per-lane fp32 sums as its tile
-// sum, fp64 prefix.  Writes y, C_{y-1} and C_y (unnormalised) and pi(y)'s
-// weight recomputed with the precise residual.
+// sum, fp64 prefix over the lanes.  The lane holding the target (else the last
+// lane with weight) hands its eight weights to thread 0, which walks them in
+// fp64: y = the first token with weight whose running sum passes the target
+// (else the lane's last token with weight).  Sets sh.y, sh.lo = C_{y-1} and
+// sh.hi = C_y (unnormalised).
 template <int DT, bool VEC, int MODE>
-__device__ int rescan_tile(const VerifyArgs& a, int b, int k, const SampleCoef& cf, double target,
-                           RefineLds& sh) {
+__device__ void rescan_tile(const VerifyArgs& a, int b, int k, const SampleCoef& cf, double target,
+                            RefineLds& sh) {
   const int tid = threadIdx.x;
   const int tsel = sh.tile;
   const void *drow, *trow;
   draw_rows<DT>(a, b, k, drow, trow);
   const int64_t j0 = (int64_t)tsel * kTile + (int64_t)tid * kUnit;
-  Raw8<DT, VEC> rd, rt;
-  load_raw<DT, VEC>(trow, j0, a.V, rt);
-  if constexpr (MODE != kModeTarget) load_raw<DT, VEC>(drow, j0, a.V, rd);
-  float ld[8], lt[8], w[8], r[8];
-  unpack<DT, VEC>(rt, lt);
-  if constexpr (MODE != kModeTarget) unpack<DT, VEC>(rd, ld);
-  sample_weights<DT, MODE, false>(ld, lt, cf, w, r);
+  float w[8];
+  {
+    Raw8<DT, VEC> rd, rt;
+    load_raw<DT, VEC>(trow, j0, a.V, rt);
+    if constexpr (MODE != kModeTarget) load_raw<DT, VEC>(drow, j0, a.V, rd);
+    float ld[8], lt[8], r[8];
+    unpack<DT, VEC>(rt, lt);
+    if constexpr (MODE != kModeTarget) unpack<DT, VEC>(rd, ld);
+    sample_weights<DT, MODE, false>(ld, lt, cf, w, r);
+  }
   float ws = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) ws += w[e];
   double tile_tot;
   const double off = block_exclusive_scan((double)ws, sh.lds_d, tile_tot);
   const double tgt = target - sh.off;
-  int cand = INT_MAX;
-  if (off <= tgt && tgt < off + (double)ws) {
-    double run = off;
-    bool found = false;
+  const int hit = (ws > 0.f && off <= tgt && tgt < off + (double)ws) ? tid : INT_MAX;
+  int owner = block_min_int(hit, sh.lds_i);
+  if (owner == INT_MAX) owner = -block_min_int(ws > 0.f ? -tid : 1, sh.lds_i);   // last lane with weight
+  if (tid == owner) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const double nx = run + (double)w[e];
-      if (!found && w[e] > 0.f && tgt < nx) {
-        cand = (int)(j0 + e);
-        found = true;
-      }
-      run = nx;
-    }
-  }
-  int y = block_min_int(cand, sh.lds_i);
-  if (y == INT_MAX) {   // rounding left the target past every running sum: last token with weight
-    int last = -1;
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      if (w[e] > 0.f) last = (int)(j0 + e);
-    y = -block_min_int(-last, sh.lds_i);
-    if (y < 0) y = (int)min<int64_t>(a.V - 1, (int64_t)tsel * kTile + kTile - 1);
-  }
-  if (y >= j0 && y < j0 + 8) {   // the owner of y reports C_{y-1}, C_y and pi(y)
-    const int idx = (int)(y - j0);
-    double run = sh.off + off, wy = 0.0;
-    float ldy = 0.f, lty = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      if (e < idx) run += (double)w[e];
-      if (e == idx) {
-        wy = (double)w[e];
-        ldy = ld[e];
-        lty = lt[e];
-      }
-    }
-    sh.lo = run;
-    sh.hi = run + wy;
-    float rr;
-    sh.w = (double)weight_rt<DT, true>(MODE, ldy, lty, cf, rr);
+    for (int e = 0; e < 8; ++e) sh.w8[e] = w[e];
+    sh.lane_off = off;
   }
   __syncthreads();
-  return y;
+  if (tid == 0) {
+    if (owner < 0) {   // no weight in the tile (not reached: its tile sum was positive)
+      sh.y = (int)min<int64_t>(a.V - 1, (int64_t)tsel * kTile + kTile - 1);
+      sh.lo = sh.hi = sh.off + tile_tot;
+    } else {
+      double run = sh.off + sh.lane_off;
+      const double tg = target;
+      int idx = -1, last = -1;
+      double lo_last = run, lo = run;
+      for (int e = 0; e < 8; ++e) {
+        const double we = (double)sh.w8[e];
+        if (we > 0.0) {
+          if (idx < 0 && tg < run + we) {
+            idx = e;
+            lo = run;
+          }
+          last = e;
+          lo_last = run;
+        }
+        run += we;
+      }
+      if (idx < 0) {
+        idx = last;
+        lo = lo_last;
+      }
+      sh.y = (int)((int64_t)tsel * kTile + (int64_t)owner * kUnit + idx);
+      sh.lo = lo;
+      sh.hi = lo + (double)sh.w8[idx];
+    }
+  }
+  __syncthreads();
 }
 
-// Locate, rescan and write the outputs (run by the last pass-B item).
+// pi(y)'s weight with the precise residual (thread 0).
+template <int DT>
+__device__ double precise_weight(const VerifyArgs& a, int b, int k, int mode, const SampleCoef& cf, int y) {
+  const void *drow, *trow;
+  draw_rows<DT>(a, b, k, drow, trow);
+  const float lt = load_one<DT>(trow, y);
+  const float ld = mode == kModeTarget ? 0.f : load_one<DT>(drow, y);
+  float w = 0.f, r;
+  with_mode(mode, [&](auto m) { w = weight_one<DT, decltype(m)::value, true>(ld, lt, cf, r); });
+  return (double)w;
+}
+
+// Recompute every tile sum of a sequence in `mode` (a zero Saguaro normaliser
+// falls back to the residual, a zero residual mass to q_k; degenerate inputs
+// only).
 template <int DT, bool VEC>
-__device__ void refine_seq(const VerifyArgs& a, int b, RefineLds& sh) {
+__device__ void recompute_tiles(const VerifyArgs& a, int b, int k, int mode, const SampleCoef& cf,
+                                RefineLds& sh) {
+  uint64_t* tiles = a.tiles + (int64_t)b * a.ntile;
+  for (int t = 0; t < a.ntile; ++t) {
+    double tw[2];
+    with_mode(mode, [&](auto m) { tile_sums<DT, VEC, decltype(m)::value, 1>(a, b, cf, k, t, tw, sh.lds_d); });
+    if (threadIdx.x == 0) slot_put(tiles + t, tw[0]);
+  }
+  if (threadIdx.x == 0) wait_mem();
+  __syncthreads();
+}
+
+template <int DT, bool VEC>
+__device__ void refine_item(const VerifyArgs& a, int b, RefineLds& sh) {
   const int tid = threadIdx.x;
+  wait_decided<false>(a, b);
   const SeqRec rec = load_rec(a.seq + b);
-  if (!rec.valid) return;   // outputs were written by the decision
-  const int g = a.gamma, k = rec.k;
-  const int64_t orow = (int64_t)b * (g + 1);
-  double* tiles = a.tiles + (int64_t)b * a.ntile;
-  const SampleCoef cf = coef_of(a, rec);
-  int mode = rec.mode;
-  if (tid == 0) sh.tile = -1;
+  if (rec.valid) {
+    const int g = a.gamma, k = rec.k;
+    const int64_t orow = (int64_t)b * (g + 1);
+    uint64_t* tiles = a.tiles + (int64_t)b * a.ntile;
+    const float epsS = rec.mode == kModeSaguaroEps ? eps_clamp(a, b, sh.lds_d) : 0.f;
+    const SampleCoef cf = coef_of(a, rec, epsS);
+    int mode = rec.mode;
+    for (int t = tid; t < a.ntile; t += kThreads) (void)poll(a, tiles + t);
+    double rtot = 0.0;   // residual mass (relative to Mt) when it differs from the tile total
+    if (mode == kModeSaguaro || mode == kModeSaguaroEps) {
+      uint64_t* rs = (mode == kModeSaguaro ? a.rsum : a.mass) + (int64_t)b * a.nt;
+      for (int i = tid; i < a.nt; i += kThreads) rtot += slot_value(poll(a, rs + i));
+    }
+    rtot = uni(block_sum(rtot, sh.lds_d));   // also orders the polls before the reads below
 
-  double rtot = 0.0;
-  for (int i = tid; i < a.nt; i += kThreads) rtot += ld_dev(a.itemsum + (int64_t)b * a.nt + i);
-  rtot = block_sum(rtot, sh.lds_d);
-  if (mode == kModeTarget) rtot = 0.0;
+    const double u = (double)a.u_smp[orow + k];
+    double target = 0.0;
+    double S = uni(locate_tile(tiles, a.ntile, u, sh, target));
+    target = uni(target);
+    if (mode == kModeResidual) rtot = S;
+    while (!(S > 0.0) && mode != kModeTarget) {
+      mode = mode == kModeResidual ? kModeTarget : kModeResidual;
+      recompute_tiles<DT, VEC>(a, b, k, mode, cf, sh);
+      S = uni(locate_tile(tiles, a.ntile, u, sh, target));
+      target = uni(target);
+      if (mode == kModeResidual) rtot = S;
+    }
+    with_mode(mode, [&](auto m) { rescan_tile<DT, VEC, decltype(m)::value>(a, b, k, cf, target, sh); });
+    const int y = sh.y;
 
-  const double u = (double)a.u_smp[orow + k];
-  double target = 0.0;
-  double S = locate_tile(tiles, a.ntile, u, sh, target);
-  while (!(S > 0.0) && mode != kModeTarget) {
-    // A zero Saguaro normaliser falls back to the residual, a zero residual
-    // mass to q_k: recompute every tile sum here (degenerate inputs only).
-    mode = mode == kModeResidual ? kModeTarget : kModeResidual;
-    if (mode == kModeTarget) rtot = 0.0;
-    const void *drow, *trow;
-    draw_rows<DT>(a, b, k, drow, trow);
-    for (int t = 0; t < a.ntile; ++t) {
-      float ws = 0.f;
-#pragma unroll 1
-      for (int e = 0; e < kUnit; ++e) {
-        const int64_t j = (int64_t)t * kTile + (int64_t)tid * kUnit + e;
-        float rr;
-        if (j < a.V)
-          ws += weight_rt<DT, false>(mode, load_one<DT>(drow, j), load_one<DT>(trow, j), cf, rr);
-      }
-      const double tw = block_sum((double)ws, sh.lds_d);
-      if (tid == 0) st_dev(tiles + t, tw);
+    if (tid <= g) {
+      int tok = -1;
+      if (tid < k) tok = a.tokens[(int64_t)b * g + tid];
+      else if (tid == k) tok = y;
+      a.out_tokens[orow + tid] = tok;
     }
     if (tid == 0) {
-      wait_mem();
-      sh.tile = -1;
+      a.out_acc[b] = k;
+      if (a.out_first_reject) a.out_first_reject[b] = k < g ? k : -1;
+      if (a.out_mask) a.out_mask[b] = rec.mask;
+      if (a.out_len) a.out_len[b] = (a.in_len ? a.in_len[b] : 0) + k + 1;
+      if (a.diag.resid_mass) a.diag.resid_mass[b] = k < g ? rtot / rec.Zt : 0.0;
+      if (a.diag.token_prob) a.diag.token_prob[b] = precise_weight<DT>(a, b, k, mode, cf, y) / S;
+      if (a.diag.cdf_lo) a.diag.cdf_lo[b] = sh.lo / S;
+      if (a.diag.cdf_hi) a.diag.cdf_hi[b] = sh.hi / S;
     }
+    // Every slot of the sequence has been read: clear them for the next call.
     __syncthreads();
-    S = locate_tile(tiles, a.ntile, u, sh, target);
+    for (int t = tid; t < a.ntile; t += kThreads) slot_clear(tiles + t);
+    if (rec.mode == kModeSaguaro)
+      for (int i = tid; i < a.nt; i += kThreads) slot_clear(a.rsum + (int64_t)b * a.nt + i);
+    if (rec.mode == kModeSaguaroEps)
+      for (int i = tid; i < a.nt; i += kThreads) slot_clear(a.mass + (int64_t)b * a.nt + i);
   }
-
-  int y = 0;
-  with_mode(mode, [&](auto m) { y = rescan_tile<DT, VEC, decltype(m)::value>(a, b, k, cf, target, sh); });
-
-  if (tid <= g) {
-    int tok = -1;
-    if (tid < k) tok = a.tokens[(int64_t)b * g + tid];
-    else if (tid == k) tok = y;
-    a.out_tokens[orow + tid] = tok;
-  }
+  // Once every residual-mass and sampling item is past its wait, clear the
+  // flag and the count.
   if (tid == 0) {
-    a.out_acc[b] = k;
-    if (a.out_first_reject) a.out_first_reject[b] = k < g ? k : -1;
-    if (a.out_mask) a.out_mask[b] = rec.mask;
-    if (a.out_len) a.out_len[b] = (a.in_len ? a.in_len[b] : 0) + k + 1;
-    if (a.diag.resid_mass) a.diag.resid_mass[b] = k < g ? rtot / rec.Zt : 0.0;
-    if (a.diag.token_prob) a.diag.token_prob[b] = sh.w / S;
-    if (a.diag.cdf_lo) a.diag.cdf_lo[b] = sh.lo / S;
-    if (a.diag.cdf_hi) a.diag.cdf_hi[b] = sh.hi / S;
+    unsigned* f = a.flag + (int64_t)b * kFlagStride;
+    const unsigned expect = (unsigned)a.nt * ((a.saguaro && a.eps > 0.f) ? 2u : 1u);
+    unsigned polls = 0;
+    while (__hip_atomic_load(f + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < expect &&
+           !give_up(a, polls)) {
+    }
+    slot_clear32(f + 1);
+    slot_clear32(f);
   }
 }
 
 // ---------------------------------------------------------------------------
-// Kernels.
-
-template <int DT, bool VEC, int U, bool DECIDE>
-__global__ __launch_bounds__(kThreads) void stream_kernel(VerifyArgs a) {
-  __shared__ float lds_f[2 * kWaves];
-  __shared__ double lds_d[kWaves];
-  const int R = 2 * a.gamma + 1;
-  const int64_t id = blockIdx.x;
-  const int per_seq = R * a.nc;
-  const int b = (int)(id / per_seq);
-  const int rem = (int)(id - (int64_t)b * per_seq);
-  const int r = rem / a.nc, c = rem - r * a.nc;
-  stream_item<DT, VEC, U>(a, b, r, c, lds_f, lds_d);
-  if constexpr (DECIDE) {
-    __shared__ int flag;
-    __shared__ DecideLds dsh;
-    if (arrive(&a.ctr[b].stream_done, (unsigned)per_seq, &flag)) decide_seq<DT>(a, b, dsh);
-  }
-}
-
-template <int DT>
-__global__ __launch_bounds__(kThreads) void decide_kernel(VerifyArgs a) {
-  __shared__ DecideLds dsh;
-  decide_seq<DT>(a, blockIdx.x, dsh);
-}
-
-template <int DT, bool VEC>
-__global__ __launch_bounds__(kThreads) void sample_a_kernel(VerifyArgs a) {
-  __shared__ double lds_d[kWaves * (kTilesPerItem + 1)];
-  __shared__ int flag;
-  const int b = blockIdx.x / a.nt, s = blockIdx.x - b * a.nt;
-  sample_item_a<DT, VEC>(a, b, s, lds_d);
-  if (arrive(&a.ctr[b].a_done, (unsigned)a.nt, &flag)) finish_a(a, b, lds_d);
-}
-
-template <int DT, bool VEC>
-__global__ __launch_bounds__(kThreads) void sample_b_kernel(VerifyArgs a) {
-  __shared__ RefineLds sh;
-  __shared__ int flag;
-  const int b = blockIdx.x / a.nt, s = blockIdx.x - b * a.nt;
-  sample_item_b<DT, VEC>(a, b, s, sh.lds_d);
-  if (arrive(&a.ctr[b].b_done, (unsigned)a.nt, &flag)) refine_seq<DT, VEC>(a, b, sh);
-}
-
-// ---------------------------------------------------------------------------
-// Fused persistent kernel.
+// Launch order.
 //
-// Items are numbered in steps: step t holds the stream items of sequence t,
-// then the residual-mass items (Saguaro eps > 0) of sequence t - LA, then the
-// sampling items of sequence t - LB.  Work-groups take item numbers in
-// increasing order from a global counter (one item ahead, so the atomic's
-// latency overlaps the current item), so items run nearly in order and a
-// sequence's sampling items start about LB steps after its rows were
-// streamed, re-reading them from the 256 MB last-level cache.  A sampling
-// item waits (bounded spin) for its sequence's decision, which the last of
-// the sequence's stream items makes.  An item waits only on items with
-// smaller numbers, all of them already taken by resident work-groups (the
-// launch is cooperative), so the smallest unfinished item can always run.
+// Step t holds, in this order: the stream items of sequence t (NS of them),
+// the decision of sequence t - LD, the residual-mass items of t - LM (NM, eps
+// > 0 only), the sampling items of t - LB (NB) and the refine item of t - LR,
+// where each exists; LD <= LM <= LB <= LR.
+
+constexpr int kKinds = 5;
+enum : int { kItemStream = 0, kItemDecide = 1, kItemMass = 2, kItemSample = 3, kItemRefine = 4 };
 
 struct Sched {
-  int B, NS, NA, NB, LA, LB;
+  int B;
+  int lag[kKinds];
+  int size[kKinds];
+  int steps;        // B + lag[kItemRefine]
   int64_t total;
 };
 
 __host__ __device__ inline int64_t sched_offset(const Sched& s, int t) {
-  const int ns = t < s.B ? t : s.B;
-  int na = t - s.LA, nb = t - s.LB;
-  na = na < 0 ? 0 : (na > s.B ? s.B : na);
-  nb = nb < 0 ? 0 : (nb > s.B ? s.B : nb);
-  return (int64_t)ns * s.NS + (int64_t)na * s.NA + (int64_t)nb * s.NB;
+  int64_t o = 0;
+  for (int i = 0; i < kKinds; ++i) {
+    int n = t - s.lag[i];
+    n = n < 0 ? 0 : (n > s.B ? s.B : n);
+    o += (int64_t)n * s.size[i];
+  }
+  return o;
 }
 
-enum : int { kItemStream = 0, kItemA = 1, kItemB = 2 };
-
-__device__ __forceinline__ void sched_decode(const Sched& s, int64_t j, int& kind, int& b, int& sub) {
-  int lo = 0, hi = s.B + s.LB;   // offset(lo) <= j < offset(hi) = total
+__host__ __device__ inline void sched_decode(const Sched& s, int64_t j, int& kind, int& b, int& sub) {
+  int lo = 0, hi = s.steps;   // offset(lo) <= j < offset(hi) = total
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
     if (sched_offset(s, mid) <= j) lo = mid;
     else hi = mid;
   }
   int64_t w = j - sched_offset(s, lo);
-  if (lo < s.B) {
-    if (w < s.NS) {
-      kind = kItemStream;
-      b = lo;
+  kind = kItemRefine;
+  b = lo - s.lag[kItemRefine];
+  sub = 0;
+  for (int i = 0; i < kKinds; ++i) {
+    const int bi = lo - s.lag[i];
+    if (bi < 0 || bi >= s.B) continue;
+    if (w < s.size[i]) {
+      kind = i;
+      b = bi;
       sub = (int)w;
       return;
     }
-    w -= s.NS;
+    w -= s.size[i];
   }
-  const int ba = lo - s.LA;
-  if (s.NA > 0 && ba >= 0 && ba < s.B) {
-    if (w < s.NA) {
-      kind = kItemA;
-      b = ba;
-      sub = (int)w;
-      return;
-    }
-    w -= s.NA;
-  }
-  kind = kItemB;
-  b = lo - s.LB;
-  sub = (int)w;
 }
 
-// Bounded spin until *flag is nonzero (thread 0 polls; the work-group follows).
-// A timeout records an error instead of hanging.
-__device__ __forceinline__ void wait_flag(const VerifyArgs& a, unsigned* flag, int* lds_flag) {
-  if (threadIdx.x == 0) {
-    unsigned polls = 0;
-    while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
-      __builtin_amdgcn_s_sleep(2);
-      if (++polls > (1u << 23)) {   // about half a second
-        __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        break;
-      }
-    }
-    *lds_flag = 0;
-  }
-  __syncthreads();
-}
+// ---------------------------------------------------------------------------
+// Kernels.
 
-__device__ __forceinline__ void set_flag(unsigned* flag) {
-  if (threadIdx.x == 0) {
-    wait_mem();
-    __hip_atomic_store(flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+union ItemLds {
+  StreamLds s;
+  DecideLds d;
+  RefineLds r;
+};
+
+// Compiled for 8 waves per SIMD (64 VGPRs): the stream items need the
+// occupancy; every other path fits without spilling for packed bf16 rows.
+template <int DT, bool VEC, int U>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8)))
+void fused_kernel(VerifyArgs a, Sched sc) {
+  __shared__ ItemLds sh;
+  int kind, b, sub;
+  sched_decode(sc, blockIdx.x, kind, b, sub);
+  switch (kind) {
+    case kItemStream: {
+      const int r = sub / a.nc, c = sub - r * a.nc;
+      stream_item<DT, VEC, U>(a, b, r, c, sh.s);
+      break;
+    }
+    case kItemDecide: decide_item<DT>(a, b, sh.d); break;
+    case kItemMass: mass_item<DT, VEC>(a, b, sub, sh.r.lds_d); break;
+    case kItemSample: sample_item<DT, VEC>(a, b, sub, sh.r.lds_d); break;
+    default: refine_item<DT, VEC>(a, b, sh.r); break;
   }
 }
 
 template <int DT, bool VEC, int U>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(SV_FUSED_WAVES, SV_FUSED_WAVES)))
-void fused_kernel(VerifyArgs a, Sched sc) {
-  __shared__ union {
-    DecideLds d;
-    RefineLds r;
-  } sh;
-  __shared__ float lds_f[2 * kWaves];
+__global__ __launch_bounds__(kThreads) void stream_kernel(VerifyArgs a) {
+  __shared__ StreamLds sh;
+  const int R = 2 * a.gamma + 1;
+  const int64_t id = blockIdx.x;
+  const int per_seq = R * a.nc;
+  const int b = (int)(id / per_seq);
+  const int rem = (int)(id - (int64_t)b * per_seq);
+  const int r = rem / a.nc, c = rem - r * a.nc;
+  stream_item<DT, VEC, U>(a, b, r, c, sh);
+}
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void decide_kernel(VerifyArgs a) {
+  __shared__ DecideLds sh;
+  decide_item<DT>(a, blockIdx.x, sh);
+}
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kThreads) void mass_kernel(VerifyArgs a) {
   __shared__ double lds_d[kWaves * (kTilesPerItem + 1)];
-  __shared__ int flag;
-  __shared__ unsigned item;
-  const bool eps_mode = a.saguaro && a.eps > 0.f;
-  const unsigned grabs = (unsigned)sc.total + gridDim.x;   // every work-group over-takes once
-  unsigned ahead = 0;
-  if (threadIdx.x == 0)
-    ahead = __hip_atomic_fetch_add(a.next, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  for (;;) {
-    if (threadIdx.x == 0) {
-      item = ahead;
-      if (ahead == grabs - 1)   // the last take of the call: leave the counter zeroed
-        __hip_atomic_store(a.next, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      else if (ahead < sc.total)
-        ahead = __hip_atomic_fetch_add(a.next, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __syncthreads();
-    const int64_t j = item;
-    if (j >= sc.total) break;
-    int kind, b, sub;
-    sched_decode(sc, j, kind, b, sub);
-    SeqCtr& ctr = a.ctr[b];
-    if (kind == kItemStream) {
-      const int r = sub / a.nc, c = sub - r * a.nc;
-      stream_item<DT, VEC, U>(a, b, r, c, lds_f, lds_d);
-      if (arrive(&ctr.stream_done, (unsigned)sc.NS, &flag)) {
-        decide_seq<DT>(a, b, sh.d);
-        __syncthreads();
-        set_flag(&ctr.decided);
-      }
-    } else if (kind == kItemA) {
-      wait_flag(a, &ctr.decided, &flag);
-      sample_item_a<DT, VEC>(a, b, sub, lds_d);
-      if (arrive(&ctr.a_done, (unsigned)a.nt, &flag)) {
-        finish_a(a, b, lds_d);
-        __syncthreads();
-        set_flag(&ctr.a_ready);
-      }
-    } else {
-      wait_flag(a, eps_mode ? &ctr.a_ready : &ctr.decided, &flag);
-      sample_item_b<DT, VEC>(a, b, sub, lds_d);
-      if (arrive(&ctr.b_done, (unsigned)a.nt, &flag)) {
-        refine_seq<DT, VEC>(a, b, sh.r);
-        if (threadIdx.x == 0) {   // every reader of the flags has passed them
-          __hip_atomic_store(&ctr.decided, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          __hip_atomic_store(&ctr.a_ready, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-      }
-    }
-    __syncthreads();
-  }
+  const int b = blockIdx.x / a.nt, s = blockIdx.x - b * a.nt;
+  mass_item<DT, VEC>(a, b, s, lds_d);
+}
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kThreads) void sample_kernel(VerifyArgs a) {
+  __shared__ double lds_d[kWaves * (kTilesPerItem + 1)];
+  const int b = blockIdx.x / a.nt, s = blockIdx.x - b * a.nt;
+  sample_item<DT, VEC>(a, b, s, lds_d);
+}
+
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kThreads) void refine_kernel(VerifyArgs a) {
+  __shared__ RefineLds sh;
+  refine_item<DT, VEC>(a, blockIdx.x, sh);
 }
 
 // ---------------------------------------------------------------------------
@@ -1004,7 +1034,7 @@ static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
   int nc, chunk, ntile, nt;
-  size_t err_off, part_off, seq_off, ctr_off, tiles_off, item_off, total;
+  size_t err_off, part_off, mraw_off, seq_off, flag_off, tiles_off, mass_off, rsum_off, total;
 };
 
 static bool sizes_ok(int B, int gamma, int V) {
@@ -1024,56 +1054,99 @@ static Layout layout(int B, int gamma, int V) {
   L.err_off = off;
   off += 256;
   L.part_off = off;
-  off += align256((size_t)B * R * L.nc * sizeof(Partial));
+  off += align256((size_t)B * R * L.nc * sizeof(uint64_t));
+  L.mraw_off = off;
+  off += align256((size_t)B * R * L.nc * sizeof(unsigned));
   L.seq_off = off;
   off += align256((size_t)B * sizeof(SeqRec));
-  L.ctr_off = off;
-  off += align256((size_t)B * sizeof(SeqCtr));
+  L.flag_off = off;
+  off += align256((size_t)B * kFlagStride * sizeof(unsigned));
   L.tiles_off = off;
-  off += align256((size_t)B * L.ntile * sizeof(double));
-  L.item_off = off;
-  off += align256((size_t)B * L.nt * sizeof(double));
+  off += align256((size_t)B * L.ntile * sizeof(uint64_t));
+  L.mass_off = off;
+  off += align256((size_t)B * L.nt * sizeof(uint64_t));
+  L.rsum_off = off;
+  off += align256((size_t)B * L.nt * sizeof(uint64_t));
   L.total = B == 0 ? 0 : off;
   return L;
 }
 
+// Work-groups of the fused kernel the device holds at once (cached per device).
+template <int DT, bool VEC>
+static hipError_t resident_groups(int& slots) {
+  static int cache[64][2][2];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  int* c = dev >= 0 && dev < 64 ? &cache[dev][DT][VEC ? 1 : 0] : nullptr;
+  if (c && *c > 0) {
+    slots = *c;
+    return hipSuccess;
+  }
+  int ncu = 0, per_cu = 0;
+  e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &per_cu, reinterpret_cast<const void*>(fused_kernel<DT, VEC, SV_STREAM_UNROLL>), kThreads, 0);
+  if (e != hipSuccess) return e;
+  slots = std::max(1, ncu * per_cu);
+  if (c) *c = slots;
+  return hipSuccess;
+}
+
+static Sched make_sched(int B, int NS, int NM, int NB, int slots) {
+  Sched s;
+  s.B = B;
+  const double spr = (double)slots / (double)NS;   // sequences streamed per round
+  auto steps = [&](int milli) { return (int)std::lround(spr * milli / 1000.0); };
+  s.lag[kItemStream] = 0;
+  s.lag[kItemDecide] = steps(SV_LAG_DECIDE);
+  s.lag[kItemMass] = s.lag[kItemDecide] + (NM > 0 ? steps(SV_LAG_MASS) : 0);
+  s.lag[kItemSample] = s.lag[kItemMass] + steps(SV_LAG_SAMPLE);
+  s.lag[kItemRefine] = s.lag[kItemSample] + steps(SV_LAG_REFINE);
+  s.size[kItemStream] = NS;
+  s.size[kItemDecide] = 1;
+  s.size[kItemMass] = NM;
+  s.size[kItemSample] = NB;
+  s.size[kItemRefine] = 1;
+  s.steps = B + s.lag[kItemRefine];
+  s.total = sched_offset(s, s.steps);
+  return s;
+}
+
+template <int DT, bool VEC>
+static hipError_t launch_kernels(const VerifyArgs& a, hipStream_t st);
+
 template <int DT, bool VEC>
 static hipError_t launch_all(const VerifyArgs& a, hipStream_t st) {
-  const int R = 2 * a.gamma + 1;
-  if (SV_FUSED) {
-    auto kern = fused_kernel<DT, VEC, SV_STREAM_UNROLL>;
-    int dev = 0, ncu = 0, per_cu = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e == hipSuccess)
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(kern),
-                                                       kThreads, 0);
+  // The single-kernel order for packed bf16 rows; float32 or unaligned rows
+  // take one kernel per item kind (their sampling paths need more registers
+  // than the stream items' occupancy leaves).
+  if constexpr (SV_FUSED && DT == kBF16 && VEC) {
+    int slots = 0;
+    hipError_t e = resident_groups<DT, VEC>(slots);
     if (e != hipSuccess) return e;
-    Sched sc;
-    sc.B = a.B;
-    sc.NS = R * a.nc;
-    sc.NA = (a.saguaro && a.eps > 0.f) ? a.nt : 0;
-    sc.NB = a.nt;
-    const int64_t all = (int64_t)a.B * (sc.NS + sc.NA + sc.NB);
-    const int64_t G = std::max<int64_t>(1, std::min<int64_t>((int64_t)per_cu * ncu, all));
-    const int64_t per_step = sc.NS + sc.NA + sc.NB;
-    const int L = (int)std::max<int64_t>(1, (G * SV_LAG_MILLIROUNDS / 1000 + per_step - 1) / per_step);
-    sc.LA = L;
-    sc.LB = sc.NA > 0 ? 2 * L : L;
-    sc.total = all;
-    VerifyArgs args = a;
-    void* params[] = {&args, &sc};
-    return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kern), dim3((unsigned)G),
-                                      dim3(kThreads), params, 0, st);
+    const bool eps_mode = a.saguaro && a.eps > 0.f;
+    const Sched sc = make_sched(a.B, (2 * a.gamma + 1) * a.nc, eps_mode ? a.nt : 0, a.nt, slots);
+    hipLaunchKernelGGL((fused_kernel<DT, VEC, SV_STREAM_UNROLL>), dim3((unsigned)sc.total), dim3(kThreads),
+                       0, st, a, sc);
+    return hipGetLastError();
+  } else {
+    return launch_kernels<DT, VEC>(a, st);
   }
+}
+
+template <int DT, bool VEC>
+static hipError_t launch_kernels(const VerifyArgs& a, hipStream_t st) {
+  const int R = 2 * a.gamma + 1;
+  const bool eps_mode = a.saguaro && a.eps > 0.f;
   const unsigned nstream = (unsigned)((int64_t)a.B * R * a.nc);
   const unsigned nsample = (unsigned)((int64_t)a.B * a.nt);
-  hipLaunchKernelGGL((stream_kernel<DT, VEC, SV_STREAM_UNROLL, false>), dim3(nstream), dim3(kThreads),
-                     0, st, a);
+  hipLaunchKernelGGL((stream_kernel<DT, VEC, SV_STREAM_UNROLL>), dim3(nstream), dim3(kThreads), 0, st, a);
   hipLaunchKernelGGL((decide_kernel<DT>), dim3((unsigned)a.B), dim3(kThreads), 0, st, a);
-  if (a.saguaro && a.eps > 0.f)
-    hipLaunchKernelGGL((sample_a_kernel<DT, VEC>), dim3(nsample), dim3(kThreads), 0, st, a);
-  hipLaunchKernelGGL((sample_b_kernel<DT, VEC>), dim3(nsample), dim3(kThreads), 0, st, a);
+  if (eps_mode) hipLaunchKernelGGL((mass_kernel<DT, VEC>), dim3(nsample), dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL((sample_kernel<DT, VEC>), dim3(nsample), dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL((refine_kernel<DT, VEC>), dim3((unsigned)a.B), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
@@ -1091,11 +1164,10 @@ static int verify_impl(const void* draft, const void* target, int dtype, const i
   if (!draft || !target || !tokens || !u_acc || !u_smp || !out_tokens || !out_acc)
     return SPEC_EINVAL;
   const Layout L = layout(B, gamma, V);
-  // Grid limit: at most 2^32 - 1 work-items per launch dimension.
-  if ((int64_t)B * (2 * gamma + 1) * L.nc * kThreads > (int64_t)UINT_MAX) return SPEC_EINVAL;
-  if ((int64_t)B * L.nt * kThreads > (int64_t)UINT_MAX) return SPEC_EINVAL;
-  // Fused item numbers (plus one extra take per work-group) fit in 32 bits.
-  if ((int64_t)B * ((2 * gamma + 1) * L.nc + 2 * L.nt) > (int64_t)INT_MAX / 2) return SPEC_EINVAL;
+  // Every launch (and the fused kernel's item count) stays within one grid
+  // dimension of 2^32 - 1 work-items, with block numbers below 2^31.
+  const int64_t items = (int64_t)B * ((2 * gamma + 1) * L.nc + 2 * L.nt + 2);
+  if (items * kThreads > (int64_t)UINT_MAX || items > (int64_t)INT_MAX) return SPEC_EINVAL;
   if (!ws || ws_bytes < L.total) return SPEC_EWORKSPACE;
 
   VerifyArgs a;
@@ -1114,12 +1186,13 @@ static int verify_impl(const void* draft, const void* target, int dtype, const i
   else a.diag = spec_diag{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
   char* w = static_cast<char*>(ws);
   a.err = reinterpret_cast<unsigned*>(w + L.err_off);
-  a.next = reinterpret_cast<unsigned*>(w + L.err_off + 8);
-  a.part = reinterpret_cast<Partial*>(w + L.part_off);
+  a.part = reinterpret_cast<uint64_t*>(w + L.part_off);
+  a.mraw = reinterpret_cast<unsigned*>(w + L.mraw_off);
   a.seq = reinterpret_cast<SeqRec*>(w + L.seq_off);
-  a.ctr = reinterpret_cast<SeqCtr*>(w + L.ctr_off);
-  a.tiles = reinterpret_cast<double*>(w + L.tiles_off);
-  a.itemsum = reinterpret_cast<double*>(w + L.item_off);
+  a.flag = reinterpret_cast<unsigned*>(w + L.flag_off);
+  a.tiles = reinterpret_cast<uint64_t*>(w + L.tiles_off);
+  a.mass = reinterpret_cast<uint64_t*>(w + L.mass_off);
+  a.rsum = reinterpret_cast<uint64_t*>(w + L.rsum_off);
   a.B = B;
   a.gamma = gamma;
   a.V = V;
