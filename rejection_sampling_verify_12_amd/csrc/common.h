@@ -105,6 +105,30 @@ __device__ __forceinline__ void load_raw(const void* row, int64_t j0, int64_t n,
   }
 }
 
+// Eight logits of an aligned row through a buffer resource: the lane's byte
+// offset `voff` stays in a vector register and the batch offset `soff` is
+// scalar, so stepping through a chunk costs no vector instructions.
+// Nontemporal (read once).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+template <int DT>
+__device__ __forceinline__ void load_raw_buf(__amdgpu_buffer_rsrc_t rs, int voff, int soff,
+                                             Raw8<DT, true>& r) {
+  constexpr int kNT = 2;   // cache policy: nontemporal
+  if constexpr (DT == kBF16) {
+    const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, kNT);
+    r.w = make_uint4(t.x, t.y, t.z, t.w);
+  } else {
+    const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, kNT);
+    const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(rs, voff + 16, soff, kNT);
+    r.v[0] = __uint_as_float(a.x); r.v[1] = __uint_as_float(a.y);
+    r.v[2] = __uint_as_float(a.z); r.v[3] = __uint_as_float(a.w);
+    r.v[4] = __uint_as_float(b.x); r.v[5] = __uint_as_float(b.y);
+    r.v[6] = __uint_as_float(b.z); r.v[7] = __uint_as_float(b.w);
+  }
+}
+
 template <int DT, bool VEC>
 __device__ __forceinline__ void unpack(const Raw8<DT, VEC>& r, float (&v)[8]) {
   if constexpr (DT == kBF16 && VEC) {

@@ -77,10 +77,6 @@ enum : int { kModeTarget = 0, kModeResidual = 1, kModeSaguaro = 2, kModeSaguaroE
 #ifndef SV_LAG_REFINE
 #define SV_LAG_REFINE 800
 #endif
-// 1: the stream loop keeps the next batch's loads in flight (two buffers).
-#ifndef SV_PIPE
-#define SV_PIPE 0
-#endif
 #ifndef SV_SAMPLE_NT
 #define SV_SAMPLE_NT 0
 #endif
@@ -110,7 +106,9 @@ __device__ __forceinline__ void slot_clear32(unsigned* p) {
   __hip_atomic_store(p, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// A sequence's decision, written by its decision item before its flag.
+// A sequence's decision, written by its decision item.  Each 64-bit word is
+// stored as its complement (no word of a record is all ones), so a word is 0
+// until written, and readers poll the words themselves.
 struct SeqRec {
   uint64_t mask;
   int k;
@@ -126,19 +124,15 @@ constexpr int kRecWords = sizeof(SeqRec) / 8;
 __device__ __forceinline__ void store_rec(SeqRec* p, const SeqRec& r) {
   const uint64_t* w = reinterpret_cast<const uint64_t*>(&r);
 #pragma unroll
-  for (int i = 0; i < kRecWords; ++i) st_dev_u64(reinterpret_cast<uint64_t*>(p) + i, w[i]);
+  for (int i = 0; i < kRecWords; ++i) st_dev_u64(reinterpret_cast<uint64_t*>(p) + i, ~w[i]);
 }
-// Read by every thread of a work-group; the fields are kept in scalar registers.
-__device__ __forceinline__ SeqRec load_rec(const SeqRec* p) {
-  SeqRec r;
-  uint64_t* w = reinterpret_cast<uint64_t*>(&r);
+__device__ __forceinline__ void clear_rec(SeqRec* p) {
 #pragma unroll
-  for (int i = 0; i < kRecWords; ++i) w[i] = uni(ld_dev_u64(reinterpret_cast<const uint64_t*>(p) + i));
-  return r;
+  for (int i = 0; i < kRecWords; ++i) st_dev_u64(reinterpret_cast<uint64_t*>(p) + i, 0ull);
 }
 
-// One 128-byte line per sequence: [0] = 1 once the decision record is
-// written; [1] = residual-mass and sampling items past their wait for it.
+// One 128-byte line per sequence: [0] = residual-mass and sampling items that
+// have read the decision record.
 constexpr int kFlagStride = 32;
 
 struct VerifyArgs {
@@ -158,7 +152,7 @@ struct VerifyArgs {
   uint64_t* part;    // [B][2*gamma+1][nc] slots: chunk log2-normalisers
   unsigned* mraw;    // [B][2*gamma+1][nc] 32-bit slots: chunk maxima of the raw logits
   SeqRec* seq;       // [B]
-  unsigned* flag;    // [B * kFlagStride]: decision flag and pass count
+  unsigned* flag;    // [B * kFlagStride]: record read counts
   uint64_t* tiles;   // [B][ntile] slots: tile sums of the sampling weights
   uint64_t* mass;    // [B][nt] slots: residual sums of the residual-mass items (eps > 0)
   uint64_t* rsum;    // [B][nt] slots: residual sums of the sampling items (Saguaro)
@@ -200,22 +194,42 @@ __device__ __forceinline__ uint64_t poll(const VerifyArgs& a, const uint64_t* p)
   while (w == 0ull && !give_up(a, polls)) w = ld_dev_u64(p);
   return w;
 }
-__device__ __forceinline__ unsigned poll32(const VerifyArgs& a, const unsigned* p) {
-  unsigned w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  unsigned polls = 0;
-  while (w == 0u && !give_up(a, polls)) w = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return w;
-}
-// Thread 0 waits for the sequence's decision flag (COUNT: and counts this
-// item as past it); the work-group follows.
+// The sequence's decision record: thread 0 waits for each word, the
+// work-group reads it from LDS (COUNT: thread 0 then counts this item as done
+// with the record).  The fields end up in scalar registers.
 template <bool COUNT>
-__device__ __forceinline__ void wait_decided(const VerifyArgs& a, int b) {
+__device__ __forceinline__ SeqRec wait_rec(const VerifyArgs& a, int b) {
+  __shared__ uint64_t w[kRecWords];
   if (threadIdx.x == 0) {
-    unsigned* f = a.flag + (int64_t)b * kFlagStride;
-    (void)poll32(a, f);
-    if (COUNT) __hip_atomic_fetch_add(f + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // All words are requested together, again until every one has arrived.
+    const uint64_t* p = reinterpret_cast<const uint64_t*>(a.seq + b);
+    uint64_t v[kRecWords];
+#pragma unroll
+    for (int i = 0; i < kRecWords; ++i) v[i] = ld_dev_u64(p + i);
+    unsigned polls = 0;
+    for (;;) {
+      bool all = true;
+#pragma unroll
+      for (int i = 0; i < kRecWords; ++i) all = all && v[i] != 0ull;
+      if (all || give_up(a, polls)) break;
+#pragma unroll
+      for (int i = 0; i < kRecWords; ++i)
+        if (v[i] == 0ull) v[i] = ld_dev_u64(p + i);
+    }
+#pragma unroll
+    for (int i = 0; i < kRecWords; ++i) w[i] = ~v[i];
   }
   __syncthreads();
+  SeqRec r;
+  uint64_t* rw = reinterpret_cast<uint64_t*>(&r);
+#pragma unroll
+  for (int i = 0; i < kRecWords; ++i) rw[i] = uni(w[i]);
+  if (COUNT) {
+    __syncthreads();
+    if (threadIdx.x == 0)
+      __hip_atomic_fetch_add(a.flag + (int64_t)b * kFlagStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  return r;
 }
 
 // ---------------------------------------------------------------------------
@@ -266,42 +280,33 @@ __device__ __forceinline__ void stream_item(const VerifyArgs& a, int b, int r, i
   float mref = kNegSentinel, mraw = -INFINITY;
   double s = 0.0;
   constexpr int64_t kStep = (int64_t)kThreads * kUnit;
-  int64_t j = begin + (int64_t)threadIdx.x * kUnit;
   constexpr int64_t kBatch = U * kStep;
-#if SV_PIPE
-  // Full batches (the same count in every lane), two buffers: the loads of
-  // the next batch are in flight while this one is reduced.
-  const int nb = (int)((end - begin) / kBatch);
-  if (nb > 0) {
-    Raw8<DT, VEC> A[U], Bf[U];
+  int64_t j;
+  if constexpr (VEC) {
+    // Full batches (as many in every lane) through a buffer resource over the
+    // chunk; the rest of the chunk unit by unit below.
+    constexpr int kEs = DT == kBF16 ? 2 : 4;
+    const int nb = (int)((end - begin) / kBatch);
+    const __amdgpu_buffer_rsrc_t rs =
+        chunk_rsrc(static_cast<const char*>(row) + begin * kEs, (int)((end - begin) * kEs));
+    const int voff = (int)threadIdx.x * kUnit * kEs;
+    for (int i = 0; i < nb; ++i) {
+      Raw8<DT, VEC> raw[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) load_raw<DT, VEC, true>(row, j + u * kStep, end, A[u]);
-    for (int i = 0;; i += 2) {
-      if (i + 1 < nb) {
+      for (int u = 0; u < U; ++u)
+        load_raw_buf<DT>(rs, voff, (int)((i * kBatch + u * kStep) * kEs), raw[u]);
+      stream_batch<DT, VEC, U>(raw, ch, cl, mref, mraw, s);
+    }
+    j = begin + nb * kBatch + (int64_t)threadIdx.x * kUnit;
+  } else {
+    // Full batches: U units, all in range, loads issued back to back.
+    for (j = begin + (int64_t)threadIdx.x * kUnit; j + (U - 1) * kStep + kUnit <= end; j += kBatch) {
+      Raw8<DT, VEC> raw[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) load_raw<DT, VEC, true>(row, j + kBatch + u * kStep, end, Bf[u]);
-      }
-      stream_batch<DT, VEC, U>(A, ch, cl, mref, mraw, s);
-      j += kBatch;
-      if (i + 1 >= nb) break;
-      if (i + 2 < nb) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) load_raw<DT, VEC, true>(row, j + kBatch + u * kStep, end, A[u]);
-      }
-      stream_batch<DT, VEC, U>(Bf, ch, cl, mref, mraw, s);
-      j += kBatch;
-      if (i + 2 >= nb) break;
+      for (int u = 0; u < U; ++u) load_raw<DT, VEC, true>(row, j + u * kStep, end, raw[u]);
+      stream_batch<DT, VEC, U>(raw, ch, cl, mref, mraw, s);
     }
   }
-#else
-  // Full batches: U units, all in range, loads issued back to back.
-  for (; j + (U - 1) * kStep + kUnit <= end; j += kBatch) {
-    Raw8<DT, VEC> raw[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) load_raw<DT, VEC, true>(row, j + u * kStep, end, raw[u]);
-    stream_batch<DT, VEC, U>(raw, ch, cl, mref, mraw, s);
-  }
-#endif
   // Remaining units of this lane (fewer than U; the last may be partial).
   for (; j < end; j += kStep) {
     Raw8<DT, VEC> raw[1];
@@ -344,11 +349,13 @@ struct DecideLds {
   double M[128];   // row offsets (integers, log2 units)
   double Z[128];   // row normalisers: sum_j 2^(l_j c_T - M)
   int bad[128];
+  int x[64];       // draft tokens, their draft and target logits, accept uniforms
+  float ldx[64], ltx[64], ux[64];
   uint64_t mask;
   int k, valid;
 };
 
-// Merge the chunk pieces of every row (16 lanes per row, 16 rows per pass;
+// Merge the chunk pieces of every row (16 lanes per row, 12 rows per pass;
 // fp64): Z = sum_c 2^(v_c - M), M = the integer ceiling of max_c v_c.  Then the accept test
 // at every draft position (wave 0, lane i = position i; fp64), the decision
 // record and its flag.  Every piece slot is cleared once read.
@@ -358,44 +365,69 @@ __device__ void decide_item(const VerifyArgs& a, int b, DecideLds& sh) {
   const int g = a.gamma, R = 2 * g + 1;
   const int64_t base = (int64_t)b * R * a.nc;
   const int sub = lane & 15;
-  for (int r0 = 0; r0 < R; r0 += 16) {
-    const int r = r0 + wave * 4 + (lane >> 4);
-    double M = -INFINITY, z = 0.0;
-    float mr = -INFINITY;
-    if (r < R) {
-      // Pieces c = sub, sub + 16, ...: wait for each, take the maximum; the
-      // first stays in a register, later ones are read again for the sum.
-      const int64_t p0 = base + (int64_t)r * a.nc;
-      double v0 = -INFINITY;
-      for (int c = sub; c < a.nc; c += 16) {
-        const double v = slot_value(poll(a, a.part + p0 + c));
-        mr = fmaxf(mr, __uint_as_float(~poll32(a, a.mraw + p0 + c)));
-        if (c == sub) v0 = v;
-        M = fmax(M, v);
+  // Wave 1 gathers the draft tokens' logits and the uniforms (independent of
+  // the row pieces) while waves 0, 2 and 3 merge the pieces, 12 rows a pass.
+  if (wave == 1) {
+    if (lane < g) {
+      const int x = a.tokens[(int64_t)b * g + lane];
+      float ldx = 0.f, ltx = 0.f;
+      if (x >= 0 && x < a.V) {
+        ldx = load_one<DT>(row_ptr<DT>(a, b, lane), x);
+        ltx = load_one<DT>(row_ptr<DT>(a, b, g + lane), x);
       }
-#pragma unroll
-      for (int o = 8; o > 0; o >>= 1) {
-        M = fmax(M, __shfl_xor(M, o, 16));
-        mr = fmaxf(mr, __shfl_xor(mr, o, 16));
-      }
-      M = ceil(M);
-      for (int c = sub; c < a.nc; c += 16) {
-        const double v = c == sub ? v0 : slot_value(ld_dev_u64(a.part + p0 + c));
-        if (v != -INFINITY) z += exp2(v - M);   // a NaN piece stays NaN
-        slot_clear(a.part + p0 + c);
-        slot_clear32(a.mraw + p0 + c);
-      }
+      sh.x[lane] = x;
+      sh.ldx[lane] = ldx;
+      sh.ltx[lane] = ltx;
+      sh.ux[lane] = a.u_acc[(int64_t)b * g + lane];
     }
+  } else {
+    for (int r0 = 0; r0 < R; r0 += 12) {
+      const int r = r0 + (wave == 0 ? 0 : wave - 1) * 4 + (lane >> 4);
+      double M = -INFINITY, z = 0.0;
+      float mr = -INFINITY;
+      if (r < R) {
+        // Pieces c = sub, sub + 16, ...: wait for each, take the maximum; the
+        // first stays in a register, later ones are read again for the sum.
+        const int64_t p0 = base + (int64_t)r * a.nc;
+        double v0 = -INFINITY;
+        for (int c = sub; c < a.nc; c += 16) {
+          // Both words of the piece are requested together.
+          uint64_t wv = ld_dev_u64(a.part + p0 + c);
+          unsigned wm = __hip_atomic_load(a.mraw + p0 + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          unsigned polls = 0;
+          while ((wv == 0ull || wm == 0u) && !give_up(a, polls)) {
+            if (wv == 0ull) wv = ld_dev_u64(a.part + p0 + c);
+            if (wm == 0u) wm = __hip_atomic_load(a.mraw + p0 + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+          const double v = slot_value(wv);
+          mr = fmaxf(mr, __uint_as_float(~wm));
+          if (c == sub) v0 = v;
+          M = fmax(M, v);
+        }
 #pragma unroll
-    for (int o = 8; o > 0; o >>= 1) z += __shfl_xor(z, o, 16);
-    if (r < R && sub == 0) {
-      // An all -inf row (M = -inf), a +inf logit (M = +inf) or a NaN logit
-      // (z = NaN) is bad.
-      const int ok = (z > 0.0) && isfinite(z) && isfinite(M);
-      sh.M[r] = M;
-      sh.Z[r] = z;
-      sh.bad[r] = !ok;
-      if (ok && a.diag.row_max) a.diag.row_max[(int64_t)b * R + r] = (double)mr * a.invT;
+        for (int o = 8; o > 0; o >>= 1) {
+          M = fmax(M, __shfl_xor(M, o, 16));
+          mr = fmaxf(mr, __shfl_xor(mr, o, 16));
+        }
+        M = ceil(M);
+        for (int c = sub; c < a.nc; c += 16) {
+          const double v = c == sub ? v0 : slot_value(ld_dev_u64(a.part + p0 + c));
+          if (v != -INFINITY) z += exp2(v - M);   // a NaN piece stays NaN
+          slot_clear(a.part + p0 + c);
+          slot_clear32(a.mraw + p0 + c);
+        }
+      }
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) z += __shfl_xor(z, o, 16);
+      if (r < R && sub == 0) {
+        // An all -inf row (M = -inf), a +inf logit (M = +inf) or a NaN logit
+        // (z = NaN) is bad.
+        const int ok = (z > 0.0) && isfinite(z) && isfinite(M);
+        sh.M[r] = M;
+        sh.Z[r] = z;
+        sh.bad[r] = !ok;
+        if (ok && a.diag.row_max) a.diag.row_max[(int64_t)b * R + r] = (double)mr * a.invT;
+      }
     }
   }
   __syncthreads();
@@ -409,17 +441,15 @@ __device__ void decide_item(const VerifyArgs& a, int b, DecideLds& sh) {
     rows_bad = __ballot(rows_bad) != 0;
     int acc = 0, bad = 0;
     if (lane < g) {
-      const int x = a.tokens[(int64_t)b * g + lane];
+      const int x = sh.x[lane];
       bad = (x < 0 || x >= a.V);
       if (!bad && !rows_bad) {
-        const float ld = load_one<DT>(row_ptr<DT>(a, b, lane), x);
-        const float lt = load_one<DT>(row_ptr<DT>(a, b, g + lane), x);
-        const double px = exp2((double)ld * a.cTd - sh.M[lane]) / sh.Z[lane];
-        const double qx = exp2((double)lt * a.cTd - sh.M[g + lane]) / sh.Z[g + lane];
+        const double px = exp2((double)sh.ldx[lane] * a.cTd - sh.M[lane]) / sh.Z[lane];
+        const double qx = exp2((double)sh.ltx[lane] * a.cTd - sh.M[g + lane]) / sh.Z[g + lane];
         double ratio;
         if (px > 0.0) ratio = fmin(1.0, qx / px);
         else ratio = qx > 0.0 ? 1.0 : 0.0;
-        acc = (double)a.u_acc[(int64_t)b * g + lane] < ratio;
+        acc = (double)sh.ux[lane] < ratio;
         if (a.diag.px) a.diag.px[(int64_t)b * g + lane] = px;
         if (a.diag.qx) a.diag.qx[(int64_t)b * g + lane] = qx;
       }
@@ -464,8 +494,6 @@ __device__ void decide_item(const VerifyArgs& a, int b, DecideLds& sh) {
       rec.K_lo = (float)(K - (double)rec.K_hi);
     }
     store_rec(a.seq + b, rec);
-    wait_mem();
-    __hip_atomic_store(a.flag + (int64_t)b * kFlagStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -474,6 +502,7 @@ __device__ void decide_item(const VerifyArgs& a, int b, DecideLds& sh) {
 
 struct SampleCoef {
   float c_hi, c_lo, Mt, K_hi, K_lo, epsS;
+  float A_hi, A_lo;   // K - Mt as an unevaluated float pair: p_j ~ 2^(ld_j c_T + K - Mt)
 };
 
 __device__ __forceinline__ SampleCoef coef_of(const VerifyArgs& a, const SeqRec& rec, float epsS) {
@@ -484,6 +513,9 @@ __device__ __forceinline__ SampleCoef coef_of(const VerifyArgs& a, const SeqRec&
   c.K_hi = rec.K_hi;
   c.K_lo = rec.K_lo;
   c.epsS = epsS;
+  const double A = ((double)rec.K_hi + (double)rec.K_lo) - (double)rec.Mt;
+  c.A_hi = uni((float)A);
+  c.A_lo = uni((float)(A - (double)c.A_hi));
   return c;
 }
 
@@ -526,6 +558,13 @@ __device__ __forceinline__ float weight_one(float ld, float lt, const SampleCoef
   if constexpr (MODE == kModeTarget) {
     r = 0.f;
     return eq;
+  } else if constexpr (MODE == kModeResidual && !PRECISE) {
+    // (q_j - p_j)+ from both scaled probabilities: the same absolute error
+    // (a few ulp of q_j) as 1 - 2^delta_j, with fewer instructions.
+    const float ep = exp2_fast(fmaf(ld, c.c_lo, fmaf(ld, c.c_hi, c.A_hi) + c.A_lo));
+    const float res = fmaxf(eq - ep, 0.f);
+    r = res;
+    return res;
   } else {
     const float dl = ld - lt;
     float d;
@@ -606,8 +645,9 @@ __device__ __forceinline__ void tile_sums(const VerifyArgs& a, int b, const Samp
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         ws += w[e];
-        rs += r[e];
+        if constexpr (MODE == kModeSaguaro || MODE == kModeSaguaroEps) rs += r[e];
       }
+      if constexpr (MODE == kModeResidual) rs += ws;   // the residual-mass items read it
       tw[g0 + i] = (double)ws;
     }
     if constexpr (G < N) __builtin_amdgcn_sched_barrier(0);   // keep the groups apart
@@ -630,8 +670,7 @@ __device__ float eps_clamp(const VerifyArgs& a, int b, double* lds_d) {
 
 template <int DT, bool VEC>
 __device__ void mass_item(const VerifyArgs& a, int b, int s, double* lds_d) {
-  wait_decided<true>(a, b);
-  const SeqRec rec = load_rec(a.seq + b);
+  const SeqRec rec = wait_rec<true>(a, b);
   if (!rec.valid || rec.mode != kModeSaguaroEps) return;
   double tw[kTilesPerItem + 1];
   tile_sums<DT, VEC, kModeResidual>(a, b, coef_of(a, rec, 0.f), rec.k, s * kTilesPerItem, tw, lds_d);
@@ -640,8 +679,7 @@ __device__ void mass_item(const VerifyArgs& a, int b, int s, double* lds_d) {
 
 template <int DT, bool VEC>
 __device__ void sample_item(const VerifyArgs& a, int b, int s, double* lds_d) {
-  wait_decided<true>(a, b);
-  const SeqRec rec = load_rec(a.seq + b);
+  const SeqRec rec = wait_rec<true>(a, b);
   if (!rec.valid) return;
   const int t0 = s * kTilesPerItem;
   const float epsS = rec.mode == kModeSaguaroEps ? eps_clamp(a, b, lds_d) : 0.f;
@@ -665,8 +703,8 @@ __device__ void sample_item(const VerifyArgs& a, int b, int s, double* lds_d) {
 struct RefineLds {
   double lds_d[kWaves * (kTilesPerItem + 1)];
   int lds_i[kWaves];
-  int tile, owner;
-  double off, lane_off, lo, hi, w;
+  int tile;
+  double off, lane_off, lo, hi;
   float w8[kUnit];
   int y;
 };
@@ -817,17 +855,32 @@ __device__ double precise_weight(const VerifyArgs& a, int b, int k, int mode, co
   return (double)w;
 }
 
-// Recompute every tile sum of a sequence in `mode` (a zero Saguaro normaliser
-// falls back to the residual, a zero residual mass to q_k; degenerate inputs
-// only).
-template <int DT, bool VEC>
+// Recompute every tile sum of a sequence in `mode`, the residual or q_k (a
+// zero Saguaro normaliser falls back to the residual, a zero residual mass to
+// q_k; degenerate inputs only).  One logit at a time, in the order and with
+// the weights the rescan uses, so its per-lane fp32 sums match.
+template <int DT>
 __device__ void recompute_tiles(const VerifyArgs& a, int b, int k, int mode, const SampleCoef& cf,
                                 RefineLds& sh) {
   uint64_t* tiles = a.tiles + (int64_t)b * a.ntile;
+  const void *drow, *trow;
+  draw_rows<DT>(a, b, k, drow, trow);
   for (int t = 0; t < a.ntile; ++t) {
-    double tw[2];
-    with_mode(mode, [&](auto m) { tile_sums<DT, VEC, decltype(m)::value, 1>(a, b, cf, k, t, tw, sh.lds_d); });
-    if (threadIdx.x == 0) slot_put(tiles + t, tw[0]);
+    const int64_t j0 = (int64_t)t * kTile + (int64_t)threadIdx.x * kUnit;
+    float ws = 0.f;
+#pragma unroll 1
+    for (int e = 0; e < kUnit; ++e) {
+      const int64_t j = j0 + e;
+      float w = 0.f, rr;
+      if (j < a.V) {
+        const float lt = load_one<DT>(trow, j);
+        if (mode == kModeResidual) w = weight_one<DT, kModeResidual, false>(load_one<DT>(drow, j), lt, cf, rr);
+        else w = weight_one<DT, kModeTarget, false>(0.f, lt, cf, rr);
+      }
+      ws += w;
+    }
+    const double tw = block_sum((double)ws, sh.lds_d);
+    if (threadIdx.x == 0) slot_put(tiles + t, tw);
   }
   if (threadIdx.x == 0) wait_mem();
   __syncthreads();
@@ -836,8 +889,7 @@ __device__ void recompute_tiles(const VerifyArgs& a, int b, int k, int mode, con
 template <int DT, bool VEC>
 __device__ void refine_item(const VerifyArgs& a, int b, RefineLds& sh) {
   const int tid = threadIdx.x;
-  wait_decided<false>(a, b);
-  const SeqRec rec = load_rec(a.seq + b);
+  const SeqRec rec = wait_rec<false>(a, b);
   if (rec.valid) {
     const int g = a.gamma, k = rec.k;
     const int64_t orow = (int64_t)b * (g + 1);
@@ -860,7 +912,7 @@ __device__ void refine_item(const VerifyArgs& a, int b, RefineLds& sh) {
     if (mode == kModeResidual) rtot = S;
     while (!(S > 0.0) && mode != kModeTarget) {
       mode = mode == kModeResidual ? kModeTarget : kModeResidual;
-      recompute_tiles<DT, VEC>(a, b, k, mode, cf, sh);
+      recompute_tiles<DT>(a, b, k, mode, cf, sh);
       S = uni(locate_tile(tiles, a.ntile, u, sh, target));
       target = uni(target);
       if (mode == kModeResidual) rtot = S;
@@ -892,17 +944,17 @@ __device__ void refine_item(const VerifyArgs& a, int b, RefineLds& sh) {
     if (rec.mode == kModeSaguaroEps)
       for (int i = tid; i < a.nt; i += kThreads) slot_clear(a.mass + (int64_t)b * a.nt + i);
   }
-  // Once every residual-mass and sampling item is past its wait, clear the
-  // flag and the count.
+  // Once every residual-mass and sampling item is done with the decision
+  // record, clear it and the count.
   if (tid == 0) {
     unsigned* f = a.flag + (int64_t)b * kFlagStride;
     const unsigned expect = (unsigned)a.nt * ((a.saguaro && a.eps > 0.f) ? 2u : 1u);
     unsigned polls = 0;
-    while (__hip_atomic_load(f + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < expect &&
+    while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < expect &&
            !give_up(a, polls)) {
     }
-    slot_clear32(f + 1);
     slot_clear32(f);
+    clear_rec(a.seq + b);
   }
 }
 
