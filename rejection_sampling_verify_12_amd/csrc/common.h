@@ -249,6 +249,28 @@ __device__ __forceinline__ void block_sum_n(double (&v)[N], double* lds) {
   __syncthreads();
 }
 
+// N maxima at once (one barrier pair); lds holds kWaves * N floats.
+template <int N>
+__device__ __forceinline__ void block_max_n(float (&v)[N], float* lds) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = wave_max(v[i]);
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  __syncthreads();
+  if (l == 0) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) lds[w * N + i] = v[i];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    float t = lds[i];
+#pragma unroll
+    for (int j = 1; j < kWaves; ++j) t = fmaxf(t, lds[j * N + i]);
+    v[i] = t;
+  }
+  __syncthreads();
+}
+
 __device__ __forceinline__ float block_max(float v, float* lds) {
   v = wave_max(v);
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;

@@ -14,32 +14,34 @@
 //     float pair (two FMAs per logit) so the temperature is exact; each lane
 //     keeps an integer offset, so every rescale is an exact ldexp, tree-sums
 //     each batch of its logits in fp32 and accumulates in fp64.
-//   decide (b): merge the pieces of every row (fp64), run the accept test at
-//     every draft position (fp64, wave ballot -> first rejection k) and write
-//     the sequence's decision record.
+//   decide (b): merge the pieces of the rows the accept tests read (fp64),
+//     run the accept test at every draft position (fp64, wave ballot -> first
+//     rejection k) and write the sequence's decision record.
 //   residual mass (b, s), Saguaro with eps > 0 only: the residual weight sum
 //     over a few 2048-logit tiles of row pair k, which the eps clamp needs.
 //   sample (b, s): per-tile sums of the sampling weights over a few tiles of
-//     row pair k (or target row gamma after a full acceptance).
-//   refine (b): locate the tile holding u * total (fp64 scan over the tile
-//     sums, token order), rescan it (fp64 prefix over the same per-lane fp32
-//     sums) and write the outputs.
+//     row pair k, or of target row gamma after a full acceptance (the bonus
+//     draw, each tile with its own offset, so it needs no row normaliser).
+//   draw (b): locate the tile holding u * total (fp64 scan over the tile
+//     sums, token order) and rescan it (fp64 prefix over the same per-lane
+//     fp32 sums): the drawn token.
+//   final (b): check target row gamma (read by the bonus draw only, hence
+//     streamed last) and write the outputs.
 //
 // Hand-off between work-groups uses 64-bit slots that are 0 when empty: a
 // producer stores ~bits(value) with one device-coherent store, a consumer
 // polls (bounded) until the slot is nonzero and clears it after use, so the
-// workspace is all zero again when a call ends (decision records aside).
-// No item waits for anything but items of the same sequence that come
-// earlier in the launch order.
+// workspace is all zero again when a call ends.  No item waits for anything
+// but items of the same sequence that come earlier in the launch order.
 //
-// Default launch: one kernel whose blocks run the items in steps, step t
-// holding the stream items of sequence t, then the decision of sequence
-// t - LD, the sampling items of t - LB and the refine item of t - LR.  A
-// sequence's later items thus start while other sequences stream, and its
-// re-read of row pair k comes from the 256 MB last-level cache.  Work-groups
-// are dispatched in block order, so the smallest unfinished block has every
-// item it waits for finished and can always run; a wait that still times out
-// sets the error word and gives up instead of hanging.
+// Default launch: one kernel whose blocks run the items in steps (see the
+// launch order below): the stream items of sequence t, then the later items
+// of earlier sequences, so that a sequence's decision, sampling and draw run
+// while other sequences stream; the target rows gamma, which no decision
+// waits for, come last.  Work-groups are dispatched in block order, so the
+// smallest unfinished block has every item it waits for finished and can
+// always run; a wait that still times out sets the error word and gives up
+// instead of hanging.
 #include "common.h"
 #include "spec_verify.h"
 
@@ -62,9 +64,10 @@ enum : int { kModeTarget = 0, kModeResidual = 1, kModeSaguaro = 2, kModeSaguaroE
 #ifndef SV_FUSED
 #define SV_FUSED 1
 #endif
-// Lags of the decision, residual-mass, sampling and refine items behind their
-// sequence's stream items, in thousandths of a round (one round = as many
-// stream items as the GPU holds at once); each is added to the one before.
+// Lags of the decision, residual-mass, sampling, draw and final items behind
+// their sequence's stream items, in thousandths of a round (one round = as
+// many stream items as the GPU holds at once); each is added to the one
+// before (the final item's to the lag of target row gamma).
 #ifndef SV_LAG_DECIDE
 #define SV_LAG_DECIDE 1400
 #endif
@@ -74,8 +77,11 @@ enum : int { kModeTarget = 0, kModeResidual = 1, kModeSaguaro = 2, kModeSaguaroE
 #ifndef SV_LAG_SAMPLE
 #define SV_LAG_SAMPLE 1000
 #endif
-#ifndef SV_LAG_REFINE
-#define SV_LAG_REFINE 800
+#ifndef SV_LAG_DRAW
+#define SV_LAG_DRAW 800
+#endif
+#ifndef SV_LAG_FINAL
+#define SV_LAG_FINAL 200
 #endif
 #ifndef SV_SAMPLE_NT
 #define SV_SAMPLE_NT 0
@@ -342,12 +348,71 @@ __device__ __forceinline__ void stream_item(const VerifyArgs& a, int b, int r, i
   }
 }
 
+// The outputs of an invalid sequence (threads 0..gamma).
+__device__ __forceinline__ void write_invalid(const VerifyArgs& a, int b, int tid) {
+  const int g = a.gamma;
+  if (tid <= g) a.out_tokens[(int64_t)b * (g + 1) + tid] = -1;
+  if (tid == 0) {
+    a.out_acc[b] = -1;
+    if (a.out_first_reject) a.out_first_reject[b] = -1;
+    if (a.out_mask) a.out_mask[b] = 0;
+    if (a.out_len) a.out_len[b] = a.in_len ? a.in_len[b] : 0;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Decision of one sequence.
+
+// Merge the chunk pieces of row r of sequence b within a 16-lane group (lane
+// `sub` takes pieces sub, sub + 16, ...): M = the integer ceiling of
+// max_c v_c, z = sum_c 2^(v_c - M) (fp64), mr = the row's largest raw logit.
+// Waits for every piece (both words of a piece together) and clears them once
+// read.  Every lane of the group returns the row's values.
+__device__ void merge_row(const VerifyArgs& a, int b, int r, int sub, double& M, double& z, float& mr) {
+  const int64_t p0 = ((int64_t)b * (2 * a.gamma + 1) + r) * a.nc;
+  M = -INFINITY;
+  z = 0.0;
+  mr = -INFINITY;
+  double v0 = -INFINITY;   // the first piece stays in a register, later ones are read again
+  for (int c = sub; c < a.nc; c += 16) {
+    uint64_t wv = ld_dev_u64(a.part + p0 + c);
+    unsigned wm = __hip_atomic_load(a.mraw + p0 + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    unsigned polls = 0;
+    while ((wv == 0ull || wm == 0u) && !give_up(a, polls)) {
+      if (wv == 0ull) wv = ld_dev_u64(a.part + p0 + c);
+      if (wm == 0u) wm = __hip_atomic_load(a.mraw + p0 + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    const double v = slot_value(wv);
+    mr = fmaxf(mr, __uint_as_float(~wm));
+    if (c == sub) v0 = v;
+    M = fmax(M, v);
+  }
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) {
+    M = fmax(M, __shfl_xor(M, o, 16));
+    mr = fmaxf(mr, __shfl_xor(mr, o, 16));
+  }
+  M = ceil(M);
+  for (int c = sub; c < a.nc; c += 16) {
+    const double v = c == sub ? v0 : slot_value(ld_dev_u64(a.part + p0 + c));
+    if (v != -INFINITY) z += exp2(v - M);   // a NaN piece stays NaN
+    slot_clear(a.part + p0 + c);
+    slot_clear32(a.mraw + p0 + c);
+  }
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) z += __shfl_xor(z, o, 16);
+}
+
+// An all -inf row (M = -inf), a +inf logit (M = +inf) or a NaN logit (z =
+// NaN) makes a row bad.
+__device__ __forceinline__ bool row_ok(double M, double z) {
+  return (z > 0.0) && isfinite(z) && isfinite(M);
+}
 
 struct DecideLds {
   double M[128];   // row offsets (integers, log2 units)
   double Z[128];   // row normalisers: sum_j 2^(l_j c_T - M)
+  float mr[128];   // row maxima of the raw logits
   int bad[128];
   int x[64];       // draft tokens, their draft and target logits, accept uniforms
   float ldx[64], ltx[64], ux[64];
@@ -355,18 +420,17 @@ struct DecideLds {
   int k, valid;
 };
 
-// Merge the chunk pieces of every row (16 lanes per row, 12 rows per pass;
-// fp64): Z = sum_c 2^(v_c - M), M = the integer ceiling of max_c v_c.  Then the accept test
-// at every draft position (wave 0, lane i = position i; fp64), the decision
-// record and its flag.  Every piece slot is cleared once read.
+// The rows the accept tests read, draft rows 0..gamma-1 and target rows
+// 0..gamma-1 (16 lanes per row, 12 rows per pass), then the accept test at
+// every draft position (wave 0, lane i = position i; fp64) and the decision
+// record.  Target row gamma is checked by the sequence's final item.  A bad
+// row or token makes the sequence invalid here, with its outputs.
 template <int DT>
 __device__ void decide_item(const VerifyArgs& a, int b, DecideLds& sh) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int g = a.gamma, R = 2 * g + 1;
-  const int64_t base = (int64_t)b * R * a.nc;
-  const int sub = lane & 15;
+  const int g = a.gamma, Rd = 2 * g, R = 2 * g + 1;
   // Wave 1 gathers the draft tokens' logits and the uniforms (independent of
-  // the row pieces) while waves 0, 2 and 3 merge the pieces, 12 rows a pass.
+  // the row pieces) while waves 0, 2 and 3 merge the pieces.
   if (wave == 1) {
     if (lane < g) {
       const int x = a.tokens[(int64_t)b * g + lane];
@@ -381,77 +445,46 @@ __device__ void decide_item(const VerifyArgs& a, int b, DecideLds& sh) {
       sh.ux[lane] = a.u_acc[(int64_t)b * g + lane];
     }
   } else {
-    for (int r0 = 0; r0 < R; r0 += 12) {
+    for (int r0 = 0; r0 < Rd; r0 += 12) {
       const int r = r0 + (wave == 0 ? 0 : wave - 1) * 4 + (lane >> 4);
-      double M = -INFINITY, z = 0.0;
-      float mr = -INFINITY;
-      if (r < R) {
-        // Pieces c = sub, sub + 16, ...: wait for each, take the maximum; the
-        // first stays in a register, later ones are read again for the sum.
-        const int64_t p0 = base + (int64_t)r * a.nc;
-        double v0 = -INFINITY;
-        for (int c = sub; c < a.nc; c += 16) {
-          // Both words of the piece are requested together.
-          uint64_t wv = ld_dev_u64(a.part + p0 + c);
-          unsigned wm = __hip_atomic_load(a.mraw + p0 + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          unsigned polls = 0;
-          while ((wv == 0ull || wm == 0u) && !give_up(a, polls)) {
-            if (wv == 0ull) wv = ld_dev_u64(a.part + p0 + c);
-            if (wm == 0u) wm = __hip_atomic_load(a.mraw + p0 + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          }
-          const double v = slot_value(wv);
-          mr = fmaxf(mr, __uint_as_float(~wm));
-          if (c == sub) v0 = v;
-          M = fmax(M, v);
+      if (r < Rd) {
+        double M, z;
+        float mr;
+        merge_row(a, b, r, lane & 15, M, z, mr);
+        if ((lane & 15) == 0) {
+          sh.M[r] = M;
+          sh.Z[r] = z;
+          sh.mr[r] = mr;
+          sh.bad[r] = !row_ok(M, z);
         }
-#pragma unroll
-        for (int o = 8; o > 0; o >>= 1) {
-          M = fmax(M, __shfl_xor(M, o, 16));
-          mr = fmaxf(mr, __shfl_xor(mr, o, 16));
-        }
-        M = ceil(M);
-        for (int c = sub; c < a.nc; c += 16) {
-          const double v = c == sub ? v0 : slot_value(ld_dev_u64(a.part + p0 + c));
-          if (v != -INFINITY) z += exp2(v - M);   // a NaN piece stays NaN
-          slot_clear(a.part + p0 + c);
-          slot_clear32(a.mraw + p0 + c);
-        }
-      }
-#pragma unroll
-      for (int o = 8; o > 0; o >>= 1) z += __shfl_xor(z, o, 16);
-      if (r < R && sub == 0) {
-        // An all -inf row (M = -inf), a +inf logit (M = +inf) or a NaN logit
-        // (z = NaN) is bad.
-        const int ok = (z > 0.0) && isfinite(z) && isfinite(M);
-        sh.M[r] = M;
-        sh.Z[r] = z;
-        sh.bad[r] = !ok;
-        if (ok && a.diag.row_max) a.diag.row_max[(int64_t)b * R + r] = (double)mr * a.invT;
       }
     }
   }
   __syncthreads();
-  if (a.diag.row_logZ)
-    for (int r = tid; r < R; r += kThreads)
-      if (!sh.bad[r]) a.diag.row_logZ[(int64_t)b * R + r] = sh.M[r] * 0.69314718055994530942 + log(sh.Z[r]);
+  for (int r = tid; r < Rd; r += kThreads) {
+    if (sh.bad[r]) continue;
+    if (a.diag.row_max) a.diag.row_max[(int64_t)b * R + r] = (double)sh.mr[r] * a.invT;
+    if (a.diag.row_logZ) a.diag.row_logZ[(int64_t)b * R + r] = sh.M[r] * 0.69314718055994530942 + log(sh.Z[r]);
+  }
 
   if (wave == 0) {
     int rows_bad = 0;
-    for (int r = lane; r < R; r += 64) rows_bad |= sh.bad[r];
+    for (int r = lane; r < Rd; r += 64) rows_bad |= sh.bad[r];
     rows_bad = __ballot(rows_bad) != 0;
     int acc = 0, bad = 0;
     if (lane < g) {
       const int x = sh.x[lane];
       bad = (x < 0 || x >= a.V);
       if (!bad && !rows_bad) {
-        const double px = exp2((double)sh.ldx[lane] * a.cTd - sh.M[lane]) / sh.Z[lane];
-        const double qx = exp2((double)sh.ltx[lane] * a.cTd - sh.M[g + lane]) / sh.Z[g + lane];
+        // p(x) = pn / Zd and q(x) = qn / Zt; the ratio with one division.
+        const double pn = exp2((double)sh.ldx[lane] * a.cTd - sh.M[lane]);
+        const double qn = exp2((double)sh.ltx[lane] * a.cTd - sh.M[g + lane]);
         double ratio;
-        if (px > 0.0) ratio = fmin(1.0, qx / px);
-        else ratio = qx > 0.0 ? 1.0 : 0.0;
+        if (pn > 0.0) ratio = fmin(1.0, (qn * sh.Z[lane]) / (pn * sh.Z[g + lane]));
+        else ratio = qn > 0.0 ? 1.0 : 0.0;
         acc = (double)sh.ux[lane] < ratio;
-        if (a.diag.px) a.diag.px[(int64_t)b * g + lane] = px;
-        if (a.diag.qx) a.diag.qx[(int64_t)b * g + lane] = qx;
+        if (a.diag.px) a.diag.px[(int64_t)b * g + lane] = pn / sh.Z[lane];
+        if (a.diag.qx) a.diag.qx[(int64_t)b * g + lane] = qn / sh.Z[g + lane];
       }
     }
     const uint64_t mask = __ballot(acc);
@@ -465,16 +498,7 @@ __device__ void decide_item(const VerifyArgs& a, int b, DecideLds& sh) {
   __syncthreads();
 
   const int k = sh.k;
-  const int64_t orow = (int64_t)b * (g + 1);
-  if (!sh.valid) {
-    if (tid <= g) a.out_tokens[orow + tid] = -1;
-    if (tid == 0) {
-      a.out_acc[b] = -1;
-      if (a.out_first_reject) a.out_first_reject[b] = -1;
-      if (a.out_mask) a.out_mask[b] = 0;
-      if (a.out_len) a.out_len[b] = a.in_len ? a.in_len[b] : 0;
-    }
-  }
+  if (!sh.valid) write_invalid(a, b, tid);
   if (tid == 0) {
     SeqRec rec;
     rec.mask = sh.mask;
@@ -485,11 +509,11 @@ __device__ void decide_item(const VerifyArgs& a, int b, DecideLds& sh) {
     rec.Mt = 0.f;
     rec.K_hi = rec.K_lo = 0.f;
     rec.Zt = 1.0;
-    if (sh.valid) {
+    if (sh.valid && k < g) {   // the bonus draw (k == gamma) offsets each tile on its own
       const double Mt = sh.M[g + k];
       rec.Mt = (float)Mt;   // exact below 2^24; otherwise Zt absorbs the rounding
       rec.Zt = ldexp(sh.Z[g + k], (int)fmin(fmax(Mt - (double)rec.Mt, -2000.0), 2000.0));
-      const double K = k < g ? (Mt - sh.M[k]) + log2(sh.Z[g + k] / sh.Z[k]) : 0.0;
+      const double K = (Mt - sh.M[k]) + log2(sh.Z[g + k] / sh.Z[k]);
       rec.K_hi = (float)K;
       rec.K_lo = (float)(K - (double)rec.K_hi);
     }
@@ -612,13 +636,22 @@ __device__ __forceinline__ void draw_rows(const VerifyArgs& a, int b, int k, con
   trow = row_ptr<DT>(a, b, a.gamma + k);
 }
 
+// Integer offset of a tile of target logits for the bonus draw (log2 units):
+// the ceiling of its largest logit times c_T; 0 for an all -inf tile.
+__device__ __forceinline__ float tile_offset(float bm, float c_hi) {
+  const float bl = bm * c_hi;
+  return bl > -1.0e30f ? ceilf(fminf(bl, 1.0e30f)) : 0.f;
+}
+
 // Tile sums of the weights over tiles [t0, t0 + N) (clipped to ntile): tw[i]
 // (fp64, identical in every thread) and, last, the residual total.  The loads
 // of G tiles are in flight together (all N for packed bf16 rows, whose raw
-// words take half the registers of floats).
+// words take half the registers of floats).  In target mode (the bonus draw)
+// every tile gets its own integer offset mt[i] (its weights are
+// 2^(lt_j c_T - mt[i])), so no row normaliser is needed.
 template <int DT, bool VEC, int MODE, int N = kTilesPerItem>
 __device__ __forceinline__ void tile_sums(const VerifyArgs& a, int b, const SampleCoef& cf, int k,
-                                          int t0, double (&tw)[N + 1], double* lds_d) {
+                                          int t0, double (&tw)[N + 1], float (&mt)[N], double* lds_d) {
   constexpr int G = (DT == kBF16 && VEC) ? N : (N >= 2 ? 2 : 1);
   static_assert(N % G == 0, "tile groups must divide the item");
   const void *drow, *trow;
@@ -635,12 +668,32 @@ __device__ __forceinline__ void tile_sums(const VerifyArgs& a, int b, const Samp
       load_raw<DT, VEC, kSampleNT>(trow, j0, a.V, rt[i]);
       if constexpr (MODE != kModeTarget) load_raw<DT, VEC, kSampleNT>(drow, j0, a.V, rd[i]);
     }
+    float off[G];
+    if constexpr (MODE == kModeTarget) {
+#pragma unroll
+      for (int i = 0; i < G; ++i) {
+        float lt[8];
+        unpack<DT, VEC>(rt[i], lt);
+        float m = lt[0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) m = fmaxf(m, lt[e]);
+        off[i] = m;
+      }
+      block_max_n<G>(off, reinterpret_cast<float*>(lds_d));
+#pragma unroll
+      for (int i = 0; i < G; ++i) off[i] = tile_offset(off[i], cf.c_hi);
+    }
 #pragma unroll
     for (int i = 0; i < G; ++i) {
       float ld[8], lt[8], w[8], r[8];
       unpack<DT, VEC>(rt[i], lt);
       if constexpr (MODE != kModeTarget) unpack<DT, VEC>(rd[i], ld);
-      sample_weights<DT, MODE, false>(ld, lt, cf, w, r);
+      SampleCoef c = cf;
+      if constexpr (MODE == kModeTarget) {
+        c.Mt = off[i];
+        mt[g0 + i] = off[i];
+      }
+      sample_weights<DT, MODE, false>(ld, lt, c, w, r);
       float ws = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -654,6 +707,13 @@ __device__ __forceinline__ void tile_sums(const VerifyArgs& a, int b, const Samp
   }
   tw[N] = (double)rs;
   block_sum_n<N + 1>(tw, lds_d);
+}
+
+// A tile's slot value: the plain sum, or in target mode log2 of it with the
+// tile's offset added (-inf for an empty tile).
+__device__ __forceinline__ double tile_slot_value(int mode, double sum, float off) {
+  if (mode != kModeTarget) return sum;
+  return sum > 0.0 ? (double)off + log2(sum) : (sum == 0.0 ? -INFINITY : sum);
 }
 
 // eps * (residual mass) for Saguaro eps > 0, from the residual-mass items'
@@ -673,7 +733,8 @@ __device__ void mass_item(const VerifyArgs& a, int b, int s, double* lds_d) {
   const SeqRec rec = wait_rec<true>(a, b);
   if (!rec.valid || rec.mode != kModeSaguaroEps) return;
   double tw[kTilesPerItem + 1];
-  tile_sums<DT, VEC, kModeResidual>(a, b, coef_of(a, rec, 0.f), rec.k, s * kTilesPerItem, tw, lds_d);
+  float mt[kTilesPerItem];
+  tile_sums<DT, VEC, kModeResidual>(a, b, coef_of(a, rec, 0.f), rec.k, s * kTilesPerItem, tw, mt, lds_d);
   if (threadIdx.x == 0) slot_put(a.mass + (int64_t)b * a.nt + s, tw[kTilesPerItem]);
 }
 
@@ -687,39 +748,58 @@ __device__ void sample_item(const VerifyArgs& a, int b, int s, double* lds_d) {
   with_mode(rec.mode, [&](auto m) {
     constexpr int MODE = decltype(m)::value;
     double tw[kTilesPerItem + 1];
-    tile_sums<DT, VEC, MODE>(a, b, cf, rec.k, t0, tw, lds_d);
+    float mt[kTilesPerItem];
+    tile_sums<DT, VEC, MODE>(a, b, cf, rec.k, t0, tw, mt, lds_d);
     if (threadIdx.x == 0) {
 #pragma unroll
       for (int i = 0; i < kTilesPerItem; ++i)
-        if (t0 + i < a.ntile) slot_put(a.tiles + (int64_t)b * a.ntile + t0 + i, tw[i]);
+        if (t0 + i < a.ntile)
+          slot_put(a.tiles + (int64_t)b * a.ntile + t0 + i, tile_slot_value(MODE, tw[i], mt[i]));
       if (MODE == kModeSaguaro) slot_put(a.rsum + (int64_t)b * a.nt + s, tw[kTilesPerItem]);
     }
   });
 }
 
 // ---------------------------------------------------------------------------
-// Refine item.
+// Draw item.
 
-struct RefineLds {
+struct DrawLds {
   double lds_d[kWaves * (kTilesPerItem + 1)];
   int lds_i[kWaves];
-  int tile;
-  double off, lane_off, lo, hi;
+  int tile, y, e;   // chosen tile, drawn token, tile units = 2^e draw units
+  double off, lane_off, lo, hi, Mp;
   float w8[kUnit];
-  int y;
 };
 
 __device__ __forceinline__ double tile_value(const uint64_t* tiles, int t) {
   return slot_value(ld_dev_u64(tiles + t));
 }
 
-// Locate the tile holding u * S (S = sum of the tile sums) by an fp64 scan
-// over the tile sums in token order; returns S, sets sh.tile and sh.off.
-__device__ double locate_tile(const uint64_t* tiles, int ntile, double u, RefineLds& sh, double& target) {
+// Target-mode tile values hold v_t = offset + log2(sum): replace each by the
+// sum in draw units, 2^(v_t - Mp) with Mp the integer ceiling of the largest
+// v_t, in place (the slots belong to the draw now).  Sets sh.Mp.
+__device__ void tiles_to_linear(uint64_t* tiles, int ntile, DrawLds& sh) {
+  const int tid = threadIdx.x;
+  float m = -INFINITY;   // an upper bound to within float rounding is all Mp needs
+  for (int t = tid; t < ntile; t += kThreads) m = fmaxf(m, (float)tile_value(tiles, t));
+  m = block_max(m, reinterpret_cast<float*>(sh.lds_d));
+  const double Mp = isfinite(m) ? ceil((double)m) + 1.0 : 0.0;
+  for (int t = tid; t < ntile; t += kThreads) {
+    const double v = tile_value(tiles, t);
+    slot_put(tiles + t, v > -INFINITY ? exp2(v - Mp) : 0.0);
+  }
+  if (tid == 0) sh.Mp = Mp;
+  wait_mem();
+  __syncthreads();
+}
+
+// Locate the tile holding u * S (S = sum of the tile values) by an fp64 scan
+// over the tile values in token order; returns S, sets sh.tile and sh.off.
+__device__ double locate_tile(const uint64_t* tiles, int ntile, double u, DrawLds& sh, double& target) {
   const int tid = threadIdx.x;
   if (tid == 0) sh.tile = -1;
   double S = 0.0;
-  if (ntile <= kThreads) {   // one tile sum per thread, loaded once
+  if (ntile <= kThreads) {   // one tile value per thread, loaded once
     const double v = tid < ntile ? tile_value(tiles, tid) : 0.0;
     double tot;
     const double off = block_exclusive_scan(v, sh.lds_d, tot);
@@ -772,20 +852,22 @@ __device__ double locate_tile(const uint64_t* tiles, int ntile, double u, Refine
 }
 
 // Rescan the chosen tile: the same weights and per-lane fp32 sums as its tile
-// sum, fp64 prefix over the lanes.  The lane holding the target (else the last
-// lane with weight) hands its eight weights to thread 0, which walks them in
-// fp64: y = the first token with weight whose running sum passes the target
-// (else the lane's last token with weight).  Sets sh.y, sh.lo = C_{y-1} and
-// sh.hi = C_y (unnormalised).
+// sum, fp64 prefix over the lanes, in tile units (one tile unit is 2^e draw
+// units; e = 0 but for the bonus draw, where it is the tile's offset minus Mp).
+// The lane holding the target (else the last lane with weight) hands its
+// eight weights to thread 0, which walks them in fp64: y = the first token
+// with weight whose running sum passes the target (else the lane's last token
+// with weight).  Sets sh.y, sh.e, sh.lo = C_{y-1} and sh.hi = C_y (draw units).
 template <int DT, bool VEC, int MODE>
 __device__ void rescan_tile(const VerifyArgs& a, int b, int k, const SampleCoef& cf, double target,
-                            RefineLds& sh) {
+                            DrawLds& sh) {
   const int tid = threadIdx.x;
   const int tsel = sh.tile;
   const void *drow, *trow;
   draw_rows<DT>(a, b, k, drow, trow);
   const int64_t j0 = (int64_t)tsel * kTile + (int64_t)tid * kUnit;
   float w[8];
+  int e = 0;
   {
     Raw8<DT, VEC> rd, rt;
     load_raw<DT, VEC>(trow, j0, a.V, rt);
@@ -793,40 +875,49 @@ __device__ void rescan_tile(const VerifyArgs& a, int b, int k, const SampleCoef&
     float ld[8], lt[8], r[8];
     unpack<DT, VEC>(rt, lt);
     if constexpr (MODE != kModeTarget) unpack<DT, VEC>(rd, ld);
-    sample_weights<DT, MODE, false>(ld, lt, cf, w, r);
+    SampleCoef c = cf;
+    if (MODE == kModeTarget && k == a.gamma) {   // the bonus draw: the tile's own offset
+      float m[1] = {lt[0]};
+#pragma unroll
+      for (int i = 1; i < 8; ++i) m[0] = fmaxf(m[0], lt[i]);
+      block_max_n<1>(m, reinterpret_cast<float*>(sh.lds_d));
+      c.Mt = tile_offset(m[0], cf.c_hi);
+      e = (int)fmin(fmax((double)c.Mt - sh.Mp, -2000.0), 2000.0);
+    }
+    sample_weights<DT, MODE, false>(ld, lt, c, w, r);
   }
   float ws = 0.f;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) ws += w[e];
+  for (int i = 0; i < 8; ++i) ws += w[i];
   double tile_tot;
   const double off = block_exclusive_scan((double)ws, sh.lds_d, tile_tot);
-  const double tgt = target - sh.off;
+  const double tgt = ldexp(target - sh.off, -e);   // in tile units
   const int hit = (ws > 0.f && off <= tgt && tgt < off + (double)ws) ? tid : INT_MAX;
   int owner = block_min_int(hit, sh.lds_i);
   if (owner == INT_MAX) owner = -block_min_int(ws > 0.f ? -tid : 1, sh.lds_i);   // last lane with weight
   if (tid == owner) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sh.w8[e] = w[e];
+    for (int i = 0; i < 8; ++i) sh.w8[i] = w[i];
     sh.lane_off = off;
   }
   __syncthreads();
   if (tid == 0) {
-    if (owner < 0) {   // no weight in the tile (not reached: its tile sum was positive)
+    sh.e = e;
+    if (owner < 0) {   // no weight in the tile (not reached: its tile value was positive)
       sh.y = (int)min<int64_t>(a.V - 1, (int64_t)tsel * kTile + kTile - 1);
-      sh.lo = sh.hi = sh.off + tile_tot;
+      sh.lo = sh.hi = sh.off + ldexp(tile_tot, e);
     } else {
-      double run = sh.off + sh.lane_off;
-      const double tg = target;
+      double run = sh.lane_off;
       int idx = -1, last = -1;
       double lo_last = run, lo = run;
-      for (int e = 0; e < 8; ++e) {
-        const double we = (double)sh.w8[e];
+      for (int i = 0; i < 8; ++i) {
+        const double we = (double)sh.w8[i];
         if (we > 0.0) {
-          if (idx < 0 && tg < run + we) {
-            idx = e;
+          if (idx < 0 && tgt < run + we) {
+            idx = i;
             lo = run;
           }
-          last = e;
+          last = i;
           lo_last = run;
         }
         run += we;
@@ -836,32 +927,36 @@ __device__ void rescan_tile(const VerifyArgs& a, int b, int k, const SampleCoef&
         lo = lo_last;
       }
       sh.y = (int)((int64_t)tsel * kTile + (int64_t)owner * kUnit + idx);
-      sh.lo = lo;
-      sh.hi = lo + (double)sh.w8[idx];
+      sh.lo = sh.off + ldexp(lo, e);
+      sh.hi = sh.off + ldexp(lo + (double)sh.w8[idx], e);
     }
   }
   __syncthreads();
 }
 
-// pi(y)'s weight with the precise residual (thread 0).
+// pi(y)'s weight in draw units, with the precise residual (thread 0).
 template <int DT>
-__device__ double precise_weight(const VerifyArgs& a, int b, int k, int mode, const SampleCoef& cf, int y) {
+__device__ double precise_weight(const VerifyArgs& a, int b, int k, int mode, const SampleCoef& cf, int y,
+                                 const DrawLds& sh) {
   const void *drow, *trow;
   draw_rows<DT>(a, b, k, drow, trow);
   const float lt = load_one<DT>(trow, y);
   const float ld = mode == kModeTarget ? 0.f : load_one<DT>(drow, y);
+  SampleCoef c = cf;
+  if (mode == kModeTarget && k == a.gamma) c.Mt = (float)(sh.Mp + sh.e);   // the tile's offset
   float w = 0.f, r;
-  with_mode(mode, [&](auto m) { w = weight_one<DT, decltype(m)::value, true>(ld, lt, cf, r); });
-  return (double)w;
+  with_mode(mode, [&](auto m) { w = weight_one<DT, decltype(m)::value, true>(ld, lt, c, r); });
+  return ldexp((double)w, sh.e);
 }
 
 // Recompute every tile sum of a sequence in `mode`, the residual or q_k (a
 // zero Saguaro normaliser falls back to the residual, a zero residual mass to
-// q_k; degenerate inputs only).  One logit at a time, in the order and with
-// the weights the rescan uses, so its per-lane fp32 sums match.
+// q_k, k < gamma, whose offset Mt is the record's; degenerate inputs only).
+// One logit at a time, with the weights and order the rescan uses, so its
+// per-lane fp32 sums match.
 template <int DT>
 __device__ void recompute_tiles(const VerifyArgs& a, int b, int k, int mode, const SampleCoef& cf,
-                                RefineLds& sh) {
+                                DrawLds& sh) {
   uint64_t* tiles = a.tiles + (int64_t)b * a.ntile;
   const void *drow, *trow;
   draw_rows<DT>(a, b, k, drow, trow);
@@ -886,69 +981,120 @@ __device__ void recompute_tiles(const VerifyArgs& a, int b, int k, int mode, con
   __syncthreads();
 }
 
-template <int DT, bool VEC>
-__device__ void refine_item(const VerifyArgs& a, int b, RefineLds& sh) {
-  const int tid = threadIdx.x;
-  const SeqRec rec = wait_rec<false>(a, b);
-  if (rec.valid) {
-    const int g = a.gamma, k = rec.k;
-    const int64_t orow = (int64_t)b * (g + 1);
-    uint64_t* tiles = a.tiles + (int64_t)b * a.ntile;
-    const float epsS = rec.mode == kModeSaguaroEps ? eps_clamp(a, b, sh.lds_d) : 0.f;
-    const SampleCoef cf = coef_of(a, rec, epsS);
-    int mode = rec.mode;
-    for (int t = tid; t < a.ntile; t += kThreads) (void)poll(a, tiles + t);
-    double rtot = 0.0;   // residual mass (relative to Mt) when it differs from the tile total
-    if (mode == kModeSaguaro || mode == kModeSaguaroEps) {
-      uint64_t* rs = (mode == kModeSaguaro ? a.rsum : a.mass) + (int64_t)b * a.nt;
-      for (int i = tid; i < a.nt; i += kThreads) rtot += slot_value(poll(a, rs + i));
-    }
-    rtot = uni(block_sum(rtot, sh.lds_d));   // also orders the polls before the reads below
+// The drawn token of a sequence: the 64-bit word at byte 8 of its count line,
+// stored as a complement (0 = not drawn yet).
+__device__ __forceinline__ uint64_t* drawn_slot(const VerifyArgs& a, int b) {
+  return reinterpret_cast<uint64_t*>(a.flag + (int64_t)b * kFlagStride + 2);
+}
 
-    const double u = (double)a.u_smp[orow + k];
-    double target = 0.0;
-    double S = uni(locate_tile(tiles, a.ntile, u, sh, target));
+// The draw at the stopping position: tile values, locate, rescan.  The token
+// goes to the sequence's drawn slot, the diagnostics out.  Clears the tile and
+// residual-sum slots once read.
+template <int DT, bool VEC>
+__device__ void draw_item(const VerifyArgs& a, int b, DrawLds& sh) {
+  const int tid = threadIdx.x;
+  const SeqRec rec = wait_rec<true>(a, b);
+  if (!rec.valid) return;
+  const int g = a.gamma, k = rec.k;
+  uint64_t* tiles = a.tiles + (int64_t)b * a.ntile;
+  const float epsS = rec.mode == kModeSaguaroEps ? eps_clamp(a, b, sh.lds_d) : 0.f;
+  const SampleCoef cf = coef_of(a, rec, epsS);
+  int mode = rec.mode;
+  for (int t = tid; t < a.ntile; t += kThreads) (void)poll(a, tiles + t);
+  double rtot = 0.0;   // residual mass (relative to Mt) when it differs from the tile total
+  if (mode == kModeSaguaro || mode == kModeSaguaroEps) {
+    uint64_t* rs = (mode == kModeSaguaro ? a.rsum : a.mass) + (int64_t)b * a.nt;
+    for (int i = tid; i < a.nt; i += kThreads) rtot += slot_value(poll(a, rs + i));
+  }
+  rtot = uni(block_sum(rtot, sh.lds_d));   // also orders the polls before the reads below
+
+  const double u = (double)a.u_smp[(int64_t)b * (g + 1) + k];
+  double target = 0.0, S = 0.0;
+  if (tid == 0) sh.Mp = 0.0;
+  // A zero Saguaro normaliser falls back to the residual, a zero residual mass
+  // to q_k (degenerate inputs only); one pass per mode.
+  if (mode == kModeTarget) tiles_to_linear(tiles, a.ntile, sh);   // the bonus draw
+  for (;;) {
+    S = uni(locate_tile(tiles, a.ntile, u, sh, target));
     target = uni(target);
     if (mode == kModeResidual) rtot = S;
-    while (!(S > 0.0) && mode != kModeTarget) {
-      mode = mode == kModeResidual ? kModeTarget : kModeResidual;
-      recompute_tiles<DT>(a, b, k, mode, cf, sh);
-      S = uni(locate_tile(tiles, a.ntile, u, sh, target));
-      target = uni(target);
-      if (mode == kModeResidual) rtot = S;
-    }
-    with_mode(mode, [&](auto m) { rescan_tile<DT, VEC, decltype(m)::value>(a, b, k, cf, target, sh); });
-    const int y = sh.y;
-
-    if (tid <= g) {
-      int tok = -1;
-      if (tid < k) tok = a.tokens[(int64_t)b * g + tid];
-      else if (tid == k) tok = y;
-      a.out_tokens[orow + tid] = tok;
-    }
-    if (tid == 0) {
-      a.out_acc[b] = k;
-      if (a.out_first_reject) a.out_first_reject[b] = k < g ? k : -1;
-      if (a.out_mask) a.out_mask[b] = rec.mask;
-      if (a.out_len) a.out_len[b] = (a.in_len ? a.in_len[b] : 0) + k + 1;
-      if (a.diag.resid_mass) a.diag.resid_mass[b] = k < g ? rtot / rec.Zt : 0.0;
-      if (a.diag.token_prob) a.diag.token_prob[b] = precise_weight<DT>(a, b, k, mode, cf, y) / S;
-      if (a.diag.cdf_lo) a.diag.cdf_lo[b] = sh.lo / S;
-      if (a.diag.cdf_hi) a.diag.cdf_hi[b] = sh.hi / S;
-    }
-    // Every slot of the sequence has been read: clear them for the next call.
-    __syncthreads();
-    for (int t = tid; t < a.ntile; t += kThreads) slot_clear(tiles + t);
-    if (rec.mode == kModeSaguaro)
-      for (int i = tid; i < a.nt; i += kThreads) slot_clear(a.rsum + (int64_t)b * a.nt + i);
-    if (rec.mode == kModeSaguaroEps)
-      for (int i = tid; i < a.nt; i += kThreads) slot_clear(a.mass + (int64_t)b * a.nt + i);
+    if (S > 0.0 || mode == kModeTarget) break;
+    mode = mode == kModeResidual ? kModeTarget : kModeResidual;
+    recompute_tiles<DT>(a, b, k, mode, cf, sh);
   }
-  // Once every residual-mass and sampling item is done with the decision
-  // record, clear it and the count.
+  with_mode(mode, [&](auto m) { rescan_tile<DT, VEC, decltype(m)::value>(a, b, k, cf, target, sh); });
+  if (tid == 0) {
+    const int y = sh.y;
+    if (a.diag.resid_mass) a.diag.resid_mass[b] = k < g ? rtot / rec.Zt : 0.0;
+    if (a.diag.token_prob) a.diag.token_prob[b] = precise_weight<DT>(a, b, k, mode, cf, y, sh) / S;
+    if (a.diag.cdf_lo) a.diag.cdf_lo[b] = sh.lo / S;
+    if (a.diag.cdf_hi) a.diag.cdf_hi[b] = sh.hi / S;
+    st_dev_u64(drawn_slot(a, b), ~(uint64_t)(uint32_t)y);
+  }
+  // Every tile and residual-sum slot of the sequence has been read.
+  __syncthreads();
+  for (int t = tid; t < a.ntile; t += kThreads) slot_clear(tiles + t);
+  if (rec.mode == kModeSaguaro)
+    for (int i = tid; i < a.nt; i += kThreads) slot_clear(a.rsum + (int64_t)b * a.nt + i);
+  if (rec.mode == kModeSaguaroEps)
+    for (int i = tid; i < a.nt; i += kThreads) slot_clear(a.mass + (int64_t)b * a.nt + i);
+}
+
+// ---------------------------------------------------------------------------
+// Final item: target row gamma, which only the bonus draw reads and which is
+// therefore streamed last, is checked, and the outputs are written.
+
+struct FinalLds {
+  int ok, y;
+};
+
+template <int DT>
+__device__ void final_item(const VerifyArgs& a, int b, FinalLds& sh) {
+  const int tid = threadIdx.x;
+  const int g = a.gamma, R = 2 * g + 1, r = 2 * g;
+  const SeqRec rec = wait_rec<false>(a, b);
+  if (tid < 16) {
+    double M, z;
+    float mr;
+    merge_row(a, b, r, tid, M, z, mr);
+    if (tid == 0) {
+      const bool ok = row_ok(M, z);
+      sh.ok = ok;
+      if (ok && a.diag.row_max) a.diag.row_max[(int64_t)b * R + r] = (double)mr * a.invT;
+      if (ok && a.diag.row_logZ) a.diag.row_logZ[(int64_t)b * R + r] = M * 0.69314718055994530942 + log(z);
+      if (rec.valid) {
+        uint64_t* ys = drawn_slot(a, b);
+        sh.y = (int)(uint32_t)~poll(a, ys);
+        slot_clear(ys);
+      }
+    }
+  }
+  __syncthreads();
+  if (rec.valid) {   // an invalid decision wrote its outputs already
+    const int k = rec.k;
+    if (!sh.ok) {
+      write_invalid(a, b, tid);
+    } else {
+      const int64_t orow = (int64_t)b * (g + 1);
+      if (tid <= g) {
+        int tok = -1;
+        if (tid < k) tok = a.tokens[(int64_t)b * g + tid];
+        else if (tid == k) tok = sh.y;
+        a.out_tokens[orow + tid] = tok;
+      }
+      if (tid == 0) {
+        a.out_acc[b] = k;
+        if (a.out_first_reject) a.out_first_reject[b] = k < g ? k : -1;
+        if (a.out_mask) a.out_mask[b] = rec.mask;
+        if (a.out_len) a.out_len[b] = (a.in_len ? a.in_len[b] : 0) + k + 1;
+      }
+    }
+  }
+  // Once every other item of the sequence is done with the decision record,
+  // clear it and the count.
   if (tid == 0) {
     unsigned* f = a.flag + (int64_t)b * kFlagStride;
-    const unsigned expect = (unsigned)a.nt * ((a.saguaro && a.eps > 0.f) ? 2u : 1u);
+    const unsigned expect = (unsigned)a.nt * ((a.saguaro && a.eps > 0.f) ? 2u : 1u) + 1u;
     unsigned polls = 0;
     while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < expect &&
            !give_up(a, polls)) {
@@ -961,19 +1107,25 @@ __device__ void refine_item(const VerifyArgs& a, int b, RefineLds& sh) {
 // ---------------------------------------------------------------------------
 // Launch order.
 //
-// Step t holds, in this order: the stream items of sequence t (NS of them),
-// the decision of sequence t - LD, the residual-mass items of t - LM (NM, eps
-// > 0 only), the sampling items of t - LB (NB) and the refine item of t - LR,
-// where each exists; LD <= LM <= LB <= LR.
+// Step t holds, in this order: the stream items of the rows the accept tests
+// read of sequence t (draft and target rows 0..gamma-1), the decision of
+// sequence t - LD, the residual-mass items of t - LM (eps > 0 only), the
+// sampling items of t - LB, the draw of t - LR, the stream items of target row
+// gamma of t - LL and the final item of t - LF, where each exists.  The lags
+// grow in that order, and LL >= B puts every target row gamma after every
+// other row, so the last bytes streamed are ones no decision waits for.
 
-constexpr int kKinds = 5;
-enum : int { kItemStream = 0, kItemDecide = 1, kItemMass = 2, kItemSample = 3, kItemRefine = 4 };
+constexpr int kKinds = 7;
+enum : int {
+  kItemStream = 0, kItemDecide = 1, kItemMass = 2, kItemSample = 3, kItemDraw = 4, kItemLast = 5,
+  kItemFinal = 6
+};
 
 struct Sched {
   int B;
   int lag[kKinds];
   int size[kKinds];
-  int steps;        // B + lag[kItemRefine]
+  int steps;        // B + lag[kItemFinal]
   int64_t total;
 };
 
@@ -995,8 +1147,8 @@ __host__ __device__ inline void sched_decode(const Sched& s, int64_t j, int& kin
     else hi = mid;
   }
   int64_t w = j - sched_offset(s, lo);
-  kind = kItemRefine;
-  b = lo - s.lag[kItemRefine];
+  kind = kItemFinal;
+  b = lo - s.lag[kItemFinal];
   sub = 0;
   for (int i = 0; i < kKinds; ++i) {
     const int bi = lo - s.lag[i];
@@ -1017,7 +1169,8 @@ __host__ __device__ inline void sched_decode(const Sched& s, int64_t j, int& kin
 union ItemLds {
   StreamLds s;
   DecideLds d;
-  RefineLds r;
+  DrawLds r;
+  FinalLds f;
 };
 
 // Compiled for 8 waves per SIMD (64 VGPRs): the stream items need the
@@ -1037,7 +1190,9 @@ void fused_kernel(VerifyArgs a, Sched sc) {
     case kItemDecide: decide_item<DT>(a, b, sh.d); break;
     case kItemMass: mass_item<DT, VEC>(a, b, sub, sh.r.lds_d); break;
     case kItemSample: sample_item<DT, VEC>(a, b, sub, sh.r.lds_d); break;
-    default: refine_item<DT, VEC>(a, b, sh.r); break;
+    case kItemDraw: draw_item<DT, VEC>(a, b, sh.r); break;
+    case kItemLast: stream_item<DT, VEC, U>(a, b, 2 * a.gamma, sub, sh.s); break;
+    default: final_item<DT>(a, b, sh.f); break;
   }
 }
 
@@ -1074,9 +1229,15 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(VerifyArgs a) {
 }
 
 template <int DT, bool VEC>
-__global__ __launch_bounds__(kThreads) void refine_kernel(VerifyArgs a) {
-  __shared__ RefineLds sh;
-  refine_item<DT, VEC>(a, blockIdx.x, sh);
+__global__ __launch_bounds__(kThreads) void draw_kernel(VerifyArgs a) {
+  __shared__ DrawLds sh;
+  draw_item<DT, VEC>(a, blockIdx.x, sh);
+}
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void final_kernel(VerifyArgs a) {
+  __shared__ FinalLds sh;
+  final_item<DT>(a, blockIdx.x, sh);
 }
 
 // ---------------------------------------------------------------------------
@@ -1146,22 +1307,28 @@ static hipError_t resident_groups(int& slots) {
   return hipSuccess;
 }
 
-static Sched make_sched(int B, int NS, int NM, int NB, int slots) {
+// NSm stream items per sequence for the rows the accept tests read, NL for
+// target row gamma, NM residual-mass and NB sampling items.
+static Sched make_sched(int B, int NSm, int NL, int NM, int NB, int slots) {
   Sched s;
   s.B = B;
-  const double spr = (double)slots / (double)NS;   // sequences streamed per round
+  const double spr = (double)slots / (double)(NSm + NL);   // sequences streamed per round
   auto steps = [&](int milli) { return (int)std::lround(spr * milli / 1000.0); };
   s.lag[kItemStream] = 0;
   s.lag[kItemDecide] = steps(SV_LAG_DECIDE);
   s.lag[kItemMass] = s.lag[kItemDecide] + (NM > 0 ? steps(SV_LAG_MASS) : 0);
   s.lag[kItemSample] = s.lag[kItemMass] + steps(SV_LAG_SAMPLE);
-  s.lag[kItemRefine] = s.lag[kItemSample] + steps(SV_LAG_REFINE);
-  s.size[kItemStream] = NS;
+  s.lag[kItemDraw] = s.lag[kItemSample] + steps(SV_LAG_DRAW);
+  s.lag[kItemLast] = std::max(B, s.lag[kItemDraw]);
+  s.lag[kItemFinal] = s.lag[kItemLast] + steps(SV_LAG_FINAL);
+  s.size[kItemStream] = NSm;
   s.size[kItemDecide] = 1;
   s.size[kItemMass] = NM;
   s.size[kItemSample] = NB;
-  s.size[kItemRefine] = 1;
-  s.steps = B + s.lag[kItemRefine];
+  s.size[kItemDraw] = 1;
+  s.size[kItemLast] = NL;
+  s.size[kItemFinal] = 1;
+  s.steps = B + s.lag[kItemFinal];
   s.total = sched_offset(s, s.steps);
   return s;
 }
@@ -1179,7 +1346,7 @@ static hipError_t launch_all(const VerifyArgs& a, hipStream_t st) {
     hipError_t e = resident_groups<DT, VEC>(slots);
     if (e != hipSuccess) return e;
     const bool eps_mode = a.saguaro && a.eps > 0.f;
-    const Sched sc = make_sched(a.B, (2 * a.gamma + 1) * a.nc, eps_mode ? a.nt : 0, a.nt, slots);
+    const Sched sc = make_sched(a.B, 2 * a.gamma * a.nc, a.nc, eps_mode ? a.nt : 0, a.nt, slots);
     hipLaunchKernelGGL((fused_kernel<DT, VEC, SV_STREAM_UNROLL>), dim3((unsigned)sc.total), dim3(kThreads),
                        0, st, a, sc);
     return hipGetLastError();
@@ -1198,7 +1365,8 @@ static hipError_t launch_kernels(const VerifyArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((decide_kernel<DT>), dim3((unsigned)a.B), dim3(kThreads), 0, st, a);
   if (eps_mode) hipLaunchKernelGGL((mass_kernel<DT, VEC>), dim3(nsample), dim3(kThreads), 0, st, a);
   hipLaunchKernelGGL((sample_kernel<DT, VEC>), dim3(nsample), dim3(kThreads), 0, st, a);
-  hipLaunchKernelGGL((refine_kernel<DT, VEC>), dim3((unsigned)a.B), dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL((draw_kernel<DT, VEC>), dim3((unsigned)a.B), dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL((final_kernel<DT>), dim3((unsigned)a.B), dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
@@ -1218,7 +1386,7 @@ static int verify_impl(const void* draft, const void* target, int dtype, const i
   const Layout L = layout(B, gamma, V);
   // Every launch (and the fused kernel's item count) stays within one grid
   // dimension of 2^32 - 1 work-items, with block numbers below 2^31.
-  const int64_t items = (int64_t)B * ((2 * gamma + 1) * L.nc + 2 * L.nt + 2);
+  const int64_t items = (int64_t)B * ((2 * gamma + 1) * L.nc + 2 * L.nt + 3);
   if (items * kThreads > (int64_t)UINT_MAX || items > (int64_t)INT_MAX) return SPEC_EINVAL;
   if (!ws || ws_bytes < L.total) return SPEC_EWORKSPACE;
 
