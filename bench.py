@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--mode", choices=("residual", "saguaro"), default="residual")
     ap.add_argument("--eps", type=float, default=0.0)
+    ap.add_argument("--predict", action="store_true",
+                    help="each step also predicts outcomes (draft top-3 per position, hits)")
     ap.add_argument("--sets", type=int, default=0,
                     help="input sets to rotate through (0: enough for > 1 GB)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -119,6 +121,8 @@ def main():
     B, g, V = batch.B, batch.gamma, batch.V
     dt_code = R.SPEC_BF16 if batch.dtype == "bf16" else R.SPEC_F32
     bytes_alg = R.bytes_algorithmic(B, g, V, dt_code)
+    if args.predict:   # draft row gamma, which only the prediction reads
+        bytes_alg += B * V * (2 if batch.dtype == "bf16" else 4)
     nsets = args.sets or max(1, -(-(1 << 30) // max(bytes_alg, 1)) + (1 if bytes_alg < (1 << 30) else 0))
 
     def dev_logits(a):
@@ -136,14 +140,20 @@ def main():
     out = R.alloc_outputs(B, g, dev)
     ws = R.new_workspace(R.spec_workspace_bytes(B, g, V, dt_code), dev)
     stream = torch.cuda.current_stream(dev)
+    pws = R.new_workspace(R.spec_predict_workspace_bytes(B, g, V, dt_code), dev) if args.predict else None
+    pout = None
 
     def call(i):
+        nonlocal pout
         d, t = sets[i % nsets]
         if args.mode == "residual":
             R.spec_verify(d, t, tok, ua, us, batch.T, out=out, workspace=ws, stream=stream)
         else:
             R.spec_verify_saguaro(d, t, tok, ua, us, batch.T, out=out, workspace=ws, stream=stream,
                                   eps=args.eps)
+        if args.predict:
+            pout = R.spec_predict_outcomes(d, out.accepted, out.tokens, out=pout, workspace=pws,
+                                           stream=stream)
 
     for i in range(args.warmup):
         call(i)
@@ -181,7 +191,8 @@ def main():
                    "logits": batch.dtype, "mode": args.mode, "eps": args.eps,
                    "input_sets": nsets, "alpha_target": [float(batch.alpha_target.min()),
                                                          float(batch.alpha_target.max())],
-                   "mean_accepted": float(acc.mean())},
+                   "mean_accepted": float(acc.mean()), "predict": bool(args.predict),
+                   **({"hit_rate": float(pout.hit.float().mean().item())} if args.predict else {})},
         "event_ms": {"mean": ev_ms, "p10": float(np.percentile(per_call_ms, 10)),
                      "p50": float(np.percentile(per_call_ms, 50)),
                      "p90": float(np.percentile(per_call_ms, 90))},

@@ -8,10 +8,12 @@
 // among the candidates of the realised k.
 //
 // Kernel 1 (top3_chunk): one work-group per (sequence, position, chunk)
-//   streams a chunk of a draft row and keeps each lane's best three 64-bit
-//   keys (order-preserving map of the logit's bits, then the complemented
-//   token id so that equal logits rank the lower id first); three rounds of a
-//   work-group max extract the chunk's top-3.
+//   streams a chunk of a draft row (16-byte nontemporal loads) and keeps each
+//   lane's best three (value, index), testing eight elements at a time on
+//   their maximum; the lanes' candidates become 64-bit keys (order-preserving
+//   map of the logit's bits, then the complemented token id so that equal
+//   logits rank the lower id first) and three rounds of a work-group max
+//   extract the chunk's top-3.
 // Kernel 2 (top3_merge): one wave per sequence merges the chunk candidates of
 //   each position and evaluates the hit.
 #include "common.h"
@@ -32,16 +34,6 @@ __device__ __forceinline__ uint64_t make_key(uint32_t bits, int64_t idx) {
   if (bits == 0x80000000u) bits = 0u;
   const uint32_t mono = (bits & 0x80000000u) ? ~bits : (bits | 0x80000000u);
   return ((uint64_t)mono << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)idx);
-}
-
-__device__ __forceinline__ bool is_nan_bits(uint32_t bits) {
-  return (bits & 0x7FFFFFFFu) > 0x7F800000u;
-}
-
-template <int DT>
-__device__ __forceinline__ uint32_t load_bits(const void* row, int64_t j) {
-  if constexpr (DT == kBF16) return (uint32_t)static_cast<const uint16_t*>(row)[j] << 16;
-  else return static_cast<const uint32_t*>(row)[j];
 }
 
 __device__ __forceinline__ void insert3(uint64_t (&t)[3], uint64_t k) {
@@ -93,35 +85,121 @@ struct PredictArgs {
   int B, gamma, V, nc;
 };
 
-template <int DT>
+// A lane's best three elements, largest first.  Elements arrive in increasing
+// index order, so an equal value never displaces an earlier one (ties go to
+// the lower id); an empty slot holds (-inf, INT_MAX) and takes any non-NaN
+// value.  +0.0 and -0.0 compare equal.  A NaN never enters.
+struct Best3 {
+  float v[3];
+  int i[3];
+};
+
+__device__ __forceinline__ bool beats(float v, float sv, int si) {
+  return v > sv || (v == sv && si == INT_MAX);
+}
+
+__device__ __forceinline__ void offer(Best3& t, float v, int idx) {
+  if (!beats(v, t.v[2], t.i[2])) return;
+  if (beats(v, t.v[1], t.i[1])) {
+    t.v[2] = t.v[1];
+    t.i[2] = t.i[1];
+    if (beats(v, t.v[0], t.i[0])) {
+      t.v[1] = t.v[0];
+      t.i[1] = t.i[0];
+      t.v[0] = v;
+      t.i[0] = idx;
+    } else {
+      t.v[1] = v;
+      t.i[1] = idx;
+    }
+  } else {
+    t.v[2] = v;
+    t.i[2] = idx;
+  }
+}
+
+// Eight elements of a lane (indices j0..j0+7, those < end): a cheap test on
+// their maximum first, the careful insertion only when it can change the best
+// three; NaN bits are or-ed into `nan`.
+template <int DT, bool VEC>
+__device__ __forceinline__ void offer8(Best3& t, const Raw8<DT, VEC>& raw, int64_t j0, int64_t end,
+                                       bool full, uint32_t& nan) {
+  float v[8];
+  unpack<DT, VEC>(raw, v);
+  if constexpr (DT == kBF16 && VEC) {   // (h & 0x7FFF) > 0x7F80 per half: a NaN
+    const uint32_t w[4] = {raw.w.x, raw.w.y, raw.w.z, raw.w.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) nan |= ((w[q] & 0x7FFF7FFFu) + 0x007F007Fu) & 0x80008000u;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) nan |= (uint32_t)(v[e] != v[e]);
+  }
+  float m = v[0];
+#pragma unroll
+  for (int e = 1; e < 8; ++e) m = fmaxf(m, v[e]);
+  if (!full || beats(m, t.v[2], t.i[2])) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if (full || j0 + e < end) offer(t, v[e], (int)(j0 + e));
+  }
+}
+
+template <int DT, bool VEC>
 __global__ __launch_bounds__(kThreads) void top3_chunk_kernel(PredictArgs a) {
   __shared__ uint64_t lds[kWaves];
   __shared__ int lds_i[kWaves];
-  const int G1 = a.gamma + 1;
   const int64_t id = blockIdx.x;
   const int64_t row = id / a.nc;   // b * (gamma+1) + k
   const int c = (int)(id - row * a.nc);
-  const int es = DT == kBF16 ? 2 : 4;
-  const void* rp = static_cast<const char*>(a.draft) + row * (int64_t)a.V * es;
+  constexpr int kEs = DT == kBF16 ? 2 : 4;
+  const void* rp = static_cast<const char*>(a.draft) + row * (int64_t)a.V * kEs;
   const int64_t begin = (int64_t)c * kChunk;
   const int64_t end = min<int64_t>(begin + kChunk, a.V);
-  uint64_t t[3] = {0, 0, 0};
-  int nan = 0;
-  for (int64_t j = begin + threadIdx.x; j < end; j += kThreads) {
-    const uint32_t bits = load_bits<DT>(rp, j);
-    nan |= is_nan_bits(bits);
-    insert3(t, make_key(bits, j));
+  constexpr int U = 4;
+  constexpr int64_t kStep = (int64_t)kThreads * kUnit, kBatch = U * kStep;
+  Best3 t;
+#pragma unroll
+  for (int r = 0; r < 3; ++r) {
+    t.v[r] = -INFINITY;
+    t.i[r] = INT_MAX;
   }
-  (void)G1;
-  const int any_nan = -block_min_int(-nan, lds_i);
+  uint32_t nan = 0;
+  int64_t j;
+  if constexpr (VEC) {
+    // Full batches through a buffer resource over the chunk (nontemporal).
+    const int nb = (int)((end - begin) / kBatch);
+    const __amdgpu_buffer_rsrc_t rs =
+        chunk_rsrc(static_cast<const char*>(rp) + begin * kEs, (int)((end - begin) * kEs));
+    const int voff = (int)threadIdx.x * kUnit * kEs;
+    for (int i = 0; i < nb; ++i) {
+      Raw8<DT, VEC> raw[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) load_raw_buf<DT>(rs, voff, (int)((i * kBatch + u * kStep) * kEs), raw[u]);
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        offer8<DT, VEC>(t, raw[u], begin + i * kBatch + u * kStep + (int64_t)threadIdx.x * kUnit, end, true, nan);
+    }
+    j = begin + nb * kBatch + (int64_t)threadIdx.x * kUnit;
+  } else {
+    j = begin + (int64_t)threadIdx.x * kUnit;
+  }
+  for (; j < end; j += kStep) {   // the rest, unit by unit, bounds-checked
+    Raw8<DT, VEC> raw;
+    load_raw<DT, VEC, true>(rp, j, end, raw);
+    offer8<DT, VEC>(t, raw, j, end, false, nan);
+  }
+  const int any_nan = -block_min_int(nan != 0 ? -1 : 0, lds_i);
+  uint64_t k3[3];
+#pragma unroll
+  for (int r = 0; r < 3; ++r) k3[r] = t.i[r] == INT_MAX ? 0 : make_key(__float_as_uint(t.v[r]), t.i[r]);
   uint64_t best[3];
 #pragma unroll
   for (int r = 0; r < 3; ++r) {
-    best[r] = block_max_u64(t[0], lds);
-    if (best[r] != 0 && t[0] == best[r]) {   // keys are unique: the owner pops it
-      t[0] = t[1];
-      t[1] = t[2];
-      t[2] = 0;
+    best[r] = block_max_u64(k3[0], lds);
+    if (best[r] != 0 && k3[0] == best[r]) {   // keys are unique: the owner pops it
+      k3[0] = k3[1];
+      k3[1] = k3[2];
+      k3[2] = 0;
     }
   }
   if (threadIdx.x == 0) {
@@ -218,10 +296,14 @@ int spec_predict_outcomes(const void* draft_logits, int dtype, int B, int gamma,
   a.nc = nc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  if (dtype == SPEC_BF16)
-    hipLaunchKernelGGL(top3_chunk_kernel<kBF16>, dim3((unsigned)nblk), dim3(kThreads), 0, st, a);
-  else
-    hipLaunchKernelGGL(top3_chunk_kernel<kF32>, dim3((unsigned)nblk), dim3(kThreads), 0, st, a);
+  const bool vec = (V % 8 == 0) && ((uintptr_t)draft_logits % 16 == 0);
+  if (dtype == SPEC_BF16) {
+    if (vec) hipLaunchKernelGGL((top3_chunk_kernel<kBF16, true>), dim3((unsigned)nblk), dim3(kThreads), 0, st, a);
+    else hipLaunchKernelGGL((top3_chunk_kernel<kBF16, false>), dim3((unsigned)nblk), dim3(kThreads), 0, st, a);
+  } else {
+    if (vec) hipLaunchKernelGGL((top3_chunk_kernel<kF32, true>), dim3((unsigned)nblk), dim3(kThreads), 0, st, a);
+    else hipLaunchKernelGGL((top3_chunk_kernel<kF32, false>), dim3((unsigned)nblk), dim3(kThreads), 0, st, a);
+  }
   hipLaunchKernelGGL(top3_merge_kernel, dim3((unsigned)B), dim3(64), 0, st, a);
   return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ELAUNCH;
 }

@@ -1179,8 +1179,20 @@ template <int DT, bool VEC, int U>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8)))
 void fused_kernel(VerifyArgs a, Sched sc) {
   __shared__ ItemLds sh;
-  int kind, b, sub;
-  sched_decode(sc, blockIdx.x, kind, b, sub);
+  __shared__ int item[3];
+  // One wave decodes the block number (a search on the scalar unit, which
+  // the CU's waves share) and hands the item to the others.
+  if (threadIdx.x < 64) {
+    int kind, b, sub;
+    sched_decode(sc, blockIdx.x, kind, b, sub);
+    if (threadIdx.x == 0) {
+      item[0] = kind;
+      item[1] = b;
+      item[2] = sub;
+    }
+  }
+  __syncthreads();
+  const int kind = uni(item[0]), b = uni(item[1]), sub = uni(item[2]);
   switch (kind) {
     case kItemStream: {
       const int r = sub / a.nc, c = sub - r * a.nc;
