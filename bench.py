@@ -40,7 +40,10 @@ def parse():
     ap.add_argument("--mode", choices=("residual", "saguaro"), default="residual")
     ap.add_argument("--eps", type=float, default=0.0)
     ap.add_argument("--predict", action="store_true",
-                    help="each step also predicts outcomes (draft top-3 per position, hits)")
+                    help="each step also predicts outcomes (draft top-3 per position, hits), in "
+                         "the same pass as the verification (spec_verify_predict)")
+    ap.add_argument("--predict-separate", action="store_true",
+                    help="with --predict: verification, then the stand-alone prediction call")
     ap.add_argument("--sets", type=int, default=0,
                     help="input sets to rotate through (0: enough for > 1 GB)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -140,18 +143,22 @@ def main():
     out = R.alloc_outputs(B, g, dev)
     ws = R.new_workspace(R.spec_workspace_bytes(B, g, V, dt_code), dev)
     stream = torch.cuda.current_stream(dev)
-    pws = R.new_workspace(R.spec_predict_workspace_bytes(B, g, V, dt_code), dev) if args.predict else None
-    pout = None
+    sep = args.predict and args.predict_separate
+    pws = R.new_workspace(R.spec_predict_workspace_bytes(B, g, V, dt_code), dev) if sep else None
+    pout = R.alloc_predict_outputs(B, g, dev) if args.predict else None
 
     def call(i):
         nonlocal pout
         d, t = sets[i % nsets]
-        if args.mode == "residual":
+        if args.predict and not sep:
+            R.spec_verify_predict(d, t, tok, ua, us, batch.T, out=out, pred=pout, workspace=ws,
+                                  stream=stream, saguaro=args.mode == "saguaro", eps=args.eps)
+        elif args.mode == "residual":
             R.spec_verify(d, t, tok, ua, us, batch.T, out=out, workspace=ws, stream=stream)
         else:
             R.spec_verify_saguaro(d, t, tok, ua, us, batch.T, out=out, workspace=ws, stream=stream,
                                   eps=args.eps)
-        if args.predict:
+        if sep:
             pout = R.spec_predict_outcomes(d, out.accepted, out.tokens, out=pout, workspace=pws,
                                            stream=stream)
 
@@ -191,7 +198,8 @@ def main():
                    "logits": batch.dtype, "mode": args.mode, "eps": args.eps,
                    "input_sets": nsets, "alpha_target": [float(batch.alpha_target.min()),
                                                          float(batch.alpha_target.max())],
-                   "mean_accepted": float(acc.mean()), "predict": bool(args.predict),
+                   "mean_accepted": float(acc.mean()),
+                   "predict": ("separate" if sep else "fused") if args.predict else False,
                    **({"hit_rate": float(pout.hit.float().mean().item())} if args.predict else {})},
         "event_ms": {"mean": ev_ms, "p10": float(np.percentile(per_call_ms, 10)),
                      "p50": float(np.percentile(per_call_ms, 50)),

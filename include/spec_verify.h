@@ -163,6 +163,30 @@ int spec_predict_outcomes(const void* draft_logits, int dtype, int B, int gamma,
                           int32_t* hit, int32_t* cand_idx, void* workspace,
                           size_t workspace_bytes, void* stream);
 
+/*
+ * Verification and outcome prediction in one pass over the logits
+ * ("Speculative Speculative Decoding (Saguaro)", section 3.1: the outcomes
+ * (k, bonus) are enumerated from the draft logits' top-3 and checked against
+ * the verification's result).  The verification arguments and outputs are
+ * those of spec_verify (saguaro = 0; eps is ignored) or spec_verify_saguaro
+ * (saguaro = 1, eps as there); any other saguaro value is SPEC_EINVAL.  The
+ * outcome outputs are those of spec_predict_outcomes given this call's
+ * out_accepted and out_tokens:
+ *   cand: [B][gamma+1][3] int32 (required); hit, cand_idx: [B] int32 (nullable).
+ * The draft rows are read once: while the verification streams draft rows
+ * 0..gamma-1 it also ranks them, and it streams draft row gamma for the
+ * ranking alone.  The workspace is the verification's (spec_workspace_bytes),
+ * with the same zero-on-entry rule; outputs equal those of the two separate
+ * calls.
+ */
+int spec_verify_predict(const void* draft_logits, const void* target_logits, int dtype,
+                        const int32_t* draft_tokens, const float* u_accept, const float* u_sample,
+                        int B, int gamma, int V, float temperature, const int32_t* in_len,
+                        int32_t* out_tokens, int32_t* out_accepted, int32_t* out_first_reject,
+                        uint64_t* out_accept_mask, int32_t* out_len, const spec_diag* diag,
+                        int saguaro, float eps, int32_t* cand, int32_t* hit, int32_t* cand_idx,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
 /* A static, human-readable description of a status code. */
 const char* spec_status_str(int status);
 

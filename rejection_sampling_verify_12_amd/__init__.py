@@ -19,7 +19,8 @@ SPEC_OK, SPEC_EINVAL, SPEC_EDTYPE, SPEC_EWORKSPACE, SPEC_ELAUNCH = 0, -1, -2, -3
 SPEC_F32, SPEC_BF16 = 0, 1
 
 EXPORTED = ("spec_workspace_bytes", "spec_verify", "spec_verify_saguaro",
-            "spec_predict_workspace_bytes", "spec_predict_outcomes", "spec_status_str")
+            "spec_predict_workspace_bytes", "spec_predict_outcomes", "spec_verify_predict",
+            "spec_status_str")
 
 
 class SpecDiag(ctypes.Structure):
@@ -53,6 +54,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.spec_predict_workspace_bytes.restype = sz
     lib.spec_predict_outcomes.argtypes = [vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.spec_predict_outcomes.restype = i32
+    lib.spec_verify_predict.argtypes = verify_args[:-3] + [i32, f32, vp, vp, vp] + verify_args[-3:]
+    lib.spec_verify_predict.restype = i32
     lib.spec_status_str.argtypes = [i32]
     lib.spec_status_str.restype = ctypes.c_char_p
     _lib = lib
@@ -132,7 +135,7 @@ def alloc_outputs(B: int, gamma: int, device, diag: bool = False) -> VerifyOut:
 
 def _verify_call(saguaro: bool, draft_logits, target_logits, draft_tokens, u_accept, u_sample,
                  temperature: float, in_len=None, out: VerifyOut | None = None, diag: bool = False,
-                 workspace=None, stream=None, eps: float = 0.0) -> VerifyOut:
+                 workspace=None, stream=None, eps: float = 0.0, pred=None) -> VerifyOut:
     lib = load_library()
     B, G1, V = draft_logits.shape
     gamma = G1 - 1
@@ -155,7 +158,11 @@ def _verify_call(saguaro: bool, draft_logits, target_logits, draft_tokens, u_acc
             out.first_reject.data_ptr(), out.accept_mask.data_ptr(), out.out_len.data_ptr(),
             ctypes.byref(dg) if dg is not None else None, workspace.data_ptr(),
             workspace.numel(), _stream_handle(stream, dev)]
-    if saguaro:
+    if pred is not None:
+        _check_dev(*pred)
+        st = lib.spec_verify_predict(*args[:-3], int(saguaro), float(eps), pred.cand.data_ptr(),
+                                     _ptr(pred.hit), _ptr(pred.cand_idx), *args[-3:])
+    elif saguaro:
         st = lib.spec_verify_saguaro(*args, float(eps))
     else:
         st = lib.spec_verify(*args)
@@ -207,6 +214,27 @@ def spec_predict_outcomes(draft_logits, accepted=None, out_tokens=None, out=None
     if st != SPEC_OK:
         raise SpecError(st)
     return out
+
+
+def alloc_predict_outputs(B: int, gamma: int, device) -> "PredictOut":
+    import torch
+    i32 = dict(dtype=torch.int32, device=device)
+    return PredictOut(torch.empty((B, gamma + 1, 3), **i32), torch.empty((B,), **i32),
+                      torch.empty((B,), **i32))
+
+
+def spec_verify_predict(draft_logits, target_logits, draft_tokens, u_accept, u_sample,
+                        temperature, in_len=None, out=None, pred=None, diag=False, workspace=None,
+                        stream=None, saguaro: bool = False, eps: float = 0.0):
+    """Verification (residual, or Saguaro with ``saguaro=True``) and outcome
+    prediction in one pass; returns (VerifyOut, PredictOut) (see spec_verify.h)."""
+    B, G1, _ = draft_logits.shape
+    if pred is None:
+        pred = alloc_predict_outputs(B, G1 - 1, draft_logits.device)
+    out = _verify_call(bool(saguaro), draft_logits, target_logits, draft_tokens, u_accept,
+                       u_sample, temperature, in_len, out, diag, workspace, stream,
+                       eps if saguaro else 0.0, pred)
+    return out, pred
 
 
 def bytes_algorithmic(B: int, gamma: int, V: int, dtype: int) -> int:

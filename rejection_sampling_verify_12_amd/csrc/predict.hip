@@ -7,83 +7,26 @@
 // after k acceptances; after the real verification, hit = the emitted token is
 // among the candidates of the realised k.
 //
+// Stand-alone path (spec_predict_outcomes):
 // Kernel 1 (top3_chunk): one work-group per (sequence, position, chunk)
 //   streams a chunk of a draft row (16-byte nontemporal loads) and keeps each
 //   lane's best three (value, index), testing eight elements at a time on
-//   their maximum; the lanes' candidates become 64-bit keys (order-preserving
-//   map of the logit's bits, then the complemented token id so that equal
-//   logits rank the lower id first) and three rounds of a work-group max
-//   extract the chunk's top-3.
+//   their maximum; each wave extracts its top-3 keys and the first thread
+//   merges the waves'.
 // Kernel 2 (top3_merge): one wave per sequence merges the chunk candidates of
 //   each position and evaluates the hit.
+// Fused path (spec_verify_predict): the verification's stream items record
+// each chunk's three best lane leaders (see topk.h); top3_lanes then re-reads
+// the (at most three) leading lanes of every draft row, ranks their elements
+// and evaluates the hit.
 #include "common.h"
+#include "predict.h"
 #include "spec_verify.h"
+#include "topk.h"
 
 #include <limits.h>
 
 namespace sv {
-
-struct Top3 {
-  uint64_t key[3];
-  uint64_t nan;   // nonzero when the chunk held a NaN
-};
-
-// Order-preserving key: larger logit -> larger key; equal logits -> lower id
-// larger.  -0.0 is folded onto +0.0.  0 never occurs for a real element.
-__device__ __forceinline__ uint64_t make_key(uint32_t bits, int64_t idx) {
-  if (bits == 0x80000000u) bits = 0u;
-  const uint32_t mono = (bits & 0x80000000u) ? ~bits : (bits | 0x80000000u);
-  return ((uint64_t)mono << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)idx);
-}
-
-__device__ __forceinline__ void insert3(uint64_t (&t)[3], uint64_t k) {
-  if (k > t[2]) {
-    if (k > t[1]) {
-      t[2] = t[1];
-      if (k > t[0]) {
-        t[1] = t[0];
-        t[0] = k;
-      } else {
-        t[1] = k;
-      }
-    } else {
-      t[2] = k;
-    }
-  }
-}
-
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const uint64_t t = __shfl_xor(v, o, 64);
-    v = t > v ? t : v;
-  }
-  return v;
-}
-
-__device__ __forceinline__ uint64_t block_max_u64(uint64_t v, uint64_t* lds) {
-  v = wave_max_u64(v);
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-  __syncthreads();
-  if (l == 0) lds[w] = v;
-  __syncthreads();
-  uint64_t t = lds[0];
-#pragma unroll
-  for (int i = 1; i < kWaves; ++i) t = lds[i] > t ? lds[i] : t;
-  __syncthreads();
-  return t;
-}
-
-struct PredictArgs {
-  const void* draft;
-  const int32_t* accepted;
-  const int32_t* out_tokens;
-  int32_t* cand;
-  int32_t* hit;
-  int32_t* cand_idx;
-  Top3* part;   // [B][gamma+1][nc]
-  int B, gamma, V, nc;
-};
 
 // A lane's best three elements, largest first.  Elements arrive in increasing
 // index order, so an equal value never displaces an earlier one (ties go to
@@ -144,10 +87,49 @@ __device__ __forceinline__ void offer8(Best3& t, const Raw8<DT, VEC>& raw, int64
   }
 }
 
+template <int DT>
+__device__ __forceinline__ uint32_t load_bits(const void* row, int64_t j) {
+  if constexpr (DT == kBF16) return (uint32_t)static_cast<const uint16_t*>(row)[j] << 16;
+  else return static_cast<const uint32_t*>(row)[j];
+}
+
+// The work-group's three best keys and NaN flag from each wave's: the first
+// lane of every wave leaves its wave's in LDS, thread 0 merges them.
+struct ChunkLds {
+  uint64_t key[kWaves * 3];
+  int nan[kWaves];
+};
+__device__ __forceinline__ void chunk_top3(uint64_t (&t)[3], bool nan, ChunkLds& sh, Top3* out) {
+  uint64_t w3[3];
+  wave_top3(t, w3);
+  const bool wn = __ballot(nan) != 0;
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+#pragma unroll
+    for (int r = 0; r < 3; ++r) sh.key[w * 3 + r] = w3[r];
+    sh.nan[w] = wn ? 1 : 0;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint64_t m[3] = {0, 0, 0};
+    int any = 0;
+    for (int i = 0; i < kWaves; ++i) {
+      any |= sh.nan[i];
+#pragma unroll
+      for (int r = 0; r < 3; ++r) insert3(m, sh.key[i * 3 + r]);
+    }
+    Top3 o;
+    o.key[0] = m[0];
+    o.key[1] = m[1];
+    o.key[2] = m[2];
+    o.nan = (uint64_t)any;
+    *out = o;
+  }
+}
+
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kThreads) void top3_chunk_kernel(PredictArgs a) {
-  __shared__ uint64_t lds[kWaves];
-  __shared__ int lds_i[kWaves];
+  __shared__ ChunkLds sh;
   const int64_t id = blockIdx.x;
   const int64_t row = id / a.nc;   // b * (gamma+1) + k
   const int c = (int)(id - row * a.nc);
@@ -188,28 +170,30 @@ __global__ __launch_bounds__(kThreads) void top3_chunk_kernel(PredictArgs a) {
     load_raw<DT, VEC, true>(rp, j, end, raw);
     offer8<DT, VEC>(t, raw, j, end, false, nan);
   }
-  const int any_nan = -block_min_int(nan != 0 ? -1 : 0, lds_i);
   uint64_t k3[3];
 #pragma unroll
   for (int r = 0; r < 3; ++r) k3[r] = t.i[r] == INT_MAX ? 0 : make_key(__float_as_uint(t.v[r]), t.i[r]);
-  uint64_t best[3];
-#pragma unroll
-  for (int r = 0; r < 3; ++r) {
-    best[r] = block_max_u64(k3[0], lds);
-    if (best[r] != 0 && k3[0] == best[r]) {   // keys are unique: the owner pops it
-      k3[0] = k3[1];
-      k3[1] = k3[2];
-      k3[2] = 0;
+  chunk_top3(k3, nan != 0, sh, a.part + id);
+}
+
+// Hit flag and candidate index of sequence b from its candidates in LDS.
+__device__ __forceinline__ void eval_hit(const PredictArgs& a, int b, const int* s_cand) {
+  if (!a.accepted || !a.out_tokens) return;
+  const int G1 = a.gamma + 1;
+  const int K = a.accepted[b];
+  int h = 0, idx = -1;
+  if (K >= 0 && K < G1) {
+    const int y = a.out_tokens[(int64_t)b * G1 + K];
+    for (int r = 0; r < 3; ++r) {
+      if (y >= 0 && s_cand[K * 3 + r] == y) {
+        h = 1;
+        idx = 3 * K + r;
+        break;
+      }
     }
   }
-  if (threadIdx.x == 0) {
-    Top3 o;
-    o.key[0] = best[0];
-    o.key[1] = best[1];
-    o.key[2] = best[2];
-    o.nan = (uint64_t)any_nan;
-    a.part[id] = o;
-  }
+  if (a.hit) a.hit[b] = h;
+  if (a.cand_idx) a.cand_idx[b] = idx;
 }
 
 __global__ __launch_bounds__(64) void top3_merge_kernel(PredictArgs a) {
@@ -228,34 +212,84 @@ __global__ __launch_bounds__(64) void top3_merge_kernel(PredictArgs a) {
     }
 #pragma unroll
     for (int r = 0; r < 3; ++r) {
-      const int tok = (nan || t[r] == 0) ? -1 : (int)(0xFFFFFFFFu - (uint32_t)(t[r] & 0xFFFFFFFFu));
+      const int tok = (nan || t[r] == 0) ? -1 : key_index(t[r]);
       s_cand[k * 3 + r] = tok;
       a.cand[((int64_t)b * G1 + k) * 3 + r] = tok;
     }
   }
   __syncthreads();
-  if (k == 0 && a.accepted && a.out_tokens) {
-    const int K = a.accepted[b];
-    int h = 0, idx = -1;
-    if (K >= 0 && K < G1) {
-      const int y = a.out_tokens[(int64_t)b * G1 + K];
-      for (int r = 0; r < 3; ++r) {
-        if (y >= 0 && s_cand[K * 3 + r] == y) {
-          h = 1;
-          idx = 3 * K + r;
-          break;
-        }
-      }
-    }
-    if (a.hit) a.hit[b] = h;
-    if (a.cand_idx) a.cand_idx[b] = idx;
-  }
+  if (k == 0) eval_hit(a, b, s_cand);
 }
 
-static inline size_t predict_bytes(int B, int gamma, int V) {
+// One work-group per sequence; wave w ranks positions w, w + 4, ...  The
+// chunk records hold lane leaders (key index = start of the leader's best
+// unit); the row's three best leaders are found first, then lanes 16l..16l+15
+// re-read leader l's units (every kTile-th unit of its chunk) and the wave
+// ranks those elements.
+template <int DT>
+__global__ __launch_bounds__(kThreads) void top3_lanes_kernel(PredictArgs a) {
+  __shared__ int s_cand[64 * 3];
+  const int b = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int G1 = a.gamma + 1;
+  constexpr int kEs = DT == kBF16 ? 2 : 4;
+  for (int k = wave; k < G1; k += kWaves) {
+    const int64_t row = (int64_t)b * G1 + k;
+    const Top3* P = a.part + row * a.nc;
+    uint64_t t[3] = {0, 0, 0};
+    if (lane < 3 * a.nc) t[0] = P[lane / 3].key[lane % 3];
+    const bool nan = __ballot(lane < a.nc && P[lane < a.nc ? lane : 0].nan != 0) != 0;
+    uint64_t lead[3];
+    wave_top3(t, lead);
+    const int l = lane >> 4;
+    const uint64_t mine = l == 0 ? lead[0] : (l == 1 ? lead[1] : (l == 2 ? lead[2] : 0ull));
+    uint64_t e3[3] = {0, 0, 0};
+    if (mine != 0) {
+      const void* rp = static_cast<const char*>(a.draft) + row * (int64_t)a.V * kEs;
+      const int64_t s0 = key_index(mine);
+      const int64_t cb = s0 / a.chunk * a.chunk;
+      const int64_t ce = min<int64_t>(cb + a.chunk, a.V);
+      for (int64_t j = s0 - (s0 - cb) / kTile * kTile + (int64_t)(lane & 15) * kTile; j < ce; j += 16 * kTile)
+        for (int e = 0; e < kUnit && j + e < ce; ++e)
+          insert3(e3, make_key(load_bits<DT>(rp, j + e), j + e));
+    }
+    uint64_t best[3];
+    wave_top3(e3, best);
+    if (lane < 3) {
+      const uint64_t kb = lane == 0 ? best[0] : (lane == 1 ? best[1] : best[2]);
+      const int tok = (nan || kb == 0) ? -1 : key_index(kb);
+      s_cand[k * 3 + lane] = tok;
+      a.cand[row * 3 + lane] = tok;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) eval_hit(a, b, s_cand);
+}
+
+size_t predict_part_bytes(int B, int gamma, int V) {
   if (B == 0) return 0;
   const size_t nc = (size_t)((V + kChunk - 1) / kChunk);
   return (((size_t)B * (gamma + 1) * nc * sizeof(Top3)) + 255) & ~(size_t)255;
+}
+
+hipError_t predict_launch_rows(const PredictArgs& a, int dtype, bool vec, hipStream_t st) {
+  const int64_t nblk = (int64_t)a.B * (a.gamma + 1) * a.nc;
+  if (dtype == SPEC_BF16) {
+    if (vec) hipLaunchKernelGGL((top3_chunk_kernel<kBF16, true>), dim3((unsigned)nblk), dim3(kThreads), 0, st, a);
+    else hipLaunchKernelGGL((top3_chunk_kernel<kBF16, false>), dim3((unsigned)nblk), dim3(kThreads), 0, st, a);
+  } else {
+    if (vec) hipLaunchKernelGGL((top3_chunk_kernel<kF32, true>), dim3((unsigned)nblk), dim3(kThreads), 0, st, a);
+    else hipLaunchKernelGGL((top3_chunk_kernel<kF32, false>), dim3((unsigned)nblk), dim3(kThreads), 0, st, a);
+  }
+  hipLaunchKernelGGL(top3_merge_kernel, dim3((unsigned)a.B), dim3(64), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t predict_launch_leaders(const PredictArgs& a, int dtype, hipStream_t st) {
+  if (dtype == SPEC_BF16)
+    hipLaunchKernelGGL((top3_lanes_kernel<kBF16>), dim3((unsigned)a.B), dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((top3_lanes_kernel<kF32>), dim3((unsigned)a.B), dim3(kThreads), 0, st, a);
+  return hipGetLastError();
 }
 
 }  // namespace sv
@@ -265,7 +299,7 @@ extern "C" {
 size_t spec_predict_workspace_bytes(int B, int gamma, int V, int dtype) {
   if ((dtype != SPEC_F32 && dtype != SPEC_BF16) || B < 0 || gamma < 1 || gamma > 63 || V < 1)
     return 0;
-  return sv::predict_bytes(B, gamma, V);
+  return sv::predict_part_bytes(B, gamma, V);
 }
 
 int spec_predict_outcomes(const void* draft_logits, int dtype, int B, int gamma, int V,
@@ -281,7 +315,7 @@ int spec_predict_outcomes(const void* draft_logits, int dtype, int B, int gamma,
   const int nc = (V + kChunk - 1) / kChunk;
   const int64_t nblk = (int64_t)B * (gamma + 1) * nc;
   if (nblk * kThreads > (int64_t)UINT_MAX) return SPEC_EINVAL;
-  if (!workspace || workspace_bytes < predict_bytes(B, gamma, V)) return SPEC_EWORKSPACE;
+  if (!workspace || workspace_bytes < predict_part_bytes(B, gamma, V)) return SPEC_EWORKSPACE;
   PredictArgs a;
   a.draft = draft_logits;
   a.accepted = accepted;
@@ -294,18 +328,11 @@ int spec_predict_outcomes(const void* draft_logits, int dtype, int B, int gamma,
   a.gamma = gamma;
   a.V = V;
   a.nc = nc;
-  hipStream_t st = static_cast<hipStream_t>(stream);
+  a.chunk = kChunk;
   (void)hipGetLastError();
   const bool vec = (V % 8 == 0) && ((uintptr_t)draft_logits % 16 == 0);
-  if (dtype == SPEC_BF16) {
-    if (vec) hipLaunchKernelGGL((top3_chunk_kernel<kBF16, true>), dim3((unsigned)nblk), dim3(kThreads), 0, st, a);
-    else hipLaunchKernelGGL((top3_chunk_kernel<kBF16, false>), dim3((unsigned)nblk), dim3(kThreads), 0, st, a);
-  } else {
-    if (vec) hipLaunchKernelGGL((top3_chunk_kernel<kF32, true>), dim3((unsigned)nblk), dim3(kThreads), 0, st, a);
-    else hipLaunchKernelGGL((top3_chunk_kernel<kF32, false>), dim3((unsigned)nblk), dim3(kThreads), 0, st, a);
-  }
-  hipLaunchKernelGGL(top3_merge_kernel, dim3((unsigned)B), dim3(64), 0, st, a);
-  return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ELAUNCH;
+  const hipError_t e = predict_launch_rows(a, dtype, vec, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SPEC_OK : SPEC_ELAUNCH;
 }
 
 }  // extern "C"

@@ -43,6 +43,7 @@
 // always run; a wait that still times out sets the error word and gives up
 // instead of hanging.
 #include "common.h"
+#include "predict.h"
 #include "spec_verify.h"
 
 #include <cmath>
@@ -162,6 +163,7 @@ struct VerifyArgs {
   uint64_t* tiles;   // [B][ntile] slots: tile sums of the sampling weights
   uint64_t* mass;    // [B][nt] slots: residual sums of the residual-mass items (eps > 0)
   uint64_t* rsum;    // [B][nt] slots: residual sums of the sampling items (Saguaro)
+  Top3* cpart;       // [B][gamma+1][nc] lane leaders of the draft rows (outcome prediction)
   int B, gamma, V;
   int nc, chunk;     // stream chunks per row and their length
   int ntile, nt;     // sampling tiles per row; sampling items per sequence
@@ -244,16 +246,25 @@ __device__ __forceinline__ SeqRec wait_rec(const VerifyArgs& a, int b) {
 // One batch of N units (8 logits each) of a lane: raise the lane's integer
 // offset if the batch holds a larger logit (rescaling the running sum by an
 // exact power of two), then add the batch's terms 2^(l c_T - mref), tree-summed
-// in fp32, to the fp64 running sum.
-template <int DT, bool VEC, int N>
+// in fp32, to the fp64 running sum.  LEAD: also track the lane's leader unit
+// (units start at jb + u kTile).
+template <int DT, bool VEC, int N, bool LEAD = false>
 __device__ __forceinline__ void stream_batch(const Raw8<DT, VEC> (&raw)[N], float ch, float cl,
-                                             float& mref, float& mraw, double& s) {
+                                             float& mref, float& mraw, double& s, int& pos, int jb) {
   float v[N * 8];
 #pragma unroll
   for (int u = 0; u < N; ++u) unpack<DT, VEC>(raw[u], *reinterpret_cast<float(*)[8]>(v + u * 8));
-  float bm = v[0];
+  float um[N];
 #pragma unroll
-  for (int e = 1; e < N * 8; ++e) bm = fmaxf(bm, v[e]);
+  for (int u = 0; u < N; ++u) {
+    um[u] = v[u * 8];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) um[u] = fmaxf(um[u], v[u * 8 + e]);
+  }
+  float bm = um[0];
+#pragma unroll
+  for (int u = 1; u < N; ++u) bm = fmaxf(bm, um[u]);
+  if constexpr (LEAD) lead_batch<N>(um, bm, jb, mraw, pos);
   mraw = fmaxf(mraw, bm);
   const float bl = bm * ch;
   if (bl > mref) {
@@ -273,9 +284,37 @@ __device__ __forceinline__ void stream_batch(const Raw8<DT, VEC> (&raw)[N], floa
 struct StreamLds {
   float f[2 * kWaves];
   double d[kWaves];
+  uint64_t key[kWaves * 3];   // each wave's three best lane leaders
+  int nan[kWaves];
 };
 
-template <int DT, bool VEC, int U>
+// The chunk's three best lane leaders (LEAD items): each wave ranks its lanes
+// and leaves its three in LDS before the barrier that follows.
+__device__ __forceinline__ void wave_leaders(float mx, int pos, StreamLds& sh) {
+  uint64_t t[3] = {pos >= 0 ? make_key(__float_as_uint(mx), pos) : 0ull, 0ull, 0ull};
+  uint64_t w3[3];
+  wave_top3(t, w3);
+  if ((threadIdx.x & 63) == 0) {
+#pragma unroll
+    for (int r = 0; r < 3; ++r) sh.key[(threadIdx.x >> 6) * 3 + r] = w3[r];
+  }
+}
+// After that barrier, thread 0: merge the waves' leaders into the record.
+__device__ __forceinline__ void store_leaders(const StreamLds& sh, bool nan, Top3* out) {
+  uint64_t m[3] = {0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < kWaves * 3; ++i) insert3(m, sh.key[i]);
+  Top3 o;
+  o.key[0] = m[0];
+  o.key[1] = m[1];
+  o.key[2] = m[2];
+  o.nan = nan ? 1u : 0u;
+  *out = o;
+}
+
+// LEAD (draft rows, with outcome prediction): also record the chunk's lane
+// leaders in cpart.
+template <int DT, bool VEC, int U, bool LEAD = false>
 __device__ __forceinline__ void stream_item(const VerifyArgs& a, int b, int r, int c, StreamLds& sh) {
   const void* row = row_ptr<DT>(a, b, r);
   const int64_t begin = (int64_t)c * a.chunk;
@@ -285,6 +324,7 @@ __device__ __forceinline__ void stream_item(const VerifyArgs& a, int b, int r, i
   // mref: this lane's integer offset (log2 units); s: fp64 sum of 2^(l*c_T - mref).
   float mref = kNegSentinel, mraw = -INFINITY;
   double s = 0.0;
+  int pos = -1;
   constexpr int64_t kStep = (int64_t)kThreads * kUnit;
   constexpr int64_t kBatch = U * kStep;
   int64_t j;
@@ -301,7 +341,8 @@ __device__ __forceinline__ void stream_item(const VerifyArgs& a, int b, int r, i
 #pragma unroll
       for (int u = 0; u < U; ++u)
         load_raw_buf<DT>(rs, voff, (int)((i * kBatch + u * kStep) * kEs), raw[u]);
-      stream_batch<DT, VEC, U>(raw, ch, cl, mref, mraw, s);
+      stream_batch<DT, VEC, U, LEAD>(raw, ch, cl, mref, mraw, s, pos,
+                                     (int)(begin + i * kBatch) + (int)threadIdx.x * kUnit);
     }
     j = begin + nb * kBatch + (int64_t)threadIdx.x * kUnit;
   } else {
@@ -310,14 +351,14 @@ __device__ __forceinline__ void stream_item(const VerifyArgs& a, int b, int r, i
       Raw8<DT, VEC> raw[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) load_raw<DT, VEC, true>(row, j + u * kStep, end, raw[u]);
-      stream_batch<DT, VEC, U>(raw, ch, cl, mref, mraw, s);
+      stream_batch<DT, VEC, U, LEAD>(raw, ch, cl, mref, mraw, s, pos, (int)j);
     }
   }
   // Remaining units of this lane (fewer than U; the last may be partial).
   for (; j < end; j += kStep) {
     Raw8<DT, VEC> raw[1];
     load_raw<DT, VEC, true>(row, j, end, raw[0]);
-    stream_batch<DT, VEC, 1>(raw, ch, cl, mref, mraw, s);
+    stream_batch<DT, VEC, 1, LEAD>(raw, ch, cl, mref, mraw, s, pos, (int)j);
   }
   // Merge the lanes: wave shuffles, then one barrier; thread 0 publishes.
   const float wm = wave_max(mref);
@@ -325,6 +366,7 @@ __device__ __forceinline__ void stream_item(const VerifyArgs& a, int b, int r, i
   double sd = (s != 0.0) ? ldexp(s, (int)fmaxf(mref - wm, -2000.f)) : 0.0;
   sd = wave_sum(sd);
   const int wave = threadIdx.x >> 6;
+  if constexpr (LEAD) wave_leaders(mraw, pos, sh);
   if ((threadIdx.x & 63) == 0) {
     sh.f[wave] = wm;
     sh.f[kWaves + wave] = wr;
@@ -345,6 +387,74 @@ __device__ __forceinline__ void stream_item(const VerifyArgs& a, int b, int r, i
     const int64_t idx = ((int64_t)b * (2 * a.gamma + 1) + r) * a.nc + c;
     slot_put32(a.mraw + idx, mr);
     slot_put(a.part + idx, v);
+    if constexpr (LEAD) store_leaders(sh, v != v, a.cpart + ((int64_t)b * (a.gamma + 1) + r) * a.nc + c);
+  }
+}
+
+// Draft row gamma (outcome prediction only): one chunk's lane leaders and
+// NaN flag, nothing else.
+template <int DT, bool VEC, int U>
+__device__ void leader_item(const VerifyArgs& a, int b, int c, StreamLds& sh) {
+  constexpr int kEs = DT == kBF16 ? 2 : 4;
+  const int64_t ridx = (int64_t)b * (a.gamma + 1) + a.gamma;
+  const void* row = static_cast<const char*>(a.draft) + ridx * a.V * kEs;
+  const int64_t begin = (int64_t)c * a.chunk;
+  const int64_t end = min<int64_t>(begin + a.chunk, a.V);
+  float mx = -INFINITY;
+  int pos = -1;
+  bool nan = false;
+  constexpr int64_t kStep = (int64_t)kThreads * kUnit;
+  constexpr int64_t kBatch = U * kStep;
+  auto batch = [&](const auto& raw, auto n, int jb) {
+    constexpr int N = decltype(n)::value;
+    float um[N];
+#pragma unroll
+    for (int u = 0; u < N; ++u) {
+      float v[8];
+      unpack<DT, VEC>(raw[u], v);
+      um[u] = v[0];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        nan = nan || v[e] != v[e];
+        um[u] = fmaxf(um[u], v[e]);
+      }
+    }
+    float bm = um[0];
+#pragma unroll
+    for (int u = 1; u < N; ++u) bm = fmaxf(bm, um[u]);
+    lead_batch<N>(um, bm, jb, mx, pos);
+    mx = fmaxf(mx, bm);
+  };
+  int64_t j;
+  if constexpr (VEC) {
+    const int nb = (int)((end - begin) / kBatch);
+    const __amdgpu_buffer_rsrc_t rs =
+        chunk_rsrc(static_cast<const char*>(row) + begin * kEs, (int)((end - begin) * kEs));
+    const int voff = (int)threadIdx.x * kUnit * kEs;
+    for (int i = 0; i < nb; ++i) {
+      Raw8<DT, VEC> raw[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        load_raw_buf<DT>(rs, voff, (int)((i * kBatch + u * kStep) * kEs), raw[u]);
+      batch(raw, std::integral_constant<int, U>{}, (int)(begin + i * kBatch) + (int)threadIdx.x * kUnit);
+    }
+    j = begin + nb * kBatch + (int64_t)threadIdx.x * kUnit;
+  } else {
+    j = begin + (int64_t)threadIdx.x * kUnit;
+  }
+  for (; j < end; j += kStep) {
+    Raw8<DT, VEC> raw[1];
+    load_raw<DT, VEC, true>(row, j, end, raw[0]);
+    batch(raw, std::integral_constant<int, 1>{}, (int)j);
+  }
+  wave_leaders(mx, pos, sh);
+  const bool wn = __ballot(nan) != 0;
+  if ((threadIdx.x & 63) == 0) sh.nan[threadIdx.x >> 6] = wn ? 1 : 0;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int any = 0;
+    for (int i = 0; i < kWaves; ++i) any |= sh.nan[i];
+    store_leaders(sh, any != 0, a.cpart + ridx * a.nc + c);
   }
 }
 
@@ -1175,7 +1285,9 @@ union ItemLds {
 
 // Compiled for 8 waves per SIMD (64 VGPRs): the stream items need the
 // occupancy; every other path fits without spilling for packed bf16 rows.
-template <int DT, bool VEC, int U>
+// PRED: outcome prediction too (draft-row items record lane leaders; the
+// items of target row gamma are followed by leader items of draft row gamma).
+template <int DT, bool VEC, int U, bool PRED>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8)))
 void fused_kernel(VerifyArgs a, Sched sc) {
   __shared__ ItemLds sh;
@@ -1196,14 +1308,18 @@ void fused_kernel(VerifyArgs a, Sched sc) {
   switch (kind) {
     case kItemStream: {
       const int r = sub / a.nc, c = sub - r * a.nc;
-      stream_item<DT, VEC, U>(a, b, r, c, sh.s);
+      if (PRED && r < a.gamma) stream_item<DT, VEC, U, PRED>(a, b, r, c, sh.s);
+      else stream_item<DT, VEC, U>(a, b, r, c, sh.s);
       break;
     }
     case kItemDecide: decide_item<DT>(a, b, sh.d); break;
     case kItemMass: mass_item<DT, VEC>(a, b, sub, sh.r.lds_d); break;
     case kItemSample: sample_item<DT, VEC>(a, b, sub, sh.r.lds_d); break;
     case kItemDraw: draw_item<DT, VEC>(a, b, sh.r); break;
-    case kItemLast: stream_item<DT, VEC, U>(a, b, 2 * a.gamma, sub, sh.s); break;
+    case kItemLast:
+      if (!PRED || sub < a.nc) stream_item<DT, VEC, U>(a, b, 2 * a.gamma, sub, sh.s);
+      else leader_item<DT, VEC, U>(a, b, sub - a.nc, sh.s);
+      break;
     default: final_item<DT>(a, b, sh.f); break;
   }
 }
@@ -1259,7 +1375,8 @@ static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
   int nc, chunk, ntile, nt;
-  size_t err_off, part_off, mraw_off, seq_off, flag_off, tiles_off, mass_off, rsum_off, total;
+  size_t err_off, part_off, mraw_off, seq_off, flag_off, tiles_off, mass_off, rsum_off, cpart_off,
+      total;
 };
 
 static bool sizes_ok(int B, int gamma, int V) {
@@ -1292,18 +1409,20 @@ static Layout layout(int B, int gamma, int V) {
   off += align256((size_t)B * L.nt * sizeof(uint64_t));
   L.rsum_off = off;
   off += align256((size_t)B * L.nt * sizeof(uint64_t));
+  L.cpart_off = off;
+  off += align256((size_t)B * (gamma + 1) * L.nc * sizeof(Top3));
   L.total = B == 0 ? 0 : off;
   return L;
 }
 
 // Work-groups of the fused kernel the device holds at once (cached per device).
-template <int DT, bool VEC>
+template <int DT, bool VEC, bool PRED>
 static hipError_t resident_groups(int& slots) {
-  static int cache[64][2][2];
+  static int cache[64][2][2][2];
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  int* c = dev >= 0 && dev < 64 ? &cache[dev][DT][VEC ? 1 : 0] : nullptr;
+  int* c = dev >= 0 && dev < 64 ? &cache[dev][DT][VEC ? 1 : 0][PRED ? 1 : 0] : nullptr;
   if (c && *c > 0) {
     slots = *c;
     return hipSuccess;
@@ -1312,7 +1431,7 @@ static hipError_t resident_groups(int& slots) {
   e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
   if (e == hipSuccess)
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &per_cu, reinterpret_cast<const void*>(fused_kernel<DT, VEC, SV_STREAM_UNROLL>), kThreads, 0);
+        &per_cu, reinterpret_cast<const void*>(fused_kernel<DT, VEC, SV_STREAM_UNROLL, PRED>), kThreads, 0);
   if (e != hipSuccess) return e;
   slots = std::max(1, ncu * per_cu);
   if (c) *c = slots;
@@ -1348,22 +1467,32 @@ static Sched make_sched(int B, int NSm, int NL, int NM, int NB, int slots) {
 template <int DT, bool VEC>
 static hipError_t launch_kernels(const VerifyArgs& a, hipStream_t st);
 
+// pa: NULL, or outcome prediction after the verification.
 template <int DT, bool VEC>
-static hipError_t launch_all(const VerifyArgs& a, hipStream_t st) {
+static hipError_t launch_all(const VerifyArgs& a, const PredictArgs* pa, hipStream_t st) {
   // The single-kernel order for packed bf16 rows; float32 or unaligned rows
   // take one kernel per item kind (their sampling paths need more registers
-  // than the stream items' occupancy leaves).
+  // than the stream items' occupancy leaves) and the stand-alone prediction.
   if constexpr (SV_FUSED && DT == kBF16 && VEC) {
     int slots = 0;
-    hipError_t e = resident_groups<DT, VEC>(slots);
+    hipError_t e = pa ? resident_groups<DT, VEC, true>(slots) : resident_groups<DT, VEC, false>(slots);
     if (e != hipSuccess) return e;
     const bool eps_mode = a.saguaro && a.eps > 0.f;
-    const Sched sc = make_sched(a.B, 2 * a.gamma * a.nc, a.nc, eps_mode ? a.nt : 0, a.nt, slots);
-    hipLaunchKernelGGL((fused_kernel<DT, VEC, SV_STREAM_UNROLL>), dim3((unsigned)sc.total), dim3(kThreads),
-                       0, st, a, sc);
+    const Sched sc = make_sched(a.B, 2 * a.gamma * a.nc, (pa ? 2 : 1) * a.nc, eps_mode ? a.nt : 0, a.nt, slots);
+    if (pa) {
+      hipLaunchKernelGGL((fused_kernel<DT, VEC, SV_STREAM_UNROLL, true>), dim3((unsigned)sc.total),
+                         dim3(kThreads), 0, st, a, sc);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      return predict_launch_leaders(*pa, SPEC_BF16, st);
+    }
+    hipLaunchKernelGGL((fused_kernel<DT, VEC, SV_STREAM_UNROLL, false>), dim3((unsigned)sc.total),
+                       dim3(kThreads), 0, st, a, sc);
     return hipGetLastError();
   } else {
-    return launch_kernels<DT, VEC>(a, st);
+    hipError_t e = launch_kernels<DT, VEC>(a, st);
+    if (e != hipSuccess || !pa) return e;
+    return predict_launch_rows(*pa, DT == kBF16 ? SPEC_BF16 : SPEC_F32, VEC, st);
   }
 }
 
@@ -1387,7 +1516,8 @@ static int verify_impl(const void* draft, const void* target, int dtype, const i
                        const int32_t* in_len, int32_t* out_tokens, int32_t* out_acc,
                        int32_t* out_fr, uint64_t* out_mask, int32_t* out_len,
                        const spec_diag* diag, void* ws, size_t ws_bytes, void* stream,
-                       int saguaro, float eps) {
+                       int saguaro, float eps, int32_t* cand = nullptr, int32_t* hit = nullptr,
+                       int32_t* cand_idx = nullptr) {
   if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_EDTYPE;
   if (!sizes_ok(B, gamma, V)) return SPEC_EINVAL;
   if (!(T > 0.f) || !std::isfinite(T)) return SPEC_EINVAL;
@@ -1398,7 +1528,7 @@ static int verify_impl(const void* draft, const void* target, int dtype, const i
   const Layout L = layout(B, gamma, V);
   // Every launch (and the fused kernel's item count) stays within one grid
   // dimension of 2^32 - 1 work-items, with block numbers below 2^31.
-  const int64_t items = (int64_t)B * ((2 * gamma + 1) * L.nc + 2 * L.nt + 3);
+  const int64_t items = (int64_t)B * ((2 * gamma + 2) * L.nc + 2 * L.nt + 3);
   if (items * kThreads > (int64_t)UINT_MAX || items > (int64_t)INT_MAX) return SPEC_EINVAL;
   if (!ws || ws_bytes < L.total) return SPEC_EWORKSPACE;
 
@@ -1425,6 +1555,7 @@ static int verify_impl(const void* draft, const void* target, int dtype, const i
   a.tiles = reinterpret_cast<uint64_t*>(w + L.tiles_off);
   a.mass = reinterpret_cast<uint64_t*>(w + L.mass_off);
   a.rsum = reinterpret_cast<uint64_t*>(w + L.rsum_off);
+  a.cpart = reinterpret_cast<Top3*>(w + L.cpart_off);
   a.B = B;
   a.gamma = gamma;
   a.V = V;
@@ -1447,12 +1578,28 @@ static int verify_impl(const void* draft, const void* target, int dtype, const i
   a.saguaro = saguaro;
   a.eps = eps;
 
+  PredictArgs p;
+  if (cand) {
+    p.draft = draft;
+    p.accepted = out_acc;
+    p.out_tokens = out_tokens;
+    p.cand = cand;
+    p.hit = hit;
+    p.cand_idx = cand_idx;
+    p.part = a.cpart;
+    p.B = B;
+    p.gamma = gamma;
+    p.V = V;
+    p.nc = L.nc;
+    p.chunk = L.chunk;
+  }
+  const PredictArgs* pa = cand ? &p : nullptr;
   const bool vec = (V % 8 == 0) && ((uintptr_t)draft % 16 == 0) && ((uintptr_t)target % 16 == 0);
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   hipError_t e;
-  if (dtype == SPEC_BF16) e = vec ? launch_all<kBF16, true>(a, st) : launch_all<kBF16, false>(a, st);
-  else e = vec ? launch_all<kF32, true>(a, st) : launch_all<kF32, false>(a, st);
+  if (dtype == SPEC_BF16) e = vec ? launch_all<kBF16, true>(a, pa, st) : launch_all<kBF16, false>(a, pa, st);
+  else e = vec ? launch_all<kF32, true>(a, pa, st) : launch_all<kF32, false>(a, pa, st);
   return e == hipSuccess ? SPEC_OK : SPEC_ELAUNCH;
 }
 
@@ -1485,6 +1632,20 @@ int spec_verify_saguaro(const void* draft_logits, const void* target_logits, int
   return sv::verify_impl(draft_logits, target_logits, dtype, draft_tokens, u_accept, u_sample, B,
                          gamma, V, temperature, in_len, out_tokens, out_accepted, out_first_reject,
                          out_accept_mask, out_len, diag, workspace, workspace_bytes, stream, 1, eps);
+}
+
+int spec_verify_predict(const void* draft_logits, const void* target_logits, int dtype,
+                        const int32_t* draft_tokens, const float* u_accept, const float* u_sample,
+                        int B, int gamma, int V, float temperature, const int32_t* in_len,
+                        int32_t* out_tokens, int32_t* out_accepted, int32_t* out_first_reject,
+                        uint64_t* out_accept_mask, int32_t* out_len, const spec_diag* diag,
+                        int saguaro, float eps, int32_t* cand, int32_t* hit, int32_t* cand_idx,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  if (!cand || (saguaro != 0 && saguaro != 1)) return SPEC_EINVAL;
+  return sv::verify_impl(draft_logits, target_logits, dtype, draft_tokens, u_accept, u_sample, B,
+                         gamma, V, temperature, in_len, out_tokens, out_accepted, out_first_reject,
+                         out_accept_mask, out_len, diag, workspace, workspace_bytes, stream, saguaro,
+                         eps, cand, hit, cand_idx);
 }
 
 const char* spec_status_str(int status) {

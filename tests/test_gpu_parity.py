@@ -244,3 +244,88 @@ def test_predict_edges(dtype):
                        "target": draft[:, :, :2].copy()})
     cand2, _, _ = _predict(small)
     np.testing.assert_array_equal(cand2, O.predict_outcomes(W.decode_f64(small.draft, dtype)))
+
+
+# --------------------------------------------------------------------------- verification + prediction in one pass
+
+def _verify_predict(batch, mode="residual", eps=0.0, db=None, ws=None):
+    import rejection_sampling_verify_12_amd as R
+    H.say(f"[verify_predict] {batch.name} B={batch.B} gamma={batch.gamma} V={batch.V} "
+          f"{batch.dtype} mode={mode} eps={eps}")
+    db = db or H.to_device(batch)
+    if ws is None:
+        dt = R.SPEC_BF16 if batch.dtype == "bf16" else R.SPEC_F32
+        ws = R.new_workspace(R.spec_workspace_bytes(batch.B, batch.gamma, batch.V, dt), "cuda")
+    out, pred = R.spec_verify_predict(db.draft, db.target, db.tokens, db.u_accept, db.u_sample,
+                                      batch.T, in_len=db.in_len, workspace=ws,
+                                      saguaro=(mode == "saguaro"), eps=eps)
+    torch.cuda.synchronize()
+    assert int(ws[:4].view(torch.int32).item()) == 0, "bounded wait timed out"
+    return {"tokens": out.tokens.cpu().numpy(), "accepted": out.accepted.cpu().numpy(),
+            "first_reject": out.first_reject.cpu().numpy(),
+            "mask": out.accept_mask.cpu().numpy().view(np.uint64),
+            "out_len": out.out_len.cpu().numpy(), "cand": pred.cand.cpu().numpy(),
+            "hit": pred.hit.cpu().numpy(), "cand_idx": pred.cand_idx.cpu().numpy()}
+
+
+def _check_verify_predict(batch, got, mode="residual", eps=0.0):
+    """Verification outputs equal the verification-only call's; candidates equal
+    the oracle's top-3; hit and index follow from them and the outputs."""
+    alone = H.run_gpu(batch, mode, eps, diag=False)
+    for k in ("tokens", "accepted", "first_reject", "mask", "out_len"):
+        np.testing.assert_array_equal(got[k], alone[k], err_msg=k)
+    ref_cand = O.predict_outcomes(batch.draft64())
+    np.testing.assert_array_equal(got["cand"], ref_cand)
+    ref_hit, ref_idx = O.predict_hits(ref_cand, got["accepted"], got["tokens"])
+    np.testing.assert_array_equal(got["hit"], ref_hit)
+    np.testing.assert_array_equal(got["cand_idx"], ref_idx)
+
+
+@pytest.mark.parametrize("mode,eps", [("residual", 0.0), ("saguaro", 0.0)])
+def test_verify_predict_workload(mode, eps):
+    batch = workload("B128_g4_V128256_bf16")
+    got = _verify_predict(batch, mode, eps)
+    _check_verify_predict(batch, got, mode, eps)
+    H.say(f"[verify_predict] hit rate {got['hit'].mean():.3f}")
+
+
+@pytest.mark.parametrize("V", [50000, 50001, 2048 * 3 + 8])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_verify_predict_ragged(V, dtype):
+    """Partial last chunks and partial lane periods (V = 50000, 6152), and a V
+    the packed path cannot take (50001)."""
+    batch = random_batch(5, 3, V, dtype, 1.0, seed=4100 + V % 97)
+    _check_verify_predict(batch, _verify_predict(batch))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_verify_predict_ties_and_bad_rows(dtype):
+    """Heavy ties across lanes (logits rounded to 0.1), +-0, an all -inf draft
+    row, the maximum at the last id, a NaN and a +inf draft logit; then a second,
+    smaller call on the same workspace."""
+    B, g, V = 6, 3, 40000
+    rng = np.random.default_rng(11)
+    d64 = np.round(rng.normal(size=(B, g + 1, V)), 1)
+    d64[0, 0, :] = 0.0
+    d64[0, 0, 5] = -0.0
+    d64[2, 3, V - 1] = 50.0
+    d64[3, 1, :] = -np.inf
+    d64[4, 2, 7] = np.inf
+    t64 = d64 + 0.3 * rng.normal(size=d64.shape)
+    t64[3, 1, :] = 0.0
+    draft, target = W.encode(d64, dtype), W.encode(np.nan_to_num(t64, posinf=50.0), dtype)
+    draft[1, 1, 100] = np.uint16(0x7FC0) if dtype == "bf16" else np.float32(np.nan)
+    tokens = rng.integers(0, V, size=(B, g)).astype(np.int32)
+    batch = W.Batch(name=f"pred_ties_{dtype}", B=B, gamma=g, V=V, T=1.0, dtype=dtype,
+                    draft=draft, target=target, draft_tokens=tokens,
+                    u_accept=W.uniforms24(W.philox(12, 1), (B, g)),
+                    u_sample=W.uniforms24(W.philox(12, 2), (B, g + 1)),
+                    in_len=np.zeros(B, np.int32))
+    import rejection_sampling_verify_12_amd as R
+    dt = R.SPEC_BF16 if dtype == "bf16" else R.SPEC_F32
+    ws = R.new_workspace(R.spec_workspace_bytes(B, g, V, dt), "cuda")
+    _check_verify_predict(batch, _verify_predict(batch, ws=ws))
+    small = W.Batch(**{**batch.__dict__, "B": 3, "draft": draft[3:].copy(), "target": target[3:].copy(),
+                       "draft_tokens": tokens[3:].copy(), "u_accept": batch.u_accept[3:].copy(),
+                       "u_sample": batch.u_sample[3:].copy(), "in_len": batch.in_len[3:].copy()})
+    _check_verify_predict(small, _verify_predict(small, ws=ws))
