@@ -23,6 +23,10 @@ from .verify import (  # noqa: F401
     predict_outcomes,
     predict_hits,
     SeqResult,
+    first_argmax,
+    verify_greedy,
+    verify_greedy_one,
+    GreedyResult,
 )
 from .closed_forms import (  # noqa: F401
     acceptance_probability,

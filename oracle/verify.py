@@ -45,6 +45,13 @@ notes with its justification):
   tokens -1, mask 0, first_reject -1, out_len = in_len.
 * p(x) = 0 at a draft token: accept iff q(x) > 0.
 * out_len = in_len + k + 1 (tokens committed this round).
+* Greedy verification is the temperature -> 0 limit of the rule: accept x_i
+  iff it is the target's most likely token at position i, and emit the
+  target's most likely token at the stopping position (the correction after a
+  rejection, the bonus after gamma acceptances).  Equal logits: the lowest
+  token id.  It reads only target rows; one holding a NaN makes the sequence
+  invalid when the rule reads it (rows 0..gamma-1 always, row gamma iff k =
+  gamma); +-inf logits are ordinary values there.
 """
 from __future__ import annotations
 
@@ -229,6 +236,63 @@ def verify(draft64, target64, draft_tokens, u_accept, u_sample, T, mode="residua
     in_len = np.zeros(B, dtype=np.int64) if in_len is None else np.asarray(in_len)
     return [verify_one(draft64[b], target64[b], draft_tokens[b], u_accept[b], u_sample[b],
                        T, mode, eps, int(in_len[b])) for b in range(B)]
+
+
+# ---------------------------------------------------------------------------
+# Greedy verification: the temperature -> 0 limit ([SD] section 5.4 ties the
+# rule to the sampling temperature; "SSSD: Simply-Scalable Speculative
+# Decoding" (papernotes.org note), training-strategy section: speculation runs
+# in greedy and in speculative-sampling mode).
+
+def first_argmax(row64: np.ndarray) -> int:
+    """The lowest token id among the row's largest logits (row without NaN)."""
+    l = np.asarray(row64, dtype=np.float64)
+    m = l.max()
+    return int(np.nonzero(l == m)[0][0])
+
+
+@dataclasses.dataclass
+class GreedyResult:
+    valid: bool
+    accepted: int        # k, or -1 when invalid
+    first_reject: int    # k if k < gamma else -1
+    mask: int            # bit i: x_i is the target's argmax at position i
+    tokens: np.ndarray   # [gamma+1]: x_0..x_{k-1}, argmax q_k, then -1
+    out_len: int
+
+
+def verify_greedy_one(target64, tokens, in_len=0) -> GreedyResult:
+    """Greedy verification of one sequence: target64 [gamma+1, V] logits,
+    tokens [gamma] draft tokens."""
+    t = np.asarray(target64, dtype=np.float64)
+    gamma = len(tokens)
+    V = t.shape[-1]
+    x = np.asarray(tokens, dtype=np.int64)
+    bad = GreedyResult(False, -1, -1, 0, np.full(gamma + 1, -1, dtype=np.int32), int(in_len))
+    if ((x < 0) | (x >= V)).any() or np.isnan(t[:gamma]).any():
+        return bad
+    g = [first_argmax(t[i]) for i in range(gamma)]
+    mask = 0
+    for i in range(gamma):
+        if x[i] == g[i]:
+            mask |= 1 << i
+    k = gamma
+    for i in range(gamma):
+        if x[i] != g[i]:
+            k = i
+            break
+    if k == gamma and np.isnan(t[gamma]).any():
+        return bad
+    out = np.full(gamma + 1, -1, dtype=np.int32)
+    out[:k] = x[:k]
+    out[k] = g[k] if k < gamma else first_argmax(t[gamma])
+    return GreedyResult(True, k, k if k < gamma else -1, mask, out, int(in_len) + k + 1)
+
+
+def verify_greedy(target64, draft_tokens, in_len=None) -> list[GreedyResult]:
+    B = len(draft_tokens)
+    in_len = np.zeros(B, dtype=np.int64) if in_len is None else np.asarray(in_len)
+    return [verify_greedy_one(target64[b], draft_tokens[b], int(in_len[b])) for b in range(B)]
 
 
 # ---------------------------------------------------------------------------

@@ -432,3 +432,90 @@ def test_predict_hit_rate_closed_form():
             assert idx[b] // 3 == k and cand[k, idx[b] % 3] == res[b].tokens[k]
         else:
             assert idx[b] == -1
+
+
+# --------------------------------------------------------------------------- greedy verification
+
+def test_greedy_is_the_zero_temperature_limit():
+    """With distinct row maxima (gaps >= 0.5) and draft tokens = the draft's own
+    argmax, the sampled rule at T = 0.002 (every probability off the maximum is
+    below e^-250) must give exactly the greedy result for uniforms in
+    [1e-3, 1 - 1e-3): accept iff the target's argmax agrees, emit its argmax."""
+    rng = np.random.default_rng(21)
+    T = 0.002
+    for trial in range(40):
+        g = int(rng.integers(1, 6))
+        V = int(rng.integers(5, 60))
+        d = np.stack([rng.permutation(V) * 0.5 for _ in range(g + 1)])
+        t = d.copy()
+        for i in range(g + 1):            # move the target's maximum elsewhere sometimes
+            if rng.random() < 0.35:
+                a, b = np.argmax(t[i]), int(rng.integers(V))
+                t[i, [a, b]] = t[i, [b, a]]
+        x = np.argmax(d[:g], axis=1)
+        ua = rng.uniform(1e-3, 1 - 1e-3, g)
+        us = rng.uniform(1e-3, 1 - 1e-3, g + 1)
+        s = O.verify_one(d, t, x, ua, us, T, in_len=3)
+        r = O.verify_greedy_one(t, x, in_len=3)
+        assert (r.accepted, r.mask, r.out_len) == (s.accepted, s.mask, s.out_len), trial
+        np.testing.assert_array_equal(r.tokens, s.tokens)
+
+
+def test_greedy_speculation_reproduces_target_greedy_decoding():
+    """Greedy speculative decoding of a Markov chain (draft proposes its own
+    argmax continuation of gamma tokens, the target verifies them) emits
+    exactly the target's own greedy decode, whatever the draft."""
+    rng = np.random.default_rng(5)
+    V = 7
+    for trial in range(20):
+        Pd = rng.normal(size=(V, V))
+        Qt = Pd + rng.normal(scale=1.0, size=(V, V))   # overlapping, not equal
+        g = int(rng.integers(1, 7))
+        prev, out = 0, []
+        while len(out) < 64:
+            x, c = [], prev
+            for _ in range(g):                            # draft's greedy proposal
+                c = int(np.argmax(Pd[c]))
+                x.append(c)
+            ctx = [prev] + x                              # target scores gamma+1 positions
+            t = np.stack([Qt[c] for c in ctx])
+            r = O.verify_greedy_one(t, np.array(x))
+            emitted = r.tokens[: r.accepted + 1].tolist()
+            assert len(emitted) >= 1
+            out += emitted
+            prev = out[-1]
+        ref, c = [], 0
+        while len(ref) < len(out):
+            c = int(np.argmax(Qt[c]))
+            ref.append(c)
+        assert out == ref, trial
+
+
+def test_greedy_ties_and_invalid_rows():
+    # Ties go to the lowest id, as numpy's argmax does.
+    rng = np.random.default_rng(8)
+    for _ in range(50):
+        row = rng.integers(0, 3, size=int(rng.integers(1, 40))).astype(np.float64)
+        assert O.first_argmax(row) == int(np.argmax(row))
+    assert O.first_argmax(np.array([-np.inf, -np.inf])) == 0
+    assert O.first_argmax(np.array([1.0, np.inf, 3.0, np.inf])) == 1
+    assert O.first_argmax(np.array([-0.0, 0.0])) == 0
+    g, V = 2, 5
+    t = np.zeros((g + 1, V))
+    t[0, 3] = t[1, 1] = t[2, 4] = 1.0
+    r = O.verify_greedy_one(t, [3, 1], in_len=4)
+    assert (r.accepted, r.first_reject, r.mask, r.out_len) == (2, -1, 3, 7)
+    assert r.tokens.tolist() == [3, 1, 4]
+    r = O.verify_greedy_one(t, [3, 2])
+    assert (r.accepted, r.first_reject, r.mask) == (1, 1, 1) and r.tokens.tolist() == [3, 1, -1]
+    r = O.verify_greedy_one(t, [0, 1])          # a later acceptance still shows in the mask
+    assert (r.accepted, r.mask) == (0, 2) and r.tokens.tolist() == [3, -1, -1]
+    t2 = t.copy()
+    t2[2, 0] = np.nan                            # row gamma: read only after gamma acceptances
+    assert O.verify_greedy_one(t2, [3, 2]).accepted == 1
+    assert O.verify_greedy_one(t2, [3, 1]).accepted == -1
+    t3 = t.copy()
+    t3[1, 2] = np.nan                            # rows < gamma are always read
+    assert O.verify_greedy_one(t3, [0, 1]).accepted == -1
+    r = O.verify_greedy_one(t, [3, 5], in_len=9)  # token outside [0, V)
+    assert (r.accepted, r.out_len, r.mask) == (-1, 9, 0) and (r.tokens == -1).all()
