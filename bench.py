@@ -37,7 +37,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--mode", choices=("residual", "saguaro"), default="residual")
+    ap.add_argument("--mode", choices=("residual", "saguaro", "greedy"), default="residual",
+                    help="greedy: temperature -> 0 verification of the draft's own argmax tokens "
+                         "(reads target rows only)")
     ap.add_argument("--eps", type=float, default=0.0)
     ap.add_argument("--predict", action="store_true",
                     help="each step also predicts outcomes (draft top-3 per position, hits), in "
@@ -76,15 +78,19 @@ def traffic_record(workload: str, mode: str):
     return rec.get("bytes_per_call")
 
 
-def cpu_baseline(batch, mode: str, eps: float, budget_s: float) -> dict:
+def cpu_baseline(batch, mode: str, eps: float, budget_s: float, tokens=None) -> dict:
     """The fp64 oracle on the first sequences of the same workload, one thread."""
     import oracle as O
     import workloads as W
     t0 = time.perf_counter()
     n = 0
     while n < batch.B:
-        O.verify_one(W.decode_f64(batch.draft[n], batch.dtype), W.decode_f64(batch.target[n], batch.dtype),
-                     batch.draft_tokens[n], batch.u_accept[n], batch.u_sample[n], batch.T, mode, eps)
+        if mode == "greedy":
+            O.verify_greedy_one(W.decode_f64(batch.target[n], batch.dtype), tokens[n])
+        else:
+            O.verify_one(W.decode_f64(batch.draft[n], batch.dtype),
+                         W.decode_f64(batch.target[n], batch.dtype), batch.draft_tokens[n],
+                         batch.u_accept[n], batch.u_sample[n], batch.T, mode, eps)
         n += 1
         if time.perf_counter() - t0 > budget_s:
             break
@@ -123,7 +129,15 @@ def main():
           flush=True)
     B, g, V = batch.B, batch.gamma, batch.V
     dt_code = R.SPEC_BF16 if batch.dtype == "bf16" else R.SPEC_F32
-    bytes_alg = R.bytes_algorithmic(B, g, V, dt_code)
+    if args.predict and args.mode == "greedy":
+        sys.exit("--predict is not available with --mode greedy")
+    greedy = args.mode == "greedy"
+    es = 2 if batch.dtype == "bf16" else 4
+    if greedy:   # target rows, draft tokens, lengths and the outputs
+        bytes_alg = (B * (g + 1) * V * es + B * g * 4 + B * 4 + B * (g + 1) * 4
+                     + B * (4 + 4 + 8 + 4))
+    else:
+        bytes_alg = R.bytes_algorithmic(B, g, V, dt_code)
     if args.predict:   # draft row gamma, which only the prediction reads
         bytes_alg += B * V * (2 if batch.dtype == "bf16" else 4)
     nsets = args.sets or max(1, -(-(1 << 30) // max(bytes_alg, 1)) + (1 if bytes_alg < (1 << 30) else 0))
@@ -137,11 +151,15 @@ def main():
     sets = [(base_d, base_t)]
     for s in range(1, nsets):   # extra copies so that successive calls miss the 256 MB cache
         sets.append((base_d.clone(), base_t.clone()))
-    tok = torch.from_numpy(batch.draft_tokens).to(dev)
+    gtok = None
+    if greedy:   # the draft's greedy tokens
+        gtok = np.argmax(W.decode_f64(batch.draft[:, :g], batch.dtype), axis=-1).astype(np.int32)
+    tok = torch.from_numpy(gtok if greedy else batch.draft_tokens).to(dev)
     ua = torch.from_numpy(batch.u_accept).to(dev)
     us = torch.from_numpy(batch.u_sample).to(dev)
     out = R.alloc_outputs(B, g, dev)
-    ws = R.new_workspace(R.spec_workspace_bytes(B, g, V, dt_code), dev)
+    ws = R.new_workspace((R.spec_greedy_workspace_bytes if greedy else R.spec_workspace_bytes)(
+        B, g, V, dt_code), dev)
     stream = torch.cuda.current_stream(dev)
     sep = args.predict and args.predict_separate
     pws = R.new_workspace(R.spec_predict_workspace_bytes(B, g, V, dt_code), dev) if sep else None
@@ -150,7 +168,9 @@ def main():
     def call(i):
         nonlocal pout
         d, t = sets[i % nsets]
-        if args.predict and not sep:
+        if greedy:
+            R.spec_verify_greedy(t, tok, out=out, workspace=ws, stream=stream)
+        elif args.predict and not sep:
             R.spec_verify_predict(d, t, tok, ua, us, batch.T, out=out, pred=pout, workspace=ws,
                                   stream=stream, saguaro=args.mode == "saguaro", eps=args.eps)
         elif args.mode == "residual":
@@ -206,12 +226,13 @@ def main():
                      "p90": float(np.percentile(per_call_ms, 90))},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic_record(args.workload, args.mode),
-                     "kernel": "one spec_verify call (every kernel it launches), event-timed on its stream",
+                     "kernel": f"one {'spec_verify_greedy' if greedy else 'spec_verify'} call (every "
+                               "kernel it launches), event-timed on its stream",
                      "bytes_alg": bytes_alg},
         "source_digest": source_digest(),
     }
     if not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline(batch, args.mode, args.eps, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(batch, args.mode, args.eps, args.cpu_seconds, gtok)
     print(json.dumps(result), flush=True)
 
 

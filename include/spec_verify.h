@@ -187,6 +187,39 @@ int spec_verify_predict(const void* draft_logits, const void* target_logits, int
                         int saguaro, float eps, int32_t* cand, int32_t* hit, int32_t* cand_idx,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Bytes of device workspace spec_verify_greedy needs (same zero-on-entry rule
+ * and error word as spec_workspace_bytes; 0 for B == 0 or arguments
+ * spec_verify_greedy would reject).
+ */
+size_t spec_greedy_workspace_bytes(int B, int gamma, int V, int dtype);
+
+/*
+ * Greedy verification: the temperature -> 0 limit of the rule
+ * ("Speculative Decoding: small model guesses, large model verifies",
+ * sections 3 and 5.4; greedy and sampling modes as in "SSSD: Simply-Scalable
+ * Speculative Decoding", training-strategy section).  With g_i the lowest
+ * token id among the largest logits of target row i:
+ *   - position i is accepted iff draft_tokens[b][i] == g_i (all gamma
+ *     decisions are reported in the mask);
+ *   - k = the first rejected position, or gamma;
+ *   - the emitted token is g_k (the correction after a rejection, the bonus
+ *     from row gamma after gamma acceptances).
+ * Only target rows are read (no draft logits, no uniforms, no temperature).
+ *   target_logits: [B][gamma+1][V] of dtype; draft_tokens: [B][gamma] int32.
+ *   in_len and the outputs are as in spec_verify.
+ * A sequence is invalid (accepted = -1, tokens -1, first_reject -1, mask 0,
+ * out_len = in_len) when a draft token lies outside [0, V) or a row the rule
+ * reads holds a NaN: rows 0..gamma-1 always, row gamma iff k == gamma.
+ * Infinite logits are ordinary values here.  Host-checkable errors as for
+ * spec_verify; the workspace is spec_greedy_workspace_bytes() bytes.
+ */
+int spec_verify_greedy(const void* target_logits, int dtype, const int32_t* draft_tokens, int B,
+                       int gamma, int V, const int32_t* in_len, int32_t* out_tokens,
+                       int32_t* out_accepted, int32_t* out_first_reject,
+                       uint64_t* out_accept_mask, int32_t* out_len, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
 /* A static, human-readable description of a status code. */
 const char* spec_status_str(int status);
 

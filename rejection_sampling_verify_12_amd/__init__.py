@@ -20,7 +20,7 @@ SPEC_F32, SPEC_BF16 = 0, 1
 
 EXPORTED = ("spec_workspace_bytes", "spec_verify", "spec_verify_saguaro",
             "spec_predict_workspace_bytes", "spec_predict_outcomes", "spec_verify_predict",
-            "spec_status_str")
+            "spec_greedy_workspace_bytes", "spec_verify_greedy", "spec_status_str")
 
 
 class SpecDiag(ctypes.Structure):
@@ -56,6 +56,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.spec_predict_outcomes.restype = i32
     lib.spec_verify_predict.argtypes = verify_args[:-3] + [i32, f32, vp, vp, vp] + verify_args[-3:]
     lib.spec_verify_predict.restype = i32
+    lib.spec_greedy_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.spec_greedy_workspace_bytes.restype = sz
+    lib.spec_verify_greedy.argtypes = [vp, i32, vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.spec_verify_greedy.restype = i32
     lib.spec_status_str.argtypes = [i32]
     lib.spec_status_str.restype = ctypes.c_char_p
     _lib = lib
@@ -211,6 +215,34 @@ def spec_predict_outcomes(draft_logits, accepted=None, out_tokens=None, out=None
                                    _ptr(out_tokens), out.cand.data_ptr(), _ptr(out.hit),
                                    _ptr(out.cand_idx), workspace.data_ptr(), workspace.numel(),
                                    _stream_handle(stream, dev))
+    if st != SPEC_OK:
+        raise SpecError(st)
+    return out
+
+
+def spec_greedy_workspace_bytes(B: int, gamma: int, V: int, dtype: int) -> int:
+    return int(load_library().spec_greedy_workspace_bytes(B, gamma, V, dtype))
+
+
+def spec_verify_greedy(target_logits, draft_tokens, in_len=None, out=None, workspace=None,
+                       stream=None) -> VerifyOut:
+    """Greedy (temperature -> 0) verification of a [B, gamma+1, V] batch of
+    target logits (see spec_verify.h)."""
+    lib = load_library()
+    B, G1, V = target_logits.shape
+    gamma = G1 - 1
+    _check_dev(target_logits, draft_tokens, in_len)
+    dt = _dtype_code(target_logits)
+    dev = target_logits.device
+    if out is None:
+        out = alloc_outputs(B, gamma, dev)
+    if workspace is None:
+        workspace = new_workspace(spec_greedy_workspace_bytes(B, gamma, V, dt), dev)
+    st = lib.spec_verify_greedy(target_logits.data_ptr(), dt, draft_tokens.data_ptr(), B, gamma, V,
+                                _ptr(in_len), out.tokens.data_ptr(), out.accepted.data_ptr(),
+                                out.first_reject.data_ptr(), out.accept_mask.data_ptr(),
+                                out.out_len.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                _stream_handle(stream, dev))
     if st != SPEC_OK:
         raise SpecError(st)
     return out

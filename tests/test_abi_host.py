@@ -120,3 +120,47 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
     monkeypatch.setattr(R, "_lib", None)
     with pytest.raises(RuntimeError, match="no CPU fallback"):
         R.load_library(str(tmp_path / "absent.so"))
+
+
+def test_greedy_rejects_bad_arguments():
+    lib = R.load_library()
+
+    def call(**kw):
+        a = dict(target=FAKE, dtype=R.SPEC_BF16, tokens=FAKE, B=4, gamma=3, V=1000, in_len=None,
+                 out_tokens=FAKE, out_acc=FAKE, out_fr=None, out_mask=None, out_len=None,
+                 ws=FAKE, ws_bytes=1 << 30, stream=None)
+        a.update(kw)
+        return lib.spec_verify_greedy(*a.values())
+
+    assert call(B=-1) == R.SPEC_EINVAL
+    assert call(gamma=0) == R.SPEC_EINVAL
+    assert call(gamma=64) == R.SPEC_EINVAL
+    assert call(V=0) == R.SPEC_EINVAL
+    assert call(dtype=5) == R.SPEC_EDTYPE
+    assert call(target=None) == R.SPEC_EINVAL
+    assert call(tokens=None) == R.SPEC_EINVAL
+    assert call(out_tokens=None) == R.SPEC_EINVAL
+    assert call(out_acc=None) == R.SPEC_EINVAL
+    assert call(ws=None) == R.SPEC_EWORKSPACE
+    assert call(ws_bytes=8) == R.SPEC_EWORKSPACE
+    assert call(B=0, target=None, ws=None) == R.SPEC_OK
+    assert R.spec_greedy_workspace_bytes(256, 8, 152064, R.SPEC_BF16) > 0
+    assert R.spec_greedy_workspace_bytes(0, 8, 152064, R.SPEC_BF16) == 0
+    assert R.spec_greedy_workspace_bytes(4, 64, 100, R.SPEC_BF16) == 0
+
+
+def test_verify_predict_rejects_bad_arguments():
+    lib = R.load_library()
+
+    def call(saguaro=0, eps=0.0, cand=FAKE, **kw):
+        a = dict(draft=FAKE, target=FAKE, dtype=R.SPEC_BF16, tokens=FAKE, ua=FAKE, us=FAKE, B=4,
+                 gamma=3, V=1000, T=1.0, in_len=None, out_tokens=FAKE, out_acc=FAKE, out_fr=None,
+                 out_mask=None, out_len=None, diag=None)
+        a.update(kw)
+        return lib.spec_verify_predict(*a.values(), saguaro, eps, cand, None, None, FAKE, 1 << 30, None)
+
+    assert call(cand=None) == R.SPEC_EINVAL
+    assert call(saguaro=2) == R.SPEC_EINVAL
+    assert call(saguaro=1, eps=-1.0) == R.SPEC_EINVAL
+    assert call(T=0.0) == R.SPEC_EINVAL
+    assert call(dtype=3) == R.SPEC_EDTYPE
