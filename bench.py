@@ -67,7 +67,8 @@ def source_digest() -> str:
 
 def traffic_record(workload: str, mode: str):
     """HBM bytes per call from committed rocprofv3 counter runs, if they were
-    taken on the current kernel sources; None otherwise."""
+    taken on the current kernel sources; None otherwise.  mode: residual,
+    saguaro or greedy, with "_predict" for the fused prediction."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}_{mode}.json")
     if not os.path.exists(path):
         return None
@@ -225,7 +226,8 @@ def main():
                      "p50": float(np.percentile(per_call_ms, 50)),
                      "p90": float(np.percentile(per_call_ms, 90))},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic_record(args.workload, args.mode),
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic_record(
+                         args.workload, args.mode + ("_predict" if args.predict and not sep else "")),
                      "kernel": f"one {'spec_verify_greedy' if greedy else 'spec_verify'} call (every "
                                "kernel it launches), event-timed on its stream",
                      "bytes_alg": bytes_alg},
