@@ -19,6 +19,7 @@ from .verify import (  # noqa: F401
     saguaro_distribution,
     verify,
     verify_one,
+    verify_early_one,
     top3,
     predict_outcomes,
     predict_hits,

@@ -229,6 +229,75 @@ def verify_one(draft64, target64, tokens, u_accept, u_sample, T, mode="residual"
         px=px, qx=qx, resid_mass=S, token_prob=float(pi[y]), cdf_lo=lo, cdf_hi=hi)
 
 
+def verify_early_one(draft64, target64, tokens, u_accept, u_sample, T, mode="residual",
+                     eps=0.0, in_len=0) -> SeqResult:
+    """Early-exit verification of one sequence: the page's loop exactly as
+    written ([SD] section 3: test position i, stop at the first rejection),
+    reading a position's rows only when every earlier position was accepted.
+
+    Same arguments as verify_one.  What differs from verify_one:
+    * validity only concerns what the loop reads - draft tokens x_0..x_k,
+      draft rows 0..min(k, gamma-1), target rows 0..k (row gamma only when
+      k = gamma);
+    * the mask holds the decisions made, bits 0..k-1 (all set);
+    * row statistics, p(x) and q(x) exist only for the rows and positions read
+      (NaN elsewhere).
+    """
+    draft64 = np.asarray(draft64, dtype=np.float64)
+    target64 = np.asarray(target64, dtype=np.float64)
+    gamma = len(tokens)
+    V = draft64.shape[-1]
+    x = np.asarray(tokens, dtype=np.int64)
+    ua = np.asarray(u_accept, dtype=np.float64)
+    nan = np.full(gamma, np.nan)
+    a = nan.copy()
+    px, qx = nan.copy(), nan.copy()
+    row_max = np.full(2 * gamma + 1, np.nan)
+    row_logZ = np.full(2 * gamma + 1, np.nan)
+    k = gamma
+    p_k = q_k = None
+    for i in range(gamma):
+        if not (0 <= x[i] < V) or not (row_valid(draft64[i]) and row_valid(target64[i])):
+            return _invalid(gamma, in_len)
+        p, pm, plz = softmax_rows(draft64[i], T)
+        q, qm, qlz = softmax_rows(target64[i], T)
+        row_max[i], row_logZ[i] = pm, plz
+        row_max[gamma + i], row_logZ[gamma + i] = qm, qlz
+        px[i], qx[i] = p[x[i]], q[x[i]]
+        if px[i] > 0:
+            a[i] = min(1.0, qx[i] / px[i])
+        else:
+            a[i] = 1.0 if qx[i] > 0 else 0.0
+        if not ua[i] < a[i]:
+            k = i
+            p_k, q_k = p, q
+            break
+    us = float(np.asarray(u_sample, dtype=np.float64)[k])
+    if k < gamma:
+        w = residual_weights(p_k, q_k)
+        S = float(w.sum())
+        if S > 0:
+            pi = w / S if mode == "residual" else saguaro_distribution(p_k, w, eps)
+        else:
+            pi = q_k
+    else:
+        if not row_valid(target64[gamma]):
+            return _invalid(gamma, in_len)
+        q_g, qm, qlz = softmax_rows(target64[gamma], T)
+        row_max[2 * gamma], row_logZ[2 * gamma] = qm, qlz
+        S = 0.0
+        pi = q_g
+    y, lo, hi = choice(pi, us)
+    out = np.full(gamma + 1, -1, dtype=np.int32)
+    out[:k] = x[:k]
+    out[k] = y
+    return SeqResult(
+        valid=True, accepted=k, first_reject=k if k < gamma else -1, mask=(1 << k) - 1,
+        tokens=out, out_len=int(in_len) + k + 1, a=a, acc_margin=np.abs(ua - a),
+        sample_margin=min(us - lo, hi - us), row_max=row_max, row_logZ=row_logZ,
+        px=px, qx=qx, resid_mass=S, token_prob=float(pi[y]), cdf_lo=lo, cdf_hi=hi)
+
+
 def verify(draft64, target64, draft_tokens, u_accept, u_sample, T, mode="residual",
            eps=0.0, in_len=None) -> list[SeqResult]:
     """Verify a batch: [B, gamma+1, V] logits; one SeqResult per sequence."""

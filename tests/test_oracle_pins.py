@@ -519,3 +519,65 @@ def test_greedy_ties_and_invalid_rows():
     assert O.verify_greedy_one(t3, [0, 1]).accepted == -1
     r = O.verify_greedy_one(t, [3, 5], in_len=9)  # token outside [0, V)
     assert (r.accepted, r.out_len, r.mask) == (-1, 9, 0) and (r.tokens == -1).all()
+
+
+# --------------------------------------------------------------------------- early-exit verification
+
+def test_early_exit_loop_equals_all_tests_then_first_rejection():
+    """The page's loop with its break (early exit) and the all-positions
+    formulation (every test, then the first rejection) give the same round on
+    valid inputs; the early loop's mask is the full mask cut below k."""
+    rng = np.random.default_rng(31)
+    for trial in range(200):
+        g = int(rng.integers(1, 7))
+        V = int(rng.integers(2, 40))
+        d = rng.normal(size=(g + 1, V)) * 2
+        t = d + rng.normal(size=(g + 1, V)) * rng.uniform(0.05, 2.0)
+        x = rng.integers(0, V, size=g)
+        ua = rng.random(g)
+        us = rng.random(g + 1)
+        T = float(rng.choice([0.5, 1.0, 1.7]))
+        mode, eps = [("residual", 0.0), ("saguaro", 0.0), ("saguaro", 1e-8)][trial % 3]
+        f = O.verify_one(d, t, x, ua, us, T, mode, eps, in_len=2)
+        e = O.verify_early_one(d, t, x, ua, us, T, mode, eps, in_len=2)
+        assert (e.accepted, e.first_reject, e.out_len) == (f.accepted, f.first_reject, f.out_len)
+        np.testing.assert_array_equal(e.tokens, f.tokens)
+        assert e.mask == f.mask & ((1 << f.accepted) - 1)
+        assert e.token_prob == f.token_prob and (e.cdf_lo, e.cdf_hi) == (f.cdf_lo, f.cdf_hi)
+        k = f.accepted
+        np.testing.assert_array_equal(e.px[: k + 1 if k < g else g], f.px[: k + 1 if k < g else g])
+        assert np.isnan(e.px[k + 1:]).all()
+
+
+def test_early_exit_reads_only_up_to_the_first_rejection():
+    g, V = 3, 6
+    d = np.zeros((g + 1, V))
+    t = np.zeros((g + 1, V))
+    t[1, 0] = -np.inf              # q_1(x_1 = 0) = 0: position 1 always rejects
+    x = [1, 0, 2]
+    u = [0.5, 0.5, 0.5]
+    us = [0.3, 0.3, 0.3, 0.3]
+    assert O.verify_early_one(d, t, x, u, us, 1.0).accepted == 1
+    for bad in ("draft2", "target2", "target3", "token2"):
+        d2, t2, x2 = d.copy(), t.copy(), list(x)
+        if bad == "draft2":
+            d2[2, 4] = np.nan
+        elif bad == "target2":
+            t2[2, 1] = np.inf
+        elif bad == "target3":
+            t2[3, :] = -np.inf
+        else:
+            x2[2] = V
+        e = O.verify_early_one(d2, t2, x2, u, us, 1.0)
+        f = O.verify_one(d2, t2, x2, u, us, 1.0)
+        assert e.accepted == 1 and e.mask == 1 and f.accepted == -1, bad
+    d3 = d.copy()
+    d3[1, 3] = np.nan              # a row the loop does read
+    assert O.verify_early_one(d3, t, x, u, us, 1.0).accepted == -1
+    t4 = t.copy()
+    t4[1, 0] = 0.0                 # now every position accepts (p == q) ...
+    t4[3, 2] = np.nan              # ... and the bonus row is read
+    assert O.verify_early_one(d, t4, x, u, us, 1.0).accepted == -1
+    t4[3, 2] = 0.0
+    r = O.verify_early_one(d, t4, x, u, us, 1.0, in_len=4)
+    assert (r.accepted, r.mask, r.out_len) == (3, 7, 8)
