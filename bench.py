@@ -44,6 +44,9 @@ def parse():
     ap.add_argument("--predict", action="store_true",
                     help="each step also predicts outcomes (draft top-3 per position, hits), in "
                          "the same pass as the verification (spec_verify_predict)")
+    ap.add_argument("--early", action="store_true",
+                    help="early-exit verification (spec_verify_early): rows are read only up to the "
+                         "first rejection; the roofline prices the rows the rule reads")
     ap.add_argument("--predict-separate", action="store_true",
                     help="with --predict: verification, then the stand-alone prediction call")
     ap.add_argument("--sets", type=int, default=0,
@@ -130,8 +133,10 @@ def main():
           flush=True)
     B, g, V = batch.B, batch.gamma, batch.V
     dt_code = R.SPEC_BF16 if batch.dtype == "bf16" else R.SPEC_F32
-    if args.predict and args.mode == "greedy":
-        sys.exit("--predict is not available with --mode greedy")
+    if (args.predict or args.early) and args.mode == "greedy":
+        sys.exit("--predict and --early are not available with --mode greedy")
+    if args.predict and args.early:
+        sys.exit("--predict and --early do not combine")
     greedy = args.mode == "greedy"
     es = 2 if batch.dtype == "bf16" else 4
     if greedy:   # target rows, draft tokens, lengths and the outputs
@@ -171,6 +176,9 @@ def main():
         d, t = sets[i % nsets]
         if greedy:
             R.spec_verify_greedy(t, tok, out=out, workspace=ws, stream=stream)
+        elif args.early:
+            R.spec_verify_early(d, t, tok, ua, us, batch.T, out=out, workspace=ws, stream=stream,
+                                saguaro=args.mode == "saguaro", eps=args.eps)
         elif args.predict and not sep:
             R.spec_verify_predict(d, t, tok, ua, us, batch.T, out=out, pred=pout, workspace=ws,
                                   stream=stream, saguaro=args.mode == "saguaro", eps=args.eps)
@@ -200,6 +208,10 @@ def main():
     ms_step = wall * 1e3 / args.steps
     ev_ms = float(per_call_ms.mean())
     acc = out.accepted.cpu().numpy()
+    if args.early:   # the rows the loop reads: 2(k+1) rows before a rejection, 2 gamma + 1 after none
+        rows = np.where(acc < g, 2 * (acc + 1), 2 * g + 1)
+        small = R.bytes_algorithmic(B, g, V, dt_code) - (2 * g + 1) * B * V * es   # tokens, uniforms, outputs
+        bytes_alg = int(rows.sum()) * V * es + small
 
     achieved = bytes_alg / (ev_ms * 1e-3) / 1e9
     result = {
@@ -221,15 +233,17 @@ def main():
                                                          float(batch.alpha_target.max())],
                    "mean_accepted": float(acc.mean()),
                    "predict": ("separate" if sep else "fused") if args.predict else False,
+                   "early_exit": bool(args.early),
                    **({"hit_rate": float(pout.hit.float().mean().item())} if args.predict else {})},
         "event_ms": {"mean": ev_ms, "p10": float(np.percentile(per_call_ms, 10)),
                      "p50": float(np.percentile(per_call_ms, 50)),
                      "p90": float(np.percentile(per_call_ms, 90))},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic_record(
-                         args.workload, args.mode + ("_predict" if args.predict and not sep else "")),
-                     "kernel": f"one {'spec_verify_greedy' if greedy else 'spec_verify'} call (every "
-                               "kernel it launches), event-timed on its stream",
+                         args.workload, args.mode + ("_predict" if args.predict and not sep else "")
+                         + ("_early" if args.early else "")),
+                     "kernel": f"one {'spec_verify_greedy' if greedy else ('spec_verify_early' if args.early else 'spec_verify')} "
+                               "call (every kernel it launches), event-timed on its stream",
                      "bytes_alg": bytes_alg},
         "source_digest": source_digest(),
     }

@@ -188,6 +188,33 @@ int spec_verify_predict(const void* draft_logits, const void* target_logits, int
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Early-exit verification: the rule's loop with its break, reading a
+ * position's rows only while every earlier position was accepted
+ * ("Speculative Decoding: small model guesses, large model verifies",
+ * section 3: test position i, stop at the first rejection).  Arguments,
+ * workspace and outputs as spec_verify (saguaro = 0; eps ignored) or
+ * spec_verify_saguaro (saguaro = 1); any other saguaro value is SPEC_EINVAL.
+ * The tokens, k, first_reject and out_len equal spec_verify's; what differs:
+ *   - out_accept_mask holds the decisions the loop makes: bits 0..k-1 (all
+ *     set), never a decision after the first rejection;
+ *   - validity only concerns what the loop reads: draft tokens x_0..x_k
+ *     (x_0..x_{gamma-1} when k == gamma), draft and target rows 0..k (k <
+ *     gamma), target row gamma only when k == gamma;
+ *   - diagnostics exist only for the rows and positions read (other entries
+ *     are left unwritten).
+ * Positions are processed in order across the whole batch, and a rejection
+ * is published as soon as it is known, so the rows of later positions of
+ * that sequence are usually not read at all (how many are skipped depends on
+ * timing; the outputs do not).
+ */
+int spec_verify_early(const void* draft_logits, const void* target_logits, int dtype,
+                      const int32_t* draft_tokens, const float* u_accept, const float* u_sample,
+                      int B, int gamma, int V, float temperature, const int32_t* in_len,
+                      int32_t* out_tokens, int32_t* out_accepted, int32_t* out_first_reject,
+                      uint64_t* out_accept_mask, int32_t* out_len, const spec_diag* diag,
+                      int saguaro, float eps, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Bytes of device workspace spec_verify_greedy needs (same zero-on-entry rule
  * and error word as spec_workspace_bytes; 0 for B == 0 or arguments
  * spec_verify_greedy would reject).

@@ -20,7 +20,8 @@ SPEC_F32, SPEC_BF16 = 0, 1
 
 EXPORTED = ("spec_workspace_bytes", "spec_verify", "spec_verify_saguaro",
             "spec_predict_workspace_bytes", "spec_predict_outcomes", "spec_verify_predict",
-            "spec_greedy_workspace_bytes", "spec_verify_greedy", "spec_status_str")
+            "spec_greedy_workspace_bytes", "spec_verify_greedy", "spec_verify_early",
+            "spec_status_str")
 
 
 class SpecDiag(ctypes.Structure):
@@ -56,6 +57,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.spec_predict_outcomes.restype = i32
     lib.spec_verify_predict.argtypes = verify_args[:-3] + [i32, f32, vp, vp, vp] + verify_args[-3:]
     lib.spec_verify_predict.restype = i32
+    lib.spec_verify_early.argtypes = verify_args[:-3] + [i32, f32] + verify_args[-3:]
+    lib.spec_verify_early.restype = i32
     lib.spec_greedy_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.spec_greedy_workspace_bytes.restype = sz
     lib.spec_verify_greedy.argtypes = [vp, i32, vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -139,7 +142,7 @@ def alloc_outputs(B: int, gamma: int, device, diag: bool = False) -> VerifyOut:
 
 def _verify_call(saguaro: bool, draft_logits, target_logits, draft_tokens, u_accept, u_sample,
                  temperature: float, in_len=None, out: VerifyOut | None = None, diag: bool = False,
-                 workspace=None, stream=None, eps: float = 0.0, pred=None) -> VerifyOut:
+                 workspace=None, stream=None, eps: float = 0.0, pred=None, early=False) -> VerifyOut:
     lib = load_library()
     B, G1, V = draft_logits.shape
     gamma = G1 - 1
@@ -162,7 +165,9 @@ def _verify_call(saguaro: bool, draft_logits, target_logits, draft_tokens, u_acc
             out.first_reject.data_ptr(), out.accept_mask.data_ptr(), out.out_len.data_ptr(),
             ctypes.byref(dg) if dg is not None else None, workspace.data_ptr(),
             workspace.numel(), _stream_handle(stream, dev)]
-    if pred is not None:
+    if early:
+        st = lib.spec_verify_early(*args[:-3], int(saguaro), float(eps), *args[-3:])
+    elif pred is not None:
         _check_dev(*pred)
         st = lib.spec_verify_predict(*args[:-3], int(saguaro), float(eps), pred.cand.data_ptr(),
                                      _ptr(pred.hit), _ptr(pred.cand_idx), *args[-3:])
@@ -218,6 +223,16 @@ def spec_predict_outcomes(draft_logits, accepted=None, out_tokens=None, out=None
     if st != SPEC_OK:
         raise SpecError(st)
     return out
+
+
+def spec_verify_early(draft_logits, target_logits, draft_tokens, u_accept, u_sample, temperature,
+                      in_len=None, out=None, diag=False, workspace=None, stream=None,
+                      saguaro: bool = False, eps: float = 0.0) -> VerifyOut:
+    """Early-exit verification (residual, or Saguaro with ``saguaro=True``):
+    rows are read only up to the first rejection (see spec_verify.h)."""
+    return _verify_call(bool(saguaro), draft_logits, target_logits, draft_tokens, u_accept,
+                        u_sample, temperature, in_len, out, diag, workspace, stream,
+                        eps if saguaro else 0.0, None, True)
 
 
 def spec_greedy_workspace_bytes(B: int, gamma: int, V: int, dtype: int) -> int:

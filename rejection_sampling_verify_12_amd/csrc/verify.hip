@@ -84,6 +84,10 @@ enum : int { kModeTarget = 0, kModeResidual = 1, kModeSaguaro = 2, kModeSaguaroE
 #ifndef SV_LAG_FINAL
 #define SV_LAG_FINAL 200
 #endif
+// Early exit: lag of a position's test behind its rows (thousandths of a round).
+#ifndef SV_LAG_TEST
+#define SV_LAG_TEST 800
+#endif
 #ifndef SV_SAMPLE_NT
 #define SV_SAMPLE_NT 0
 #endif
@@ -139,8 +143,17 @@ __device__ __forceinline__ void clear_rec(SeqRec* p) {
 }
 
 // One 128-byte line per sequence: [0] = residual-mass and sampling items that
-// have read the decision record.
+// have read the decision record; [2..3] the drawn token's slot.  Early exit
+// also uses [4] = 64 - (a position known to stop the sequence), raised by
+// atomic max (0: none known), [5] = positions known accepted in a row from
+// position 0, [6] = position tests done.
 constexpr int kFlagStride = 32;
+constexpr int kStopWord = 4, kProgWord = 5, kTestsWord = 6;
+// A stream item of early exit that finds its position beyond a known stop
+// publishes these instead of its piece (their values are NaN; no real piece
+// has these words).
+constexpr uint64_t kSkipPiece = 1ull;
+constexpr unsigned kSkipRaw = 1u;
 
 struct VerifyArgs {
   const void* draft;
@@ -172,6 +185,7 @@ struct VerifyArgs {
   double invT;
   int saguaro;
   float eps;
+  int early;         // early exit: rows beyond the first rejection are not needed
 };
 
 template <int DT>
@@ -195,6 +209,9 @@ __device__ __forceinline__ bool give_up(const VerifyArgs& a, unsigned& polls) {
   }
   __builtin_amdgcn_s_sleep(2);
   return false;
+}
+__device__ __forceinline__ unsigned ld_dev_u32(const unsigned* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint64_t poll(const VerifyArgs& a, const uint64_t* p) {
   uint64_t w = ld_dev_u64(p);
@@ -624,6 +641,135 @@ __device__ void decide_item(const VerifyArgs& a, int b, DecideLds& sh) {
       rec.Mt = (float)Mt;   // exact below 2^24; otherwise Zt absorbs the rounding
       rec.Zt = ldexp(sh.Z[g + k], (int)fmin(fmax(Mt - (double)rec.Mt, -2000.0), 2000.0));
       const double K = (Mt - sh.M[k]) + log2(sh.Z[g + k] / sh.Z[k]);
+      rec.K_hi = (float)K;
+      rec.K_lo = (float)(K - (double)rec.K_hi);
+    }
+    store_rec(a.seq + b, rec);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Early exit: the accept test of one position ("Speculative Decoding: small
+// model guesses, large model verifies", section 3: test position i only once
+// every earlier position was accepted; stop at the first rejection).
+
+struct TestLds {
+  double M[2], Z[2];
+  float mr[2];
+  int bad[2];
+  int x;
+  float ldx, ltx, ux;
+  int decided, acc, bad_all;
+};
+
+// Position i of sequence b: merges (and clears) the pieces of draft row i and
+// target row i, tests the position, and publishes a rejection (or a bad row
+// or token) at once through the stop word, so later positions' stream items
+// skip their rows.  It then waits for the earlier positions - every one
+// accepted (the progress word reaches i) or one of them stopped the sequence
+// - which are decided by items with smaller block numbers.  If every earlier
+// position was accepted, this item decides: it advances the progress word
+// (accepted, more positions follow) or writes the decision record (rejected,
+// invalid, or the last position accepted).
+template <int DT>
+__device__ void test_item(const VerifyArgs& a, int b, int i, TestLds& sh) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int g = a.gamma, R = 2 * g + 1;
+  unsigned* fl = a.flag + (int64_t)b * kFlagStride;
+  if (wave == 0) {
+    if (lane < 32) {
+      const int h = lane >> 4;   // 0: draft row i, 1: target row i
+      double M, z;
+      float mr;
+      merge_row(a, b, h ? g + i : i, lane & 15, M, z, mr);
+      if ((lane & 15) == 0) {
+        sh.M[h] = M;
+        sh.Z[h] = z;
+        sh.mr[h] = mr;
+        sh.bad[h] = !row_ok(M, z);
+      }
+    }
+  } else if (wave == 1 && lane == 0) {
+    const int x = a.tokens[(int64_t)b * g + i];
+    float ldx = 0.f, ltx = 0.f;
+    if (x >= 0 && x < a.V) {
+      ldx = load_one<DT>(row_ptr<DT>(a, b, i), x);
+      ltx = load_one<DT>(row_ptr<DT>(a, b, g + i), x);
+    }
+    sh.x = x;
+    sh.ldx = ldx;
+    sh.ltx = ltx;
+    sh.ux = a.u_acc[(int64_t)b * g + i];
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const int x = sh.x;
+    const bool bad = x < 0 || x >= a.V || sh.bad[0] || sh.bad[1];
+    bool acc = false;
+    double pn = 0.0, qn = 0.0;
+    if (!bad) {
+      pn = exp2((double)sh.ldx * a.cTd - sh.M[0]);
+      qn = exp2((double)sh.ltx * a.cTd - sh.M[1]);
+      double ratio;
+      if (pn > 0.0) ratio = fmin(1.0, (qn * sh.Z[0]) / (pn * sh.Z[1]));
+      else ratio = qn > 0.0 ? 1.0 : 0.0;
+      acc = (double)sh.ux < ratio;
+    }
+    const unsigned mine = 64u - (unsigned)i;
+    if (bad || !acc) __hip_atomic_fetch_max(fl + kStopWord, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    bool decided = false;
+    if (i == 0) {
+      decided = true;
+    } else {
+      unsigned polls = 0;
+      for (;;) {
+        if (ld_dev_u32(fl + kStopWord) > mine) break;              // an earlier position stopped it
+        if (ld_dev_u32(fl + kProgWord) >= (unsigned)i) {           // every earlier one accepted
+          decided = true;
+          break;
+        }
+        if (give_up(a, polls)) break;
+      }
+    }
+    if (decided && !bad && acc && i + 1 < g)
+      __hip_atomic_store(fl + kProgWord, (unsigned)(i + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (decided && !bad) {
+      if (a.diag.px) a.diag.px[(int64_t)b * g + i] = pn / sh.Z[0];
+      if (a.diag.qx) a.diag.qx[(int64_t)b * g + i] = qn / sh.Z[1];
+      if (a.diag.row_max) {
+        a.diag.row_max[(int64_t)b * R + i] = (double)sh.mr[0] * a.invT;
+        a.diag.row_max[(int64_t)b * R + g + i] = (double)sh.mr[1] * a.invT;
+      }
+      if (a.diag.row_logZ) {
+        a.diag.row_logZ[(int64_t)b * R + i] = sh.M[0] * 0.69314718055994530942 + log(sh.Z[0]);
+        a.diag.row_logZ[(int64_t)b * R + g + i] = sh.M[1] * 0.69314718055994530942 + log(sh.Z[1]);
+      }
+    }
+    sh.decided = decided && (bad || !acc || i + 1 == g);
+    sh.acc = acc;
+    sh.bad_all = bad;
+    __hip_atomic_fetch_add(fl + kTestsWord, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (!sh.decided) return;
+  const bool valid = !sh.bad_all;
+  const int k = valid && sh.acc ? g : i;
+  if (!valid) write_invalid(a, b, tid);
+  if (tid == 0) {
+    SeqRec rec;
+    rec.mask = (k >= 64) ? ~0ull : ((1ull << k) - 1);
+    rec.k = k;
+    rec.valid = valid;
+    rec.mode = k == g ? kModeTarget
+                      : (!a.saguaro ? kModeResidual : (a.eps > 0.f ? kModeSaguaroEps : kModeSaguaro));
+    rec.Mt = 0.f;
+    rec.K_hi = rec.K_lo = 0.f;
+    rec.Zt = 1.0;
+    if (valid && k < g) {
+      const double Mt = sh.M[1];
+      rec.Mt = (float)Mt;
+      rec.Zt = ldexp(sh.Z[1], (int)fmin(fmax(Mt - (double)rec.Mt, -2000.0), 2000.0));
+      const double K = (Mt - sh.M[0]) + log2(sh.Z[1] / sh.Z[0]);
       rec.K_hi = (float)K;
       rec.K_lo = (float)(K - (double)rec.K_hi);
     }
@@ -1170,8 +1316,9 @@ __device__ void final_item(const VerifyArgs& a, int b, FinalLds& sh) {
     if (tid == 0) {
       const bool ok = row_ok(M, z);
       sh.ok = ok;
-      if (ok && a.diag.row_max) a.diag.row_max[(int64_t)b * R + r] = (double)mr * a.invT;
-      if (ok && a.diag.row_logZ) a.diag.row_logZ[(int64_t)b * R + r] = M * 0.69314718055994530942 + log(z);
+      const bool read = !a.early || (rec.valid && rec.k == g);
+      if (ok && read && a.diag.row_max) a.diag.row_max[(int64_t)b * R + r] = (double)mr * a.invT;
+      if (ok && read && a.diag.row_logZ) a.diag.row_logZ[(int64_t)b * R + r] = M * 0.69314718055994530942 + log(z);
       if (rec.valid) {
         uint64_t* ys = drawn_slot(a, b);
         sh.y = (int)(uint32_t)~poll(a, ys);
@@ -1182,7 +1329,7 @@ __device__ void final_item(const VerifyArgs& a, int b, FinalLds& sh) {
   __syncthreads();
   if (rec.valid) {   // an invalid decision wrote its outputs already
     const int k = rec.k;
-    if (!sh.ok) {
+    if (!sh.ok && (!a.early || k == g)) {   // early exit reads target row gamma only for the bonus
       write_invalid(a, b, tid);
     } else {
       const int64_t orow = (int64_t)b * (g + 1);
@@ -1209,6 +1356,13 @@ __device__ void final_item(const VerifyArgs& a, int b, FinalLds& sh) {
     while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < expect &&
            !give_up(a, polls)) {
     }
+    if (a.early) {   // every position test has read the stop and progress words
+      while (ld_dev_u32(f + kTestsWord) < (unsigned)g && !give_up(a, polls)) {
+      }
+      slot_clear32(f + kStopWord);
+      slot_clear32(f + kProgWord);
+      slot_clear32(f + kTestsWord);
+    }
     slot_clear32(f);
     clear_rec(a.seq + b);
   }
@@ -1225,17 +1379,28 @@ __device__ void final_item(const VerifyArgs& a, int b, FinalLds& sh) {
 // grow in that order, and LL >= B puts every target row gamma after every
 // other row, so the last bytes streamed are ones no decision waits for.
 
-constexpr int kKinds = 7;
+//
+// Early exit is position-major instead: step i*B + b holds the stream items of
+// draft and target row i of sequence b, so the rows of position i+1 of a
+// sequence come B steps after those of position i, and the test of (i, b)
+// sits LT steps after its rows.  A test only waits for its rows and for the
+// test of (i-1, b), both earlier in the order.  The sampling, draw, target
+// row gamma and final items of every sequence follow the last position.
+
+constexpr int kKinds = 8;
 enum : int {
   kItemStream = 0, kItemDecide = 1, kItemMass = 2, kItemSample = 3, kItemDraw = 4, kItemLast = 5,
-  kItemFinal = 6
+  kItemFinal = 6, kItemTest = 7
 };
 
+// Kind i has `count[i]` instances (sequences, or positions x sequences for
+// the early-exit stream and test kinds) of `size[i]` items each, instance n at
+// step lag[i] + n.
 struct Sched {
-  int B;
   int lag[kKinds];
   int size[kKinds];
-  int steps;        // B + lag[kItemFinal]
+  int count[kKinds];
+  int steps;        // max over kinds of lag + count
   int64_t total;
 };
 
@@ -1243,7 +1408,7 @@ __host__ __device__ inline int64_t sched_offset(const Sched& s, int t) {
   int64_t o = 0;
   for (int i = 0; i < kKinds; ++i) {
     int n = t - s.lag[i];
-    n = n < 0 ? 0 : (n > s.B ? s.B : n);
+    n = n < 0 ? 0 : (n > s.count[i] ? s.count[i] : n);
     o += (int64_t)n * s.size[i];
   }
   return o;
@@ -1262,7 +1427,7 @@ __host__ __device__ inline void sched_decode(const Sched& s, int64_t j, int& kin
   sub = 0;
   for (int i = 0; i < kKinds; ++i) {
     const int bi = lo - s.lag[i];
-    if (bi < 0 || bi >= s.B) continue;
+    if (bi < 0 || bi >= s.count[i]) continue;
     if (w < s.size[i]) {
       kind = i;
       b = bi;
@@ -1281,17 +1446,36 @@ union ItemLds {
   DecideLds d;
   DrawLds r;
   FinalLds f;
+  TestLds t;
 };
+
+// Early exit: a stream item of position pos (1..gamma-1) skips its rows when
+// an earlier position is known to stop the sequence; an item of target row
+// gamma (pos = gamma) skips on any known stop.  Read by one thread; the
+// work-group follows its answer.
+__device__ __forceinline__ bool early_stopped(const VerifyArgs& a, int b, int pos) {
+  const unsigned st = ld_dev_u32(a.flag + (int64_t)b * kFlagStride + kStopWord);
+  return pos >= a.gamma ? st != 0u : st > 64u - (unsigned)pos;
+}
+// A skipping item publishes skip markers in place of its piece.
+__device__ __forceinline__ void early_skip(const VerifyArgs& a, int b, int r, int c) {
+  if (threadIdx.x == 0) {
+    const int64_t idx = ((int64_t)b * (2 * a.gamma + 1) + r) * a.nc + c;
+    __hip_atomic_store(a.mraw + idx, kSkipRaw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    st_dev_u64(a.part + idx, kSkipPiece);
+  }
+}
 
 // Compiled for 8 waves per SIMD (64 VGPRs): the stream items need the
 // occupancy; every other path fits without spilling for packed bf16 rows.
 // PRED: outcome prediction too (draft-row items record lane leaders; the
 // items of target row gamma are followed by leader items of draft row gamma).
-template <int DT, bool VEC, int U, bool PRED>
+// EARLY: the early-exit order (position-major stream items, position tests).
+template <int DT, bool VEC, int U, bool PRED, bool EARLY>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8)))
 void fused_kernel(VerifyArgs a, Sched sc) {
   __shared__ ItemLds sh;
-  __shared__ int item[3];
+  __shared__ int item[4];
   // One wave decodes the block number (a search on the scalar unit, which
   // the CU's waves share) and hands the item to the others.
   if (threadIdx.x < 64) {
@@ -1301,22 +1485,42 @@ void fused_kernel(VerifyArgs a, Sched sc) {
       item[0] = kind;
       item[1] = b;
       item[2] = sub;
+      bool skip = false;
+      if constexpr (EARLY) {
+        if (kind == kItemStream && b >= a.B) skip = early_stopped(a, b - b / a.B * a.B, b / a.B);
+        else if (kind == kItemLast) skip = early_stopped(a, b, a.gamma);
+      }
+      item[3] = skip;
     }
   }
   __syncthreads();
-  const int kind = uni(item[0]), b = uni(item[1]), sub = uni(item[2]);
+  const int kind = uni(item[0]), b = uni(item[1]), sub = uni(item[2]), skip = uni(item[3]);
   switch (kind) {
     case kItemStream: {
-      const int r = sub / a.nc, c = sub - r * a.nc;
-      if (PRED && r < a.gamma) stream_item<DT, VEC, U, PRED>(a, b, r, c, sh.s);
-      else stream_item<DT, VEC, U>(a, b, r, c, sh.s);
+      if constexpr (EARLY) {   // b = i * B + sequence; sub: draft row i, then target row i
+        const int i = b / a.B, q = b - i * a.B;
+        const int h = sub >= a.nc, c = sub - h * a.nc, r = h ? a.gamma + i : i;
+        if (skip) early_skip(a, q, r, c);
+        else stream_item<DT, VEC, U>(a, q, r, c, sh.s);
+      } else {
+        const int r = sub / a.nc, c = sub - r * a.nc;
+        if (PRED && r < a.gamma) stream_item<DT, VEC, U, PRED>(a, b, r, c, sh.s);
+        else stream_item<DT, VEC, U>(a, b, r, c, sh.s);
+      }
       break;
     }
+    case kItemTest:
+      if constexpr (EARLY) test_item<DT>(a, b - b / a.B * a.B, b / a.B, sh.t);
+      break;
     case kItemDecide: decide_item<DT>(a, b, sh.d); break;
     case kItemMass: mass_item<DT, VEC>(a, b, sub, sh.r.lds_d); break;
     case kItemSample: sample_item<DT, VEC>(a, b, sub, sh.r.lds_d); break;
     case kItemDraw: draw_item<DT, VEC>(a, b, sh.r); break;
     case kItemLast:
+      if (EARLY && skip) {
+        early_skip(a, b, 2 * a.gamma, sub);
+        break;
+      }
       if (!PRED || sub < a.nc) stream_item<DT, VEC, U>(a, b, 2 * a.gamma, sub, sh.s);
       else leader_item<DT, VEC, U>(a, b, sub - a.nc, sh.s);
       break;
@@ -1340,6 +1544,13 @@ template <int DT>
 __global__ __launch_bounds__(kThreads) void decide_kernel(VerifyArgs a) {
   __shared__ DecideLds sh;
   decide_item<DT>(a, blockIdx.x, sh);
+}
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void test_kernel(VerifyArgs a) {
+  __shared__ TestLds sh;
+  const int i = blockIdx.x / a.B;
+  test_item<DT>(a, blockIdx.x - i * a.B, i, sh);
 }
 
 template <int DT, bool VEC>
@@ -1416,13 +1627,13 @@ static Layout layout(int B, int gamma, int V) {
 }
 
 // Work-groups of the fused kernel the device holds at once (cached per device).
-template <int DT, bool VEC, bool PRED>
+template <int DT, bool VEC, bool PRED, bool EARLY>
 static hipError_t resident_groups(int& slots) {
-  static int cache[64][2][2][2];
+  static int cache[64][2][2][2][2];
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  int* c = dev >= 0 && dev < 64 ? &cache[dev][DT][VEC ? 1 : 0][PRED ? 1 : 0] : nullptr;
+  int* c = dev >= 0 && dev < 64 ? &cache[dev][DT][VEC ? 1 : 0][PRED ? 1 : 0][EARLY ? 1 : 0] : nullptr;
   if (c && *c > 0) {
     slots = *c;
     return hipSuccess;
@@ -1431,7 +1642,8 @@ static hipError_t resident_groups(int& slots) {
   e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
   if (e == hipSuccess)
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-        &per_cu, reinterpret_cast<const void*>(fused_kernel<DT, VEC, SV_STREAM_UNROLL, PRED>), kThreads, 0);
+        &per_cu, reinterpret_cast<const void*>(fused_kernel<DT, VEC, SV_STREAM_UNROLL, PRED, EARLY>),
+        kThreads, 0);
   if (e != hipSuccess) return e;
   slots = std::max(1, ncu * per_cu);
   if (c) *c = slots;
@@ -1442,7 +1654,9 @@ static hipError_t resident_groups(int& slots) {
 // target row gamma, NM residual-mass and NB sampling items.
 static Sched make_sched(int B, int NSm, int NL, int NM, int NB, int slots) {
   Sched s;
-  s.B = B;
+  for (int i = 0; i < kKinds; ++i) s.count[i] = B;
+  s.lag[kItemTest] = 0;
+  s.size[kItemTest] = 0;
   const double spr = (double)slots / (double)(NSm + NL);   // sequences streamed per round
   auto steps = [&](int milli) { return (int)std::lround(spr * milli / 1000.0); };
   s.lag[kItemStream] = 0;
@@ -1464,6 +1678,36 @@ static Sched make_sched(int B, int NSm, int NL, int NM, int NB, int slots) {
   return s;
 }
 
+// Early exit: G positions, NC chunks per row.
+static Sched make_sched_early(int B, int G, int NC, int NM, int NB, int slots) {
+  Sched s;
+  const double spr = (double)slots / (double)(2 * NC + 1);   // position-steps per round
+  auto steps = [&](int milli) { return (int)std::lround(spr * milli / 1000.0); };
+  for (int i = 0; i < kKinds; ++i) s.count[i] = B;
+  s.count[kItemStream] = s.count[kItemTest] = G * B;
+  s.lag[kItemStream] = 0;
+  s.lag[kItemTest] = std::min(steps(SV_LAG_TEST), std::max(B - 1, 0));
+  const int base = (G - 1) * B + s.lag[kItemTest] + 1;   // after the test of the last position
+  s.lag[kItemDecide] = 0;
+  s.lag[kItemMass] = base;
+  s.lag[kItemSample] = base + (NM > 0 ? steps(SV_LAG_SAMPLE) : 0);
+  s.lag[kItemDraw] = s.lag[kItemSample] + steps(SV_LAG_DRAW);
+  s.lag[kItemLast] = std::max(G * B, s.lag[kItemDraw]);
+  s.lag[kItemFinal] = s.lag[kItemLast] + steps(SV_LAG_FINAL);
+  s.size[kItemStream] = 2 * NC;
+  s.size[kItemTest] = 1;
+  s.size[kItemDecide] = 0;
+  s.size[kItemMass] = NM;
+  s.size[kItemSample] = NB;
+  s.size[kItemDraw] = 1;
+  s.size[kItemLast] = NC;
+  s.size[kItemFinal] = 1;
+  s.steps = 0;
+  for (int i = 0; i < kKinds; ++i) s.steps = std::max(s.steps, s.lag[i] + s.count[i]);
+  s.total = sched_offset(s, s.steps);
+  return s;
+}
+
 template <int DT, bool VEC>
 static hipError_t launch_kernels(const VerifyArgs& a, hipStream_t st);
 
@@ -1475,18 +1719,26 @@ static hipError_t launch_all(const VerifyArgs& a, const PredictArgs* pa, hipStre
   // than the stream items' occupancy leaves) and the stand-alone prediction.
   if constexpr (SV_FUSED && DT == kBF16 && VEC) {
     int slots = 0;
-    hipError_t e = pa ? resident_groups<DT, VEC, true>(slots) : resident_groups<DT, VEC, false>(slots);
-    if (e != hipSuccess) return e;
     const bool eps_mode = a.saguaro && a.eps > 0.f;
+    if (a.early) {
+      hipError_t e = resident_groups<DT, VEC, false, true>(slots);
+      if (e != hipSuccess) return e;
+      const Sched sc = make_sched_early(a.B, a.gamma, a.nc, eps_mode ? a.nt : 0, a.nt, slots);
+      hipLaunchKernelGGL((fused_kernel<DT, VEC, SV_STREAM_UNROLL, false, true>), dim3((unsigned)sc.total),
+                         dim3(kThreads), 0, st, a, sc);
+      return hipGetLastError();
+    }
+    hipError_t e = pa ? resident_groups<DT, VEC, true, false>(slots) : resident_groups<DT, VEC, false, false>(slots);
+    if (e != hipSuccess) return e;
     const Sched sc = make_sched(a.B, 2 * a.gamma * a.nc, (pa ? 2 : 1) * a.nc, eps_mode ? a.nt : 0, a.nt, slots);
     if (pa) {
-      hipLaunchKernelGGL((fused_kernel<DT, VEC, SV_STREAM_UNROLL, true>), dim3((unsigned)sc.total),
+      hipLaunchKernelGGL((fused_kernel<DT, VEC, SV_STREAM_UNROLL, true, false>), dim3((unsigned)sc.total),
                          dim3(kThreads), 0, st, a, sc);
       e = hipGetLastError();
       if (e != hipSuccess) return e;
       return predict_launch_leaders(*pa, SPEC_BF16, st);
     }
-    hipLaunchKernelGGL((fused_kernel<DT, VEC, SV_STREAM_UNROLL, false>), dim3((unsigned)sc.total),
+    hipLaunchKernelGGL((fused_kernel<DT, VEC, SV_STREAM_UNROLL, false, false>), dim3((unsigned)sc.total),
                        dim3(kThreads), 0, st, a, sc);
     return hipGetLastError();
   } else {
@@ -1503,7 +1755,10 @@ static hipError_t launch_kernels(const VerifyArgs& a, hipStream_t st) {
   const unsigned nstream = (unsigned)((int64_t)a.B * R * a.nc);
   const unsigned nsample = (unsigned)((int64_t)a.B * a.nt);
   hipLaunchKernelGGL((stream_kernel<DT, VEC, SV_STREAM_UNROLL>), dim3(nstream), dim3(kThreads), 0, st, a);
-  hipLaunchKernelGGL((decide_kernel<DT>), dim3((unsigned)a.B), dim3(kThreads), 0, st, a);
+  if (a.early)   // position-major: the test of (i - 1, b) has a smaller block number than (i, b)'s
+    hipLaunchKernelGGL((test_kernel<DT>), dim3((unsigned)((int64_t)a.gamma * a.B)), dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((decide_kernel<DT>), dim3((unsigned)a.B), dim3(kThreads), 0, st, a);
   if (eps_mode) hipLaunchKernelGGL((mass_kernel<DT, VEC>), dim3(nsample), dim3(kThreads), 0, st, a);
   hipLaunchKernelGGL((sample_kernel<DT, VEC>), dim3(nsample), dim3(kThreads), 0, st, a);
   hipLaunchKernelGGL((draw_kernel<DT, VEC>), dim3((unsigned)a.B), dim3(kThreads), 0, st, a);
@@ -1517,7 +1772,7 @@ static int verify_impl(const void* draft, const void* target, int dtype, const i
                        int32_t* out_fr, uint64_t* out_mask, int32_t* out_len,
                        const spec_diag* diag, void* ws, size_t ws_bytes, void* stream,
                        int saguaro, float eps, int32_t* cand = nullptr, int32_t* hit = nullptr,
-                       int32_t* cand_idx = nullptr) {
+                       int32_t* cand_idx = nullptr, int early = 0) {
   if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_EDTYPE;
   if (!sizes_ok(B, gamma, V)) return SPEC_EINVAL;
   if (!(T > 0.f) || !std::isfinite(T)) return SPEC_EINVAL;
@@ -1528,7 +1783,7 @@ static int verify_impl(const void* draft, const void* target, int dtype, const i
   const Layout L = layout(B, gamma, V);
   // Every launch (and the fused kernel's item count) stays within one grid
   // dimension of 2^32 - 1 work-items, with block numbers below 2^31.
-  const int64_t items = (int64_t)B * ((2 * gamma + 2) * L.nc + 2 * L.nt + 3);
+  const int64_t items = (int64_t)B * ((2 * gamma + 2) * L.nc + 2 * L.nt + 3 + gamma);
   if (items * kThreads > (int64_t)UINT_MAX || items > (int64_t)INT_MAX) return SPEC_EINVAL;
   if (!ws || ws_bytes < L.total) return SPEC_EWORKSPACE;
 
@@ -1577,6 +1832,7 @@ static int verify_impl(const void* draft, const void* target, int dtype, const i
   }
   a.saguaro = saguaro;
   a.eps = eps;
+  a.early = early;
 
   PredictArgs p;
   if (cand) {
@@ -1646,6 +1902,19 @@ int spec_verify_predict(const void* draft_logits, const void* target_logits, int
                          gamma, V, temperature, in_len, out_tokens, out_accepted, out_first_reject,
                          out_accept_mask, out_len, diag, workspace, workspace_bytes, stream, saguaro,
                          eps, cand, hit, cand_idx);
+}
+
+int spec_verify_early(const void* draft_logits, const void* target_logits, int dtype,
+                      const int32_t* draft_tokens, const float* u_accept, const float* u_sample,
+                      int B, int gamma, int V, float temperature, const int32_t* in_len,
+                      int32_t* out_tokens, int32_t* out_accepted, int32_t* out_first_reject,
+                      uint64_t* out_accept_mask, int32_t* out_len, const spec_diag* diag,
+                      int saguaro, float eps, void* workspace, size_t workspace_bytes, void* stream) {
+  if (saguaro != 0 && saguaro != 1) return SPEC_EINVAL;
+  return sv::verify_impl(draft_logits, target_logits, dtype, draft_tokens, u_accept, u_sample, B,
+                         gamma, V, temperature, in_len, out_tokens, out_accepted, out_first_reject,
+                         out_accept_mask, out_len, diag, workspace, workspace_bytes, stream, saguaro,
+                         eps, nullptr, nullptr, nullptr, 1);
 }
 
 const char* spec_status_str(int status) {

@@ -60,11 +60,17 @@ def to_device(batch: W.Batch, dev="cuda") -> DeviceBatch:
         torch.from_numpy(np.ascontiguousarray(batch.in_len, dtype=np.int32)).to(dev))
 
 
-def run_gpu(batch: W.Batch, mode="residual", eps=0.0, diag=True, db: DeviceBatch | None = None):
+def run_gpu(batch: W.Batch, mode="residual", eps=0.0, diag=True, db: DeviceBatch | None = None,
+            early=False, ws=None):
     db = db or to_device(batch)
     dt = R.SPEC_BF16 if batch.dtype == "bf16" else R.SPEC_F32
-    ws = R.new_workspace(R.spec_workspace_bytes(batch.B, batch.gamma, batch.V, dt), db.draft.device)
-    if mode == "residual":
+    if ws is None:
+        ws = R.new_workspace(R.spec_workspace_bytes(batch.B, batch.gamma, batch.V, dt), db.draft.device)
+    if early:
+        out = R.spec_verify_early(db.draft, db.target, db.tokens, db.u_accept, db.u_sample, batch.T,
+                                  in_len=db.in_len, diag=diag, workspace=ws,
+                                  saguaro=mode == "saguaro", eps=eps)
+    elif mode == "residual":
         out = R.spec_verify(db.draft, db.target, db.tokens, db.u_accept, db.u_sample, batch.T,
                             in_len=db.in_len, diag=diag, workspace=ws)
     else:
@@ -73,6 +79,8 @@ def run_gpu(batch: W.Batch, mode="residual", eps=0.0, diag=True, db: DeviceBatch
     torch.cuda.synchronize()
     # The workspace's first word records a timed-out wait; it must stay zero.
     assert batch.B == 0 or int(ws[:4].view(torch.int32).item()) == 0, "bounded wait timed out"
+    if batch.B:
+        assert int(ws.to(torch.int64).sum().item()) == 0, "workspace not left zeroed"
     host = {
         "tokens": out.tokens.cpu().numpy(), "accepted": out.accepted.cpu().numpy(),
         "first_reject": out.first_reject.cpu().numpy(),
@@ -84,14 +92,15 @@ def run_gpu(batch: W.Batch, mode="residual", eps=0.0, diag=True, db: DeviceBatch
     return host
 
 
-def run_oracle(batch: W.Batch, mode="residual", eps=0.0, seqs=None):
+def run_oracle(batch: W.Batch, mode="residual", eps=0.0, seqs=None, early=False):
     seqs = range(batch.B) if seqs is None else seqs
     out = {}
+    fn = O.verify_early_one if early else O.verify_one
     for b in seqs:
         db = W.decode_f64(batch.draft[b], batch.dtype)
         tb = W.decode_f64(batch.target[b], batch.dtype)
-        out[b] = O.verify_one(db, tb, batch.draft_tokens[b], batch.u_accept[b], batch.u_sample[b],
-                              batch.T, mode, eps, int(batch.in_len[b]))
+        out[b] = fn(db, tb, batch.draft_tokens[b], batch.u_accept[b], batch.u_sample[b],
+                    batch.T, mode, eps, int(batch.in_len[b]))
     return out
 
 
@@ -209,11 +218,12 @@ def compare(batch: W.Batch, gpu: dict, ref: dict, check_diag: bool = True) -> Re
     return rep
 
 
-def parity(batch: W.Batch, mode="residual", eps=0.0, seqs=None, check_diag=True) -> Report:
+def parity(batch: W.Batch, mode="residual", eps=0.0, seqs=None, check_diag=True,
+           early=False) -> Report:
     say(f"[parity] {batch.name} B={batch.B} gamma={batch.gamma} V={batch.V} dtype={batch.dtype} "
-        f"T={batch.T} mode={mode} eps={eps}")
-    gpu = run_gpu(batch, mode, eps, diag=check_diag)
-    ref = run_oracle(batch, mode, eps, seqs)
+        f"T={batch.T} mode={mode} eps={eps} early={early}")
+    gpu = run_gpu(batch, mode, eps, diag=check_diag, early=early)
+    ref = run_oracle(batch, mode, eps, seqs, early=early)
     rep = compare(batch, gpu, ref, check_diag)
     say(f"[parity]   {rep}")
     return rep
