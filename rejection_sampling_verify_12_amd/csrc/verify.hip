@@ -88,6 +88,11 @@ enum : int { kModeTarget = 0, kModeResidual = 1, kModeSaguaro = 2, kModeSaguaroE
 #ifndef SV_LAG_TEST
 #define SV_LAG_TEST 800
 #endif
+// Early exit: stream chunk length (a multiple of the default; fewer, longer
+// items per row make the items that skip rows fewer).
+#ifndef SV_EARLY_CHUNK
+#define SV_EARLY_CHUNK SV_CHUNK
+#endif
 #ifndef SV_SAMPLE_NT
 #define SV_SAMPLE_NT 0
 #endif
@@ -1395,16 +1400,25 @@ enum : int {
 
 // Kind i has `count[i]` instances (sequences, or positions x sequences for
 // the early-exit stream and test kinds) of `size[i]` items each, instance n at
-// step lag[i] + n.
+// step lag[i] + n.  Between consecutive lag / lag + count boundaries the same
+// kinds are active on every step, so the order is cut into at most
+// 2 kKinds + 1 segments of equal steps; the host lists them, and a block finds
+// its item with a short scan and one division on the scalar unit.
+constexpr int kMaxSeg = 2 * kKinds + 1;
 struct Sched {
   int lag[kKinds];
   int size[kKinds];
   int count[kKinds];
   int steps;        // max over kinds of lag + count
   int64_t total;
+  int nseg;
+  int seg_step[kMaxSeg];       // first step of the segment
+  int seg_first[kMaxSeg];      // number of the segment's first item
+  int seg_per[kMaxSeg];        // items per step (0: an empty stretch)
+  unsigned seg_mask[kMaxSeg];  // kinds active on its steps
 };
 
-__host__ __device__ inline int64_t sched_offset(const Sched& s, int t) {
+static int64_t sched_offset(const Sched& s, int t) {
   int64_t o = 0;
   for (int i = 0; i < kKinds; ++i) {
     int n = t - s.lag[i];
@@ -1414,17 +1428,67 @@ __host__ __device__ inline int64_t sched_offset(const Sched& s, int t) {
   return o;
 }
 
-__host__ __device__ inline void sched_decode(const Sched& s, int64_t j, int& kind, int& b, int& sub) {
-  int lo = 0, hi = s.steps;   // offset(lo) <= j < offset(hi) = total
+// Fills steps, total and the segments from lag, size and count.
+static void sched_finish(Sched& s) {
+  s.steps = 0;
+  for (int i = 0; i < kKinds; ++i)
+    if (s.size[i] > 0 && s.count[i] > 0) s.steps = std::max(s.steps, s.lag[i] + s.count[i]);
+  s.total = sched_offset(s, s.steps);
+  int cut[2 * kKinds + 2];
+  int nc = 0;
+  cut[nc++] = 0;
+  for (int i = 0; i < kKinds; ++i) {
+    if (s.size[i] <= 0 || s.count[i] <= 0) continue;
+    cut[nc++] = std::min(std::max(s.lag[i], 0), s.steps);
+    cut[nc++] = std::min(std::max(s.lag[i] + s.count[i], 0), s.steps);
+  }
+  std::sort(cut, cut + nc);
+  nc = (int)(std::unique(cut, cut + nc) - cut);
+  s.nseg = 0;
+  for (int q = 0; q < nc; ++q) {
+    const int t0 = cut[q];
+    if (t0 >= s.steps) break;
+    unsigned mask = 0;
+    int per = 0;
+    for (int i = 0; i < kKinds; ++i) {
+      if (s.size[i] > 0 && s.lag[i] <= t0 && t0 < s.lag[i] + s.count[i]) {
+        mask |= 1u << i;
+        per += s.size[i];
+      }
+    }
+    s.seg_step[s.nseg] = t0;
+    s.seg_first[s.nseg] = (int)sched_offset(s, t0);
+    s.seg_per[s.nseg] = per;
+    s.seg_mask[s.nseg] = mask;
+    ++s.nseg;
+  }
+}
+
+// Two decoders of a block number: a binary search over the steps (the
+// default order measures faster with it) and the segment table (the
+// early-exit order, whose many short items gain from the shorter decode).
+__device__ inline int64_t sched_offset_dev(const Sched& s, int t) {
+  int64_t o = 0;
+#pragma unroll
+  for (int i = 0; i < kKinds; ++i) {
+    int n = t - s.lag[i];
+    n = n < 0 ? 0 : (n > s.count[i] ? s.count[i] : n);
+    o += (int64_t)n * s.size[i];
+  }
+  return o;
+}
+__device__ inline void sched_decode_search(const Sched& s, int j, int& kind, int& b, int& sub) {
+  int lo = 0, hi = s.steps;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (sched_offset(s, mid) <= j) lo = mid;
+    if (sched_offset_dev(s, mid) <= j) lo = mid;
     else hi = mid;
   }
-  int64_t w = j - sched_offset(s, lo);
+  int64_t w = j - sched_offset_dev(s, lo);
   kind = kItemFinal;
   b = lo - s.lag[kItemFinal];
   sub = 0;
+#pragma unroll
   for (int i = 0; i < kKinds; ++i) {
     const int bi = lo - s.lag[i];
     if (bi < 0 || bi >= s.count[i]) continue;
@@ -1435,6 +1499,42 @@ __host__ __device__ inline void sched_decode(const Sched& s, int64_t j, int& kin
       return;
     }
     w -= s.size[i];
+  }
+}
+// Every index into the table is a constant (unrolled loops and selects), so
+// the table is read straight from the kernel arguments.
+__device__ inline void sched_decode_table(const Sched& s, int j, int& kind, int& b, int& sub) {
+  int step = s.seg_step[0], first = s.seg_first[0], per = s.seg_per[0];
+  unsigned mask = s.seg_mask[0];
+#pragma unroll
+  for (int i = 1; i < kMaxSeg; ++i) {   // the last segment starting at or before j (empty
+    if (i < s.nseg && s.seg_first[i] <= j) {   // ones share their start with the next)
+      step = s.seg_step[i];
+      first = s.seg_first[i];
+      per = s.seg_per[i];
+      mask = s.seg_mask[i];
+    }
+  }
+  const int rel = j - first;
+  const int dt = rel / per;
+  const int t = step + dt;
+  int w = rel - dt * per;
+  kind = kItemFinal;
+  b = 0;
+  sub = 0;
+  bool found = false;
+#pragma unroll
+  for (int i = 0; i < kKinds; ++i) {
+    if (!found && ((mask >> i) & 1u)) {
+      if (w < s.size[i]) {
+        kind = i;
+        b = t - s.lag[i];
+        sub = w;
+        found = true;
+      } else {
+        w -= s.size[i];
+      }
+    }
   }
 }
 
@@ -1480,7 +1580,8 @@ void fused_kernel(VerifyArgs a, Sched sc) {
   // the CU's waves share) and hands the item to the others.
   if (threadIdx.x < 64) {
     int kind, b, sub;
-    sched_decode(sc, blockIdx.x, kind, b, sub);
+    if constexpr (EARLY) sched_decode_table(sc, (int)blockIdx.x, kind, b, sub);
+    else sched_decode_search(sc, (int)blockIdx.x, kind, b, sub);
     if (threadIdx.x == 0) {
       item[0] = kind;
       item[1] = b;
@@ -1673,8 +1774,7 @@ static Sched make_sched(int B, int NSm, int NL, int NM, int NB, int slots) {
   s.size[kItemDraw] = 1;
   s.size[kItemLast] = NL;
   s.size[kItemFinal] = 1;
-  s.steps = B + s.lag[kItemFinal];
-  s.total = sched_offset(s, s.steps);
+  sched_finish(s);
   return s;
 }
 
@@ -1702,9 +1802,7 @@ static Sched make_sched_early(int B, int G, int NC, int NM, int NB, int slots) {
   s.size[kItemDraw] = 1;
   s.size[kItemLast] = NC;
   s.size[kItemFinal] = 1;
-  s.steps = 0;
-  for (int i = 0; i < kKinds; ++i) s.steps = std::max(s.steps, s.lag[i] + s.count[i]);
-  s.total = sched_offset(s, s.steps);
+  sched_finish(s);
   return s;
 }
 
@@ -1723,9 +1821,13 @@ static hipError_t launch_all(const VerifyArgs& a, const PredictArgs* pa, hipStre
     if (a.early) {
       hipError_t e = resident_groups<DT, VEC, false, true>(slots);
       if (e != hipSuccess) return e;
-      const Sched sc = make_sched_early(a.B, a.gamma, a.nc, eps_mode ? a.nt : 0, a.nt, slots);
+      static_assert(SV_EARLY_CHUNK % SV_CHUNK == 0, "early-exit chunks are whole default chunks");
+      VerifyArgs b = a;   // never more chunks than the workspace holds
+      b.chunk = SV_EARLY_CHUNK;
+      b.nc = (int)(((int64_t)a.V + b.chunk - 1) / b.chunk);
+      const Sched sc = make_sched_early(b.B, b.gamma, b.nc, eps_mode ? b.nt : 0, b.nt, slots);
       hipLaunchKernelGGL((fused_kernel<DT, VEC, SV_STREAM_UNROLL, false, true>), dim3((unsigned)sc.total),
-                         dim3(kThreads), 0, st, a, sc);
+                         dim3(kThreads), 0, st, b, sc);
       return hipGetLastError();
     }
     hipError_t e = pa ? resident_groups<DT, VEC, true, false>(slots) : resident_groups<DT, VEC, false, false>(slots);
