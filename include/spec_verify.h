@@ -215,6 +215,43 @@ int spec_verify_early(const void* draft_logits, const void* target_logits, int d
                       int saguaro, float eps, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Options of spec_verify_ex.  A zero-filled struct (or a NULL pointer) is
+ * spec_verify's behaviour.
+ *   saguaro, eps: as spec_verify_saguaro when saguaro == 1 (0: residual).
+ *   early: nonzero = early exit, as spec_verify_early.
+ *   temperature: NULL, or a DEVICE array [B] of per-sequence temperatures
+ *     that replaces the scalar argument (which is then not checked): sequence
+ *     b uses T_b for both models ("Speculative Decoding: small model guesses,
+ *     large model verifies", section 5.4: the same temperature on both sides;
+ *     section 3, after its numerical check of unbiasedness: the rule stacks on
+ *     temperature sampling unchanged).
+ *     A T_b that is not finite and positive makes only that sequence invalid.
+ *   cand, hit, cand_idx: outcome prediction outputs as spec_verify_predict
+ *     (cand NULL = no prediction; hit / cand_idx need cand).
+ * early and prediction do not combine (SPEC_EINVAL).
+ */
+typedef struct spec_options {
+  int saguaro;
+  float eps;
+  int early;
+  const float* temperature;
+  int32_t* cand;
+  int32_t* hit;
+  int32_t* cand_idx;
+} spec_options;
+
+/*
+ * Verification with options: the arguments of spec_verify plus `opts` (a
+ * host pointer, may be NULL).  Workspace: spec_workspace_bytes().
+ */
+int spec_verify_ex(const void* draft_logits, const void* target_logits, int dtype,
+                   const int32_t* draft_tokens, const float* u_accept, const float* u_sample, int B,
+                   int gamma, int V, float temperature, const int32_t* in_len, int32_t* out_tokens,
+                   int32_t* out_accepted, int32_t* out_first_reject, uint64_t* out_accept_mask,
+                   int32_t* out_len, const spec_diag* diag, const spec_options* opts,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Bytes of device workspace spec_verify_greedy needs (same zero-on-entry rule
  * and error word as spec_workspace_bytes; 0 for B == 0 or arguments
  * spec_verify_greedy would reject).

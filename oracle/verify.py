@@ -45,6 +45,8 @@ notes with its justification):
   tokens -1, mask 0, first_reject -1, out_len = in_len.
 * p(x) = 0 at a draft token: accept iff q(x) > 0.
 * out_len = in_len + k + 1 (tokens committed this round).
+* A per-sequence temperature that is not finite and positive makes that
+  sequence invalid (a batch-wide one is rejected before any work).
 * Greedy verification is the temperature -> 0 limit of the rule: accept x_i
   iff it is the target's most likely token at position i, and emit the
   target's most likely token at the stopping position (the correction after a
@@ -171,7 +173,7 @@ def verify_one(draft64, target64, tokens, u_accept, u_sample, T, mode="residual"
     gamma = len(tokens)
     V = draft64.shape[-1]
     x = np.asarray(tokens, dtype=np.int64)
-    if ((x < 0) | (x >= V)).any():
+    if not (np.isfinite(T) and T > 0) or ((x < 0) | (x >= V)).any():
         return _invalid(gamma, in_len)
     if not (row_valid(draft64[:gamma]).all() and row_valid(target64[:gamma + 1]).all()):
         return _invalid(gamma, in_len)
@@ -248,6 +250,8 @@ def verify_early_one(draft64, target64, tokens, u_accept, u_sample, T, mode="res
     gamma = len(tokens)
     V = draft64.shape[-1]
     x = np.asarray(tokens, dtype=np.int64)
+    if not (np.isfinite(T) and T > 0):
+        return _invalid(gamma, in_len)
     ua = np.asarray(u_accept, dtype=np.float64)
     nan = np.full(gamma, np.nan)
     a = nan.copy()

@@ -21,7 +21,14 @@ SPEC_F32, SPEC_BF16 = 0, 1
 EXPORTED = ("spec_workspace_bytes", "spec_verify", "spec_verify_saguaro",
             "spec_predict_workspace_bytes", "spec_predict_outcomes", "spec_verify_predict",
             "spec_greedy_workspace_bytes", "spec_verify_greedy", "spec_verify_early",
-            "spec_status_str")
+            "spec_verify_ex", "spec_status_str")
+
+
+class SpecOptions(ctypes.Structure):
+    """struct spec_options (see spec_verify.h)."""
+    _fields_ = [("saguaro", ctypes.c_int), ("eps", ctypes.c_float), ("early", ctypes.c_int),
+                ("temperature", ctypes.c_void_p), ("cand", ctypes.c_void_p),
+                ("hit", ctypes.c_void_p), ("cand_idx", ctypes.c_void_p)]
 
 
 class SpecDiag(ctypes.Structure):
@@ -58,6 +65,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.spec_verify_predict.argtypes = verify_args[:-3] + [i32, f32, vp, vp, vp] + verify_args[-3:]
     lib.spec_verify_predict.restype = i32
     lib.spec_verify_early.argtypes = verify_args[:-3] + [i32, f32] + verify_args[-3:]
+    lib.spec_verify_ex.argtypes = verify_args[:-3] + [ctypes.POINTER(SpecOptions)] + verify_args[-3:]
+    lib.spec_verify_ex.restype = i32
     lib.spec_verify_early.restype = i32
     lib.spec_greedy_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.spec_greedy_workspace_bytes.restype = sz
@@ -142,7 +151,8 @@ def alloc_outputs(B: int, gamma: int, device, diag: bool = False) -> VerifyOut:
 
 def _verify_call(saguaro: bool, draft_logits, target_logits, draft_tokens, u_accept, u_sample,
                  temperature: float, in_len=None, out: VerifyOut | None = None, diag: bool = False,
-                 workspace=None, stream=None, eps: float = 0.0, pred=None, early=False) -> VerifyOut:
+                 workspace=None, stream=None, eps: float = 0.0, pred=None, early=False,
+                 temps=None, ex=False) -> VerifyOut:
     lib = load_library()
     B, G1, V = draft_logits.shape
     gamma = G1 - 1
@@ -165,7 +175,16 @@ def _verify_call(saguaro: bool, draft_logits, target_logits, draft_tokens, u_acc
             out.first_reject.data_ptr(), out.accept_mask.data_ptr(), out.out_len.data_ptr(),
             ctypes.byref(dg) if dg is not None else None, workspace.data_ptr(),
             workspace.numel(), _stream_handle(stream, dev)]
-    if early:
+    if ex:
+        _check_dev(temps)
+        if pred is not None:
+            _check_dev(*pred)
+        opts = SpecOptions(int(saguaro), float(eps), int(early), _ptr(temps),
+                           pred.cand.data_ptr() if pred is not None else None,
+                           _ptr(pred.hit) if pred is not None else None,
+                           _ptr(pred.cand_idx) if pred is not None else None)
+        st = lib.spec_verify_ex(*args[:-3], ctypes.byref(opts), *args[-3:])
+    elif early:
         st = lib.spec_verify_early(*args[:-3], int(saguaro), float(eps), *args[-3:])
     elif pred is not None:
         _check_dev(*pred)
@@ -233,6 +252,22 @@ def spec_verify_early(draft_logits, target_logits, draft_tokens, u_accept, u_sam
     return _verify_call(bool(saguaro), draft_logits, target_logits, draft_tokens, u_accept,
                         u_sample, temperature, in_len, out, diag, workspace, stream,
                         eps if saguaro else 0.0, None, True)
+
+
+def spec_verify_ex(draft_logits, target_logits, draft_tokens, u_accept, u_sample, temperature,
+                   in_len=None, out=None, diag=False, workspace=None, stream=None,
+                   saguaro: bool = False, eps: float = 0.0, early: bool = False, pred=None):
+    """Verification with options (see spec_verify.h): ``temperature`` is a float
+    for the whole batch or a [B] float32 device tensor of per-sequence
+    temperatures; ``pred`` (a PredictOut) asks for outcome prediction.
+    Returns VerifyOut, or (VerifyOut, PredictOut) when ``pred`` is given."""
+    import torch
+    temps = temperature if isinstance(temperature, torch.Tensor) else None
+    T = 1.0 if temps is not None else float(temperature)
+    out = _verify_call(bool(saguaro), draft_logits, target_logits, draft_tokens, u_accept,
+                       u_sample, T, in_len, out, diag, workspace, stream,
+                       eps if saguaro else 0.0, pred, early, temps, ex=True)
+    return (out, pred) if pred is not None else out
 
 
 def spec_greedy_workspace_bytes(B: int, gamma: int, V: int, dtype: int) -> int:

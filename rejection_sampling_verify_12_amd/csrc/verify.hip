@@ -191,7 +191,44 @@ struct VerifyArgs {
   int saguaro;
   float eps;
   int early;         // early exit: rows beyond the first rejection are not needed
+  const float* temps;   // [B] per-sequence temperatures, or NULL (c_hi, c_lo, cTd, invT for all)
 };
+
+// The temperature scale of sequence b: log2(e) / T as an unevaluated float
+// pair (c_hi rounded toward zero, so c_lo > 0), their double sum, and 1 / T.
+// Per-sequence temperatures are scaled here exactly as the host scales the
+// common one; a temperature that is not finite and positive is scaled as 1
+// and makes the sequence invalid (decision items check temp_ok).
+struct TCoef {
+  float c_hi, c_lo;
+  double cTd, invT;
+};
+__device__ __forceinline__ bool temp_ok(float T) { return T > 0.f && T <= 3.402823466e38f; }
+__device__ __forceinline__ float seq_temp(const VerifyArgs& a, int b) {
+  return a.temps ? uni(a.temps[b]) : 1.f;
+}
+__device__ __forceinline__ TCoef temp_coef(const VerifyArgs& a, int b) {
+  TCoef t;
+  if (!a.temps) {
+    t.c_hi = a.c_hi;
+    t.c_lo = a.c_lo;
+    t.cTd = a.cTd;
+    t.invT = a.invT;
+    return t;
+  }
+  float T = seq_temp(a, b);
+  if (!temp_ok(T)) T = 1.f;
+  const double c = 1.4426950408889634073599246810019 / (double)T;
+  float ch = (float)c;
+  if ((double)ch >= c) ch = __int_as_float(__float_as_int(ch) - 1);   // next float toward zero
+  float cl = (float)(c - (double)ch);
+  if (!(cl > 0.f)) cl = 1.17549435e-38f;
+  t.c_hi = uni(ch);
+  t.c_lo = uni(cl);
+  t.cTd = uni((double)t.c_hi + (double)t.c_lo);
+  t.invT = uni(1.0 / (double)T);
+  return t;
+}
 
 template <int DT>
 __device__ __forceinline__ const void* row_ptr(const VerifyArgs& a, int b, int r) {
@@ -341,7 +378,8 @@ __device__ __forceinline__ void stream_item(const VerifyArgs& a, int b, int r, i
   const void* row = row_ptr<DT>(a, b, r);
   const int64_t begin = (int64_t)c * a.chunk;
   const int64_t end = min<int64_t>(begin + a.chunk, a.V);
-  const float ch = a.c_hi, cl = a.c_lo;
+  const TCoef tc = temp_coef(a, b);
+  const float ch = tc.c_hi, cl = tc.c_lo;
 
   // mref: this lane's integer offset (log2 units); s: fp64 sum of 2^(l*c_T - mref).
   float mref = kNegSentinel, mraw = -INFINITY;
@@ -593,24 +631,25 @@ __device__ void decide_item(const VerifyArgs& a, int b, DecideLds& sh) {
     }
   }
   __syncthreads();
+  const TCoef tc = temp_coef(a, b);
   for (int r = tid; r < Rd; r += kThreads) {
     if (sh.bad[r]) continue;
-    if (a.diag.row_max) a.diag.row_max[(int64_t)b * R + r] = (double)sh.mr[r] * a.invT;
+    if (a.diag.row_max) a.diag.row_max[(int64_t)b * R + r] = (double)sh.mr[r] * tc.invT;
     if (a.diag.row_logZ) a.diag.row_logZ[(int64_t)b * R + r] = sh.M[r] * 0.69314718055994530942 + log(sh.Z[r]);
   }
 
   if (wave == 0) {
     int rows_bad = 0;
     for (int r = lane; r < Rd; r += 64) rows_bad |= sh.bad[r];
-    rows_bad = __ballot(rows_bad) != 0;
+    rows_bad = __ballot(rows_bad) != 0 || (a.temps && !temp_ok(seq_temp(a, b)));
     int acc = 0, bad = 0;
     if (lane < g) {
       const int x = sh.x[lane];
       bad = (x < 0 || x >= a.V);
       if (!bad && !rows_bad) {
         // p(x) = pn / Zd and q(x) = qn / Zt; the ratio with one division.
-        const double pn = exp2((double)sh.ldx[lane] * a.cTd - sh.M[lane]);
-        const double qn = exp2((double)sh.ltx[lane] * a.cTd - sh.M[g + lane]);
+        const double pn = exp2((double)sh.ldx[lane] * tc.cTd - sh.M[lane]);
+        const double qn = exp2((double)sh.ltx[lane] * tc.cTd - sh.M[g + lane]);
         double ratio;
         if (pn > 0.0) ratio = fmin(1.0, (qn * sh.Z[lane]) / (pn * sh.Z[g + lane]));
         else ratio = qn > 0.0 ? 1.0 : 0.0;
@@ -708,13 +747,14 @@ __device__ void test_item(const VerifyArgs& a, int b, int i, TestLds& sh) {
   }
   __syncthreads();
   if (tid == 0) {
+    const TCoef tc = temp_coef(a, b);
     const int x = sh.x;
-    const bool bad = x < 0 || x >= a.V || sh.bad[0] || sh.bad[1];
+    const bool bad = x < 0 || x >= a.V || sh.bad[0] || sh.bad[1] || (a.temps && !temp_ok(seq_temp(a, b)));
     bool acc = false;
     double pn = 0.0, qn = 0.0;
     if (!bad) {
-      pn = exp2((double)sh.ldx * a.cTd - sh.M[0]);
-      qn = exp2((double)sh.ltx * a.cTd - sh.M[1]);
+      pn = exp2((double)sh.ldx * tc.cTd - sh.M[0]);
+      qn = exp2((double)sh.ltx * tc.cTd - sh.M[1]);
       double ratio;
       if (pn > 0.0) ratio = fmin(1.0, (qn * sh.Z[0]) / (pn * sh.Z[1]));
       else ratio = qn > 0.0 ? 1.0 : 0.0;
@@ -742,8 +782,8 @@ __device__ void test_item(const VerifyArgs& a, int b, int i, TestLds& sh) {
       if (a.diag.px) a.diag.px[(int64_t)b * g + i] = pn / sh.Z[0];
       if (a.diag.qx) a.diag.qx[(int64_t)b * g + i] = qn / sh.Z[1];
       if (a.diag.row_max) {
-        a.diag.row_max[(int64_t)b * R + i] = (double)sh.mr[0] * a.invT;
-        a.diag.row_max[(int64_t)b * R + g + i] = (double)sh.mr[1] * a.invT;
+        a.diag.row_max[(int64_t)b * R + i] = (double)sh.mr[0] * tc.invT;
+        a.diag.row_max[(int64_t)b * R + g + i] = (double)sh.mr[1] * tc.invT;
       }
       if (a.diag.row_logZ) {
         a.diag.row_logZ[(int64_t)b * R + i] = sh.M[0] * 0.69314718055994530942 + log(sh.Z[0]);
@@ -790,10 +830,11 @@ struct SampleCoef {
   float A_hi, A_lo;   // K - Mt as an unevaluated float pair: p_j ~ 2^(ld_j c_T + K - Mt)
 };
 
-__device__ __forceinline__ SampleCoef coef_of(const VerifyArgs& a, const SeqRec& rec, float epsS) {
+__device__ __forceinline__ SampleCoef coef_of(const VerifyArgs& a, int b, const SeqRec& rec, float epsS) {
   SampleCoef c;
-  c.c_hi = a.c_hi;
-  c.c_lo = a.c_lo;
+  const TCoef tc = temp_coef(a, b);
+  c.c_hi = tc.c_hi;
+  c.c_lo = tc.c_lo;
   c.Mt = rec.Mt;
   c.K_hi = rec.K_hi;
   c.K_lo = rec.K_lo;
@@ -995,7 +1036,7 @@ __device__ void mass_item(const VerifyArgs& a, int b, int s, double* lds_d) {
   if (!rec.valid || rec.mode != kModeSaguaroEps) return;
   double tw[kTilesPerItem + 1];
   float mt[kTilesPerItem];
-  tile_sums<DT, VEC, kModeResidual>(a, b, coef_of(a, rec, 0.f), rec.k, s * kTilesPerItem, tw, mt, lds_d);
+  tile_sums<DT, VEC, kModeResidual>(a, b, coef_of(a, b, rec, 0.f), rec.k, s * kTilesPerItem, tw, mt, lds_d);
   if (threadIdx.x == 0) slot_put(a.mass + (int64_t)b * a.nt + s, tw[kTilesPerItem]);
 }
 
@@ -1005,7 +1046,7 @@ __device__ void sample_item(const VerifyArgs& a, int b, int s, double* lds_d) {
   if (!rec.valid) return;
   const int t0 = s * kTilesPerItem;
   const float epsS = rec.mode == kModeSaguaroEps ? eps_clamp(a, b, lds_d) : 0.f;
-  const SampleCoef cf = coef_of(a, rec, epsS);
+  const SampleCoef cf = coef_of(a, b, rec, epsS);
   with_mode(rec.mode, [&](auto m) {
     constexpr int MODE = decltype(m)::value;
     double tw[kTilesPerItem + 1];
@@ -1259,7 +1300,7 @@ __device__ void draw_item(const VerifyArgs& a, int b, DrawLds& sh) {
   const int g = a.gamma, k = rec.k;
   uint64_t* tiles = a.tiles + (int64_t)b * a.ntile;
   const float epsS = rec.mode == kModeSaguaroEps ? eps_clamp(a, b, sh.lds_d) : 0.f;
-  const SampleCoef cf = coef_of(a, rec, epsS);
+  const SampleCoef cf = coef_of(a, b, rec, epsS);
   int mode = rec.mode;
   for (int t = tid; t < a.ntile; t += kThreads) (void)poll(a, tiles + t);
   double rtot = 0.0;   // residual mass (relative to Mt) when it differs from the tile total
@@ -1322,7 +1363,7 @@ __device__ void final_item(const VerifyArgs& a, int b, FinalLds& sh) {
       const bool ok = row_ok(M, z);
       sh.ok = ok;
       const bool read = !a.early || (rec.valid && rec.k == g);
-      if (ok && read && a.diag.row_max) a.diag.row_max[(int64_t)b * R + r] = (double)mr * a.invT;
+      if (ok && read && a.diag.row_max) a.diag.row_max[(int64_t)b * R + r] = (double)mr * temp_coef(a, b).invT;
       if (ok && read && a.diag.row_logZ) a.diag.row_logZ[(int64_t)b * R + r] = M * 0.69314718055994530942 + log(z);
       if (rec.valid) {
         uint64_t* ys = drawn_slot(a, b);
@@ -1874,10 +1915,11 @@ static int verify_impl(const void* draft, const void* target, int dtype, const i
                        int32_t* out_fr, uint64_t* out_mask, int32_t* out_len,
                        const spec_diag* diag, void* ws, size_t ws_bytes, void* stream,
                        int saguaro, float eps, int32_t* cand = nullptr, int32_t* hit = nullptr,
-                       int32_t* cand_idx = nullptr, int early = 0) {
+                       int32_t* cand_idx = nullptr, int early = 0, const float* temps = nullptr) {
   if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_EDTYPE;
   if (!sizes_ok(B, gamma, V)) return SPEC_EINVAL;
-  if (!(T > 0.f) || !std::isfinite(T)) return SPEC_EINVAL;
+  if (!temps && (!(T > 0.f) || !std::isfinite(T))) return SPEC_EINVAL;
+  if (temps) T = 1.f;   // unused: every sequence has its own
   if (!(eps >= 0.f) || !std::isfinite(eps)) return SPEC_EINVAL;
   if (B == 0) return SPEC_OK;
   if (!draft || !target || !tokens || !u_acc || !u_smp || !out_tokens || !out_acc)
@@ -1935,6 +1977,7 @@ static int verify_impl(const void* draft, const void* target, int dtype, const i
   a.saguaro = saguaro;
   a.eps = eps;
   a.early = early;
+  a.temps = temps;
 
   PredictArgs p;
   if (cand) {
@@ -2017,6 +2060,24 @@ int spec_verify_early(const void* draft_logits, const void* target_logits, int d
                          gamma, V, temperature, in_len, out_tokens, out_accepted, out_first_reject,
                          out_accept_mask, out_len, diag, workspace, workspace_bytes, stream, saguaro,
                          eps, nullptr, nullptr, nullptr, 1);
+}
+
+int spec_verify_ex(const void* draft_logits, const void* target_logits, int dtype,
+                   const int32_t* draft_tokens, const float* u_accept, const float* u_sample, int B,
+                   int gamma, int V, float temperature, const int32_t* in_len, int32_t* out_tokens,
+                   int32_t* out_accepted, int32_t* out_first_reject, uint64_t* out_accept_mask,
+                   int32_t* out_len, const spec_diag* diag, const spec_options* opts,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  spec_options o{};
+  if (opts) o = *opts;
+  if (o.saguaro != 0 && o.saguaro != 1) return SPEC_EINVAL;
+  if (o.early && o.cand) return SPEC_EINVAL;
+  if (!o.cand && (o.hit || o.cand_idx)) return SPEC_EINVAL;
+  return sv::verify_impl(draft_logits, target_logits, dtype, draft_tokens, u_accept, u_sample, B,
+                         gamma, V, temperature, in_len, out_tokens, out_accepted, out_first_reject,
+                         out_accept_mask, out_len, diag, workspace, workspace_bytes, stream,
+                         o.saguaro, o.saguaro ? o.eps : 0.f, o.cand, o.hit, o.cand_idx, o.early ? 1 : 0,
+                         o.temperature);
 }
 
 const char* spec_status_str(int status) {

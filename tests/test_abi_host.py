@@ -164,3 +164,22 @@ def test_verify_predict_rejects_bad_arguments():
     assert call(saguaro=1, eps=-1.0) == R.SPEC_EINVAL
     assert call(T=0.0) == R.SPEC_EINVAL
     assert call(dtype=3) == R.SPEC_EDTYPE
+
+
+def test_verify_ex_rejects_bad_options():
+    lib = R.load_library()
+
+    def call(T=1.0, **o):
+        opts = R.SpecOptions(o.get("saguaro", 0), o.get("eps", 0.0), o.get("early", 0),
+                             o.get("temps"), o.get("cand"), o.get("hit"), o.get("idx"))
+        return lib.spec_verify_ex(FAKE, FAKE, R.SPEC_BF16, FAKE, FAKE, FAKE, 4, 3, 1000, T, None,
+                                  FAKE, FAKE, None, None, None, None, ctypes.byref(opts), FAKE,
+                                  1 << 30, None)
+
+    assert call(saguaro=2) == R.SPEC_EINVAL
+    assert call(saguaro=1, eps=-1.0) == R.SPEC_EINVAL
+    assert call(early=1, cand=FAKE) == R.SPEC_EINVAL
+    assert call(hit=FAKE) == R.SPEC_EINVAL
+    assert call(idx=FAKE) == R.SPEC_EINVAL
+    assert call(T=0.0) == R.SPEC_EINVAL              # the scalar is checked without an array
+    assert call(T=math.nan) == R.SPEC_EINVAL

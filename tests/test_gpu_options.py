@@ -1,0 +1,112 @@
+"""GPU parity of spec_verify_ex options: per-sequence temperatures (with every
+mode: residual, Saguaro, early exit, outcome prediction) against the fp64
+oracle run at each sequence's own temperature.
+
+Every case prints its name, shapes and seed before touching the GPU.
+"""
+import functools
+
+import numpy as np
+import pytest
+
+import oracle as O
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+H = pytest.importorskip("gpu_harness")
+from test_gpu_parity import random_batch  # noqa: E402
+
+
+@functools.lru_cache(maxsize=None)
+def workload(name):
+    H.say(f"[gen] {name}")
+    return W.make_workload(name, workers=8)
+
+
+def run_ex(batch, temps, mode="residual", eps=0.0, early=False, predict=False, diag=True):
+    import rejection_sampling_verify_12_amd as R
+    H.say(f"[options] {batch.name} B={batch.B} gamma={batch.gamma} V={batch.V} {batch.dtype} "
+          f"mode={mode} eps={eps} early={early} predict={predict}")
+    db = H.to_device(batch)
+    dt = R.SPEC_BF16 if batch.dtype == "bf16" else R.SPEC_F32
+    ws = R.new_workspace(R.spec_workspace_bytes(batch.B, batch.gamma, batch.V, dt), "cuda")
+    T = temps if np.isscalar(temps) else torch.from_numpy(np.asarray(temps, np.float32)).cuda()
+    pred = R.alloc_predict_outputs(batch.B, batch.gamma, "cuda") if predict else None
+    res = R.spec_verify_ex(db.draft, db.target, db.tokens, db.u_accept, db.u_sample, T,
+                           in_len=db.in_len, diag=diag, workspace=ws, saguaro=mode == "saguaro",
+                           eps=eps, early=early, pred=pred)
+    out = res[0] if predict else res
+    torch.cuda.synchronize()
+    assert int(ws[:4].view(torch.int32).item()) == 0, "bounded wait timed out"
+    host = {"tokens": out.tokens.cpu().numpy(), "accepted": out.accepted.cpu().numpy(),
+            "first_reject": out.first_reject.cpu().numpy(),
+            "mask": out.accept_mask.cpu().numpy().view(np.uint64), "out_len": out.out_len.cpu().numpy()}
+    if out.diag is not None:
+        host["diag"] = {k: v.cpu().numpy() for k, v in out.diag.items()}
+    if predict:
+        host["cand"] = pred.cand.cpu().numpy()
+        host["hit"] = pred.hit.cpu().numpy()
+        host["cand_idx"] = pred.cand_idx.cpu().numpy()
+    return host
+
+
+def oracle_per_seq(batch, temps, mode="residual", eps=0.0, early=False):
+    fn = O.verify_early_one if early else O.verify_one
+    d64, t64 = batch.draft64(), batch.target64()
+    return {b: fn(d64[b], t64[b], batch.draft_tokens[b], batch.u_accept[b], batch.u_sample[b],
+                  float(temps[b]), mode, eps, int(batch.in_len[b])) for b in range(batch.B)}
+
+
+TEMPS = [0.25, 0.7, 1.0, 1.6, 3.0, 0.0, -1.0, np.nan, np.inf, 0.9, 1.2, 0.5]
+
+
+@pytest.mark.parametrize("mode,eps,early", [("residual", 0.0, False), ("saguaro", 0.0, False),
+                                            ("saguaro", 1e-8, False), ("residual", 0.0, True)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_per_sequence_temperature(mode, eps, early, dtype):
+    batch = random_batch(len(TEMPS), 4, 50000, dtype, 1.0, seed=6100)
+    temps = np.array(TEMPS, np.float32)
+    gpu = run_ex(batch, temps, mode, eps, early)
+    ref = oracle_per_seq(batch, temps, mode, eps, early)
+    assert [ref[b].valid for b in range(batch.B)] == [bool(np.isfinite(t) and t > 0) for t in temps]
+    rep = H.compare(batch, gpu, ref)
+    H.say(f"[options]   {rep}")
+    rep.check()
+
+
+def test_per_sequence_temperature_with_prediction():
+    batch = random_batch(len(TEMPS), 4, 50000, "bf16", 1.0, seed=6101)
+    temps = np.array(TEMPS, np.float32)
+    gpu = run_ex(batch, temps, predict=True)
+    ref = oracle_per_seq(batch, temps)
+    H.compare(batch, gpu, ref).check()
+    ref_cand = O.predict_outcomes(batch.draft64())
+    np.testing.assert_array_equal(gpu["cand"], ref_cand)
+    hit, idx = O.predict_hits(ref_cand, gpu["accepted"], gpu["tokens"])
+    np.testing.assert_array_equal(gpu["hit"], hit)
+    np.testing.assert_array_equal(gpu["cand_idx"], idx)
+
+
+def test_temperature_ramp_on_the_b256_workload():
+    """T_b from 0.5 to 2.0 across the 256 sequences, against the oracle."""
+    batch = workload("B256_g8_V152064_bf16")
+    temps = np.linspace(0.5, 2.0, batch.B).astype(np.float32)
+    gpu = run_ex(batch, temps)
+    ref = oracle_per_seq(batch, temps)
+    rep = H.compare(batch, gpu, ref)
+    H.say(f"[options]   {rep}")
+    rep.check()
+
+
+def test_equal_temperatures_match_the_scalar_call():
+    """A per-sequence array of the batch temperature gives the scalar call's
+    outputs and diagnostics bit for bit."""
+    batch = workload("B128_g4_V128256_bf16")
+    a = run_ex(batch, np.full(batch.B, batch.T, np.float32))
+    b = run_ex(batch, float(batch.T))
+    for k in ("tokens", "accepted", "first_reject", "mask", "out_len"):
+        np.testing.assert_array_equal(a[k], b[k], err_msg=k)
+    for k, v in a["diag"].items():
+        np.testing.assert_array_equal(v, b["diag"][k], err_msg=k)

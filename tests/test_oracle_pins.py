@@ -581,3 +581,12 @@ def test_early_exit_reads_only_up_to_the_first_rejection():
     t4[3, 2] = 0.0
     r = O.verify_early_one(d, t4, x, u, us, 1.0, in_len=4)
     assert (r.accepted, r.mask, r.out_len) == (3, 7, 8)
+
+
+def test_bad_temperature_makes_the_sequence_invalid():
+    d = np.zeros((3, 4))
+    for T in (0.0, -1.0, np.nan, np.inf):
+        for fn in (O.verify_one, O.verify_early_one):
+            r = fn(d, d, [0, 1], [0.1, 0.1], [0.2, 0.2, 0.2], T, in_len=5)
+            assert r.accepted == -1 and r.out_len == 5 and (r.tokens == -1).all()
+    assert O.verify_one(d, d, [0, 1], [0.1, 0.1], [0.2, 0.2, 0.2], 1e-3).accepted == 2
