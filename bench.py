@@ -49,6 +49,14 @@ def parse():
                          "first rejection; the roofline prices the rows the rule reads")
     ap.add_argument("--predict-separate", action="store_true",
                     help="with --predict: verification, then the stand-alone prediction call")
+    ap.add_argument("--ssd", action="store_true",
+                    help="speculative speculative decoding pipeline with synthetic timed models: "
+                         "standard SD (one stream) against SSD (two streams), one sequence per round")
+    ap.add_argument("--ssd-rounds", type=int, default=64)
+    ap.add_argument("--ssd-t", type=float, default=0.5, help="temperature of the SSD rounds")
+    ap.add_argument("--ssd-draft-us", type=float, default=220.0,
+                    help="draft model time per round (gamma draft steps)")
+    ap.add_argument("--ssd-target-us", type=float, default=330.0, help="target model time per round")
     ap.add_argument("--sets", type=int, default=0,
                     help="input sets to rotate through (0: enough for > 1 GB)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -104,12 +112,65 @@ def cpu_baseline(batch, mode: str, eps: float, budget_s: float, tokens=None) -> 
                       f"{dt:.1f} s"}
 
 
+def ssd_main(args):
+    """SD vs SSD rounds on one sequence at a time (the B=128 workload's
+    sequences in turn, draft tokens drawn at --ssd-t)."""
+    import numpy as np
+    import torch
+
+    import rejection_sampling_verify_12_amd as R
+    import workloads as W
+    from rejection_sampling_verify_12_amd import ssd
+
+    name = args.workload if args.workload != DEFAULT_WORKLOAD else "B128_g4_V128256_bf16"
+    batch = W.make_workload(name, seqs=np.arange(min(32, W.WORKLOADS[name][0])),
+                            workers=min(16, os.cpu_count() or 1))
+    T = args.ssd_t
+    tok = W.gumbel_argmax(batch.draft64()[:, :batch.gamma], T, W.philox(batch.seed, 91))
+    dev = torch.device("cuda:0")
+
+    def logits(a):
+        if batch.dtype == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    rounds = [(logits(batch.draft[i:i + 1]), logits(batch.target[i:i + 1]),
+               torch.from_numpy(tok[i:i + 1].astype(np.int32)).to(dev),
+               torch.from_numpy(batch.u_accept[i:i + 1]).to(dev),
+               torch.from_numpy(batch.u_sample[i:i + 1]).to(dev)) for i in range(batch.B)]
+    td, tt = int(args.ssd_draft_us * 1e3), int(args.ssd_target_us * 1e3)
+    ssd.run_sd(rounds, T, td, tt, 4)       # warm-up
+    ssd.run_ssd(rounds, T, td, tt, 4)
+    n = args.ssd_rounds
+    t_sd, o_sd = ssd.run_sd(rounds, T, td, tt, n)
+    t_ssd, o_ssd, p_ssd = ssd.run_ssd(rounds, T, td, tt, n)
+    tokens = ssd.emitted_tokens(o_sd)
+    assert tokens == ssd.emitted_tokens(o_ssd)
+    hit = float(np.mean([int(p.hit.item()) for p in p_ssd]))
+    # verification time alone, for the predicted round times
+    t_v = ssd.run_sd(rounds, T, 0, 0, n)[0] / n
+    sd_round, ssd_round = t_sd / n, t_ssd / n
+    pred_ssd = max(td * 1e-9, tt * 1e-9 + t_v) + (1 - hit) * td * 1e-9
+    print(json.dumps({
+        "metric": "tokens/s of a speculative-decoding loop with synthetic timed models",
+        "sd_tokens_per_s": tokens / t_sd, "ssd_tokens_per_s": tokens / t_ssd,
+        "speedup": t_sd / t_ssd, "hit_rate": hit, "tokens": tokens, "rounds": n,
+        "round_us": {"sd": sd_round * 1e6, "ssd": ssd_round * 1e6, "verify_only": t_v * 1e6,
+                     "ssd_expected": pred_ssd * 1e6,
+                     "sd_expected": (td + tt) * 1e-3 + t_v * 1e6},
+        "config": {"workload": name, "B_per_round": 1, "gamma": batch.gamma, "V": batch.V,
+                   "T": T, "draft_us": args.ssd_draft_us, "target_us": args.ssd_target_us},
+        "data": "synthetic", "source_digest": source_digest()}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU: --gpus {args.gpus} is not supported (sequences are "
               "independent; a multi-GPU run would shard B with no communication).", file=sys.stderr)
         sys.exit(2)
+    if args.ssd:
+        return ssd_main(args)
 
     import numpy as np
     import torch

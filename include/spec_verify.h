@@ -284,6 +284,19 @@ int spec_verify_greedy(const void* target_logits, int dtype, const int32_t* draf
                        uint64_t* out_accept_mask, int32_t* out_len, void* workspace,
                        size_t workspace_bytes, void* stream);
 
+/*
+ * A timed stand-in for a model forward pass, for scheduling experiments
+ * around the verification ("Speculative Speculative Decoding (Saguaro)",
+ * section 4.1: the draft model runs on its own stream while the target
+ * verifies; SSD summary, AMD MI300X part: two HIP streams and events).  It
+ * keeps one work-group of `stream` busy for `ns` nanoseconds of wall time
+ * (0 <= ns <= 1e8), so it occupies its stream without taking the compute
+ * units the verification uses.  With hit != NULL (a DEVICE array [n] of a
+ * prediction's hit flags) it first checks them on the device and returns at
+ * once when none is 0 (no fallback pass is needed).  Enqueues only.
+ */
+int spec_synthetic_busy(int64_t ns, const int32_t* hit, int n, void* stream);
+
 /* A static, human-readable description of a status code. */
 const char* spec_status_str(int status);
 

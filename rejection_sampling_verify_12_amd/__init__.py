@@ -21,7 +21,7 @@ SPEC_F32, SPEC_BF16 = 0, 1
 EXPORTED = ("spec_workspace_bytes", "spec_verify", "spec_verify_saguaro",
             "spec_predict_workspace_bytes", "spec_predict_outcomes", "spec_verify_predict",
             "spec_greedy_workspace_bytes", "spec_verify_greedy", "spec_verify_early",
-            "spec_verify_ex", "spec_status_str")
+            "spec_verify_ex", "spec_synthetic_busy", "spec_status_str")
 
 
 class SpecOptions(ctypes.Structure):
@@ -67,6 +67,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.spec_verify_early.argtypes = verify_args[:-3] + [i32, f32] + verify_args[-3:]
     lib.spec_verify_ex.argtypes = verify_args[:-3] + [ctypes.POINTER(SpecOptions)] + verify_args[-3:]
     lib.spec_verify_ex.restype = i32
+    lib.spec_synthetic_busy.argtypes = [ctypes.c_int64, vp, i32, vp]
+    lib.spec_synthetic_busy.restype = i32
     lib.spec_verify_early.restype = i32
     lib.spec_greedy_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.spec_greedy_workspace_bytes.restype = sz
@@ -268,6 +270,18 @@ def spec_verify_ex(draft_logits, target_logits, draft_tokens, u_accept, u_sample
                        u_sample, T, in_len, out, diag, workspace, stream,
                        eps if saguaro else 0.0, pred, early, temps, ex=True)
     return (out, pred) if pred is not None else out
+
+
+def spec_synthetic_busy(ns: int, hit=None, stream=None, device=None):
+    """Keep one work-group of the stream busy for ns nanoseconds (a stand-in
+    for a model forward pass); with ``hit``, only if some flag is 0."""
+    import torch
+    dev = hit.device if hit is not None else (device or torch.device("cuda"))
+    _check_dev(hit)
+    st = load_library().spec_synthetic_busy(int(ns), _ptr(hit), 0 if hit is None else hit.numel(),
+                                            _stream_handle(stream, dev))
+    if st != SPEC_OK:
+        raise SpecError(st)
 
 
 def spec_greedy_workspace_bytes(B: int, gamma: int, V: int, dtype: int) -> int:

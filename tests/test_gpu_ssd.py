@@ -1,0 +1,78 @@
+"""The SSD pipeline (two streams, synthetic timed models) around the real
+verification and prediction kernels: same tokens as standard SD, and round
+times that follow the schedule (max(draft, target + verify) when every
+outcome was predicted, plus a fallback draft when one was not).
+
+Every case prints its name before touching the GPU.
+"""
+import numpy as np
+import pytest
+
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+H = pytest.importorskip("gpu_harness")
+
+
+def rounds_forced(hit: bool, n=6, g=4, V=4096, seed=3):
+    """One-sequence rounds where every draft is accepted (p == q on rows < gamma)
+    and target row gamma is one-hot at a token that is (hit) or is not (miss)
+    among the draft's top-3 at position gamma."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for r in range(n):
+        d = rng.normal(size=(1, g + 1, V)).astype(np.float32)
+        t = d.copy()
+        top = np.argsort(-d[0, g])[:3]
+        y = int(top[0]) if hit else int(np.argsort(-d[0, g])[V // 2])
+        t[0, g] = -30.0
+        t[0, g, y] = 30.0
+        x = np.argmax(d[0, :g], axis=-1)[None].astype(np.int32)
+        dev = "cuda"
+        out.append((torch.from_numpy(d).to(dev), torch.from_numpy(t).to(dev),
+                    torch.from_numpy(x).to(dev), torch.full((1, g), 0.5, device=dev),
+                    torch.full((1, g + 1), 0.5, device=dev)))
+    return out
+
+
+@pytest.mark.parametrize("hit", [True, False])
+def test_ssd_schedule_follows_the_hits(hit):
+    from rejection_sampling_verify_12_amd import ssd
+    H.say(f"[ssd] forced {'hits' if hit else 'misses'}")
+    rounds = rounds_forced(hit)
+    td, tt, n = 600_000, 900_000, 12            # ns: draft 0.6 ms, target 0.9 ms per round
+    ssd.run_ssd(rounds, 1.0, td, tt, 2)          # warm-up
+    t_sd, o_sd = ssd.run_sd(rounds, 1.0, td, tt, n)
+    t_ssd, o_ssd, p_ssd = ssd.run_ssd(rounds, 1.0, td, tt, n)
+    hits = [int(p.hit.item()) for p in p_ssd]
+    assert hits == [int(hit)] * n
+    for a, b in zip(o_sd, o_ssd):
+        assert torch.equal(a.tokens, b.tokens) and torch.equal(a.accepted, b.accepted)
+    assert ssd.emitted_tokens(o_sd) == n * 5
+    sd_round, ssd_round = t_sd / n * 1e6, t_ssd / n * 1e6
+    H.say(f"[ssd] round us: sd {sd_round:.0f}, ssd {ssd_round:.0f}")
+    assert 1500 <= sd_round <= 1500 * 1.25             # draft + target (+ verify)
+    if hit:
+        assert 900 <= ssd_round <= 900 * 1.25 + 100     # max(draft, target + verify)
+    else:
+        assert 1500 <= ssd_round <= 1500 * 1.25        # the fallback draft is paid every round
+
+
+def test_ssd_on_workload_rows():
+    """Rows of the B=128 workload at T = 0.5, one sequence per round: the same
+    tokens both ways, and SSD no slower than SD."""
+    from rejection_sampling_verify_12_amd import ssd
+    H.say("[ssd] workload rows")
+    b = W.make_workload("B128_g4_V128256_bf16", seqs=np.arange(8), workers=4)
+    tok = W.gumbel_argmax(b.draft64()[:, :b.gamma], 0.5, W.philox(b.seed, 91))
+    rounds = [(H.logits_to_device(b.draft[i:i + 1], "bf16"), H.logits_to_device(b.target[i:i + 1], "bf16"),
+               torch.from_numpy(tok[i:i + 1].astype(np.int32)).cuda(),
+               torch.from_numpy(b.u_accept[i:i + 1]).cuda(),
+               torch.from_numpy(b.u_sample[i:i + 1]).cuda()) for i in range(b.B)]
+    t_sd, o_sd = ssd.run_sd(rounds, 0.5, 300_000, 400_000, 8)
+    t_ssd, o_ssd, _ = ssd.run_ssd(rounds, 0.5, 300_000, 400_000, 8)
+    for a, c in zip(o_sd, o_ssd):
+        assert torch.equal(a.tokens, c.tokens)
+    assert t_ssd <= t_sd * 1.05
