@@ -20,6 +20,8 @@ from .verify import (  # noqa: F401
     verify,
     verify_one,
     verify_early_one,
+    nucleus,
+    cut_to_nucleus,
     top3,
     predict_outcomes,
     predict_hits,

@@ -47,6 +47,14 @@ notes with its justification):
 * out_len = in_len + k + 1 (tokens committed this round).
 * A per-sequence temperature that is not finite and positive makes that
   sequence invalid (a batch-wide one is rejected before any work).
+* Top-p ([SD] section 3, after the unbiasedness check: the rule stacks on
+  top-p sampling unchanged, when both sides use the same setting, section
+  5.4): each row's distribution is cut to its nucleus and renormalised, and
+  the rule runs on the cut distributions.  The pages do not define the
+  nucleus; here it is every token whose logit is at least L, where L is the
+  largest logit value at which the mass of the tokens with logits >= L
+  reaches top_p (equal logits are all in or all out, so no order among equal
+  tokens is needed).  top_p >= 1 keeps every token.
 * Greedy verification is the temperature -> 0 limit of the rule: accept x_i
   iff it is the target's most likely token at position i, and emit the
   target's most likely token at the stopping position (the correction after a
@@ -112,6 +120,31 @@ def choice(pi: np.ndarray, u: float) -> tuple[int, float, float]:
 
 
 # ---------------------------------------------------------------------------
+# Top-p cut of one row.
+
+def nucleus(logits64_row: np.ndarray, T: float, top_p: float):
+    """(L, mass, margin): the nucleus threshold logit, the probability mass of
+    the tokens with logit >= L, and the distance of top_p from the two running
+    masses around the cut (the boundary margin).  top_p >= 1: (-inf, 1, inf)."""
+    l = np.asarray(logits64_row, dtype=np.float64)
+    if top_p >= 1.0:
+        return -np.inf, 1.0, np.inf
+    prob, _, _ = softmax_rows(l, T)
+    vals = np.unique(l)[::-1]                  # distinct logits, descending
+    run = 0.0
+    for v in vals:
+        before = run
+        run += prob[l == v].sum()
+        if run >= top_p:
+            return float(v), run, min(top_p - before, run - top_p)
+    return float(vals[-1]), run, abs(run - top_p)
+
+
+def cut_to_nucleus(prob: np.ndarray, logits64_row: np.ndarray, L: float, mass: float) -> np.ndarray:
+    return np.where(np.asarray(logits64_row) >= L, prob / mass, 0.0)
+
+
+# ---------------------------------------------------------------------------
 # O4: the distribution drawn from after a rejection.
 
 def residual_weights(p_k: np.ndarray, q_k: np.ndarray) -> np.ndarray:
@@ -162,7 +195,7 @@ def _invalid(gamma: int, in_len: int) -> SeqResult:
 
 
 def verify_one(draft64, target64, tokens, u_accept, u_sample, T, mode="residual",
-               eps=0.0, in_len=0) -> SeqResult:
+               eps=0.0, in_len=0, top_p=1.0) -> SeqResult:
     """Verify one sequence.
 
     draft64, target64: [gamma+1, V] float64 logits.  tokens: [gamma] draft tokens.
@@ -181,6 +214,16 @@ def verify_one(draft64, target64, tokens, u_accept, u_sample, T, mode="residual"
     # O1
     p, pm, plz = softmax_rows(draft64[:gamma], T)
     q, qm, qlz = softmax_rows(target64[:gamma + 1], T)
+    topp_margin = np.inf
+    if top_p < 1.0:   # the rule on the nucleus of every row ([SD] section 3)
+        for i in range(gamma):
+            L, P, m = nucleus(draft64[i], T, top_p)
+            p[i] = cut_to_nucleus(p[i], draft64[i], L, P)
+            topp_margin = min(topp_margin, m)
+        for i in range(gamma + 1):
+            L, P, m = nucleus(target64[i], T, top_p)
+            q[i] = cut_to_nucleus(q[i], target64[i], L, P)
+            topp_margin = min(topp_margin, m)
 
     # O2: every position's decision (the mask reports all gamma of them).
     idx = np.arange(gamma)
@@ -225,8 +268,9 @@ def verify_one(draft64, target64, tokens, u_accept, u_sample, T, mode="residual"
     out[k] = y
     return SeqResult(
         valid=True, accepted=k, first_reject=k if k < gamma else -1, mask=mask,
-        tokens=out, out_len=int(in_len) + k + 1, a=a, acc_margin=np.abs(ua - a),
-        sample_margin=min(us - lo, hi - us),
+        tokens=out, out_len=int(in_len) + k + 1, a=a,
+        acc_margin=np.minimum(np.abs(ua - a), topp_margin),
+        sample_margin=min(us - lo, hi - us, topp_margin),
         row_max=np.concatenate([pm, qm]), row_logZ=np.concatenate([plz, qlz]),
         px=px, qx=qx, resid_mass=S, token_prob=float(pi[y]), cdf_lo=lo, cdf_hi=hi)
 

@@ -590,3 +590,72 @@ def test_bad_temperature_makes_the_sequence_invalid():
             r = fn(d, d, [0, 1], [0.1, 0.1], [0.2, 0.2, 0.2], T, in_len=5)
             assert r.accepted == -1 and r.out_len == 5 and (r.tokens == -1).all()
     assert O.verify_one(d, d, [0, 1], [0.1, 0.1], [0.2, 0.2, 0.2], 1e-3).accepted == 2
+
+
+# --------------------------------------------------------------------------- top-p
+
+def _nucleus_by_sorting(l, T, top_p):
+    """The shortest prefix of the tokens sorted by probability (then id) whose
+    mass reaches top_p, extended to every token tied with its last one."""
+    prob, _, _ = O.softmax_rows(l, T)
+    order = np.lexsort((np.arange(len(l)), -l))
+    run, last = 0.0, None
+    for j in order:
+        run += prob[j]
+        last = j
+        if run >= top_p:
+            break
+    keep = l >= l[last]
+    return keep, prob[keep].sum()
+
+
+def test_nucleus_against_sorting():
+    rng = np.random.default_rng(41)
+    for trial in range(300):
+        V = int(rng.integers(1, 30))
+        l = np.round(rng.normal(size=V) * 2, int(rng.integers(0, 2)))   # ties
+        T = float(rng.choice([0.5, 1.0, 2.0]))
+        top_p = float(rng.choice([0.1, 0.5, 0.8, 0.9, 0.95, 0.999]))
+        L, mass, _ = O.nucleus(l, T, top_p)
+        keep, m2 = _nucleus_by_sorting(l, T, top_p)
+        np.testing.assert_array_equal(l >= L, keep)
+        assert abs(mass - m2) < 1e-12
+    L, mass, _ = O.nucleus(np.array([1.0, 2.0]), 1.0, 1.0)
+    assert L == -np.inf and mass == 1.0
+
+
+def test_top_p_one_is_no_cut():
+    rng = np.random.default_rng(42)
+    d = rng.normal(size=(4, 9))
+    t = d + 0.5 * rng.normal(size=d.shape)
+    a = O.verify_one(d, t, [1, 2, 3], [0.3, 0.6, 0.9], [0.1, 0.5, 0.7, 0.2], 1.0)
+    b = O.verify_one(d, t, [1, 2, 3], [0.3, 0.6, 0.9], [0.1, 0.5, 0.7, 0.2], 1.0, top_p=1.0)
+    np.testing.assert_array_equal(a.tokens, b.tokens)
+    assert a.mask == b.mask and a.token_prob == b.token_prob
+
+
+def test_top_p_rule_emits_the_cut_target_distribution():
+    """With draft tokens drawn from the cut draft distribution, the first
+    emitted token follows the cut target distribution (the pages' unbiasedness
+    claim, with top-p on both sides), by a chi-square test over 60k rounds."""
+    rng = np.random.default_rng(43)
+    V, T, top_p = 7, 1.0, 0.8
+    d = np.log(np.array([[.30, .20, .15, .12, .10, .08, .05]] * 2))
+    t = np.log(np.array([[.10, .28, .22, .16, .11, .08, .05]] * 2))
+    pd, _, _ = O.softmax_rows(d[0], T)
+    Ld, Pd, _ = O.nucleus(d[0], T, top_p)
+    p_cut = O.cut_to_nucleus(pd, d[0], Ld, Pd)
+    qt, _, _ = O.softmax_rows(t[0], T)
+    Lt, Pt, _ = O.nucleus(t[0], T, top_p)
+    q_cut = O.cut_to_nucleus(qt, t[0], Lt, Pt)
+    n = 60000
+    xs = rng.choice(V, size=n, p=p_cut)
+    ua, us = rng.random(n), rng.random((n, 2))
+    counts = np.zeros(V)
+    for i in range(n):
+        r = O.verify_one(d, t, [xs[i]], [ua[i]], us[i], T, top_p=top_p)
+        counts[r.tokens[0]] += 1
+    assert counts[q_cut == 0].sum() == 0
+    nz = q_cut > 0
+    chi = scipy.stats.chisquare(counts[nz], q_cut[nz] * n)
+    assert chi.pvalue > 1e-3, (counts / n, q_cut)
