@@ -49,6 +49,8 @@ def parse():
                          "first rejection; the roofline prices the rows the rule reads")
     ap.add_argument("--predict-separate", action="store_true",
                     help="with --predict: verification, then the stand-alone prediction call")
+    ap.add_argument("--top-p", type=float, default=0.0,
+                    help="cut every row to its top-p nucleus (spec_verify_ex); 0 = no cut")
     ap.add_argument("--ssd", action="store_true",
                     help="speculative speculative decoding pipeline with synthetic timed models: "
                          "standard SD (one stream) against SSD (two streams), one sequence per round")
@@ -194,6 +196,8 @@ def main():
           flush=True)
     B, g, V = batch.B, batch.gamma, batch.V
     dt_code = R.SPEC_BF16 if batch.dtype == "bf16" else R.SPEC_F32
+    if args.top_p > 0.0 and (args.predict or args.early or args.mode == "greedy"):
+        sys.exit("--top-p combines with residual or Saguaro verification only")
     if (args.predict or args.early) and args.mode == "greedy":
         sys.exit("--predict and --early are not available with --mode greedy")
     if args.predict and args.early:
@@ -237,6 +241,10 @@ def main():
         d, t = sets[i % nsets]
         if greedy:
             R.spec_verify_greedy(t, tok, out=out, workspace=ws, stream=stream)
+        elif args.top_p > 0.0:
+            R.spec_verify_ex(d, t, tok, ua, us, batch.T, out=out, workspace=ws, stream=stream,
+                             saguaro=args.mode == "saguaro", eps=args.eps, top_p=args.top_p,
+                             early=args.early)
         elif args.early:
             R.spec_verify_early(d, t, tok, ua, us, batch.T, out=out, workspace=ws, stream=stream,
                                 saguaro=args.mode == "saguaro", eps=args.eps)
@@ -294,7 +302,7 @@ def main():
                                                          float(batch.alpha_target.max())],
                    "mean_accepted": float(acc.mean()),
                    "predict": ("separate" if sep else "fused") if args.predict else False,
-                   "early_exit": bool(args.early),
+                   "early_exit": bool(args.early), "top_p": args.top_p or None,
                    **({"hit_rate": float(pout.hit.float().mean().item())} if args.predict else {})},
         "event_ms": {"mean": ev_ms, "p10": float(np.percentile(per_call_ms, 10)),
                      "p50": float(np.percentile(per_call_ms, 50)),

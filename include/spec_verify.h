@@ -228,7 +228,16 @@ int spec_verify_early(const void* draft_logits, const void* target_logits, int d
  *     A T_b that is not finite and positive makes only that sequence invalid.
  *   cand, hit, cand_idx: outcome prediction outputs as spec_verify_predict
  *     (cand NULL = no prediction; hit / cand_idx need cand).
- * early and prediction do not combine (SPEC_EINVAL).
+ *   top_p: 0 or 1 = no cut; in (0, 1): every row's distribution (draft rows
+ *     0..gamma-1, target rows 0..gamma) is cut to its nucleus and
+ *     renormalised, and the rule runs on the cut distributions (same section
+ *     3 remark: the rule stacks on top-p sampling; section 5.4: the same
+ *     setting on both sides).  The nucleus is every token whose logit is >= L,
+ *     L the largest logit value at which the mass of the tokens with logits
+ *     >= L reaches top_p (equal logits all in or all out).  Diagnostics report
+ *     p(x), q(x), pi(y) and the running sums of the cut distributions and the
+ *     row statistics of the uncut rows.  Outside [0, 1] or NaN: SPEC_EINVAL.
+ * early combines with neither prediction nor a top-p cut (SPEC_EINVAL).
  */
 typedef struct spec_options {
   int saguaro;
@@ -238,6 +247,7 @@ typedef struct spec_options {
   int32_t* cand;
   int32_t* hit;
   int32_t* cand_idx;
+  float top_p;
 } spec_options;
 
 /*

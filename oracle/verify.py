@@ -125,19 +125,23 @@ def choice(pi: np.ndarray, u: float) -> tuple[int, float, float]:
 def nucleus(logits64_row: np.ndarray, T: float, top_p: float):
     """(L, mass, margin): the nucleus threshold logit, the probability mass of
     the tokens with logit >= L, and the distance of top_p from the two running
-    masses around the cut (the boundary margin).  top_p >= 1: (-inf, 1, inf)."""
+    masses around the cut (the boundary margin).  top_p >= 1: (-inf, 1, inf).
+
+    The tokens are sorted by logit (descending); the running mass is read at
+    the end of each run of equal logits, and the first run end at which it
+    reaches top_p gives L."""
     l = np.asarray(logits64_row, dtype=np.float64)
     if top_p >= 1.0:
         return -np.inf, 1.0, np.inf
     prob, _, _ = softmax_rows(l, T)
-    vals = np.unique(l)[::-1]                  # distinct logits, descending
-    run = 0.0
-    for v in vals:
-        before = run
-        run += prob[l == v].sum()
-        if run >= top_p:
-            return float(v), run, min(top_p - before, run - top_p)
-    return float(vals[-1]), run, abs(run - top_p)
+    order = np.argsort(-l, kind="stable")
+    ls, run = l[order], np.cumsum(prob[order])
+    ends = np.nonzero(np.append(ls[1:] != ls[:-1], True))[0]   # last index of each run
+    at = run[ends]
+    hit = np.nonzero(at >= top_p)[0]
+    g = int(hit[0]) if hit.size else len(ends) - 1
+    before = float(at[g - 1]) if g > 0 else 0.0
+    return float(ls[ends[g]]), float(at[g]), abs(min(top_p - before, float(at[g]) - top_p))
 
 
 def cut_to_nucleus(prob: np.ndarray, logits64_row: np.ndarray, L: float, mass: float) -> np.ndarray:

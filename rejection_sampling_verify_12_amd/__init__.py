@@ -28,7 +28,7 @@ class SpecOptions(ctypes.Structure):
     """struct spec_options (see spec_verify.h)."""
     _fields_ = [("saguaro", ctypes.c_int), ("eps", ctypes.c_float), ("early", ctypes.c_int),
                 ("temperature", ctypes.c_void_p), ("cand", ctypes.c_void_p),
-                ("hit", ctypes.c_void_p), ("cand_idx", ctypes.c_void_p)]
+                ("hit", ctypes.c_void_p), ("cand_idx", ctypes.c_void_p), ("top_p", ctypes.c_float)]
 
 
 class SpecDiag(ctypes.Structure):
@@ -154,7 +154,7 @@ def alloc_outputs(B: int, gamma: int, device, diag: bool = False) -> VerifyOut:
 def _verify_call(saguaro: bool, draft_logits, target_logits, draft_tokens, u_accept, u_sample,
                  temperature: float, in_len=None, out: VerifyOut | None = None, diag: bool = False,
                  workspace=None, stream=None, eps: float = 0.0, pred=None, early=False,
-                 temps=None, ex=False) -> VerifyOut:
+                 temps=None, ex=False, top_p: float = 0.0) -> VerifyOut:
     lib = load_library()
     B, G1, V = draft_logits.shape
     gamma = G1 - 1
@@ -184,7 +184,7 @@ def _verify_call(saguaro: bool, draft_logits, target_logits, draft_tokens, u_acc
         opts = SpecOptions(int(saguaro), float(eps), int(early), _ptr(temps),
                            pred.cand.data_ptr() if pred is not None else None,
                            _ptr(pred.hit) if pred is not None else None,
-                           _ptr(pred.cand_idx) if pred is not None else None)
+                           _ptr(pred.cand_idx) if pred is not None else None, float(top_p))
         st = lib.spec_verify_ex(*args[:-3], ctypes.byref(opts), *args[-3:])
     elif early:
         st = lib.spec_verify_early(*args[:-3], int(saguaro), float(eps), *args[-3:])
@@ -258,7 +258,8 @@ def spec_verify_early(draft_logits, target_logits, draft_tokens, u_accept, u_sam
 
 def spec_verify_ex(draft_logits, target_logits, draft_tokens, u_accept, u_sample, temperature,
                    in_len=None, out=None, diag=False, workspace=None, stream=None,
-                   saguaro: bool = False, eps: float = 0.0, early: bool = False, pred=None):
+                   saguaro: bool = False, eps: float = 0.0, early: bool = False, pred=None,
+                   top_p: float = 0.0):
     """Verification with options (see spec_verify.h): ``temperature`` is a float
     for the whole batch or a [B] float32 device tensor of per-sequence
     temperatures; ``pred`` (a PredictOut) asks for outcome prediction.
@@ -268,7 +269,7 @@ def spec_verify_ex(draft_logits, target_logits, draft_tokens, u_accept, u_sample
     T = 1.0 if temps is not None else float(temperature)
     out = _verify_call(bool(saguaro), draft_logits, target_logits, draft_tokens, u_accept,
                        u_sample, T, in_len, out, diag, workspace, stream,
-                       eps if saguaro else 0.0, pred, early, temps, ex=True)
+                       eps if saguaro else 0.0, pred, early, temps, ex=True, top_p=top_p)
     return (out, pred) if pred is not None else out
 
 

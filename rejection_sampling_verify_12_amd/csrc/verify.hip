@@ -160,6 +160,19 @@ constexpr int kStopWord = 4, kProgWord = 5, kTestsWord = 6;
 constexpr uint64_t kSkipPiece = 1ull;
 constexpr unsigned kSkipRaw = 1u;
 
+// Top-p state of one row (the rows of the rule, numbered as the pieces):
+// its normaliser, the radix selection of the nucleus threshold, and the
+// result.  Masses are in units of 2^M (the row's integer offset).
+struct TopPRow {
+  double M, Z;       // the row's offset and normaliser
+  double rem;        // mass still to reach inside the selected key prefix
+  double above;      // mass of the keys above the selected prefix
+  double P;          // nucleus mass / Z (1 without a cut)
+  uint32_t prefix;   // selected high digits of the threshold key
+  float L;           // threshold logit: the nucleus is l >= L (-inf: no cut)
+};
+constexpr int kDigits = 256;   // 8-bit radix digits
+
 struct VerifyArgs {
   const void* draft;
   const void* target;
@@ -192,6 +205,9 @@ struct VerifyArgs {
   float eps;
   int early;         // early exit: rows beyond the first rejection are not needed
   const float* temps;   // [B] per-sequence temperatures, or NULL (c_hi, c_lo, cTd, invT for all)
+  TopPRow* topp;        // [B][2*gamma+1] with a top-p cut, else NULL
+  double* hist;         // [B][2*gamma+1][kDigits] radix histograms of the cut
+  float top_p;
 };
 
 // The temperature scale of sequence b: log2(e) / T as an unevaluated float
@@ -595,7 +611,7 @@ struct DecideLds {
 // every draft position (wave 0, lane i = position i; fp64) and the decision
 // record.  Target row gamma is checked by the sequence's final item.  A bad
 // row or token makes the sequence invalid here, with its outputs.
-template <int DT>
+template <int DT, bool CUT = false>
 __device__ void decide_item(const VerifyArgs& a, int b, DecideLds& sh) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = a.gamma, Rd = 2 * g, R = 2 * g + 1;
@@ -648,8 +664,13 @@ __device__ void decide_item(const VerifyArgs& a, int b, DecideLds& sh) {
       bad = (x < 0 || x >= a.V);
       if (!bad && !rows_bad) {
         // p(x) = pn / Zd and q(x) = qn / Zt; the ratio with one division.
-        const double pn = exp2((double)sh.ldx[lane] * tc.cTd - sh.M[lane]);
-        const double qn = exp2((double)sh.ltx[lane] * tc.cTd - sh.M[g + lane]);
+        double pn = exp2((double)sh.ldx[lane] * tc.cTd - sh.M[lane]);
+        double qn = exp2((double)sh.ltx[lane] * tc.cTd - sh.M[g + lane]);
+        if constexpr (CUT) {   // p'(x) = p(x) / P_d inside the draft nucleus, else 0; q' alike
+          const TopPRow* tp = a.topp + (int64_t)b * R;
+          pn = sh.ldx[lane] >= tp[lane].L ? pn / tp[lane].P : 0.0;
+          qn = sh.ltx[lane] >= tp[g + lane].L ? qn / tp[g + lane].P : 0.0;
+        }
         double ratio;
         if (pn > 0.0) ratio = fmin(1.0, (qn * sh.Z[lane]) / (pn * sh.Z[g + lane]));
         else ratio = qn > 0.0 ? 1.0 : 0.0;
@@ -682,9 +703,14 @@ __device__ void decide_item(const VerifyArgs& a, int b, DecideLds& sh) {
     rec.Zt = 1.0;
     if (sh.valid && k < g) {   // the bonus draw (k == gamma) offsets each tile on its own
       const double Mt = sh.M[g + k];
+      double Pt = 1.0, Pd = 1.0;   // nucleus masses (top-p): q' = q / Pt, p' = p / Pd
+      if constexpr (CUT) {
+        Pt = a.topp[(int64_t)b * R + g + k].P;
+        Pd = a.topp[(int64_t)b * R + k].P;
+      }
       rec.Mt = (float)Mt;   // exact below 2^24; otherwise Zt absorbs the rounding
-      rec.Zt = ldexp(sh.Z[g + k], (int)fmin(fmax(Mt - (double)rec.Mt, -2000.0), 2000.0));
-      const double K = (Mt - sh.M[k]) + log2(sh.Z[g + k] / sh.Z[k]);
+      rec.Zt = ldexp(sh.Z[g + k] * Pt, (int)fmin(fmax(Mt - (double)rec.Mt, -2000.0), 2000.0));
+      const double K = (Mt - sh.M[k]) + log2((sh.Z[g + k] * Pt) / (sh.Z[k] * Pd));
       rec.K_hi = (float)K;
       rec.K_lo = (float)(K - (double)rec.K_hi);
     }
@@ -828,8 +854,25 @@ __device__ void test_item(const VerifyArgs& a, int b, int i, TestLds& sh) {
 struct SampleCoef {
   float c_hi, c_lo, Mt, K_hi, K_lo, epsS;
   float A_hi, A_lo;   // K - Mt as an unevaluated float pair: p_j ~ 2^(ld_j c_T + K - Mt)
+  float Ld, Lt;       // top-p thresholds of the rows drawn from (-inf: no cut)
 };
 
+// A top-p cut: logits below the row's threshold act as -inf (probability 0);
+// the renormalisation is folded into the decision record's constants.
+template <bool CUT>
+__device__ __forceinline__ void cut8(float (&v)[8], float L) {
+  if constexpr (CUT) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = v[e] >= L ? v[e] : -INFINITY;
+  }
+}
+template <bool CUT>
+__device__ __forceinline__ float cut1(float v, float L) {
+  if constexpr (CUT) return v >= L ? v : -INFINITY;
+  else return v;
+}
+
+template <bool CUT = false>
 __device__ __forceinline__ SampleCoef coef_of(const VerifyArgs& a, int b, const SeqRec& rec, float epsS) {
   SampleCoef c;
   const TCoef tc = temp_coef(a, b);
@@ -842,6 +885,13 @@ __device__ __forceinline__ SampleCoef coef_of(const VerifyArgs& a, int b, const 
   const double A = ((double)rec.K_hi + (double)rec.K_lo) - (double)rec.Mt;
   c.A_hi = uni((float)A);
   c.A_lo = uni((float)(A - (double)c.A_hi));
+  c.Ld = -INFINITY;
+  c.Lt = -INFINITY;
+  if (CUT && a.topp && rec.k >= 0 && rec.k <= a.gamma) {
+    const TopPRow* tp = a.topp + (int64_t)b * (2 * a.gamma + 1);
+    c.Lt = uni(tp[a.gamma + rec.k].L);
+    if (rec.k < a.gamma) c.Ld = uni(tp[rec.k].L);
+  }
   return c;
 }
 
@@ -900,6 +950,7 @@ __device__ __forceinline__ float weight_one(float ld, float lt, const SampleCoef
       const float bb = dl - ld;
       const float err = (ld - (dl - bb)) - (lt + bb);             // ld - lt = dl + err
       d = fmaf(dl, c.c_hi, c.K_hi) + fmaf(err, c.c_hi, fmaf(dl, c.c_lo, c.K_lo));
+      if (ld == -INFINITY) d = -INFINITY;   // p_j = 0 (the two-sum of an infinite difference is NaN)
     }
     const float ex = exp2_fast(d);          // p_j / q_j
     const float em1 = one_minus_exp2<PRECISE>(d, ex);
@@ -908,7 +959,10 @@ __device__ __forceinline__ float weight_one(float ld, float lt, const SampleCoef
     r = res;
     if constexpr (MODE == kModeResidual) return res;
     else if constexpr (MODE == kModeSaguaro) return pos ? eq * sqrtf(ex * em1) : 0.f;
-    else return (eq > 0.f) ? sqrtf(eq * ex * fmaxf(res, c.epsS)) : 0.f;
+    else {   // p_j from its own exponential where q_j = 0 (eq ex would be 0 * inf)
+      const float pj = eq > 0.f ? eq * ex : exp2_fast(fmaf(ld, c.c_lo, fmaf(ld, c.c_hi, c.A_hi) + c.A_lo));
+      return sqrtf(pj * fmaxf(res, c.epsS));
+    }
   }
 }
 
@@ -919,14 +973,17 @@ __device__ __forceinline__ void sample_weights(const float (&ld)[8], const float
   for (int e = 0; e < 8; ++e) w[e] = weight_one<DT, MODE, PRECISE>(ld[e], lt[e], c, r[e]);
 }
 
-// Call f with the weight mode as a compile-time constant.
-template <class F>
+// Call f with the weight mode as a compile-time constant.  EPS = false: code
+// that never sees the Saguaro eps > 0 mode (the fused kernel) leaves it out.
+template <bool EPS = true, class F>
 __device__ __forceinline__ void with_mode(int mode, F&& f) {
   switch (mode) {
     case kModeTarget: f(std::integral_constant<int, kModeTarget>{}); break;
     case kModeResidual: f(std::integral_constant<int, kModeResidual>{}); break;
     case kModeSaguaro: f(std::integral_constant<int, kModeSaguaro>{}); break;
-    default: f(std::integral_constant<int, kModeSaguaroEps>{}); break;
+    default:
+      if constexpr (EPS) f(std::integral_constant<int, kModeSaguaroEps>{});
+      break;
   }
 }
 
@@ -951,7 +1008,7 @@ __device__ __forceinline__ float tile_offset(float bm, float c_hi) {
 // words take half the registers of floats).  In target mode (the bonus draw)
 // every tile gets its own integer offset mt[i] (its weights are
 // 2^(lt_j c_T - mt[i])), so no row normaliser is needed.
-template <int DT, bool VEC, int MODE, int N = kTilesPerItem>
+template <int DT, bool VEC, int MODE, bool CUT = false, int N = kTilesPerItem>
 __device__ __forceinline__ void tile_sums(const VerifyArgs& a, int b, const SampleCoef& cf, int k,
                                           int t0, double (&tw)[N + 1], float (&mt)[N], double* lds_d) {
   constexpr int G = (DT == kBF16 && VEC) ? N : (N >= 2 ? 2 : 1);
@@ -976,6 +1033,7 @@ __device__ __forceinline__ void tile_sums(const VerifyArgs& a, int b, const Samp
       for (int i = 0; i < G; ++i) {
         float lt[8];
         unpack<DT, VEC>(rt[i], lt);
+        cut8<CUT>(lt, cf.Lt);
         float m = lt[0];
 #pragma unroll
         for (int e = 1; e < 8; ++e) m = fmaxf(m, lt[e]);
@@ -989,7 +1047,11 @@ __device__ __forceinline__ void tile_sums(const VerifyArgs& a, int b, const Samp
     for (int i = 0; i < G; ++i) {
       float ld[8], lt[8], w[8], r[8];
       unpack<DT, VEC>(rt[i], lt);
-      if constexpr (MODE != kModeTarget) unpack<DT, VEC>(rd[i], ld);
+      cut8<CUT>(lt, cf.Lt);
+      if constexpr (MODE != kModeTarget) {
+        unpack<DT, VEC>(rd[i], ld);
+        cut8<CUT>(ld, cf.Ld);
+      }
       SampleCoef c = cf;
       if constexpr (MODE == kModeTarget) {
         c.Mt = off[i];
@@ -1030,28 +1092,28 @@ __device__ float eps_clamp(const VerifyArgs& a, int b, double* lds_d) {
 // ---------------------------------------------------------------------------
 // Residual-mass and sampling items.
 
-template <int DT, bool VEC>
+template <int DT, bool VEC, bool CUT = false>
 __device__ void mass_item(const VerifyArgs& a, int b, int s, double* lds_d) {
   const SeqRec rec = wait_rec<true>(a, b);
   if (!rec.valid || rec.mode != kModeSaguaroEps) return;
   double tw[kTilesPerItem + 1];
   float mt[kTilesPerItem];
-  tile_sums<DT, VEC, kModeResidual>(a, b, coef_of(a, b, rec, 0.f), rec.k, s * kTilesPerItem, tw, mt, lds_d);
+  tile_sums<DT, VEC, kModeResidual, CUT>(a, b, coef_of<CUT>(a, b, rec, 0.f), rec.k, s * kTilesPerItem, tw, mt, lds_d);
   if (threadIdx.x == 0) slot_put(a.mass + (int64_t)b * a.nt + s, tw[kTilesPerItem]);
 }
 
-template <int DT, bool VEC>
+template <int DT, bool VEC, bool CUT = false, bool EPS = true>
 __device__ void sample_item(const VerifyArgs& a, int b, int s, double* lds_d) {
   const SeqRec rec = wait_rec<true>(a, b);
   if (!rec.valid) return;
   const int t0 = s * kTilesPerItem;
   const float epsS = rec.mode == kModeSaguaroEps ? eps_clamp(a, b, lds_d) : 0.f;
-  const SampleCoef cf = coef_of(a, b, rec, epsS);
-  with_mode(rec.mode, [&](auto m) {
+  const SampleCoef cf = coef_of<CUT>(a, b, rec, epsS);
+  with_mode<EPS>(rec.mode, [&](auto m) {
     constexpr int MODE = decltype(m)::value;
     double tw[kTilesPerItem + 1];
     float mt[kTilesPerItem];
-    tile_sums<DT, VEC, MODE>(a, b, cf, rec.k, t0, tw, mt, lds_d);
+    tile_sums<DT, VEC, MODE, CUT>(a, b, cf, rec.k, t0, tw, mt, lds_d);
     if (threadIdx.x == 0) {
 #pragma unroll
       for (int i = 0; i < kTilesPerItem; ++i)
@@ -1160,7 +1222,7 @@ __device__ double locate_tile(const uint64_t* tiles, int ntile, double u, DrawLd
 // eight weights to thread 0, which walks them in fp64: y = the first token
 // with weight whose running sum passes the target (else the lane's last token
 // with weight).  Sets sh.y, sh.e, sh.lo = C_{y-1} and sh.hi = C_y (draw units).
-template <int DT, bool VEC, int MODE>
+template <int DT, bool VEC, int MODE, bool CUT = false>
 __device__ void rescan_tile(const VerifyArgs& a, int b, int k, const SampleCoef& cf, double target,
                             DrawLds& sh) {
   const int tid = threadIdx.x;
@@ -1176,7 +1238,11 @@ __device__ void rescan_tile(const VerifyArgs& a, int b, int k, const SampleCoef&
     if constexpr (MODE != kModeTarget) load_raw<DT, VEC>(drow, j0, a.V, rd);
     float ld[8], lt[8], r[8];
     unpack<DT, VEC>(rt, lt);
-    if constexpr (MODE != kModeTarget) unpack<DT, VEC>(rd, ld);
+    cut8<CUT>(lt, cf.Lt);
+    if constexpr (MODE != kModeTarget) {
+      unpack<DT, VEC>(rd, ld);
+      cut8<CUT>(ld, cf.Ld);
+    }
     SampleCoef c = cf;
     if (MODE == kModeTarget && k == a.gamma) {   // the bonus draw: the tile's own offset
       float m[1] = {lt[0]};
@@ -1237,17 +1303,17 @@ __device__ void rescan_tile(const VerifyArgs& a, int b, int k, const SampleCoef&
 }
 
 // pi(y)'s weight in draw units, with the precise residual (thread 0).
-template <int DT>
+template <int DT, bool CUT = false, bool EPS = true>
 __device__ double precise_weight(const VerifyArgs& a, int b, int k, int mode, const SampleCoef& cf, int y,
                                  const DrawLds& sh) {
   const void *drow, *trow;
   draw_rows<DT>(a, b, k, drow, trow);
-  const float lt = load_one<DT>(trow, y);
-  const float ld = mode == kModeTarget ? 0.f : load_one<DT>(drow, y);
+  const float lt = cut1<CUT>(load_one<DT>(trow, y), cf.Lt);
+  const float ld = mode == kModeTarget ? 0.f : cut1<CUT>(load_one<DT>(drow, y), cf.Ld);
   SampleCoef c = cf;
   if (mode == kModeTarget && k == a.gamma) c.Mt = (float)(sh.Mp + sh.e);   // the tile's offset
   float w = 0.f, r;
-  with_mode(mode, [&](auto m) { w = weight_one<DT, decltype(m)::value, true>(ld, lt, c, r); });
+  with_mode<EPS>(mode, [&](auto m) { w = weight_one<DT, decltype(m)::value, true>(ld, lt, c, r); });
   return ldexp((double)w, sh.e);
 }
 
@@ -1256,7 +1322,7 @@ __device__ double precise_weight(const VerifyArgs& a, int b, int k, int mode, co
 // q_k, k < gamma, whose offset Mt is the record's; degenerate inputs only).
 // One logit at a time, with the weights and order the rescan uses, so its
 // per-lane fp32 sums match.
-template <int DT>
+template <int DT, bool CUT = false>
 __device__ void recompute_tiles(const VerifyArgs& a, int b, int k, int mode, const SampleCoef& cf,
                                 DrawLds& sh) {
   uint64_t* tiles = a.tiles + (int64_t)b * a.ntile;
@@ -1270,8 +1336,9 @@ __device__ void recompute_tiles(const VerifyArgs& a, int b, int k, int mode, con
       const int64_t j = j0 + e;
       float w = 0.f, rr;
       if (j < a.V) {
-        const float lt = load_one<DT>(trow, j);
-        if (mode == kModeResidual) w = weight_one<DT, kModeResidual, false>(load_one<DT>(drow, j), lt, cf, rr);
+        const float lt = cut1<CUT>(load_one<DT>(trow, j), cf.Lt);
+        if (mode == kModeResidual)
+          w = weight_one<DT, kModeResidual, false>(cut1<CUT>(load_one<DT>(drow, j), cf.Ld), lt, cf, rr);
         else w = weight_one<DT, kModeTarget, false>(0.f, lt, cf, rr);
       }
       ws += w;
@@ -1292,7 +1359,7 @@ __device__ __forceinline__ uint64_t* drawn_slot(const VerifyArgs& a, int b) {
 // The draw at the stopping position: tile values, locate, rescan.  The token
 // goes to the sequence's drawn slot, the diagnostics out.  Clears the tile and
 // residual-sum slots once read.
-template <int DT, bool VEC>
+template <int DT, bool VEC, bool CUT = false, bool EPS = true>
 __device__ void draw_item(const VerifyArgs& a, int b, DrawLds& sh) {
   const int tid = threadIdx.x;
   const SeqRec rec = wait_rec<true>(a, b);
@@ -1300,7 +1367,7 @@ __device__ void draw_item(const VerifyArgs& a, int b, DrawLds& sh) {
   const int g = a.gamma, k = rec.k;
   uint64_t* tiles = a.tiles + (int64_t)b * a.ntile;
   const float epsS = rec.mode == kModeSaguaroEps ? eps_clamp(a, b, sh.lds_d) : 0.f;
-  const SampleCoef cf = coef_of(a, b, rec, epsS);
+  const SampleCoef cf = coef_of<CUT>(a, b, rec, epsS);
   int mode = rec.mode;
   for (int t = tid; t < a.ntile; t += kThreads) (void)poll(a, tiles + t);
   double rtot = 0.0;   // residual mass (relative to Mt) when it differs from the tile total
@@ -1322,13 +1389,13 @@ __device__ void draw_item(const VerifyArgs& a, int b, DrawLds& sh) {
     if (mode == kModeResidual) rtot = S;
     if (S > 0.0 || mode == kModeTarget) break;
     mode = mode == kModeResidual ? kModeTarget : kModeResidual;
-    recompute_tiles<DT>(a, b, k, mode, cf, sh);
+    recompute_tiles<DT, CUT>(a, b, k, mode, cf, sh);
   }
-  with_mode(mode, [&](auto m) { rescan_tile<DT, VEC, decltype(m)::value>(a, b, k, cf, target, sh); });
+  with_mode<EPS>(mode, [&](auto m) { rescan_tile<DT, VEC, decltype(m)::value, CUT>(a, b, k, cf, target, sh); });
   if (tid == 0) {
     const int y = sh.y;
     if (a.diag.resid_mass) a.diag.resid_mass[b] = k < g ? rtot / rec.Zt : 0.0;
-    if (a.diag.token_prob) a.diag.token_prob[b] = precise_weight<DT>(a, b, k, mode, cf, y, sh) / S;
+    if (a.diag.token_prob) a.diag.token_prob[b] = precise_weight<DT, CUT, EPS>(a, b, k, mode, cf, y, sh) / S;
     if (a.diag.cdf_lo) a.diag.cdf_lo[b] = sh.lo / S;
     if (a.diag.cdf_hi) a.diag.cdf_hi[b] = sh.hi / S;
     st_dev_u64(drawn_slot(a, b), ~(uint64_t)(uint32_t)y);
@@ -1655,9 +1722,9 @@ void fused_kernel(VerifyArgs a, Sched sc) {
       if constexpr (EARLY) test_item<DT>(a, b - b / a.B * a.B, b / a.B, sh.t);
       break;
     case kItemDecide: decide_item<DT>(a, b, sh.d); break;
-    case kItemMass: mass_item<DT, VEC>(a, b, sub, sh.r.lds_d); break;
-    case kItemSample: sample_item<DT, VEC>(a, b, sub, sh.r.lds_d); break;
-    case kItemDraw: draw_item<DT, VEC>(a, b, sh.r); break;
+    case kItemMass: break;   // Saguaro with eps > 0 runs as separate kernels
+    case kItemSample: sample_item<DT, VEC, false, false>(a, b, sub, sh.r.lds_d); break;
+    case kItemDraw: draw_item<DT, VEC, false, false>(a, b, sh.r); break;
     case kItemLast:
       if (EARLY && skip) {
         early_skip(a, b, 2 * a.gamma, sub);
@@ -1682,10 +1749,10 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(VerifyArgs a) {
   stream_item<DT, VEC, U>(a, b, r, c, sh);
 }
 
-template <int DT>
+template <int DT, bool CUT>
 __global__ __launch_bounds__(kThreads) void decide_kernel(VerifyArgs a) {
   __shared__ DecideLds sh;
-  decide_item<DT>(a, blockIdx.x, sh);
+  decide_item<DT, CUT>(a, blockIdx.x, sh);
 }
 
 template <int DT>
@@ -1695,24 +1762,164 @@ __global__ __launch_bounds__(kThreads) void test_kernel(VerifyArgs a) {
   test_item<DT>(a, blockIdx.x - i * a.B, i, sh);
 }
 
-template <int DT, bool VEC>
+template <int DT, bool VEC, bool CUT>
 __global__ __launch_bounds__(kThreads) void mass_kernel(VerifyArgs a) {
   __shared__ double lds_d[kWaves * (kTilesPerItem + 1)];
   const int b = blockIdx.x / a.nt, s = blockIdx.x - b * a.nt;
-  mass_item<DT, VEC>(a, b, s, lds_d);
+  mass_item<DT, VEC, CUT>(a, b, s, lds_d);
 }
 
-template <int DT, bool VEC>
+template <int DT, bool VEC, bool CUT>
 __global__ __launch_bounds__(kThreads) void sample_kernel(VerifyArgs a) {
   __shared__ double lds_d[kWaves * (kTilesPerItem + 1)];
   const int b = blockIdx.x / a.nt, s = blockIdx.x - b * a.nt;
-  sample_item<DT, VEC>(a, b, s, lds_d);
+  sample_item<DT, VEC, CUT>(a, b, s, lds_d);
 }
 
-template <int DT, bool VEC>
+template <int DT, bool VEC, bool CUT>
 __global__ __launch_bounds__(kThreads) void draw_kernel(VerifyArgs a) {
   __shared__ DrawLds sh;
-  draw_item<DT, VEC>(a, blockIdx.x, sh);
+  draw_item<DT, VEC, CUT>(a, blockIdx.x, sh);
+}
+
+// ---------------------------------------------------------------------------
+// Top-p: the nucleus threshold of every row by a radix selection over the
+// logits' order-preserving keys (16 bits for bfloat16, 32 for float32; 8 bits
+// a pass), each key weighted by its probability mass, from the highest key
+// down, until the mass reaches top_p.
+
+// The order-preserving key of a logit (+0.0 and -0.0 share one), in kb bits.
+template <int DT>
+__device__ __forceinline__ uint32_t logit_key(float v) {
+  uint32_t b = __float_as_uint(v);
+  if (b == 0x80000000u) b = 0u;
+  const uint32_t k = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return DT == kBF16 ? k >> 16 : k;
+}
+template <int DT>
+__device__ __forceinline__ float key_logit(uint32_t k) {
+  if constexpr (DT == kBF16) {
+    const uint32_t b = (k & 0x8000u) ? (k & 0x7FFFu) : (~k & 0xFFFFu);
+    return __uint_as_float(b << 16);
+  } else {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+  }
+}
+
+// One wave per row: the row's offset and normaliser from its pieces (left in
+// place for the decision), and the selection's start.
+__global__ __launch_bounds__(64) void topp_init_kernel(VerifyArgs a) {
+  const int64_t row = blockIdx.x;
+  const int lane = threadIdx.x;
+  const uint64_t* p = a.part + row * a.nc;
+  double M = -INFINITY;
+  for (int c = lane; c < a.nc; c += 64) M = fmax(M, slot_value(ld_dev_u64(p + c)));
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) M = fmax(M, __shfl_xor(M, o, 64));
+  M = ceil(M);
+  double z = 0.0;
+  for (int c = lane; c < a.nc; c += 64) {
+    const double v = slot_value(ld_dev_u64(p + c));
+    if (v != -INFINITY) z += exp2(v - M);
+  }
+  z = wave_sum(z);
+  if (lane == 0) {
+    TopPRow t;
+    t.M = M;
+    t.Z = z;
+    t.rem = (double)a.top_p * z;
+    t.above = 0.0;
+    t.P = 1.0;
+    t.prefix = 0u;
+    t.L = -INFINITY;
+    a.topp[row] = t;
+  }
+}
+
+// (row, chunk) items: the masses of the chunk's logits whose key matches the
+// selected prefix, by the pass's digit, into the row's histogram.
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kThreads) void topp_hist_kernel(VerifyArgs a, int pass) {
+  __shared__ double h[kDigits];
+  const int R = 2 * a.gamma + 1;
+  const int64_t id = blockIdx.x;
+  const int64_t row = id / a.nc;
+  const int c = (int)(id - row * a.nc);
+  const int b = (int)(row / R), r = (int)(row - (int64_t)b * R);
+  const TCoef tc = temp_coef(a, b);
+  const float Mf = (float)uni(a.topp[row].M);
+  const uint32_t prefix = (uint32_t)uni((int)a.topp[row].prefix);
+  constexpr int KB = DT == kBF16 ? 16 : 32;
+  const int shift = KB - 8 * (pass + 1);
+  for (int i = threadIdx.x; i < kDigits; i += kThreads) h[i] = 0.0;
+  __syncthreads();
+  const void* rp = row_ptr<DT>(a, b, r);
+  const int64_t begin = (int64_t)c * a.chunk;
+  const int64_t end = min<int64_t>(begin + a.chunk, a.V);
+  int cur = -1;
+  double acc = 0.0;
+  for (int64_t j = begin + (int64_t)threadIdx.x * kUnit; j < end; j += kTile) {
+    Raw8<DT, VEC> raw;
+    load_raw<DT, VEC>(rp, j, end, raw);
+    float v[8];
+    unpack<DT, VEC>(raw, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if (j + e >= end) continue;
+      const uint32_t key = logit_key<DT>(v[e]);
+      if (pass > 0 && (key >> (shift + 8)) != prefix) continue;
+      const int d = (int)((key >> shift) & 0xFFu);
+      const double m = (double)exp2_fast(fmaf(v[e], tc.c_lo, fmaf(v[e], tc.c_hi, -Mf)));
+      if (d != cur) {   // runs of one digit are summed before one atomic add
+        if (cur >= 0) atomicAdd(&h[cur], acc);
+        cur = d;
+        acc = 0.0;
+      }
+      acc += m;
+    }
+  }
+  if (cur >= 0) atomicAdd(&h[cur], acc);
+  __syncthreads();
+  double* g = a.hist + row * kDigits;
+  for (int i = threadIdx.x; i < kDigits; i += kThreads)
+    if (h[i] != 0.0) atomicAdd(g + i, h[i]);
+}
+
+// One thread per row: the digit at which the mass from the top reaches the
+// remaining target; clears the histogram.  After the last pass, the threshold
+// logit and the nucleus mass.
+template <int DT>
+__global__ __launch_bounds__(64) void topp_select_kernel(VerifyArgs a, int pass, int npass) {
+  const int64_t row = (int64_t)blockIdx.x * 64 + threadIdx.x;
+  if (row >= (int64_t)a.B * (2 * a.gamma + 1)) return;
+  TopPRow t = a.topp[row];
+  double* g = a.hist + row * kDigits;
+  double run = 0.0, hsel = 0.0;
+  int sel = -1, low = -1;
+  for (int d = kDigits - 1; d >= 0; --d) {
+    const double m = g[d];
+    if (m > 0.0) low = d;
+    if (sel < 0 && run + m >= t.rem && m > 0.0) {
+      sel = d;
+      hsel = m;
+    } else if (sel < 0) {
+      run += m;
+    }
+  }
+  if (sel < 0) {   // rounding left the target above the total: keep everything
+    sel = low < 0 ? 0 : low;
+    hsel = low < 0 ? 0.0 : g[sel];
+    run -= hsel;
+  }
+  for (int d = 0; d < kDigits; ++d) g[d] = 0.0;
+  t.above += run;
+  t.rem -= run;
+  t.prefix = (t.prefix << 8) | (uint32_t)sel;
+  if (pass == npass - 1) {
+    t.L = key_logit<DT>(t.prefix);
+    t.P = (t.above + hsel) / t.Z;
+  }
+  a.topp[row] = t;
 }
 
 template <int DT>
@@ -1729,7 +1936,7 @@ static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 struct Layout {
   int nc, chunk, ntile, nt;
   size_t err_off, part_off, mraw_off, seq_off, flag_off, tiles_off, mass_off, rsum_off, cpart_off,
-      total;
+      topp_off, hist_off, total;
 };
 
 static bool sizes_ok(int B, int gamma, int V) {
@@ -1764,6 +1971,10 @@ static Layout layout(int B, int gamma, int V) {
   off += align256((size_t)B * L.nt * sizeof(uint64_t));
   L.cpart_off = off;
   off += align256((size_t)B * (gamma + 1) * L.nc * sizeof(Top3));
+  L.topp_off = off;
+  off += align256((size_t)B * R * sizeof(TopPRow));
+  L.hist_off = off;
+  off += align256((size_t)B * R * kDigits * sizeof(double));
   L.total = B == 0 ? 0 : off;
   return L;
 }
@@ -1857,56 +2068,73 @@ static hipError_t launch_all(const VerifyArgs& a, const PredictArgs* pa, hipStre
   // take one kernel per item kind (their sampling paths need more registers
   // than the stream items' occupancy leaves) and the stand-alone prediction.
   if constexpr (SV_FUSED && DT == kBF16 && VEC) {
-    int slots = 0;
-    const bool eps_mode = a.saguaro && a.eps > 0.f;
-    if (a.early) {
-      hipError_t e = resident_groups<DT, VEC, false, true>(slots);
+    if (!a.topp && !(a.saguaro && a.eps > 0.f)) {
+      int slots = 0;
+      const bool eps_mode = a.saguaro && a.eps > 0.f;
+      if (a.early) {
+        hipError_t e = resident_groups<DT, VEC, false, true>(slots);
+        if (e != hipSuccess) return e;
+        static_assert(SV_EARLY_CHUNK % SV_CHUNK == 0, "early-exit chunks are whole default chunks");
+        VerifyArgs b = a;   // never more chunks than the workspace holds
+        b.chunk = SV_EARLY_CHUNK;
+        b.nc = (int)(((int64_t)a.V + b.chunk - 1) / b.chunk);
+        const Sched sc = make_sched_early(b.B, b.gamma, b.nc, eps_mode ? b.nt : 0, b.nt, slots);
+        hipLaunchKernelGGL((fused_kernel<DT, VEC, SV_STREAM_UNROLL, false, true>), dim3((unsigned)sc.total),
+                           dim3(kThreads), 0, st, b, sc);
+        return hipGetLastError();
+      }
+      hipError_t e = pa ? resident_groups<DT, VEC, true, false>(slots) : resident_groups<DT, VEC, false, false>(slots);
       if (e != hipSuccess) return e;
-      static_assert(SV_EARLY_CHUNK % SV_CHUNK == 0, "early-exit chunks are whole default chunks");
-      VerifyArgs b = a;   // never more chunks than the workspace holds
-      b.chunk = SV_EARLY_CHUNK;
-      b.nc = (int)(((int64_t)a.V + b.chunk - 1) / b.chunk);
-      const Sched sc = make_sched_early(b.B, b.gamma, b.nc, eps_mode ? b.nt : 0, b.nt, slots);
-      hipLaunchKernelGGL((fused_kernel<DT, VEC, SV_STREAM_UNROLL, false, true>), dim3((unsigned)sc.total),
-                         dim3(kThreads), 0, st, b, sc);
+      const Sched sc = make_sched(a.B, 2 * a.gamma * a.nc, (pa ? 2 : 1) * a.nc, eps_mode ? a.nt : 0, a.nt, slots);
+      if (pa) {
+        hipLaunchKernelGGL((fused_kernel<DT, VEC, SV_STREAM_UNROLL, true, false>), dim3((unsigned)sc.total),
+                           dim3(kThreads), 0, st, a, sc);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        return predict_launch_leaders(*pa, SPEC_BF16, st);
+      }
+      hipLaunchKernelGGL((fused_kernel<DT, VEC, SV_STREAM_UNROLL, false, false>), dim3((unsigned)sc.total),
+                         dim3(kThreads), 0, st, a, sc);
       return hipGetLastError();
     }
-    hipError_t e = pa ? resident_groups<DT, VEC, true, false>(slots) : resident_groups<DT, VEC, false, false>(slots);
-    if (e != hipSuccess) return e;
-    const Sched sc = make_sched(a.B, 2 * a.gamma * a.nc, (pa ? 2 : 1) * a.nc, eps_mode ? a.nt : 0, a.nt, slots);
-    if (pa) {
-      hipLaunchKernelGGL((fused_kernel<DT, VEC, SV_STREAM_UNROLL, true, false>), dim3((unsigned)sc.total),
-                         dim3(kThreads), 0, st, a, sc);
-      e = hipGetLastError();
-      if (e != hipSuccess) return e;
-      return predict_launch_leaders(*pa, SPEC_BF16, st);
-    }
-    hipLaunchKernelGGL((fused_kernel<DT, VEC, SV_STREAM_UNROLL, false, false>), dim3((unsigned)sc.total),
-                       dim3(kThreads), 0, st, a, sc);
-    return hipGetLastError();
-  } else {
+  }
+  {
     hipError_t e = launch_kernels<DT, VEC>(a, st);
     if (e != hipSuccess || !pa) return e;
     return predict_launch_rows(*pa, DT == kBF16 ? SPEC_BF16 : SPEC_F32, VEC, st);
   }
 }
 
-template <int DT, bool VEC>
-static hipError_t launch_kernels(const VerifyArgs& a, hipStream_t st) {
+template <int DT, bool VEC, bool CUT>
+static hipError_t launch_kernels_cut(const VerifyArgs& a, hipStream_t st) {
   const int R = 2 * a.gamma + 1;
   const bool eps_mode = a.saguaro && a.eps > 0.f;
   const unsigned nstream = (unsigned)((int64_t)a.B * R * a.nc);
   const unsigned nsample = (unsigned)((int64_t)a.B * a.nt);
   hipLaunchKernelGGL((stream_kernel<DT, VEC, SV_STREAM_UNROLL>), dim3(nstream), dim3(kThreads), 0, st, a);
+  if constexpr (CUT) {   // the nucleus of every row, then the rule on the cut rows
+    const unsigned rows = (unsigned)((int64_t)a.B * R);
+    constexpr int npass = DT == kBF16 ? 2 : 4;
+    hipLaunchKernelGGL(topp_init_kernel, dim3(rows), dim3(64), 0, st, a);
+    for (int pass = 0; pass < npass; ++pass) {
+      hipLaunchKernelGGL((topp_hist_kernel<DT, VEC>), dim3(nstream), dim3(kThreads), 0, st, a, pass);
+      hipLaunchKernelGGL((topp_select_kernel<DT>), dim3((rows + 63) / 64), dim3(64), 0, st, a, pass, npass);
+    }
+  }
   if (a.early)   // position-major: the test of (i - 1, b) has a smaller block number than (i, b)'s
     hipLaunchKernelGGL((test_kernel<DT>), dim3((unsigned)((int64_t)a.gamma * a.B)), dim3(kThreads), 0, st, a);
   else
-    hipLaunchKernelGGL((decide_kernel<DT>), dim3((unsigned)a.B), dim3(kThreads), 0, st, a);
-  if (eps_mode) hipLaunchKernelGGL((mass_kernel<DT, VEC>), dim3(nsample), dim3(kThreads), 0, st, a);
-  hipLaunchKernelGGL((sample_kernel<DT, VEC>), dim3(nsample), dim3(kThreads), 0, st, a);
-  hipLaunchKernelGGL((draw_kernel<DT, VEC>), dim3((unsigned)a.B), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((decide_kernel<DT, CUT>), dim3((unsigned)a.B), dim3(kThreads), 0, st, a);
+  if (eps_mode) hipLaunchKernelGGL((mass_kernel<DT, VEC, CUT>), dim3(nsample), dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL((sample_kernel<DT, VEC, CUT>), dim3(nsample), dim3(kThreads), 0, st, a);
+  hipLaunchKernelGGL((draw_kernel<DT, VEC, CUT>), dim3((unsigned)a.B), dim3(kThreads), 0, st, a);
   hipLaunchKernelGGL((final_kernel<DT>), dim3((unsigned)a.B), dim3(kThreads), 0, st, a);
   return hipGetLastError();
+}
+
+template <int DT, bool VEC>
+static hipError_t launch_kernels(const VerifyArgs& a, hipStream_t st) {
+  return a.topp ? launch_kernels_cut<DT, VEC, true>(a, st) : launch_kernels_cut<DT, VEC, false>(a, st);
 }
 
 static int verify_impl(const void* draft, const void* target, int dtype, const int32_t* tokens,
@@ -1915,7 +2143,8 @@ static int verify_impl(const void* draft, const void* target, int dtype, const i
                        int32_t* out_fr, uint64_t* out_mask, int32_t* out_len,
                        const spec_diag* diag, void* ws, size_t ws_bytes, void* stream,
                        int saguaro, float eps, int32_t* cand = nullptr, int32_t* hit = nullptr,
-                       int32_t* cand_idx = nullptr, int early = 0, const float* temps = nullptr) {
+                       int32_t* cand_idx = nullptr, int early = 0, const float* temps = nullptr,
+                       float top_p = 1.f) {
   if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_EDTYPE;
   if (!sizes_ok(B, gamma, V)) return SPEC_EINVAL;
   if (!temps && (!(T > 0.f) || !std::isfinite(T))) return SPEC_EINVAL;
@@ -1978,6 +2207,13 @@ static int verify_impl(const void* draft, const void* target, int dtype, const i
   a.eps = eps;
   a.early = early;
   a.temps = temps;
+  a.top_p = top_p;
+  a.topp = nullptr;
+  a.hist = nullptr;
+  if (top_p < 1.f) {
+    a.topp = reinterpret_cast<TopPRow*>(w + L.topp_off);
+    a.hist = reinterpret_cast<double*>(w + L.hist_off);
+  }
 
   PredictArgs p;
   if (cand) {
@@ -2072,12 +2308,15 @@ int spec_verify_ex(const void* draft_logits, const void* target_logits, int dtyp
   if (opts) o = *opts;
   if (o.saguaro != 0 && o.saguaro != 1) return SPEC_EINVAL;
   if (o.early && o.cand) return SPEC_EINVAL;
+  if (!(o.top_p >= 0.f && o.top_p <= 1.f)) return SPEC_EINVAL;   // NaN included
+  const float top_p = o.top_p > 0.f ? o.top_p : 1.f;
+  if (o.early && top_p < 1.f) return SPEC_EINVAL;
   if (!o.cand && (o.hit || o.cand_idx)) return SPEC_EINVAL;
   return sv::verify_impl(draft_logits, target_logits, dtype, draft_tokens, u_accept, u_sample, B,
                          gamma, V, temperature, in_len, out_tokens, out_accepted, out_first_reject,
                          out_accept_mask, out_len, diag, workspace, workspace_bytes, stream,
                          o.saguaro, o.saguaro ? o.eps : 0.f, o.cand, o.hit, o.cand_idx, o.early ? 1 : 0,
-                         o.temperature);
+                         o.temperature, top_p);
 }
 
 const char* spec_status_str(int status) {

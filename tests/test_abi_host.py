@@ -183,3 +183,13 @@ def test_verify_ex_rejects_bad_options():
     assert call(idx=FAKE) == R.SPEC_EINVAL
     assert call(T=0.0) == R.SPEC_EINVAL              # the scalar is checked without an array
     assert call(T=math.nan) == R.SPEC_EINVAL
+
+
+def test_verify_ex_rejects_bad_top_p():
+    lib = R.load_library()
+    for top_p, early in ((-0.1, 0), (1.5, 0), (math.nan, 0), (0.9, 1)):
+        opts = R.SpecOptions(0, 0.0, early, None, None, None, None, top_p)
+        st = lib.spec_verify_ex(FAKE, FAKE, R.SPEC_BF16, FAKE, FAKE, FAKE, 4, 3, 1000, 1.0, None,
+                                FAKE, FAKE, None, None, None, None, ctypes.byref(opts), FAKE,
+                                1 << 30, None)
+        assert st == R.SPEC_EINVAL, (top_p, early)

@@ -25,10 +25,10 @@ def workload(name):
     return W.make_workload(name, workers=8)
 
 
-def run_ex(batch, temps, mode="residual", eps=0.0, early=False, predict=False, diag=True):
+def run_ex(batch, temps, mode="residual", eps=0.0, early=False, predict=False, diag=True, top_p=0.0):
     import rejection_sampling_verify_12_amd as R
     H.say(f"[options] {batch.name} B={batch.B} gamma={batch.gamma} V={batch.V} {batch.dtype} "
-          f"mode={mode} eps={eps} early={early} predict={predict}")
+          f"mode={mode} eps={eps} early={early} predict={predict} top_p={top_p}")
     db = H.to_device(batch)
     dt = R.SPEC_BF16 if batch.dtype == "bf16" else R.SPEC_F32
     ws = R.new_workspace(R.spec_workspace_bytes(batch.B, batch.gamma, batch.V, dt), "cuda")
@@ -36,7 +36,7 @@ def run_ex(batch, temps, mode="residual", eps=0.0, early=False, predict=False, d
     pred = R.alloc_predict_outputs(batch.B, batch.gamma, "cuda") if predict else None
     res = R.spec_verify_ex(db.draft, db.target, db.tokens, db.u_accept, db.u_sample, T,
                            in_len=db.in_len, diag=diag, workspace=ws, saguaro=mode == "saguaro",
-                           eps=eps, early=early, pred=pred)
+                           eps=eps, early=early, pred=pred, top_p=top_p)
     out = res[0] if predict else res
     torch.cuda.synchronize()
     assert int(ws[:4].view(torch.int32).item()) == 0, "bounded wait timed out"
@@ -52,11 +52,15 @@ def run_ex(batch, temps, mode="residual", eps=0.0, early=False, predict=False, d
     return host
 
 
-def oracle_per_seq(batch, temps, mode="residual", eps=0.0, early=False):
-    fn = O.verify_early_one if early else O.verify_one
+def oracle_per_seq(batch, temps, mode="residual", eps=0.0, early=False, top_p=1.0):
     d64, t64 = batch.draft64(), batch.target64()
-    return {b: fn(d64[b], t64[b], batch.draft_tokens[b], batch.u_accept[b], batch.u_sample[b],
-                  float(temps[b]), mode, eps, int(batch.in_len[b])) for b in range(batch.B)}
+    if early:
+        return {b: O.verify_early_one(d64[b], t64[b], batch.draft_tokens[b], batch.u_accept[b],
+                                      batch.u_sample[b], float(temps[b]), mode, eps,
+                                      int(batch.in_len[b])) for b in range(batch.B)}
+    return {b: O.verify_one(d64[b], t64[b], batch.draft_tokens[b], batch.u_accept[b],
+                            batch.u_sample[b], float(temps[b]), mode, eps, int(batch.in_len[b]),
+                            top_p=top_p) for b in range(batch.B)}
 
 
 TEMPS = [0.25, 0.7, 1.0, 1.6, 3.0, 0.0, -1.0, np.nan, np.inf, 0.9, 1.2, 0.5]
@@ -110,3 +114,54 @@ def test_equal_temperatures_match_the_scalar_call():
         np.testing.assert_array_equal(a[k], b[k], err_msg=k)
     for k, v in a["diag"].items():
         np.testing.assert_array_equal(v, b["diag"][k], err_msg=k)
+
+
+# --------------------------------------------------------------------------- top-p
+
+@pytest.mark.parametrize("top_p", [0.5, 0.9, 0.99])
+@pytest.mark.parametrize("mode,eps", [("residual", 0.0), ("saguaro", 0.0), ("saguaro", 1e-8)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_top_p(top_p, mode, eps, dtype):
+    batch = random_batch(10, 4, 30000, dtype, 1.0, seed=6300, scale=2.0, sigma=0.4)
+    temps = np.full(batch.B, 1.0, np.float32)
+    gpu = run_ex(batch, 1.0, mode, eps, top_p=top_p)
+    ref = oracle_per_seq(batch, temps, mode, eps, top_p=top_p)
+    rep = H.compare(batch, gpu, ref)
+    H.say(f"[options]   {rep}")
+    rep.check()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_top_p_ties_temperatures_and_prediction(dtype):
+    """Rounded logits (many equal values at the cut), per-sequence
+    temperatures and outcome prediction together."""
+    batch = random_batch(8, 3, 20000, dtype, 1.0, seed=6301, scale=2.0, sigma=0.3)
+    d64 = np.round(batch.draft64(), 1)
+    t64 = np.round(batch.target64(), 1)
+    batch = W.Batch(**{**batch.__dict__, "draft": W.encode(d64, dtype), "target": W.encode(t64, dtype),
+                       "draft_tokens": W.gumbel_argmax(W.decode_f64(W.encode(d64, dtype), dtype)[:, :3],
+                                                       1.0, W.philox(6301, 3))})
+    temps = np.array([0.5, 0.8, 1.0, 1.2, 1.5, 2.0, 0.7, 1.1], np.float32)
+    gpu = run_ex(batch, temps, top_p=0.85, predict=True)
+    ref = oracle_per_seq(batch, temps, top_p=0.85)
+    rep = H.compare(batch, gpu, ref)
+    H.say(f"[options]   {rep}")
+    rep.check()
+    np.testing.assert_array_equal(gpu["cand"], O.predict_outcomes(batch.draft64()))
+
+
+def test_top_p_one_equals_no_cut():
+    batch = workload("B64_g5_V128256_bf16")
+    a = run_ex(batch, float(batch.T), top_p=1.0)
+    b = run_ex(batch, float(batch.T))
+    for k in ("tokens", "accepted", "first_reject", "mask", "out_len"):
+        np.testing.assert_array_equal(a[k], b[k], err_msg=k)
+
+
+def test_top_p_on_the_b256_workload():
+    batch = workload("B256_g8_V152064_bf16")
+    gpu = run_ex(batch, float(batch.T), top_p=0.9)
+    ref = oracle_per_seq(batch, np.full(batch.B, batch.T), top_p=0.9)
+    rep = H.compare(batch, gpu, ref)
+    H.say(f"[options]   {rep}")
+    rep.check()

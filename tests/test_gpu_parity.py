@@ -329,3 +329,17 @@ def test_verify_predict_ties_and_bad_rows(dtype):
                        "draft_tokens": tokens[3:].copy(), "u_accept": batch.u_accept[3:].copy(),
                        "u_sample": batch.u_sample[3:].copy(), "in_len": batch.in_len[3:].copy()})
     _check_verify_predict(small, _verify_predict(small, ws=ws))
+
+
+def test_saguaro_eps_where_the_target_has_zero_probability():
+    """Saguaro with eps > 0 gives a token with q = 0 and p > 0 the weight
+    sqrt(p * eps) ("Speculative Speculative Decoding (Saguaro)", section 3.2
+    code: the clamp applies to every token); half of each target row is -inf."""
+    for dtype in ("bf16", "f32"):
+        batch = random_batch(12, 3, 8192, dtype, 1.0, seed=7100, scale=1.0, sigma=0.5)
+        t64 = batch.target64()
+        t64[:, :, ::2] = -np.inf
+        batch = W.Batch(**{**batch.__dict__, "target": W.encode(t64, dtype)})
+        rep = H.parity(batch, "saguaro", 1e-3)
+        rep.check()
+        assert rep.n_draws > 0

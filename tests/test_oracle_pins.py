@@ -609,6 +609,18 @@ def _nucleus_by_sorting(l, T, top_p):
     return keep, prob[keep].sum()
 
 
+def _nucleus_by_values(l, T, top_p):
+    """The definition: distinct logits from the largest down, adding the mass
+    of each value's tokens, until the mass reaches top_p."""
+    prob, _, _ = O.softmax_rows(l, T)
+    run = 0.0
+    for v in np.unique(l)[::-1]:
+        run += prob[l == v].sum()
+        if run >= top_p:
+            return v, run
+    return np.unique(l)[0], run
+
+
 def test_nucleus_against_sorting():
     rng = np.random.default_rng(41)
     for trial in range(300):
@@ -620,6 +632,8 @@ def test_nucleus_against_sorting():
         keep, m2 = _nucleus_by_sorting(l, T, top_p)
         np.testing.assert_array_equal(l >= L, keep)
         assert abs(mass - m2) < 1e-12
+        v, m3 = _nucleus_by_values(l, T, top_p)
+        assert v == L and abs(mass - m3) < 1e-12
     L, mass, _ = O.nucleus(np.array([1.0, 2.0]), 1.0, 1.0)
     assert L == -np.inf and mass == 1.0
 
