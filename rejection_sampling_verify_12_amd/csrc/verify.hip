@@ -1837,10 +1837,12 @@ __global__ __launch_bounds__(64) void topp_init_kernel(VerifyArgs a) {
 }
 
 // (row, chunk) items: the masses of the chunk's logits whose key matches the
-// selected prefix, by the pass's digit, into the row's histogram.
+// selected prefix, by the pass's digit, into the row's histogram.  Each wave
+// has its own LDS histogram (fewer colliding atomics); a lane sums runs of
+// one digit before adding.  Loads: four units in flight per lane.
 template <int DT, bool VEC>
 __global__ __launch_bounds__(kThreads) void topp_hist_kernel(VerifyArgs a, int pass) {
-  __shared__ double h[kDigits];
+  __shared__ double h[kWaves][kDigits];
   const int R = 2 * a.gamma + 1;
   const int64_t id = blockIdx.x;
   const int64_t row = id / a.nc;
@@ -1851,16 +1853,15 @@ __global__ __launch_bounds__(kThreads) void topp_hist_kernel(VerifyArgs a, int p
   const uint32_t prefix = (uint32_t)uni((int)a.topp[row].prefix);
   constexpr int KB = DT == kBF16 ? 16 : 32;
   const int shift = KB - 8 * (pass + 1);
-  for (int i = threadIdx.x; i < kDigits; i += kThreads) h[i] = 0.0;
+  const int wave = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < kWaves * kDigits; i += kThreads) (&h[0][0])[i] = 0.0;
   __syncthreads();
   const void* rp = row_ptr<DT>(a, b, r);
   const int64_t begin = (int64_t)c * a.chunk;
   const int64_t end = min<int64_t>(begin + a.chunk, a.V);
   int cur = -1;
   double acc = 0.0;
-  for (int64_t j = begin + (int64_t)threadIdx.x * kUnit; j < end; j += kTile) {
-    Raw8<DT, VEC> raw;
-    load_raw<DT, VEC>(rp, j, end, raw);
+  auto take = [&](const Raw8<DT, VEC>& raw, int64_t j) {
     float v[8];
     unpack<DT, VEC>(raw, v);
 #pragma unroll
@@ -1870,57 +1871,118 @@ __global__ __launch_bounds__(kThreads) void topp_hist_kernel(VerifyArgs a, int p
       if (pass > 0 && (key >> (shift + 8)) != prefix) continue;
       const int d = (int)((key >> shift) & 0xFFu);
       const double m = (double)exp2_fast(fmaf(v[e], tc.c_lo, fmaf(v[e], tc.c_hi, -Mf)));
-      if (d != cur) {   // runs of one digit are summed before one atomic add
-        if (cur >= 0) atomicAdd(&h[cur], acc);
+      if (d != cur) {
+        if (cur >= 0) atomicAdd(&h[wave][cur], acc);
         cur = d;
         acc = 0.0;
       }
       acc += m;
     }
+  };
+  constexpr int U = 4;
+  int64_t j = begin + (int64_t)threadIdx.x * kUnit;
+  for (; j + (U - 1) * (int64_t)kTile < end; j += U * (int64_t)kTile) {
+    Raw8<DT, VEC> raw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) load_raw<DT, VEC, true>(rp, j + u * (int64_t)kTile, end, raw[u]);
+#pragma unroll
+    for (int u = 0; u < U; ++u) take(raw[u], j + u * (int64_t)kTile);
   }
-  if (cur >= 0) atomicAdd(&h[cur], acc);
+  for (; j < end; j += kTile) {
+    Raw8<DT, VEC> raw;
+    load_raw<DT, VEC, true>(rp, j, end, raw);
+    take(raw, j);
+  }
+  if (cur >= 0) atomicAdd(&h[wave][cur], acc);
   __syncthreads();
   double* g = a.hist + row * kDigits;
-  for (int i = threadIdx.x; i < kDigits; i += kThreads)
-    if (h[i] != 0.0) atomicAdd(g + i, h[i]);
+  for (int i = threadIdx.x; i < kDigits; i += kThreads) {
+    double t = 0.0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) t += h[w][i];
+    if (t != 0.0) atomicAdd(g + i, t);
+  }
 }
 
-// One thread per row: the digit at which the mass from the top reaches the
-// remaining target; clears the histogram.  After the last pass, the threshold
+// One wave per row: the digit at which the mass from the top reaches the
+// remaining target; clears the histogram.  Lane l holds digits 4l..4l+3 and
+// a suffix sum over the lanes gives the mass above each lane's digits.  If
+// rounding left the target above the row's total, every digit is kept (the
+// lowest digit with mass is selected).  After the last pass, the threshold
 // logit and the nucleus mass.
 template <int DT>
 __global__ __launch_bounds__(64) void topp_select_kernel(VerifyArgs a, int pass, int npass) {
-  const int64_t row = (int64_t)blockIdx.x * 64 + threadIdx.x;
-  if (row >= (int64_t)a.B * (2 * a.gamma + 1)) return;
+  const int64_t row = blockIdx.x;
+  const int lane = threadIdx.x;
   TopPRow t = a.topp[row];
   double* g = a.hist + row * kDigits;
-  double run = 0.0, hsel = 0.0;
-  int sel = -1, low = -1;
-  for (int d = kDigits - 1; d >= 0; --d) {
-    const double m = g[d];
-    if (m > 0.0) low = d;
-    if (sel < 0 && run + m >= t.rem && m > 0.0) {
-      sel = d;
-      hsel = m;
-    } else if (sel < 0) {
-      run += m;
+  double m[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) m[q] = g[4 * lane + q];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) g[4 * lane + q] = 0.0;
+  const double mine = (m[0] + m[1]) + (m[2] + m[3]);
+  double incl = mine;   // inclusive suffix sum over the lanes (higher digits)
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const double x = __shfl_down(incl, o, 64);
+    if (lane + o < 64) incl += x;
+  }
+  const double above_lane = incl - mine;
+  // In this lane, from its highest digit down: the first that reaches the target.
+  int sel = -1;
+  double run = above_lane, hsel = 0.0, before = 0.0;
+#pragma unroll
+  for (int q = 3; q >= 0; --q) {
+    if (sel < 0 && m[q] > 0.0 && run + m[q] >= t.rem) {
+      sel = 4 * lane + q;
+      hsel = m[q];
+      before = run;
+    }
+    if (sel < 0) run += m[q];
+  }
+  // The lowest digit with mass in this lane, for the keep-everything case.
+  int low = -1;
+  double low_h = 0.0, low_before = 0.0;
+  {
+    double r2 = above_lane;
+#pragma unroll
+    for (int q = 3; q >= 0; --q) {
+      if (m[q] > 0.0) {
+        low = 4 * lane + q;
+        low_h = m[q];
+        low_before = r2;
+      }
+      r2 += m[q];
     }
   }
-  if (sel < 0) {   // rounding left the target above the total: keep everything
-    sel = low < 0 ? 0 : low;
-    hsel = low < 0 ? 0.0 : g[sel];
-    run -= hsel;
+  const uint64_t has = __ballot(sel >= 0);
+  const uint64_t haslow = __ballot(low >= 0);
+  int src, s_sel;
+  double s_h, s_before;
+  if (has) {   // the highest digit (lane) that reaches the target
+    src = 63 - __builtin_clzll(has);
+    s_sel = __shfl(sel, src, 64);
+    s_h = __shfl(hsel, src, 64);
+    s_before = __shfl(before, src, 64);
+  } else {     // keep everything down to the lowest digit with mass
+    src = haslow ? __builtin_ctzll(haslow) : 0;
+    s_sel = haslow ? __shfl(low, src, 64) : 0;
+    s_h = haslow ? __shfl(low_h, src, 64) : 0.0;
+    s_before = haslow ? __shfl(low_before, src, 64) : 0.0;
   }
-  for (int d = 0; d < kDigits; ++d) g[d] = 0.0;
-  t.above += run;
-  t.rem -= run;
-  t.prefix = (t.prefix << 8) | (uint32_t)sel;
-  if (pass == npass - 1) {
-    t.L = key_logit<DT>(t.prefix);
-    t.P = (t.above + hsel) / t.Z;
+  if (lane == 0) {
+    t.above += s_before;
+    t.rem -= s_before;
+    t.prefix = (t.prefix << 8) | (uint32_t)s_sel;
+    if (pass == npass - 1) {
+      t.L = key_logit<DT>(t.prefix);
+      t.P = (t.above + s_h) / t.Z;
+    }
+    a.topp[row] = t;
   }
-  a.topp[row] = t;
 }
+
 
 template <int DT>
 __global__ __launch_bounds__(kThreads) void final_kernel(VerifyArgs a) {
@@ -2118,7 +2180,7 @@ static hipError_t launch_kernels_cut(const VerifyArgs& a, hipStream_t st) {
     hipLaunchKernelGGL(topp_init_kernel, dim3(rows), dim3(64), 0, st, a);
     for (int pass = 0; pass < npass; ++pass) {
       hipLaunchKernelGGL((topp_hist_kernel<DT, VEC>), dim3(nstream), dim3(kThreads), 0, st, a, pass);
-      hipLaunchKernelGGL((topp_select_kernel<DT>), dim3((rows + 63) / 64), dim3(64), 0, st, a, pass, npass);
+      hipLaunchKernelGGL((topp_select_kernel<DT>), dim3(rows), dim3(64), 0, st, a, pass, npass);
     }
   }
   if (a.early)   // position-major: the test of (i - 1, b) has a smaller block number than (i, b)'s
