@@ -221,48 +221,61 @@ __global__ __launch_bounds__(64) void top3_merge_kernel(PredictArgs a) {
   if (k == 0) eval_hit(a, b, s_cand);
 }
 
-// One work-group per sequence; wave w ranks positions w, w + 4, ...  The
-// chunk records hold lane leaders (key index = start of the leader's best
-// unit); the row's three best leaders are found first, then lanes 16l..16l+15
-// re-read leader l's units (every kTile-th unit of its chunk) and the wave
-// ranks those elements.
+// One wave per (sequence, position).  The chunk records hold lane leaders
+// (key index = start of the leader's best unit); the row's three best leaders
+// are found first, then lanes 16l..16l+15 re-read leader l's units (every
+// kTile-th unit of its chunk) and the wave ranks those elements.  The wave of
+// the realised position (position 0 for an invalid sequence) also evaluates
+// the hit; its emitted token is loaded while the leaders are re-read.
 template <int DT>
-__global__ __launch_bounds__(kThreads) void top3_lanes_kernel(PredictArgs a) {
-  __shared__ int s_cand[64 * 3];
-  const int b = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+__global__ __launch_bounds__(64) void top3_lanes_kernel(PredictArgs a) {
   const int G1 = a.gamma + 1;
+  const int64_t row = blockIdx.x;   // b * (gamma + 1) + k
+  const int b = (int)(row / G1), k = (int)(row - (int64_t)b * G1);
+  const int lane = threadIdx.x;
   constexpr int kEs = DT == kBF16 ? 2 : 4;
-  for (int k = wave; k < G1; k += kWaves) {
-    const int64_t row = (int64_t)b * G1 + k;
-    const Top3* P = a.part + row * a.nc;
-    uint64_t t[3] = {0, 0, 0};
-    if (lane < 3 * a.nc) t[0] = P[lane / 3].key[lane % 3];
-    const bool nan = __ballot(lane < a.nc && P[lane < a.nc ? lane : 0].nan != 0) != 0;
-    uint64_t lead[3];
-    wave_top3(t, lead);
-    const int l = lane >> 4;
-    const uint64_t mine = l == 0 ? lead[0] : (l == 1 ? lead[1] : (l == 2 ? lead[2] : 0ull));
-    uint64_t e3[3] = {0, 0, 0};
-    if (mine != 0) {
-      const void* rp = static_cast<const char*>(a.draft) + row * (int64_t)a.V * kEs;
-      const int64_t s0 = key_index(mine);
-      const int64_t cb = s0 / a.chunk * a.chunk;
-      const int64_t ce = min<int64_t>(cb + a.chunk, a.V);
-      for (int64_t j = s0 - (s0 - cb) / kTile * kTile + (int64_t)(lane & 15) * kTile; j < ce; j += 16 * kTile)
-        for (int e = 0; e < kUnit && j + e < ce; ++e)
-          insert3(e3, make_key(load_bits<DT>(rp, j + e), j + e));
-    }
-    uint64_t best[3];
-    wave_top3(e3, best);
-    if (lane < 3) {
-      const uint64_t kb = lane == 0 ? best[0] : (lane == 1 ? best[1] : best[2]);
-      const int tok = (nan || kb == 0) ? -1 : key_index(kb);
-      s_cand[k * 3 + lane] = tok;
-      a.cand[row * 3 + lane] = tok;
-    }
+  const bool with_hit = a.accepted && a.out_tokens;
+  const int K = with_hit ? a.accepted[b] : -1;
+  const bool mine_hit = with_hit && (K == k || ((K < 0 || K >= G1) && k == 0));
+  const Top3* P = a.part + row * a.nc;
+  uint64_t t[3] = {0, 0, 0};
+  if (lane < 3 * a.nc) t[0] = P[lane / 3].key[lane % 3];
+  const bool nan = __ballot(lane < a.nc && P[lane < a.nc ? lane : 0].nan != 0) != 0;
+  uint64_t lead[3];
+  wave_top3(t, lead);
+  int y = -1;
+  if (mine_hit && K == k) y = a.out_tokens[row];   // in flight with the re-read below
+  const int l = lane >> 4;
+  const uint64_t mine = l == 0 ? lead[0] : (l == 1 ? lead[1] : (l == 2 ? lead[2] : 0ull));
+  uint64_t e3[3] = {0, 0, 0};
+  if (mine != 0) {
+    const void* rp = static_cast<const char*>(a.draft) + row * (int64_t)a.V * kEs;
+    const int64_t s0 = key_index(mine);
+    const int64_t cb = s0 / a.chunk * a.chunk;
+    const int64_t ce = min<int64_t>(cb + a.chunk, a.V);
+    for (int64_t j = s0 - (s0 - cb) / kTile * kTile + (int64_t)(lane & 15) * kTile; j < ce; j += 16 * kTile)
+      for (int e = 0; e < kUnit && j + e < ce; ++e)
+        insert3(e3, make_key(load_bits<DT>(rp, j + e), j + e));
   }
-  __syncthreads();
-  if (threadIdx.x == 0) eval_hit(a, b, s_cand);
+  uint64_t best[3];
+  wave_top3(e3, best);
+  int tok[3];
+#pragma unroll
+  for (int r = 0; r < 3; ++r) tok[r] = (nan || best[r] == 0) ? -1 : key_index(best[r]);
+  if (lane < 3) a.cand[row * 3 + lane] = lane == 0 ? tok[0] : (lane == 1 ? tok[1] : tok[2]);
+  if (mine_hit && lane == 0) {
+    int h = 0, idx = -1;
+    if (K == k && y >= 0) {
+#pragma unroll
+      for (int r = 2; r >= 0; --r)
+        if (tok[r] == y) {
+          h = 1;
+          idx = 3 * k + r;
+        }
+    }
+    if (a.hit) a.hit[b] = h;
+    if (a.cand_idx) a.cand_idx[b] = idx;
+  }
 }
 
 size_t predict_part_bytes(int B, int gamma, int V) {
@@ -285,10 +298,11 @@ hipError_t predict_launch_rows(const PredictArgs& a, int dtype, bool vec, hipStr
 }
 
 hipError_t predict_launch_leaders(const PredictArgs& a, int dtype, hipStream_t st) {
+  const unsigned rows = (unsigned)((int64_t)a.B * (a.gamma + 1));
   if (dtype == SPEC_BF16)
-    hipLaunchKernelGGL((top3_lanes_kernel<kBF16>), dim3((unsigned)a.B), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((top3_lanes_kernel<kBF16>), dim3(rows), dim3(64), 0, st, a);
   else
-    hipLaunchKernelGGL((top3_lanes_kernel<kF32>), dim3((unsigned)a.B), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((top3_lanes_kernel<kF32>), dim3(rows), dim3(64), 0, st, a);
   return hipGetLastError();
 }
 
