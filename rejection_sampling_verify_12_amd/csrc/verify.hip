@@ -1984,6 +1984,357 @@ __global__ __launch_bounds__(64) void topp_select_kernel(VerifyArgs a, int pass,
 }
 
 
+// Top-p of bfloat16 rows by counting.  A bfloat16 row holds at most 65536
+// distinct values and every logit of one value carries the same mass, so the
+// row's masses in value order follow exactly from how often each value
+// occurs.  One 1024-thread work-group per row:
+//   * counts the row's values by their 16-bit order-preserving keys in LDS,
+//     two 16-bit counters per 32-bit word.  A counter wraps only where one
+//     value occurs 65536 times or more; the counters then sum to less than V,
+//     and the row is counted again with returning atomics that record every
+//     wrap, so only such rows are read twice;
+//   * from the counts, from the top key down: the largest finite value (the
+//     row offset), the row normaliser in fp64, and the nucleus threshold (the
+//     first value at whose end the running mass reaches top_p times the
+//     normaliser; each value is one run of equal logits);
+//   * writes the row's normaliser piece (the whole row in piece 0, -inf in
+//     the others) and its maximum where the stream items would, so a cut
+//     bfloat16 row needs no stream items.
+constexpr int kCountThreads = 1024;
+constexpr int kCountWaves = kCountThreads / 64;
+constexpr int kCountWords = 32768;                                // 128 KB of counters
+constexpr int kKeysPerThread = 2 * kCountWords / kCountThreads;   // 64
+// Wraps in a row of V logits: at most V / 65536 of low counters, plus
+// (V + those) / 65536 of high counters (each low wrap carries one into the
+// high counter of its word): at most 256 up to this row length.  Longer
+// bfloat16 rows take the radix selection.
+constexpr int64_t kCountMaxV = (int64_t)1 << 24;
+constexpr int kCountEvents = 288;
+constexpr uint32_t kKeyNegInf = 0x007Fu, kKeyNegZero = 0x7FFFu, kKeyPosZero = 0x8000u,
+                   kKeyPosInf = 0xFF80u;
+
+struct CountLds {
+  uint32_t cnt[kCountWords];
+  uint32_t ev[kCountEvents];   // keys whose counter wrapped (checked pass)
+  uint32_t nev;
+  uint32_t sum[kCountWaves];
+  int kmax[kCountWaves], flags[kCountWaves];
+  double tot[kCountWaves];
+  int sel;
+  double P;
+};
+
+// The keys of the two bfloat16 logits in w (its halves), in the halves of
+// the result: a negative value's bits inverted, a non-negative value's sign
+// bit set.  -0 takes key 0x7FFF, next below +0's 0x8000; both are the value
+// zero and are merged when the counts are read.
+__device__ __forceinline__ uint32_t bf16_key_pair(uint32_t w) {
+  const uint32_t s = w & 0x80008000u;
+  return w ^ (0x80008000u | (s - (s >> 15)));
+}
+
+__device__ __forceinline__ void count_wrap(CountLds& sh, uint32_t k) {
+  const uint32_t e = __hip_atomic_fetch_add(&sh.nev, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  if (e < (uint32_t)kCountEvents) sh.ev[e] = k;
+}
+
+// Even keys count in the low half of word k / 2, odd keys in the high half.
+// CHECK: the atomic returns the old word, and a counter that was 0xFFFF has
+// wrapped (a low one carrying into the high one, which may wrap in turn).
+template <bool CHECK>
+__device__ __forceinline__ void count_key(CountLds& sh, uint32_t k) {
+  const uint32_t inc = (k & 1u) * 0xFFFFu + 1u;
+  uint32_t* w = sh.cnt + (k >> 1);
+  if constexpr (!CHECK) {
+    __hip_atomic_fetch_add(w, inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  } else {
+    const uint32_t old = __hip_atomic_fetch_add(w, inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    const uint32_t lo = old & 0xFFFFu, hi = old >> 16;
+    if ((k & 1u) ? hi == 0xFFFFu : lo == 0xFFFFu) {
+      count_wrap(sh, k);
+      if (!(k & 1u) && hi == 0xFFFFu) count_wrap(sh, k + 1u);
+    }
+  }
+}
+template <bool CHECK>
+__device__ __forceinline__ void count_pair(CountLds& sh, uint32_t w) {
+  const uint32_t kp = bf16_key_pair(w);
+  count_key<CHECK>(sh, kp & 0xFFFFu);
+  count_key<CHECK>(sh, kp >> 16);
+}
+
+// Every logit of the row, once.  Lane t takes 8-logit units t, t + 1024, ...
+// (eight in flight), then one of the last V mod 8 logits.
+template <bool VEC, bool CHECK>
+__device__ void count_row(const uint16_t* row, int64_t V, CountLds& sh) {
+  const int t = threadIdx.x;
+  const int64_t units = V >> 3;
+  int64_t u = t;
+  if constexpr (VEC) {
+    constexpr int U = 8;
+    constexpr int64_t kBatch = (int64_t)U * kCountThreads;
+    const __amdgpu_buffer_rsrc_t rs = chunk_rsrc(row, (int)(units * 16));
+    const int voff = t * 16;
+    const int64_t nb = units / kBatch;
+    for (int64_t i = 0; i < nb; ++i) {
+      u32x4 w[U];
+#pragma unroll
+      for (int q = 0; q < U; ++q)
+        w[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, (int)((i * kBatch + q * kCountThreads) * 16), 2);
+#pragma unroll
+      for (int q = 0; q < U; ++q) {
+        count_pair<CHECK>(sh, w[q].x);
+        count_pair<CHECK>(sh, w[q].y);
+        count_pair<CHECK>(sh, w[q].z);
+        count_pair<CHECK>(sh, w[q].w);
+      }
+    }
+    for (u = nb * kBatch + t; u < units; u += kCountThreads) {
+      const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, (int)((u - t) * 16), 2);
+      count_pair<CHECK>(sh, w.x);
+      count_pair<CHECK>(sh, w.y);
+      count_pair<CHECK>(sh, w.z);
+      count_pair<CHECK>(sh, w.w);
+    }
+  } else {
+    for (; u < units; u += kCountThreads) {
+#pragma unroll
+      for (int e = 0; e < 8; e += 2)
+        count_pair<CHECK>(sh, (uint32_t)row[u * 8 + e] | ((uint32_t)row[u * 8 + e + 1] << 16));
+    }
+  }
+  if (t < V - units * 8) count_key<CHECK>(sh, bf16_key_pair(row[units * 8 + t]) & 0xFFFFu);
+}
+
+__device__ __forceinline__ bool key_finite(uint32_t k) { return k > kKeyNegInf && k < kKeyPosInf; }
+
+// Thread t holds counter words 32t .. 32t + 31 (keys 64t .. 64t + 63) in
+// registers, read as 16-byte groups in a rotated order - x[q] is group
+// (q + t) mod 8 - so that the lanes of a wave read from different banks.
+__device__ __forceinline__ void read_words(const CountLds& sh, uint4 (&x)[8]) {
+  const int t = threadIdx.x;
+  const uint4* c4 = reinterpret_cast<const uint4*>(sh.cnt) + t * 8;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) x[q] = c4[(q + t) & 7];
+}
+// The key of half h of word e of group x[q] of thread t.
+// (Recomputed at each use: the opaque step keeps the compiler from holding
+// all 64 keys in registers between the passes.)
+__device__ __forceinline__ uint32_t held_key(int q, int e, int h) {
+  uint32_t w = 32u * threadIdx.x + 4u * ((q + threadIdx.x) & 7u);
+  asm volatile("" : "+v"(w));
+  return 2u * (w + (uint32_t)e) + (uint32_t)h;
+}
+__device__ __forceinline__ uint32_t word_of(const uint4& x, int e) {
+  return e == 0 ? x.x : e == 1 ? x.y : e == 2 ? x.z : x.w;
+}
+// The count of key k from its 16-bit counter h and the recorded wraps.
+__device__ __forceinline__ uint32_t wrap_fix(const CountLds& sh, int nev, uint32_t k, uint32_t h) {
+  for (int e = 0; e < nev; ++e) {
+    const uint32_t x = sh.ev[e];
+    if (x == k) h += 65536u;
+    else if ((k & 1u) && x == k - 1u) h -= 1u;
+  }
+  return h;
+}
+
+// Flags of a key outside the finite range: 1 for a NaN, 2 for +inf, 0 for -inf.
+__device__ __forceinline__ int nonfinite_flag(uint32_t k) {
+  return k == kKeyNegInf ? 0 : (k == kKeyPosInf ? 2 : 1);
+}
+
+// The row's statistics: the sum of the counts, the largest finite key with
+// a count, and flags (1: a NaN, 2: +inf).  nev = 0: from the held 16-bit
+// counters; otherwise every key's count from LDS and the recorded wraps.
+// The two keys of a counter word are both finite or both not.  Every thread
+// returns the row's values.
+__device__ __forceinline__ void count_stats(CountLds& sh, const uint4 (&x)[8], int nev, uint32_t& sum,
+                                            int& kmax, int& flags) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  sum = 0;
+  kmax = -1;
+  flags = 0;
+  if (nev == 0) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t w = word_of(x[q], e);
+        sum += (w & 0xFFFFu) + (w >> 16);
+        if (w != 0u) {
+          const uint32_t k = held_key(q, e, 0);
+          if (key_finite(k)) {
+            kmax = max(kmax, (int)k + ((w >> 16) ? 1 : 0));
+          } else {   // NaN, -inf or +inf keys: each half on its own
+            if (w & 0xFFFFu) flags |= nonfinite_flag(k);
+            if (w >> 16) flags |= nonfinite_flag(k + 1u);
+          }
+        }
+      }
+  } else {
+    for (uint32_t k = threadIdx.x * kKeysPerThread; k < (threadIdx.x + 1u) * kKeysPerThread; ++k) {
+      const uint32_t n = wrap_fix(sh, nev, k, (sh.cnt[k >> 1] >> (16 * (k & 1u))) & 0xFFFFu);
+      sum += n;
+      if (n == 0u) continue;
+      if (key_finite(k)) kmax = max(kmax, (int)k);
+      else flags |= nonfinite_flag(k);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    sum += __shfl_xor(sum, o, 64);
+    kmax = max(kmax, __shfl_xor(kmax, o, 64));
+    flags |= __shfl_xor(flags, o, 64);
+  }
+  if (lane == 0) {
+    sh.sum[wave] = sum;
+    sh.kmax[wave] = kmax;
+    sh.flags[wave] = flags;
+  }
+  __syncthreads();
+  sum = 0;
+  for (int i = 0; i < kCountWaves; ++i) {
+    sum += sh.sum[i];
+    kmax = max(kmax, sh.kmax[i]);
+    flags |= sh.flags[i];
+  }
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(kCountThreads) void topp_count_kernel(VerifyArgs a) {
+  __shared__ CountLds sh;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int R = 2 * a.gamma + 1;
+  const int64_t row = blockIdx.x;
+  const int b = (int)(row / R), r = (int)(row - (int64_t)b * R);
+  const uint16_t* rp = static_cast<const uint16_t*>(row_ptr<kBF16>(a, b, r));
+  const TCoef tc = temp_coef(a, b);
+
+  uint4* c4 = reinterpret_cast<uint4*>(sh.cnt);
+  for (int i = t; i < kCountWords / 4; i += kCountThreads) c4[i] = make_uint4(0u, 0u, 0u, 0u);
+  if (t == 0) sh.nev = 0u;
+  __syncthreads();
+  count_row<VEC, false>(rp, a.V, sh);
+  __syncthreads();
+  uint4 x[8];
+  read_words(sh, x);
+  uint32_t sum;
+  int kmax, flags, nev = 0;
+  count_stats(sh, x, 0, sum, kmax, flags);
+  if ((int64_t)sum != a.V) {   // a counter wrapped: count again, recording the wraps
+    __syncthreads();           // every thread is done with the counters
+    for (int i = t; i < kCountWords / 4; i += kCountThreads) c4[i] = make_uint4(0u, 0u, 0u, 0u);
+    __syncthreads();
+    count_row<VEC, true>(rp, a.V, sh);
+    __syncthreads();
+    nev = (int)min(sh.nev, (uint32_t)kCountEvents);
+    read_words(sh, x);
+    count_stats(sh, x, nev, sum, kmax, flags);
+  }
+
+  // The masses count * 2^(l c_T - mref) in fp64; -0 counts with +0.
+  const bool bad = flags != 0 || kmax < 0;
+  const float vmax = kmax >= 0 ? key_logit<kBF16>((uint32_t)kmax) : -INFINITY;
+  const float mref = bad ? 0.f : ceilf(fminf(vmax * tc.c_hi, 1.0e30f));
+  const uint32_t nzero = wrap_fix(sh, nev, kKeyNegZero, sh.cnt[kKeyNegZero >> 1] >> 16);
+  auto mass = [&](uint32_t k, uint32_t n) -> double {
+    if (k == kKeyNegZero) n = 0u;
+    if (k == kKeyPosZero) n += nzero;
+    if (n == 0u || !key_finite(k)) return 0.0;
+    const float v = key_logit<kBF16>(k);
+    return (double)n * (double)exp2_fast(fmaf(v, tc.c_lo, fmaf(v, tc.c_hi, -mref)));
+  };
+  double s = 0.0;
+  if (!bad && nev == 0) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        // One word at a time (the opaque step orders the words): computing
+        // all 64 terms ahead of the additions would not fit the registers.
+        uint32_t w = word_of(x[q], e);
+        asm volatile("" : "+v"(w), "+v"(s));
+        s += mass(held_key(q, e, 0), w & 0xFFFFu) + mass(held_key(q, e, 1), w >> 16);
+      }
+  } else if (!bad) {   // wrapped counters: each key's count from LDS and the wraps
+    for (uint32_t k = t * kKeysPerThread; k < (t + 1u) * kKeysPerThread; ++k)
+      s += mass(k, wrap_fix(sh, nev, k, (sh.cnt[k >> 1] >> (16 * (k & 1u))) & 0xFFFFu));
+  }
+  // Suffix sums over the threads (higher threads hold higher keys).  A
+  // thread's `above` is the next thread's `incl`, the same value, so the
+  // intervals (above, incl] tile (0, Z] exactly.
+  double incl = s;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const double y = __shfl_down(incl, o, 64);
+    if (lane + o < 64) incl += y;
+  }
+  double above = __shfl_down(incl, 1, 64);
+  if (lane == 63) above = 0.0;
+  if (lane == 0) sh.tot[wave] = incl;
+  if (t == 0) sh.sel = -1;
+  __syncthreads();
+  double off = 0.0;   // the waves above this one, summed from the top
+  for (int i = kCountWaves - 1; i > wave; --i) off = off + sh.tot[i];
+  double Z = off;
+  for (int i = wave; i >= 0; --i) Z = Z + sh.tot[i];
+  incl = incl + off;
+  above = above + off;
+  const double tgt = (double)a.top_p * Z;
+  // The wave whose thread c holds the threshold: lane l takes key 64c + l,
+  // a suffix sum over the lanes gives the mass of the keys >= each, and the
+  // highest key with mass whose sum reaches the target ends the nucleus
+  // (rounding aside: else the lowest key with mass).
+  const uint64_t cross = __ballot(!bad && above < tgt && tgt <= incl);
+  if (cross) {
+    const int c = __builtin_ctzll(cross);
+    const double ab = __shfl(above, c, 64);
+    const uint32_t k = (uint32_t)(wave * 64 + c) * kKeysPerThread + lane;
+    const double m = mass(k, wrap_fix(sh, nev, k, (sh.cnt[k >> 1] >> (16 * (k & 1u))) & 0xFFFFu));
+    double run = m;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const double y = __shfl_down(run, o, 64);
+      if (lane + o < 64) run += y;
+    }
+    run += ab;
+    const uint64_t hit = __ballot(m != 0.0 && run >= tgt);
+    const uint64_t has = __ballot(m != 0.0);
+    const int src = hit ? 63 - __builtin_clzll(hit) : __builtin_ctzll(has);
+    if (lane == src) {
+      sh.sel = (int)k;
+      sh.P = run / Z;
+    }
+  }
+  __syncthreads();
+
+  const int64_t p0 = row * a.nc;
+  for (int i = t; i < a.nc; i += kCountThreads) {
+    double v = -INFINITY;
+    float mr = -INFINITY;
+    if (i == 0) {
+      if (flags & 1) v = NAN;
+      else if (flags & 2) v = INFINITY;
+      else if (kmax >= 0) v = (double)mref + log2(Z);
+      mr = (flags & 2) ? INFINITY : vmax;
+    }
+    slot_put32(a.mraw + p0 + i, mr);
+    slot_put(a.part + p0 + i, v);
+  }
+  if (t == 0) {
+    TopPRow tp;
+    tp.M = mref;
+    tp.Z = Z;
+    tp.rem = 0.0;
+    tp.above = 0.0;
+    const bool cut = !bad && sh.sel >= 0;
+    tp.P = cut ? sh.P : 1.0;
+    tp.prefix = cut ? (uint32_t)sh.sel : 0u;
+    tp.L = cut ? key_logit<kBF16>((uint32_t)sh.sel) : -INFINITY;
+    a.topp[row] = tp;
+  }
+}
+
 template <int DT>
 __global__ __launch_bounds__(kThreads) void final_kernel(VerifyArgs a) {
   __shared__ FinalLds sh;
@@ -2173,14 +2524,19 @@ static hipError_t launch_kernels_cut(const VerifyArgs& a, hipStream_t st) {
   const bool eps_mode = a.saguaro && a.eps > 0.f;
   const unsigned nstream = (unsigned)((int64_t)a.B * R * a.nc);
   const unsigned nsample = (unsigned)((int64_t)a.B * a.nt);
-  hipLaunchKernelGGL((stream_kernel<DT, VEC, SV_STREAM_UNROLL>), dim3(nstream), dim3(kThreads), 0, st, a);
-  if constexpr (CUT) {   // the nucleus of every row, then the rule on the cut rows
-    const unsigned rows = (unsigned)((int64_t)a.B * R);
-    constexpr int npass = DT == kBF16 ? 2 : 4;
-    hipLaunchKernelGGL(topp_init_kernel, dim3(rows), dim3(64), 0, st, a);
-    for (int pass = 0; pass < npass; ++pass) {
-      hipLaunchKernelGGL((topp_hist_kernel<DT, VEC>), dim3(nstream), dim3(kThreads), 0, st, a, pass);
-      hipLaunchKernelGGL((topp_select_kernel<DT>), dim3(rows), dim3(64), 0, st, a, pass, npass);
+  const unsigned rows = (unsigned)((int64_t)a.B * R);
+  if (CUT && DT == kBF16 && a.V <= kCountMaxV) {
+    // Counting gives each row's nucleus and its normaliser piece in one read.
+    hipLaunchKernelGGL((topp_count_kernel<VEC>), dim3(rows), dim3(kCountThreads), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((stream_kernel<DT, VEC, SV_STREAM_UNROLL>), dim3(nstream), dim3(kThreads), 0, st, a);
+    if constexpr (CUT) {   // the nucleus of every row by radix selection
+      constexpr int npass = DT == kBF16 ? 2 : 4;
+      hipLaunchKernelGGL(topp_init_kernel, dim3(rows), dim3(64), 0, st, a);
+      for (int pass = 0; pass < npass; ++pass) {
+        hipLaunchKernelGGL((topp_hist_kernel<DT, VEC>), dim3(nstream), dim3(kThreads), 0, st, a, pass);
+        hipLaunchKernelGGL((topp_select_kernel<DT>), dim3(rows), dim3(64), 0, st, a, pass, npass);
+      }
     }
   }
   if (a.early)   // position-major: the test of (i - 1, b) has a smaller block number than (i, b)'s

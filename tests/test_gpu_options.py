@@ -165,3 +165,49 @@ def test_top_p_on_the_b256_workload():
     rep = H.compare(batch, gpu, ref)
     H.say(f"[options]   {rep}")
     rep.check()
+
+
+def counted_rows_batch(V, seed):
+    """bfloat16 rows for the counting top-p path: values repeated 65536 times
+    or more (16-bit counters wrap), constant rows, +0 and -0 at the cut, a
+    near one-hot row, scattered -inf, and invalid rows (NaN, +inf, all -inf)."""
+    B, g = 10, 3
+    base = random_batch(B, g, V, "bf16", 1.0, seed=seed, scale=2.0, sigma=0.4)
+    d64, t64 = base.draft64().copy(), base.target64().copy()
+    rng = W.philox(seed, 11)
+    heavy = rng.permutation(V)[:66000]
+    d64[0, :, heavy] = -3.0                  # one value 66000 times in every row
+    t64[0, :, heavy[:65536]] = 0.5           # exactly 65536 times
+    d64[1], t64[1] = 1.5, 1.5                # constant rows: every token ties
+    zeros = rng.permutation(V)[:V // 2]
+    for r in range(g + 1):                   # half the row is zero, of either sign
+        d64[2, r, zeros] = np.where(np.arange(zeros.size) % 2 == 0, 0.0, -0.0)
+        t64[2, r, zeros] = np.where(np.arange(zeros.size) % 3 == 0, -0.0, 0.0)
+    t64[6, :, 5] = 40.0                      # near one-hot target rows
+    d64[7, :, rng.permutation(V)[:V // 3]] = -np.inf
+    d = W.encode(d64, "bf16")
+    t = W.encode(t64, "bf16")
+    x = W.gumbel_argmax(W.decode_f64(d, "bf16")[:, :g], 1.0, W.philox(seed, 12))
+    d[3, 1, 77] = np.uint16(0x7FC0)          # NaN in draft row 1
+    t[4, 0, V - 1] = np.uint16(0x7F80)       # +inf in target row 0
+    t[5, 2, :] = np.uint16(0xFF80)           # target row 2 all -inf
+    t[8, 1, 3] = np.uint16(0xFFC1)           # a negative NaN (key below -inf)
+    t[9, 1, :100] = np.uint16(0xFF80)        # -inf, and a NaN whose key shares its counter word
+    t[9, 1, 100] = np.uint16(0xFF81)
+    return W.Batch(**{**base.__dict__, "draft": d, "target": t, "draft_tokens": x,
+                      "name": f"counted_V{V}"})
+
+
+@pytest.mark.parametrize("V", [70000, 70001])   # aligned and unaligned rows
+@pytest.mark.parametrize("top_p", [0.3, 0.95])
+@pytest.mark.parametrize("mode,eps", [("residual", 0.0), ("saguaro", 1e-8)])
+def test_top_p_counted_rows(V, top_p, mode, eps):
+    batch = counted_rows_batch(V, seed=6400 + V % 2)
+    d = batch.draft.view(np.uint16)
+    assert (d[2] == 0x8000).any() and (d[2] == 0).any()
+    gpu = run_ex(batch, 1.0, mode, eps, top_p=top_p)
+    ref = oracle_per_seq(batch, np.full(batch.B, 1.0), mode, eps, top_p=top_p)
+    assert [ref[b].valid for b in range(batch.B)] == [True] * 3 + [False] * 3 + [True] * 2 + [False] * 2
+    rep = H.compare(batch, gpu, ref)
+    H.say(f"[options]   {rep}")
+    rep.check()
