@@ -1989,10 +1989,13 @@ __global__ __launch_bounds__(64) void topp_select_kernel(VerifyArgs a, int pass,
 // row's masses in value order follow exactly from how often each value
 // occurs.  One 1024-thread work-group per row:
 //   * counts the row's values by their 16-bit order-preserving keys in LDS,
-//     two 16-bit counters per 32-bit word.  A counter wraps only where one
-//     value occurs 65536 times or more; the counters then sum to less than V,
-//     and the row is counted again with returning atomics that record every
-//     wrap, so only such rows are read twice;
+//     two 16-bit counters per 32-bit word: word w counts key w (a negative
+//     value) in its low half and key w + 32768 (a non-negative one) in its
+//     high half, so neighbouring values, which a row's logits crowd, fall in
+//     different words.  A counter wraps only where one value occurs 65536
+//     times or more; the counters then sum to less than V, and the row is
+//     counted again with returning atomics that record every wrap, so only
+//     such rows are read twice;
 //   * from the counts, from the top key down: the largest finite value (the
 //     row offset), the row normaliser in fp64, and the nucleus threshold (the
 //     first value at whose end the running mass reaches top_p times the
@@ -2002,8 +2005,8 @@ __global__ __launch_bounds__(64) void topp_select_kernel(VerifyArgs a, int pass,
 //     bfloat16 row needs no stream items.
 constexpr int kCountThreads = 1024;
 constexpr int kCountWaves = kCountThreads / 64;
-constexpr int kCountWords = 32768;                                // 128 KB of counters
-constexpr int kKeysPerThread = 2 * kCountWords / kCountThreads;   // 64
+constexpr int kCountWords = 32768;                                     // 128 KB of counters
+constexpr int kWordsPerThread = kCountWords / kCountThreads;           // 32
 // Wraps in a row of V logits: at most V / 65536 of low counters, plus
 // (V + those) / 65536 of high counters (each low wrap carries one into the
 // high counter of its word): at most 256 up to this row length.  Longer
@@ -2019,7 +2022,7 @@ struct CountLds {
   uint32_t nev;
   uint32_t sum[kCountWaves];
   int kmax[kCountWaves], flags[kCountWaves];
-  double tot[kCountWaves];
+  double tot[2][kCountWaves];
   int sel;
   double P;
 };
@@ -2038,21 +2041,20 @@ __device__ __forceinline__ void count_wrap(CountLds& sh, uint32_t k) {
   if (e < (uint32_t)kCountEvents) sh.ev[e] = k;
 }
 
-// Even keys count in the low half of word k / 2, odd keys in the high half.
 // CHECK: the atomic returns the old word, and a counter that was 0xFFFF has
 // wrapped (a low one carrying into the high one, which may wrap in turn).
 template <bool CHECK>
 __device__ __forceinline__ void count_key(CountLds& sh, uint32_t k) {
-  const uint32_t inc = (k & 1u) * 0xFFFFu + 1u;
-  uint32_t* w = sh.cnt + (k >> 1);
+  const uint32_t inc = (k >> 15) * 0xFFFFu + 1u;
+  uint32_t* w = sh.cnt + (k & 0x7FFFu);
   if constexpr (!CHECK) {
     __hip_atomic_fetch_add(w, inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   } else {
     const uint32_t old = __hip_atomic_fetch_add(w, inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     const uint32_t lo = old & 0xFFFFu, hi = old >> 16;
-    if ((k & 1u) ? hi == 0xFFFFu : lo == 0xFFFFu) {
+    if ((k >> 15) ? hi == 0xFFFFu : lo == 0xFFFFu) {
       count_wrap(sh, k);
-      if (!(k & 1u) && hi == 0xFFFFu) count_wrap(sh, k + 1u);
+      if (!(k >> 15) && hi == 0xFFFFu) count_wrap(sh, k + 32768u);
     }
   }
 }
@@ -2064,14 +2066,15 @@ __device__ __forceinline__ void count_pair(CountLds& sh, uint32_t w) {
 }
 
 // Every logit of the row, once.  Lane t takes 8-logit units t, t + 1024, ...
-// (eight in flight), then one of the last V mod 8 logits.
+// (eight in flight; one in the rarely run checked pass, whose code stays
+// small), then one of the last V mod 8 logits.
 template <bool VEC, bool CHECK>
 __device__ void count_row(const uint16_t* row, int64_t V, CountLds& sh) {
   const int t = threadIdx.x;
   const int64_t units = V >> 3;
   int64_t u = t;
   if constexpr (VEC) {
-    constexpr int U = 8;
+    constexpr int U = CHECK ? 1 : 8;
     constexpr int64_t kBatch = (int64_t)U * kCountThreads;
     const __amdgpu_buffer_rsrc_t rs = chunk_rsrc(row, (int)(units * 16));
     const int voff = t * 16;
@@ -2107,99 +2110,40 @@ __device__ void count_row(const uint16_t* row, int64_t V, CountLds& sh) {
 }
 
 __device__ __forceinline__ bool key_finite(uint32_t k) { return k > kKeyNegInf && k < kKeyPosInf; }
-
-// Thread t holds counter words 32t .. 32t + 31 (keys 64t .. 64t + 63) in
-// registers, read as 16-byte groups in a rotated order - x[q] is group
-// (q + t) mod 8 - so that the lanes of a wave read from different banks.
-__device__ __forceinline__ void read_words(const CountLds& sh, uint4 (&x)[8]) {
-  const int t = threadIdx.x;
-  const uint4* c4 = reinterpret_cast<const uint4*>(sh.cnt) + t * 8;
-#pragma unroll
-  for (int q = 0; q < 8; ++q) x[q] = c4[(q + t) & 7];
-}
-// The key of half h of word e of group x[q] of thread t.
-// (Recomputed at each use: the opaque step keeps the compiler from holding
-// all 64 keys in registers between the passes.)
-__device__ __forceinline__ uint32_t held_key(int q, int e, int h) {
-  uint32_t w = 32u * threadIdx.x + 4u * ((q + threadIdx.x) & 7u);
-  asm volatile("" : "+v"(w));
-  return 2u * (w + (uint32_t)e) + (uint32_t)h;
-}
-__device__ __forceinline__ uint32_t word_of(const uint4& x, int e) {
-  return e == 0 ? x.x : e == 1 ? x.y : e == 2 ? x.z : x.w;
-}
-// The count of key k from its 16-bit counter h and the recorded wraps.
-__device__ __forceinline__ uint32_t wrap_fix(const CountLds& sh, int nev, uint32_t k, uint32_t h) {
-  for (int e = 0; e < nev; ++e) {
-    const uint32_t x = sh.ev[e];
-    if (x == k) h += 65536u;
-    else if ((k & 1u) && x == k - 1u) h -= 1u;
-  }
-  return h;
-}
-
 // Flags of a key outside the finite range: 1 for a NaN, 2 for +inf, 0 for -inf.
 __device__ __forceinline__ int nonfinite_flag(uint32_t k) {
   return k == kKeyNegInf ? 0 : (k == kKeyPosInf ? 2 : 1);
 }
 
-// The row's statistics: the sum of the counts, the largest finite key with
-// a count, and flags (1: a NaN, 2: +inf).  nev = 0: from the held 16-bit
-// counters; otherwise every key's count from LDS and the recorded wraps.
-// The two keys of a counter word are both finite or both not.  Every thread
-// returns the row's values.
-__device__ __forceinline__ void count_stats(CountLds& sh, const uint4 (&x)[8], int nev, uint32_t& sum,
-                                            int& kmax, int& flags) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  sum = 0;
-  kmax = -1;
-  flags = 0;
-  if (nev == 0) {
-#pragma unroll
-    for (int q = 0; q < 8; ++q)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t w = word_of(x[q], e);
-        sum += (w & 0xFFFFu) + (w >> 16);
-        if (w != 0u) {
-          const uint32_t k = held_key(q, e, 0);
-          if (key_finite(k)) {
-            kmax = max(kmax, (int)k + ((w >> 16) ? 1 : 0));
-          } else {   // NaN, -inf or +inf keys: each half on its own
-            if (w & 0xFFFFu) flags |= nonfinite_flag(k);
-            if (w >> 16) flags |= nonfinite_flag(k + 1u);
-          }
-        }
-      }
-  } else {
-    for (uint32_t k = threadIdx.x * kKeysPerThread; k < (threadIdx.x + 1u) * kKeysPerThread; ++k) {
-      const uint32_t n = wrap_fix(sh, nev, k, (sh.cnt[k >> 1] >> (16 * (k & 1u))) & 0xFFFFu);
-      sum += n;
-      if (n == 0u) continue;
-      if (key_finite(k)) kmax = max(kmax, (int)k);
-      else flags |= nonfinite_flag(k);
-    }
+// The count of key k from its 16-bit counter and the recorded wraps: 65536
+// more per wrap of k, one less per carry into k (a wrap of the low counter
+// of k's word, when k is the high one).
+__device__ __forceinline__ uint32_t key_count(const CountLds& sh, int nev, uint32_t k) {
+  uint32_t h = (sh.cnt[k & 0x7FFFu] >> (16 * (k >> 15))) & 0xFFFFu;
+  for (int e = 0; e < nev; ++e) {
+    const uint32_t x = sh.ev[e];
+    if (x == k) h += 65536u;
+    else if ((k >> 15) && x == k - 32768u) h -= 1u;
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    sum += __shfl_xor(sum, o, 64);
-    kmax = max(kmax, __shfl_xor(kmax, o, 64));
-    flags |= __shfl_xor(flags, o, 64);
-  }
-  if (lane == 0) {
-    sh.sum[wave] = sum;
-    sh.kmax[wave] = kmax;
-    sh.flags[wave] = flags;
-  }
-  __syncthreads();
-  sum = 0;
-  for (int i = 0; i < kCountWaves; ++i) {
-    sum += sh.sum[i];
-    kmax = max(kmax, sh.kmax[i]);
-    flags |= sh.flags[i];
-  }
+  return h;
 }
 
+// Inclusive suffix sum over the lanes of a wave (lane 63 first).
+template <typename F>
+__device__ __forceinline__ F wave_suffix_sum(F v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const F y = __shfl_down(v, o, 64);
+    if (lane + o < 64) v += y;
+  }
+  return v;
+}
+
+// After counting, wave w holds words 2048w + 64j + lane (j = 0..31) in
+// registers: consecutive words in consecutive lanes, so a band of crowded
+// values spreads over the lanes.  From the top key down the order is: the
+// high halves (non-negative values) of waves 15..0, then the low halves of
+// waves 15..0; within a wave, rows j = 31..0, lanes 63..0.
 template <bool VEC>
 __global__ __launch_bounds__(kCountThreads) void topp_count_kernel(VerifyArgs a) {
   __shared__ CountLds sh;
@@ -2216,90 +2160,176 @@ __global__ __launch_bounds__(kCountThreads) void topp_count_kernel(VerifyArgs a)
   __syncthreads();
   count_row<VEC, false>(rp, a.V, sh);
   __syncthreads();
-  uint4 x[8];
-  read_words(sh, x);
-  uint32_t sum;
-  int kmax, flags, nev = 0;
-  count_stats(sh, x, 0, sum, kmax, flags);
-  if ((int64_t)sum != a.V) {   // a counter wrapped: count again, recording the wraps
-    __syncthreads();           // every thread is done with the counters
-    for (int i = t; i < kCountWords / 4; i += kCountThreads) c4[i] = make_uint4(0u, 0u, 0u, 0u);
+
+  const uint32_t wbase = 2048u * (uint32_t)wave + (uint32_t)lane;   // word of row j: wbase + 64 j
+  uint32_t cw[32];
+#pragma unroll
+  for (int j = 0; j < 32; ++j) cw[j] = sh.cnt[wbase + 64u * j];
+  int nev = 0;
+  {   // the 16-bit counters sum to V unless one wrapped: then count again, recording the wraps
+    uint32_t sum = 0;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) sum += (cw[j] & 0xFFFFu) + (cw[j] >> 16);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 64);
+    if (lane == 0) sh.sum[wave] = sum;
     __syncthreads();
-    count_row<VEC, true>(rp, a.V, sh);
-    __syncthreads();
-    nev = (int)min(sh.nev, (uint32_t)kCountEvents);
-    read_words(sh, x);
-    count_stats(sh, x, nev, sum, kmax, flags);
+    sum = 0;
+    for (int i = 0; i < kCountWaves; ++i) sum += sh.sum[i];
+    if ((int64_t)sum != a.V) {
+      __syncthreads();   // every thread is done with the counters
+      for (int i = t; i < kCountWords / 4; i += kCountThreads) c4[i] = make_uint4(0u, 0u, 0u, 0u);
+      __syncthreads();
+      count_row<VEC, true>(rp, a.V, sh);
+      __syncthreads();
+      nev = (int)min(sh.nev, (uint32_t)kCountEvents);
+#pragma unroll
+      for (int j = 0; j < 32; ++j) cw[j] = sh.cnt[wbase + 64u * j];
+    }
+  }
+  // The count of key half h of row j (with the recorded wraps, if any); -0
+  // counts with +0 (key 0x8000, the high half of word 0).
+  const uint32_t nzero = key_count(sh, nev, kKeyNegZero);
+  auto count_at = [&](int j, int h) -> uint32_t {
+    const uint32_t k = wbase + 64u * j + 32768u * h;
+    uint32_t n = nev ? key_count(sh, nev, k) : ((cw[j] >> (16 * h)) & 0xFFFFu);
+    return k == kKeyNegZero ? 0u : (k == kKeyPosZero ? n + nzero : n);
+  };
+
+  // The largest finite key with a count, and flags (1: a NaN, 2: +inf).
+  // Keys outside the finite range: the low halves of words 0..127 (wave 0,
+  // rows 0 and 1) and the high halves of words 32640..32767 (wave 15, rows
+  // 30 and 31).
+  int kmax = -1, flags = 0;
+  auto take = [&](uint32_t k, uint32_t n) {
+    const bool fin = key_finite(k);
+    kmax = (n != 0u && fin) ? max(kmax, (int)k) : kmax;
+    flags |= (n != 0u && !fin) ? nonfinite_flag(k) : 0;
+  };
+  if (nev == 0) {
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      uint32_t w = cw[j];
+      asm volatile("" : "+v"(w), "+v"(kmax), "+v"(flags));
+      const uint32_t k = wbase + 64u * j;
+      take(k, k == kKeyNegZero ? 0u : (w & 0xFFFFu));
+      take(k + 32768u, k == 0u ? (w >> 16) + nzero : (w >> 16));
+    }
+  } else {
+    for (uint32_t j = 0; j < 32u; ++j)
+      for (uint32_t h = 0; h < 2u; ++h) {
+        const uint32_t k = wbase + 64u * j + 32768u * h;
+        const uint32_t n = key_count(sh, nev, k);
+        take(k, k == kKeyNegZero ? 0u : (k == kKeyPosZero ? n + nzero : n));
+      }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    kmax = max(kmax, __shfl_xor(kmax, o, 64));
+    flags |= __shfl_xor(flags, o, 64);
+  }
+  if (lane == 0) {
+    sh.kmax[wave] = kmax;
+    sh.flags[wave] = flags;
+  }
+  __syncthreads();
+  for (int i = 0; i < kCountWaves; ++i) {
+    kmax = max(kmax, sh.kmax[i]);
+    flags |= sh.flags[i];
   }
 
-  // The masses count * 2^(l c_T - mref) in fp64; -0 counts with +0.
+  // Masses count * 2^(l c_T - mref) (0 for no count or a key outside the
+  // finite range): each wave's sums over its high and low halves, in fp64.
   const bool bad = flags != 0 || kmax < 0;
   const float vmax = kmax >= 0 ? key_logit<kBF16>((uint32_t)kmax) : -INFINITY;
   const float mref = bad ? 0.f : ceilf(fminf(vmax * tc.c_hi, 1.0e30f));
-  const uint32_t nzero = wrap_fix(sh, nev, kKeyNegZero, sh.cnt[kKeyNegZero >> 1] >> 16);
-  auto mass = [&](uint32_t k, uint32_t n) -> double {
-    if (k == kKeyNegZero) n = 0u;
-    if (k == kKeyPosZero) n += nzero;
-    if (n == 0u || !key_finite(k)) return 0.0;
+  auto mass = [&](uint32_t k, uint32_t n) -> float {
     const float v = key_logit<kBF16>(k);
-    return (double)n * (double)exp2_fast(fmaf(v, tc.c_lo, fmaf(v, tc.c_hi, -mref)));
+    const float m = (float)n * exp2_fast(fmaf(v, tc.c_lo, fmaf(v, tc.c_hi, -mref)));
+    return (n != 0u && key_finite(k)) ? m : 0.f;
   };
-  double s = 0.0;
-  if (!bad && nev == 0) {
+  double cs[2] = {0.0, 0.0};
+  if (!bad) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
+    for (int j = 0; j < 32; ++j) {
+      // One row at a time (the opaque step orders them): computing every
+      // term ahead of the additions would not fit the registers.
+      uint32_t w = cw[j];
+      asm volatile("" : "+v"(w), "+v"(cs[0]), "+v"(cs[1]));
+      if (w != 0u || nev != 0 || (t == 0 && j == 0)) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        // One word at a time (the opaque step orders the words): computing
-        // all 64 terms ahead of the additions would not fit the registers.
-        uint32_t w = word_of(x[q], e);
-        asm volatile("" : "+v"(w), "+v"(s));
-        s += mass(held_key(q, e, 0), w & 0xFFFFu) + mass(held_key(q, e, 1), w >> 16);
+        for (int h = 0; h < 2; ++h) cs[h] += (double)mass(wbase + 64u * j + 32768u * h, count_at(j, h));
       }
-  } else if (!bad) {   // wrapped counters: each key's count from LDS and the wraps
-    for (uint32_t k = t * kKeysPerThread; k < (t + 1u) * kKeysPerThread; ++k)
-      s += mass(k, wrap_fix(sh, nev, k, (sh.cnt[k >> 1] >> (16 * (k & 1u))) & 0xFFFFu));
+    }
   }
-  // Suffix sums over the threads (higher threads hold higher keys).  A
-  // thread's `above` is the next thread's `incl`, the same value, so the
-  // intervals (above, incl] tile (0, Z] exactly.
-  double incl = s;
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const double y = __shfl_down(incl, o, 64);
-    if (lane + o < 64) incl += y;
+  for (int h = 0; h < 2; ++h) {
+    const double wt = wave_sum(cs[h]);
+    if (lane == 0) sh.tot[h][wave] = wt;
   }
-  double above = __shfl_down(incl, 1, 64);
-  if (lane == 63) above = 0.0;
-  if (lane == 0) sh.tot[wave] = incl;
   if (t == 0) sh.sel = -1;
   __syncthreads();
-  double off = 0.0;   // the waves above this one, summed from the top
-  for (int i = kCountWaves - 1; i > wave; --i) off = off + sh.tot[i];
-  double Z = off;
-  for (int i = wave; i >= 0; --i) Z = Z + sh.tot[i];
-  incl = incl + off;
-  above = above + off;
+
+  // Running sums over the 32 (half, wave) blocks from the top, the same
+  // additions in the same order in every thread: Z, and the first block at
+  // whose end the sum reaches top_p * Z (ab: the sum before it).
+  double Z = 0.0;
+  for (int i = 2 * kCountWaves - 1; i >= 0; --i) Z = Z + sh.tot[i / kCountWaves][i % kCountWaves];
   const double tgt = (double)a.top_p * Z;
-  // The wave whose thread c holds the threshold: lane l takes key 64c + l,
-  // a suffix sum over the lanes gives the mass of the keys >= each, and the
-  // highest key with mass whose sum reaches the target ends the nucleus
-  // (rounding aside: else the lowest key with mass).
-  const uint64_t cross = __ballot(!bad && above < tgt && tgt <= incl);
-  if (cross) {
-    const int c = __builtin_ctzll(cross);
-    const double ab = __shfl(above, c, 64);
-    const uint32_t k = (uint32_t)(wave * 64 + c) * kKeysPerThread + lane;
-    const double m = mass(k, wrap_fix(sh, nev, k, (sh.cnt[k >> 1] >> (16 * (k & 1u))) & 0xFFFFu));
-    double run = m;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const double y = __shfl_down(run, o, 64);
-      if (lane + o < 64) run += y;
+  double ab = 0.0;
+  int hx = -1, wx = -1;
+  {
+    double run = 0.0;
+    for (int i = 2 * kCountWaves - 1; i >= 0 && hx < 0; --i) {
+      const double bt = sh.tot[i / kCountWaves][i % kCountWaves], nx = run + bt;
+      if (bt > 0.0 && nx >= tgt) {
+        hx = i / kCountWaves;
+        wx = i % kCountWaves;
+        ab = run;
+      }
+      run = nx;
     }
-    run += ab;
-    const uint64_t hit = __ballot(m != 0.0 && run >= tgt);
-    const uint64_t has = __ballot(m != 0.0);
+  }
+  if (!bad && wave == wx) {
+    // The rows' sums of half hx over the lanes: a butterfly that halves the
+    // rows each lane carries at every step leaves row lane / 2 in lanes
+    // 2j and 2j + 1.
+    float m[32];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) m[j] = mass(wbase + 64u * j + 32768u * hx, count_at(j, hx));
+#pragma unroll
+    for (int step = 0; step < 5; ++step) {
+      const int half = 16 >> step, o = 32 >> step;
+      const bool up = (lane & o) != 0;
+#pragma unroll
+      for (int k = 0; k < half; ++k) {
+        const float send = up ? m[k] : m[k + half];
+        const float recv = __shfl_xor(send, o, 64);
+        m[k] = (up ? m[k + half] : m[k]) + recv;
+      }
+    }
+    const float rj = m[0] + __shfl_xor(m[0], 1, 64);   // row lane / 2
+    // Suffix sums over the rows (row 31 first): lane 2j holds rows >= j.
+    const double sj = wave_suffix_sum((lane & 1) ? 0.0 : (double)rj, lane);
+    const double incl = ab + sj;
+    const double nxt = __shfl_down(sj, 2, 64);
+    const double above = lane >= 62 ? ab : ab + nxt;
+    const uint64_t crossr = __ballot(!(lane & 1) && rj > 0.f && above < tgt && tgt <= incl);
+    const uint64_t hasr = __ballot(!(lane & 1) && rj > 0.f);
+    // The crossing row; rounding aside (the rows' sums and the block's
+    // differ in order), else the lowest row with mass.
+    const int jl = crossr ? (63 - __builtin_clzll(crossr)) : __builtin_ctzll(hasr);
+    const int jx = jl >> 1;
+    const double ab_row = __shfl(above, jl, 64);
+    // Keys of row jx, one per lane: the highest with mass whose running sum
+    // reaches the target ends the nucleus (else the lowest with mass).
+    const uint32_t k = wbase + 64u * (uint32_t)jx + 32768u * (uint32_t)hx;
+    uint32_t n = nev ? key_count(sh, nev, k) : ((sh.cnt[k & 0x7FFFu] >> (16 * hx)) & 0xFFFFu);
+    n = k == kKeyNegZero ? 0u : (k == kKeyPosZero ? n + nzero : n);
+    const float mk = mass(k, n);
+    const double run = wave_suffix_sum((double)mk, lane) + ab_row;
+    const uint64_t hit = __ballot(mk != 0.f && run >= tgt);
+    const uint64_t has = __ballot(mk != 0.f);
     const int src = hit ? 63 - __builtin_clzll(hit) : __builtin_ctzll(has);
     if (lane == src) {
       sh.sel = (int)k;
@@ -2322,16 +2352,16 @@ __global__ __launch_bounds__(kCountThreads) void topp_count_kernel(VerifyArgs a)
     slot_put(a.part + p0 + i, v);
   }
   if (t == 0) {
-    TopPRow tp;
-    tp.M = mref;
-    tp.Z = Z;
-    tp.rem = 0.0;
-    tp.above = 0.0;
+    TopPRow tr;
+    tr.M = mref;
+    tr.Z = Z;
+    tr.rem = 0.0;
+    tr.above = 0.0;
     const bool cut = !bad && sh.sel >= 0;
-    tp.P = cut ? sh.P : 1.0;
-    tp.prefix = cut ? (uint32_t)sh.sel : 0u;
-    tp.L = cut ? key_logit<kBF16>((uint32_t)sh.sel) : -INFINITY;
-    a.topp[row] = tp;
+    tr.P = cut ? sh.P : 1.0;
+    tr.prefix = cut ? (uint32_t)sh.sel : 0u;
+    tr.L = cut ? key_logit<kBF16>((uint32_t)sh.sel) : -INFINITY;
+    a.topp[row] = tr;
   }
 }
 
