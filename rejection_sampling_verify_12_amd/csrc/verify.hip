@@ -2016,11 +2016,19 @@ constexpr int kCountEvents = 288;
 constexpr uint32_t kKeyNegInf = 0x007Fu, kKeyNegZero = 0x7FFFu, kKeyPosZero = 0x8000u,
                    kKeyPosInf = 0xFF80u;
 
+// The counted row's words with a count, compacted in ascending order (word,
+// low count | high count << 16) for the wave that finishes the row while the
+// next one is counted; a row with more takes the in-place finish.
+constexpr int kListCap = 3328;
+constexpr int kCountingWaves = kCountWaves - 1;
+constexpr int kCountingThreads = 64 * kCountingWaves;
+
 struct CountLds {
   uint32_t cnt[kCountWords];
+  uint2 list[kListCap];
   uint32_t ev[kCountEvents];   // keys whose counter wrapped (checked pass)
   uint32_t nev;
-  uint32_t sum[kCountWaves];
+  uint32_t sum[kCountWaves], nzw[kCountWaves];
   int kmax[kCountWaves], flags[kCountWaves];
   double tot[2][kCountWaves];
   int sel;
@@ -2065,17 +2073,17 @@ __device__ __forceinline__ void count_pair(CountLds& sh, uint32_t w) {
   count_key<CHECK>(sh, kp >> 16);
 }
 
-// Every logit of the row, once.  Lane t takes 8-logit units t, t + 1024, ...
-// (eight in flight; one in the rarely run checked pass, whose code stays
-// small), then one of the last V mod 8 logits.
-template <bool VEC, bool CHECK>
+// Every logit of the row, once, by threads 0 .. NT - 1.  Lane t takes
+// 8-logit units t, t + NT, ... (eight in flight; one in the rarely run
+// checked pass, whose code stays small), then one of the last V mod 8.
+template <bool VEC, bool CHECK, int NT>
 __device__ void count_row(const uint16_t* row, int64_t V, CountLds& sh) {
   const int t = threadIdx.x;
   const int64_t units = V >> 3;
   int64_t u = t;
   if constexpr (VEC) {
     constexpr int U = CHECK ? 1 : 8;
-    constexpr int64_t kBatch = (int64_t)U * kCountThreads;
+    constexpr int64_t kBatch = (int64_t)U * NT;
     const __amdgpu_buffer_rsrc_t rs = chunk_rsrc(row, (int)(units * 16));
     const int voff = t * 16;
     const int64_t nb = units / kBatch;
@@ -2083,7 +2091,7 @@ __device__ void count_row(const uint16_t* row, int64_t V, CountLds& sh) {
       u32x4 w[U];
 #pragma unroll
       for (int q = 0; q < U; ++q)
-        w[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, (int)((i * kBatch + q * kCountThreads) * 16), 2);
+        w[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, (int)((i * kBatch + q * NT) * 16), 2);
 #pragma unroll
       for (int q = 0; q < U; ++q) {
         count_pair<CHECK>(sh, w[q].x);
@@ -2092,7 +2100,7 @@ __device__ void count_row(const uint16_t* row, int64_t V, CountLds& sh) {
         count_pair<CHECK>(sh, w[q].w);
       }
     }
-    for (u = nb * kBatch + t; u < units; u += kCountThreads) {
+    for (u = nb * kBatch + t; u < units; u += NT) {
       const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, (int)((u - t) * 16), 2);
       count_pair<CHECK>(sh, w.x);
       count_pair<CHECK>(sh, w.y);
@@ -2100,7 +2108,7 @@ __device__ void count_row(const uint16_t* row, int64_t V, CountLds& sh) {
       count_pair<CHECK>(sh, w.w);
     }
   } else {
-    for (; u < units; u += kCountThreads) {
+    for (; u < units; u += NT) {
 #pragma unroll
       for (int e = 0; e < 8; e += 2)
         count_pair<CHECK>(sh, (uint32_t)row[u * 8 + e] | ((uint32_t)row[u * 8 + e + 1] << 16));
@@ -2139,37 +2147,68 @@ __device__ __forceinline__ F wave_suffix_sum(F v, int lane) {
   return v;
 }
 
-// After counting, wave w holds words 2048w + 64j + lane (j = 0..31) in
-// registers: consecutive words in consecutive lanes, so a band of crowded
-// values spreads over the lanes.  From the top key down the order is: the
-// high halves (non-negative values) of waves 15..0, then the low halves of
-// waves 15..0; within a wave, rows j = 31..0, lanes 63..0.
+// A counted row's outputs: its normaliser piece (the whole row in piece 0,
+// -inf in the others) and maximum where the stream items would put them,
+// and its nucleus (threshold sel, mass fraction P; none for a bad row).
+// Threads tid = 0 .. nthr - 1.
+__device__ __forceinline__ void count_outputs(const VerifyArgs& a, int64_t row, int flags, int kmax, float mref,
+                                              double Z, int sel, double P, int tid, int nthr) {
+  const bool bad = flags != 0 || kmax < 0;
+  const float vmax = kmax >= 0 ? key_logit<kBF16>((uint32_t)kmax) : -INFINITY;
+  const int64_t p0 = row * a.nc;
+  for (int i = tid; i < a.nc; i += nthr) {
+    double v = -INFINITY;
+    float mr = -INFINITY;
+    if (i == 0) {
+      if (flags & 1) v = NAN;
+      else if (flags & 2) v = INFINITY;
+      else if (kmax >= 0) v = (double)mref + log2(Z);
+      mr = (flags & 2) ? INFINITY : vmax;
+    }
+    slot_put32(a.mraw + p0 + i, mr);
+    slot_put(a.part + p0 + i, v);
+  }
+  if (tid == 0) {
+    TopPRow tr;
+    tr.M = mref;
+    tr.Z = Z;
+    tr.rem = 0.0;
+    tr.above = 0.0;
+    const bool cut = !bad && sel >= 0;
+    tr.P = cut ? P : 1.0;
+    tr.prefix = cut ? (uint32_t)sel : 0u;
+    tr.L = cut ? key_logit<kBF16>((uint32_t)sel) : -INFINITY;
+    a.topp[row] = tr;
+  }
+}
+
+// The in-place finish of a counted row (every thread): wave w takes words
+// 2048w + 64j + lane (j = 0..31) in registers, consecutive words in
+// consecutive lanes, so a band of crowded values spreads over the lanes.
+// From the top key down the order is: the high halves (non-negative values)
+// of waves 15..0, then the low halves of waves 15..0; within a wave, rows
+// j = 31..0, lanes 63..0.  Leaves counts in the counters.
 template <bool VEC>
-__global__ __launch_bounds__(kCountThreads) void topp_count_kernel(VerifyArgs a) {
-  __shared__ CountLds sh;
+__device__ void finish_inplace(const VerifyArgs& a, int64_t row, CountLds& sh) {
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int R = 2 * a.gamma + 1;
-  const int64_t row = blockIdx.x;
   const int b = (int)(row / R), r = (int)(row - (int64_t)b * R);
   const uint16_t* rp = static_cast<const uint16_t*>(row_ptr<kBF16>(a, b, r));
   const TCoef tc = temp_coef(a, b);
-
   uint4* c4 = reinterpret_cast<uint4*>(sh.cnt);
-  for (int i = t; i < kCountWords / 4; i += kCountThreads) c4[i] = make_uint4(0u, 0u, 0u, 0u);
-  if (t == 0) sh.nev = 0u;
-  __syncthreads();
-  count_row<VEC, false>(rp, a.V, sh);
-  __syncthreads();
 
-  const uint32_t wbase = 2048u * (uint32_t)wave + (uint32_t)lane;   // word of row j: wbase + 64 j
-  uint32_t cw[32];
-#pragma unroll
-  for (int j = 0; j < 32; ++j) cw[j] = sh.cnt[wbase + 64u * j];
+  // Word of row j: wbase + 64 j (the opaque step keeps the compiler from
+  // precomputing every such address outside the caller's loop).
+  uint32_t wbase = 2048u * (uint32_t)wave + (uint32_t)lane;
+  asm volatile("" : "+v"(wbase));
+  // The counter words are read from LDS where used (rare path: registers
+  // stay free).
+  auto cw = [&](int j) -> uint32_t { return sh.cnt[wbase + 64u * j]; };
   int nev = 0;
   {   // the 16-bit counters sum to V unless one wrapped: then count again, recording the wraps
     uint32_t sum = 0;
 #pragma unroll
-    for (int j = 0; j < 32; ++j) sum += (cw[j] & 0xFFFFu) + (cw[j] >> 16);
+    for (int j = 0; j < 32; ++j) sum += (cw(j) & 0xFFFFu) + (cw(j) >> 16);
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 64);
     if (lane == 0) sh.sum[wave] = sum;
@@ -2179,12 +2218,11 @@ __global__ __launch_bounds__(kCountThreads) void topp_count_kernel(VerifyArgs a)
     if ((int64_t)sum != a.V) {
       __syncthreads();   // every thread is done with the counters
       for (int i = t; i < kCountWords / 4; i += kCountThreads) c4[i] = make_uint4(0u, 0u, 0u, 0u);
+      if (t == 0) sh.nev = 0u;
       __syncthreads();
-      count_row<VEC, true>(rp, a.V, sh);
+      count_row<VEC, true, kCountThreads>(rp, a.V, sh);
       __syncthreads();
       nev = (int)min(sh.nev, (uint32_t)kCountEvents);
-#pragma unroll
-      for (int j = 0; j < 32; ++j) cw[j] = sh.cnt[wbase + 64u * j];
     }
   }
   // The count of key half h of row j (with the recorded wraps, if any); -0
@@ -2192,7 +2230,7 @@ __global__ __launch_bounds__(kCountThreads) void topp_count_kernel(VerifyArgs a)
   const uint32_t nzero = key_count(sh, nev, kKeyNegZero);
   auto count_at = [&](int j, int h) -> uint32_t {
     const uint32_t k = wbase + 64u * j + 32768u * h;
-    uint32_t n = nev ? key_count(sh, nev, k) : ((cw[j] >> (16 * h)) & 0xFFFFu);
+    uint32_t n = nev ? key_count(sh, nev, k) : ((cw(j) >> (16 * h)) & 0xFFFFu);
     return k == kKeyNegZero ? 0u : (k == kKeyPosZero ? n + nzero : n);
   };
 
@@ -2209,7 +2247,7 @@ __global__ __launch_bounds__(kCountThreads) void topp_count_kernel(VerifyArgs a)
   if (nev == 0) {
 #pragma unroll
     for (int j = 0; j < 32; ++j) {
-      uint32_t w = cw[j];
+      uint32_t w = cw(j);
       asm volatile("" : "+v"(w), "+v"(kmax), "+v"(flags));
       const uint32_t k = wbase + 64u * j;
       take(k, k == kKeyNegZero ? 0u : (w & 0xFFFFu));
@@ -2254,7 +2292,7 @@ __global__ __launch_bounds__(kCountThreads) void topp_count_kernel(VerifyArgs a)
     for (int j = 0; j < 32; ++j) {
       // One row at a time (the opaque step orders them): computing every
       // term ahead of the additions would not fit the registers.
-      uint32_t w = cw[j];
+      uint32_t w = cw(j);
       asm volatile("" : "+v"(w), "+v"(cs[0]), "+v"(cs[1]));
       if (w != 0u || nev != 0 || (t == 0 && j == 0)) {
 #pragma unroll
@@ -2337,31 +2375,179 @@ __global__ __launch_bounds__(kCountThreads) void topp_count_kernel(VerifyArgs a)
     }
   }
   __syncthreads();
+  count_outputs(a, row, flags, kmax, mref, Z, sh.sel, sh.P, t, kCountThreads);
+}
 
-  const int64_t p0 = row * a.nc;
-  for (int i = t; i < a.nc; i += kCountThreads) {
-    double v = -INFINITY;
-    float mr = -INFINITY;
-    if (i == 0) {
-      if (flags & 1) v = NAN;
-      else if (flags & 2) v = INFINITY;
-      else if (kmax >= 0) v = (double)mref + log2(Z);
-      mr = (flags & 2) ? INFINITY : vmax;
+// The previous row's finish from its compacted words (one wave, while the
+// other waves count the next row).  Lane l takes a run of consecutive
+// entries; from the top key down the order is the high halves of entries
+// E-1..0, then the low halves of entries E-1..0.  -0 has been counted with
+// +0 already and no counter wrapped.
+__device__ void finish_list(const VerifyArgs& a, int64_t row, const CountLds& sh, int E) {
+  const int lane = threadIdx.x & 63;
+  const int R = 2 * a.gamma + 1;
+  const int b = (int)(row / R);
+  const TCoef tc = temp_coef(a, b);
+  const int per = (E + 63) >> 6;
+  const int e0 = min(lane * per, E), e1 = min(e0 + per, E);
+  int kmax = -1, flags = 0;
+  for (int e = e0; e < e1; ++e) {
+    const uint2 en = sh.list[e];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t k = en.x + 32768u * h, n = (en.y >> (16 * h)) & 0xFFFFu;
+      if (n == 0u) continue;
+      if (key_finite(k)) kmax = max(kmax, (int)k);
+      else flags |= nonfinite_flag(k);
     }
-    slot_put32(a.mraw + p0 + i, mr);
-    slot_put(a.part + p0 + i, v);
   }
-  if (t == 0) {
-    TopPRow tr;
-    tr.M = mref;
-    tr.Z = Z;
-    tr.rem = 0.0;
-    tr.above = 0.0;
-    const bool cut = !bad && sh.sel >= 0;
-    tr.P = cut ? sh.P : 1.0;
-    tr.prefix = cut ? (uint32_t)sh.sel : 0u;
-    tr.L = cut ? key_logit<kBF16>((uint32_t)sh.sel) : -INFINITY;
-    a.topp[row] = tr;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    kmax = max(kmax, __shfl_xor(kmax, o, 64));
+    flags |= __shfl_xor(flags, o, 64);
+  }
+  const bool bad = flags != 0 || kmax < 0;
+  const float vmax = kmax >= 0 ? key_logit<kBF16>((uint32_t)kmax) : -INFINITY;
+  const float mref = bad ? 0.f : ceilf(fminf(vmax * tc.c_hi, 1.0e30f));
+  auto mass = [&](uint32_t k, uint32_t n) -> float {
+    const float v = key_logit<kBF16>(k);
+    const float m = (float)n * exp2_fast(fmaf(v, tc.c_lo, fmaf(v, tc.c_hi, -mref)));
+    return (n != 0u && key_finite(k)) ? m : 0.f;
+  };
+  double sm[2] = {0.0, 0.0};
+  if (!bad) {
+    for (int e = e0; e < e1; ++e) {
+      const uint2 en = sh.list[e];
+      sm[0] += (double)mass(en.x, en.y & 0xFFFFu);
+      sm[1] += (double)mass(en.x + 32768u, en.y >> 16);
+    }
+  }
+  // Suffix sums over the lanes, the high halves first; a lane's `above` is
+  // the next lane's `incl`, the same value, so the intervals tile (0, Z].
+  const double s1 = wave_suffix_sum(sm[1], lane), s0 = wave_suffix_sum(sm[0], lane);
+  const double H = __shfl(s1, 0, 64);
+  const double d1 = __shfl_down(s1, 1, 64), d0 = __shfl_down(s0, 1, 64);
+  const double incl1 = s1, above1 = lane == 63 ? 0.0 : d1;
+  const double incl0 = s0 + H, above0 = (lane == 63 ? 0.0 : d0) + H;
+  const double Z = __shfl(incl0, 0, 64);
+  const double tgt = (double)a.top_p * Z;
+  const bool c1 = !bad && above1 < tgt && tgt <= incl1, c0 = !bad && above0 < tgt && tgt <= incl0;
+  int sel = -1;
+  double P = 1.0;
+  if (c1 || c0) {   // this lane's entries hold the threshold: walk them from the top
+    const int h = c1 ? 1 : 0;
+    double run = c1 ? above1 : above0, Pl = run;
+    int low = -1;
+    for (int e = e1 - 1; e >= e0; --e) {
+      const uint2 en = sh.list[e];
+      const uint32_t k = en.x + 32768u * h;
+      const float m = mass(k, (en.y >> (16 * h)) & 0xFFFFu);
+      if (m == 0.f) continue;
+      run += (double)m;
+      low = (int)k;
+      Pl = run;
+      if (run >= tgt) break;
+    }
+    sel = low;
+    P = Pl / Z;
+  }
+  const uint64_t who = __ballot(sel >= 0);
+  if (who) {
+    const int src = __builtin_ctzll(who);
+    sel = __shfl(sel, src, 64);
+    P = __shfl(P, src, 64);
+  }
+  count_outputs(a, row, flags, kmax, mref, Z, sel, P, lane, 64);
+}
+
+// Persistent: work-group g counts rows g, g + G, ...  While waves 0..14
+// count a row, wave 15 finishes the row before it from its compacted words
+// (the counting is limited by LDS atomics, the finish by latency, so they
+// overlap).  After each row every thread compacts its words with a count
+// into the list and clears its counters; a row whose 16-bit counters
+// wrapped, or whose words do not fit the list, is finished in place.
+template <bool VEC>
+__global__ __launch_bounds__(kCountThreads) void topp_count_kernel(VerifyArgs a, int64_t nrows) {
+  __shared__ CountLds sh;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int R = 2 * a.gamma + 1;
+  uint4* c4 = reinterpret_cast<uint4*>(sh.cnt);
+  for (int i = t; i < kCountWords / 4; i += kCountThreads) c4[i] = make_uint4(0u, 0u, 0u, 0u);
+  __syncthreads();
+  int64_t prev = -1;
+  int E = 0;
+  for (int64_t row = blockIdx.x;; row += gridDim.x) {
+    const bool have = row < nrows;
+    if (wave < kCountingWaves) {
+      if (have) {
+        const int b = (int)(row / R), r = (int)(row - (int64_t)b * R);
+        count_row<VEC, false, kCountingThreads>(static_cast<const uint16_t*>(row_ptr<kBF16>(a, b, r)), a.V, sh);
+      }
+    } else if (prev >= 0) {
+      finish_list(a, prev, sh, E);
+    }
+    __syncthreads();
+    if (!have) break;
+
+    // Compaction.  -0 (the low half of word 32767) moves to +0 (the high
+    // half of word 0); the sum of the counters checks for a wrap.  Words
+    // are read from LDS as needed (registers stay free for the counting);
+    // word of row j: wbase + 64 j.
+    uint32_t wbase = 2048u * (uint32_t)wave + (uint32_t)lane;
+    asm volatile("" : "+v"(wbase));
+    const uint32_t nzero = sh.cnt[kKeyNegZero] & 0xFFFFu;
+    auto word = [&](int j) -> uint32_t {
+      uint32_t w = sh.cnt[wbase + 64u * j];
+      if (t == kCountThreads - 1 && j == 31) w &= 0xFFFF0000u;
+      if (t == 0 && j == 0) w += nzero << 16;   // checked against overflow below
+      return w;
+    };
+    uint32_t sum = 0, nzc = 0;
+    int over = t == 0 && (sh.cnt[0] >> 16) + nzero > 0xFFFFu;
+#pragma unroll 8
+    for (int j = 0; j < 32; ++j) {
+      const uint32_t w = sh.cnt[wbase + 64u * j];
+      sum += (w & 0xFFFFu) + (w >> 16);
+      nzc += (uint32_t)__popcll(__ballot(word(j) != 0u));
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 64);
+    over = __ballot(over) != 0;
+    if (lane == 0) {
+      sh.sum[wave] = sum;
+      sh.nzw[wave] = nzc;
+      sh.flags[wave] = over;
+    }
+    __syncthreads();
+    uint32_t tsum = 0, base = 0, tot = 0;
+    for (int i = 0; i < kCountWaves; ++i) {
+      tsum += sh.sum[i];
+      base += i < wave ? sh.nzw[i] : 0u;
+      tot += sh.nzw[i];
+      over |= sh.flags[i];
+    }
+    if ((int64_t)tsum == a.V && tot <= (uint32_t)kListCap && !over) {
+      const uint64_t lt = (1ull << lane) - 1ull;
+      __syncthreads();   // thread 0 has read -0's counter
+#pragma unroll 8
+      for (int j = 0; j < 32; ++j) {
+        const uint32_t w = word(j);
+        const uint64_t bal = __ballot(w != 0u);
+        if (w != 0u) sh.list[base + (uint32_t)__popcll(bal & lt)] = make_uint2(wbase + 64u * j, w);
+        base += (uint32_t)__popcll(bal);
+      }
+      __syncthreads();   // every word is read before any is cleared
+#pragma unroll 8
+      for (int j = 0; j < 32; ++j) sh.cnt[wbase + 64u * j] = 0u;
+      prev = row;
+      E = (int)tot;
+    } else {
+      finish_inplace<VEC>(a, row, sh);
+      __syncthreads();
+      for (int i = t; i < kCountWords / 4; i += kCountThreads) c4[i] = make_uint4(0u, 0u, 0u, 0u);
+      prev = -1;
+    }
+    __syncthreads();
   }
 }
 
@@ -2557,7 +2743,12 @@ static hipError_t launch_kernels_cut(const VerifyArgs& a, hipStream_t st) {
   const unsigned rows = (unsigned)((int64_t)a.B * R);
   if (CUT && DT == kBF16 && a.V <= kCountMaxV) {
     // Counting gives each row's nucleus and its normaliser piece in one read.
-    hipLaunchKernelGGL((topp_count_kernel<VEC>), dim3(rows), dim3(kCountThreads), 0, st, a);
+    int ncu = 0, dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((topp_count_kernel<VEC>), dim3(std::min<unsigned>(rows, (unsigned)std::max(ncu, 1))),
+                       dim3(kCountThreads), 0, st, a, (int64_t)rows);
   } else {
     hipLaunchKernelGGL((stream_kernel<DT, VEC, SV_STREAM_UNROLL>), dim3(nstream), dim3(kThreads), 0, st, a);
     if constexpr (CUT) {   // the nucleus of every row by radix selection

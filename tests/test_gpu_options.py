@@ -185,6 +185,8 @@ def counted_rows_batch(V, seed):
         t64[2, r, zeros] = np.where(np.arange(zeros.size) % 3 == 0, -0.0, 0.0)
     t64[6, :, 5] = 40.0                      # near one-hot target rows
     d64[7, :, rng.permutation(V)[:V // 3]] = -np.inf
+    wide = rng.permutation(V)[:V // 2]       # thousands of distinct values (the in-place finish)
+    t64[7][:, wide] = np.sign(rng.standard_normal((g + 1, wide.size))) * np.exp(rng.uniform(-40, 2.5, (g + 1, wide.size)))
     d = W.encode(d64, "bf16")
     t = W.encode(t64, "bf16")
     x = W.gumbel_argmax(W.decode_f64(d, "bf16")[:, :g], 1.0, W.philox(seed, 12))
