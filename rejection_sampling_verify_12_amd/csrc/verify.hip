@@ -2527,18 +2527,17 @@ __global__ __launch_bounds__(kCountThreads) void topp_count_kernel(VerifyArgs a,
       over |= sh.flags[i];
     }
     if ((int64_t)tsum == a.V && tot <= (uint32_t)kListCap && !over) {
+      // Each thread reads only its own words here (-0's counter was read
+      // before the barrier above), so it clears each once read.
       const uint64_t lt = (1ull << lane) - 1ull;
-      __syncthreads();   // thread 0 has read -0's counter
 #pragma unroll 8
       for (int j = 0; j < 32; ++j) {
         const uint32_t w = word(j);
+        sh.cnt[wbase + 64u * j] = 0u;
         const uint64_t bal = __ballot(w != 0u);
         if (w != 0u) sh.list[base + (uint32_t)__popcll(bal & lt)] = make_uint2(wbase + 64u * j, w);
         base += (uint32_t)__popcll(bal);
       }
-      __syncthreads();   // every word is read before any is cleared
-#pragma unroll 8
-      for (int j = 0; j < 32; ++j) sh.cnt[wbase + 64u * j] = 0u;
       prev = row;
       E = (int)tot;
     } else {
