@@ -1,0 +1,149 @@
+// Kernels: the single kernel and one kernel per item kind.
+#pragma once
+#include "verify_sched.h"
+
+namespace sv {
+
+// ---------------------------------------------------------------------------
+// Kernels.
+
+union ItemLds {
+  StreamLds s;
+  DecideLds d;
+  DrawLds r;
+  FinalLds f;
+  TestLds t;
+};
+
+// Early exit: a stream item of position pos (1..gamma-1) skips its rows when
+// an earlier position is known to stop the sequence; an item of target row
+// gamma (pos = gamma) skips on any known stop.  Read by one thread; the
+// work-group follows its answer.
+__device__ __forceinline__ bool early_stopped(const VerifyArgs& a, int b, int pos) {
+  const unsigned st = ld_dev_u32(a.flag + (int64_t)b * kFlagStride + kStopWord);
+  return pos >= a.gamma ? st != 0u : st > 64u - (unsigned)pos;
+}
+// A skipping item publishes skip markers in place of its piece.
+__device__ __forceinline__ void early_skip(const VerifyArgs& a, int b, int r, int c) {
+  if (threadIdx.x == 0) {
+    const int64_t idx = ((int64_t)b * (2 * a.gamma + 1) + r) * a.nc + c;
+    __hip_atomic_store(a.mraw + idx, kSkipRaw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    st_dev_u64(a.part + idx, kSkipPiece);
+  }
+}
+
+// Compiled for 8 waves per SIMD (64 VGPRs): the stream items need the
+// occupancy; every other path fits without spilling for packed bf16 rows.
+// PRED: outcome prediction too (draft-row items record lane leaders; the
+// items of target row gamma are followed by leader items of draft row gamma).
+// EARLY: the early-exit order (position-major stream items, position tests).
+template <int DT, bool VEC, int U, bool PRED, bool EARLY>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8)))
+void fused_kernel(VerifyArgs a, Sched sc) {
+  __shared__ ItemLds sh;
+  __shared__ int item[4];
+  // One wave decodes the block number (a search on the scalar unit, which
+  // the CU's waves share) and hands the item to the others.
+  if (threadIdx.x < 64) {
+    int kind, b, sub;
+    if constexpr (EARLY) sched_decode_table(sc, (int)blockIdx.x, kind, b, sub);
+    else sched_decode_search(sc, (int)blockIdx.x, kind, b, sub);
+    if (threadIdx.x == 0) {
+      item[0] = kind;
+      item[1] = b;
+      item[2] = sub;
+      bool skip = false;
+      if constexpr (EARLY) {
+        if (kind == kItemStream && b >= a.B) skip = early_stopped(a, b - b / a.B * a.B, b / a.B);
+        else if (kind == kItemLast) skip = early_stopped(a, b, a.gamma);
+      }
+      item[3] = skip;
+    }
+  }
+  __syncthreads();
+  const int kind = uni(item[0]), b = uni(item[1]), sub = uni(item[2]), skip = uni(item[3]);
+  switch (kind) {
+    case kItemStream: {
+      if constexpr (EARLY) {   // b = i * B + sequence; sub: draft row i, then target row i
+        const int i = b / a.B, q = b - i * a.B;
+        const int h = sub >= a.nc, c = sub - h * a.nc, r = h ? a.gamma + i : i;
+        if (skip) early_skip(a, q, r, c);
+        else stream_item<DT, VEC, U>(a, q, r, c, sh.s);
+      } else {
+        const int r = sub / a.nc, c = sub - r * a.nc;
+        if (PRED && r < a.gamma) stream_item<DT, VEC, U, PRED>(a, b, r, c, sh.s);
+        else stream_item<DT, VEC, U>(a, b, r, c, sh.s);
+      }
+      break;
+    }
+    case kItemTest:
+      if constexpr (EARLY) test_item<DT>(a, b - b / a.B * a.B, b / a.B, sh.t);
+      break;
+    case kItemDecide: decide_item<DT>(a, b, sh.d); break;
+    case kItemMass: break;   // Saguaro with eps > 0 runs as separate kernels
+    case kItemSample: sample_item<DT, VEC, false, false>(a, b, sub, sh.r.lds_d); break;
+    case kItemDraw: draw_item<DT, VEC, false, false>(a, b, sh.r); break;
+    case kItemLast:
+      if (EARLY && skip) {
+        early_skip(a, b, 2 * a.gamma, sub);
+        break;
+      }
+      if (!PRED || sub < a.nc) stream_item<DT, VEC, U>(a, b, 2 * a.gamma, sub, sh.s);
+      else leader_item<DT, VEC, U>(a, b, sub - a.nc, sh.s);
+      break;
+    default: final_item<DT>(a, b, sh.f); break;
+  }
+}
+
+template <int DT, bool VEC, int U>
+__global__ __launch_bounds__(kThreads) void stream_kernel(VerifyArgs a) {
+  __shared__ StreamLds sh;
+  const int R = 2 * a.gamma + 1;
+  const int64_t id = blockIdx.x;
+  const int per_seq = R * a.nc;
+  const int b = (int)(id / per_seq);
+  const int rem = (int)(id - (int64_t)b * per_seq);
+  const int r = rem / a.nc, c = rem - r * a.nc;
+  stream_item<DT, VEC, U>(a, b, r, c, sh);
+}
+
+template <int DT, bool CUT>
+__global__ __launch_bounds__(kThreads) void decide_kernel(VerifyArgs a) {
+  __shared__ DecideLds sh;
+  decide_item<DT, CUT>(a, blockIdx.x, sh);
+}
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void test_kernel(VerifyArgs a) {
+  __shared__ TestLds sh;
+  const int i = blockIdx.x / a.B;
+  test_item<DT>(a, blockIdx.x - i * a.B, i, sh);
+}
+
+template <int DT, bool VEC, bool CUT>
+__global__ __launch_bounds__(kThreads) void mass_kernel(VerifyArgs a) {
+  __shared__ double lds_d[kWaves * (kTilesPerItem + 1)];
+  const int b = blockIdx.x / a.nt, s = blockIdx.x - b * a.nt;
+  mass_item<DT, VEC, CUT>(a, b, s, lds_d);
+}
+
+template <int DT, bool VEC, bool CUT>
+__global__ __launch_bounds__(kThreads) void sample_kernel(VerifyArgs a) {
+  __shared__ double lds_d[kWaves * (kTilesPerItem + 1)];
+  const int b = blockIdx.x / a.nt, s = blockIdx.x - b * a.nt;
+  sample_item<DT, VEC, CUT>(a, b, s, lds_d);
+}
+
+template <int DT, bool VEC, bool CUT>
+__global__ __launch_bounds__(kThreads) void draw_kernel(VerifyArgs a) {
+  __shared__ DrawLds sh;
+  draw_item<DT, VEC, CUT>(a, blockIdx.x, sh);
+}
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void final_kernel(VerifyArgs a) {
+  __shared__ FinalLds sh;
+  final_item<DT>(a, blockIdx.x, sh);
+}
+
+}  // namespace sv

@@ -1,0 +1,640 @@
+// Sampling: weights, residual-mass, sampling, draw and final items.
+#pragma once
+#include "verify_decide.h"
+
+namespace sv {
+
+// ---------------------------------------------------------------------------
+// Sampling weights.
+
+struct SampleCoef {
+  float c_hi, c_lo, Mt, K_hi, K_lo, epsS;
+  float A_hi, A_lo;   // K - Mt as an unevaluated float pair: p_j ~ 2^(ld_j c_T + K - Mt)
+  float Ld, Lt;       // top-p thresholds of the rows drawn from (-inf: no cut)
+};
+
+// A top-p cut: logits below the row's threshold act as -inf (probability 0);
+// the renormalisation is folded into the decision record's constants.
+template <bool CUT>
+__device__ __forceinline__ void cut8(float (&v)[8], float L) {
+  if constexpr (CUT) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = v[e] >= L ? v[e] : -INFINITY;
+  }
+}
+template <bool CUT>
+__device__ __forceinline__ float cut1(float v, float L) {
+  if constexpr (CUT) return v >= L ? v : -INFINITY;
+  else return v;
+}
+
+template <bool CUT = false>
+__device__ __forceinline__ SampleCoef coef_of(const VerifyArgs& a, int b, const SeqRec& rec, float epsS) {
+  SampleCoef c;
+  const TCoef tc = temp_coef(a, b);
+  c.c_hi = tc.c_hi;
+  c.c_lo = tc.c_lo;
+  c.Mt = rec.Mt;
+  c.K_hi = rec.K_hi;
+  c.K_lo = rec.K_lo;
+  c.epsS = epsS;
+  const double A = ((double)rec.K_hi + (double)rec.K_lo) - (double)rec.Mt;
+  c.A_hi = uni((float)A);
+  c.A_lo = uni((float)(A - (double)c.A_hi));
+  c.Ld = -INFINITY;
+  c.Lt = -INFINITY;
+  if (CUT && a.topp && rec.k >= 0 && rec.k <= a.gamma) {
+    const TopPRow* tp = a.topp + (int64_t)b * (2 * a.gamma + 1);
+    c.Lt = uni(tp[a.gamma + rec.k].L);
+    if (rec.k < a.gamma) c.Ld = uni(tp[rec.k].L);
+  }
+  return c;
+}
+
+constexpr float kLn2f = 0.69314718055994530942f;
+
+// 1 - 2^d.  PRECISE: for d in (-1, 0], -expm1(d ln 2) by its Taylor series
+// (degree 9, truncation below 1e-8 relative), so a small residual keeps its
+// relative precision; otherwise (and for d <= -1) 1 - 2^d from the rounded
+// exponential, whose error is a few ulp of 1 (of q_j, not of the residual).
+template <bool PRECISE>
+__device__ __forceinline__ float one_minus_exp2(float d, float ex) {
+  if constexpr (!PRECISE) {
+    return 1.f - ex;
+  } else {
+    const float x = d * kLn2f;
+    float p = 1.f / 362880.f;
+    p = fmaf(p, x, 1.f / 40320.f);
+    p = fmaf(p, x, 1.f / 5040.f);
+    p = fmaf(p, x, 1.f / 720.f);
+    p = fmaf(p, x, 1.f / 120.f);
+    p = fmaf(p, x, 1.f / 24.f);
+    p = fmaf(p, x, 1.f / 6.f);
+    p = fmaf(p, x, 0.5f);
+    p = fmaf(p, x, 1.f);
+    return d > -1.f ? -x * p : 1.f - ex;
+  }
+}
+
+// Sampling weight of one logit pair, proportional (one factor per sequence)
+// to the probability of the distribution drawn from:
+//   target row:  q_j                      (eq_j = 2^(lt_j c_T - Mt))
+//   residual:    (q_j - p_j)+             (eq_j (1 - 2^delta_j) where delta_j < 0)
+//   Saguaro:     sqrt(p_j (q_j - p_j)+)   (eq_j sqrt(2^delta_j (1 - 2^delta_j)))
+//   Saguaro eps: sqrt(p_j max(r_j, eps))  (sqrt(eq_j 2^delta_j max(res_j, eps sum res)))
+// with delta_j = log2(p_j / q_j) = (ld_j - lt_j) c_T + K (exact logit
+// difference for bf16, a two-sum for float32).  r = the residual weight.
+template <int DT, int MODE, bool PRECISE>
+__device__ __forceinline__ float weight_one(float ld, float lt, const SampleCoef& c, float& r) {
+  const float eq = exp2_fast(fmaf(lt, c.c_lo, fmaf(lt, c.c_hi, -c.Mt)));
+  if constexpr (MODE == kModeTarget) {
+    r = 0.f;
+    return eq;
+  } else if constexpr (MODE == kModeResidual && !PRECISE) {
+    // (q_j - p_j)+ from both scaled probabilities: the same absolute error
+    // (a few ulp of q_j) as 1 - 2^delta_j, with fewer instructions.
+    const float ep = exp2_fast(fmaf(ld, c.c_lo, fmaf(ld, c.c_hi, c.A_hi) + c.A_lo));
+    const float res = fmaxf(eq - ep, 0.f);
+    r = res;
+    return res;
+  } else {
+    const float dl = ld - lt;
+    float d;
+    if constexpr (DT == kBF16) {
+      d = fmaf(dl, c.c_hi, c.K_hi) + fmaf(dl, c.c_lo, c.K_lo);   // dl is exact
+    } else {
+      const float bb = dl - ld;
+      const float err = (ld - (dl - bb)) - (lt + bb);             // ld - lt = dl + err
+      d = fmaf(dl, c.c_hi, c.K_hi) + fmaf(err, c.c_hi, fmaf(dl, c.c_lo, c.K_lo));
+      if (ld == -INFINITY) d = -INFINITY;   // p_j = 0 (the two-sum of an infinite difference is NaN)
+    }
+    const float ex = exp2_fast(d);          // p_j / q_j
+    const float em1 = one_minus_exp2<PRECISE>(d, ex);
+    const bool pos = (eq > 0.f) && (d < 0.f);
+    const float res = pos ? eq * em1 : 0.f;
+    r = res;
+    if constexpr (MODE == kModeResidual) return res;
+    else if constexpr (MODE == kModeSaguaro) return pos ? eq * sqrtf(ex * em1) : 0.f;
+    else {   // p_j from its own exponential where q_j = 0 (eq ex would be 0 * inf)
+      const float pj = eq > 0.f ? eq * ex : exp2_fast(fmaf(ld, c.c_lo, fmaf(ld, c.c_hi, c.A_hi) + c.A_lo));
+      return sqrtf(pj * fmaxf(res, c.epsS));
+    }
+  }
+}
+
+template <int DT, int MODE, bool PRECISE>
+__device__ __forceinline__ void sample_weights(const float (&ld)[8], const float (&lt)[8],
+                                               const SampleCoef& c, float (&w)[8], float (&r)[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) w[e] = weight_one<DT, MODE, PRECISE>(ld[e], lt[e], c, r[e]);
+}
+
+// Call f with the weight mode as a compile-time constant.  EPS = false: code
+// that never sees the Saguaro eps > 0 mode (the fused kernel) leaves it out.
+template <bool EPS = true, class F>
+__device__ __forceinline__ void with_mode(int mode, F&& f) {
+  switch (mode) {
+    case kModeTarget: f(std::integral_constant<int, kModeTarget>{}); break;
+    case kModeResidual: f(std::integral_constant<int, kModeResidual>{}); break;
+    case kModeSaguaro: f(std::integral_constant<int, kModeSaguaro>{}); break;
+    default:
+      if constexpr (EPS) f(std::integral_constant<int, kModeSaguaroEps>{});
+      break;
+  }
+}
+
+// Rows of the draw: target row k and (on a rejection) draft row k.
+template <int DT>
+__device__ __forceinline__ void draw_rows(const VerifyArgs& a, int b, int k, const void*& drow,
+                                          const void*& trow) {
+  drow = row_ptr<DT>(a, b, k < a.gamma ? k : 0);
+  trow = row_ptr<DT>(a, b, a.gamma + k);
+}
+
+// Integer offset of a tile of target logits for the bonus draw (log2 units):
+// the ceiling of its largest logit times c_T; 0 for an all -inf tile.
+__device__ __forceinline__ float tile_offset(float bm, float c_hi) {
+  const float bl = bm * c_hi;
+  return bl > -1.0e30f ? ceilf(fminf(bl, 1.0e30f)) : 0.f;
+}
+
+// Tile sums of the weights over tiles [t0, t0 + N) (clipped to ntile): tw[i]
+// (fp64, identical in every thread) and, last, the residual total.  The loads
+// of G tiles are in flight together (all N for packed bf16 rows, whose raw
+// words take half the registers of floats).  In target mode (the bonus draw)
+// every tile gets its own integer offset mt[i] (its weights are
+// 2^(lt_j c_T - mt[i])), so no row normaliser is needed.
+template <int DT, bool VEC, int MODE, bool CUT = false, int N = kTilesPerItem>
+__device__ __forceinline__ void tile_sums(const VerifyArgs& a, int b, const SampleCoef& cf, int k,
+                                          int t0, double (&tw)[N + 1], float (&mt)[N], double* lds_d) {
+  constexpr int G = (DT == kBF16 && VEC) ? N : (N >= 2 ? 2 : 1);
+  static_assert(N % G == 0, "tile groups must divide the item");
+  const void *drow, *trow;
+  draw_rows<DT>(a, b, k, drow, trow);
+  const int64_t lane_off = (int64_t)threadIdx.x * kUnit;
+  float rs = 0.f;
+#pragma unroll
+  for (int g0 = 0; g0 < N; g0 += G) {
+    Raw8<DT, VEC> rd[G], rt[G];
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      const int t = t0 + g0 + i;
+      const int64_t j0 = t < a.ntile ? (int64_t)t * kTile + lane_off : (int64_t)a.V;
+      load_raw<DT, VEC, kSampleNT>(trow, j0, a.V, rt[i]);
+      if constexpr (MODE != kModeTarget) load_raw<DT, VEC, kSampleNT>(drow, j0, a.V, rd[i]);
+    }
+    float off[G];
+    if constexpr (MODE == kModeTarget) {
+#pragma unroll
+      for (int i = 0; i < G; ++i) {
+        float lt[8];
+        unpack<DT, VEC>(rt[i], lt);
+        cut8<CUT>(lt, cf.Lt);
+        float m = lt[0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) m = fmaxf(m, lt[e]);
+        off[i] = m;
+      }
+      block_max_n<G>(off, reinterpret_cast<float*>(lds_d));
+#pragma unroll
+      for (int i = 0; i < G; ++i) off[i] = tile_offset(off[i], cf.c_hi);
+    }
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      float ld[8], lt[8], w[8], r[8];
+      unpack<DT, VEC>(rt[i], lt);
+      cut8<CUT>(lt, cf.Lt);
+      if constexpr (MODE != kModeTarget) {
+        unpack<DT, VEC>(rd[i], ld);
+        cut8<CUT>(ld, cf.Ld);
+      }
+      SampleCoef c = cf;
+      if constexpr (MODE == kModeTarget) {
+        c.Mt = off[i];
+        mt[g0 + i] = off[i];
+      }
+      sample_weights<DT, MODE, false>(ld, lt, c, w, r);
+      float ws = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        ws += w[e];
+        if constexpr (MODE == kModeSaguaro || MODE == kModeSaguaroEps) rs += r[e];
+      }
+      if constexpr (MODE == kModeResidual) rs += ws;   // the residual-mass items read it
+      tw[g0 + i] = (double)ws;
+    }
+    if constexpr (G < N) __builtin_amdgcn_sched_barrier(0);   // keep the groups apart
+  }
+  tw[N] = (double)rs;
+  block_sum_n<N + 1>(tw, lds_d);
+}
+
+// A tile's slot value: the plain sum, or in target mode log2 of it with the
+// tile's offset added (-inf for an empty tile).
+__device__ __forceinline__ double tile_slot_value(int mode, double sum, float off) {
+  if (mode != kModeTarget) return sum;
+  return sum > 0.0 ? (double)off + log2(sum) : (sum == 0.0 ? -INFINITY : sum);
+}
+
+// eps * (residual mass) for Saguaro eps > 0, from the residual-mass items'
+// slots (waited for), summed in the same order by every reader.
+__device__ float eps_clamp(const VerifyArgs& a, int b, double* lds_d) {
+  double v = 0.0;
+  for (int i = threadIdx.x; i < a.nt; i += kThreads) v += slot_value(poll(a, a.mass + (int64_t)b * a.nt + i));
+  v = block_sum(v, lds_d);
+  return uni((float)(v * (double)a.eps));
+}
+
+// ---------------------------------------------------------------------------
+// Residual-mass and sampling items.
+
+template <int DT, bool VEC, bool CUT = false>
+__device__ void mass_item(const VerifyArgs& a, int b, int s, double* lds_d) {
+  const SeqRec rec = wait_rec<true>(a, b);
+  if (!rec.valid || rec.mode != kModeSaguaroEps) return;
+  double tw[kTilesPerItem + 1];
+  float mt[kTilesPerItem];
+  tile_sums<DT, VEC, kModeResidual, CUT>(a, b, coef_of<CUT>(a, b, rec, 0.f), rec.k, s * kTilesPerItem, tw, mt, lds_d);
+  if (threadIdx.x == 0) slot_put(a.mass + (int64_t)b * a.nt + s, tw[kTilesPerItem]);
+}
+
+template <int DT, bool VEC, bool CUT = false, bool EPS = true>
+__device__ void sample_item(const VerifyArgs& a, int b, int s, double* lds_d) {
+  const SeqRec rec = wait_rec<true>(a, b);
+  if (!rec.valid) return;
+  const int t0 = s * kTilesPerItem;
+  const float epsS = rec.mode == kModeSaguaroEps ? eps_clamp(a, b, lds_d) : 0.f;
+  const SampleCoef cf = coef_of<CUT>(a, b, rec, epsS);
+  with_mode<EPS>(rec.mode, [&](auto m) {
+    constexpr int MODE = decltype(m)::value;
+    double tw[kTilesPerItem + 1];
+    float mt[kTilesPerItem];
+    tile_sums<DT, VEC, MODE, CUT>(a, b, cf, rec.k, t0, tw, mt, lds_d);
+    if (threadIdx.x == 0) {
+#pragma unroll
+      for (int i = 0; i < kTilesPerItem; ++i)
+        if (t0 + i < a.ntile)
+          slot_put(a.tiles + (int64_t)b * a.ntile + t0 + i, tile_slot_value(MODE, tw[i], mt[i]));
+      if (MODE == kModeSaguaro) slot_put(a.rsum + (int64_t)b * a.nt + s, tw[kTilesPerItem]);
+    }
+  });
+}
+
+// ---------------------------------------------------------------------------
+// Draw item.
+
+struct DrawLds {
+  double lds_d[kWaves * (kTilesPerItem + 1)];
+  int lds_i[kWaves];
+  int tile, y, e;   // chosen tile, drawn token, tile units = 2^e draw units
+  double off, lane_off, lo, hi, Mp;
+  float w8[kUnit];
+};
+
+__device__ __forceinline__ double tile_value(const uint64_t* tiles, int t) {
+  return slot_value(ld_dev_u64(tiles + t));
+}
+
+// Target-mode tile values hold v_t = offset + log2(sum): replace each by the
+// sum in draw units, 2^(v_t - Mp) with Mp the integer ceiling of the largest
+// v_t, in place (the slots belong to the draw now).  Sets sh.Mp.
+__device__ void tiles_to_linear(uint64_t* tiles, int ntile, DrawLds& sh) {
+  const int tid = threadIdx.x;
+  float m = -INFINITY;   // an upper bound to within float rounding is all Mp needs
+  for (int t = tid; t < ntile; t += kThreads) m = fmaxf(m, (float)tile_value(tiles, t));
+  m = block_max(m, reinterpret_cast<float*>(sh.lds_d));
+  const double Mp = isfinite(m) ? ceil((double)m) + 1.0 : 0.0;
+  for (int t = tid; t < ntile; t += kThreads) {
+    const double v = tile_value(tiles, t);
+    slot_put(tiles + t, v > -INFINITY ? exp2(v - Mp) : 0.0);
+  }
+  if (tid == 0) sh.Mp = Mp;
+  wait_mem();
+  __syncthreads();
+}
+
+// Locate the tile holding u * S (S = sum of the tile values) by an fp64 scan
+// over the tile values in token order; returns S, sets sh.tile and sh.off.
+__device__ double locate_tile(const uint64_t* tiles, int ntile, double u, DrawLds& sh, double& target) {
+  const int tid = threadIdx.x;
+  if (tid == 0) sh.tile = -1;
+  double S = 0.0;
+  if (ntile <= kThreads) {   // one tile value per thread, loaded once
+    const double v = tid < ntile ? tile_value(tiles, tid) : 0.0;
+    double tot;
+    const double off = block_exclusive_scan(v, sh.lds_d, tot);
+    S = tot;
+    target = u * S;
+    const int hit = (tid < ntile && off <= target && target < off + v) ? tid : INT_MAX;
+    const int first = block_min_int(hit, sh.lds_i);
+    if (first != INT_MAX && tid == first) {
+      sh.tile = tid;
+      sh.off = off;
+    }
+  } else {
+    double v = 0.0;
+    for (int i = tid; i < ntile; i += kThreads) v += tile_value(tiles, i);
+    S = block_sum(v, sh.lds_d);
+    target = u * S;
+    double carry = 0.0;
+    for (int base = 0; base < ntile; base += kThreads) {
+      const int t = base + tid;
+      const double x = t < ntile ? tile_value(tiles, t) : 0.0;
+      double tot;
+      const double off = carry + block_exclusive_scan(x, sh.lds_d, tot);
+      const int hit = (t < ntile && off <= target && target < off + x) ? t : INT_MAX;
+      const int first = block_min_int(hit, sh.lds_i);
+      if (first != INT_MAX) {
+        if (t == first) {
+          sh.tile = t;
+          sh.off = off;
+        }
+        break;
+      }
+      carry += tot;
+    }
+  }
+  __syncthreads();
+  if (sh.tile < 0) {   // u * S at or past the last running sum (rounding): last nonzero tile
+    int last = -1;
+    for (int t = tid; t < ntile; t += kThreads)
+      if (tile_value(tiles, t) > 0.0) last = t;
+    last = -block_min_int(-last, sh.lds_i);
+    if (tid == 0) {
+      sh.tile = max(last, 0);
+      double off = 0.0;
+      for (int t = 0; t < last; ++t) off += tile_value(tiles, t);
+      sh.off = off;
+    }
+    __syncthreads();
+  }
+  return S;
+}
+
+// Rescan the chosen tile: the same weights and per-lane fp32 sums as its tile
+// sum, fp64 prefix over the lanes, in tile units (one tile unit is 2^e draw
+// units; e = 0 but for the bonus draw, where it is the tile's offset minus Mp).
+// The lane holding the target (else the last lane with weight) hands its
+// eight weights to thread 0, which walks them in fp64: y = the first token
+// with weight whose running sum passes the target (else the lane's last token
+// with weight).  Sets sh.y, sh.e, sh.lo = C_{y-1} and sh.hi = C_y (draw units).
+template <int DT, bool VEC, int MODE, bool CUT = false>
+__device__ void rescan_tile(const VerifyArgs& a, int b, int k, const SampleCoef& cf, double target,
+                            DrawLds& sh) {
+  const int tid = threadIdx.x;
+  const int tsel = sh.tile;
+  const void *drow, *trow;
+  draw_rows<DT>(a, b, k, drow, trow);
+  const int64_t j0 = (int64_t)tsel * kTile + (int64_t)tid * kUnit;
+  float w[8];
+  int e = 0;
+  {
+    Raw8<DT, VEC> rd, rt;
+    load_raw<DT, VEC>(trow, j0, a.V, rt);
+    if constexpr (MODE != kModeTarget) load_raw<DT, VEC>(drow, j0, a.V, rd);
+    float ld[8], lt[8], r[8];
+    unpack<DT, VEC>(rt, lt);
+    cut8<CUT>(lt, cf.Lt);
+    if constexpr (MODE != kModeTarget) {
+      unpack<DT, VEC>(rd, ld);
+      cut8<CUT>(ld, cf.Ld);
+    }
+    SampleCoef c = cf;
+    if (MODE == kModeTarget && k == a.gamma) {   // the bonus draw: the tile's own offset
+      float m[1] = {lt[0]};
+#pragma unroll
+      for (int i = 1; i < 8; ++i) m[0] = fmaxf(m[0], lt[i]);
+      block_max_n<1>(m, reinterpret_cast<float*>(sh.lds_d));
+      c.Mt = tile_offset(m[0], cf.c_hi);
+      e = (int)fmin(fmax((double)c.Mt - sh.Mp, -2000.0), 2000.0);
+    }
+    sample_weights<DT, MODE, false>(ld, lt, c, w, r);
+  }
+  float ws = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ws += w[i];
+  double tile_tot;
+  const double off = block_exclusive_scan((double)ws, sh.lds_d, tile_tot);
+  const double tgt = ldexp(target - sh.off, -e);   // in tile units
+  const int hit = (ws > 0.f && off <= tgt && tgt < off + (double)ws) ? tid : INT_MAX;
+  int owner = block_min_int(hit, sh.lds_i);
+  if (owner == INT_MAX) owner = -block_min_int(ws > 0.f ? -tid : 1, sh.lds_i);   // last lane with weight
+  if (tid == owner) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) sh.w8[i] = w[i];
+    sh.lane_off = off;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    sh.e = e;
+    if (owner < 0) {   // no weight in the tile (not reached: its tile value was positive)
+      sh.y = (int)min<int64_t>(a.V - 1, (int64_t)tsel * kTile + kTile - 1);
+      sh.lo = sh.hi = sh.off + ldexp(tile_tot, e);
+    } else {
+      double run = sh.lane_off;
+      int idx = -1, last = -1;
+      double lo_last = run, lo = run;
+      for (int i = 0; i < 8; ++i) {
+        const double we = (double)sh.w8[i];
+        if (we > 0.0) {
+          if (idx < 0 && tgt < run + we) {
+            idx = i;
+            lo = run;
+          }
+          last = i;
+          lo_last = run;
+        }
+        run += we;
+      }
+      if (idx < 0) {
+        idx = last;
+        lo = lo_last;
+      }
+      sh.y = (int)((int64_t)tsel * kTile + (int64_t)owner * kUnit + idx);
+      sh.lo = sh.off + ldexp(lo, e);
+      sh.hi = sh.off + ldexp(lo + (double)sh.w8[idx], e);
+    }
+  }
+  __syncthreads();
+}
+
+// pi(y)'s weight in draw units, with the precise residual (thread 0).
+template <int DT, bool CUT = false, bool EPS = true>
+__device__ double precise_weight(const VerifyArgs& a, int b, int k, int mode, const SampleCoef& cf, int y,
+                                 const DrawLds& sh) {
+  const void *drow, *trow;
+  draw_rows<DT>(a, b, k, drow, trow);
+  const float lt = cut1<CUT>(load_one<DT>(trow, y), cf.Lt);
+  const float ld = mode == kModeTarget ? 0.f : cut1<CUT>(load_one<DT>(drow, y), cf.Ld);
+  SampleCoef c = cf;
+  if (mode == kModeTarget && k == a.gamma) c.Mt = (float)(sh.Mp + sh.e);   // the tile's offset
+  float w = 0.f, r;
+  with_mode<EPS>(mode, [&](auto m) { w = weight_one<DT, decltype(m)::value, true>(ld, lt, c, r); });
+  return ldexp((double)w, sh.e);
+}
+
+// Recompute every tile sum of a sequence in `mode`, the residual or q_k (a
+// zero Saguaro normaliser falls back to the residual, a zero residual mass to
+// q_k, k < gamma, whose offset Mt is the record's; degenerate inputs only).
+// One logit at a time, with the weights and order the rescan uses, so its
+// per-lane fp32 sums match.
+template <int DT, bool CUT = false>
+__device__ void recompute_tiles(const VerifyArgs& a, int b, int k, int mode, const SampleCoef& cf,
+                                DrawLds& sh) {
+  uint64_t* tiles = a.tiles + (int64_t)b * a.ntile;
+  const void *drow, *trow;
+  draw_rows<DT>(a, b, k, drow, trow);
+  for (int t = 0; t < a.ntile; ++t) {
+    const int64_t j0 = (int64_t)t * kTile + (int64_t)threadIdx.x * kUnit;
+    float ws = 0.f;
+#pragma unroll 1
+    for (int e = 0; e < kUnit; ++e) {
+      const int64_t j = j0 + e;
+      float w = 0.f, rr;
+      if (j < a.V) {
+        const float lt = cut1<CUT>(load_one<DT>(trow, j), cf.Lt);
+        if (mode == kModeResidual)
+          w = weight_one<DT, kModeResidual, false>(cut1<CUT>(load_one<DT>(drow, j), cf.Ld), lt, cf, rr);
+        else w = weight_one<DT, kModeTarget, false>(0.f, lt, cf, rr);
+      }
+      ws += w;
+    }
+    const double tw = block_sum((double)ws, sh.lds_d);
+    if (threadIdx.x == 0) slot_put(tiles + t, tw);
+  }
+  if (threadIdx.x == 0) wait_mem();
+  __syncthreads();
+}
+
+// The drawn token of a sequence: the 64-bit word at byte 8 of its count line,
+// stored as a complement (0 = not drawn yet).
+__device__ __forceinline__ uint64_t* drawn_slot(const VerifyArgs& a, int b) {
+  return reinterpret_cast<uint64_t*>(a.flag + (int64_t)b * kFlagStride + 2);
+}
+
+// The draw at the stopping position: tile values, locate, rescan.  The token
+// goes to the sequence's drawn slot, the diagnostics out.  Clears the tile and
+// residual-sum slots once read.
+template <int DT, bool VEC, bool CUT = false, bool EPS = true>
+__device__ void draw_item(const VerifyArgs& a, int b, DrawLds& sh) {
+  const int tid = threadIdx.x;
+  const SeqRec rec = wait_rec<true>(a, b);
+  if (!rec.valid) return;
+  const int g = a.gamma, k = rec.k;
+  uint64_t* tiles = a.tiles + (int64_t)b * a.ntile;
+  const float epsS = rec.mode == kModeSaguaroEps ? eps_clamp(a, b, sh.lds_d) : 0.f;
+  const SampleCoef cf = coef_of<CUT>(a, b, rec, epsS);
+  int mode = rec.mode;
+  for (int t = tid; t < a.ntile; t += kThreads) (void)poll(a, tiles + t);
+  double rtot = 0.0;   // residual mass (relative to Mt) when it differs from the tile total
+  if (mode == kModeSaguaro || mode == kModeSaguaroEps) {
+    uint64_t* rs = (mode == kModeSaguaro ? a.rsum : a.mass) + (int64_t)b * a.nt;
+    for (int i = tid; i < a.nt; i += kThreads) rtot += slot_value(poll(a, rs + i));
+  }
+  rtot = uni(block_sum(rtot, sh.lds_d));   // also orders the polls before the reads below
+
+  const double u = (double)a.u_smp[(int64_t)b * (g + 1) + k];
+  double target = 0.0, S = 0.0;
+  if (tid == 0) sh.Mp = 0.0;
+  // A zero Saguaro normaliser falls back to the residual, a zero residual mass
+  // to q_k (degenerate inputs only); one pass per mode.
+  if (mode == kModeTarget) tiles_to_linear(tiles, a.ntile, sh);   // the bonus draw
+  for (;;) {
+    S = uni(locate_tile(tiles, a.ntile, u, sh, target));
+    target = uni(target);
+    if (mode == kModeResidual) rtot = S;
+    if (S > 0.0 || mode == kModeTarget) break;
+    mode = mode == kModeResidual ? kModeTarget : kModeResidual;
+    recompute_tiles<DT, CUT>(a, b, k, mode, cf, sh);
+  }
+  with_mode<EPS>(mode, [&](auto m) { rescan_tile<DT, VEC, decltype(m)::value, CUT>(a, b, k, cf, target, sh); });
+  if (tid == 0) {
+    const int y = sh.y;
+    if (a.diag.resid_mass) a.diag.resid_mass[b] = k < g ? rtot / rec.Zt : 0.0;
+    if (a.diag.token_prob) a.diag.token_prob[b] = precise_weight<DT, CUT, EPS>(a, b, k, mode, cf, y, sh) / S;
+    if (a.diag.cdf_lo) a.diag.cdf_lo[b] = sh.lo / S;
+    if (a.diag.cdf_hi) a.diag.cdf_hi[b] = sh.hi / S;
+    st_dev_u64(drawn_slot(a, b), ~(uint64_t)(uint32_t)y);
+  }
+  // Every tile and residual-sum slot of the sequence has been read.
+  __syncthreads();
+  for (int t = tid; t < a.ntile; t += kThreads) slot_clear(tiles + t);
+  if (rec.mode == kModeSaguaro)
+    for (int i = tid; i < a.nt; i += kThreads) slot_clear(a.rsum + (int64_t)b * a.nt + i);
+  if (rec.mode == kModeSaguaroEps)
+    for (int i = tid; i < a.nt; i += kThreads) slot_clear(a.mass + (int64_t)b * a.nt + i);
+}
+
+// ---------------------------------------------------------------------------
+// Final item: target row gamma, which only the bonus draw reads and which is
+// therefore streamed last, is checked, and the outputs are written.
+
+struct FinalLds {
+  int ok, y;
+};
+
+template <int DT>
+__device__ void final_item(const VerifyArgs& a, int b, FinalLds& sh) {
+  const int tid = threadIdx.x;
+  const int g = a.gamma, R = 2 * g + 1, r = 2 * g;
+  const SeqRec rec = wait_rec<false>(a, b);
+  if (tid < 16) {
+    double M, z;
+    float mr;
+    merge_row(a, b, r, tid, M, z, mr);
+    if (tid == 0) {
+      const bool ok = row_ok(M, z);
+      sh.ok = ok;
+      const bool read = !a.early || (rec.valid && rec.k == g);
+      if (ok && read && a.diag.row_max) a.diag.row_max[(int64_t)b * R + r] = (double)mr * temp_coef(a, b).invT;
+      if (ok && read && a.diag.row_logZ) a.diag.row_logZ[(int64_t)b * R + r] = M * 0.69314718055994530942 + log(z);
+      if (rec.valid) {
+        uint64_t* ys = drawn_slot(a, b);
+        sh.y = (int)(uint32_t)~poll(a, ys);
+        slot_clear(ys);
+      }
+    }
+  }
+  __syncthreads();
+  if (rec.valid) {   // an invalid decision wrote its outputs already
+    const int k = rec.k;
+    if (!sh.ok && (!a.early || k == g)) {   // early exit reads target row gamma only for the bonus
+      write_invalid(a, b, tid);
+    } else {
+      const int64_t orow = (int64_t)b * (g + 1);
+      if (tid <= g) {
+        int tok = -1;
+        if (tid < k) tok = a.tokens[(int64_t)b * g + tid];
+        else if (tid == k) tok = sh.y;
+        a.out_tokens[orow + tid] = tok;
+      }
+      if (tid == 0) {
+        a.out_acc[b] = k;
+        if (a.out_first_reject) a.out_first_reject[b] = k < g ? k : -1;
+        if (a.out_mask) a.out_mask[b] = rec.mask;
+        if (a.out_len) a.out_len[b] = (a.in_len ? a.in_len[b] : 0) + k + 1;
+      }
+    }
+  }
+  // Once every other item of the sequence is done with the decision record,
+  // clear it and the count.
+  if (tid == 0) {
+    unsigned* f = a.flag + (int64_t)b * kFlagStride;
+    const unsigned expect = (unsigned)a.nt * ((a.saguaro && a.eps > 0.f) ? 2u : 1u) + 1u;
+    unsigned polls = 0;
+    while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < expect &&
+           !give_up(a, polls)) {
+    }
+    if (a.early) {   // every position test has read the stop and progress words
+      while (ld_dev_u32(f + kTestsWord) < (unsigned)g && !give_up(a, polls)) {
+      }
+      slot_clear32(f + kStopWord);
+      slot_clear32(f + kProgWord);
+      slot_clear32(f + kTestsWord);
+    }
+    slot_clear32(f);
+    clear_rec(a.seq + b);
+  }
+}
+
+}  // namespace sv

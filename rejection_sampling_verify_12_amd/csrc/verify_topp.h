@@ -1,0 +1,775 @@
+// Top-p: each row's nucleus by radix selection (float32) or by counting (bfloat16).
+#pragma once
+#include "verify_kernels.h"
+
+namespace sv {
+
+// ---------------------------------------------------------------------------
+// Top-p: the nucleus threshold of every row by a radix selection over the
+// logits' order-preserving keys (16 bits for bfloat16, 32 for float32; 8 bits
+// a pass), each key weighted by its probability mass, from the highest key
+// down, until the mass reaches top_p.
+
+// The order-preserving key of a logit (+0.0 and -0.0 share one), in kb bits.
+template <int DT>
+__device__ __forceinline__ uint32_t logit_key(float v) {
+  uint32_t b = __float_as_uint(v);
+  if (b == 0x80000000u) b = 0u;
+  const uint32_t k = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return DT == kBF16 ? k >> 16 : k;
+}
+template <int DT>
+__device__ __forceinline__ float key_logit(uint32_t k) {
+  if constexpr (DT == kBF16) {
+    const uint32_t b = (k & 0x8000u) ? (k & 0x7FFFu) : (~k & 0xFFFFu);
+    return __uint_as_float(b << 16);
+  } else {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+  }
+}
+
+// One wave per row: the row's offset and normaliser from its pieces (left in
+// place for the decision), and the selection's start.
+__global__ __launch_bounds__(64) void topp_init_kernel(VerifyArgs a) {
+  const int64_t row = blockIdx.x;
+  const int lane = threadIdx.x;
+  const uint64_t* p = a.part + row * a.nc;
+  double M = -INFINITY;
+  for (int c = lane; c < a.nc; c += 64) M = fmax(M, slot_value(ld_dev_u64(p + c)));
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) M = fmax(M, __shfl_xor(M, o, 64));
+  M = ceil(M);
+  double z = 0.0;
+  for (int c = lane; c < a.nc; c += 64) {
+    const double v = slot_value(ld_dev_u64(p + c));
+    if (v != -INFINITY) z += exp2(v - M);
+  }
+  z = wave_sum(z);
+  if (lane == 0) {
+    TopPRow t;
+    t.M = M;
+    t.Z = z;
+    t.rem = (double)a.top_p * z;
+    t.above = 0.0;
+    t.P = 1.0;
+    t.prefix = 0u;
+    t.L = -INFINITY;
+    a.topp[row] = t;
+  }
+}
+
+// (row, chunk) items: the masses of the chunk's logits whose key matches the
+// selected prefix, by the pass's digit, into the row's histogram.  Each wave
+// has its own LDS histogram (fewer colliding atomics); a lane sums runs of
+// one digit before adding.  Loads: four units in flight per lane.
+template <int DT, bool VEC>
+__global__ __launch_bounds__(kThreads) void topp_hist_kernel(VerifyArgs a, int pass) {
+  __shared__ double h[kWaves][kDigits];
+  const int R = 2 * a.gamma + 1;
+  const int64_t id = blockIdx.x;
+  const int64_t row = id / a.nc;
+  const int c = (int)(id - row * a.nc);
+  const int b = (int)(row / R), r = (int)(row - (int64_t)b * R);
+  const TCoef tc = temp_coef(a, b);
+  const float Mf = (float)uni(a.topp[row].M);
+  const uint32_t prefix = (uint32_t)uni((int)a.topp[row].prefix);
+  constexpr int KB = DT == kBF16 ? 16 : 32;
+  const int shift = KB - 8 * (pass + 1);
+  const int wave = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < kWaves * kDigits; i += kThreads) (&h[0][0])[i] = 0.0;
+  __syncthreads();
+  const void* rp = row_ptr<DT>(a, b, r);
+  const int64_t begin = (int64_t)c * a.chunk;
+  const int64_t end = min<int64_t>(begin + a.chunk, a.V);
+  int cur = -1;
+  double acc = 0.0;
+  auto take = [&](const Raw8<DT, VEC>& raw, int64_t j) {
+    float v[8];
+    unpack<DT, VEC>(raw, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if (j + e >= end) continue;
+      const uint32_t key = logit_key<DT>(v[e]);
+      if (pass > 0 && (key >> (shift + 8)) != prefix) continue;
+      const int d = (int)((key >> shift) & 0xFFu);
+      const double m = (double)exp2_fast(fmaf(v[e], tc.c_lo, fmaf(v[e], tc.c_hi, -Mf)));
+      if (d != cur) {
+        if (cur >= 0) atomicAdd(&h[wave][cur], acc);
+        cur = d;
+        acc = 0.0;
+      }
+      acc += m;
+    }
+  };
+  constexpr int U = 4;
+  int64_t j = begin + (int64_t)threadIdx.x * kUnit;
+  for (; j + (U - 1) * (int64_t)kTile < end; j += U * (int64_t)kTile) {
+    Raw8<DT, VEC> raw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) load_raw<DT, VEC, true>(rp, j + u * (int64_t)kTile, end, raw[u]);
+#pragma unroll
+    for (int u = 0; u < U; ++u) take(raw[u], j + u * (int64_t)kTile);
+  }
+  for (; j < end; j += kTile) {
+    Raw8<DT, VEC> raw;
+    load_raw<DT, VEC, true>(rp, j, end, raw);
+    take(raw, j);
+  }
+  if (cur >= 0) atomicAdd(&h[wave][cur], acc);
+  __syncthreads();
+  double* g = a.hist + row * kDigits;
+  for (int i = threadIdx.x; i < kDigits; i += kThreads) {
+    double t = 0.0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) t += h[w][i];
+    if (t != 0.0) atomicAdd(g + i, t);
+  }
+}
+
+// One wave per row: the digit at which the mass from the top reaches the
+// remaining target; clears the histogram.  Lane l holds digits 4l..4l+3 and
+// a suffix sum over the lanes gives the mass above each lane's digits.  If
+// rounding left the target above the row's total, every digit is kept (the
+// lowest digit with mass is selected).  After the last pass, the threshold
+// logit and the nucleus mass.
+template <int DT>
+__global__ __launch_bounds__(64) void topp_select_kernel(VerifyArgs a, int pass, int npass) {
+  const int64_t row = blockIdx.x;
+  const int lane = threadIdx.x;
+  TopPRow t = a.topp[row];
+  double* g = a.hist + row * kDigits;
+  double m[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) m[q] = g[4 * lane + q];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) g[4 * lane + q] = 0.0;
+  const double mine = (m[0] + m[1]) + (m[2] + m[3]);
+  double incl = mine;   // inclusive suffix sum over the lanes (higher digits)
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const double x = __shfl_down(incl, o, 64);
+    if (lane + o < 64) incl += x;
+  }
+  const double above_lane = incl - mine;
+  // In this lane, from its highest digit down: the first that reaches the target.
+  int sel = -1;
+  double run = above_lane, hsel = 0.0, before = 0.0;
+#pragma unroll
+  for (int q = 3; q >= 0; --q) {
+    if (sel < 0 && m[q] > 0.0 && run + m[q] >= t.rem) {
+      sel = 4 * lane + q;
+      hsel = m[q];
+      before = run;
+    }
+    if (sel < 0) run += m[q];
+  }
+  // The lowest digit with mass in this lane, for the keep-everything case.
+  int low = -1;
+  double low_h = 0.0, low_before = 0.0;
+  {
+    double r2 = above_lane;
+#pragma unroll
+    for (int q = 3; q >= 0; --q) {
+      if (m[q] > 0.0) {
+        low = 4 * lane + q;
+        low_h = m[q];
+        low_before = r2;
+      }
+      r2 += m[q];
+    }
+  }
+  const uint64_t has = __ballot(sel >= 0);
+  const uint64_t haslow = __ballot(low >= 0);
+  int src, s_sel;
+  double s_h, s_before;
+  if (has) {   // the highest digit (lane) that reaches the target
+    src = 63 - __builtin_clzll(has);
+    s_sel = __shfl(sel, src, 64);
+    s_h = __shfl(hsel, src, 64);
+    s_before = __shfl(before, src, 64);
+  } else {     // keep everything down to the lowest digit with mass
+    src = haslow ? __builtin_ctzll(haslow) : 0;
+    s_sel = haslow ? __shfl(low, src, 64) : 0;
+    s_h = haslow ? __shfl(low_h, src, 64) : 0.0;
+    s_before = haslow ? __shfl(low_before, src, 64) : 0.0;
+  }
+  if (lane == 0) {
+    t.above += s_before;
+    t.rem -= s_before;
+    t.prefix = (t.prefix << 8) | (uint32_t)s_sel;
+    if (pass == npass - 1) {
+      t.L = key_logit<DT>(t.prefix);
+      t.P = (t.above + s_h) / t.Z;
+    }
+    a.topp[row] = t;
+  }
+}
+
+
+// Top-p of bfloat16 rows by counting.  A bfloat16 row holds at most 65536
+// distinct values and every logit of one value carries the same mass, so the
+// row's masses in value order follow exactly from how often each value
+// occurs.  One 1024-thread work-group per row:
+//   * counts the row's values by their 16-bit order-preserving keys in LDS,
+//     two 16-bit counters per 32-bit word: word w counts key w (a negative
+//     value) in its low half and key w + 32768 (a non-negative one) in its
+//     high half, so neighbouring values, which a row's logits crowd, fall in
+//     different words.  A counter wraps only where one value occurs 65536
+//     times or more; the counters then sum to less than V, and the row is
+//     counted again with returning atomics that record every wrap, so only
+//     such rows are read twice;
+//   * from the counts, from the top key down: the largest finite value (the
+//     row offset), the row normaliser in fp64, and the nucleus threshold (the
+//     first value at whose end the running mass reaches top_p times the
+//     normaliser; each value is one run of equal logits);
+//   * writes the row's normaliser piece (the whole row in piece 0, -inf in
+//     the others) and its maximum where the stream items would, so a cut
+//     bfloat16 row needs no stream items.
+constexpr int kCountThreads = 1024;
+constexpr int kCountWaves = kCountThreads / 64;
+constexpr int kCountWords = 32768;                                     // 128 KB of counters
+constexpr int kWordsPerThread = kCountWords / kCountThreads;           // 32
+// Wraps in a row of V logits: at most V / 65536 of low counters, plus
+// (V + those) / 65536 of high counters (each low wrap carries one into the
+// high counter of its word): at most 256 up to this row length.  Longer
+// bfloat16 rows take the radix selection.
+constexpr int64_t kCountMaxV = (int64_t)1 << 24;
+constexpr int kCountEvents = 288;
+constexpr uint32_t kKeyNegInf = 0x007Fu, kKeyNegZero = 0x7FFFu, kKeyPosZero = 0x8000u,
+                   kKeyPosInf = 0xFF80u;
+
+// The counted row's words with a count, compacted in ascending order (word,
+// low count | high count << 16) for the wave that finishes the row while the
+// next one is counted; a row with more takes the in-place finish.
+constexpr int kListCap = 3328;
+constexpr int kCountingWaves = kCountWaves - 1;
+constexpr int kCountingThreads = 64 * kCountingWaves;
+
+struct CountLds {
+  uint32_t cnt[kCountWords];
+  uint2 list[kListCap];
+  uint32_t ev[kCountEvents];   // keys whose counter wrapped (checked pass)
+  uint32_t nev;
+  uint32_t sum[kCountWaves], nzw[kCountWaves];
+  int kmax[kCountWaves], flags[kCountWaves];
+  double tot[2][kCountWaves];
+  int sel;
+  double P;
+};
+
+// The keys of the two bfloat16 logits in w (its halves), in the halves of
+// the result: a negative value's bits inverted, a non-negative value's sign
+// bit set.  -0 takes key 0x7FFF, next below +0's 0x8000; both are the value
+// zero and are merged when the counts are read.
+__device__ __forceinline__ uint32_t bf16_key_pair(uint32_t w) {
+  const uint32_t s = w & 0x80008000u;
+  return w ^ (0x80008000u | (s - (s >> 15)));
+}
+
+__device__ __forceinline__ void count_wrap(CountLds& sh, uint32_t k) {
+  const uint32_t e = __hip_atomic_fetch_add(&sh.nev, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  if (e < (uint32_t)kCountEvents) sh.ev[e] = k;
+}
+
+// CHECK: the atomic returns the old word, and a counter that was 0xFFFF has
+// wrapped (a low one carrying into the high one, which may wrap in turn).
+template <bool CHECK>
+__device__ __forceinline__ void count_key(CountLds& sh, uint32_t k) {
+  const uint32_t inc = (k >> 15) * 0xFFFFu + 1u;
+  uint32_t* w = sh.cnt + (k & 0x7FFFu);
+  if constexpr (!CHECK) {
+    __hip_atomic_fetch_add(w, inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  } else {
+    const uint32_t old = __hip_atomic_fetch_add(w, inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    const uint32_t lo = old & 0xFFFFu, hi = old >> 16;
+    if ((k >> 15) ? hi == 0xFFFFu : lo == 0xFFFFu) {
+      count_wrap(sh, k);
+      if (!(k >> 15) && hi == 0xFFFFu) count_wrap(sh, k + 32768u);
+    }
+  }
+}
+template <bool CHECK>
+__device__ __forceinline__ void count_pair(CountLds& sh, uint32_t w) {
+  const uint32_t kp = bf16_key_pair(w);
+  count_key<CHECK>(sh, kp & 0xFFFFu);
+  count_key<CHECK>(sh, kp >> 16);
+}
+
+// Every logit of the row, once, by threads 0 .. NT - 1.  Lane t takes
+// 8-logit units t, t + NT, ... (eight in flight; one in the rarely run
+// checked pass, whose code stays small), then one of the last V mod 8.
+template <bool VEC, bool CHECK, int NT>
+__device__ void count_row(const uint16_t* row, int64_t V, CountLds& sh) {
+  const int t = threadIdx.x;
+  const int64_t units = V >> 3;
+  int64_t u = t;
+  if constexpr (VEC) {
+    constexpr int U = CHECK ? 1 : 8;
+    constexpr int64_t kBatch = (int64_t)U * NT;
+    const __amdgpu_buffer_rsrc_t rs = chunk_rsrc(row, (int)(units * 16));
+    const int voff = t * 16;
+    const int64_t nb = units / kBatch;
+    for (int64_t i = 0; i < nb; ++i) {
+      u32x4 w[U];
+#pragma unroll
+      for (int q = 0; q < U; ++q)
+        w[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, (int)((i * kBatch + q * NT) * 16), 2);
+#pragma unroll
+      for (int q = 0; q < U; ++q) {
+        count_pair<CHECK>(sh, w[q].x);
+        count_pair<CHECK>(sh, w[q].y);
+        count_pair<CHECK>(sh, w[q].z);
+        count_pair<CHECK>(sh, w[q].w);
+      }
+    }
+    for (u = nb * kBatch + t; u < units; u += NT) {
+      const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, (int)((u - t) * 16), 2);
+      count_pair<CHECK>(sh, w.x);
+      count_pair<CHECK>(sh, w.y);
+      count_pair<CHECK>(sh, w.z);
+      count_pair<CHECK>(sh, w.w);
+    }
+  } else {
+    for (; u < units; u += NT) {
+#pragma unroll
+      for (int e = 0; e < 8; e += 2)
+        count_pair<CHECK>(sh, (uint32_t)row[u * 8 + e] | ((uint32_t)row[u * 8 + e + 1] << 16));
+    }
+  }
+  if (t < V - units * 8) count_key<CHECK>(sh, bf16_key_pair(row[units * 8 + t]) & 0xFFFFu);
+}
+
+__device__ __forceinline__ bool key_finite(uint32_t k) { return k > kKeyNegInf && k < kKeyPosInf; }
+// Flags of a key outside the finite range: 1 for a NaN, 2 for +inf, 0 for -inf.
+__device__ __forceinline__ int nonfinite_flag(uint32_t k) {
+  return k == kKeyNegInf ? 0 : (k == kKeyPosInf ? 2 : 1);
+}
+
+// The count of key k from its 16-bit counter and the recorded wraps: 65536
+// more per wrap of k, one less per carry into k (a wrap of the low counter
+// of k's word, when k is the high one).
+__device__ __forceinline__ uint32_t key_count(const CountLds& sh, int nev, uint32_t k) {
+  uint32_t h = (sh.cnt[k & 0x7FFFu] >> (16 * (k >> 15))) & 0xFFFFu;
+  for (int e = 0; e < nev; ++e) {
+    const uint32_t x = sh.ev[e];
+    if (x == k) h += 65536u;
+    else if ((k >> 15) && x == k - 32768u) h -= 1u;
+  }
+  return h;
+}
+
+// Inclusive suffix sum over the lanes of a wave (lane 63 first).
+template <typename F>
+__device__ __forceinline__ F wave_suffix_sum(F v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const F y = __shfl_down(v, o, 64);
+    if (lane + o < 64) v += y;
+  }
+  return v;
+}
+
+// A counted row's outputs: its normaliser piece (the whole row in piece 0,
+// -inf in the others) and maximum where the stream items would put them,
+// and its nucleus (threshold sel, mass fraction P; none for a bad row).
+// Threads tid = 0 .. nthr - 1.
+__device__ __forceinline__ void count_outputs(const VerifyArgs& a, int64_t row, int flags, int kmax, float mref,
+                                              double Z, int sel, double P, int tid, int nthr) {
+  const bool bad = flags != 0 || kmax < 0;
+  const float vmax = kmax >= 0 ? key_logit<kBF16>((uint32_t)kmax) : -INFINITY;
+  const int64_t p0 = row * a.nc;
+  for (int i = tid; i < a.nc; i += nthr) {
+    double v = -INFINITY;
+    float mr = -INFINITY;
+    if (i == 0) {
+      if (flags & 1) v = NAN;
+      else if (flags & 2) v = INFINITY;
+      else if (kmax >= 0) v = (double)mref + log2(Z);
+      mr = (flags & 2) ? INFINITY : vmax;
+    }
+    slot_put32(a.mraw + p0 + i, mr);
+    slot_put(a.part + p0 + i, v);
+  }
+  if (tid == 0) {
+    TopPRow tr;
+    tr.M = mref;
+    tr.Z = Z;
+    tr.rem = 0.0;
+    tr.above = 0.0;
+    const bool cut = !bad && sel >= 0;
+    tr.P = cut ? P : 1.0;
+    tr.prefix = cut ? (uint32_t)sel : 0u;
+    tr.L = cut ? key_logit<kBF16>((uint32_t)sel) : -INFINITY;
+    a.topp[row] = tr;
+  }
+}
+
+// The in-place finish of a counted row (every thread): wave w takes words
+// 2048w + 64j + lane (j = 0..31) in registers, consecutive words in
+// consecutive lanes, so a band of crowded values spreads over the lanes.
+// From the top key down the order is: the high halves (non-negative values)
+// of waves 15..0, then the low halves of waves 15..0; within a wave, rows
+// j = 31..0, lanes 63..0.  Leaves counts in the counters.
+template <bool VEC>
+__device__ void finish_inplace(const VerifyArgs& a, int64_t row, CountLds& sh) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int R = 2 * a.gamma + 1;
+  const int b = (int)(row / R), r = (int)(row - (int64_t)b * R);
+  const uint16_t* rp = static_cast<const uint16_t*>(row_ptr<kBF16>(a, b, r));
+  const TCoef tc = temp_coef(a, b);
+  uint4* c4 = reinterpret_cast<uint4*>(sh.cnt);
+
+  // Word of row j: wbase + 64 j (the opaque step keeps the compiler from
+  // precomputing every such address outside the caller's loop).
+  uint32_t wbase = 2048u * (uint32_t)wave + (uint32_t)lane;
+  asm volatile("" : "+v"(wbase));
+  // The counter words are read from LDS where used (rare path: registers
+  // stay free).
+  auto cw = [&](int j) -> uint32_t { return sh.cnt[wbase + 64u * j]; };
+  int nev = 0;
+  {   // the 16-bit counters sum to V unless one wrapped: then count again, recording the wraps
+    uint32_t sum = 0;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) sum += (cw(j) & 0xFFFFu) + (cw(j) >> 16);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 64);
+    if (lane == 0) sh.sum[wave] = sum;
+    __syncthreads();
+    sum = 0;
+    for (int i = 0; i < kCountWaves; ++i) sum += sh.sum[i];
+    if ((int64_t)sum != a.V) {
+      __syncthreads();   // every thread is done with the counters
+      for (int i = t; i < kCountWords / 4; i += kCountThreads) c4[i] = make_uint4(0u, 0u, 0u, 0u);
+      if (t == 0) sh.nev = 0u;
+      __syncthreads();
+      count_row<VEC, true, kCountThreads>(rp, a.V, sh);
+      __syncthreads();
+      nev = (int)min(sh.nev, (uint32_t)kCountEvents);
+    }
+  }
+  // The count of key half h of row j (with the recorded wraps, if any); -0
+  // counts with +0 (key 0x8000, the high half of word 0).
+  const uint32_t nzero = key_count(sh, nev, kKeyNegZero);
+  auto count_at = [&](int j, int h) -> uint32_t {
+    const uint32_t k = wbase + 64u * j + 32768u * h;
+    uint32_t n = nev ? key_count(sh, nev, k) : ((cw(j) >> (16 * h)) & 0xFFFFu);
+    return k == kKeyNegZero ? 0u : (k == kKeyPosZero ? n + nzero : n);
+  };
+
+  // The largest finite key with a count, and flags (1: a NaN, 2: +inf).
+  // Keys outside the finite range: the low halves of words 0..127 (wave 0,
+  // rows 0 and 1) and the high halves of words 32640..32767 (wave 15, rows
+  // 30 and 31).
+  int kmax = -1, flags = 0;
+  auto take = [&](uint32_t k, uint32_t n) {
+    const bool fin = key_finite(k);
+    kmax = (n != 0u && fin) ? max(kmax, (int)k) : kmax;
+    flags |= (n != 0u && !fin) ? nonfinite_flag(k) : 0;
+  };
+  if (nev == 0) {
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      uint32_t w = cw(j);
+      asm volatile("" : "+v"(w), "+v"(kmax), "+v"(flags));
+      const uint32_t k = wbase + 64u * j;
+      take(k, k == kKeyNegZero ? 0u : (w & 0xFFFFu));
+      take(k + 32768u, k == 0u ? (w >> 16) + nzero : (w >> 16));
+    }
+  } else {
+    for (uint32_t j = 0; j < 32u; ++j)
+      for (uint32_t h = 0; h < 2u; ++h) {
+        const uint32_t k = wbase + 64u * j + 32768u * h;
+        const uint32_t n = key_count(sh, nev, k);
+        take(k, k == kKeyNegZero ? 0u : (k == kKeyPosZero ? n + nzero : n));
+      }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    kmax = max(kmax, __shfl_xor(kmax, o, 64));
+    flags |= __shfl_xor(flags, o, 64);
+  }
+  if (lane == 0) {
+    sh.kmax[wave] = kmax;
+    sh.flags[wave] = flags;
+  }
+  __syncthreads();
+  for (int i = 0; i < kCountWaves; ++i) {
+    kmax = max(kmax, sh.kmax[i]);
+    flags |= sh.flags[i];
+  }
+
+  // Masses count * 2^(l c_T - mref) (0 for no count or a key outside the
+  // finite range): each wave's sums over its high and low halves, in fp64.
+  const bool bad = flags != 0 || kmax < 0;
+  const float vmax = kmax >= 0 ? key_logit<kBF16>((uint32_t)kmax) : -INFINITY;
+  const float mref = bad ? 0.f : ceilf(fminf(vmax * tc.c_hi, 1.0e30f));
+  auto mass = [&](uint32_t k, uint32_t n) -> float {
+    const float v = key_logit<kBF16>(k);
+    const float m = (float)n * exp2_fast(fmaf(v, tc.c_lo, fmaf(v, tc.c_hi, -mref)));
+    return (n != 0u && key_finite(k)) ? m : 0.f;
+  };
+  double cs[2] = {0.0, 0.0};
+  if (!bad) {
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      // One row at a time (the opaque step orders them): computing every
+      // term ahead of the additions would not fit the registers.
+      uint32_t w = cw(j);
+      asm volatile("" : "+v"(w), "+v"(cs[0]), "+v"(cs[1]));
+      if (w != 0u || nev != 0 || (t == 0 && j == 0)) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) cs[h] += (double)mass(wbase + 64u * j + 32768u * h, count_at(j, h));
+      }
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const double wt = wave_sum(cs[h]);
+    if (lane == 0) sh.tot[h][wave] = wt;
+  }
+  if (t == 0) sh.sel = -1;
+  __syncthreads();
+
+  // Running sums over the 32 (half, wave) blocks from the top, the same
+  // additions in the same order in every thread: Z, and the first block at
+  // whose end the sum reaches top_p * Z (ab: the sum before it).
+  double Z = 0.0;
+  for (int i = 2 * kCountWaves - 1; i >= 0; --i) Z = Z + sh.tot[i / kCountWaves][i % kCountWaves];
+  const double tgt = (double)a.top_p * Z;
+  double ab = 0.0;
+  int hx = -1, wx = -1;
+  {
+    double run = 0.0;
+    for (int i = 2 * kCountWaves - 1; i >= 0 && hx < 0; --i) {
+      const double bt = sh.tot[i / kCountWaves][i % kCountWaves], nx = run + bt;
+      if (bt > 0.0 && nx >= tgt) {
+        hx = i / kCountWaves;
+        wx = i % kCountWaves;
+        ab = run;
+      }
+      run = nx;
+    }
+  }
+  if (!bad && wave == wx) {
+    // The rows' sums of half hx over the lanes: a butterfly that halves the
+    // rows each lane carries at every step leaves row lane / 2 in lanes
+    // 2j and 2j + 1.
+    float m[32];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) m[j] = mass(wbase + 64u * j + 32768u * hx, count_at(j, hx));
+#pragma unroll
+    for (int step = 0; step < 5; ++step) {
+      const int half = 16 >> step, o = 32 >> step;
+      const bool up = (lane & o) != 0;
+#pragma unroll
+      for (int k = 0; k < half; ++k) {
+        const float send = up ? m[k] : m[k + half];
+        const float recv = __shfl_xor(send, o, 64);
+        m[k] = (up ? m[k + half] : m[k]) + recv;
+      }
+    }
+    const float rj = m[0] + __shfl_xor(m[0], 1, 64);   // row lane / 2
+    // Suffix sums over the rows (row 31 first): lane 2j holds rows >= j.
+    const double sj = wave_suffix_sum((lane & 1) ? 0.0 : (double)rj, lane);
+    const double incl = ab + sj;
+    const double nxt = __shfl_down(sj, 2, 64);
+    const double above = lane >= 62 ? ab : ab + nxt;
+    const uint64_t crossr = __ballot(!(lane & 1) && rj > 0.f && above < tgt && tgt <= incl);
+    const uint64_t hasr = __ballot(!(lane & 1) && rj > 0.f);
+    // The crossing row; rounding aside (the rows' sums and the block's
+    // differ in order), else the lowest row with mass.
+    const int jl = crossr ? (63 - __builtin_clzll(crossr)) : __builtin_ctzll(hasr);
+    const int jx = jl >> 1;
+    const double ab_row = __shfl(above, jl, 64);
+    // Keys of row jx, one per lane: the highest with mass whose running sum
+    // reaches the target ends the nucleus (else the lowest with mass).
+    const uint32_t k = wbase + 64u * (uint32_t)jx + 32768u * (uint32_t)hx;
+    uint32_t n = nev ? key_count(sh, nev, k) : ((sh.cnt[k & 0x7FFFu] >> (16 * hx)) & 0xFFFFu);
+    n = k == kKeyNegZero ? 0u : (k == kKeyPosZero ? n + nzero : n);
+    const float mk = mass(k, n);
+    const double run = wave_suffix_sum((double)mk, lane) + ab_row;
+    const uint64_t hit = __ballot(mk != 0.f && run >= tgt);
+    const uint64_t has = __ballot(mk != 0.f);
+    const int src = hit ? 63 - __builtin_clzll(hit) : __builtin_ctzll(has);
+    if (lane == src) {
+      sh.sel = (int)k;
+      sh.P = run / Z;
+    }
+  }
+  __syncthreads();
+  count_outputs(a, row, flags, kmax, mref, Z, sh.sel, sh.P, t, kCountThreads);
+}
+
+// The previous row's finish from its compacted words (one wave, while the
+// other waves count the next row).  Lane l takes a run of consecutive
+// entries; from the top key down the order is the high halves of entries
+// E-1..0, then the low halves of entries E-1..0.  -0 has been counted with
+// +0 already and no counter wrapped.
+__device__ void finish_list(const VerifyArgs& a, int64_t row, const CountLds& sh, int E) {
+  const int lane = threadIdx.x & 63;
+  const int R = 2 * a.gamma + 1;
+  const int b = (int)(row / R);
+  const TCoef tc = temp_coef(a, b);
+  const int per = (E + 63) >> 6;
+  const int e0 = min(lane * per, E), e1 = min(e0 + per, E);
+  int kmax = -1, flags = 0;
+  for (int e = e0; e < e1; ++e) {
+    const uint2 en = sh.list[e];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t k = en.x + 32768u * h, n = (en.y >> (16 * h)) & 0xFFFFu;
+      if (n == 0u) continue;
+      if (key_finite(k)) kmax = max(kmax, (int)k);
+      else flags |= nonfinite_flag(k);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    kmax = max(kmax, __shfl_xor(kmax, o, 64));
+    flags |= __shfl_xor(flags, o, 64);
+  }
+  const bool bad = flags != 0 || kmax < 0;
+  const float vmax = kmax >= 0 ? key_logit<kBF16>((uint32_t)kmax) : -INFINITY;
+  const float mref = bad ? 0.f : ceilf(fminf(vmax * tc.c_hi, 1.0e30f));
+  auto mass = [&](uint32_t k, uint32_t n) -> float {
+    const float v = key_logit<kBF16>(k);
+    const float m = (float)n * exp2_fast(fmaf(v, tc.c_lo, fmaf(v, tc.c_hi, -mref)));
+    return (n != 0u && key_finite(k)) ? m : 0.f;
+  };
+  double sm[2] = {0.0, 0.0};
+  if (!bad) {
+    for (int e = e0; e < e1; ++e) {
+      const uint2 en = sh.list[e];
+      sm[0] += (double)mass(en.x, en.y & 0xFFFFu);
+      sm[1] += (double)mass(en.x + 32768u, en.y >> 16);
+    }
+  }
+  // Suffix sums over the lanes, the high halves first; a lane's `above` is
+  // the next lane's `incl`, the same value, so the intervals tile (0, Z].
+  const double s1 = wave_suffix_sum(sm[1], lane), s0 = wave_suffix_sum(sm[0], lane);
+  const double H = __shfl(s1, 0, 64);
+  const double d1 = __shfl_down(s1, 1, 64), d0 = __shfl_down(s0, 1, 64);
+  const double incl1 = s1, above1 = lane == 63 ? 0.0 : d1;
+  const double incl0 = s0 + H, above0 = (lane == 63 ? 0.0 : d0) + H;
+  const double Z = __shfl(incl0, 0, 64);
+  const double tgt = (double)a.top_p * Z;
+  const bool c1 = !bad && above1 < tgt && tgt <= incl1, c0 = !bad && above0 < tgt && tgt <= incl0;
+  int sel = -1;
+  double P = 1.0;
+  if (c1 || c0) {   // this lane's entries hold the threshold: walk them from the top
+    const int h = c1 ? 1 : 0;
+    double run = c1 ? above1 : above0, Pl = run;
+    int low = -1;
+    for (int e = e1 - 1; e >= e0; --e) {
+      const uint2 en = sh.list[e];
+      const uint32_t k = en.x + 32768u * h;
+      const float m = mass(k, (en.y >> (16 * h)) & 0xFFFFu);
+      if (m == 0.f) continue;
+      run += (double)m;
+      low = (int)k;
+      Pl = run;
+      if (run >= tgt) break;
+    }
+    sel = low;
+    P = Pl / Z;
+  }
+  const uint64_t who = __ballot(sel >= 0);
+  if (who) {
+    const int src = __builtin_ctzll(who);
+    sel = __shfl(sel, src, 64);
+    P = __shfl(P, src, 64);
+  }
+  count_outputs(a, row, flags, kmax, mref, Z, sel, P, lane, 64);
+}
+
+// Persistent: work-group g counts rows g, g + G, ...  While waves 0..14
+// count a row, wave 15 finishes the row before it from its compacted words
+// (the counting is limited by LDS atomics, the finish by latency, so they
+// overlap).  After each row every thread compacts its words with a count
+// into the list and clears its counters; a row whose 16-bit counters
+// wrapped, or whose words do not fit the list, is finished in place.
+template <bool VEC>
+__global__ __launch_bounds__(kCountThreads) void topp_count_kernel(VerifyArgs a, int64_t nrows) {
+  __shared__ CountLds sh;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int R = 2 * a.gamma + 1;
+  uint4* c4 = reinterpret_cast<uint4*>(sh.cnt);
+  for (int i = t; i < kCountWords / 4; i += kCountThreads) c4[i] = make_uint4(0u, 0u, 0u, 0u);
+  __syncthreads();
+  int64_t prev = -1;
+  int E = 0;
+  for (int64_t row = blockIdx.x;; row += gridDim.x) {
+    const bool have = row < nrows;
+    if (wave < kCountingWaves) {
+      if (have) {
+        const int b = (int)(row / R), r = (int)(row - (int64_t)b * R);
+        count_row<VEC, false, kCountingThreads>(static_cast<const uint16_t*>(row_ptr<kBF16>(a, b, r)), a.V, sh);
+      }
+    } else if (prev >= 0) {
+      finish_list(a, prev, sh, E);
+    }
+    __syncthreads();
+    if (!have) break;
+
+    // Compaction.  -0 (the low half of word 32767) moves to +0 (the high
+    // half of word 0); the sum of the counters checks for a wrap.  Words
+    // are read from LDS as needed (registers stay free for the counting);
+    // word of row j: wbase + 64 j.
+    uint32_t wbase = 2048u * (uint32_t)wave + (uint32_t)lane;
+    asm volatile("" : "+v"(wbase));
+    const uint32_t nzero = sh.cnt[kKeyNegZero] & 0xFFFFu;
+    auto word = [&](int j) -> uint32_t {
+      uint32_t w = sh.cnt[wbase + 64u * j];
+      if (t == kCountThreads - 1 && j == 31) w &= 0xFFFF0000u;
+      if (t == 0 && j == 0) w += nzero << 16;   // checked against overflow below
+      return w;
+    };
+    uint32_t sum = 0, nzc = 0;
+    int over = t == 0 && (sh.cnt[0] >> 16) + nzero > 0xFFFFu;
+#pragma unroll 8
+    for (int j = 0; j < 32; ++j) {
+      const uint32_t w = sh.cnt[wbase + 64u * j];
+      sum += (w & 0xFFFFu) + (w >> 16);
+      nzc += (uint32_t)__popcll(__ballot(word(j) != 0u));
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 64);
+    over = __ballot(over) != 0;
+    if (lane == 0) {
+      sh.sum[wave] = sum;
+      sh.nzw[wave] = nzc;
+      sh.flags[wave] = over;
+    }
+    __syncthreads();
+    uint32_t tsum = 0, base = 0, tot = 0;
+    for (int i = 0; i < kCountWaves; ++i) {
+      tsum += sh.sum[i];
+      base += i < wave ? sh.nzw[i] : 0u;
+      tot += sh.nzw[i];
+      over |= sh.flags[i];
+    }
+    if ((int64_t)tsum == a.V && tot <= (uint32_t)kListCap && !over) {
+      // Each thread reads only its own words here (-0's counter was read
+      // before the barrier above), so it clears each once read.
+      const uint64_t lt = (1ull << lane) - 1ull;
+#pragma unroll 8
+      for (int j = 0; j < 32; ++j) {
+        const uint32_t w = word(j);
+        sh.cnt[wbase + 64u * j] = 0u;
+        const uint64_t bal = __ballot(w != 0u);
+        if (w != 0u) sh.list[base + (uint32_t)__popcll(bal & lt)] = make_uint2(wbase + 64u * j, w);
+        base += (uint32_t)__popcll(bal);
+      }
+      prev = row;
+      E = (int)tot;
+    } else {
+      finish_inplace<VEC>(a, row, sh);
+      __syncthreads();
+      for (int i = t; i < kCountWords / 4; i += kCountThreads) c4[i] = make_uint4(0u, 0u, 0u, 0u);
+      prev = -1;
+    }
+    __syncthreads();
+  }
+}
+
+}  // namespace sv
