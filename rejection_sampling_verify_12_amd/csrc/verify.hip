@@ -64,7 +64,7 @@ static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 struct Layout {
   int nc, chunk, ntile, nt;
   size_t err_off, part_off, mraw_off, seq_off, flag_off, tiles_off, mass_off, rsum_off, cpart_off,
-      topp_off, hist_off, total;
+      topp_off, hist_off, redo_off, total;
 };
 
 static bool sizes_ok(int B, int gamma, int V) {
@@ -103,6 +103,8 @@ static Layout layout(int B, int gamma, int V) {
   off += align256((size_t)B * R * sizeof(TopPRow));
   L.hist_off = off;
   off += align256((size_t)B * R * kDigits * sizeof(double));
+  L.redo_off = off;
+  off += align256(((size_t)B * R + 2) * sizeof(unsigned));
   L.total = B == 0 ? 0 : off;
   return L;
 }
@@ -246,8 +248,10 @@ static hipError_t launch_kernels_cut(const VerifyArgs& a, hipStream_t st) {
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((topp_count_kernel<VEC>), dim3(std::min<unsigned>(rows, (unsigned)std::max(ncu, 1))),
-                       dim3(kCountThreads), 0, st, a, (int64_t)rows);
+    const unsigned grid = std::min<unsigned>(rows, (unsigned)std::max(ncu, 1));
+    hipLaunchKernelGGL((topp_count_kernel<VEC>), dim3(grid), dim3(kCountThreads), 0, st, a, (int64_t)rows);
+    // Few work-groups: the rows it redoes are rare, and an empty pass is short.
+    hipLaunchKernelGGL((topp_redo_kernel<VEC>), dim3(std::min(grid, 32u)), dim3(kCountThreads), 0, st, a);
   } else {
     hipLaunchKernelGGL((stream_kernel<DT, VEC, SV_STREAM_UNROLL>), dim3(nstream), dim3(kThreads), 0, st, a);
     if constexpr (CUT) {   // the nucleus of every row by radix selection
@@ -348,9 +352,11 @@ static int verify_impl(const void* draft, const void* target, int dtype, const i
   a.top_p = top_p;
   a.topp = nullptr;
   a.hist = nullptr;
+  a.redo = nullptr;
   if (top_p < 1.f) {
     a.topp = reinterpret_cast<TopPRow*>(w + L.topp_off);
     a.hist = reinterpret_cast<double*>(w + L.hist_off);
+    a.redo = reinterpret_cast<unsigned*>(w + L.redo_off);
   }
 
   PredictArgs p;

@@ -165,6 +165,8 @@ struct VerifyArgs {
   const float* temps;   // [B] per-sequence temperatures, or NULL (c_hi, c_lo, cTd, invT for all)
   TopPRow* topp;        // [B][2*gamma+1] with a top-p cut, else NULL
   double* hist;         // [B][2*gamma+1][kDigits] radix histograms of the cut
+  unsigned* redo;       // [2 + B*(2*gamma+1)]: rows the counting kernel leaves to the in-place
+                        // finish (count, work-groups done, then row + 1 each)
   float top_p;
 };
 

@@ -687,7 +687,8 @@ __device__ void finish_list(const VerifyArgs& a, int64_t row, const CountLds& sh
 // (the counting is limited by LDS atomics, the finish by latency, so they
 // overlap).  After each row every thread compacts its words with a count
 // into the list and clears its counters; a row whose 16-bit counters
-// wrapped, or whose words do not fit the list, is finished in place.
+// wrapped, or whose words do not fit the list, is left to topp_redo_kernel
+// (keeping the in-place finish out of this kernel keeps its registers).
 template <bool VEC>
 __global__ __launch_bounds__(kCountThreads) void topp_count_kernel(VerifyArgs a, int64_t nrows) {
   __shared__ CountLds sh;
@@ -762,13 +763,47 @@ __global__ __launch_bounds__(kCountThreads) void topp_count_kernel(VerifyArgs a,
       }
       prev = row;
       E = (int)tot;
-    } else {
-      finish_inplace<VEC>(a, row, sh);
-      __syncthreads();
+    } else {   // left to topp_redo_kernel
+      if (t == 0) {
+        const unsigned i = __hip_atomic_fetch_add(a.redo, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(a.redo + 2 + i, (unsigned)row + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
       for (int i = t; i < kCountWords / 4; i += kCountThreads) c4[i] = make_uint4(0u, 0u, 0u, 0u);
       prev = -1;
     }
     __syncthreads();
+  }
+}
+
+// The rows the counting kernel left (16-bit counters that wrapped, or more
+// words with a count than its list holds), each counted again and finished
+// in place by a whole work-group.  Clears the list as it goes; the last
+// work-group to finish clears the two counters.  Launched after the
+// counting kernel on the same stream, so the list is complete.
+template <bool VEC>
+__global__ __launch_bounds__(kCountThreads) void topp_redo_kernel(VerifyArgs a) {
+  __shared__ CountLds sh;
+  const int t = threadIdx.x;
+  const unsigned n = __hip_atomic_load(a.redo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  uint4* c4 = reinterpret_cast<uint4*>(sh.cnt);
+  for (unsigned i = blockIdx.x; i < n; i += gridDim.x) {
+    const int64_t row = (int64_t)__hip_atomic_load(a.redo + 2 + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - 1;
+    for (int j = t; j < kCountWords / 4; j += kCountThreads) c4[j] = make_uint4(0u, 0u, 0u, 0u);
+    __syncthreads();
+    const int R = 2 * a.gamma + 1;
+    const int b = (int)(row / R), r = (int)(row - (int64_t)b * R);
+    count_row<VEC, false, kCountThreads>(static_cast<const uint16_t*>(row_ptr<kBF16>(a, b, r)), a.V, sh);
+    __syncthreads();
+    finish_inplace<VEC>(a, row, sh);
+    __syncthreads();
+    if (t == 0) __hip_atomic_store(a.redo + 2 + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (t == 0) {
+    const unsigned d = __hip_atomic_fetch_add(a.redo + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (d == gridDim.x - 1) {
+      __hip_atomic_store(a.redo, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.redo + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 }
 
