@@ -310,8 +310,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic_record(
                          args.workload, args.mode + ("_predict" if args.predict and not sep else "")
-                         + ("_early" if args.early else "")),
-                     "kernel": f"one {'spec_verify_greedy' if greedy else ('spec_verify_early' if args.early else 'spec_verify')} "
+                         + ("_early" if args.early else "") + ("_topp" if args.top_p else "")),
+                     "kernel": f"one {'spec_verify_greedy' if greedy else ('spec_verify_early' if args.early else ('spec_verify_ex' if args.top_p else 'spec_verify'))} "
                                "call (every kernel it launches), event-timed on its stream",
                      "bytes_alg": bytes_alg},
         "source_digest": source_digest(),
