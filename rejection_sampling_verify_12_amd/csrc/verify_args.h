@@ -166,7 +166,8 @@ struct VerifyArgs {
   TopPRow* topp;        // [B][2*gamma+1] with a top-p cut, else NULL
   double* hist;         // [B][2*gamma+1][kDigits] radix histograms of the cut
   unsigned* redo;       // [2 + B*(2*gamma+1)]: rows the counting kernel leaves to the in-place
-                        // finish (count, work-groups done, then row + 1 each)
+                        // finish (count, work-groups done, then row + 1 each, with a flag
+                        // where the row's counters wrapped)
   float top_p;
 };
 

@@ -209,15 +209,16 @@ __global__ __launch_bounds__(64) void topp_select_kernel(VerifyArgs a, int pass,
 // Top-p of bfloat16 rows by counting.  A bfloat16 row holds at most 65536
 // distinct values and every logit of one value carries the same mass, so the
 // row's masses in value order follow exactly from how often each value
-// occurs.  One 1024-thread work-group per row:
+// occurs.  For each row a 1024-thread work-group (all 128 KB of counters
+// fill its CU's LDS):
 //   * counts the row's values by their 16-bit order-preserving keys in LDS,
 //     two 16-bit counters per 32-bit word: word w counts key w (a negative
 //     value) in its low half and key w + 32768 (a non-negative one) in its
 //     high half, so neighbouring values, which a row's logits crowd, fall in
 //     different words.  A counter wraps only where one value occurs 65536
 //     times or more; the counters then sum to less than V, and the row is
-//     counted again with returning atomics that record every wrap, so only
-//     such rows are read twice;
+//     counted again (topp_redo_kernel) with returning atomics that record
+//     every wrap, so only such rows are read a second time;
 //   * from the counts, from the top key down: the largest finite value (the
 //     row offset), the row normaliser in fp64, and the nucleus threshold (the
 //     first value at whose end the running mass reaches top_p times the
@@ -231,8 +232,9 @@ constexpr int kCountWords = 32768;                                     // 128 KB
 constexpr int kWordsPerThread = kCountWords / kCountThreads;           // 32
 // Wraps in a row of V logits: at most V / 65536 of low counters, plus
 // (V + those) / 65536 of high counters (each low wrap carries one into the
-// high counter of its word): at most 256 up to this row length.  Longer
-// bfloat16 rows take the radix selection.
+// high counter of its word): at most 257 up to this row length, within the
+// kCountEvents the checked pass records.  Longer bfloat16 rows take the
+// radix selection.
 constexpr int64_t kCountMaxV = (int64_t)1 << 24;
 constexpr int kCountEvents = 288;
 constexpr uint32_t kKeyNegInf = 0x007Fu, kKeyNegZero = 0x7FFFu, kKeyPosZero = 0x8000u,
@@ -240,8 +242,9 @@ constexpr uint32_t kKeyNegInf = 0x007Fu, kKeyNegZero = 0x7FFFu, kKeyPosZero = 0x
 
 // The counted row's words with a count, compacted in ascending order (word,
 // low count | high count << 16) for the wave that finishes the row while the
-// next one is counted; a row with more takes the in-place finish.
+// next one is counted; a row with more is left to topp_redo_kernel.
 constexpr int kListCap = 3328;
+constexpr unsigned kRedoWrapped = 0x80000000u;   // a redo entry's flag: the row's counters wrapped
 constexpr int kCountingWaves = kCountWaves - 1;
 constexpr int kCountingThreads = 64 * kCountingWaves;
 
@@ -404,14 +407,17 @@ __device__ __forceinline__ void count_outputs(const VerifyArgs& a, int64_t row, 
   }
 }
 
-// The in-place finish of a counted row (every thread): wave w takes words
-// 2048w + 64j + lane (j = 0..31) in registers, consecutive words in
+// The in-place finish of a counted row (every thread; topp_redo_kernel):
+// wave w takes words 2048w + 64j + lane (j = 0..31), consecutive words in
 // consecutive lanes, so a band of crowded values spreads over the lanes.
 // From the top key down the order is: the high halves (non-negative values)
 // of waves 15..0, then the low halves of waves 15..0; within a wave, rows
-// j = 31..0, lanes 63..0.  Leaves counts in the counters.
+// j = 31..0, lanes 63..0.  checked: the counters come from the checked
+// pass (its wraps are recorded); otherwise, if they sum to less than V, the
+// row is counted again with the checked pass first.  Leaves counts in the
+// counters.
 template <bool VEC>
-__device__ void finish_inplace(const VerifyArgs& a, int64_t row, CountLds& sh) {
+__device__ void finish_inplace(const VerifyArgs& a, int64_t row, CountLds& sh, bool checked) {
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int R = 2 * a.gamma + 1;
   const int b = (int)(row / R), r = (int)(row - (int64_t)b * R);
@@ -426,8 +432,8 @@ __device__ void finish_inplace(const VerifyArgs& a, int64_t row, CountLds& sh) {
   // The counter words are read from LDS where used (rare path: registers
   // stay free).
   auto cw = [&](int j) -> uint32_t { return sh.cnt[wbase + 64u * j]; };
-  int nev = 0;
-  {   // the 16-bit counters sum to V unless one wrapped: then count again, recording the wraps
+  int nev = checked ? (int)min(sh.nev, (uint32_t)kCountEvents) : 0;
+  if (!checked) {   // the 16-bit counters sum to V unless one wrapped: then count again, recording the wraps
     uint32_t sum = 0;
 #pragma unroll
     for (int j = 0; j < 32; ++j) sum += (cw(j) & 0xFFFFu) + (cw(j) >> 16);
@@ -766,7 +772,9 @@ __global__ __launch_bounds__(kCountThreads) void topp_count_kernel(VerifyArgs a,
     } else {   // left to topp_redo_kernel
       if (t == 0) {
         const unsigned i = __hip_atomic_fetch_add(a.redo, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(a.redo + 2 + i, (unsigned)row + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const unsigned wrapped = (int64_t)tsum != a.V ? kRedoWrapped : 0u;
+        __hip_atomic_store(a.redo + 2 + i, ((unsigned)row + 1u) | wrapped, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
       }
       for (int i = t; i < kCountWords / 4; i += kCountThreads) c4[i] = make_uint4(0u, 0u, 0u, 0u);
       prev = -1;
@@ -776,8 +784,9 @@ __global__ __launch_bounds__(kCountThreads) void topp_count_kernel(VerifyArgs a,
 }
 
 // The rows the counting kernel left (16-bit counters that wrapped, or more
-// words with a count than its list holds), each counted again and finished
-// in place by a whole work-group.  Clears the list as it goes; the last
+// words with a count than its list holds), each counted again - with the
+// checked pass straight away where the counters wrapped - and finished in
+// place by a whole work-group.  Clears the list as it goes; the last
 // work-group to finish clears the two counters.  Launched after the
 // counting kernel on the same stream, so the list is complete.
 template <bool VEC>
@@ -787,14 +796,19 @@ __global__ __launch_bounds__(kCountThreads) void topp_redo_kernel(VerifyArgs a) 
   const unsigned n = __hip_atomic_load(a.redo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   uint4* c4 = reinterpret_cast<uint4*>(sh.cnt);
   for (unsigned i = blockIdx.x; i < n; i += gridDim.x) {
-    const int64_t row = (int64_t)__hip_atomic_load(a.redo + 2 + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - 1;
+    const unsigned e = __hip_atomic_load(a.redo + 2 + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int64_t row = (int64_t)(e & ~kRedoWrapped) - 1;
+    const bool wrapped = (e & kRedoWrapped) != 0u;
     for (int j = t; j < kCountWords / 4; j += kCountThreads) c4[j] = make_uint4(0u, 0u, 0u, 0u);
+    if (t == 0) sh.nev = 0u;
     __syncthreads();
     const int R = 2 * a.gamma + 1;
     const int b = (int)(row / R), r = (int)(row - (int64_t)b * R);
-    count_row<VEC, false, kCountThreads>(static_cast<const uint16_t*>(row_ptr<kBF16>(a, b, r)), a.V, sh);
+    const uint16_t* rp = static_cast<const uint16_t*>(row_ptr<kBF16>(a, b, r));
+    if (wrapped) count_row<VEC, true, kCountThreads>(rp, a.V, sh);   // record the wraps at once
+    else count_row<VEC, false, kCountThreads>(rp, a.V, sh);
     __syncthreads();
-    finish_inplace<VEC>(a, row, sh);
+    finish_inplace<VEC>(a, row, sh, wrapped);
     __syncthreads();
     if (t == 0) __hip_atomic_store(a.redo + 2 + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
