@@ -189,6 +189,15 @@ class SeqResult:
     token_prob: float             # pi(y)
     cdf_lo: float                 # C_{y-1}
     cdf_hi: float                 # C_y
+    zero_margin: float = np.inf   # S at a rejection with S > 0 (its distance from the S = 0 fallback)
+
+
+def _zero_margin(S: float, k: int, gamma: int) -> float:
+    """Distance of a rejection's residual mass S from the S = 0 fallback
+    (reading C7: S = 0 draws from q_k).  S is the total-variation distance of
+    p_k and q_k; a residual that small is within float rounding of zero, so
+    the draw is a boundary case like a u within rounding of a running sum."""
+    return S if (k < gamma and S > 0.0) else np.inf
 
 
 def _invalid(gamma: int, in_len: int) -> SeqResult:
@@ -274,7 +283,7 @@ def verify_one(draft64, target64, tokens, u_accept, u_sample, T, mode="residual"
         valid=True, accepted=k, first_reject=k if k < gamma else -1, mask=mask,
         tokens=out, out_len=int(in_len) + k + 1, a=a,
         acc_margin=np.minimum(np.abs(ua - a), topp_margin),
-        sample_margin=min(us - lo, hi - us, topp_margin),
+        sample_margin=min(us - lo, hi - us, topp_margin), zero_margin=_zero_margin(S, k, gamma),
         row_max=np.concatenate([pm, qm]), row_logZ=np.concatenate([plz, qlz]),
         px=px, qx=qx, resid_mass=S, token_prob=float(pi[y]), cdf_lo=lo, cdf_hi=hi)
 
@@ -346,7 +355,8 @@ def verify_early_one(draft64, target64, tokens, u_accept, u_sample, T, mode="res
     return SeqResult(
         valid=True, accepted=k, first_reject=k if k < gamma else -1, mask=(1 << k) - 1,
         tokens=out, out_len=int(in_len) + k + 1, a=a, acc_margin=np.abs(ua - a),
-        sample_margin=min(us - lo, hi - us), row_max=row_max, row_logZ=row_logZ,
+        sample_margin=min(us - lo, hi - us), zero_margin=_zero_margin(S, k, gamma), row_max=row_max,
+        row_logZ=row_logZ,
         px=px, qx=qx, resid_mass=S, token_prob=float(pi[y]), cdf_lo=lo, cdf_hi=hi)
 
 

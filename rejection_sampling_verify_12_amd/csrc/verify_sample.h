@@ -537,12 +537,24 @@ __device__ void draw_item(const VerifyArgs& a, int b, DrawLds& sh) {
   double target = 0.0, S = 0.0;
   if (tid == 0) sh.Mp = 0.0;
   // A zero Saguaro normaliser falls back to the residual, a zero residual mass
-  // to q_k (degenerate inputs only); one pass per mode.
-  if (mode == kModeTarget) tiles_to_linear(tiles, a.ntile, sh);   // the bonus draw
+  // to q_k; one pass per mode.  The residual counts as zero below 2^-21 of
+  // q_k's mass (rec.Zt, draw units): where p_k and q_k agree, the fp32
+  // weights leave only rounding (a few ulp of q_k), below that.  A top-p cut
+  // can make both the same one-token distribution; otherwise only degenerate
+  // inputs get here.
+  const double zero_res = 0x1p-21 * rec.Zt;
+  if ((mode == kModeSaguaro || mode == kModeSaguaroEps) && rtot <= zero_res) {
+    mode = kModeTarget;
+    recompute_tiles<DT, CUT>(a, b, k, mode, cf, sh);
+  }
+  if (mode == kModeTarget && k == g) tiles_to_linear(tiles, a.ntile, sh);   // the bonus draw
   for (;;) {
     S = uni(locate_tile(tiles, a.ntile, u, sh, target));
     target = uni(target);
-    if (mode == kModeResidual) rtot = S;
+    if (mode == kModeResidual) {
+      rtot = S;
+      if (S <= zero_res) S = 0.0;
+    }
     if (S > 0.0 || mode == kModeTarget) break;
     mode = mode == kModeResidual ? kModeTarget : kModeResidual;
     recompute_tiles<DT, CUT>(a, b, k, mode, cf, sh);

@@ -153,7 +153,11 @@ def compare(batch: W.Batch, gpu: dict, ref: dict, check_diag: bool = True) -> Re
             continue
         gm = int(gpu["mask"][b])
         rep.n_draws += g + 1
-        rep.boundary_draws += int((r.acc_margin < EXCUSE).sum()) + int(r.sample_margin < EXCUSE)
+        # A draw is a boundary case when u is within rounding of a running sum,
+        # or when the residual mass is within rounding of the S = 0 fallback.
+        zero_boundary = getattr(r, "zero_margin", np.inf) < EXCUSE
+        draw_boundary = r.sample_margin < EXCUSE or zero_boundary
+        rep.boundary_draws += int((r.acc_margin < EXCUSE).sum()) + int(draw_boundary)
         excused = False
         for i in range(g):
             if ((gm >> i) & 1) != ((r.mask >> i) & 1):
@@ -173,7 +177,7 @@ def compare(batch: W.Batch, gpu: dict, ref: dict, check_diag: bool = True) -> Re
         k = gk
         exp_tokens = r.tokens.copy()
         if int(gt[k]) != int(exp_tokens[k]):
-            if r.sample_margin < EXCUSE:
+            if draw_boundary:
                 rep.excused += 1
                 continue
             rep.failures.append(f"seq {b}: token gpu {int(gt[k])} vs oracle {int(exp_tokens[k])} "
@@ -203,6 +207,8 @@ def compare(batch: W.Batch, gpu: dict, ref: dict, check_diag: bool = True) -> Re
             rm = np.abs(d["row_max"][b] - r.row_max)
             if (rm > 1e-6 * np.maximum(1, np.abs(r.row_max))).any():
                 rep.failures.append(f"seq {b}: row_max err {rm.max():.3g}")
+            if zero_boundary:   # the GPU may have drawn from q_k: the draw's diagnostics differ
+                continue
             if r.resid_mass > 0 and _rel(d["resid_mass"][b], r.resid_mass) > PROB_RTOL:
                 rep.failures.append(f"seq {b}: resid_mass {d['resid_mass'][b]} vs {r.resid_mass}")
             # pi(y) relative to 1e-5 above 1e-4; below, absolute 1e-9 (the fp32 residual's

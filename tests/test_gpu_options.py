@@ -213,3 +213,49 @@ def test_top_p_counted_rows(V, top_p, mode, eps):
     rep = H.compare(batch, gpu, ref)
     H.say(f"[options]   {rep}")
     rep.check()
+
+
+@pytest.mark.parametrize("V", [1, 5, 9, 1000, 2049])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_top_p_small_vocabularies(V, dtype):
+    """Rows shorter than one 8-logit unit per thread, a single token, and
+    lengths that leave a partial unit."""
+    batch = random_batch(6, 3, V, dtype, 1.0, seed=6500 + V, scale=2.0, sigma=0.4)
+    for top_p in (0.5, 0.9):
+        gpu = run_ex(batch, 1.0, top_p=top_p)
+        ref = oracle_per_seq(batch, np.full(batch.B, 1.0), top_p=top_p)
+        rep = H.compare(batch, gpu, ref)
+        H.say(f"[options]   {rep}")
+        rep.check()
+
+
+@pytest.mark.parametrize("mode,eps", [("residual", 0.0), ("saguaro", 0.0), ("saguaro", 1e-8)])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_top_p_equal_one_token_nuclei(mode, eps, dtype):
+    """Both rows' nuclei are the same single token and the draft tokens lie
+    outside them: every position rejects with a zero residual, and the draw
+    falls back to the cut target, that token (the oracle pins the closed
+    form).  The GPU's fp32 residual is rounding noise here and must count as
+    zero."""
+    B, g, V = 8, 3, 4099
+    rng = W.philox(6600, 1)
+    d64 = rng.standard_normal((B, g + 1, V)) * 0.5 - 4.0
+    t64 = rng.standard_normal((B, g + 1, V)) * 0.5 - 4.0
+    hot = rng.integers(0, V, B)
+    for b in range(B):
+        d64[b, :, hot[b]] = 6.0 + 0.1 * b
+        t64[b, :, hot[b]] = 5.0 + 0.2 * b
+    x = np.array([[(hot[b] + 1 + i) % V for i in range(g)] for b in range(B)], np.int32)
+    batch = W.Batch(name=f"onehot_{dtype}", B=B, gamma=g, V=V, T=1.0, dtype=dtype,
+                    draft=W.encode(d64, dtype), target=W.encode(t64, dtype), draft_tokens=x,
+                    u_accept=W.uniforms24(W.philox(6600, 2), (B, g)),
+                    u_sample=W.uniforms24(W.philox(6600, 3), (B, g + 1)),
+                    in_len=np.zeros(B, np.int32), seed=6600)
+    gpu = run_ex(batch, 1.0, mode, eps, top_p=0.5)
+    ref = oracle_per_seq(batch, np.full(B, 1.0), mode, eps, top_p=0.5)
+    assert all(ref[b].accepted == 0 and ref[b].tokens[0] == hot[b] and ref[b].resid_mass == 0.0
+               for b in range(B))
+    rep = H.compare(batch, gpu, ref)
+    H.say(f"[options]   {rep}")
+    rep.check()
+    assert rep.excused == 0

@@ -166,6 +166,7 @@ def test_accept_threshold_on_toy():
     assert r.out_len == 11
     assert abs(r.cdf_lo - 0.6) < 1e-14 and abs(r.cdf_hi - 0.8) < 1e-14
     assert abs(r.sample_margin - 0.1) < 1e-12
+    assert abs(r.zero_margin - 0.05) < 1e-15   # the residual mass: far from the S = 0 fallback
 
 
 def test_special_cases():
@@ -673,3 +674,19 @@ def test_top_p_rule_emits_the_cut_target_distribution():
     nz = q_cut > 0
     chi = scipy.stats.chisquare(counts[nz], q_cut[nz] * n)
     assert chi.pvalue > 1e-3, (counts / n, q_cut)
+
+
+def test_top_p_equal_one_token_nuclei_fall_back_to_q():
+    """Closed form: both rows' nuclei are the same single token t and the draft
+    token lies outside them, so p'(x) = q'(x) = 0 rejects (reading 3), the
+    residual (q' - p')+ is zero, and the draw falls back to q' = one-hot(t)
+    (reading C7) whatever u is."""
+    V, t = 9, 4
+    d = np.full((2, V), -3.0)
+    q = np.full((2, V), -2.0)
+    d[:, t] = 4.0     # p(t) = e^7 / (e^7 + 8) ~ 0.993 > top_p
+    q[:, t] = 3.0
+    for us in (0.0, 0.5, 0.999):
+        r = O.verify_one(d, q, [1], [0.3], [us, 0.0], 1.0, top_p=0.9)
+        assert r.accepted == 0 and r.tokens.tolist() == [t, -1]
+        assert r.resid_mass == 0.0 and r.token_prob == 1.0 and r.zero_margin == np.inf
