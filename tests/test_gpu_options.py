@@ -259,3 +259,30 @@ def test_top_p_equal_one_token_nuclei(mode, eps, dtype):
     H.say(f"[options]   {rep}")
     rep.check()
     assert rep.excused == 0
+
+
+@pytest.mark.parametrize("top_p", [1e-6, 0.99999994])   # the largest float below 1
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_top_p_extremes(top_p, dtype):
+    """A nucleus of the top value (and its ties) alone, and one that keeps
+    all but a sliver of the mass."""
+    batch = random_batch(8, 4, 20000, dtype, 1.0, seed=6700, scale=2.0, sigma=0.4)
+    gpu = run_ex(batch, 1.0, top_p=top_p)
+    ref = oracle_per_seq(batch, np.full(batch.B, 1.0), top_p=top_p)
+    rep = H.compare(batch, gpu, ref)
+    H.say(f"[options]   {rep}")
+    rep.check()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_top_p_with_per_sequence_temperatures(dtype):
+    """Temperatures from 0.25 to 3 and invalid ones (0, -1, NaN, +inf: only
+    their sequence is invalid) under a top-p cut."""
+    batch = random_batch(len(TEMPS), 4, 50000, dtype, 1.0, seed=6701)
+    temps = np.array(TEMPS, np.float32)
+    gpu = run_ex(batch, temps, top_p=0.8)
+    ref = oracle_per_seq(batch, temps, top_p=0.8)
+    assert [ref[b].valid for b in range(batch.B)] == [bool(np.isfinite(t) and t > 0) for t in temps]
+    rep = H.compare(batch, gpu, ref)
+    H.say(f"[options]   {rep}")
+    rep.check()
