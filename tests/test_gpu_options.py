@@ -286,3 +286,20 @@ def test_top_p_with_per_sequence_temperatures(dtype):
     rep = H.compare(batch, gpu, ref)
     H.say(f"[options]   {rep}")
     rep.check()
+
+
+@pytest.mark.parametrize("V", [1 << 24, (1 << 24) + 8])
+def test_top_p_longest_rows(V):
+    """bfloat16 rows at the counting path's longest (2^24 logits: its hot
+    values occur well over 65536 times, so the counters wrap) and just past
+    it (the radix selection takes over)."""
+    batch = random_batch(1, 1, V, "bf16", 1.0, seed=6800 + V % 7, scale=2.0, sigma=0.4)
+    d, t = batch.draft.copy(), batch.target.copy()
+    d[..., ::50] = np.uint16(0xBF80)   # -1.0, 335545 times a row
+    t[..., ::40] = np.uint16(0xBFC0)   # -1.5
+    batch = W.Batch(**{**batch.__dict__, "draft": d, "target": t, "name": f"long_V{V}"})
+    gpu = run_ex(batch, 1.0, top_p=0.9)
+    ref = oracle_per_seq(batch, np.full(batch.B, 1.0), top_p=0.9)
+    rep = H.compare(batch, gpu, ref)
+    H.say(f"[options]   {rep}")
+    rep.check()
