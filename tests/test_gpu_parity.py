@@ -289,11 +289,13 @@ def test_verify_predict_workload(mode, eps):
     H.say(f"[verify_predict] hit rate {got['hit'].mean():.3f}")
 
 
-@pytest.mark.parametrize("V", [50000, 50001, 2048 * 3 + 8])
+@pytest.mark.parametrize("V", [50000, 50001, 2048 * 3 + 8, 8, 16, 2])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_verify_predict_ragged(V, dtype):
-    """Partial last chunks and partial lane periods (V = 50000, 6152), and a V
-    the packed path cannot take (50001)."""
+    """Partial last chunks and partial lane periods (V = 50000, 6152), a V
+    the packed path cannot take (50001), the smallest rows the single kernel
+    takes (8, 16: one lane holds the whole row) and fewer tokens than
+    candidates (2)."""
     batch = random_batch(5, 3, V, dtype, 1.0, seed=4100 + V % 97)
     _check_verify_predict(batch, _verify_predict(batch))
 
