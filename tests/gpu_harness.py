@@ -156,7 +156,10 @@ def compare(batch: W.Batch, gpu: dict, ref: dict, check_diag: bool = True) -> Re
         # A draw is a boundary case when u is within rounding of a running sum,
         # or when the residual mass is within rounding of the S = 0 fallback.
         zero_boundary = getattr(r, "zero_margin", np.inf) < EXCUSE
-        draw_boundary = r.sample_margin < EXCUSE or zero_boundary
+        # A residual draw compares u * S with the unnormalised running sums
+        # (reading C6), so its distances are measured in those units.
+        scale = getattr(r, "draw_scale", 1.0)
+        draw_boundary = r.sample_margin * scale < EXCUSE or zero_boundary
         rep.boundary_draws += int((r.acc_margin < EXCUSE).sum()) + int(draw_boundary)
         excused = False
         for i in range(g):
@@ -217,7 +220,7 @@ def compare(batch: W.Batch, gpu: dict, ref: dict, check_diag: bool = True) -> Re
             rep.max_token_prob_abs = max(rep.max_token_prob_abs, tp_err)
             if tp_err > (PROB_RTOL * r.token_prob if r.token_prob >= 1e-4 else 1e-9):
                 rep.failures.append(f"seq {b}: token_prob {d['token_prob'][b]} vs {r.token_prob}")
-            ce = max(abs(d["cdf_lo"][b] - r.cdf_lo), abs(d["cdf_hi"][b] - r.cdf_hi))
+            ce = max(abs(d["cdf_lo"][b] - r.cdf_lo), abs(d["cdf_hi"][b] - r.cdf_hi)) * scale
             rep.max_cdf_err = max(rep.max_cdf_err, ce)
             if ce > EXCUSE:
                 rep.failures.append(f"seq {b}: running-sum error {ce:.3g}")

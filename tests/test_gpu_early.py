@@ -47,7 +47,7 @@ def test_early_equals_full_verification_outputs():
     np.testing.assert_array_equal(e["mask"], f["mask"] & ((np.uint64(1) << k) - np.uint64(1)))
 
 
-@pytest.mark.parametrize("V", [50000, 50001, 2048 * 3 + 8, 7])
+@pytest.mark.parametrize("V", [50000, 50001, 2048 * 3 + 8, 7, 8, 1])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_early_ragged(V, dtype):
     batch = random_batch(6, 5, V, dtype, 0.9, seed=5200 + V % 89)
