@@ -303,3 +303,18 @@ def test_top_p_longest_rows(V):
     rep = H.compare(batch, gpu, ref)
     H.say(f"[options]   {rep}")
     rep.check()
+
+
+@pytest.mark.parametrize("V", [2, 8, 33])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("mode,eps", [("residual", 0.0), ("saguaro", 1e-8)])
+def test_top_p_small_peaked_rows(V, dtype, mode, eps):
+    """Few tokens with one dominant under a cut: one-token nuclei, zero and
+    small residuals."""
+    batch = random_batch(24, 4, V, dtype, 1.0, seed=7400 + V, scale=6.0, sigma=0.3)
+    for top_p in (0.3, 0.7):
+        gpu = run_ex(batch, 1.0, mode, eps, top_p=top_p)
+        ref = oracle_per_seq(batch, np.full(batch.B, 1.0), mode, eps, top_p=top_p)
+        rep = H.compare(batch, gpu, ref)
+        H.say(f"[options]   {rep}")
+        rep.check()

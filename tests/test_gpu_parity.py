@@ -345,3 +345,16 @@ def test_saguaro_eps_where_the_target_has_zero_probability():
         rep = H.parity(batch, "saguaro", 1e-3)
         rep.check()
         assert rep.n_draws > 0
+
+
+# --------------------------------------------------------------------------- small, peaked rows
+
+@pytest.mark.parametrize("V", [2, 3, 8, 16, 33])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("mode,eps", [("residual", 0.0), ("saguaro", 0.0), ("saguaro", 1e-8)])
+def test_small_peaked_rows(V, dtype, mode, eps):
+    """Few tokens with one dominant: residual masses are small next to q_j,
+    the regime where fp32 rounding weighs most."""
+    batch = random_batch(24, 4, V, dtype, 1.0, seed=7300 + V, scale=6.0, sigma=0.3)
+    H.parity(batch, mode, eps).check()
+    H.parity(batch, mode, eps, early=True).check()
