@@ -268,7 +268,8 @@ static hipError_t launch_kernels_cut(const VerifyArgs& a, hipStream_t st) {
   else
     hipLaunchKernelGGL((decide_kernel<DT, CUT>), dim3((unsigned)a.B), dim3(kThreads), 0, st, a);
   if (eps_mode) hipLaunchKernelGGL((mass_kernel<DT, VEC, CUT>), dim3(nsample), dim3(kThreads), 0, st, a);
-  hipLaunchKernelGGL((sample_kernel<DT, VEC, CUT>), dim3(nsample), dim3(kThreads), 0, st, a);
+  if (eps_mode) hipLaunchKernelGGL((sample_kernel<DT, VEC, CUT, true>), dim3(nsample), dim3(kThreads), 0, st, a);
+  else hipLaunchKernelGGL((sample_kernel<DT, VEC, CUT, false>), dim3(nsample), dim3(kThreads), 0, st, a);
   hipLaunchKernelGGL((draw_kernel<DT, VEC, CUT>), dim3((unsigned)a.B), dim3(kThreads), 0, st, a);
   hipLaunchKernelGGL((final_kernel<DT>), dim3((unsigned)a.B), dim3(kThreads), 0, st, a);
   return hipGetLastError();

@@ -127,11 +127,12 @@ __global__ __launch_bounds__(kThreads) void mass_kernel(VerifyArgs a) {
   mass_item<DT, VEC, CUT>(a, b, s, lds_d);
 }
 
-template <int DT, bool VEC, bool CUT>
+// EPS: the call may use the Saguaro eps mode (its weights need more registers).
+template <int DT, bool VEC, bool CUT, bool EPS>
 __global__ __launch_bounds__(kThreads) void sample_kernel(VerifyArgs a) {
   __shared__ double lds_d[kWaves * (kTilesPerItem + 1)];
   const int b = blockIdx.x / a.nt, s = blockIdx.x - b * a.nt;
-  sample_item<DT, VEC, CUT>(a, b, s, lds_d);
+  sample_item<DT, VEC, CUT, EPS>(a, b, s, lds_d);
 }
 
 template <int DT, bool VEC, bool CUT>
