@@ -194,9 +194,10 @@ static hipError_t launch_kernels(const VerifyArgs& a, hipStream_t st);
 // pa: NULL, or outcome prediction after the verification.
 template <int DT, bool VEC>
 static hipError_t launch_all(const VerifyArgs& a, const PredictArgs* pa, hipStream_t st) {
-  // The single-kernel order for packed bf16 rows; float32 or unaligned rows
-  // take one kernel per item kind (their sampling paths need more registers
-  // than the stream items' occupancy leaves) and the stand-alone prediction.
+  // The single-kernel order for packed bf16 rows.  float32 or unaligned rows
+  // take it for the plain rule (at half the occupancy, below); with a cut,
+  // eps, early exit or prediction they take one kernel per item kind and the
+  // stand-alone prediction.
   if constexpr (SV_FUSED && DT == kBF16 && VEC) {
     if (!a.topp && !(a.saguaro && a.eps > 0.f)) {
       int slots = 0;
@@ -223,6 +224,20 @@ static hipError_t launch_all(const VerifyArgs& a, const PredictArgs* pa, hipStre
         if (e != hipSuccess) return e;
         return predict_launch_leaders(*pa, SPEC_BF16, st);
       }
+      hipLaunchKernelGGL((fused_kernel<DT, VEC, SV_STREAM_UNROLL, false, false>), dim3((unsigned)sc.total),
+                         dim3(kThreads), 0, st, a, sc);
+      return hipGetLastError();
+    }
+  }
+  if constexpr (SV_FUSED && !(DT == kBF16 && VEC)) {
+    // float32 or unaligned rows: the single kernel in the default order, for
+    // the rule without a cut, eps or prediction (one launch instead of a
+    // chain of five, which is what a small batch waits for).
+    if (!a.topp && !(a.saguaro && a.eps > 0.f) && !a.early && !pa) {
+      int slots = 0;
+      hipError_t e = resident_groups<DT, VEC, false, false>(slots);
+      if (e != hipSuccess) return e;
+      const Sched sc = make_sched(a.B, 2 * a.gamma * a.nc, a.nc, 0, a.nt, slots);
       hipLaunchKernelGGL((fused_kernel<DT, VEC, SV_STREAM_UNROLL, false, false>), dim3((unsigned)sc.total),
                          dim3(kThreads), 0, st, a, sc);
       return hipGetLastError();

@@ -32,13 +32,18 @@ __device__ __forceinline__ void early_skip(const VerifyArgs& a, int b, int r, in
   }
 }
 
-// Compiled for 8 waves per SIMD (64 VGPRs): the stream items need the
-// occupancy; every other path fits without spilling for packed bf16 rows.
+// Packed bf16 rows: compiled for 8 waves per SIMD (64 VGPRs), which the
+// stream items need and every other path fits without spilling.  float32
+// and unaligned rows hold twice the registers per logit in flight, and their
+// sampling paths need more: 4 waves per SIMD (128 VGPRs).
+template <int DT, bool VEC>
+constexpr int kFusedWaves = DT == kBF16 && VEC ? 8 : 4;
+
 // PRED: outcome prediction too (draft-row items record lane leaders; the
 // items of target row gamma are followed by leader items of draft row gamma).
 // EARLY: the early-exit order (position-major stream items, position tests).
 template <int DT, bool VEC, int U, bool PRED, bool EARLY>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8, 8)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kFusedWaves<DT, VEC>, 8)))
 void fused_kernel(VerifyArgs a, Sched sc) {
   __shared__ ItemLds sh;
   __shared__ int item[4];
