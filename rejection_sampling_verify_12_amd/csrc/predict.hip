@@ -238,9 +238,18 @@ __global__ __launch_bounds__(64) void top3_lanes_kernel(PredictArgs a) {
   const int K = with_hit ? a.accepted[b] : -1;
   const bool mine_hit = with_hit && (K == k || ((K < 0 || K >= G1) && k == 0));
   const Top3* P = a.part + row * a.nc;
+  // Lane l merges the records of chunks l, l + 64, ...; then the wave merges
+  // the lanes.
   uint64_t t[3] = {0, 0, 0};
-  if (lane < 3 * a.nc) t[0] = P[lane / 3].key[lane % 3];
-  const bool nan = __ballot(lane < a.nc && P[lane < a.nc ? lane : 0].nan != 0) != 0;
+  bool nan_l = false;
+  for (int c = lane; c < a.nc; c += 64) {
+    const Top3 r = P[c];
+    insert3(t, r.key[0]);
+    insert3(t, r.key[1]);
+    insert3(t, r.key[2]);
+    nan_l = nan_l || r.nan != 0u;
+  }
+  const bool nan = __ballot(nan_l) != 0;
   uint64_t lead[3];
   wave_top3(t, lead);
   int y = -1;

@@ -2,6 +2,7 @@
 
 Every case prints its name, shapes and seed before touching the GPU.
 """
+import dataclasses
 import functools
 
 import numpy as np
@@ -298,6 +299,22 @@ def test_verify_predict_ragged(V, dtype):
     candidates (2)."""
     batch = random_batch(5, 3, V, dtype, 1.0, seed=4100 + V % 97)
     _check_verify_predict(batch, _verify_predict(batch))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_verify_predict_many_chunks(dtype):
+    """Rows of more than 21 chunks of 32768 logits (more candidate records
+    than a wave holds three to a lane), each row's maximum planted in its
+    last, partial chunk and its runner-up in the first."""
+    V = 22 * 32768 - 4000
+    batch = random_batch(2, 1, V, dtype, 1.0, seed=4177)
+    d64 = W.decode_f64(batch.draft, dtype)
+    d64[:, :, V - 3] = d64.max() + 2.0
+    d64[:, :, 5] = d64.max() - 1.0
+    batch = dataclasses.replace(batch, draft=W.encode(d64, dtype))
+    got = _verify_predict(batch)
+    assert (got["cand"][:, :, 0] == V - 3).all() and (got["cand"][:, :, 1] == 5).all()
+    _check_verify_predict(batch, got)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
