@@ -74,9 +74,17 @@ static bool sizes_ok(int B, int gamma, int V) {
 static Layout layout(int B, int gamma, int V) {
   Layout L;
   // Chunks are a multiple of the batch stride (SV_STREAM_UNROLL * 2048 logits),
-  // so only a row's last chunk has a partial batch.
+  // so only a row's last chunk has a partial batch.  A call with few rows
+  // takes shorter chunks (down to one batch stride), so that its rows still
+  // spread over many work-groups and each one's loads run fewer batches deep.
+  const int64_t rows = (int64_t)B * (2 * gamma + 1);
   L.chunk = kChunk;
+  while (L.chunk > kMinChunk && rows * (((int64_t)V + L.chunk - 1) / L.chunk) < kSmallCallItems) L.chunk /= 2;
   L.nc = (int)(((int64_t)V + L.chunk - 1) / L.chunk);
+  // Per-chunk records: at least what any call with shortened chunks needs,
+  // so that a workspace sized for a call serves every smaller one.
+  const size_t nrec = std::max<size_t>((size_t)rows * L.nc, (size_t)kSmallCallItems * (kChunk / kMinChunk));
+  const size_t nrec_d = std::max<size_t>((size_t)B * (gamma + 1) * L.nc, (size_t)kSmallCallItems * (kChunk / kMinChunk));
   L.ntile = (V + kTile - 1) / kTile;
   L.nt = (L.ntile + kTilesPerItem - 1) / kTilesPerItem;
   const size_t R = 2 * (size_t)gamma + 1;
@@ -84,9 +92,9 @@ static Layout layout(int B, int gamma, int V) {
   L.err_off = off;
   off += 256;
   L.part_off = off;
-  off += align256((size_t)B * R * L.nc * sizeof(uint64_t));
+  off += align256(nrec * sizeof(uint64_t));
   L.mraw_off = off;
-  off += align256((size_t)B * R * L.nc * sizeof(unsigned));
+  off += align256(nrec * sizeof(unsigned));
   L.seq_off = off;
   off += align256((size_t)B * sizeof(SeqRec));
   L.flag_off = off;
@@ -98,7 +106,7 @@ static Layout layout(int B, int gamma, int V) {
   L.rsum_off = off;
   off += align256((size_t)B * L.nt * sizeof(uint64_t));
   L.cpart_off = off;
-  off += align256((size_t)B * (gamma + 1) * L.nc * sizeof(Top3));
+  off += align256(nrec_d * sizeof(Top3));
   L.topp_off = off;
   off += align256((size_t)B * R * sizeof(TopPRow));
   L.hist_off = off;
@@ -207,7 +215,7 @@ static hipError_t launch_all(const VerifyArgs& a, const PredictArgs* pa, hipStre
         if (e != hipSuccess) return e;
         static_assert(SV_EARLY_CHUNK % SV_CHUNK == 0, "early-exit chunks are whole default chunks");
         VerifyArgs b = a;   // never more chunks than the workspace holds
-        b.chunk = SV_EARLY_CHUNK;
+        b.chunk = a.chunk < kChunk ? a.chunk : SV_EARLY_CHUNK;   // a short call keeps its short chunks
         b.nc = (int)(((int64_t)a.V + b.chunk - 1) / b.chunk);
         const Sched sc = make_sched_early(b.B, b.gamma, b.nc, eps_mode ? b.nt : 0, b.nt, slots);
         hipLaunchKernelGGL((fused_kernel<DT, VEC, SV_STREAM_UNROLL, false, true>), dim3((unsigned)sc.total),

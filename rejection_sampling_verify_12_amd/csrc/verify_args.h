@@ -56,6 +56,12 @@ enum : int { kModeTarget = 0, kModeResidual = 1, kModeSaguaro = 2, kModeSaguaroE
 #endif
 constexpr int kTilesPerItem = SV_TILES_PER_ITEM;
 constexpr bool kSampleNT = SV_SAMPLE_NT != 0;   // nontemporal loads in the sampling items
+// The shortest chunk (one batch stride), and the stream items below which a
+// call shortens its chunks towards it.
+constexpr int kMinChunk = SV_STREAM_UNROLL * kThreads * kUnit;
+constexpr int64_t kSmallCallItems = 512;
+static_assert(kChunk % kMinChunk == 0 && (kChunk / kMinChunk & (kChunk / kMinChunk - 1)) == 0,
+              "chunks halve down to the batch stride");
 static_assert(kChunk % (SV_STREAM_UNROLL * kThreads * kUnit) == 0,
               "a stream chunk must hold whole batches");
 constexpr unsigned kMaxPolls = 1u << 22;   // bounded waits: about a quarter of a second

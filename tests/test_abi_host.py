@@ -53,6 +53,20 @@ def test_workspace_bytes():
     assert R.spec_predict_workspace_bytes(0, 4, 128256, R.SPEC_BF16) == 0
 
 
+@pytest.mark.parametrize("gamma,V", [(4, 32000), (1, 7), (8, 152064), (4, 128256), (63, 40000)])
+def test_workspace_serves_every_smaller_call(gamma, V):
+    """Calls with few rows take shorter chunks (more per-chunk records per
+    row); the workspace of a call still covers every call with fewer
+    sequences, shorter rows or fewer positions."""
+    for dt in (R.SPEC_BF16, R.SPEC_F32):
+        sizes = [R.spec_workspace_bytes(B, gamma, V, dt) for B in range(1, 130)]
+        assert all(x <= y for x, y in zip(sizes, sizes[1:])), (gamma, V, dt)
+        for B in (1, 3, 17, 64):
+            big = R.spec_workspace_bytes(B, gamma, V, dt)
+            assert R.spec_workspace_bytes(B, gamma, max(V // 3, 1), dt) <= big
+            assert R.spec_workspace_bytes(B, max(gamma // 2, 1), V, dt) <= big
+
+
 FAKE = 4096   # never dereferenced: every call below fails validation first
 
 
