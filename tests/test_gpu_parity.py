@@ -199,6 +199,34 @@ def test_deterministic_replay():
             assert np.array_equal(v, again["diag"][k], equal_nan=True), k
 
 
+def test_concurrent_calls_on_two_streams():
+    """Calls on two streams with their own workspaces, launched back to back
+    (a bf16 batch and a float32 one, several times each, no synchronisation
+    in between), give the outputs the same calls give one at a time."""
+    import rejection_sampling_verify_12_amd as R
+    batches = [workload("B64_g5_V128256_bf16"), random_batch(9, 4, 30001, "f32", 0.9, seed=4321)]
+    dbs = [H.to_device(b) for b in batches]
+    dts = [R.SPEC_BF16, R.SPEC_F32]
+    ws = [R.new_workspace(R.spec_workspace_bytes(b.B, b.gamma, b.V, dt), "cuda") for b, dt in zip(batches, dts)]
+    alone = [H.run_gpu(b, db=db, diag=False) for b, db in zip(batches, dbs)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    outs = [[], []]
+    for _ in range(4):
+        for i in (0, 1):
+            b, db = batches[i], dbs[i]
+            with torch.cuda.stream(streams[i]):
+                outs[i].append(R.spec_verify(db.draft, db.target, db.tokens, db.u_accept, db.u_sample,
+                                             b.T, in_len=db.in_len, workspace=ws[i], stream=streams[i]))
+    torch.cuda.synchronize()
+    for i in (0, 1):
+        assert int(ws[i][:4].view(torch.int32).item()) == 0, "bounded wait timed out"
+        for o in outs[i]:
+            np.testing.assert_array_equal(o.tokens.cpu().numpy(), alone[i]["tokens"])
+            np.testing.assert_array_equal(o.accepted.cpu().numpy(), alone[i]["accepted"])
+            np.testing.assert_array_equal(o.out_len.cpu().numpy(), alone[i]["out_len"])
+
+
 # --------------------------------------------------------------------------- outcome prediction
 
 def _predict(batch, gpu=None):
