@@ -227,6 +227,42 @@ def test_concurrent_calls_on_two_streams():
             np.testing.assert_array_equal(o.out_len.cpu().numpy(), alone[i]["out_len"])
 
 
+@pytest.mark.parametrize("early", [False, True])
+def test_graph_capture_replays(early):
+    """One call captured in a graph (outputs and workspace allocated
+    beforehand) and replayed five times, with eager work and a
+    synchronisation between the replays: every replay gives the eager call's
+    outputs and leaves the workspace's error word clear."""
+    import rejection_sampling_verify_12_amd as R
+    batch = random_batch(24, 4, 50000, "bf16", 1.0, seed=4333)
+    db = H.to_device(batch)
+    ref = H.run_gpu(batch, db=db, diag=False, early=early)
+    ws = R.new_workspace(R.spec_workspace_bytes(batch.B, batch.gamma, batch.V, R.SPEC_BF16), "cuda")
+    out = R.alloc_outputs(batch.B, batch.gamma, "cuda")
+    call = R.spec_verify_early if early else R.spec_verify
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):   # warm-up outside the capture
+        call(db.draft, db.target, db.tokens, db.u_accept, db.u_sample, batch.T, in_len=db.in_len,
+             out=out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(db.draft, db.target, db.tokens, db.u_accept, db.u_sample, batch.T, in_len=db.in_len,
+             out=out, workspace=ws)
+    for _ in range(5):
+        out.tokens.fill_(-7)
+        out.accepted.fill_(-7)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert int(ws[:4].view(torch.int32).item()) == 0, "bounded wait timed out"
+        np.testing.assert_array_equal(out.tokens.cpu().numpy(), ref["tokens"])
+        np.testing.assert_array_equal(out.accepted.cpu().numpy(), ref["accepted"])
+        np.testing.assert_array_equal(out.out_len.cpu().numpy(), ref["out_len"])
+
+
 # --------------------------------------------------------------------------- outcome prediction
 
 def _predict(batch, gpu=None):
