@@ -19,6 +19,9 @@
  *     target scores gamma+1 positions);
  *   - every draw takes the first token id j whose running probability sum in
  *     token-id order exceeds u_sample[b][k] (section 3, the choice helper);
+ *     a residual draw whose residual mass is below 1/16 of q_k's is taken
+ *     in fp64 from the logits (a kernel after the call's others), so that
+ *     its running sums stay within 1e-6 of the exact ones;
  *   - the committed length is in_len + k + 1 (SSD summary, AMD MI300X part:
  *     on rejection only the valid-length pointer of the KV cache moves).
  *
@@ -28,7 +31,8 @@
  *     stream and return; nothing is synchronised.
  *   - The caller owns every buffer.  The library never allocates or frees
  *     device memory; its only global state is a per-device cache of how many
- *     work-groups the GPU holds at once (queried on the first call).
+ *     work-groups the GPU holds at once (queried on the first call; its
+ *     entries are atomics, so host threads may call concurrently).
  *     Concurrent calls need distinct workspaces.
  *   - Logits are row-major [B][gamma+1][V], contiguous, float32 (SPEC_F32) or
  *     bfloat16 (SPEC_BF16).  Row i of sequence b starts at element
@@ -93,9 +97,14 @@ typedef struct spec_diag {
  * completes leaves it ready for the next one, so a workspace is allocated and
  * cleared once and then reused by calls on one stream.  Its first 32-bit word
  * is an error flag: the kernels hand partial results between work-groups
- * through the workspace and wait for them with bounded polls; a poll that
- * times out (never expected) sets the word to 1 and the call's outputs are
- * then unreliable.  After that, zero the whole workspace before reusing it.
+ * through the workspace and wait for them with bounded polls.  A poll that
+ * times out (never expected) sets the word to 1; from then on every wait of
+ * the call gives up within a few microseconds, every kernel returns, and no
+ * sequence is reported valid from a value that did not arrive: a sequence
+ * whose decision is taken with the word set, or any of whose waits gave up,
+ * comes back invalid (accepted = -1, tokens -1).  The call still returns
+ * SPEC_OK (nothing is synchronised); check the word after the stream, and
+ * zero the whole workspace before reusing it once it is set.
  */
 size_t spec_workspace_bytes(int B, int gamma, int V, int dtype);
 

@@ -19,6 +19,7 @@
 //     the gamma positions with one wave ballot and writes the outputs.
 // Blocks are dispatched in order, so a final item only waits for stream items
 // that were dispatched before it and never wait themselves: every poll ends.
+#include <atomic>
 #include "common.h"
 #include "spec_verify.h"
 #include "topk.h"
@@ -134,6 +135,8 @@ __device__ void greedy_stream(const GreedyArgs& a, int b, int r, int c, GreedyLd
   }
 }
 
+// A slot's word, or ~kNanKey when the wait gives up: the row then counts as
+// holding a NaN, so nothing is taken from it.
 __device__ __forceinline__ uint64_t greedy_poll(const GreedyArgs& a, const uint64_t* p) {
   uint64_t w = ld_dev_u64(p);
   unsigned polls = 0;
@@ -142,7 +145,7 @@ __device__ __forceinline__ uint64_t greedy_poll(const GreedyArgs& a, const uint6
     if ((polls & 63u) == 0u &&
         (polls > kGreedyPolls || __hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))) {
       __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      break;
+      return ~kNanKey;
     }
     __builtin_amdgcn_s_sleep(2);
     w = ld_dev_u64(p);
@@ -153,6 +156,8 @@ __device__ __forceinline__ uint64_t greedy_poll(const GreedyArgs& a, const uint6
 __device__ void greedy_final(const GreedyArgs& a, int b, GreedyLds& sh) {
   const int G1 = a.gamma + 1;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // The error word, read early so its latency overlaps the polls.
+  const unsigned err = __hip_atomic_load(a.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   // Rows by wave, chunks by lane: every slot is polled, consumed and cleared.
   for (int r = wave; r < G1; r += kWaves) {
     uint64_t best = 0;
@@ -177,7 +182,9 @@ __device__ void greedy_final(const GreedyArgs& a, int b, GreedyLds& sh) {
   const uint64_t rk = pos ? sh.row[lane] : 0ull;
   const bool nan_i = pos && rk == kNanKey;
   const uint64_t mask = __ballot(pos && !bad_x && !nan_i && key_index(rk) == x);
-  bool bad = __ballot(bad_x || nan_i) != 0;
+  // After a bounded wait has given up anywhere in the call (the error word),
+  // the sequence is reported invalid.
+  bool bad = __ballot(bad_x || nan_i) != 0 || err != 0u;
   const int k = __builtin_ctzll(~mask);   // <= gamma: bit gamma of mask is clear
   const uint64_t ky = sh.row[k];
   if (k == a.gamma && ky == kNanKey) bad = true;
@@ -255,15 +262,19 @@ size_t greedy_bytes(int B, int gamma, int V) {
   return 256 + (((size_t)B * (gamma + 1) * nc * sizeof(uint64_t) + 255) & ~(size_t)255);
 }
 
+// Work-groups the device holds at once, cached per device.  The entries are
+// atomics: concurrent callers may fill one at the same time, with the same
+// value.
 template <int DT, bool VEC>
 hipError_t greedy_slots(int& slots) {
-  static int cache[64];
+  static std::atomic<int> cache[64];
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  int* c = dev >= 0 && dev < 64 ? &cache[dev] : nullptr;
-  if (c && *c > 0) {
-    slots = *c;
+  std::atomic<int>* c = dev >= 0 && dev < 64 ? &cache[dev] : nullptr;
+  const int cached = c ? c->load(std::memory_order_relaxed) : 0;
+  if (cached > 0) {
+    slots = cached;
     return hipSuccess;
   }
   int ncu = 0, per_cu = 0;
@@ -273,7 +284,7 @@ hipError_t greedy_slots(int& slots) {
         &per_cu, reinterpret_cast<const void*>(greedy_kernel<DT, VEC>), kThreads, 0);
   if (e != hipSuccess) return e;
   slots = std::max(1, ncu * per_cu);
-  if (c) *c = slots;
+  if (c) c->store(slots, std::memory_order_relaxed);
   return hipSuccess;
 }
 

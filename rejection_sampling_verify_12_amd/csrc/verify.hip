@@ -53,6 +53,7 @@
 #include <cmath>
 #include <limits.h>
 #include <algorithm>
+#include <atomic>
 
 namespace sv {
 
@@ -64,7 +65,7 @@ static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 struct Layout {
   int nc, chunk, ntile, nt;
   size_t err_off, part_off, mraw_off, seq_off, flag_off, tiles_off, mass_off, rsum_off, cpart_off,
-      topp_off, hist_off, redo_off, total;
+      ref_off, topp_off, hist_off, redo_off, total;
 };
 
 static bool sizes_ok(int B, int gamma, int V) {
@@ -107,6 +108,8 @@ static Layout layout(int B, int gamma, int V) {
   off += align256((size_t)B * L.nt * sizeof(uint64_t));
   L.cpart_off = off;
   off += align256(nrec_d * sizeof(Top3));
+  L.ref_off = off;
+  off += align256((size_t)B * L.ntile * 4 * sizeof(uint64_t));
   L.topp_off = off;
   off += align256((size_t)B * R * sizeof(TopPRow));
   L.hist_off = off;
@@ -117,16 +120,19 @@ static Layout layout(int B, int gamma, int V) {
   return L;
 }
 
-// Work-groups of the fused kernel the device holds at once (cached per device).
+// Work-groups of the fused kernel the device holds at once, cached per
+// device and kernel variant.  The entries are atomics: concurrent callers may
+// fill one at the same time, with the same value.
 template <int DT, bool VEC, bool PRED, bool EARLY>
 static hipError_t resident_groups(int& slots) {
-  static int cache[64][2][2][2][2];
+  static std::atomic<int> cache[64];
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  int* c = dev >= 0 && dev < 64 ? &cache[dev][DT][VEC ? 1 : 0][PRED ? 1 : 0][EARLY ? 1 : 0] : nullptr;
-  if (c && *c > 0) {
-    slots = *c;
+  std::atomic<int>* c = dev >= 0 && dev < 64 ? &cache[dev] : nullptr;
+  const int cached = c ? c->load(std::memory_order_relaxed) : 0;
+  if (cached > 0) {
+    slots = cached;
     return hipSuccess;
   }
   int ncu = 0, per_cu = 0;
@@ -137,7 +143,7 @@ static hipError_t resident_groups(int& slots) {
         kThreads, 0);
   if (e != hipSuccess) return e;
   slots = std::max(1, ncu * per_cu);
-  if (c) *c = slots;
+  if (c) c->store(slots, std::memory_order_relaxed);
   return hipSuccess;
 }
 
@@ -199,6 +205,15 @@ static Sched make_sched_early(int B, int G, int NC, int NM, int NB, int slots) {
 template <int DT, bool VEC>
 static hipError_t launch_kernels(const VerifyArgs& a, hipStream_t st);
 
+// After the call's other kernels: the refined residual draws (a.refine).
+template <int DT, bool CUT>
+static hipError_t launch_refine(const VerifyArgs& a, hipStream_t st) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || !a.refine) return e;
+  hipLaunchKernelGGL((refine_kernel<DT, CUT>), dim3((unsigned)a.B), dim3(kThreads), 0, st, a);
+  return hipGetLastError();
+}
+
 // pa: NULL, or outcome prediction after the verification.
 template <int DT, bool VEC>
 static hipError_t launch_all(const VerifyArgs& a, const PredictArgs* pa, hipStream_t st) {
@@ -220,7 +235,7 @@ static hipError_t launch_all(const VerifyArgs& a, const PredictArgs* pa, hipStre
         const Sched sc = make_sched_early(b.B, b.gamma, b.nc, eps_mode ? b.nt : 0, b.nt, slots);
         hipLaunchKernelGGL((fused_kernel<DT, VEC, SV_STREAM_UNROLL, false, true>), dim3((unsigned)sc.total),
                            dim3(kThreads), 0, st, b, sc);
-        return hipGetLastError();
+        return launch_refine<DT, false>(b, st);
       }
       hipError_t e = pa ? resident_groups<DT, VEC, true, false>(slots) : resident_groups<DT, VEC, false, false>(slots);
       if (e != hipSuccess) return e;
@@ -228,13 +243,13 @@ static hipError_t launch_all(const VerifyArgs& a, const PredictArgs* pa, hipStre
       if (pa) {
         hipLaunchKernelGGL((fused_kernel<DT, VEC, SV_STREAM_UNROLL, true, false>), dim3((unsigned)sc.total),
                            dim3(kThreads), 0, st, a, sc);
-        e = hipGetLastError();
+        e = launch_refine<DT, false>(a, st);
         if (e != hipSuccess) return e;
         return predict_launch_leaders(*pa, SPEC_BF16, st);
       }
       hipLaunchKernelGGL((fused_kernel<DT, VEC, SV_STREAM_UNROLL, false, false>), dim3((unsigned)sc.total),
                          dim3(kThreads), 0, st, a, sc);
-      return hipGetLastError();
+      return launch_refine<DT, false>(a, st);
     }
   }
   if constexpr (SV_FUSED && !(DT == kBF16 && VEC)) {
@@ -248,7 +263,7 @@ static hipError_t launch_all(const VerifyArgs& a, const PredictArgs* pa, hipStre
       const Sched sc = make_sched(a.B, 2 * a.gamma * a.nc, a.nc, 0, a.nt, slots);
       hipLaunchKernelGGL((fused_kernel<DT, VEC, SV_STREAM_UNROLL, false, false>), dim3((unsigned)sc.total),
                          dim3(kThreads), 0, st, a, sc);
-      return hipGetLastError();
+      return hipGetLastError();   // its final items refine in place (registers to spare)
     }
   }
   {
@@ -295,7 +310,7 @@ static hipError_t launch_kernels_cut(const VerifyArgs& a, hipStream_t st) {
   else hipLaunchKernelGGL((sample_kernel<DT, VEC, CUT, false>), dim3(nsample), dim3(kThreads), 0, st, a);
   hipLaunchKernelGGL((draw_kernel<DT, VEC, CUT>), dim3((unsigned)a.B), dim3(kThreads), 0, st, a);
   hipLaunchKernelGGL((final_kernel<DT>), dim3((unsigned)a.B), dim3(kThreads), 0, st, a);
-  return hipGetLastError();
+  return launch_refine<DT, CUT>(a, st);
 }
 
 template <int DT, bool VEC>
@@ -350,6 +365,11 @@ static int verify_impl(const void* draft, const void* target, int dtype, const i
   a.mass = reinterpret_cast<uint64_t*>(w + L.mass_off);
   a.rsum = reinterpret_cast<uint64_t*>(w + L.rsum_off);
   a.cpart = reinterpret_cast<Top3*>(w + L.cpart_off);
+  a.ref = reinterpret_cast<uint64_t*>(w + L.ref_off);
+  // Residual draws of a small residual mass are refined in fp64 by a kernel
+  // after the call's others.  (A Saguaro call falls back to the residual only
+  // on degenerate inputs, and draws that fallback in fp32.)
+  a.refine = saguaro ? 0 : 1;
   a.B = B;
   a.gamma = gamma;
   a.V = V;

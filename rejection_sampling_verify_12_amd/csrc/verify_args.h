@@ -159,6 +159,8 @@ struct VerifyArgs {
   uint64_t* mass;    // [B][nt] slots: residual sums of the residual-mass items (eps > 0)
   uint64_t* rsum;    // [B][nt] slots: residual sums of the sampling items (Saguaro)
   Top3* cpart;       // [B][gamma+1][nc] lane leaders of the draft rows (outcome prediction)
+  uint64_t* ref;     // [B][ntile][4] slots: fp64 tile sums of a refined residual draw
+  int refine;        // 1: refine_kernel follows the call's kernels (small residual masses are refined)
   int B, gamma, V;
   int nc, chunk;     // stream chunks per row and their length
   int ntile, nt;     // sampling tiles per row; sampling items per sequence
@@ -215,16 +217,20 @@ __device__ __forceinline__ TCoef temp_coef(const VerifyArgs& a, int b) {
 
 template <int DT>
 __device__ __forceinline__ const void* row_ptr(const VerifyArgs& a, int b, int r) {
-  // r < gamma: draft row r; otherwise target row r - gamma.
+  // r < gamma: draft row r; otherwise target row r - gamma.  The base is
+  // chosen by integer arithmetic: a select between the two argument fields
+  // can be turned into a load from a selected field address, which keeps
+  // the kernel's arguments in scratch memory.
   const int64_t es = DT == kBF16 ? 2 : 4;
   const bool is_draft = r < a.gamma;
   const int64_t idx = (int64_t)b * (a.gamma + 1) + (is_draft ? r : r - a.gamma);
-  const char* base = static_cast<const char*>(is_draft ? a.draft : a.target);
-  return base + idx * a.V * es;
+  const uintptr_t t = reinterpret_cast<uintptr_t>(a.target);
+  const uintptr_t base = t + (is_draft ? reinterpret_cast<uintptr_t>(a.draft) - t : (uintptr_t)0);
+  return reinterpret_cast<const char*>(base) + idx * a.V * es;
 }
 
 // Bounded polls.  A timeout (or an error already recorded by another
-// work-group) records the error and returns whatever the word holds.
+// work-group) records the error and gives up.
 __device__ __forceinline__ bool give_up(const VerifyArgs& a, unsigned& polls) {
   ++polls;
   if ((polls & 63u) == 0u &&
@@ -238,17 +244,48 @@ __device__ __forceinline__ bool give_up(const VerifyArgs& a, unsigned& polls) {
 __device__ __forceinline__ unsigned ld_dev_u32(const unsigned* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// The slot's word once it is written, or 0 if the wait gave up (a value
+// read from 0 is NaN, see slot_value; callers that derive an index or a
+// token from the word check for 0 first).
 __device__ __forceinline__ uint64_t poll(const VerifyArgs& a, const uint64_t* p) {
   uint64_t w = ld_dev_u64(p);
   unsigned polls = 0;
   while (w == 0ull && !give_up(a, polls)) w = ld_dev_u64(p);
   return w;
 }
+
+// Decode a decision record from the words as read (each stored as its
+// complement, so 0 = not written).  If any word is missing - its wait gave
+// up - the record is "lost": it decodes as an invalid sequence with k = 0
+// and the target mode, so no index or mode is ever taken from an unwritten
+// word, and `lost` tells the final item to report the sequence invalid.
+__host__ __device__ inline SeqRec decode_rec(const uint64_t (&raw)[kRecWords], bool& lost) {
+  lost = false;
+  for (int i = 0; i < kRecWords; ++i) lost = lost || raw[i] == 0ull;
+  SeqRec r;
+  if (lost) {
+    r.mask = 0ull;
+    r.k = 0;
+    r.valid = 0;
+    r.mode = kModeTarget;
+    r.Mt = 0.f;
+    r.K_hi = r.K_lo = 0.f;
+    r.Zt = 1.0;
+    return r;
+  }
+  uint64_t w[kRecWords];
+  for (int i = 0; i < kRecWords; ++i) w[i] = ~raw[i];
+  static_assert(sizeof(w) == sizeof(SeqRec), "a record is its words");
+  __builtin_memcpy(&r, w, sizeof(r));
+  return r;
+}
+
 // The sequence's decision record: thread 0 waits for each word, the
 // work-group reads it from LDS (COUNT: thread 0 then counts this item as done
-// with the record).  The fields end up in scalar registers.
+// with the record).  The fields end up in scalar registers.  `lost`: the
+// wait gave up (see decode_rec).
 template <bool COUNT>
-__device__ __forceinline__ SeqRec wait_rec(const VerifyArgs& a, int b) {
+__device__ __forceinline__ SeqRec wait_rec(const VerifyArgs& a, int b, bool& lost) {
   __shared__ uint64_t w[kRecWords];
   if (threadIdx.x == 0) {
     // All words are requested together, again until every one has arrived.
@@ -267,19 +304,24 @@ __device__ __forceinline__ SeqRec wait_rec(const VerifyArgs& a, int b) {
         if (v[i] == 0ull) v[i] = ld_dev_u64(p + i);
     }
 #pragma unroll
-    for (int i = 0; i < kRecWords; ++i) w[i] = ~v[i];
+    for (int i = 0; i < kRecWords; ++i) w[i] = v[i];
   }
   __syncthreads();
-  SeqRec r;
-  uint64_t* rw = reinterpret_cast<uint64_t*>(&r);
+  uint64_t raw[kRecWords];
 #pragma unroll
-  for (int i = 0; i < kRecWords; ++i) rw[i] = uni(w[i]);
+  for (int i = 0; i < kRecWords; ++i) raw[i] = uni(w[i]);
+  SeqRec r = decode_rec(raw, lost);
   if (COUNT) {
     __syncthreads();
     if (threadIdx.x == 0)
       __hip_atomic_fetch_add(a.flag + (int64_t)b * kFlagStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   return r;
+}
+template <bool COUNT>
+__device__ __forceinline__ SeqRec wait_rec(const VerifyArgs& a, int b) {
+  bool lost;
+  return wait_rec<COUNT>(a, b, lost);
 }
 
 }  // namespace sv

@@ -12,7 +12,7 @@ namespace sv {
 // max_c v_c, z = sum_c 2^(v_c - M) (fp64), mr = the row's largest raw logit.
 // Waits for every piece (both words of a piece together) and clears them once
 // read.  Every lane of the group returns the row's values.
-__device__ void merge_row(const VerifyArgs& a, int b, int r, int sub, double& M, double& z, float& mr) {
+__device__ __forceinline__ void merge_row(const VerifyArgs& a, int b, int r, int sub, double& M, double& z, float& mr) {
   const int64_t p0 = ((int64_t)b * (2 * a.gamma + 1) + r) * a.nc;
   M = -INFINITY;
   z = 0.0;
@@ -62,6 +62,7 @@ struct DecideLds {
   float ldx[64], ltx[64], ux[64];
   uint64_t mask;
   int k, valid;
+  unsigned err;    // the error word, read with the gathers
 };
 
 // The rows the accept tests read, draft rows 0..gamma-1 and target rows
@@ -70,7 +71,7 @@ struct DecideLds {
 // record.  Target row gamma is checked by the sequence's final item.  A bad
 // row or token makes the sequence invalid here, with its outputs.
 template <int DT, bool CUT = false>
-__device__ void decide_item(const VerifyArgs& a, int b, DecideLds& sh) {
+__device__ __forceinline__ void decide_item(const VerifyArgs& a, int b, DecideLds& sh) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = a.gamma, Rd = 2 * g, R = 2 * g + 1;
   // Wave 1 gathers the draft tokens' logits and the uniforms (independent of
@@ -88,6 +89,7 @@ __device__ void decide_item(const VerifyArgs& a, int b, DecideLds& sh) {
       sh.ltx[lane] = ltx;
       sh.ux[lane] = a.u_acc[(int64_t)b * g + lane];
     }
+    if (lane == 0) sh.err = ld_dev_u32(a.err);
   } else {
     for (int r0 = 0; r0 < Rd; r0 += 12) {
       const int r = r0 + (wave == 0 ? 0 : wave - 1) * 4 + (lane >> 4);
@@ -141,7 +143,9 @@ __device__ void decide_item(const VerifyArgs& a, int b, DecideLds& sh) {
     const uint64_t badm = __ballot(bad);
     if (lane == 0) {
       sh.mask = mask & ((1ull << g) - 1);
-      sh.valid = !rows_bad && badm == 0;
+      // After a bounded wait has given up anywhere in the call (the error
+      // word), a decision reports its sequence invalid.
+      sh.valid = !rows_bad && badm == 0 && sh.err == 0u;
       sh.k = min(g, __ffsll((unsigned long long)~mask) - 1);
     }
   }
@@ -188,6 +192,7 @@ struct TestLds {
   int x;
   float ldx, ltx, ux;
   int decided, acc, bad_all;
+  unsigned err;
 };
 
 // Position i of sequence b: merges (and clears) the pieces of draft row i and
@@ -200,7 +205,7 @@ struct TestLds {
 // (accepted, more positions follow) or writes the decision record (rejected,
 // invalid, or the last position accepted).
 template <int DT>
-__device__ void test_item(const VerifyArgs& a, int b, int i, TestLds& sh) {
+__device__ __forceinline__ void test_item(const VerifyArgs& a, int b, int i, TestLds& sh) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = a.gamma, R = 2 * g + 1;
   unsigned* fl = a.flag + (int64_t)b * kFlagStride;
@@ -228,12 +233,14 @@ __device__ void test_item(const VerifyArgs& a, int b, int i, TestLds& sh) {
     sh.ldx = ldx;
     sh.ltx = ltx;
     sh.ux = a.u_acc[(int64_t)b * g + i];
+    sh.err = ld_dev_u32(a.err);
   }
   __syncthreads();
   if (tid == 0) {
     const TCoef tc = temp_coef(a, b);
     const int x = sh.x;
-    const bool bad = x < 0 || x >= a.V || sh.bad[0] || sh.bad[1] || (a.temps && !temp_ok(seq_temp(a, b)));
+    const bool bad = x < 0 || x >= a.V || sh.bad[0] || sh.bad[1] || (a.temps && !temp_ok(seq_temp(a, b))) ||
+                     sh.err != 0u;   // a wait gave up somewhere: report the sequence invalid
     bool acc = false;
     double pn = 0.0, qn = 0.0;
     if (!bad) {

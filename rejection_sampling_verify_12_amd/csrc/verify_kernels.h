@@ -96,7 +96,7 @@ void fused_kernel(VerifyArgs a, Sched sc) {
       if (!PRED || sub < a.nc) stream_item<DT, VEC, U>(a, b, 2 * a.gamma, sub, sh.s);
       else leader_item<DT, VEC, U>(a, b, sub - a.nc, sh.s);
       break;
-    default: final_item<DT>(a, b, sh.f); break;
+    default: final_item<DT, !(DT == kBF16 && VEC)>(a, b, sh.f); break;
   }
 }
 
@@ -150,6 +150,14 @@ template <int DT>
 __global__ __launch_bounds__(kThreads) void final_kernel(VerifyArgs a) {
   __shared__ FinalLds sh;
   final_item<DT>(a, blockIdx.x, sh);
+}
+
+// The refined residual draws, after every other kernel of the call (and
+// before the outcome prediction, which reads the drawn tokens).
+template <int DT, bool CUT>
+__global__ __launch_bounds__(kThreads) void refine_kernel(VerifyArgs a) {
+  __shared__ DrawLds sh;
+  refine_item<DT, CUT>(a, blockIdx.x, sh);
 }
 
 }  // namespace sv

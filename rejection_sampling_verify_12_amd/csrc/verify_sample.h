@@ -238,6 +238,7 @@ __device__ __forceinline__ double tile_slot_value(int mode, double sum, float of
 
 // eps * (residual mass) for Saguaro eps > 0, from the residual-mass items'
 // slots (waited for), summed in the same order by every reader.
+// A slot whose wait gave up reads as NaN, so the clamp is NaN then.
 __device__ float eps_clamp(const VerifyArgs& a, int b, double* lds_d) {
   double v = 0.0;
   for (int i = threadIdx.x; i < a.nt; i += kThreads) v += slot_value(poll(a, a.mass + (int64_t)b * a.nt + i));
@@ -249,7 +250,7 @@ __device__ float eps_clamp(const VerifyArgs& a, int b, double* lds_d) {
 // Residual-mass and sampling items.
 
 template <int DT, bool VEC, bool CUT = false>
-__device__ void mass_item(const VerifyArgs& a, int b, int s, double* lds_d) {
+__device__ __forceinline__ void mass_item(const VerifyArgs& a, int b, int s, double* lds_d) {
   const SeqRec rec = wait_rec<true>(a, b);
   if (!rec.valid || rec.mode != kModeSaguaroEps) return;
   double tw[kTilesPerItem + 1];
@@ -259,7 +260,7 @@ __device__ void mass_item(const VerifyArgs& a, int b, int s, double* lds_d) {
 }
 
 template <int DT, bool VEC, bool CUT = false, bool EPS = true>
-__device__ void sample_item(const VerifyArgs& a, int b, int s, double* lds_d) {
+__device__ __forceinline__ void sample_item(const VerifyArgs& a, int b, int s, double* lds_d) {
   const SeqRec rec = wait_rec<true>(a, b);
   if (!rec.valid) return;
   const int t0 = s * kTilesPerItem;
@@ -289,6 +290,8 @@ struct DrawLds {
   int tile, y, e;   // chosen tile, drawn token, tile units = 2^e draw units
   double off, lane_off, lo, hi, Mp;
   float w8[kUnit];
+  double w8d[kUnit];                 // fp64 residual draw: the owner lane's weights
+  double n_rm, n_tp, n_lo, n_hi;     // fp64 residual draw: S, pi(y), C_{y-1}, C_y (normalised)
 };
 
 __device__ __forceinline__ double tile_value(const uint64_t* tiles, int t) {
@@ -379,7 +382,7 @@ __device__ double locate_tile(const uint64_t* tiles, int ntile, double u, DrawLd
 // with weight whose running sum passes the target (else the lane's last token
 // with weight).  Sets sh.y, sh.e, sh.lo = C_{y-1} and sh.hi = C_y (draw units).
 template <int DT, bool VEC, int MODE, bool CUT = false>
-__device__ void rescan_tile(const VerifyArgs& a, int b, int k, const SampleCoef& cf, double target,
+__device__ __forceinline__ void rescan_tile(const VerifyArgs& a, int b, int k, const SampleCoef& cf, double target,
                             DrawLds& sh) {
   const int tid = threadIdx.x;
   const int tsel = sh.tile;
@@ -479,7 +482,7 @@ __device__ double precise_weight(const VerifyArgs& a, int b, int k, int mode, co
 // One logit at a time, with the weights and order the rescan uses, so its
 // per-lane fp32 sums match.
 template <int DT, bool CUT = false>
-__device__ void recompute_tiles(const VerifyArgs& a, int b, int k, int mode, const SampleCoef& cf,
+__device__ __forceinline__ void recompute_tiles(const VerifyArgs& a, int b, int k, int mode, const SampleCoef& cf,
                                 DrawLds& sh) {
   uint64_t* tiles = a.tiles + (int64_t)b * a.ntile;
   const void *drow, *trow;
@@ -506,17 +509,291 @@ __device__ void recompute_tiles(const VerifyArgs& a, int b, int k, int mode, con
   __syncthreads();
 }
 
+// ---------------------------------------------------------------------------
+// Residual draws refined in fp64.
+//
+// The fp32 weights (q_j - p_j)+ of the sampling items carry an absolute error
+// of a few ulp of q_j and p_j, and the row normalisers from the stream a
+// relative error of the same order, so the running sums of the residual are
+// known to some 1e-8 of q_k's mass (at most 4.3e-8 over ~2800 draws of the
+// configured workloads); normalised by the residual mass S that error grows
+// by 1/S.  Down to S = kRefineMass of q_k's mass it stays below 7e-7, inside
+// the 1e-6 window a draw's uniform must clear to be decided; a smaller
+// residual (zero included) is refined: the final item leaves the sequence's
+// token at k to refine_kernel, which runs after the call's other kernels and
+// takes the draw again in fp64 from the logits - both rows' normalisers,
+// every tile's residual sum and the chosen tile's running sums.  That code
+// lives in its own kernel: inside the single kernel its registers would
+// slow every stream item.
+constexpr double kRefineMass = 0.0625;           // refined below this fraction of q_k's mass
+constexpr uint32_t kRefineToken = 0xFFFFFFFEu;   // drawn slot: the draw is refined (never a token id)
+constexpr int kPendingWord = 8;                  // flag line: 1 = a refinement is pending
+
+// e^x in fp64 for x <= 709 (0 below -745, and for -inf): x = n ln2 + r with
+// |r| <= ln2 / 2, where ln2 is split into a 32-bit head (so n * head is exact)
+// and its remainder; e^r by its Taylor polynomial of degree 12 (truncation
+// below 3e-16 relative), scaled by 2^n.  Few registers, unlike the library
+// routine, which matters inside the single kernel.
+__device__ __forceinline__ double exp_f64(double x) {
+  if (!(x > -745.0)) return 0.0;
+  constexpr double kLog2e = 1.4426950408889634;
+  constexpr double kLn2Hi = 0.6931471803691238;      // ln 2 with its low 21 significand bits clear
+  constexpr double kLn2Lo = 1.9082149292705877e-10;  // ln 2 - kLn2Hi
+  const double n = rint(x * kLog2e);
+  const double r = fma(-n, kLn2Lo, fma(-n, kLn2Hi, x));
+  double p = 1.0 / 479001600.0;   // 1/12!
+  p = fma(p, r, 1.0 / 39916800.0);
+  p = fma(p, r, 1.0 / 3628800.0);
+  p = fma(p, r, 1.0 / 362880.0);
+  p = fma(p, r, 1.0 / 40320.0);
+  p = fma(p, r, 1.0 / 5040.0);
+  p = fma(p, r, 1.0 / 720.0);
+  p = fma(p, r, 1.0 / 120.0);
+  p = fma(p, r, 1.0 / 24.0);
+  p = fma(p, r, 1.0 / 6.0);
+  p = fma(p, r, 0.5);
+  p = fma(p, r, 1.0);
+  p = fma(p, r, 1.0);
+  return ldexp(p, (int)n);
+}
+
+// Logit pair j of rows k as fp64 exponentials relative to the references:
+// et = exp(lt / T - mt), ed = exp(ld / T - md) (0 past the row, for a -inf
+// logit, or one cut away by top-p).  Loaded on its own: this path is rare,
+// and few live registers keep it from weighing on the single kernel.
+template <int DT, bool CUT>
+__device__ __forceinline__ void exp_pair(const void* drow, const void* trow, int64_t j, int64_t V, float Lt,
+                                         float Ld, double invT, double mt, double md, double& et, double& ed) {
+  float lt = -INFINITY, ld = -INFINITY;
+  if (j < V) {
+    lt = cut1<CUT>(load_one<DT>(trow, j), Lt);
+    ld = cut1<CUT>(load_one<DT>(drow, j), Ld);
+  }
+  et = exp_f64(fma((double)lt, invT, -mt));
+  ed = exp_f64(fma((double)ld, invT, -md));
+}
+
 // The drawn token of a sequence: the 64-bit word at byte 8 of its count line,
-// stored as a complement (0 = not drawn yet).
+// stored as a complement (0 = not drawn yet).  kLostToken (never a token id)
+// says that a wait of the draw gave up.
 __device__ __forceinline__ uint64_t* drawn_slot(const VerifyArgs& a, int b) {
   return reinterpret_cast<uint64_t*>(a.flag + (int64_t)b * kFlagStride + 2);
 }
+constexpr uint32_t kLostToken = 0xFFFFFFFFu;
+
+// The fp64 sums of tiles [t0, t1) of row pair k, each tile's four values in
+// its refinement slots: E_t = sum et_j and E_d = sum ed_j over the tokens
+// where et_j > ed_j, and the sums of et_j and ed_j over every token.  The
+// references of the exponentials (Mt ln 2 for the target row; (Mt - K) ln 2
+// for the draft row, log2(p_j / q_j) = (ld_j - lt_j) c_T + K) make et_j and
+// ed_j equal q_j and p_j up to one common factor each, and those factors
+// agree to the fp32 normalisers' precision, so the exact residual is
+// (et_j - rho ed_j)+ / sum et with rho = sum et / sum ed = 1 + O(1e-7): a
+// token whose et_j and ed_j agree to 2^-16 could fall on either side of the
+// condition, and its tile is marked (E_t = NaN) to be summed again with the
+// exact rho.
+__device__ __forceinline__ uint64_t* ref_slots(const VerifyArgs& a, int b, int t) {
+  return a.ref + ((int64_t)b * a.ntile + t) * 4;
+}
+struct RefineRefs {
+  double invT, mt, md;
+};
+__device__ __forceinline__ RefineRefs refine_refs(const VerifyArgs& a, int b, const SeqRec& rec) {
+  constexpr double kLn2 = 0.69314718055994530942;
+  RefineRefs r;
+  r.invT = temp_coef(a, b).invT;
+  r.mt = (double)rec.Mt * kLn2;
+  r.md = ((double)rec.Mt - ((double)rec.K_hi + (double)rec.K_lo)) * kLn2;
+  return r;
+}
+
+struct RefineCtx {
+  const void* drow;
+  const void* trow;
+  float Lt, Ld;
+  double invT, mt, md;
+};
+template <int DT, bool CUT>
+__device__ __forceinline__ RefineCtx refine_ctx(const VerifyArgs& a, int b, const SeqRec& rec) {
+  RefineCtx c;
+  draw_rows<DT>(a, b, rec.k, c.drow, c.trow);
+  const SampleCoef cf = coef_of<CUT>(a, b, rec, 0.f);
+  c.Lt = cf.Lt;
+  c.Ld = cf.Ld;
+  const RefineRefs rr = refine_refs(a, b, rec);
+  c.invT = rr.invT;
+  c.mt = rr.mt;
+  c.md = rr.md;
+  return c;
+}
+
+template <int DT, bool CUT>
+__device__ __forceinline__ void refine_tiles(const VerifyArgs& a, int b, const SeqRec& rec, int t0, int t1,
+                                             double* lds_d) {
+  const RefineCtx c = refine_ctx<DT, CUT>(a, b, rec);
+  for (int t = t0; t < t1; ++t) {
+    double v[5] = {0.0, 0.0, 0.0, 0.0, 0.0};
+    const int64_t j0 = (int64_t)t * kTile + (int64_t)threadIdx.x * kUnit;
+#pragma unroll 1
+    for (int e = 0; e < kUnit; ++e) {
+      double et, ed;
+      exp_pair<DT, CUT>(c.drow, c.trow, j0 + e, a.V, c.Lt, c.Ld, c.invT, c.mt, c.md, et, ed);
+      v[2] += et;
+      v[3] += ed;
+      if (et > ed) {
+        v[0] += et;
+        v[1] += ed;
+      }
+      if (fabs(et - ed) <= 0x1p-16 * (et + ed) && et + ed > 0.0) v[4] = 1.0;
+    }
+    block_sum_n<5>(v, lds_d);
+    if (threadIdx.x == 0) {
+      uint64_t* r = ref_slots(a, b, t);
+      slot_put(r + 0, v[4] > 0.0 ? __longlong_as_double(0x7FF8000000000000ll) : v[0]);
+      slot_put(r + 1, v[1]);
+      slot_put(r + 2, v[2]);
+      slot_put(r + 3, v[3]);
+    }
+  }
+}
+
+// The refined draw of sequence b: sums every tile in fp64 (refine_tiles),
+// forms rho from the exact sums, the tiles' residual sums (a marked tile
+// again, with the exact rho), locates u * S in token order and rescans the
+// tile in fp64: the oracle's residual ("Speculative Decoding: small model
+// guesses, large model verifies", section 3, choice over (q - p)+ /
+// sum (q - p)+).  A residual below 2^-40 of q_k's mass draws from q_k (the
+// zero-mass reading).  Sets sh.y and the normalised S, pi(y), C_{y-1}, C_y;
+// leaves the refinement and tile slots zero.
+template <int DT, bool CUT>
+__device__ __forceinline__ void refine_draw(const VerifyArgs& a, int b, const SeqRec& rec, DrawLds& sh) {
+  const int tid = threadIdx.x, k = rec.k;
+  refine_tiles<DT, CUT>(a, b, rec, 0, a.ntile, sh.lds_d);
+  if (tid == 0) wait_mem();
+  __syncthreads();
+  uint64_t* tiles = a.tiles + (int64_t)b * a.ntile;
+  // Normalisers (every thread sums its tiles, in tile order within the thread).
+  double z[2] = {0.0, 0.0};
+  for (int t = tid; t < a.ntile; t += kThreads) {
+    uint64_t* r = ref_slots(a, b, t);
+    z[0] += slot_value(poll(a, r + 2));
+    z[1] += slot_value(poll(a, r + 3));
+  }
+  block_sum_n<2>(z, sh.lds_d);
+  const double Zt = uni(z[0]), rho = uni(z[0] / z[1]);
+  // Tile sums of the residual; marked tiles are counted and summed below.
+  double tot = 0.0;
+  int marked = 0;
+  for (int t = tid; t < a.ntile; t += kThreads) {
+    uint64_t* r = ref_slots(a, b, t);
+    const double et = slot_value(poll(a, r + 0)), ed = slot_value(poll(a, r + 1));
+    if (et != et) {
+      ++marked;
+    } else {
+      const double w = fmax(et - rho * ed, 0.0);
+      slot_put(tiles + t, w);
+      tot += w;
+    }
+  }
+  const RefineCtx c = refine_ctx<DT, CUT>(a, b, rec);
+  const int64_t lane_off = (int64_t)tid * kUnit;
+  if (block_min_int(-marked, sh.lds_i) < 0) {
+    for (int t = 0; t < a.ntile; ++t) {
+      const double et0 = slot_value(ld_dev_u64(ref_slots(a, b, t)));
+      if (et0 == et0) continue;   // not marked
+      double ws = 0.0;
+#pragma unroll 1
+      for (int e = 0; e < kUnit; ++e) {
+        double et, ed;
+        exp_pair<DT, CUT>(c.drow, c.trow, (int64_t)t * kTile + lane_off + e, a.V, c.Lt, c.Ld, c.invT, c.mt, c.md,
+                          et, ed);
+        ws += fmax(et - rho * ed, 0.0);
+      }
+      ws = block_sum(ws, sh.lds_d);
+      if (tid == 0) slot_put(tiles + t, ws);
+      if (tid == 0) tot += ws;
+    }
+  }
+  tot = block_sum(tot, sh.lds_d);
+  int mode = kModeResidual;
+  if (!(tot > 0x1p-40 * Zt)) {   // a zero residual: draw from q_k
+    mode = kModeTarget;
+    for (int t = tid; t < a.ntile; t += kThreads) slot_put(tiles + t, slot_value(ld_dev_u64(ref_slots(a, b, t) + 2)));
+  }
+  wait_mem();
+  __syncthreads();
+  const double u = (double)a.u_smp[(int64_t)b * (a.gamma + 1) + k];
+  double target;
+  const double S = uni(locate_tile(tiles, a.ntile, u, sh, target));
+  target = uni(target);
+  // The chosen tile's running sums in fp64: every thread sums its unit; the
+  // owner lane's unit is then walked by thread 0, one logit at a time.
+  const int tsel = sh.tile;
+  const int64_t jt = (int64_t)tsel * kTile;
+  double ws = 0.0;
+#pragma unroll 1
+  for (int e = 0; e < kUnit; ++e) {
+    double et, ed;
+    exp_pair<DT, CUT>(c.drow, c.trow, jt + lane_off + e, a.V, c.Lt, c.Ld, c.invT, c.mt, c.md, et, ed);
+    ws += mode == kModeResidual ? fmax(et - rho * ed, 0.0) : et;
+  }
+  double tile_tot;
+  const double off = block_exclusive_scan(ws, sh.lds_d, tile_tot);
+  const double tgt = target - sh.off;
+  const int hit = (ws > 0.0 && off <= tgt && tgt < off + ws) ? tid : INT_MAX;
+  int owner = block_min_int(hit, sh.lds_i);
+  if (owner == INT_MAX) owner = -block_min_int(ws > 0.0 ? -tid : 1, sh.lds_i);   // last lane with weight
+  if (tid == owner) sh.lane_off = off;
+  __syncthreads();
+  if (tid == 0) {
+    double run = sh.lane_off, lo = run, lo_last = run;
+    int idx = -1, last = -1;
+    if (owner >= 0) {
+#pragma unroll 1
+      for (int e = 0; e < kUnit; ++e) {
+        double et, ed;
+        exp_pair<DT, CUT>(c.drow, c.trow, jt + (int64_t)owner * kUnit + e, a.V, c.Lt, c.Ld, c.invT, c.mt, c.md, et,
+                          ed);
+        const double we = mode == kModeResidual ? fmax(et - rho * ed, 0.0) : et;
+        sh.w8d[e] = we;
+        if (we > 0.0) {
+          if (idx < 0 && tgt < run + we) {
+            idx = e;
+            lo = run;
+          }
+          last = e;
+          lo_last = run;
+        }
+        run += we;
+      }
+    }
+    if (idx < 0) {
+      idx = last;
+      lo = lo_last;
+    }
+    const double wy = idx >= 0 ? sh.w8d[idx] : 0.0;
+    sh.y = idx >= 0 ? (int)((int64_t)tsel * kTile + (int64_t)owner * kUnit + idx)
+                    : (int)min<int64_t>(a.V - 1, (int64_t)tsel * kTile + kTile - 1);   // not reached
+    sh.n_rm = mode == kModeResidual ? S / Zt : 0.0;
+    sh.n_tp = wy / S;
+    sh.n_lo = (sh.off + lo) / S;
+    sh.n_hi = (sh.off + lo + wy) / S;
+  }
+  __syncthreads();
+  for (int t = tid; t < a.ntile; t += kThreads) {
+    slot_clear(tiles + t);
+    uint64_t* r = ref_slots(a, b, t);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) slot_clear(r + i);
+  }
+}
+
 
 // The draw at the stopping position: tile values, locate, rescan.  The token
 // goes to the sequence's drawn slot, the diagnostics out.  Clears the tile and
 // residual-sum slots once read.
 template <int DT, bool VEC, bool CUT = false, bool EPS = true>
-__device__ void draw_item(const VerifyArgs& a, int b, DrawLds& sh) {
+__device__ __forceinline__ void draw_item(const VerifyArgs& a, int b, DrawLds& sh) {
   const int tid = threadIdx.x;
   const SeqRec rec = wait_rec<true>(a, b);
   if (!rec.valid) return;
@@ -525,24 +802,42 @@ __device__ void draw_item(const VerifyArgs& a, int b, DrawLds& sh) {
   const float epsS = rec.mode == kModeSaguaroEps ? eps_clamp(a, b, sh.lds_d) : 0.f;
   const SampleCoef cf = coef_of<CUT>(a, b, rec, epsS);
   int mode = rec.mode;
-  for (int t = tid; t < a.ntile; t += kThreads) (void)poll(a, tiles + t);
+  int lost = 0;   // a wait gave up: no token is drawn from what arrived
+  for (int t = tid; t < a.ntile; t += kThreads) lost |= poll(a, tiles + t) == 0ull;
   double rtot = 0.0;   // residual mass (relative to Mt) when it differs from the tile total
   if (mode == kModeSaguaro || mode == kModeSaguaroEps) {
     uint64_t* rs = (mode == kModeSaguaro ? a.rsum : a.mass) + (int64_t)b * a.nt;
-    for (int i = tid; i < a.nt; i += kThreads) rtot += slot_value(poll(a, rs + i));
+    for (int i = tid; i < a.nt; i += kThreads) {
+      const uint64_t w = poll(a, rs + i);
+      lost |= w == 0ull;
+      rtot += slot_value(w);
+    }
   }
   rtot = uni(block_sum(rtot, sh.lds_d));   // also orders the polls before the reads below
+  if (block_min_int(-lost, sh.lds_i) < 0 || (mode == kModeSaguaroEps && !(epsS == epsS))) {
+    if (tid == 0) st_dev_u64(drawn_slot(a, b), ~(uint64_t)kLostToken);
+    __syncthreads();
+    for (int t = tid; t < a.ntile; t += kThreads) slot_clear(tiles + t);
+    if (mode == kModeSaguaro)
+      for (int i = tid; i < a.nt; i += kThreads) slot_clear(a.rsum + (int64_t)b * a.nt + i);
+    if (mode == kModeSaguaroEps)
+      for (int i = tid; i < a.nt; i += kThreads) slot_clear(a.mass + (int64_t)b * a.nt + i);
+    return;
+  }
 
   const double u = (double)a.u_smp[(int64_t)b * (g + 1) + k];
   double target = 0.0, S = 0.0;
   if (tid == 0) sh.Mp = 0.0;
-  // A zero Saguaro normaliser falls back to the residual, a zero residual mass
-  // to q_k; one pass per mode.  The residual counts as zero below 2^-21 of
-  // q_k's mass (rec.Zt, draw units): where p_k and q_k agree, the fp32
-  // weights leave only rounding (a few ulp of q_k), below that.  A top-p cut
-  // can make both the same one-token distribution; otherwise only degenerate
-  // inputs get here.
+  // A zero Saguaro normaliser falls back to the residual; one pass per mode.
+  // The Saguaro weights count as zero below 2^-21 of q_k's mass (rec.Zt, draw
+  // units): where p_k and q_k agree, the fp32 weights leave only rounding (a
+  // few ulp of q_k), below that.  A residual mass below kRefineMass of q_k's
+  // (zero included: the draw from q_k) is refined in fp64.  A top-p cut can
+  // make both rows the same one-token distribution; otherwise only degenerate
+  // inputs get a zero residual.
   const double zero_res = 0x1p-21 * rec.Zt;
+  const bool diag_req = a.diag.resid_mass || a.diag.token_prob || a.diag.cdf_lo || a.diag.cdf_hi;
+  bool refine = false;
   if ((mode == kModeSaguaro || mode == kModeSaguaroEps) && rtot <= zero_res) {
     mode = kModeTarget;
     recompute_tiles<DT, CUT>(a, b, k, mode, cf, sh);
@@ -553,20 +848,33 @@ __device__ void draw_item(const VerifyArgs& a, int b, DrawLds& sh) {
     target = uni(target);
     if (mode == kModeResidual) {
       rtot = S;
-      if (S <= zero_res) S = 0.0;
+      if (S < kRefineMass * rec.Zt) {   // a small residual mass (zero included): refined
+        refine = a.refine != 0;
+        if (refine) break;
+        if (S <= zero_res) S = 0.0;     // no refinement: a zero residual draws from q_k
+      }
     }
     if (S > 0.0 || mode == kModeTarget) break;
-    mode = mode == kModeResidual ? kModeTarget : kModeResidual;
+    mode = mode == kModeResidual ? kModeTarget : kModeResidual;   // a zero Saguaro normaliser, or residual
     recompute_tiles<DT, CUT>(a, b, k, mode, cf, sh);
   }
-  with_mode<EPS>(mode, [&](auto m) { rescan_tile<DT, VEC, decltype(m)::value, CUT>(a, b, k, cf, target, sh); });
+  if (!refine) {
+    with_mode<EPS>(mode, [&](auto m) { rescan_tile<DT, VEC, decltype(m)::value, CUT>(a, b, k, cf, target, sh); });
+    if (diag_req && tid == 0) {
+      sh.n_rm = k < g ? rtot / rec.Zt : 0.0;
+      sh.n_tp = precise_weight<DT, CUT, EPS>(a, b, k, mode, cf, sh.y, sh) / S;
+      sh.n_lo = sh.lo / S;
+      sh.n_hi = sh.hi / S;
+    }
+  }
   if (tid == 0) {
-    const int y = sh.y;
-    if (a.diag.resid_mass) a.diag.resid_mass[b] = k < g ? rtot / rec.Zt : 0.0;
-    if (a.diag.token_prob) a.diag.token_prob[b] = precise_weight<DT, CUT, EPS>(a, b, k, mode, cf, y, sh) / S;
-    if (a.diag.cdf_lo) a.diag.cdf_lo[b] = sh.lo / S;
-    if (a.diag.cdf_hi) a.diag.cdf_hi[b] = sh.hi / S;
-    st_dev_u64(drawn_slot(a, b), ~(uint64_t)(uint32_t)y);
+    if (!refine) {
+      if (a.diag.resid_mass) a.diag.resid_mass[b] = sh.n_rm;
+      if (a.diag.token_prob) a.diag.token_prob[b] = sh.n_tp;
+      if (a.diag.cdf_lo) a.diag.cdf_lo[b] = sh.n_lo;
+      if (a.diag.cdf_hi) a.diag.cdf_hi[b] = sh.n_hi;
+    }
+    st_dev_u64(drawn_slot(a, b), ~(uint64_t)(refine ? kRefineToken : (uint32_t)sh.y));
   }
   // Every tile and residual-sum slot of the sequence has been read.
   __syncthreads();
@@ -582,14 +890,21 @@ __device__ void draw_item(const VerifyArgs& a, int b, DrawLds& sh) {
 // therefore streamed last, is checked, and the outputs are written.
 
 struct FinalLds {
-  int ok, y;
+  int ok, y, refine;
+  DrawLds r;   // INLINE: the refined draw
 };
 
-template <int DT>
-__device__ void final_item(const VerifyArgs& a, int b, FinalLds& sh) {
+template <int DT, bool CUT>
+__device__ __forceinline__ void refine_item(const VerifyArgs& a, int b, DrawLds& sh);
+
+// INLINE: a refined draw is taken here, by this work-group, instead of by
+// refine_kernel (kernels with registers to spare for it).
+template <int DT, bool INLINE = false>
+__device__ __forceinline__ void final_item(const VerifyArgs& a, int b, FinalLds& sh) {
   const int tid = threadIdx.x;
   const int g = a.gamma, R = 2 * g + 1, r = 2 * g;
-  const SeqRec rec = wait_rec<false>(a, b);
+  bool lost_rec;
+  const SeqRec rec = wait_rec<false>(a, b, lost_rec);
   if (tid < 16) {
     double M, z;
     float mr;
@@ -600,18 +915,26 @@ __device__ void final_item(const VerifyArgs& a, int b, FinalLds& sh) {
       const bool read = !a.early || (rec.valid && rec.k == g);
       if (ok && read && a.diag.row_max) a.diag.row_max[(int64_t)b * R + r] = (double)mr * temp_coef(a, b).invT;
       if (ok && read && a.diag.row_logZ) a.diag.row_logZ[(int64_t)b * R + r] = M * 0.69314718055994530942 + log(z);
+      sh.y = -1;
+      sh.refine = 0;
       if (rec.valid) {
         uint64_t* ys = drawn_slot(a, b);
-        sh.y = (int)(uint32_t)~poll(a, ys);
+        const uint64_t w = poll(a, ys);
+        const uint32_t y = (uint32_t)~w;
+        sh.refine = w != 0ull && y == kRefineToken;
+        sh.y = (w == 0ull || y == kLostToken || y == kRefineToken) ? -1 : (int)y;   // -1: lost (or refined below)
         slot_clear(ys);
       }
     }
   }
   __syncthreads();
-  if (rec.valid) {   // an invalid decision wrote its outputs already
+  const bool refine = uni(sh.refine) != 0;   // the token at k comes from refine_kernel
+  if (lost_rec) {   // no decision arrived: nothing can be reported but an invalid sequence
+    write_invalid(a, b, tid);
+  } else if (rec.valid) {   // an invalid decision wrote its outputs already
     const int k = rec.k;
-    if (!sh.ok && (!a.early || k == g)) {   // early exit reads target row gamma only for the bonus
-      write_invalid(a, b, tid);
+    if ((!sh.ok && (!a.early || k == g)) || (sh.y < 0 && !refine)) {   // early exit reads target row
+      write_invalid(a, b, tid);   // gamma only for the bonus; sh.y < 0: the draw was lost
     } else {
       const int64_t orow = (int64_t)b * (g + 1);
       if (tid <= g) {
@@ -645,7 +968,43 @@ __device__ void final_item(const VerifyArgs& a, int b, FinalLds& sh) {
       slot_clear32(f + kTestsWord);
     }
     slot_clear32(f);
+    if (refine)   // refine_item reads the record, then clears it and the pending word
+      __hip_atomic_store(f + kPendingWord, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+      clear_rec(a.seq + b);
+  }
+  if constexpr (INLINE) {
+    if (refine) {
+      __syncthreads();
+      refine_item<DT, false>(a, b, sh.r);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Refinement: the refined residual draws of a call (see kRefineMass), after
+// its other kernels.  One work-group per sequence; those with no pending
+// refinement return at once.
+template <int DT, bool CUT>
+__device__ __forceinline__ void refine_item(const VerifyArgs& a, int b, DrawLds& sh) {
+  unsigned* f = a.flag + (int64_t)b * kFlagStride;
+  if (ld_dev_u32(f + kPendingWord) == 0u) return;
+  bool lost;
+  const SeqRec rec = wait_rec<false>(a, b, lost);
+  if (!lost && rec.valid && rec.k < a.gamma) {
+    refine_draw<DT, CUT>(a, b, rec, sh);
+    if (threadIdx.x == 0) {
+      a.out_tokens[(int64_t)b * (a.gamma + 1) + rec.k] = sh.y;
+      if (a.diag.resid_mass) a.diag.resid_mass[b] = sh.n_rm;
+      if (a.diag.token_prob) a.diag.token_prob[b] = sh.n_tp;
+      if (a.diag.cdf_lo) a.diag.cdf_lo[b] = sh.n_lo;
+      if (a.diag.cdf_hi) a.diag.cdf_hi[b] = sh.n_hi;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
     clear_rec(a.seq + b);
+    slot_clear32(f + kPendingWord);
   }
 }
 

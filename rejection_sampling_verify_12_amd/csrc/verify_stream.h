@@ -159,7 +159,7 @@ __device__ __forceinline__ void stream_item(const VerifyArgs& a, int b, int r, i
 // Draft row gamma (outcome prediction only): one chunk's lane leaders and
 // NaN flag, nothing else.
 template <int DT, bool VEC, int U>
-__device__ void leader_item(const VerifyArgs& a, int b, int c, StreamLds& sh) {
+__device__ __forceinline__ void leader_item(const VerifyArgs& a, int b, int c, StreamLds& sh) {
   constexpr int kEs = DT == kBF16 ? 2 : 4;
   const int64_t ridx = (int64_t)b * (a.gamma + 1) + a.gamma;
   const void* row = static_cast<const char*>(a.draft) + ridx * a.V * kEs;

@@ -207,3 +207,25 @@ def test_verify_ex_rejects_bad_top_p():
                                 FAKE, FAKE, None, None, None, None, ctypes.byref(opts), FAKE,
                                 1 << 30, None)
         assert st == R.SPEC_EINVAL, (top_p, early)
+
+
+def test_lost_decision_record_decodes_without_indices(tmp_path):
+    """A decision record whose bounded wait gave up decodes as an invalid
+    sequence with k = 0 (no index is derived from an unwritten word); a
+    complete record decodes to what was stored.  The real device header is
+    compiled host-only and run here (no GPU)."""
+    import shutil
+    import subprocess
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc not available")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    exe = str(tmp_path / "rec_decode_check")
+    build = subprocess.run([hipcc, "--offload-host-only", "-std=c++17", "-x", "hip",
+                            "-I", os.path.join(root, "include"),
+                            "-I", os.path.join(root, "rejection_sampling_verify_12_amd", "csrc"),
+                            os.path.join(root, "tests", "host", "rec_decode_check.hip"), "-o", exe],
+                           capture_output=True, text=True)
+    assert build.returncode == 0, build.stderr[-2000:]
+    run = subprocess.run([exe], capture_output=True, text=True)
+    assert run.returncode == 0, run.stdout + run.stderr

@@ -439,3 +439,47 @@ def test_small_peaked_rows(V, dtype, mode, eps):
     batch = random_batch(24, 4, V, dtype, 1.0, seed=7300 + V, scale=6.0, sigma=0.3)
     H.parity(batch, mode, eps).check()
     H.parity(batch, mode, eps, early=True).check()
+
+
+# --------------------------------------------------------------------------- a wait that gives up
+
+@pytest.mark.parametrize("case", ["bf16", "f32", "early", "saguaro_eps", "predict", "greedy"])
+def test_error_word_set_before_the_call(case):
+    """The workspace's error word set from the host before the call (as after
+    a bounded wait that gave up): every wait then gives up within 64 polls, so
+    every kernel returns; no sequence is reported valid from a wait that gave
+    up, and a decision taken with the word set reports its sequence invalid -
+    so every sequence comes back invalid - and the word stays set."""
+    import rejection_sampling_verify_12_amd as R
+    dtype = "f32" if case == "f32" else "bf16"
+    batch = random_batch(16, 4, 40000, dtype, 1.0, seed=4400)
+    H.say(f"[give-up] case={case} B={batch.B} gamma={batch.gamma} V={batch.V} {dtype}")
+    db = H.to_device(batch)
+    dt = R.SPEC_F32 if dtype == "f32" else R.SPEC_BF16
+    if case == "greedy":
+        ws = R.new_workspace(R.spec_greedy_workspace_bytes(batch.B, batch.gamma, batch.V, dt), "cuda")
+    else:
+        ws = R.new_workspace(R.spec_workspace_bytes(batch.B, batch.gamma, batch.V, dt), "cuda")
+    ws[:4].view(torch.int32).fill_(1)
+    out = R.alloc_outputs(batch.B, batch.gamma, "cuda")
+    for t in (out.tokens, out.accepted, out.first_reject, out.out_len):
+        t.fill_(7)
+    out.accept_mask.fill_(7)
+    args = (db.draft, db.target, db.tokens, db.u_accept, db.u_sample, batch.T)
+    if case in ("bf16", "f32"):
+        R.spec_verify(*args, in_len=db.in_len, out=out, workspace=ws)
+    elif case == "early":
+        R.spec_verify_early(*args, in_len=db.in_len, out=out, workspace=ws)
+    elif case == "saguaro_eps":
+        R.spec_verify_saguaro(*args, in_len=db.in_len, out=out, workspace=ws, eps=1e-8)
+    elif case == "predict":
+        R.spec_verify_predict(*args, in_len=db.in_len, out=out, workspace=ws)
+    else:
+        R.spec_verify_greedy(db.target, db.tokens, in_len=db.in_len, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    assert int(ws[:4].view(torch.int32).item()) == 1
+    assert (out.accepted.cpu().numpy() == -1).all()
+    assert (out.tokens.cpu().numpy() == -1).all()
+    assert (out.first_reject.cpu().numpy() == -1).all()
+    assert (out.accept_mask.cpu().numpy() == 0).all()
+    np.testing.assert_array_equal(out.out_len.cpu().numpy(), batch.in_len)
