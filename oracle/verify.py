@@ -190,7 +190,6 @@ class SeqResult:
     cdf_lo: float                 # C_{y-1}
     cdf_hi: float                 # C_y
     zero_margin: float = np.inf   # S at a rejection with S > 0 (its distance from the S = 0 fallback)
-    draw_scale: float = 1.0       # S for a residual draw, else 1: the running sums' unnormalised unit
 
 
 def _zero_margin(S: float, k: int, gamma: int) -> float:
@@ -199,14 +198,6 @@ def _zero_margin(S: float, k: int, gamma: int) -> float:
     p_k and q_k; a residual that small is within float rounding of zero, so
     the draw is a boundary case like a u within rounding of a running sum."""
     return S if (k < gamma and S > 0.0) else np.inf
-
-
-def _draw_scale(S: float, k: int, gamma: int, mode: str) -> float:
-    """The unit of a draw's running sums before normalisation: a residual
-    draw picks the first j with u * S < sum_{i <= j} w_i (reading C6), so its
-    thresholds are the unnormalised running sums, S times the normalised
-    ones; any other draw's distribution sums to 1."""
-    return S if (mode == "residual" and k < gamma and S > 0.0) else 1.0
 
 
 def _invalid(gamma: int, in_len: int) -> SeqResult:
@@ -293,7 +284,6 @@ def verify_one(draft64, target64, tokens, u_accept, u_sample, T, mode="residual"
         tokens=out, out_len=int(in_len) + k + 1, a=a,
         acc_margin=np.minimum(np.abs(ua - a), topp_margin),
         sample_margin=min(us - lo, hi - us, topp_margin), zero_margin=_zero_margin(S, k, gamma),
-        draw_scale=_draw_scale(S, k, gamma, mode),
         row_max=np.concatenate([pm, qm]), row_logZ=np.concatenate([plz, qlz]),
         px=px, qx=qx, resid_mass=S, token_prob=float(pi[y]), cdf_lo=lo, cdf_hi=hi)
 
@@ -366,7 +356,7 @@ def verify_early_one(draft64, target64, tokens, u_accept, u_sample, T, mode="res
         valid=True, accepted=k, first_reject=k if k < gamma else -1, mask=(1 << k) - 1,
         tokens=out, out_len=int(in_len) + k + 1, a=a, acc_margin=np.abs(ua - a),
         sample_margin=min(us - lo, hi - us), zero_margin=_zero_margin(S, k, gamma),
-        draw_scale=_draw_scale(S, k, gamma, mode), row_max=row_max, row_logZ=row_logZ,
+        row_max=row_max, row_logZ=row_logZ,
         px=px, qx=qx, resid_mass=S, token_prob=float(pi[y]), cdf_lo=lo, cdf_hi=hi)
 
 

@@ -6,13 +6,15 @@ Comparison rule (tolerances of the verification contract):
   committed lengths must equal the oracle's exactly;
 * the one excuse is a draw whose uniform lies within 1e-6 of its threshold:
   the first differing decision of a sequence (an accept test, or the sampled
-  token) is excused iff the oracle's margin there is below 1e-6; that
-  sequence's later outputs are not compared, and the excused rate must stay
-  at or below 1e-4 of the draws;
+  token) is excused iff the oracle's margin there is below 1e-6, measured in
+  the normalised units of the distribution drawn from; that sequence's later
+  outputs are not compared.  Excusals are counted over the whole session
+  (TOTALS), and the excused rate over every draw compared must stay at or
+  below 1e-4 (asserted by the session's last parity test);
 * normalised probabilities (p(x), q(x), residual mass, pi(y)) agree within
   1e-5 relative (pi(y) below 1e-4: 1e-9 absolute); log-normalisers within
-  1e-5 absolute; the running sums C_{y-1}, C_y within 1e-6 absolute (the
-  boundary window).
+  1e-5 absolute; the running sums C_{y-1}, C_y of the normalised distribution
+  within 1e-6 absolute (the boundary window).
 """
 from __future__ import annotations
 
@@ -124,14 +126,20 @@ class Report:
         self.failures += o.failures
 
     def check(self):
+        """No unexcused difference; the excusals join the session's totals."""
+        TOTALS.merge(dataclasses.replace(self, failures=[]))
         assert not self.failures, "\n".join(self.failures[:20])
-        assert self.excused <= max(1, 1e-4 * self.n_draws), (self.excused, self.n_draws)
 
     def __str__(self):
         return (f"seqs={self.n_seq} draws={self.n_draws} excused={self.excused} "
                 f"boundary={self.boundary_draws} max|a err|={self.max_a_err:.3g} "
                 f"max|C err|={self.max_cdf_err:.3g} max prob rel={self.max_prob_rel:.3g} "
                 f"max|pi(y) err|={self.max_token_prob_abs:.3g}")
+
+
+# Every checked comparison of the session: the excused rate is a property of
+# the whole suite, not of one test.
+TOTALS = Report()
 
 
 def _rel(a, b):
@@ -156,10 +164,7 @@ def compare(batch: W.Batch, gpu: dict, ref: dict, check_diag: bool = True) -> Re
         # A draw is a boundary case when u is within rounding of a running sum,
         # or when the residual mass is within rounding of the S = 0 fallback.
         zero_boundary = getattr(r, "zero_margin", np.inf) < EXCUSE
-        # A residual draw compares u * S with the unnormalised running sums
-        # (reading C6), so its distances are measured in those units.
-        scale = getattr(r, "draw_scale", 1.0)
-        draw_boundary = r.sample_margin * scale < EXCUSE or zero_boundary
+        draw_boundary = r.sample_margin < EXCUSE or zero_boundary
         rep.boundary_draws += int((r.acc_margin < EXCUSE).sum()) + int(draw_boundary)
         excused = False
         for i in range(g):
@@ -220,7 +225,7 @@ def compare(batch: W.Batch, gpu: dict, ref: dict, check_diag: bool = True) -> Re
             rep.max_token_prob_abs = max(rep.max_token_prob_abs, tp_err)
             if tp_err > (PROB_RTOL * r.token_prob if r.token_prob >= 1e-4 else 1e-9):
                 rep.failures.append(f"seq {b}: token_prob {d['token_prob'][b]} vs {r.token_prob}")
-            ce = max(abs(d["cdf_lo"][b] - r.cdf_lo), abs(d["cdf_hi"][b] - r.cdf_hi)) * scale
+            ce = max(abs(d["cdf_lo"][b] - r.cdf_lo), abs(d["cdf_hi"][b] - r.cdf_hi))
             rep.max_cdf_err = max(rep.max_cdf_err, ce)
             if ce > EXCUSE:
                 rep.failures.append(f"seq {b}: running-sum error {ce:.3g}")

@@ -167,9 +167,6 @@ def test_accept_threshold_on_toy():
     assert abs(r.cdf_lo - 0.6) < 1e-14 and abs(r.cdf_hi - 0.8) < 1e-14
     assert abs(r.sample_margin - 0.1) < 1e-12
     assert abs(r.zero_margin - 0.05) < 1e-15   # the residual mass: far from the S = 0 fallback
-    assert abs(r.draw_scale - 0.05) < 1e-15    # u * S against the unnormalised running sums
-    assert _one(d, t, [0], [0.95], [0.7, 0.0], mode="saguaro").draw_scale == 1.0
-    assert _one(d, t, [0], [0.0], [0.7, 0.7]).draw_scale == 1.0   # accepted: the bonus draw from q
 
 
 def test_special_cases():
