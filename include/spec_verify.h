@@ -63,7 +63,8 @@ enum spec_status {
   SPEC_EINVAL = -1,     /* bad size, temperature, eps or NULL pointer */
   SPEC_EDTYPE = -2,     /* dtype is neither SPEC_F32 nor SPEC_BF16 */
   SPEC_EWORKSPACE = -3, /* workspace NULL or smaller than required */
-  SPEC_ELAUNCH = -4     /* a kernel launch failed */
+  SPEC_ELAUNCH = -4,    /* a kernel launch failed */
+  SPEC_ESCRATCH = -5    /* spec_verify_noalloc: the sizes need more than its static scratch */
 };
 
 enum spec_dtype { SPEC_F32 = 0, SPEC_BF16 = 1 };
@@ -315,6 +316,27 @@ int spec_verify_greedy(const void* target_logits, int dtype, const int32_t* draf
  * once when none is 0 (no fallback pass is needed).  Enqueues only.
  */
 int spec_synthetic_busy(int64_t ns, const int32_t* hit, int n, void* stream);
+
+/*
+ * spec_verify without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  It allocates nothing.  Its workspace is a static
+ * array of 16 MiB in the library's device memory, one per GPU (held until the
+ * process ends), which the call clears with a kernel before it runs.  Arguments,
+ * outputs and results are those of spec_verify; sizes whose workspace
+ * (spec_workspace_bytes) exceeds 16 MiB - at gamma = 8, V = 152064 in bf16,
+ * B above 384 - return SPEC_ESCRATCH before anything is enqueued.  Every call
+ * on one GPU shares that array: calls that overlap on one GPU (different
+ * streams, or host threads) race and give undefined results; serialise them.
+ * The array keeps the last call's contents, including a set error word (see
+ * spec_workspace_bytes), which the next call clears.
+ */
+int spec_verify_noalloc(const void* draft_logits, const void* target_logits, int dtype,
+                        const int32_t* draft_tokens, const float* u_accept, const float* u_sample,
+                        int B, int gamma, int V, float temperature, const int32_t* in_len,
+                        int32_t* out_tokens, int32_t* out_accepted, int32_t* out_first_reject,
+                        uint64_t* out_accept_mask, int32_t* out_len, const spec_diag* diag,
+                        void* stream);
 
 /* A static, human-readable description of a status code. */
 const char* spec_status_str(int status);

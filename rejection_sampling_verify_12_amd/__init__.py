@@ -15,13 +15,13 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libspecverify.so")
 
-SPEC_OK, SPEC_EINVAL, SPEC_EDTYPE, SPEC_EWORKSPACE, SPEC_ELAUNCH = 0, -1, -2, -3, -4
+SPEC_OK, SPEC_EINVAL, SPEC_EDTYPE, SPEC_EWORKSPACE, SPEC_ELAUNCH, SPEC_ESCRATCH = 0, -1, -2, -3, -4, -5
 SPEC_F32, SPEC_BF16 = 0, 1
 
 EXPORTED = ("spec_workspace_bytes", "spec_verify", "spec_verify_saguaro",
             "spec_predict_workspace_bytes", "spec_predict_outcomes", "spec_verify_predict",
             "spec_greedy_workspace_bytes", "spec_verify_greedy", "spec_verify_early",
-            "spec_verify_ex", "spec_synthetic_busy", "spec_status_str")
+            "spec_verify_ex", "spec_synthetic_busy", "spec_verify_noalloc", "spec_status_str")
 
 
 class SpecOptions(ctypes.Structure):
@@ -74,6 +74,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.spec_greedy_workspace_bytes.restype = sz
     lib.spec_verify_greedy.argtypes = [vp, i32, vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.spec_verify_greedy.restype = i32
+    lib.spec_verify_noalloc.argtypes = verify_args[:-3] + [vp]
+    lib.spec_verify_noalloc.restype = i32
     lib.spec_status_str.argtypes = [i32]
     lib.spec_status_str.restype = ctypes.c_char_p
     _lib = lib
@@ -206,6 +208,34 @@ def spec_verify(draft_logits, target_logits, draft_tokens, u_accept, u_sample, t
     """Residual-mode verification of a [B, gamma+1, V] batch (see spec_verify.h)."""
     return _verify_call(False, draft_logits, target_logits, draft_tokens, u_accept, u_sample,
                         temperature, in_len, out, diag, workspace, stream)
+
+
+def spec_verify_noalloc(draft_logits, target_logits, draft_tokens, u_accept, u_sample, temperature,
+                        in_len=None, out=None, diag=False, stream=None) -> VerifyOut:
+    """spec_verify without a workspace: the library's static per-device
+    scratch (see spec_verify.h; calls on one GPU must not overlap).  With
+    ``out`` given, nothing is allocated here either."""
+    lib = load_library()
+    B, G1, V = draft_logits.shape
+    gamma = G1 - 1
+    if target_logits.shape != draft_logits.shape or target_logits.dtype != draft_logits.dtype:
+        raise ValueError("draft and target logits must share shape and dtype")
+    _check_dev(draft_logits, target_logits, draft_tokens, u_accept, u_sample, in_len)
+    dev = draft_logits.device
+    if out is None:
+        out = alloc_outputs(B, gamma, dev, diag)
+    dg = None
+    if out.diag is not None:
+        dg = SpecDiag(*[out.diag[k].data_ptr() for k in DIAG_FIELDS])
+    st = lib.spec_verify_noalloc(draft_logits.data_ptr(), target_logits.data_ptr(),
+                                 _dtype_code(draft_logits), draft_tokens.data_ptr(), u_accept.data_ptr(),
+                                 u_sample.data_ptr(), B, gamma, V, float(temperature), _ptr(in_len),
+                                 out.tokens.data_ptr(), out.accepted.data_ptr(), out.first_reject.data_ptr(),
+                                 out.accept_mask.data_ptr(), out.out_len.data_ptr(),
+                                 ctypes.byref(dg) if dg is not None else None, _stream_handle(stream, dev))
+    if st != SPEC_OK:
+        raise SpecError(st)
+    return out
 
 
 def spec_verify_saguaro(draft_logits, target_logits, draft_tokens, u_accept, u_sample,

@@ -54,6 +54,7 @@
 #include <limits.h>
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 
 namespace sv {
 
@@ -428,6 +429,36 @@ static int verify_impl(const void* draft, const void* target, int dtype, const i
   return e == hipSuccess ? SPEC_OK : SPEC_ELAUNCH;
 }
 
+// ---------------------------------------------------------------------------
+// The allocation-free entry point's workspace: one array per device, in the
+// library's own device memory (it lives until the process ends).  Host code
+// uses only its device address from hipGetSymbolAddress, fetched once per
+// device with that device current.
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+static std::atomic<void*> g_scratch_ptr[64];
+static std::mutex g_scratch_mu;
+
+static hipError_t scratch_address(void*& ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (ptr) return hipSuccess;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (ptr) return hipSuccess;
+  void* p = nullptr;
+  e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return e;
+  if (!p) return hipErrorInvalidSymbol;
+  g_scratch_ptr[dev].store(p, std::memory_order_release);
+  ptr = p;
+  return hipSuccess;
+}
+
 }  // namespace sv
 
 extern "C" {
@@ -507,6 +538,32 @@ int spec_verify_ex(const void* draft_logits, const void* target_logits, int dtyp
                          o.temperature, top_p);
 }
 
+int spec_verify_noalloc(const void* draft_logits, const void* target_logits, int dtype,
+                        const int32_t* draft_tokens, const float* u_accept, const float* u_sample,
+                        int B, int gamma, int V, float temperature, const int32_t* in_len,
+                        int32_t* out_tokens, int32_t* out_accepted, int32_t* out_first_reject,
+                        uint64_t* out_accept_mask, int32_t* out_len, const spec_diag* diag,
+                        void* stream) {
+  if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_EDTYPE;
+  if (!sv::sizes_ok(B, gamma, V)) return SPEC_EINVAL;
+  if (B == 0) return SPEC_OK;
+  const size_t need = sv::layout(B, gamma, V).total;
+  if (need > sv::kScratchBytes) return SPEC_ESCRATCH;
+  void* ws = nullptr;
+  if (sv::scratch_address(ws) != hipSuccess) return SPEC_ELAUNCH;
+  // The workspace protocol wants it zero on entry; a completed call leaves it
+  // so, but one whose wait gave up does not, so every call clears it first.
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  const size_t n16 = (need + 15) / 16;
+  const unsigned grid = (unsigned)std::min<size_t>((n16 + sv::kThreads * 4 - 1) / (sv::kThreads * 4), 2048);
+  hipLaunchKernelGGL(sv::zero_kernel, dim3(grid), dim3(sv::kThreads), 0, st, static_cast<uint4*>(ws), n16);
+  if (hipGetLastError() != hipSuccess) return SPEC_ELAUNCH;
+  return sv::verify_impl(draft_logits, target_logits, dtype, draft_tokens, u_accept, u_sample, B,
+                         gamma, V, temperature, in_len, out_tokens, out_accepted, out_first_reject,
+                         out_accept_mask, out_len, diag, ws, sv::kScratchBytes, stream, 0, 0.f);
+}
+
 const char* spec_status_str(int status) {
   switch (status) {
     case SPEC_OK: return "ok";
@@ -514,6 +571,7 @@ const char* spec_status_str(int status) {
     case SPEC_EDTYPE: return "unknown dtype (expected SPEC_F32 or SPEC_BF16)";
     case SPEC_EWORKSPACE: return "workspace missing or smaller than spec_workspace_bytes()";
     case SPEC_ELAUNCH: return "kernel launch failed";
+    case SPEC_ESCRATCH: return "sizes need more workspace than spec_verify_noalloc's static scratch (16 MiB)";
     default: return "unknown status";
   }
 }

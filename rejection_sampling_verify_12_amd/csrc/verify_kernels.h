@@ -146,6 +146,13 @@ __global__ __launch_bounds__(kThreads) void draw_kernel(VerifyArgs a) {
   draw_item<DT, VEC, CUT>(a, blockIdx.x, sh);
 }
 
+// Zero n 16-byte words (a kernel, not a memset, so a captured call records
+// no memset node).
+__global__ __launch_bounds__(kThreads) void zero_kernel(uint4* p, size_t n) {
+  const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+  for (size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (size_t)gridDim.x * kThreads) p[i] = z;
+}
+
 template <int DT>
 __global__ __launch_bounds__(kThreads) void final_kernel(VerifyArgs a) {
   __shared__ FinalLds sh;

@@ -229,3 +229,19 @@ def test_lost_decision_record_decodes_without_indices(tmp_path):
     assert build.returncode == 0, build.stderr[-2000:]
     run = subprocess.run([exe], capture_output=True, text=True)
     assert run.returncode == 0, run.stdout + run.stderr
+
+
+def test_noalloc_rejects_sizes_beyond_its_scratch():
+    """spec_verify_noalloc checks sizes against its 16 MiB static scratch (and
+    the usual arguments) before anything is enqueued or any device is used."""
+    lib = R.load_library()
+
+    def call(B, gamma, V, dtype=R.SPEC_BF16, T=1.0):
+        return lib.spec_verify_noalloc(FAKE, FAKE, dtype, FAKE, FAKE, FAKE, B, gamma, V, T, None, FAKE,
+                                       FAKE, None, None, None, None, None)
+    assert R.spec_workspace_bytes(512, 8, 152064, R.SPEC_BF16) > 16 << 20
+    assert call(512, 8, 152064) == R.SPEC_ESCRATCH
+    assert call(4, 3, 1000, dtype=9) == R.SPEC_EDTYPE
+    assert call(4, 64, 1000) == R.SPEC_EINVAL
+    assert call(0, 3, 1000) == R.SPEC_OK
+    assert "16 MiB" in R.spec_status_str(R.SPEC_ESCRATCH)
