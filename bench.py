@@ -8,11 +8,23 @@ synthetic logits already resident in HBM.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--mode residual]
 
-Prints one JSON line.  value = verified draft positions per second,
-B * gamma / (seconds per call).  The roofline block prices the whole call
-(its algorithmic bytes over its event-timed duration) against the MI355X HBM
-peak of 8 TB/s; cpu_baseline times the fp64 oracle on a bounded sample of
-the same workload on this host.
+Prints one JSON line.
+* value = verified draft positions per second, B * gamma / ms_per_step, where
+  ms_per_step is the wall time of the K timed calls (synchronised on both
+  sides) over K.
+* Before the timed calls: W untimed calls, then more until --warmup-ms of
+  sustained work has passed (after idle, this GPU runs calls ~20% slower for
+  the first ~20 ms of sustained work; see the design notes).
+* roofline prices the call's algorithmic bytes against the MI355X HBM peak
+  of 8 TB/s, over the mean HIP-event time of one call (achieved, frac) and
+  over ms_per_step (achieved_per_step, frac_per_step: also the few
+  microseconds between back-to-back calls); attainable_read is a plain read of
+  the logits with the same loads.
+* statistics: the observed mean tokens per round against the closed form
+  E[N] of the speculative-decoding blog's section 4 for these rows, and with
+  --predict the outcome-prediction hit rate against its enumerated value.
+* cpu_baseline times the fp64 oracle on the same workload on this host's
+  cores (one process, then a pool of processes over the sequences).
 """
 from __future__ import annotations
 
@@ -36,6 +48,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--warmup-ms", type=float, default=300.0,
+                    help="untimed calls continue until this much wall time of sustained work has passed")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--mode", choices=("residual", "saguaro", "greedy"), default="residual",
                     help="greedy: temperature -> 0 verification of the draft's own argmax tokens "
@@ -61,8 +75,10 @@ def parse():
     ap.add_argument("--ssd-target-us", type=float, default=330.0, help="target model time per round")
     ap.add_argument("--sets", type=int, default=0,
                     help="input sets to rotate through (0: enough for > 1 GB)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="wall-clock budget of the CPU oracle sample")
+    ap.add_argument("--cpu-seconds", type=float, default=8.0,
+                    help="wall-clock budget of each CPU oracle leg")
+    ap.add_argument("--cpu-workers", type=int, default=0,
+                    help="processes of the pooled CPU oracle leg (0: min(16, os.cpu_count()))")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device copy of this many bytes (counter calibration)")
@@ -92,26 +108,65 @@ def traffic_record(workload: str, mode: str):
     return rec.get("bytes_per_call")
 
 
-def cpu_baseline(batch, mode: str, eps: float, budget_s: float, tokens=None) -> dict:
-    """The fp64 oracle on the first sequences of the same workload, one thread."""
+_CPU_BATCH = None
+_CPU_ARGS = None
+
+
+def _oracle_seq(n):
+    """One sequence through the fp64 oracle (a pool worker's task)."""
     import oracle as O
     import workloads as W
+    batch, mode, eps, tokens = _CPU_ARGS
+    if mode == "greedy":
+        O.verify_greedy_one(W.decode_f64(batch.target[n], batch.dtype), tokens[n])
+    else:
+        O.verify_one(W.decode_f64(batch.draft[n], batch.dtype), W.decode_f64(batch.target[n], batch.dtype),
+                     batch.draft_tokens[n], batch.u_accept[n], batch.u_sample[n], batch.T, mode, eps)
+    return n
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(batch, mode: str, eps: float, budget_s: float, tokens, workers: int) -> dict:
+    """The fp64 oracle on the same workload: one process on the first
+    sequences (bounded by budget_s), then a pool of `workers` processes over
+    every sequence (bounded likewise).  Runs before the GPU is touched (the
+    pool forks)."""
+    import multiprocessing as mp
+    global _CPU_ARGS
+    _CPU_ARGS = (batch, mode, eps, tokens)
     t0 = time.perf_counter()
-    n = 0
-    while n < batch.B:
-        if mode == "greedy":
-            O.verify_greedy_one(W.decode_f64(batch.target[n], batch.dtype), tokens[n])
-        else:
-            O.verify_one(W.decode_f64(batch.draft[n], batch.dtype),
-                         W.decode_f64(batch.target[n], batch.dtype), batch.draft_tokens[n],
-                         batch.u_accept[n], batch.u_sample[n], batch.T, mode, eps)
-        n += 1
-        if time.perf_counter() - t0 > budget_s:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": n * batch.gamma / dt, "unit": "positions/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {n} of {batch.B} sequences of {batch.name}, fp64 numpy, one thread, "
-                      f"{dt:.1f} s"}
+    n1 = 0
+    while n1 < batch.B and time.perf_counter() - t0 < budget_s:
+        _oracle_seq(n1)
+        n1 += 1
+    dt1 = time.perf_counter() - t0
+    one = n1 * batch.gamma / dt1
+    ctx = mp.get_context("fork")
+    with ctx.Pool(workers) as pool:
+        pool.map(_oracle_seq, range(min(workers, batch.B)))   # start-up outside the timing
+        t0 = time.perf_counter()
+        done = 0   # sequences verified (passes over the batch until min(2 s, budget) have elapsed)
+        while time.perf_counter() - t0 < min(2.0, budget_s) or done == 0:
+            for s0 in range(0, batch.B, 4 * workers):
+                pool.map(_oracle_seq, range(s0, min(batch.B, s0 + 4 * workers)), chunksize=1)
+                done += min(batch.B, s0 + 4 * workers) - s0
+                if time.perf_counter() - t0 > budget_s:
+                    break
+        dtp = time.perf_counter() - t0
+    return {"value": done * batch.gamma / dtp, "unit": "positions/s", "cores": workers, "kind": "oracle",
+            "sample": f"{done} sequences (passes over the {batch.B} of {batch.name}) over {workers} "
+                      f"processes in {dtp:.1f} s; one process: first {n1} sequences in {dt1:.1f} s",
+            "value_one_core": one, "cpu_count": os.cpu_count(), "cpu_model": cpu_model()}
 
 
 def ssd_main(args):
@@ -165,6 +220,84 @@ def ssd_main(args):
         "data": "synthetic", "source_digest": source_digest()}), flush=True)
 
 
+def gpu_clocks() -> dict:
+    """Current gfx and memory clocks (MHz) of GPU 0, if amdsmi can read them."""
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        h = amdsmi.amdsmi_get_processor_handles()[0]
+        g = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)
+        m = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.MEM)
+        return {"gfx_mhz": g.get("clk"), "mem_mhz": m.get("clk")}
+    except Exception as e:   # a statistic, not a requirement
+        return {"error": type(e).__name__}
+
+
+def acceptance_statistics(d, t, T: float, gamma: int, chunk: int = 32):
+    """alpha[b, i] = sum_j min(p_ij, q_ij), p = softmax(draft_i / T),
+    q = softmax(target_i / T), for i < gamma, in fp64 on the GPU: the
+    per-position acceptance probability when x_i ~ p_i (speculative-decoding
+    blog, section 3).  A statistic of the workload; not on the measured path."""
+    import torch
+    B = d.shape[0]
+    alpha = torch.empty((B, gamma), dtype=torch.float64, device=d.device)
+    for b0 in range(0, B, chunk):
+        p = torch.softmax(d[b0:b0 + chunk, :gamma].double() / T, -1)
+        q = torch.softmax(t[b0:b0 + chunk, :gamma].double() / T, -1)
+        alpha[b0:b0 + chunk] = torch.minimum(p, q).sum(-1)
+    return alpha
+
+
+def tokens_per_round(alpha, accepted):
+    """Observed mean tokens per round (k + 1) against its expectation for these
+    rows: E[N_b] = sum_{j=0..gamma} prod_{i<j} alpha_bi, which is the blog's
+    section 4 closed form (1 - a^(gamma+1)) / (1 - a) when every alpha_bi = a."""
+    import torch
+    B, g = alpha.shape
+    ones = torch.ones((B, 1), dtype=alpha.dtype, device=alpha.device)
+    surv = torch.cat([ones, torch.cumprod(alpha, 1)], 1)          # P(N > j), j = 0..gamma
+    j = torch.arange(g + 1, dtype=alpha.dtype, device=alpha.device)
+    en = surv.sum(1)
+    var = ((2 * j + 1) * surv).sum(1) - en * en
+    k = torch.as_tensor(accepted, device=alpha.device)
+    valid = k >= 0
+    obs = (k[valid].double() + 1).mean().item()
+    exp = en[valid].mean().item()
+    se = (var[valid].sum().sqrt() / valid.sum()).item()
+    a_bar = alpha[valid].mean().item()
+    return {"observed": obs, "expected": exp, "se": se, "z": (obs - exp) / se if se > 0 else None,
+            "closed_form_at_mean_alpha": (1 - a_bar ** (g + 1)) / (1 - a_bar), "mean_alpha": a_bar,
+            "sequences": int(valid.sum().item())}
+
+
+def hit_rate_statistics(d, t, T: float, gamma: int, alpha, cand, hit):
+    """Outcome-prediction hit rate against its enumerated value ("Speculative
+    Speculative Decoding (Saguaro)", section 3.1): with K the first rejection
+    (x_i ~ p_i, uniforms uniform), P(hit) = sum_{k<gamma} P(K=k) sum over the
+    draft's top-3 at k of the residual (q_k - p_k)+ / (1 - alpha_k), plus
+    P(K=gamma) times q_gamma's mass on the top-3 at gamma.  Residual mode."""
+    import torch
+    B = d.shape[0]
+    ones = torch.ones((B, 1), dtype=torch.float64, device=d.device)
+    surv = torch.cat([ones, torch.cumprod(alpha, 1)], 1)
+    pk = torch.cat([surv[:, :gamma] * (1 - alpha), surv[:, gamma:]], 1)   # P(K = k), k = 0..gamma
+    mass = torch.zeros((B, gamma + 1), dtype=torch.float64, device=d.device)
+    c = cand.long().clamp(min=0)
+    for k in range(gamma + 1):
+        q = torch.softmax(t[:, k].double() / T, -1)
+        if k < gamma:
+            p = torch.softmax(d[:, k].double() / T, -1)
+            w = (q - p).clamp(min=0) / (1 - alpha[:, k:k + 1])
+        else:
+            w = q
+        mass[:, k] = (w.gather(1, c[:, k]) * (cand[:, k] >= 0)).sum(1)
+    ph = (pk * mass).sum(1)
+    obs = hit.double().mean().item()
+    exp = ph.mean().item()
+    se = ((ph * (1 - ph)).sum().sqrt() / B).item()
+    return {"observed": obs, "expected": exp, "se": se, "z": (obs - exp) / se if se > 0 else None}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -175,20 +308,9 @@ def main():
         return ssd_main(args)
 
     import numpy as np
-    import torch
 
     import rejection_sampling_verify_12_amd as R
     import workloads as W
-
-    dev = torch.device("cuda:0")
-    if args.copy_bytes:
-        src = torch.empty(args.copy_bytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
-        dst = torch.empty_like(src)
-        for _ in range(args.steps):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes": args.copy_bytes, "launches": args.steps}))
-        return
 
     t0 = time.perf_counter()
     batch = W.make_workload(args.workload, workers=min(16, os.cpu_count() or 1))
@@ -203,6 +325,30 @@ def main():
     if args.predict and args.early:
         sys.exit("--predict and --early do not combine")
     greedy = args.mode == "greedy"
+    gtok = None
+    if greedy:   # the draft's greedy tokens
+        gtok = np.argmax(W.decode_f64(batch.draft[:, :g], batch.dtype), axis=-1).astype(np.int32)
+
+    # The CPU oracle legs run first: the pool forks, which must happen before
+    # anything touches the GPU.
+    cpu = None
+    if not args.no_cpu:
+        workers = args.cpu_workers or min(16, os.cpu_count() or 1)
+        cpu = cpu_baseline(batch, args.mode, args.eps, args.cpu_seconds, gtok, workers)
+        print(f"[bench] cpu baseline {cpu['value']:.0f} positions/s over {workers} processes", file=sys.stderr,
+              flush=True)
+
+    import torch
+    dev = torch.device("cuda:0")
+    if args.copy_bytes:
+        src = torch.empty(args.copy_bytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": args.copy_bytes, "launches": args.steps}))
+        return
+
     es = 2 if batch.dtype == "bf16" else 4
     if greedy:   # target rows, draft tokens, lengths and the outputs
         bytes_alg = (B * (g + 1) * V * es + B * g * 4 + B * 4 + B * (g + 1) * 4
@@ -210,7 +356,7 @@ def main():
     else:
         bytes_alg = R.bytes_algorithmic(B, g, V, dt_code)
     if args.predict:   # draft row gamma, which only the prediction reads
-        bytes_alg += B * V * (2 if batch.dtype == "bf16" else 4)
+        bytes_alg += B * V * es
     nsets = args.sets or max(1, -(-(1 << 30) // max(bytes_alg, 1)) + (1 if bytes_alg < (1 << 30) else 0))
 
     def dev_logits(a):
@@ -222,9 +368,6 @@ def main():
     sets = [(base_d, base_t)]
     for s in range(1, nsets):   # extra copies so that successive calls miss the 256 MB cache
         sets.append((base_d.clone(), base_t.clone()))
-    gtok = None
-    if greedy:   # the draft's greedy tokens
-        gtok = np.argmax(W.decode_f64(batch.draft[:, :g], batch.dtype), axis=-1).astype(np.int32)
     tok = torch.from_numpy(gtok if greedy else batch.draft_tokens).to(dev)
     ua = torch.from_numpy(batch.u_accept).to(dev)
     us = torch.from_numpy(batch.u_sample).to(dev)
@@ -260,29 +403,74 @@ def main():
             pout = R.spec_predict_outcomes(d, out.accepted, out.tokens, out=pout, workspace=pws,
                                            stream=stream)
 
-    for i in range(args.warmup):
-        call(i)
+    # Untimed warm-up: W calls, then more until warmup_ms of wall time of
+    # sustained work have passed (synchronising every 16 calls, so the host
+    # does not queue far ahead of the GPU).
+    w0 = time.perf_counter()
+    nw = 0
+    while nw < args.warmup or (time.perf_counter() - w0) * 1e3 < args.warmup_ms:
+        call(nw)
+        nw += 1
+        if nw % 16 == 0:
+            torch.cuda.synchronize()
+    clk0 = gpu_clocks()   # read while the last warm-up calls still run
     torch.cuda.synchronize()
+    warm_ms = (time.perf_counter() - w0) * 1e3
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
     torch.cuda.synchronize()
-    w0 = time.perf_counter()
+    t_start = time.perf_counter()
     for i in range(args.steps):
         ev[i][0].record(stream)
-        call(args.warmup + i)
+        call(nw + i)
         ev[i][1].record(stream)
+    t_enq = time.perf_counter()
+    clk1 = gpu_clocks()   # read while the timed calls still run (they are queued)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
+    wall = time.perf_counter() - t_start
+    busy_at_clk1 = (t_enq - t_start) < wall
     per_call_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    region_ms = ev[0][0].elapsed_time(ev[-1][1])
     ms_step = wall * 1e3 / args.steps
     ev_ms = float(per_call_ms.mean())
     acc = out.accepted.cpu().numpy()
+    err_word = int(ws[:4].view(torch.int32).item())
     if args.early:   # the rows the loop reads: 2(k+1) rows before a rejection, 2 gamma + 1 after none
         rows = np.where(acc < g, 2 * (acc + 1), 2 * g + 1)
         small = R.bytes_algorithmic(B, g, V, dt_code) - (2 * g + 1) * B * V * es   # tokens, uniforms, outputs
         bytes_alg = int(rows.sum()) * V * es + small
 
+    # Attainable read bandwidth: the same loads over the logits (both tensors).
+    sink = torch.zeros(1, dtype=torch.int64, device=dev)
+    read_bytes = (base_d.numel() + base_t.numel()) * es
+    for _ in range(10):
+        R.spec_read_bandwidth(base_d, sink, stream=stream)
+        R.spec_read_bandwidth(base_t, sink, stream=stream)
+    torch.cuda.synchronize()
+    r0, r1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    nread = 20
+    r0.record(stream)
+    for _ in range(nread):
+        R.spec_read_bandwidth(base_d, sink, stream=stream)
+        R.spec_read_bandwidth(base_t, sink, stream=stream)
+    r1.record(stream)
+    torch.cuda.synchronize()
+    read_gbps = read_bytes * nread / (r0.elapsed_time(r1) * 1e-3) / 1e9
+
+    stats = {}
+    if not greedy and not args.top_p:
+        alpha = acceptance_statistics(base_d, base_t, batch.T, g)
+        stats["tokens_per_round"] = tokens_per_round(alpha, acc)
+        if args.predict and args.mode == "residual":
+            stats["hit_rate"] = hit_rate_statistics(base_d, base_t, batch.T, g, alpha, pout.cand, pout.hit)
+        del alpha
+        torch.cuda.empty_cache()
+
     achieved = bytes_alg / (ev_ms * 1e-3) / 1e9
+    achieved_step = bytes_alg / (ms_step * 1e-3) / 1e9
+    name = ("spec_verify_greedy" if greedy else "spec_verify_early" if args.early
+            else "spec_verify_ex" if args.top_p else "spec_verify_predict" if (args.predict and not sep)
+            else "spec_verify_saguaro" if args.mode == "saguaro" else "spec_verify")
     result = {
         "metric": METRIC,
         "value": B * g / (ms_step * 1e-3),
@@ -300,24 +488,33 @@ def main():
                    "logits": batch.dtype, "mode": args.mode, "eps": args.eps,
                    "input_sets": nsets, "alpha_target": [float(batch.alpha_target.min()),
                                                          float(batch.alpha_target.max())],
-                   "mean_accepted": float(acc.mean()),
+                   "mean_accepted": float(acc[acc >= 0].mean()) if (acc >= 0).any() else None,
                    "predict": ("separate" if sep else "fused") if args.predict else False,
                    "early_exit": bool(args.early), "top_p": args.top_p or None,
                    **({"hit_rate": float(pout.hit.float().mean().item())} if args.predict else {})},
+        "warmup_calls": nw,
+        "warmup_ms": warm_ms,
         "event_ms": {"mean": ev_ms, "p10": float(np.percentile(per_call_ms, 10)),
                      "p50": float(np.percentile(per_call_ms, 50)),
-                     "p90": float(np.percentile(per_call_ms, 90))},
+                     "p90": float(np.percentile(per_call_ms, 90)),
+                     "region_per_step": region_ms / args.steps},
+        "clocks": {"end_of_warmup": clk0, "during_timed_calls": clk1 if busy_at_clk1 else None},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic_record(
                          args.workload, args.mode + ("_predict" if args.predict and not sep else "")
                          + ("_early" if args.early else "") + ("_topp" if args.top_p else "")),
-                     "kernel": f"one {'spec_verify_greedy' if greedy else ('spec_verify_early' if args.early else ('spec_verify_ex' if args.top_p else 'spec_verify'))} "
-                               "call (every kernel it launches), event-timed on its stream",
-                     "bytes_alg": bytes_alg},
+                     "kernel": f"one {name} call (every kernel it launches), event-timed on its stream",
+                     "bytes_alg": bytes_alg,
+                     "achieved_per_step": achieved_step, "frac_per_step": achieved_step / HBM_PEAK_GBPS,
+                     "attainable_read": {"achieved": read_gbps, "frac": read_gbps / HBM_PEAK_GBPS,
+                                         "bytes": read_bytes,
+                                         "kernel": "spec_read_bandwidth over the draft and target logits"}},
+        "statistics": stats,
+        "error_word": err_word,
         "source_digest": source_digest(),
     }
-    if not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline(batch, args.mode, args.eps, args.cpu_seconds, gtok)
+    if cpu is not None:
+        result["cpu_baseline"] = cpu
     print(json.dumps(result), flush=True)
 
 

@@ -338,6 +338,18 @@ int spec_verify_noalloc(const void* draft_logits, const void* target_logits, int
                         uint64_t* out_accept_mask, int32_t* out_len, const spec_diag* diag,
                         void* stream);
 
+/*
+ * A measurement aid, not part of the verification: reads `bytes` bytes of the
+ * device buffer `buf` with the loads the verification's stream items use
+ * (16-byte nontemporal loads, 64 KB per work-group), so that the HBM read
+ * bandwidth attainable for a pass over the same bytes can be set beside the
+ * verification's own rate.  `sink` is a device word written only if the
+ * combined data equals an impossible value (it keeps the loads).  bytes must
+ * be a positive multiple of 16 and buf 16-byte aligned, else SPEC_EINVAL.
+ * Enqueues only.
+ */
+int spec_read_bandwidth(const void* buf, size_t bytes, uint64_t* sink, void* stream);
+
 /* A static, human-readable description of a status code. */
 const char* spec_status_str(int status);
 

@@ -21,7 +21,8 @@ SPEC_F32, SPEC_BF16 = 0, 1
 EXPORTED = ("spec_workspace_bytes", "spec_verify", "spec_verify_saguaro",
             "spec_predict_workspace_bytes", "spec_predict_outcomes", "spec_verify_predict",
             "spec_greedy_workspace_bytes", "spec_verify_greedy", "spec_verify_early",
-            "spec_verify_ex", "spec_synthetic_busy", "spec_verify_noalloc", "spec_status_str")
+            "spec_verify_ex", "spec_synthetic_busy", "spec_verify_noalloc", "spec_read_bandwidth",
+            "spec_status_str")
 
 
 class SpecOptions(ctypes.Structure):
@@ -74,6 +75,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.spec_greedy_workspace_bytes.restype = sz
     lib.spec_verify_greedy.argtypes = [vp, i32, vp, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.spec_verify_greedy.restype = i32
+    lib.spec_read_bandwidth.argtypes = [vp, sz, vp, vp]
+    lib.spec_read_bandwidth.restype = i32
     lib.spec_verify_noalloc.argtypes = verify_args[:-3] + [vp]
     lib.spec_verify_noalloc.restype = i32
     lib.spec_status_str.argtypes = [i32]
@@ -311,6 +314,18 @@ def spec_synthetic_busy(ns: int, hit=None, stream=None, device=None):
     _check_dev(hit)
     st = load_library().spec_synthetic_busy(int(ns), _ptr(hit), 0 if hit is None else hit.numel(),
                                             _stream_handle(stream, dev))
+    if st != SPEC_OK:
+        raise SpecError(st)
+
+
+def spec_read_bandwidth(buf, sink, nbytes=None, stream=None):
+    """Read nbytes (default: all) of the device tensor ``buf`` with the stream
+    items' loads (a measurement aid, see spec_verify.h); ``sink`` is a device
+    int64 tensor of at least one element."""
+    _check_dev(buf, sink)
+    n = buf.numel() * buf.element_size() if nbytes is None else int(nbytes)
+    st = load_library().spec_read_bandwidth(buf.data_ptr(), n, sink.data_ptr(),
+                                            _stream_handle(stream, buf.device))
     if st != SPEC_OK:
         raise SpecError(st)
 

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libspecverify.so")
-SOURCES = ["verify.hip", "predict.hip", "greedy.hip", "synthetic.hip"]
+SOURCES = ["verify.hip", "predict.hip", "greedy.hip", "synthetic.hip", "readbw.hip"]
 
 
 def hipcc() -> str:
