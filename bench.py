@@ -66,9 +66,10 @@ def parse():
     ap.add_argument("--top-p", type=float, default=0.0,
                     help="cut every row to its top-p nucleus (spec_verify_ex); 0 = no cut")
     ap.add_argument("--ssd", action="store_true",
-                    help="speculative speculative decoding pipeline with synthetic timed models: "
-                         "standard SD (one stream) against SSD (two streams), one sequence per round")
+                    help="speculative speculative decoding pipeline with synthetic bigram models and "
+                         "timed model passes: standard SD (one stream) against SSD (two streams)")
     ap.add_argument("--ssd-rounds", type=int, default=64)
+    ap.add_argument("--ssd-batch", type=int, default=1, help="sequences per SSD round")
     ap.add_argument("--ssd-t", type=float, default=0.5, help="temperature of the SSD rounds")
     ap.add_argument("--ssd-draft-us", type=float, default=220.0,
                     help="draft model time per round (gamma draft steps)")
@@ -170,52 +171,53 @@ def cpu_baseline(batch, mode: str, eps: float, budget_s: float, tokens, workers:
 
 
 def ssd_main(args):
-    """SD vs SSD rounds on one sequence at a time (the B=128 workload's
-    sequences in turn, draft tokens drawn at --ssd-t)."""
+    """SD against SSD rounds with synthetic bigram models: the workload's gamma
+    and V, 64 table rows, --ssd-batch sequences per round, drafts drawn at
+    --ssd-t, model times --ssd-draft-us and --ssd-target-us."""
     import numpy as np
     import torch
 
-    import rejection_sampling_verify_12_amd as R
     import workloads as W
     from rejection_sampling_verify_12_amd import ssd
 
     name = args.workload if args.workload != DEFAULT_WORKLOAD else "B128_g4_V128256_bf16"
-    batch = W.make_workload(name, seqs=np.arange(min(32, W.WORKLOADS[name][0])),
-                            workers=min(16, os.cpu_count() or 1))
-    T = args.ssd_t
-    tok = W.gumbel_argmax(batch.draft64()[:, :batch.gamma], T, W.philox(batch.seed, 91))
+    _, gamma, V, _, dtype, _, seed = W.WORKLOADS[name]
+    T, n, B = args.ssd_t, args.ssd_rounds, args.ssd_batch
+    s = W.bigram_setup(B, gamma, V, T, n, seed, dtype=dtype, H=64)
     dev = torch.device("cuda:0")
 
-    def logits(a):
-        if batch.dtype == "bf16":
+    def tab(a):
+        if dtype == "bf16":
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
-    rounds = [(logits(batch.draft[i:i + 1]), logits(batch.target[i:i + 1]),
-               torch.from_numpy(tok[i:i + 1].astype(np.int32)).to(dev),
-               torch.from_numpy(batch.u_accept[i:i + 1]).to(dev),
-               torch.from_numpy(batch.u_sample[i:i + 1]).to(dev)) for i in range(batch.B)]
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+    m = ssd.Models(tab(s.draft_table), tab(s.target_table), f32(s.noise), i32(s.last0),
+                   i32(s.len0), f32(s.u_accept), f32(s.u_sample), T)
     td, tt = int(args.ssd_draft_us * 1e3), int(args.ssd_target_us * 1e3)
-    ssd.run_sd(rounds, T, td, tt, 4)       # warm-up
-    ssd.run_ssd(rounds, T, td, tt, 4)
-    n = args.ssd_rounds
-    t_sd, o_sd = ssd.run_sd(rounds, T, td, tt, n)
-    t_ssd, o_ssd, p_ssd = ssd.run_ssd(rounds, T, td, tt, n)
-    tokens = ssd.emitted_tokens(o_sd)
-    assert tokens == ssd.emitted_tokens(o_ssd)
-    hit = float(np.mean([int(p.hit.item()) for p in p_ssd]))
-    # verification time alone, for the predicted round times
-    t_v = ssd.run_sd(rounds, T, 0, 0, n)[0] / n
+    ssd.run_sd(m, 4, td, tt)       # warm-up
+    ssd.run_ssd(m, 4, td, tt)
+    t_sd, sd = ssd.run_sd(m, n, td, tt)
+    t_ssd, sp = ssd.run_ssd(m, n, td, tt)
+    tokens = ssd.emitted_tokens(sd)
+    same = all(torch.equal(a.out.tokens, b.out.tokens) for a, b in zip(sd, sp))
+    hits = torch.stack([r.pred.hit for r in sp]).cpu().numpy()
+    round_hit = float((hits != 0).all(axis=1).mean())     # rounds that need no fallback
+    # rows, verification and commit alone, for the predicted round times
+    t_v = ssd.run_sd(m, n, 0, 0)[0] / n
     sd_round, ssd_round = t_sd / n, t_ssd / n
-    pred_ssd = max(td * 1e-9, tt * 1e-9 + t_v) + (1 - hit) * td * 1e-9
+    pred_ssd = max(td * 1e-9, tt * 1e-9 + t_v) + (1 - round_hit) * td * 1e-9
     print(json.dumps({
-        "metric": "tokens/s of a speculative-decoding loop with synthetic timed models",
+        "metric": "tokens/s of a speculative-decoding loop with synthetic bigram models and timed "
+                  "model passes",
         "sd_tokens_per_s": tokens / t_sd, "ssd_tokens_per_s": tokens / t_ssd,
-        "speedup": t_sd / t_ssd, "hit_rate": hit, "tokens": tokens, "rounds": n,
+        "speedup": t_sd / t_ssd, "same_tokens": same, "hit_rate": float((hits != 0).mean()),
+        "round_hit_rate": round_hit, "tokens": tokens, "rounds": n,
         "round_us": {"sd": sd_round * 1e6, "ssd": ssd_round * 1e6, "verify_only": t_v * 1e6,
                      "ssd_expected": pred_ssd * 1e6,
                      "sd_expected": (td + tt) * 1e-3 + t_v * 1e6},
-        "config": {"workload": name, "B_per_round": 1, "gamma": batch.gamma, "V": batch.V,
+        "config": {"workload": f"bigram models, gamma {gamma}, V {V}, 64 rows", "B_per_round": B,
                    "T": T, "draft_us": args.ssd_draft_us, "target_us": args.ssd_target_us},
         "data": "synthetic", "source_digest": source_digest()}), flush=True)
 

@@ -318,6 +318,58 @@ int spec_verify_greedy(const void* target_logits, int dtype, const int32_t* draf
 int spec_synthetic_busy(int64_t ns, const int32_t* hit, int n, void* stream);
 
 /*
+ * Synthetic bigram models for the pipeline of "Speculative Speculative
+ * Decoding (Saguaro)", sections 3.1 and 4.1 (no weights exist here).  A model
+ * is a DEVICE table [H][V] (dtype SPEC_F32 or SPEC_BF16, row-major, H >= 1;
+ * H = V gives every token its own row): after token t its logits are row
+ * t mod H.  Draft sampling is the Gumbel-max form: the token drawn at
+ * absolute position pos after token t is
+ *     argmax_j ( float(table[t mod H][j]) + noise[pos mod P][j] )
+ * with one fp32 addition per candidate and ties to the lower id; `noise` is a
+ * DEVICE float array [P][V] of T-scaled Gumbel variates (argmax_j(l_j/T + g_j)
+ * with standard Gumbel g is a draw from softmax(l/T)), P >= 1.  1 <= gamma <= 63.
+ * The caller owns every buffer; the calls enqueue on `stream` and return
+ * SPEC_EINVAL for a NULL required pointer or a size out of range, SPEC_ELAUNCH
+ * for a failed launch.  A token outside [0, V) where one is read makes the
+ * tokens drawn from it -1 and the rows that follow it NaN (so the verification
+ * marks the sequence invalid, and it stays so).
+ *
+ * spec_synth_draft: n chains of gamma draft steps; chain c starts after token
+ *   start_tok[c] at position start_pos[c] (NULL: 0) and writes out_tokens[c][i],
+ *   the token at position start_pos[c] + i.
+ * spec_synth_rows: a round's logits [B][gamma+1][V] (dtype of the table): row i
+ *   of sequence b is the table row (mod H) of the token before position i, which is
+ *   last[b] for i = 0 and tokens[b][i-1] ([B][gamma]) after.
+ * spec_ssd_prespeculate: the next round's drafts for every predicted outcome,
+ *   while the current round verifies.  cand [B][gamma+1][3] holds the draft's
+ *   top-3 at each position (spec_predict_outcomes); outcome c = 3k + rank is
+ *   "k drafts accepted, then cand[b][k][rank]", which leaves the sequence at
+ *   length len[b] + k + 1 (len [B], NULL: 0) with that token last, and
+ *   prepared[b][c][0..gamma) ([B][3(gamma+1)][gamma]) receives the drafts
+ *   that follow it.
+ * spec_ssd_advance: after a round's verification (out_tokens [B][gamma+1],
+ *   accepted [B], out_len [B], all from spec_verify*): next_last[b] = the
+ *   emitted token y (out_tokens[b][accepted[b]]), next_len[b] = out_len[b], and
+ *   next_tokens[b] ([B][gamma]) the drafts that follow y: prepared[b][cand_idx[b]]
+ *   when hit[b] != 0 (a hit of the prediction, spec_verify_predict), drawn
+ *   after the verification otherwise (hit == NULL: always).  A sequence with
+ *   accepted[b] < 0 gets next_last -1 and drafts -1.
+ */
+int spec_synth_draft(const void* table, int dtype, int V, int H, const float* noise, int P,
+                     int gamma, int n, const int32_t* start_tok, const int32_t* start_pos,
+                     int32_t* out_tokens, void* stream);
+int spec_synth_rows(const void* table, int dtype, int V, int H, int gamma, int B,
+                    const int32_t* last, const int32_t* tokens, void* out_rows, void* stream);
+int spec_ssd_prespeculate(const void* table, int dtype, int V, int H, const float* noise,
+                          int P, int gamma, int B, const int32_t* cand, const int32_t* len,
+                          int32_t* prepared, void* stream);
+int spec_ssd_advance(const void* table, int dtype, int V, int H, const float* noise, int P,
+                     int gamma, int B, const int32_t* out_tokens, const int32_t* accepted,
+                     const int32_t* out_len, const int32_t* hit, const int32_t* cand_idx,
+                     const int32_t* prepared, int32_t* next_last, int32_t* next_len,
+                     int32_t* next_tokens, void* stream);
+
+/*
  * spec_verify without a workspace argument, for callers that cannot allocate
  * device memory: code under HIP graph capture, tight serving loops, harnesses
  * that forbid hipMalloc.  It allocates nothing.  Its workspace is a static

@@ -22,6 +22,7 @@ EXPORTED = ("spec_workspace_bytes", "spec_verify", "spec_verify_saguaro",
             "spec_predict_workspace_bytes", "spec_predict_outcomes", "spec_verify_predict",
             "spec_greedy_workspace_bytes", "spec_verify_greedy", "spec_verify_early",
             "spec_verify_ex", "spec_synthetic_busy", "spec_verify_noalloc", "spec_read_bandwidth",
+            "spec_synth_draft", "spec_synth_rows", "spec_ssd_prespeculate", "spec_ssd_advance",
             "spec_status_str")
 
 
@@ -70,6 +71,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.spec_verify_ex.restype = i32
     lib.spec_synthetic_busy.argtypes = [ctypes.c_int64, vp, i32, vp]
     lib.spec_synthetic_busy.restype = i32
+    lib.spec_synth_draft.argtypes = [vp, i32, i32, i32, vp, i32, i32, i32, vp, vp, vp, vp]
+    lib.spec_synth_draft.restype = i32
+    lib.spec_synth_rows.argtypes = [vp, i32, i32, i32, i32, i32, vp, vp, vp, vp]
+    lib.spec_synth_rows.restype = i32
+    lib.spec_ssd_prespeculate.argtypes = [vp, i32, i32, i32, vp, i32, i32, i32, vp, vp, vp, vp]
+    lib.spec_ssd_prespeculate.restype = i32
+    lib.spec_ssd_advance.argtypes = [vp, i32, i32, i32, vp, i32, i32, i32] + [vp] * 10
+    lib.spec_ssd_advance.restype = i32
     lib.spec_verify_early.restype = i32
     lib.spec_greedy_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.spec_greedy_workspace_bytes.restype = sz
@@ -316,6 +325,93 @@ def spec_synthetic_busy(ns: int, hit=None, stream=None, device=None):
                                             _stream_handle(stream, dev))
     if st != SPEC_OK:
         raise SpecError(st)
+
+
+def _bigram(table, noise=None, ints=()):
+    import torch
+    for t in ints:
+        if t is not None and t.dtype != torch.int32:
+            raise TypeError(f"token, length and prediction arrays are int32, got {t.dtype}")
+    if noise is not None and noise.dtype != torch.float32:
+        raise TypeError(f"noise is float32, got {noise.dtype}")
+    if table.dim() != 2:
+        raise ValueError(f"a bigram table is [H, V], got {tuple(table.shape)}")
+    H, V = table.shape
+    if noise is not None and (noise.dim() != 2 or noise.shape[1] != V):
+        raise ValueError(f"noise is [P, V], got {tuple(noise.shape)}")
+    return _dtype_code(table), V, H, 0 if noise is None else noise.shape[0]
+
+
+def spec_synth_draft(table, noise, gamma: int, start_tok, start_pos=None, out=None, stream=None):
+    """gamma Gumbel-max draft steps of the bigram model ``table`` [H, V] after
+    each start token (see spec_verify.h); returns out [n, gamma] int32."""
+    import torch
+    _check_dev(table, noise, start_tok, start_pos, out)
+    dt, V, H, P = _bigram(table, noise, (start_tok, start_pos, out))
+    n = start_tok.numel()
+    if out is None:
+        out = torch.empty((n, gamma), dtype=torch.int32, device=table.device)
+    st = load_library().spec_synth_draft(table.data_ptr(), dt, V, H, noise.data_ptr(), P, gamma, n,
+                                         start_tok.data_ptr(), _ptr(start_pos), out.data_ptr(),
+                                         _stream_handle(stream, table.device))
+    if st != SPEC_OK:
+        raise SpecError(st)
+    return out
+
+
+def spec_synth_rows(table, last, tokens, out=None, stream=None):
+    """A round's logits [B, gamma+1, V] from the bigram ``table`` [H, V] (see spec_verify.h)."""
+    import torch
+    _check_dev(table, last, tokens, out)
+    dt, V, H, _ = _bigram(table, None, (last, tokens))
+    B, gamma = tokens.shape
+    if out is None:
+        out = torch.empty((B, gamma + 1, V), dtype=table.dtype, device=table.device)
+    st = load_library().spec_synth_rows(table.data_ptr(), dt, V, H, gamma, B, last.data_ptr(),
+                                        tokens.data_ptr(), out.data_ptr(),
+                                        _stream_handle(stream, table.device))
+    if st != SPEC_OK:
+        raise SpecError(st)
+    return out
+
+
+def spec_ssd_prespeculate(table, noise, cand, length=None, out=None, stream=None):
+    """Drafts [B, 3(gamma+1), gamma] for every predicted outcome of a round
+    (cand [B, gamma+1, 3] from spec_predict_outcomes; see spec_verify.h)."""
+    import torch
+    _check_dev(table, noise, cand, length, out)
+    dt, V, H, P = _bigram(table, noise, (cand, length, out))
+    B, G1, _ = cand.shape
+    if out is None:
+        out = torch.empty((B, 3 * G1, G1 - 1), dtype=torch.int32, device=table.device)
+    st = load_library().spec_ssd_prespeculate(table.data_ptr(), dt, V, H, noise.data_ptr(), P, G1 - 1,
+                                              B, cand.data_ptr(), _ptr(length), out.data_ptr(),
+                                              _stream_handle(stream, table.device))
+    if st != SPEC_OK:
+        raise SpecError(st)
+    return out
+
+
+def spec_ssd_advance(table, noise, vout, pred=None, prepared=None, out=None, stream=None):
+    """The committed state and next drafts after a round (see spec_verify.h):
+    returns (next_last [B], next_len [B], next_tokens [B, gamma])."""
+    import torch
+    _check_dev(table, noise, vout.tokens, prepared)
+    dt, V, H, P = _bigram(table, noise, (vout.tokens, vout.accepted, vout.out_len, prepared))
+    B, G1 = vout.tokens.shape
+    if out is None:
+        i32 = dict(dtype=torch.int32, device=table.device)
+        out = (torch.empty((B,), **i32), torch.empty((B,), **i32), torch.empty((B, G1 - 1), **i32))
+    hit = idx = None
+    if pred is not None:
+        hit, idx = pred.hit, pred.cand_idx
+    st = load_library().spec_ssd_advance(
+        table.data_ptr(), dt, V, H, noise.data_ptr(), P, G1 - 1, B, vout.tokens.data_ptr(),
+        vout.accepted.data_ptr(), vout.out_len.data_ptr(), _ptr(hit), _ptr(idx), _ptr(prepared),
+        out[0].data_ptr(), out[1].data_ptr(), out[2].data_ptr(), _stream_handle(stream, table.device))
+    if st != SPEC_OK:
+        raise SpecError(st)
+    return out
 
 
 def spec_read_bandwidth(buf, sink, nbytes=None, stream=None):

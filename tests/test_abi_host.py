@@ -245,3 +245,41 @@ def test_noalloc_rejects_sizes_beyond_its_scratch():
     assert call(4, 64, 1000) == R.SPEC_EINVAL
     assert call(0, 3, 1000) == R.SPEC_OK
     assert "16 MiB" in R.spec_status_str(R.SPEC_ESCRATCH)
+
+
+def test_bigram_and_pipeline_calls_reject_bad_arguments():
+    """The synthetic-model and pre-speculation calls check their arguments
+    before anything is enqueued; empty batches are no-ops."""
+    lib = R.load_library()
+    bf = R.SPEC_BF16
+    # spec_synth_draft(table, dtype, V, H, noise, P, gamma, n, start_tok, start_pos, out, stream)
+    for kw in (dict(V=0), dict(H=0), dict(P=0), dict(gamma=0), dict(gamma=64), dict(n=-1),
+               dict(dtype=7), dict(table=None), dict(noise=None), dict(tok=None), dict(out=None)):
+        a = dict(table=FAKE, dtype=bf, V=100, H=10, noise=FAKE, P=8, gamma=4, n=3, tok=FAKE,
+                 pos=None, out=FAKE, stream=None)
+        a.update(kw)
+        assert lib.spec_synth_draft(*a.values()) == R.SPEC_EINVAL, kw
+    assert lib.spec_synth_draft(FAKE, bf, 100, 10, FAKE, 8, 4, 0, None, None, None, None) == R.SPEC_OK
+    # spec_synth_rows(table, dtype, V, H, gamma, B, last, tokens, out, stream)
+    for kw in (dict(V=0), dict(H=0), dict(gamma=64), dict(B=-1), dict(dtype=7), dict(last=None),
+               dict(out=None)):
+        a = dict(table=FAKE, dtype=bf, V=100, H=10, gamma=4, B=2, last=FAKE, tok=FAKE, out=FAKE,
+                 stream=None)
+        a.update(kw)
+        assert lib.spec_synth_rows(*a.values()) == R.SPEC_EINVAL, kw
+    assert lib.spec_synth_rows(FAKE, bf, 100, 10, 4, 0, None, None, None, None) == R.SPEC_OK
+    # spec_ssd_prespeculate(table, dtype, V, H, noise, P, gamma, B, cand, len, prepared, stream)
+    for kw in (dict(gamma=64), dict(B=-1), dict(cand=None), dict(prep=None), dict(noise=None)):
+        a = dict(table=FAKE, dtype=bf, V=100, H=10, noise=FAKE, P=8, gamma=4, B=2, cand=FAKE,
+                 len=None, prep=FAKE, stream=None)
+        a.update(kw)
+        assert lib.spec_ssd_prespeculate(*a.values()) == R.SPEC_EINVAL, kw
+    # spec_ssd_advance(table, dtype, V, H, noise, P, gamma, B, out_tokens, accepted, out_len,
+    #                  hit, cand_idx, prepared, next_last, next_len, next_tokens, stream)
+    for kw in (dict(acc=None), dict(olen=None), dict(nl=None), dict(hit=FAKE),
+               dict(hit=FAKE, idx=FAKE), dict(B=-1), dict(P=0)):
+        a = dict(table=FAKE, dtype=bf, V=100, H=10, noise=FAKE, P=8, gamma=4, B=2, tok=FAKE,
+                 acc=FAKE, olen=FAKE, hit=None, idx=None, prep=None, nl=FAKE, nlen=FAKE, nt=FAKE,
+                 stream=None)
+        a.update(kw)
+        assert lib.spec_ssd_advance(*a.values()) == R.SPEC_EINVAL, kw

@@ -295,3 +295,91 @@ def make_workload(name: str, seqs=None, table: dict | None = None, workers: int 
                          "alpha_target")}
         return dataclasses.replace(parts[0], B=len(seqs), **cat)
     return zipf_batch(name, B, gamma, V, T, dtype, workload_alpha(name), seed, seqs=seqs, table=table)
+
+
+# ---------------------------------------------------------------------------
+# Bigram models for the speculative-speculative-decoding pipeline.
+
+@dataclasses.dataclass
+class BigramSetup:
+    """Inputs of a multi-round pipeline run with synthetic bigram models.
+
+    draft_table, target_table: [H, V] logits (float32 array or bf16 bits); row
+    t mod H holds the logits after token t.  noise: [P, V] float32 T-scaled Gumbel
+    variates, row = absolute position mod P.  last0, len0: [B] int32 start
+    state.  u_accept: [R, B, gamma], u_sample: [R, B, gamma+1] float32.
+    """
+    name: str
+    B: int
+    gamma: int
+    V: int
+    T: float
+    dtype: str
+    rounds: int
+    draft_table: np.ndarray
+    target_table: np.ndarray
+    noise: np.ndarray
+    last0: np.ndarray
+    len0: np.ndarray
+    u_accept: np.ndarray
+    u_sample: np.ndarray
+    seed: int = 0
+
+    def draft64(self) -> np.ndarray:
+        return decode_f64(self.draft_table, self.dtype)
+
+    def target64(self) -> np.ndarray:
+        return decode_f64(self.target_table, self.dtype)
+
+
+def bigram_setup(B: int, gamma: int, V: int, T: float, rounds: int, seed: int,
+                 dtype: str = "bf16", kind: str = "zipf", zipf: float = 1.5,
+                 draft_noise: float = 0.5, target_noise: float = 0.6, max_len0: int = 64,
+                 P: int | None = None, len_stride: int = 0, H: int | None = None) -> BigramSetup:
+    """Bigram tables, noise, start state and uniforms.
+
+    kind "zipf": draft rows -zipf ln(rank) over a random permutation per row
+    plus N(0, draft_noise^2); the target adds N(0, target_noise^2) to them.
+    kind "hit": peaked draft rows (the top token 25 above a -2 ln(rank) tail)
+    and the target equal to the draft: every draft is accepted and the bonus
+    is the draft's top token, so every outcome is among the predictions.
+    kind "miss": the same draft; the target raises the token the draft ranks
+    V/2 to 60, so the first draft is rejected and the residual draw is that
+    token, never among the draft's top-3.
+    len_stride > 0 gives sequence b the start length b * len_stride (no two
+    sequences share a noise row then, when P covers every position).  H rows
+    (default V): token t's logits are row t mod H.
+    """
+    H = V if H is None else H
+    rng = philox(seed, _S_LOGITS)
+    if kind == "zipf":
+        base = -zipf * np.log(np.arange(1, V + 1, dtype=np.float64))
+    else:
+        base = -2.0 * np.log(np.arange(1, V + 1, dtype=np.float64))
+        base[0] += 25.0
+    perm = rng.permuted(np.tile(np.arange(V), (H, 1)), axis=1)   # perm[row, rank] = token
+    d = np.empty((H, V), dtype=np.float64)
+    np.put_along_axis(d, perm, np.broadcast_to(base, (H, V)), axis=1)
+    if kind == "zipf":
+        d += draft_noise * rng.standard_normal((H, V))
+        t = d + target_noise * rng.standard_normal((H, V))
+    elif kind == "hit":
+        t = d.copy()
+    elif kind == "miss":
+        t = d.copy()
+        t[np.arange(H), perm[:, V // 2]] = 60.0
+    else:
+        raise ValueError(kind)
+    misc = philox(seed, _S_MISC)
+    last0 = misc.integers(0, V, size=B).astype(np.int32)
+    if len_stride > 0:
+        len0 = (np.arange(B) * len_stride).astype(np.int32)
+    else:
+        len0 = misc.integers(0, max_len0 + 1, size=B).astype(np.int32)
+    if P is None:
+        P = int(len0.max()) + rounds * (gamma + 1) + 2 * gamma + 2
+    noise = (T * philox(seed, _S_TOKENS).gumbel(size=(P, V))).astype(np.float32)
+    ua = uniforms24(philox(seed, _S_UACC), (rounds, B, gamma))
+    us = uniforms24(philox(seed, _S_USAMP), (rounds, B, gamma + 1))
+    return BigramSetup(f"bigram_{kind}_B{B}_g{gamma}_V{V}_{dtype}", B, gamma, V, T, dtype, rounds,
+                       encode(d, dtype), encode(t, dtype), noise, last0, len0, ua, us, seed)
