@@ -39,7 +39,10 @@
  *     (b*(gamma+1)+i)*V.  The verification reads draft rows 0..gamma-1 and
  *     target rows 0..gamma; draft row gamma is read only by outcome prediction.
  *   - Host-checkable errors return a negative status before anything is
- *     enqueued: B < 0, gamma outside [1, 63], V < 1, T not finite or <= 0,
+ *     enqueued: B < 0, gamma outside [1, 63], V < 1 or V > 2^30,
+ *     B * (2 gamma + 1) * ceil(V / 2048) > 2^29 (about 2^40 logits per tensor,
+ *     beyond any one GPU's memory; it keeps every count in 32 bits), T not
+ *     finite or <= 0,
  *     eps not finite or < 0, a NULL required pointer, an unknown dtype, a
  *     workspace smaller than spec_workspace_bytes().  B == 0 is a no-op.
  *   - Data errors found on the device mark only their sequence: a draft token

@@ -19,6 +19,18 @@ constexpr float kNegSentinel = -1.0e30f;    // "no finite logit seen yet"
 
 enum : int { kF32 = 0, kBF16 = 1 };
 
+// Sizes every entry point accepts: B >= 0, 1 <= gamma <= 63, 1 <= V <= 2^30,
+// and B * (2 gamma + 1) * ceil(V / 2048) <= 2^29 (about 2^40 logits per
+// tensor, terabytes beyond one GPU's memory).  Within these limits every row,
+// tile, chunk and item count of a call, and every schedule step, fits a
+// 32-bit int.
+constexpr int kMaxV = 1 << 30;
+inline bool sizes_in_range(int B, int gamma, int V) {
+  if (B < 0 || gamma < 1 || gamma > 63 || V < 1 || V > kMaxV) return false;
+  const int64_t rows = (int64_t)B * (2 * gamma + 1);
+  return rows * (((int64_t)V + kTile - 1) / kTile) <= ((int64_t)1 << 29);
+}
+
 // ---------------------------------------------------------------------------
 // Logit loads.  A row is `const void*`; element j is float32 or bfloat16.
 

@@ -309,7 +309,7 @@ extern "C" int spec_verify_greedy(const void* target_logits, int dtype, const in
                                   size_t workspace_bytes, void* stream) {
   using namespace sv;
   if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_EDTYPE;
-  if (B < 0 || gamma < 1 || gamma > 63 || V < 1) return SPEC_EINVAL;
+  if (!sizes_in_range(B, gamma, V)) return SPEC_EINVAL;
   if (B == 0) return SPEC_OK;
   if (!target_logits || !draft_tokens || !out_tokens || !out_accepted) return SPEC_EINVAL;
   const int nc = (V + kChunk - 1) / kChunk;
@@ -346,7 +346,7 @@ extern "C" int spec_verify_greedy(const void* target_logits, int dtype, const in
 }
 
 extern "C" size_t spec_greedy_workspace_bytes(int B, int gamma, int V, int dtype) {
-  if ((dtype != SPEC_F32 && dtype != SPEC_BF16) || B < 0 || gamma < 1 || gamma > 63 || V < 1)
+  if ((dtype != SPEC_F32 && dtype != SPEC_BF16) || !sv::sizes_in_range(B, gamma, V))
     return 0;
   return sv::greedy_bytes(B, gamma, V);
 }

@@ -320,7 +320,7 @@ hipError_t predict_launch_leaders(const PredictArgs& a, int dtype, hipStream_t s
 extern "C" {
 
 size_t spec_predict_workspace_bytes(int B, int gamma, int V, int dtype) {
-  if ((dtype != SPEC_F32 && dtype != SPEC_BF16) || B < 0 || gamma < 1 || gamma > 63 || V < 1)
+  if ((dtype != SPEC_F32 && dtype != SPEC_BF16) || !sv::sizes_in_range(B, gamma, V))
     return 0;
   return sv::predict_part_bytes(B, gamma, V);
 }
@@ -331,7 +331,7 @@ int spec_predict_outcomes(const void* draft_logits, int dtype, int B, int gamma,
                           size_t workspace_bytes, void* stream) {
   using namespace sv;
   if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_EDTYPE;
-  if (B < 0 || gamma < 1 || gamma > 63 || V < 1) return SPEC_EINVAL;
+  if (!sizes_in_range(B, gamma, V)) return SPEC_EINVAL;
   if (B == 0) return SPEC_OK;
   if (!draft_logits || !cand) return SPEC_EINVAL;
   if ((accepted == nullptr) != (out_tokens == nullptr)) return SPEC_EINVAL;

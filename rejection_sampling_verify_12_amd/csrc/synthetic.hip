@@ -8,6 +8,8 @@
 // uses, as a model on a separate device would.
 #include "spec_verify.h"
 
+#include "common.h"
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -253,7 +255,7 @@ __global__ __launch_bounds__(kRowThreads) void rows_kernel(
 
 bool bigram_args_ok(const void* table, int dtype, int V, int H, const float* noise, int P,
                     int gamma) {
-  return table && noise && V >= 1 && H >= 1 && P >= 1 && gamma >= 1 && gamma <= 63 &&
+  return table && noise && V >= 1 && V <= kMaxV && H >= 1 && P >= 1 && gamma >= 1 && gamma <= 63 &&
          (dtype == SPEC_F32 || dtype == SPEC_BF16);
 }
 
@@ -282,7 +284,7 @@ extern "C" int spec_synth_draft(const void* table, int dtype, int V, int H, cons
 extern "C" int spec_synth_rows(const void* table, int dtype, int V, int H, int gamma, int B,
                                const int32_t* last, const int32_t* tokens, void* out_rows,
                                void* stream) {
-  if (!table || V < 1 || H < 1 || gamma < 1 || gamma > 63 || B < 0 ||
+  if (!table || H < 1 || !sv::sizes_in_range(B, gamma, V) ||
       (dtype != SPEC_F32 && dtype != SPEC_BF16))
     return SPEC_EINVAL;
   if (B == 0) return SPEC_OK;
@@ -302,7 +304,8 @@ extern "C" int spec_synth_rows(const void* table, int dtype, int V, int H, int g
 extern "C" int spec_ssd_prespeculate(const void* table, int dtype, int V, int H, const float* noise,
                                      int P, int gamma, int B, const int32_t* cand,
                                      const int32_t* len, int32_t* prepared, void* stream) {
-  if (!sv::bigram_args_ok(table, dtype, V, H, noise, P, gamma) || B < 0) return SPEC_EINVAL;
+  if (!sv::bigram_args_ok(table, dtype, V, H, noise, P, gamma) || !sv::sizes_in_range(B, gamma, V))
+    return SPEC_EINVAL;
   if (B == 0) return SPEC_OK;
   if (!cand || !prepared) return SPEC_EINVAL;
   (void)hipGetLastError();
@@ -323,7 +326,8 @@ extern "C" int spec_ssd_advance(const void* table, int dtype, int V, int H, cons
                                 const int32_t* hit, const int32_t* cand_idx,
                                 const int32_t* prepared, int32_t* next_last, int32_t* next_len,
                                 int32_t* next_tokens, void* stream) {
-  if (!sv::bigram_args_ok(table, dtype, V, H, noise, P, gamma) || B < 0) return SPEC_EINVAL;
+  if (!sv::bigram_args_ok(table, dtype, V, H, noise, P, gamma) || !sv::sizes_in_range(B, gamma, V))
+    return SPEC_EINVAL;
   if (B == 0) return SPEC_OK;
   if (!out_tokens || !accepted || !out_len || !next_last || !next_len || !next_tokens ||
       (hit && (!cand_idx || !prepared)))

@@ -69,9 +69,7 @@ struct Layout {
       ref_off, topp_off, hist_off, redo_off, total;
 };
 
-static bool sizes_ok(int B, int gamma, int V) {
-  return B >= 0 && gamma >= 1 && gamma <= 63 && V >= 1;
-}
+static bool sizes_ok(int B, int gamma, int V) { return sizes_in_range(B, gamma, V); }
 
 static Layout layout(int B, int gamma, int V) {
   Layout L;

@@ -283,3 +283,33 @@ def test_bigram_and_pipeline_calls_reject_bad_arguments():
                  stream=None)
         a.update(kw)
         assert lib.spec_ssd_advance(*a.values()) == R.SPEC_EINVAL, kw
+
+
+@pytest.mark.slow
+def test_host_layer_under_address_and_undefined_behaviour_sanitizers(tmp_path):
+    """The library's sources built with ASan and UBSan on the host code
+    (device code compiled as usual, never launched) and driven through the
+    size queries at the limits of int and every entry point's rejection of bad
+    arguments (tests/host/abi_sanitize.hip).  Any sanitizer report fails."""
+    import shutil
+    import subprocess
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc not available")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    csrc = os.path.join(root, "rejection_sampling_verify_12_amd", "csrc")
+    srcs = [os.path.join(csrc, s) for s in ("verify.hip", "predict.hip", "greedy.hip",
+                                            "synthetic.hip", "readbw.hip")]
+    exe = str(tmp_path / "abi_sanitize")
+    cmd = [hipcc, "--offload-arch=gfx950", "-std=c++17", "-x", "hip", "-g", "-O1",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=all",
+           "-I", os.path.join(root, "include"), "-I", csrc, *srcs,
+           os.path.join(root, "tests", "host", "abi_sanitize.hip"), "-o", exe]
+    build = subprocess.run(cmd, capture_output=True, text=True)
+    assert build.returncode == 0, build.stderr[-3000:]
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=0",
+               UBSAN_OPTIONS="print_stacktrace=1")
+    run = subprocess.run([exe], capture_output=True, text=True, env=env)
+    assert run.returncode == 0 and "ok (0 failures)" in run.stdout, run.stdout + run.stderr[-3000:]

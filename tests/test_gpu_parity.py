@@ -186,12 +186,15 @@ def test_empty_batch_is_noop():
     assert out.tokens.shape == (0, 5)
 
 
-def test_deterministic_replay():
-    """Identical inputs give bit-identical outputs (including diagnostics)."""
-    batch = workload("B64_g5_V128256_bf16")
+@pytest.mark.parametrize("name", ["B64_g5_V128256_bf16", "B256_g8_V152064_bf16"])
+def test_deterministic_replay(name):
+    """Identical inputs give bit-identical outputs (including diagnostics) over
+    100 replays."""
+    batch = workload(name)
+    H.say(f"[replay] {name} x100")
     db = H.to_device(batch)
     first = H.run_gpu(batch, db=db)
-    for _ in range(20):
+    for _ in range(100):
         again = H.run_gpu(batch, db=db)
         for k in ("tokens", "accepted", "mask", "out_len"):
             assert np.array_equal(first[k], again[k])
