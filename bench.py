@@ -74,6 +74,9 @@ def parse():
     ap.add_argument("--ssd-draft-us", type=float, default=220.0,
                     help="draft model time per round (gamma draft steps)")
     ap.add_argument("--ssd-target-us", type=float, default=330.0, help="target model time per round")
+    ap.add_argument("--timeline", action="store_true",
+                    help="measurement build (python -m rejection_sampling_verify_12_amd.build --timeline): "
+                         "after the timed calls, one more call's per-block timeline of the single kernel")
     ap.add_argument("--sets", type=int, default=0,
                     help="input sets to rotate through (0: enough for > 1 GB)")
     ap.add_argument("--cpu-seconds", type=float, default=8.0,
@@ -222,6 +225,64 @@ def ssd_main(args):
         "data": "synthetic", "source_digest": source_digest()}), flush=True)
 
 
+KINDS = ("stream", "decide", "mass", "sample", "draw", "last", "final", "test")
+
+
+def timeline_report(args, batch, one_call, R):
+    """One more call of the single kernel in the timeline build: per item
+    kind, per XCC and for the sequence that finishes last, in microseconds
+    from the kernel's first block (s_memrealtime, 100 MHz)."""
+    import ctypes
+
+    import numpy as np
+    import torch
+    lib = R.load_library()
+    lib.spec_timeline_copy.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    lib.spec_timeline_copy.restype = ctypes.c_int
+    torch.cuda.synchronize()
+    one_call()
+    torch.cuda.synchronize()
+    raw = np.zeros((1 << 17, 2, 4), dtype=np.uint32)
+    if lib.spec_timeline_copy(raw.ctypes.data, 1 << 18) != 0:
+        sys.exit("spec_timeline_copy failed")
+    n = int((raw[:, 0, 1] != 0).sum())
+    if n == 0:
+        sys.exit("no timeline: this call does not run the single kernel")
+    rec = raw[:n, 0, :].astype(np.int64)
+    t0 = rec[:, 0].min()
+    start, end = (rec[:, 0] - t0) / 100.0, (rec[:, 1] - t0) / 100.0
+    kind, seq = rec[:, 2] & 0xFF, rec[:, 3]
+    xcc = raw[:n, 1, 1].astype(np.int64) & 0xF
+    r1 = lambda x: round(float(x), 1)
+    kinds = {}
+    for k in range(len(KINDS)):
+        m = kind == k
+        if m.any():
+            d = end[m] - start[m]
+            kinds[KINDS[k]] = {"n": int(m.sum()), "first_start": r1(start[m].min()),
+                               "last_start": r1(start[m].max()), "last_end": r1(end[m].max()),
+                               "dur_mean": r1(d.mean()), "dur_p50": r1(np.median(d)), "dur_max": r1(d.max())}
+    per_xcc = {}
+    for x in range(8):
+        m = (kind == 0) & (xcc == x)
+        if m.any():
+            per_xcc[str(x)] = {"n": int(m.sum()), "dur_mean": r1((end[m] - start[m]).mean()),
+                               "end_p50": r1(np.median(end[m])), "end_max": r1(end[m].max())}
+    fin = kind == 6
+    b_last = int(seq[fin][np.argmax(end[fin])]) if fin.any() else -1
+    chain = {}
+    for k in range(len(KINDS)):
+        m = (kind == k) & (seq == b_last)
+        if m.any():
+            chain[KINDS[k]] = [r1(start[m].min()), r1(end[m].max())]
+    edges = np.arange(0.0, end.max() + 2.0, 2.0)
+    active = [int(((start < e + 2.0) & (end > e)).sum()) for e in edges]
+    print(json.dumps({"timeline": {
+        "workload": args.workload, "span_us": r1(end.max()), "blocks": n, "kinds": kinds,
+        "stream_by_xcc": per_xcc, "last_sequence": b_last, "last_sequence_items": chain,
+        "active_blocks_per_2us": active}, "source_digest": source_digest()}), flush=True)
+
+
 def gpu_clocks() -> dict:
     """Current gfx and memory clocks (MHz) of GPU 0, if amdsmi can read them."""
     try:
@@ -313,6 +374,11 @@ def main():
 
     import rejection_sampling_verify_12_amd as R
     import workloads as W
+
+    if args.timeline:
+        from rejection_sampling_verify_12_amd import build as BLD
+        R._lib = None
+        R.load_library(BLD.TIMELINE_LIB)
 
     t0 = time.perf_counter()
     batch = W.make_workload(args.workload, workers=min(16, os.cpu_count() or 1))
@@ -431,6 +497,8 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     busy_at_clk1 = (t_enq - t_start) < wall
+    if args.timeline:
+        return timeline_report(args, batch, lambda: call(nw + args.steps), R)
     per_call_ms = np.array([a.elapsed_time(b) for a, b in ev])
     region_ms = ev[0][0].elapsed_time(ev[-1][1])
     ms_step = wall * 1e3 / args.steps

@@ -50,6 +50,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with "
                            "`python -m rejection_sampling_verify_12_amd.build` (no CPU fallback)")
+    # torch first, so that the library binds to the HIP runtime torch loads:
+    # the one that owns the device memory and streams handed to it.  Loaded
+    # the other way round, the process holds two runtimes and launches fail.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     verify_args = [vp, vp, i32, vp, vp, vp, i32, i32, i32, f32, vp, vp, vp, vp, vp, vp,

@@ -1,6 +1,7 @@
 """Build libspecverify.so (HIP, gfx950) in-tree.
 
     python -m rejection_sampling_verify_12_amd.build
+    python -m rejection_sampling_verify_12_amd.build --timeline   (the measurement build)
 
 Every HIP source is compiled with packed-FP32 instructions disabled
 (-Xclang -target-feature -Xclang -packed-fp32-ops); the host pass warns that
@@ -18,6 +19,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libspecverify.so")
+# A measurement build: the same library with SV_TIMELINE=1, whose single
+# kernel records every block's start, end, item and CU (bench.py --timeline).
+TIMELINE_LIB = os.path.join(PKG, "libspecverify_timeline.so")
 SOURCES = ["verify.hip", "predict.hip", "greedy.hip", "synthetic.hip", "readbw.hip"]
 
 
@@ -50,5 +54,13 @@ def build(verbose: bool = False, out: str = LIB, defines: dict | None = None) ->
     return out
 
 
+def build_timeline(verbose: bool = False) -> str:
+    """Compile the timeline measurement build (TIMELINE_LIB)."""
+    return build(verbose, TIMELINE_LIB, {"SV_TIMELINE": 1})
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--timeline" in sys.argv:
+        print(build_timeline(verbose="-v" in sys.argv))
+    else:
+        print(build(verbose="-v" in sys.argv))

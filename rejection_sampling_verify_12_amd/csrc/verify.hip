@@ -536,6 +536,18 @@ int spec_verify_ex(const void* draft_logits, const void* target_logits, int dtyp
                          o.temperature, top_p);
 }
 
+#if SV_TIMELINE
+// Measurement build only (not declared in spec_verify.h): copies n uint4
+// words (two per block, see g_timeline) of the last single-kernel launch to
+// host memory `dst`.  Synchronous.
+int spec_timeline_copy(void* dst, size_t n) {
+  if (!dst) return SPEC_EINVAL;
+  n = std::min<size_t>(n, 2 * (size_t)sv::kTimelineBlocks);
+  return hipMemcpyFromSymbol(dst, HIP_SYMBOL(sv::g_timeline), n * sizeof(uint4), 0,
+                             hipMemcpyDeviceToHost) == hipSuccess ? SPEC_OK : SPEC_ELAUNCH;
+}
+#endif
+
 int spec_verify_noalloc(const void* draft_logits, const void* target_logits, int dtype,
                         const int32_t* draft_tokens, const float* u_accept, const float* u_sample,
                         int B, int gamma, int V, float temperature, const int32_t* in_len,

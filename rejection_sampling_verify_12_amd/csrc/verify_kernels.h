@@ -7,6 +7,17 @@ namespace sv {
 // ---------------------------------------------------------------------------
 // Kernels.
 
+#ifndef SV_TIMELINE
+#define SV_TIMELINE 0
+#endif
+#if SV_TIMELINE
+// Measurement build only: per block of the single kernel, its start and end
+// (s_memrealtime, 100 MHz), item (kind | sub << 8), sequence, and the
+// hardware ids of the CU and XCC it ran on.  Read with spec_timeline_copy.
+constexpr unsigned kTimelineBlocks = 1u << 17;
+__device__ uint4 g_timeline[2 * kTimelineBlocks];
+#endif
+
 union ItemLds {
   StreamLds s;
   DecideLds d;
@@ -47,6 +58,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kFused
 void fused_kernel(VerifyArgs a, Sched sc) {
   __shared__ ItemLds sh;
   __shared__ int item[4];
+#if SV_TIMELINE
+  const uint64_t tl_start = __builtin_amdgcn_s_memrealtime();
+#endif
   // One wave decodes the block number (a search on the scalar unit, which
   // the CU's waves share) and hands the item to the others.
   if (threadIdx.x < 64) {
@@ -98,6 +112,17 @@ void fused_kernel(VerifyArgs a, Sched sc) {
       break;
     default: final_item<DT, !(DT == kBF16 && VEC)>(a, b, sh.f); break;
   }
+#if SV_TIMELINE
+  if (threadIdx.x == 0 && blockIdx.x < kTimelineBlocks) {
+    const uint64_t tl_end = __builtin_amdgcn_s_memrealtime();
+    unsigned hw, xcc;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(hw));
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+    g_timeline[2 * blockIdx.x] = make_uint4((unsigned)tl_start, (unsigned)tl_end,
+                                            (unsigned)kind | ((unsigned)sub << 8), (unsigned)b);
+    g_timeline[2 * blockIdx.x + 1] = make_uint4(hw, xcc, 0u, 0u);
+  }
+#endif
 }
 
 template <int DT, bool VEC, int U>
