@@ -284,16 +284,32 @@ def timeline_report(args, batch, one_call, R):
 
 
 def gpu_clocks() -> dict:
-    """Current gfx and memory clocks (MHz) of GPU 0, if amdsmi can read them."""
+    """Gfx and memory clocks (MHz) of GPU 0, if amdsmi can read them: the
+    clock-info reading, and the GPU metrics table's per-XCC current and
+    average gfx clocks (the clock-info value has read far below the clock the
+    kernels run at, so the metrics are recorded beside it)."""
+    out = {}
     try:
         import amdsmi
         amdsmi.amdsmi_init()
         h = amdsmi.amdsmi_get_processor_handles()[0]
-        g = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)
-        m = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.MEM)
-        return {"gfx_mhz": g.get("clk"), "mem_mhz": m.get("clk")}
     except Exception as e:   # a statistic, not a requirement
         return {"error": type(e).__name__}
+    try:
+        out["gfx_mhz"] = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX).get("clk")
+        out["mem_mhz"] = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.MEM).get("clk")
+    except Exception as e:
+        out["clock_info_error"] = type(e).__name__
+    try:
+        m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+        xcc = m.get("current_gfxclks")
+        if isinstance(xcc, (list, tuple)):
+            xcc = [v for v in xcc if isinstance(v, int) and 0 < v < 10000]
+        out["metrics"] = {"current_gfxclks": xcc, "average_gfxclk_frequency": m.get("average_gfxclk_frequency"),
+                          "current_uclk": m.get("current_uclk")}
+    except Exception as e:
+        out["metrics_error"] = type(e).__name__
+    return out
 
 
 def acceptance_statistics(d, t, T: float, gamma: int, chunk: int = 32):
