@@ -380,7 +380,7 @@ int spec_ssd_advance(const void* table, int dtype, int V, int H, const float* no
  * process ends), which the call clears with a kernel before it runs.  Arguments,
  * outputs and results are those of spec_verify; sizes whose workspace
  * (spec_workspace_bytes) exceeds 16 MiB - at gamma = 8, V = 152064 in bf16,
- * B above 384 - return SPEC_ESCRATCH before anything is enqueued.  Every call
+ * B above 400 - return SPEC_ESCRATCH before anything is enqueued.  Every call
  * on one GPU shares that array: calls that overlap on one GPU (different
  * streams, or host threads) race and give undefined results; serialise them.
  * The array keeps the last call's contents, including a set error word (see

@@ -55,6 +55,7 @@ enum : int { kModeTarget = 0, kModeResidual = 1, kModeSaguaro = 2, kModeSaguaroE
 #define SV_SAMPLE_NT 0
 #endif
 constexpr int kTilesPerItem = SV_TILES_PER_ITEM;
+constexpr int kShortTiles = kTilesPerItem >= 2 ? kTilesPerItem / 2 : 1;   // short calls' sampling items
 constexpr bool kSampleNT = SV_SAMPLE_NT != 0;   // nontemporal loads in the sampling items
 // The shortest chunk (one batch stride), and the stream items below which a
 // call shortens its chunks towards it.

@@ -53,7 +53,8 @@ constexpr int kFusedWaves = DT == kBF16 && VEC ? 8 : 4;
 // PRED: outcome prediction too (draft-row items record lane leaders; the
 // items of target row gamma are followed by leader items of draft row gamma).
 // EARLY: the early-exit order (position-major stream items, position tests).
-template <int DT, bool VEC, int U, bool PRED, bool EARLY>
+// N: tiles per sampling item.
+template <int DT, bool VEC, int U, bool PRED, bool EARLY, int N = kTilesPerItem>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kFusedWaves<DT, VEC>, 8)))
 void fused_kernel(VerifyArgs a, Sched sc) {
   __shared__ ItemLds sh;
@@ -100,7 +101,7 @@ void fused_kernel(VerifyArgs a, Sched sc) {
       break;
     case kItemDecide: decide_item<DT>(a, b, sh.d); break;
     case kItemMass: break;   // Saguaro with eps > 0 runs as separate kernels
-    case kItemSample: sample_item<DT, VEC, false, false>(a, b, sub, sh.r.lds_d); break;
+    case kItemSample: sample_item<DT, VEC, false, false, N>(a, b, sub, sh.r.lds_d); break;
     case kItemDraw: draw_item<DT, VEC, false, false>(a, b, sh.r); break;
     case kItemLast:
       if (EARLY && skip) {

@@ -259,24 +259,27 @@ __device__ __forceinline__ void mass_item(const VerifyArgs& a, int b, int s, dou
   if (threadIdx.x == 0) slot_put(a.mass + (int64_t)b * a.nt + s, tw[kTilesPerItem]);
 }
 
-template <int DT, bool VEC, bool CUT = false, bool EPS = true>
+// N tiles per item (kTilesPerItem, or fewer for short calls: see
+// sample_tiles); a.nt items per sequence.
+template <int DT, bool VEC, bool CUT = false, bool EPS = true, int N = kTilesPerItem>
 __device__ __forceinline__ void sample_item(const VerifyArgs& a, int b, int s, double* lds_d) {
+  static_assert(N >= 1 && N <= kTilesPerItem, "the LDS of a sampling item holds kTilesPerItem tiles");
   const SeqRec rec = wait_rec<true>(a, b);
   if (!rec.valid) return;
-  const int t0 = s * kTilesPerItem;
+  const int t0 = s * N;
   const float epsS = rec.mode == kModeSaguaroEps ? eps_clamp(a, b, lds_d) : 0.f;
   const SampleCoef cf = coef_of<CUT>(a, b, rec, epsS);
   with_mode<EPS>(rec.mode, [&](auto m) {
     constexpr int MODE = decltype(m)::value;
-    double tw[kTilesPerItem + 1];
-    float mt[kTilesPerItem];
-    tile_sums<DT, VEC, MODE, CUT>(a, b, cf, rec.k, t0, tw, mt, lds_d);
+    double tw[N + 1];
+    float mt[N];
+    tile_sums<DT, VEC, MODE, CUT, N>(a, b, cf, rec.k, t0, tw, mt, lds_d);
     if (threadIdx.x == 0) {
 #pragma unroll
-      for (int i = 0; i < kTilesPerItem; ++i)
+      for (int i = 0; i < N; ++i)
         if (t0 + i < a.ntile)
           slot_put(a.tiles + (int64_t)b * a.ntile + t0 + i, tile_slot_value(MODE, tw[i], mt[i]));
-      if (MODE == kModeSaguaro) slot_put(a.rsum + (int64_t)b * a.nt + s, tw[kTilesPerItem]);
+      if (MODE == kModeSaguaro) slot_put(a.rsum + (int64_t)b * a.nt + s, tw[N]);
     }
   });
 }

@@ -241,6 +241,10 @@ def test_noalloc_rejects_sizes_beyond_its_scratch():
                                        FAKE, None, None, None, None, None)
     assert R.spec_workspace_bytes(512, 8, 152064, R.SPEC_BF16) > 16 << 20
     assert call(512, 8, 152064) == R.SPEC_ESCRATCH
+    # the boundary the header states for gamma = 8, V = 152064, bf16: B above 400
+    assert R.spec_workspace_bytes(400, 8, 152064, R.SPEC_BF16) <= 16 << 20
+    assert R.spec_workspace_bytes(401, 8, 152064, R.SPEC_BF16) > 16 << 20
+    assert call(401, 8, 152064) == R.SPEC_ESCRATCH
     assert call(4, 3, 1000, dtype=9) == R.SPEC_EDTYPE
     assert call(4, 64, 1000) == R.SPEC_EINVAL
     assert call(0, 3, 1000) == R.SPEC_OK
