@@ -377,6 +377,33 @@ __device__ double locate_tile(const uint64_t* tiles, int ntile, double u, DrawLd
   return S;
 }
 
+// locate_tile for at most kThreads tiles whose values the threads already
+// hold: thread t passes tile t's value v (0 past ntile).  The same scan, and
+// the same tile and offset, without reading the slots again.
+__device__ double locate_tile_held(double v, int ntile, double u, DrawLds& sh, double& target) {
+  const int tid = threadIdx.x;
+  double tot;
+  const double off = block_exclusive_scan(v, sh.lds_d, tot);
+  const double S = tot;
+  target = u * S;
+  const int hit = (tid < ntile && off <= target && target < off + v) ? tid : INT_MAX;
+  const int first = block_min_int(hit, sh.lds_i);
+  if (first != INT_MAX) {
+    if (tid == first) {
+      sh.tile = tid;
+      sh.off = off;
+    }
+  } else {   // u * S at or past the last running sum (rounding): the last tile with mass
+    const int last = -block_min_int((tid < ntile && v > 0.0) ? -tid : 1, sh.lds_i);
+    if (tid == max(last, 0)) {
+      sh.tile = max(last, 0);
+      sh.off = last > 0 ? off : 0.0;
+    }
+  }
+  __syncthreads();
+  return S;
+}
+
 // Rescan the chosen tile: the same weights and per-lane fp32 sums as its tile
 // sum, fp64 prefix over the lanes, in tile units (one tile unit is 2^e draw
 // units; e = 0 but for the bonus draw, where it is the tile's offset minus Mp).
@@ -805,8 +832,14 @@ __device__ __forceinline__ void draw_item(const VerifyArgs& a, int b, DrawLds& s
   const float epsS = rec.mode == kModeSaguaroEps ? eps_clamp(a, b, sh.lds_d) : 0.f;
   const SampleCoef cf = coef_of<CUT>(a, b, rec, epsS);
   int mode = rec.mode;
+  const double u = (double)a.u_smp[(int64_t)b * (g + 1) + k];   // in flight while the tiles arrive
   int lost = 0;   // a wait gave up: no token is drawn from what arrived
-  for (int t = tid; t < a.ntile; t += kThreads) lost |= poll(a, tiles + t) == 0ull;
+  uint64_t own = 0;   // tile tid's slot word as polled
+  for (int t = tid; t < a.ntile; t += kThreads) {
+    const uint64_t w = poll(a, tiles + t);
+    if (t == tid) own = w;
+    lost |= w == 0ull;
+  }
   double rtot = 0.0;   // residual mass (relative to Mt) when it differs from the tile total
   if (mode == kModeSaguaro || mode == kModeSaguaroEps) {
     uint64_t* rs = (mode == kModeSaguaro ? a.rsum : a.mass) + (int64_t)b * a.nt;
@@ -828,7 +861,6 @@ __device__ __forceinline__ void draw_item(const VerifyArgs& a, int b, DrawLds& s
     return;
   }
 
-  const double u = (double)a.u_smp[(int64_t)b * (g + 1) + k];
   double target = 0.0, S = 0.0;
   if (tid == 0) sh.Mp = 0.0;
   // A zero Saguaro normaliser falls back to the residual; one pass per mode.
@@ -841,13 +873,29 @@ __device__ __forceinline__ void draw_item(const VerifyArgs& a, int b, DrawLds& s
   const double zero_res = 0x1p-21 * rec.Zt;
   const bool diag_req = a.diag.resid_mass || a.diag.token_prob || a.diag.cdf_lo || a.diag.cdf_hi;
   bool refine = false;
+  // held: every tile value is in a register of its thread (at most kThreads
+  // tiles, slots as polled), so the first scan reads no slot again.
+  bool held = a.ntile <= kThreads;
+  double hv = (held && tid < a.ntile) ? slot_value(own) : 0.0;
   if ((mode == kModeSaguaro || mode == kModeSaguaroEps) && rtot <= zero_res) {
     mode = kModeTarget;
     recompute_tiles<DT, CUT>(a, b, k, mode, cf, sh);
+    held = false;   // the slots were rewritten
   }
-  if (mode == kModeTarget && k == g) tiles_to_linear(tiles, a.ntile, sh);   // the bonus draw
+  if (mode == kModeTarget && k == g) {   // the bonus draw: log2 tile values made linear
+    if (held) {   // in registers, as tiles_to_linear does in the slots
+      float m = tid < a.ntile ? (float)hv : -INFINITY;
+      m = block_max(m, reinterpret_cast<float*>(sh.lds_d));
+      const double Mp = isfinite(m) ? ceil((double)m) + 1.0 : 0.0;
+      hv = (tid < a.ntile && hv > -INFINITY) ? exp2(hv - Mp) : 0.0;
+      if (tid == 0) sh.Mp = Mp;
+    } else {
+      tiles_to_linear(tiles, a.ntile, sh);
+    }
+  }
   for (;;) {
-    S = uni(locate_tile(tiles, a.ntile, u, sh, target));
+    S = uni(held ? locate_tile_held(hv, a.ntile, u, sh, target) : locate_tile(tiles, a.ntile, u, sh, target));
+    held = false;   // a second pass follows a rewrite of the slots
     target = uni(target);
     if (mode == kModeResidual) {
       rtot = S;
