@@ -283,16 +283,22 @@ def timeline_report(args, batch, one_call, R):
         "active_blocks_per_2us": active}, "source_digest": source_digest()}), flush=True)
 
 
+_SMI = None
+
+
 def gpu_clocks() -> dict:
     """Gfx and memory clocks (MHz) of GPU 0, if amdsmi can read them: the
     clock-info reading, and the GPU metrics table's per-XCC current and
     average gfx clocks (the clock-info value has read far below the clock the
     kernels run at, so the metrics are recorded beside it)."""
+    global _SMI
     out = {}
     try:
         import amdsmi
-        amdsmi.amdsmi_init()
-        h = amdsmi.amdsmi_get_processor_handles()[0]
+        if _SMI is None:   # once: a later read then returns while the queued calls still run
+            amdsmi.amdsmi_init()
+            _SMI = amdsmi.amdsmi_get_processor_handles()[0]
+        h = _SMI
     except Exception as e:   # a statistic, not a requirement
         return {"error": type(e).__name__}
     try:
@@ -487,6 +493,7 @@ def main():
             pout = R.spec_predict_outcomes(d, out.accepted, out.tokens, out=pout, workspace=pws,
                                            stream=stream)
 
+    gpu_clocks()   # opens the SMI handle before anything is timed
     # Untimed warm-up: W calls, then more until warmup_ms of wall time of
     # sustained work have passed (synchronising every 16 calls, so the host
     # does not queue far ahead of the GPU).
