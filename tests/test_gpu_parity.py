@@ -230,6 +230,65 @@ def test_concurrent_calls_on_two_streams():
             np.testing.assert_array_equal(o.out_len.cpu().numpy(), alone[i]["out_len"])
 
 
+def test_calls_from_four_host_threads():
+    """Four host threads, each with its own stream and workspace, call the
+    library at once (ctypes releases the interpreter lock during a call):
+    the plain rule in bf16 and float32, Saguaro with eps, and early exit.
+    Every call's outputs equal the same call made alone."""
+    import threading
+
+    import rejection_sampling_verify_12_amd as R
+    cases = [("residual", workload("B64_g5_V128256_bf16")),
+             ("residual", random_batch(9, 4, 30001, "f32", 0.9, seed=4341)),
+             ("saguaro", random_batch(12, 3, 20000, "bf16", 1.0, seed=4343)),
+             ("early", random_batch(16, 5, 40000, "bf16", 0.8, seed=4347))]
+    H.say("[threads] four host threads, eight calls each")
+    dbs = [H.to_device(b) for _, b in cases]
+    alone = [H.run_gpu(b, mode="saguaro" if m == "saguaro" else "residual", eps=1e-8 if m == "saguaro" else 0.0,
+                       db=db, diag=False, early=m == "early") for (m, b), db in zip(cases, dbs)]
+    torch.cuda.synchronize()
+    results = [[] for _ in cases]
+    errors = []
+
+    def worker(i):
+        try:
+            m, b = cases[i]
+            db = dbs[i]
+            dt = R.SPEC_BF16 if b.dtype == "bf16" else R.SPEC_F32
+            st = torch.cuda.Stream()
+            ws = R.new_workspace(R.spec_workspace_bytes(b.B, b.gamma, b.V, dt), "cuda")
+            torch.cuda.synchronize()
+            with torch.cuda.stream(st):
+                for _ in range(8):
+                    args = (db.draft, db.target, db.tokens, db.u_accept, db.u_sample, b.T)
+                    if m == "saguaro":
+                        o = R.spec_verify_saguaro(*args, in_len=db.in_len, workspace=ws, stream=st, eps=1e-8)
+                    elif m == "early":
+                        o = R.spec_verify_early(*args, in_len=db.in_len, workspace=ws, stream=st)
+                    else:
+                        o = R.spec_verify(*args, in_len=db.in_len, workspace=ws, stream=st)
+                    results[i].append(o)
+            st.synchronize()
+            assert int(ws[:4].view(torch.int32).item()) == 0, "bounded wait timed out"
+        except Exception as e:   # reported by the main thread
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(len(cases))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not any(t.is_alive() for t in threads), "a calling thread did not finish"
+    assert not errors, errors
+    torch.cuda.synchronize()
+    for i in range(len(cases)):
+        assert len(results[i]) == 8
+        for o in results[i]:
+            np.testing.assert_array_equal(o.tokens.cpu().numpy(), alone[i]["tokens"])
+            np.testing.assert_array_equal(o.accepted.cpu().numpy(), alone[i]["accepted"])
+            np.testing.assert_array_equal(o.out_len.cpu().numpy(), alone[i]["out_len"])
+
+
 @pytest.mark.parametrize("early", [False, True])
 def test_graph_capture_replays(early):
     """One call captured in a graph (outputs and workspace allocated
