@@ -108,7 +108,12 @@ typedef struct spec_diag {
  * whose decision is taken with the word set, or any of whose waits gave up,
  * comes back invalid (accepted = -1, tokens -1).  The call still returns
  * SPEC_OK (nothing is synchronised); check the word after the stream, and
- * zero the whole workspace before reusing it once it is set.
+ * zero the whole workspace before reusing it once it is set.  The second
+ * 32-bit word is the check word of the library's checks build (a separate
+ * library, compiled with SV_CHECKS=1, that tests every index its kernels form
+ * against the size of its array): nonzero names the site of the first failed
+ * test, whose index was clamped into range.  The default build never writes
+ * it.  spec_verify_greedy's workspace starts the same way.
  */
 size_t spec_workspace_bytes(int B, int gamma, int V, int dtype);
 

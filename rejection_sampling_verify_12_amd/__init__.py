@@ -146,7 +146,10 @@ def _check_dev(*ts):
 
 
 def new_workspace(nbytes: int, device):
-    """A zero-filled workspace (the library leaves it zeroed after each call)."""
+    """A zero-filled workspace (each call leaves it ready for the next: all
+    zero again, but for the rows' statistics of a top-p cut and the lane
+    leaders of outcome prediction, which every such call rewrites before it
+    reads them)."""
     import torch
     return torch.zeros(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 

@@ -2,6 +2,7 @@
 
     python -m rejection_sampling_verify_12_amd.build
     python -m rejection_sampling_verify_12_amd.build --timeline   (the measurement build)
+    python -m rejection_sampling_verify_12_amd.build --checks     (the checks build)
 
 Every HIP source is compiled with packed-FP32 instructions disabled
 (-Xclang -target-feature -Xclang -packed-fp32-ops); the host pass warns that
@@ -22,6 +23,10 @@ LIB = os.path.join(PKG, "libspecverify.so")
 # A measurement build: the same library with SV_TIMELINE=1, whose single
 # kernel records every block's start, end, item and CU (bench.py --timeline).
 TIMELINE_LIB = os.path.join(PKG, "libspecverify_timeline.so")
+# The checks build: the same library with SV_CHECKS=1, whose kernels test
+# every index they form against its array's size and record a failure in the
+# workspace's second word instead of trapping (tests/test_gpu_checks.py).
+CHECKS_LIB = os.path.join(PKG, "libspecverify_checks.so")
 SOURCES = ["verify.hip", "predict.hip", "greedy.hip", "synthetic.hip", "readbw.hip"]
 
 
@@ -59,8 +64,15 @@ def build_timeline(verbose: bool = False) -> str:
     return build(verbose, TIMELINE_LIB, {"SV_TIMELINE": 1})
 
 
+def build_checks(verbose: bool = False) -> str:
+    """Compile the checks build (CHECKS_LIB)."""
+    return build(verbose, CHECKS_LIB, {"SV_CHECKS": 1})
+
+
 if __name__ == "__main__":
     if "--timeline" in sys.argv:
         print(build_timeline(verbose="-v" in sys.argv))
+    elif "--checks" in sys.argv:
+        print(build_checks(verbose="-v" in sys.argv))
     else:
         print(build(verbose="-v" in sys.argv))

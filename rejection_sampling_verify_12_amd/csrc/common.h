@@ -32,6 +32,45 @@ inline bool sizes_in_range(int B, int gamma, int V) {
 }
 
 // ---------------------------------------------------------------------------
+// Checks build (SV_CHECKS=1, a separate library).  Every index a kernel forms
+// into the workspace, an input or an output array, and every row, chunk and
+// tile an item selects, is tested against its array's size before use.  A
+// failed test never traps: it records its site (the source file's number,
+// below, times 2^16 plus the line) in the call's check word - the first
+// failure wins - and the index is clamped into the array, so the access
+// stays in bounds and the call runs to its end.  The default build compiles
+// the tests out.  Source file numbers: 1 verify_args.h, 2 verify_stream.h,
+// 3 verify_decide.h, 4 verify_sample.h, 5 verify_topp.h, 6 verify_kernels.h,
+// 7 greedy.hip.  The check word is the workspace's second 32-bit word (the
+// first is the error word of the bounded waits); like the error word it stays
+// set until the caller clears it.  The stand-alone outcome prediction has no
+// check word and no checks.
+#ifndef SV_CHECKS
+#define SV_CHECKS 0
+#endif
+#if SV_CHECKS
+__device__ __noinline__ int64_t check_failed(unsigned* chk, int64_t i, int64_t n, unsigned site) {
+  atomicCAS(chk, 0u, site);
+  return i < 0 || n <= 0 ? 0 : n - 1;
+}
+__device__ __forceinline__ int64_t check_index(unsigned* chk, int64_t i, int64_t n, unsigned site) {
+  return (i >= 0 && i < n) ? i : check_failed(chk, i, n, site);
+}
+#define SV_SITE ((unsigned)SV_FILE << 16 | (unsigned)__LINE__)
+// Index i of array n elements long (the index, clamped on failure), and
+// element i of array field f of the arguments a, whose length is a.n_f.
+#define SV_IDX(a, i, n) ::sv::check_index((a).chk, (int64_t)(i), (int64_t)(n), SV_SITE)
+#define SV_AT(a, f, i) ((a).f + SV_IDX(a, i, (a).n_##f))
+#else
+// The default build leaves every index expression as it was written: i is
+// not parenthesised, so a.f + x + y keeps its association (pass a single
+// term, a sum or a product; an index written as one unit is parenthesised at
+// its call).
+#define SV_IDX(a, i, n) (i)
+#define SV_AT(a, f, i) ((a).f + i)
+#endif
+
+// ---------------------------------------------------------------------------
 // Logit loads.  A row is `const void*`; element j is float32 or bfloat16.
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

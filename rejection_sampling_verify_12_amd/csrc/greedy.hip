@@ -29,6 +29,9 @@
 #include <algorithm>
 #include <cmath>
 
+#undef SV_FILE
+#define SV_FILE 7
+
 namespace sv {
 namespace {
 
@@ -55,6 +58,10 @@ struct GreedyArgs {
   int B, gamma, V, nc, chunk;
   int per_seq;      // stream items per sequence, (gamma+1) * nc
   int lag;          // steps between a sequence's stream items and its final item
+#if SV_CHECKS
+  unsigned* chk;    // the workspace's second word: site of the first failed check
+  int64_t n_slot, n_tokens, n_in_len, n_out_tokens, n_out_acc, n_out_fr, n_out_mask, n_out_len;
+#endif
 };
 
 // Eight logits of a lane (unit start j0): the lane's running maximum and the
@@ -85,6 +92,11 @@ struct GreedyLds {
 template <int DT, bool VEC, int U>
 __device__ void greedy_stream(const GreedyArgs& a, int b, int r, int c, GreedyLds& sh) {
   constexpr int kEs = DT == kBF16 ? 2 : 4;
+#if SV_CHECKS
+  b = (int)SV_IDX(a, b, a.B);
+  r = (int)SV_IDX(a, r, a.gamma + 1);
+  c = (int)SV_IDX(a, c, a.nc);
+#endif
   const int64_t ridx = (int64_t)b * (a.gamma + 1) + r;
   const void* row = static_cast<const char*>(a.target) + ridx * a.V * kEs;
   const int64_t begin = (int64_t)c * a.chunk;
@@ -131,7 +143,7 @@ __device__ void greedy_stream(const GreedyArgs& a, int b, int r, int c, GreedyLd
       k = sh.key[i] > k ? sh.key[i] : k;
       any |= sh.nan[i];
     }
-    st_dev_u64(a.slot + ridx * a.nc + c, ~(any ? kNanKey : k));
+    st_dev_u64(SV_AT(a, slot, ridx * a.nc + c), ~(any ? kNanKey : k));
   }
 }
 
@@ -162,7 +174,7 @@ __device__ void greedy_final(const GreedyArgs& a, int b, GreedyLds& sh) {
   for (int r = wave; r < G1; r += kWaves) {
     uint64_t best = 0;
     bool nan = false;
-    uint64_t* p = a.slot + ((int64_t)b * G1 + r) * a.nc;
+    uint64_t* p = SV_AT(a, slot, ((int64_t)b * G1 + r) * a.nc);
     for (int c = lane; c < a.nc; c += 64) {
       const uint64_t k = ~greedy_poll(a, p + c);
       st_dev_u64(p + c, 0ull);
@@ -177,7 +189,7 @@ __device__ void greedy_final(const GreedyArgs& a, int b, GreedyLds& sh) {
   if (wave != 0) return;
   // Wave 0 decides: lane i < gamma tests position i.
   const bool pos = lane < a.gamma;
-  const int x = pos ? a.tokens[(int64_t)b * a.gamma + lane] : 0;
+  const int x = pos ? *SV_AT(a, tokens, ((int64_t)b * a.gamma + lane)) : 0;
   const bool bad_x = pos && (x < 0 || x >= a.V);
   const uint64_t rk = pos ? sh.row[lane] : 0ull;
   const bool nan_i = pos && rk == kNanKey;
@@ -185,20 +197,20 @@ __device__ void greedy_final(const GreedyArgs& a, int b, GreedyLds& sh) {
   // After a bounded wait has given up anywhere in the call (the error word),
   // the sequence is reported invalid.
   bool bad = __ballot(bad_x || nan_i) != 0 || err != 0u;
-  const int k = __builtin_ctzll(~mask);   // <= gamma: bit gamma of mask is clear
+  const int k = (int)SV_IDX(a, __builtin_ctzll(~mask), G1);   // <= gamma: bit gamma of mask is clear
   const uint64_t ky = sh.row[k];
   if (k == a.gamma && ky == kNanKey) bad = true;
   const int y = key_index(ky);
   if (lane < G1) {
     const int t = bad ? -1 : (lane < k ? x : (lane == k ? y : -1));
-    a.out_tokens[(int64_t)b * G1 + lane] = t;
+    *SV_AT(a, out_tokens, ((int64_t)b * G1 + lane)) = t;
   }
   if (lane == 0) {
-    const int in = a.in_len ? a.in_len[b] : 0;
-    a.out_acc[b] = bad ? -1 : k;
-    if (a.out_fr) a.out_fr[b] = bad ? -1 : (k < a.gamma ? k : -1);
-    if (a.out_mask) a.out_mask[b] = bad ? 0ull : mask;
-    if (a.out_len) a.out_len[b] = bad ? in : in + k + 1;
+    const int in = a.in_len ? *SV_AT(a, in_len, b) : 0;
+    *SV_AT(a, out_acc, b) = bad ? -1 : k;
+    if (a.out_fr) *SV_AT(a, out_fr, b) = bad ? -1 : (k < a.gamma ? k : -1);
+    if (a.out_mask) *SV_AT(a, out_mask, b) = bad ? 0ull : mask;
+    if (a.out_len) *SV_AT(a, out_len, b) = bad ? in : in + k + 1;
   }
 }
 
@@ -248,6 +260,12 @@ __global__ __launch_bounds__(kThreads) void greedy_kernel(GreedyArgs a) {
   }
   __syncthreads();
   const int fin = uni(item[0]), b = uni(item[1]), sub = uni(item[2]);
+#if SV_CHECKS
+  if (threadIdx.x == 0) {   // the decoded item: a sequence, and a part of it
+    SV_IDX(a, b, a.B);
+    SV_IDX(a, sub, fin ? 1 : a.per_seq);
+  }
+#endif
   if (fin) {
     greedy_final(a, b, sh);
   } else {
@@ -336,6 +354,17 @@ extern "C" int spec_verify_greedy(const void* target_logits, int dtype, const in
   a.chunk = kChunk;
   a.per_seq = (int)per_seq;
   a.lag = 1;
+#if SV_CHECKS
+  a.chk = a.err + 1;
+  a.n_slot = (int64_t)B * (gamma + 1) * nc;
+  a.n_tokens = (int64_t)B * gamma;
+  a.n_in_len = in_len ? B : 0;
+  a.n_out_tokens = (int64_t)B * (gamma + 1);
+  a.n_out_acc = B;
+  a.n_out_fr = out_first_reject ? B : 0;
+  a.n_out_mask = out_accept_mask ? B : 0;
+  a.n_out_len = out_len ? B : 0;
+#endif
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   const bool vec = (V % 8 == 0) && ((uintptr_t)target_logits % 16 == 0);

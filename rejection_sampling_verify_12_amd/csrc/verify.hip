@@ -65,6 +65,7 @@ static inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
   int nc, chunk, ntile, nt, nt_max;
+  size_t nrec, nrec_d;   // per-chunk records: all rows, draft rows (lane leaders)
   size_t err_off, part_off, mraw_off, seq_off, flag_off, tiles_off, mass_off, rsum_off, cpart_off,
       ref_off, topp_off, hist_off, redo_off, total;
 };
@@ -85,6 +86,8 @@ static Layout layout(int B, int gamma, int V) {
   // so that a workspace sized for a call serves every smaller one.
   const size_t nrec = std::max<size_t>((size_t)rows * L.nc, (size_t)kSmallCallItems * (kChunk / kMinChunk));
   const size_t nrec_d = std::max<size_t>((size_t)B * (gamma + 1) * L.nc, (size_t)kSmallCallItems * (kChunk / kMinChunk));
+  L.nrec = nrec;
+  L.nrec_d = nrec_d;
   L.ntile = (V + kTile - 1) / kTile;
   L.nt = (L.ntile + kTilesPerItem - 1) / kTilesPerItem;
   L.nt_max = (L.ntile + kShortTiles - 1) / kShortTiles;   // short calls' sampling items
@@ -435,6 +438,30 @@ static int verify_impl(const void* draft, const void* target, int dtype, const i
     a.hist = reinterpret_cast<double*>(w + L.hist_off);
     a.redo = reinterpret_cast<unsigned*>(w + L.redo_off);
   }
+#if SV_CHECKS
+  {
+    const int64_t b = B, R = 2 * (int64_t)gamma + 1, cut = a.topp ? 1 : 0;
+    a.chk = a.err + 1;
+    a.n_part = a.n_mraw = (int64_t)L.nrec;
+    a.n_cpart = (int64_t)L.nrec_d;
+    a.n_seq = b;
+    a.n_flag = b * kFlagStride;
+    a.n_tiles = b * L.ntile;
+    a.n_mass = a.n_rsum = b * L.nt_max;
+    a.n_ref = b * L.ntile * 4;
+    a.n_topp = cut * b * R;
+    a.n_hist = cut * b * R * kDigits;
+    a.n_redo = cut * (b * R + 2);
+    a.n_tokens = a.n_u_acc = b * gamma;
+    a.n_u_smp = a.n_out_tokens = b * (gamma + 1);
+    a.n_in_len = in_len ? b : 0;
+    a.n_temps = temps ? b : 0;
+    a.n_out_acc = b;
+    a.n_out_first_reject = out_fr ? b : 0;
+    a.n_out_mask = out_mask ? b : 0;
+    a.n_out_len = out_len ? b : 0;
+  }
+#endif
 
   PredictArgs p;
   if (cand) {
@@ -569,6 +596,11 @@ int spec_verify_ex(const void* draft_logits, const void* target_logits, int dtyp
                          o.saguaro, o.saguaro ? o.eps : 0.f, o.cand, o.hit, o.cand_idx, o.early ? 1 : 0,
                          o.temperature, top_p);
 }
+
+#if SV_CHECKS
+// Present only in the checks build: lets a caller confirm which library it loaded.
+int spec_checks_build(void) { return 1; }
+#endif
 
 #if SV_TIMELINE
 // Measurement build only (not declared in spec_verify.h): copies n uint4

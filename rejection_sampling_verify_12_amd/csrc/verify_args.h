@@ -9,6 +9,9 @@
 #include <algorithm>
 #include <type_traits>
 
+#undef SV_FILE
+#define SV_FILE 1
+
 namespace sv {
 
 enum : int { kModeTarget = 0, kModeResidual = 1, kModeSaguaro = 2, kModeSaguaroEps = 3 };
@@ -178,6 +181,13 @@ struct VerifyArgs {
                         // finish (count, work-groups done, then row + 1 each, with a flag
                         // where the row's counters wrapped)
   float top_p;
+#if SV_CHECKS
+  unsigned* chk;        // the workspace's second word: site of the first failed check
+  // Elements of each array (diag arrays: B rows of their width).
+  int64_t n_part, n_mraw, n_seq, n_flag, n_tiles, n_mass, n_rsum, n_cpart, n_ref, n_topp, n_hist,
+      n_redo, n_tokens, n_u_acc, n_u_smp, n_in_len, n_temps, n_out_tokens, n_out_acc,
+      n_out_first_reject, n_out_mask, n_out_len;
+#endif
 };
 
 // The temperature scale of sequence b: log2(e) / T as an unevaluated float
@@ -191,7 +201,7 @@ struct TCoef {
 };
 __device__ __forceinline__ bool temp_ok(float T) { return T > 0.f && T <= 3.402823466e38f; }
 __device__ __forceinline__ float seq_temp(const VerifyArgs& a, int b) {
-  return a.temps ? uni(a.temps[b]) : 1.f;
+  return a.temps ? uni(*SV_AT(a, temps, b)) : 1.f;
 }
 __device__ __forceinline__ TCoef temp_coef(const VerifyArgs& a, int b) {
   TCoef t;
@@ -223,6 +233,10 @@ __device__ __forceinline__ const void* row_ptr(const VerifyArgs& a, int b, int r
   // can be turned into a load from a selected field address, which keeps
   // the kernel's arguments in scratch memory.
   const int64_t es = DT == kBF16 ? 2 : 4;
+#if SV_CHECKS
+  b = (int)SV_IDX(a, b, a.B);
+  r = (int)SV_IDX(a, r, 2 * a.gamma + 1);
+#endif
   const bool is_draft = r < a.gamma;
   const int64_t idx = (int64_t)b * (a.gamma + 1) + (is_draft ? r : r - a.gamma);
   const uintptr_t t = reinterpret_cast<uintptr_t>(a.target);
@@ -290,7 +304,7 @@ __device__ __forceinline__ SeqRec wait_rec(const VerifyArgs& a, int b, bool& los
   __shared__ uint64_t w[kRecWords];
   if (threadIdx.x == 0) {
     // All words are requested together, again until every one has arrived.
-    const uint64_t* p = reinterpret_cast<const uint64_t*>(a.seq + b);
+    const uint64_t* p = reinterpret_cast<const uint64_t*>(SV_AT(a, seq, b));
     uint64_t v[kRecWords];
 #pragma unroll
     for (int i = 0; i < kRecWords; ++i) v[i] = ld_dev_u64(p + i);
@@ -315,7 +329,8 @@ __device__ __forceinline__ SeqRec wait_rec(const VerifyArgs& a, int b, bool& los
   if (COUNT) {
     __syncthreads();
     if (threadIdx.x == 0)
-      __hip_atomic_fetch_add(a.flag + (int64_t)b * kFlagStride, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_add(SV_AT(a, flag, (int64_t)b * kFlagStride), 1u, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
   }
   return r;
 }

@@ -2,6 +2,9 @@
 #pragma once
 #include "verify_stream.h"
 
+#undef SV_FILE
+#define SV_FILE 3
+
 namespace sv {
 
 // ---------------------------------------------------------------------------
@@ -19,12 +22,12 @@ __device__ __forceinline__ void merge_row(const VerifyArgs& a, int b, int r, int
   mr = -INFINITY;
   double v0 = -INFINITY;   // the first piece stays in a register, later ones are read again
   for (int c = sub; c < a.nc; c += 16) {
-    uint64_t wv = ld_dev_u64(a.part + p0 + c);
-    unsigned wm = __hip_atomic_load(a.mraw + p0 + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint64_t wv = ld_dev_u64(SV_AT(a, part, p0 + c));
+    unsigned wm = __hip_atomic_load(SV_AT(a, mraw, p0 + c), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     unsigned polls = 0;
     while ((wv == 0ull || wm == 0u) && !give_up(a, polls)) {
-      if (wv == 0ull) wv = ld_dev_u64(a.part + p0 + c);
-      if (wm == 0u) wm = __hip_atomic_load(a.mraw + p0 + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (wv == 0ull) wv = ld_dev_u64(SV_AT(a, part, p0 + c));
+      if (wm == 0u) wm = __hip_atomic_load(SV_AT(a, mraw, p0 + c), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     const double v = slot_value(wv);
     mr = fmaxf(mr, __uint_as_float(~wm));
@@ -38,10 +41,10 @@ __device__ __forceinline__ void merge_row(const VerifyArgs& a, int b, int r, int
   }
   M = ceil(M);
   for (int c = sub; c < a.nc; c += 16) {
-    const double v = c == sub ? v0 : slot_value(ld_dev_u64(a.part + p0 + c));
+    const double v = c == sub ? v0 : slot_value(ld_dev_u64(SV_AT(a, part, p0 + c)));
     if (v != -INFINITY) z += exp2(v - M);   // a NaN piece stays NaN
-    slot_clear(a.part + p0 + c);
-    slot_clear32(a.mraw + p0 + c);
+    slot_clear(SV_AT(a, part, p0 + c));
+    slot_clear32(SV_AT(a, mraw, p0 + c));
   }
 #pragma unroll
   for (int o = 8; o > 0; o >>= 1) z += __shfl_xor(z, o, 16);
@@ -78,7 +81,7 @@ __device__ __forceinline__ void decide_item(const VerifyArgs& a, int b, DecideLd
   // the row pieces) while waves 0, 2 and 3 merge the pieces.
   if (wave == 1) {
     if (lane < g) {
-      const int x = a.tokens[(int64_t)b * g + lane];
+      const int x = *SV_AT(a, tokens, ((int64_t)b * g + lane));
       float ldx = 0.f, ltx = 0.f;
       if (x >= 0 && x < a.V) {
         ldx = load_one<DT>(row_ptr<DT>(a, b, lane), x);
@@ -87,7 +90,7 @@ __device__ __forceinline__ void decide_item(const VerifyArgs& a, int b, DecideLd
       sh.x[lane] = x;
       sh.ldx[lane] = ldx;
       sh.ltx[lane] = ltx;
-      sh.ux[lane] = a.u_acc[(int64_t)b * g + lane];
+      sh.ux[lane] = *SV_AT(a, u_acc, ((int64_t)b * g + lane));
     }
     if (lane == 0) sh.err = ld_dev_u32(a.err);
   } else {
@@ -110,8 +113,9 @@ __device__ __forceinline__ void decide_item(const VerifyArgs& a, int b, DecideLd
   const TCoef tc = temp_coef(a, b);
   for (int r = tid; r < Rd; r += kThreads) {
     if (sh.bad[r]) continue;
-    if (a.diag.row_max) a.diag.row_max[(int64_t)b * R + r] = (double)sh.mr[r] * tc.invT;
-    if (a.diag.row_logZ) a.diag.row_logZ[(int64_t)b * R + r] = sh.M[r] * 0.69314718055994530942 + log(sh.Z[r]);
+    if (a.diag.row_max) a.diag.row_max[SV_IDX(a, (int64_t)b * R + r, (int64_t)a.B * R)] = (double)sh.mr[r] * tc.invT;
+    if (a.diag.row_logZ)
+      a.diag.row_logZ[SV_IDX(a, (int64_t)b * R + r, (int64_t)a.B * R)] = sh.M[r] * 0.69314718055994530942 + log(sh.Z[r]);
   }
 
   if (wave == 0) {
@@ -127,16 +131,17 @@ __device__ __forceinline__ void decide_item(const VerifyArgs& a, int b, DecideLd
         double pn = exp2((double)sh.ldx[lane] * tc.cTd - sh.M[lane]);
         double qn = exp2((double)sh.ltx[lane] * tc.cTd - sh.M[g + lane]);
         if constexpr (CUT) {   // p'(x) = p(x) / P_d inside the draft nucleus, else 0; q' alike
-          const TopPRow* tp = a.topp + (int64_t)b * R;
-          pn = sh.ldx[lane] >= tp[lane].L ? pn / tp[lane].P : 0.0;
-          qn = sh.ltx[lane] >= tp[g + lane].L ? qn / tp[g + lane].P : 0.0;
+          const TopPRow* tpd = SV_AT(a, topp, (int64_t)b * R + lane);
+          const TopPRow* tpt = SV_AT(a, topp, (int64_t)b * R + (g + lane));
+          pn = sh.ldx[lane] >= tpd->L ? pn / tpd->P : 0.0;
+          qn = sh.ltx[lane] >= tpt->L ? qn / tpt->P : 0.0;
         }
         double ratio;
         if (pn > 0.0) ratio = fmin(1.0, (qn * sh.Z[lane]) / (pn * sh.Z[g + lane]));
         else ratio = qn > 0.0 ? 1.0 : 0.0;
         acc = (double)sh.ux[lane] < ratio;
-        if (a.diag.px) a.diag.px[(int64_t)b * g + lane] = pn / sh.Z[lane];
-        if (a.diag.qx) a.diag.qx[(int64_t)b * g + lane] = qn / sh.Z[g + lane];
+        if (a.diag.px) a.diag.px[SV_IDX(a, (int64_t)b * g + lane, (int64_t)a.B * g)] = pn / sh.Z[lane];
+        if (a.diag.qx) a.diag.qx[SV_IDX(a, (int64_t)b * g + lane, (int64_t)a.B * g)] = qn / sh.Z[g + lane];
       }
     }
     const uint64_t mask = __ballot(acc);
@@ -167,8 +172,8 @@ __device__ __forceinline__ void decide_item(const VerifyArgs& a, int b, DecideLd
       const double Mt = sh.M[g + k];
       double Pt = 1.0, Pd = 1.0;   // nucleus masses (top-p): q' = q / Pt, p' = p / Pd
       if constexpr (CUT) {
-        Pt = a.topp[(int64_t)b * R + g + k].P;
-        Pd = a.topp[(int64_t)b * R + k].P;
+        Pt = SV_AT(a, topp, ((int64_t)b * R + g + k))->P;
+        Pd = SV_AT(a, topp, ((int64_t)b * R + k))->P;
       }
       rec.Mt = (float)Mt;   // exact below 2^24; otherwise Zt absorbs the rounding
       rec.Zt = ldexp(sh.Z[g + k] * Pt, (int)fmin(fmax(Mt - (double)rec.Mt, -2000.0), 2000.0));
@@ -176,7 +181,7 @@ __device__ __forceinline__ void decide_item(const VerifyArgs& a, int b, DecideLd
       rec.K_hi = (float)K;
       rec.K_lo = (float)(K - (double)rec.K_hi);
     }
-    store_rec(a.seq + b, rec);
+    store_rec(SV_AT(a, seq, b), rec);
   }
 }
 
@@ -208,7 +213,7 @@ template <int DT>
 __device__ __forceinline__ void test_item(const VerifyArgs& a, int b, int i, TestLds& sh) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = a.gamma, R = 2 * g + 1;
-  unsigned* fl = a.flag + (int64_t)b * kFlagStride;
+  unsigned* fl = SV_AT(a, flag, (int64_t)b * kFlagStride);
   if (wave == 0) {
     if (lane < 32) {
       const int h = lane >> 4;   // 0: draft row i, 1: target row i
@@ -223,7 +228,7 @@ __device__ __forceinline__ void test_item(const VerifyArgs& a, int b, int i, Tes
       }
     }
   } else if (wave == 1 && lane == 0) {
-    const int x = a.tokens[(int64_t)b * g + i];
+    const int x = *SV_AT(a, tokens, ((int64_t)b * g + i));
     float ldx = 0.f, ltx = 0.f;
     if (x >= 0 && x < a.V) {
       ldx = load_one<DT>(row_ptr<DT>(a, b, i), x);
@@ -232,7 +237,7 @@ __device__ __forceinline__ void test_item(const VerifyArgs& a, int b, int i, Tes
     sh.x = x;
     sh.ldx = ldx;
     sh.ltx = ltx;
-    sh.ux = a.u_acc[(int64_t)b * g + i];
+    sh.ux = *SV_AT(a, u_acc, ((int64_t)b * g + i));
     sh.err = ld_dev_u32(a.err);
   }
   __syncthreads();
@@ -270,15 +275,17 @@ __device__ __forceinline__ void test_item(const VerifyArgs& a, int b, int i, Tes
     if (decided && !bad && acc && i + 1 < g)
       __hip_atomic_store(fl + kProgWord, (unsigned)(i + 1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (decided && !bad) {
-      if (a.diag.px) a.diag.px[(int64_t)b * g + i] = pn / sh.Z[0];
-      if (a.diag.qx) a.diag.qx[(int64_t)b * g + i] = qn / sh.Z[1];
+      if (a.diag.px) a.diag.px[SV_IDX(a, (int64_t)b * g + i, (int64_t)a.B * g)] = pn / sh.Z[0];
+      if (a.diag.qx) a.diag.qx[SV_IDX(a, (int64_t)b * g + i, (int64_t)a.B * g)] = qn / sh.Z[1];
       if (a.diag.row_max) {
-        a.diag.row_max[(int64_t)b * R + i] = (double)sh.mr[0] * tc.invT;
-        a.diag.row_max[(int64_t)b * R + g + i] = (double)sh.mr[1] * tc.invT;
+        a.diag.row_max[SV_IDX(a, (int64_t)b * R + i, (int64_t)a.B * R)] = (double)sh.mr[0] * tc.invT;
+        a.diag.row_max[SV_IDX(a, (int64_t)b * R + g + i, (int64_t)a.B * R)] = (double)sh.mr[1] * tc.invT;
       }
       if (a.diag.row_logZ) {
-        a.diag.row_logZ[(int64_t)b * R + i] = sh.M[0] * 0.69314718055994530942 + log(sh.Z[0]);
-        a.diag.row_logZ[(int64_t)b * R + g + i] = sh.M[1] * 0.69314718055994530942 + log(sh.Z[1]);
+        a.diag.row_logZ[SV_IDX(a, (int64_t)b * R + i, (int64_t)a.B * R)] =
+            sh.M[0] * 0.69314718055994530942 + log(sh.Z[0]);
+        a.diag.row_logZ[SV_IDX(a, (int64_t)b * R + g + i, (int64_t)a.B * R)] =
+            sh.M[1] * 0.69314718055994530942 + log(sh.Z[1]);
       }
     }
     sh.decided = decided && (bad || !acc || i + 1 == g);
@@ -309,7 +316,7 @@ __device__ __forceinline__ void test_item(const VerifyArgs& a, int b, int i, Tes
       rec.K_hi = (float)K;
       rec.K_lo = (float)(K - (double)rec.K_hi);
     }
-    store_rec(a.seq + b, rec);
+    store_rec(SV_AT(a, seq, b), rec);
   }
 }
 

@@ -2,6 +2,9 @@
 #pragma once
 #include "verify_sched.h"
 
+#undef SV_FILE
+#define SV_FILE 6
+
 namespace sv {
 
 // ---------------------------------------------------------------------------
@@ -31,15 +34,15 @@ union ItemLds {
 // gamma (pos = gamma) skips on any known stop.  Read by one thread; the
 // work-group follows its answer.
 __device__ __forceinline__ bool early_stopped(const VerifyArgs& a, int b, int pos) {
-  const unsigned st = ld_dev_u32(a.flag + (int64_t)b * kFlagStride + kStopWord);
+  const unsigned st = ld_dev_u32(SV_AT(a, flag, (int64_t)b * kFlagStride + kStopWord));
   return pos >= a.gamma ? st != 0u : st > 64u - (unsigned)pos;
 }
 // A skipping item publishes skip markers in place of its piece.
 __device__ __forceinline__ void early_skip(const VerifyArgs& a, int b, int r, int c) {
   if (threadIdx.x == 0) {
     const int64_t idx = ((int64_t)b * (2 * a.gamma + 1) + r) * a.nc + c;
-    __hip_atomic_store(a.mraw + idx, kSkipRaw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    st_dev_u64(a.part + idx, kSkipPiece);
+    __hip_atomic_store(SV_AT(a, mraw, idx), kSkipRaw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    st_dev_u64(SV_AT(a, part, idx), kSkipPiece);
   }
 }
 
@@ -82,6 +85,14 @@ void fused_kernel(VerifyArgs a, Sched sc) {
   }
   __syncthreads();
   const int kind = uni(item[0]), b = uni(item[1]), sub = uni(item[2]), skip = uni(item[3]);
+#if SV_CHECKS
+  // The decoded item: a kind with instances, instance and part in range.
+  if (threadIdx.x == 0) {
+    const int kd = (int)SV_IDX(a, kind, kKinds);
+    SV_IDX(a, b, sc.count[kd]);
+    SV_IDX(a, sub, sc.size[kd]);
+  }
+#endif
   switch (kind) {
     case kItemStream: {
       if constexpr (EARLY) {   // b = i * B + sequence; sub: draft row i, then target row i

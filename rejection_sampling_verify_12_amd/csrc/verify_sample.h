@@ -1,6 +1,8 @@
 // Sampling: weights, residual-mass, sampling, draw and final items.
 #pragma once
 #include "verify_decide.h"
+#undef SV_FILE
+#define SV_FILE 4
 
 namespace sv {
 
@@ -44,9 +46,9 @@ __device__ __forceinline__ SampleCoef coef_of(const VerifyArgs& a, int b, const 
   c.Ld = -INFINITY;
   c.Lt = -INFINITY;
   if (CUT && a.topp && rec.k >= 0 && rec.k <= a.gamma) {
-    const TopPRow* tp = a.topp + (int64_t)b * (2 * a.gamma + 1);
-    c.Lt = uni(tp[a.gamma + rec.k].L);
-    if (rec.k < a.gamma) c.Ld = uni(tp[rec.k].L);
+    const int64_t t0 = (int64_t)b * (2 * a.gamma + 1);
+    c.Lt = uni(SV_AT(a, topp, t0 + (a.gamma + rec.k))->L);
+    if (rec.k < a.gamma) c.Ld = uni(SV_AT(a, topp, t0 + rec.k)->L);
   }
   return c;
 }
@@ -241,7 +243,7 @@ __device__ __forceinline__ double tile_slot_value(int mode, double sum, float of
 // A slot whose wait gave up reads as NaN, so the clamp is NaN then.
 __device__ float eps_clamp(const VerifyArgs& a, int b, double* lds_d) {
   double v = 0.0;
-  for (int i = threadIdx.x; i < a.nt; i += kThreads) v += slot_value(poll(a, a.mass + (int64_t)b * a.nt + i));
+  for (int i = threadIdx.x; i < a.nt; i += kThreads) v += slot_value(poll(a, SV_AT(a, mass, (int64_t)b * a.nt + i)));
   v = block_sum(v, lds_d);
   return uni((float)(v * (double)a.eps));
 }
@@ -256,7 +258,7 @@ __device__ __forceinline__ void mass_item(const VerifyArgs& a, int b, int s, dou
   double tw[kTilesPerItem + 1];
   float mt[kTilesPerItem];
   tile_sums<DT, VEC, kModeResidual, CUT>(a, b, coef_of<CUT>(a, b, rec, 0.f), rec.k, s * kTilesPerItem, tw, mt, lds_d);
-  if (threadIdx.x == 0) slot_put(a.mass + (int64_t)b * a.nt + s, tw[kTilesPerItem]);
+  if (threadIdx.x == 0) slot_put(SV_AT(a, mass, (int64_t)b * a.nt + s), tw[kTilesPerItem]);
 }
 
 // N tiles per item (kTilesPerItem, or fewer for short calls: see
@@ -266,7 +268,7 @@ __device__ __forceinline__ void sample_item(const VerifyArgs& a, int b, int s, d
   static_assert(N >= 1 && N <= kTilesPerItem, "the LDS of a sampling item holds kTilesPerItem tiles");
   const SeqRec rec = wait_rec<true>(a, b);
   if (!rec.valid) return;
-  const int t0 = s * N;
+  const int t0 = (int)SV_IDX(a, s * N, a.ntile);
   const float epsS = rec.mode == kModeSaguaroEps ? eps_clamp(a, b, lds_d) : 0.f;
   const SampleCoef cf = coef_of<CUT>(a, b, rec, epsS);
   with_mode<EPS>(rec.mode, [&](auto m) {
@@ -278,8 +280,8 @@ __device__ __forceinline__ void sample_item(const VerifyArgs& a, int b, int s, d
 #pragma unroll
       for (int i = 0; i < N; ++i)
         if (t0 + i < a.ntile)
-          slot_put(a.tiles + (int64_t)b * a.ntile + t0 + i, tile_slot_value(MODE, tw[i], mt[i]));
-      if (MODE == kModeSaguaro) slot_put(a.rsum + (int64_t)b * a.nt + s, tw[N]);
+          slot_put(SV_AT(a, tiles, (int64_t)b * a.ntile + t0 + i), tile_slot_value(MODE, tw[i], mt[i]));
+      if (MODE == kModeSaguaro) slot_put(SV_AT(a, rsum, (int64_t)b * a.nt + s), tw[N]);
     }
   });
 }
@@ -415,7 +417,7 @@ template <int DT, bool VEC, int MODE, bool CUT = false>
 __device__ __forceinline__ void rescan_tile(const VerifyArgs& a, int b, int k, const SampleCoef& cf, double target,
                             DrawLds& sh) {
   const int tid = threadIdx.x;
-  const int tsel = sh.tile;
+  const int tsel = (int)SV_IDX(a, sh.tile, a.ntile);
   const void *drow, *trow;
   draw_rows<DT>(a, b, k, drow, trow);
   const int64_t j0 = (int64_t)tsel * kTile + (int64_t)tid * kUnit;
@@ -497,6 +499,7 @@ __device__ double precise_weight(const VerifyArgs& a, int b, int k, int mode, co
                                  const DrawLds& sh) {
   const void *drow, *trow;
   draw_rows<DT>(a, b, k, drow, trow);
+  y = (int)SV_IDX(a, y, a.V);
   const float lt = cut1<CUT>(load_one<DT>(trow, y), cf.Lt);
   const float ld = mode == kModeTarget ? 0.f : cut1<CUT>(load_one<DT>(drow, y), cf.Ld);
   SampleCoef c = cf;
@@ -514,7 +517,7 @@ __device__ double precise_weight(const VerifyArgs& a, int b, int k, int mode, co
 template <int DT, bool CUT = false>
 __device__ __forceinline__ void recompute_tiles(const VerifyArgs& a, int b, int k, int mode, const SampleCoef& cf,
                                 DrawLds& sh) {
-  uint64_t* tiles = a.tiles + (int64_t)b * a.ntile;
+  uint64_t* tiles = SV_AT(a, tiles, (int64_t)b * a.ntile);
   const void *drow, *trow;
   draw_rows<DT>(a, b, k, drow, trow);
   for (int t = 0; t < a.ntile; ++t) {
@@ -607,7 +610,7 @@ __device__ __forceinline__ void exp_pair(const void* drow, const void* trow, int
 // stored as a complement (0 = not drawn yet).  kLostToken (never a token id)
 // says that a wait of the draw gave up.
 __device__ __forceinline__ uint64_t* drawn_slot(const VerifyArgs& a, int b) {
-  return reinterpret_cast<uint64_t*>(a.flag + (int64_t)b * kFlagStride + 2);
+  return reinterpret_cast<uint64_t*>(SV_AT(a, flag, (int64_t)b * kFlagStride + 2));
 }
 constexpr uint32_t kLostToken = 0xFFFFFFFFu;
 
@@ -623,7 +626,7 @@ constexpr uint32_t kLostToken = 0xFFFFFFFFu;
 // condition, and its tile is marked (E_t = NaN) to be summed again with the
 // exact rho.
 __device__ __forceinline__ uint64_t* ref_slots(const VerifyArgs& a, int b, int t) {
-  return a.ref + ((int64_t)b * a.ntile + t) * 4;
+  return SV_AT(a, ref, ((int64_t)b * a.ntile + t) * 4);
 }
 struct RefineRefs {
   double invT, mt, md;
@@ -701,7 +704,7 @@ __device__ __forceinline__ void refine_draw(const VerifyArgs& a, int b, const Se
   refine_tiles<DT, CUT>(a, b, rec, 0, a.ntile, sh.lds_d);
   if (tid == 0) wait_mem();
   __syncthreads();
-  uint64_t* tiles = a.tiles + (int64_t)b * a.ntile;
+  uint64_t* tiles = SV_AT(a, tiles, (int64_t)b * a.ntile);
   // Normalisers (every thread sums its tiles, in tile order within the thread).
   double z[2] = {0.0, 0.0};
   for (int t = tid; t < a.ntile; t += kThreads) {
@@ -752,13 +755,13 @@ __device__ __forceinline__ void refine_draw(const VerifyArgs& a, int b, const Se
   }
   wait_mem();
   __syncthreads();
-  const double u = (double)a.u_smp[(int64_t)b * (a.gamma + 1) + k];
+  const double u = (double)*SV_AT(a, u_smp, ((int64_t)b * (a.gamma + 1) + k));
   double target;
   const double S = uni(locate_tile(tiles, a.ntile, u, sh, target));
   target = uni(target);
   // The chosen tile's running sums in fp64: every thread sums its unit; the
   // owner lane's unit is then walked by thread 0, one logit at a time.
-  const int tsel = sh.tile;
+  const int tsel = (int)SV_IDX(a, sh.tile, a.ntile);
   const int64_t jt = (int64_t)tsel * kTile;
   double ws = 0.0;
 #pragma unroll 1
@@ -828,11 +831,11 @@ __device__ __forceinline__ void draw_item(const VerifyArgs& a, int b, DrawLds& s
   const SeqRec rec = wait_rec<true>(a, b);
   if (!rec.valid) return;
   const int g = a.gamma, k = rec.k;
-  uint64_t* tiles = a.tiles + (int64_t)b * a.ntile;
+  uint64_t* tiles = SV_AT(a, tiles, (int64_t)b * a.ntile);
   const float epsS = rec.mode == kModeSaguaroEps ? eps_clamp(a, b, sh.lds_d) : 0.f;
   const SampleCoef cf = coef_of<CUT>(a, b, rec, epsS);
   int mode = rec.mode;
-  const double u = (double)a.u_smp[(int64_t)b * (g + 1) + k];   // in flight while the tiles arrive
+  const double u = (double)*SV_AT(a, u_smp, ((int64_t)b * (g + 1) + k));   // in flight while the tiles arrive
   int lost = 0;   // a wait gave up: no token is drawn from what arrived
   uint64_t own = 0;   // tile tid's slot word as polled
   for (int t = tid; t < a.ntile; t += kThreads) {
@@ -842,7 +845,11 @@ __device__ __forceinline__ void draw_item(const VerifyArgs& a, int b, DrawLds& s
   }
   double rtot = 0.0;   // residual mass (relative to Mt) when it differs from the tile total
   if (mode == kModeSaguaro || mode == kModeSaguaroEps) {
+#if SV_CHECKS
+    uint64_t* rs = mode == kModeSaguaro ? SV_AT(a, rsum, (int64_t)b * a.nt) : SV_AT(a, mass, (int64_t)b * a.nt);
+#else
     uint64_t* rs = (mode == kModeSaguaro ? a.rsum : a.mass) + (int64_t)b * a.nt;
+#endif
     for (int i = tid; i < a.nt; i += kThreads) {
       const uint64_t w = poll(a, rs + i);
       lost |= w == 0ull;
@@ -855,9 +862,9 @@ __device__ __forceinline__ void draw_item(const VerifyArgs& a, int b, DrawLds& s
     __syncthreads();
     for (int t = tid; t < a.ntile; t += kThreads) slot_clear(tiles + t);
     if (mode == kModeSaguaro)
-      for (int i = tid; i < a.nt; i += kThreads) slot_clear(a.rsum + (int64_t)b * a.nt + i);
+      for (int i = tid; i < a.nt; i += kThreads) slot_clear(SV_AT(a, rsum, (int64_t)b * a.nt + i));
     if (mode == kModeSaguaroEps)
-      for (int i = tid; i < a.nt; i += kThreads) slot_clear(a.mass + (int64_t)b * a.nt + i);
+      for (int i = tid; i < a.nt; i += kThreads) slot_clear(SV_AT(a, mass, (int64_t)b * a.nt + i));
     return;
   }
 
@@ -920,10 +927,10 @@ __device__ __forceinline__ void draw_item(const VerifyArgs& a, int b, DrawLds& s
   }
   if (tid == 0) {
     if (!refine) {
-      if (a.diag.resid_mass) a.diag.resid_mass[b] = sh.n_rm;
-      if (a.diag.token_prob) a.diag.token_prob[b] = sh.n_tp;
-      if (a.diag.cdf_lo) a.diag.cdf_lo[b] = sh.n_lo;
-      if (a.diag.cdf_hi) a.diag.cdf_hi[b] = sh.n_hi;
+      if (a.diag.resid_mass) a.diag.resid_mass[SV_IDX(a, b, a.B)] = sh.n_rm;
+      if (a.diag.token_prob) a.diag.token_prob[SV_IDX(a, b, a.B)] = sh.n_tp;
+      if (a.diag.cdf_lo) a.diag.cdf_lo[SV_IDX(a, b, a.B)] = sh.n_lo;
+      if (a.diag.cdf_hi) a.diag.cdf_hi[SV_IDX(a, b, a.B)] = sh.n_hi;
     }
     st_dev_u64(drawn_slot(a, b), ~(uint64_t)(refine ? kRefineToken : (uint32_t)sh.y));
   }
@@ -931,9 +938,9 @@ __device__ __forceinline__ void draw_item(const VerifyArgs& a, int b, DrawLds& s
   __syncthreads();
   for (int t = tid; t < a.ntile; t += kThreads) slot_clear(tiles + t);
   if (rec.mode == kModeSaguaro)
-    for (int i = tid; i < a.nt; i += kThreads) slot_clear(a.rsum + (int64_t)b * a.nt + i);
+    for (int i = tid; i < a.nt; i += kThreads) slot_clear(SV_AT(a, rsum, (int64_t)b * a.nt + i));
   if (rec.mode == kModeSaguaroEps)
-    for (int i = tid; i < a.nt; i += kThreads) slot_clear(a.mass + (int64_t)b * a.nt + i);
+    for (int i = tid; i < a.nt; i += kThreads) slot_clear(SV_AT(a, mass, (int64_t)b * a.nt + i));
 }
 
 // ---------------------------------------------------------------------------
@@ -964,8 +971,10 @@ __device__ __forceinline__ void final_item(const VerifyArgs& a, int b, FinalLds&
       const bool ok = row_ok(M, z);
       sh.ok = ok;
       const bool read = !a.early || (rec.valid && rec.k == g);
-      if (ok && read && a.diag.row_max) a.diag.row_max[(int64_t)b * R + r] = (double)mr * temp_coef(a, b).invT;
-      if (ok && read && a.diag.row_logZ) a.diag.row_logZ[(int64_t)b * R + r] = M * 0.69314718055994530942 + log(z);
+      if (ok && read && a.diag.row_max)
+        a.diag.row_max[SV_IDX(a, (int64_t)b * R + r, (int64_t)a.B * R)] = (double)mr * temp_coef(a, b).invT;
+      if (ok && read && a.diag.row_logZ)
+        a.diag.row_logZ[SV_IDX(a, (int64_t)b * R + r, (int64_t)a.B * R)] = M * 0.69314718055994530942 + log(z);
       sh.y = -1;
       sh.refine = 0;
       if (rec.valid) {
@@ -990,22 +999,22 @@ __device__ __forceinline__ void final_item(const VerifyArgs& a, int b, FinalLds&
       const int64_t orow = (int64_t)b * (g + 1);
       if (tid <= g) {
         int tok = -1;
-        if (tid < k) tok = a.tokens[(int64_t)b * g + tid];
+        if (tid < k) tok = *SV_AT(a, tokens, ((int64_t)b * g + tid));
         else if (tid == k) tok = sh.y;
-        a.out_tokens[orow + tid] = tok;
+        *SV_AT(a, out_tokens, (orow + tid)) = tok;
       }
       if (tid == 0) {
-        a.out_acc[b] = k;
-        if (a.out_first_reject) a.out_first_reject[b] = k < g ? k : -1;
-        if (a.out_mask) a.out_mask[b] = rec.mask;
-        if (a.out_len) a.out_len[b] = (a.in_len ? a.in_len[b] : 0) + k + 1;
+        *SV_AT(a, out_acc, b) = k;
+        if (a.out_first_reject) *SV_AT(a, out_first_reject, b) = k < g ? k : -1;
+        if (a.out_mask) *SV_AT(a, out_mask, b) = rec.mask;
+        if (a.out_len) *SV_AT(a, out_len, b) = (a.in_len ? *SV_AT(a, in_len, b) : 0) + k + 1;
       }
     }
   }
   // Once every other item of the sequence is done with the decision record,
   // clear it and the count.
   if (tid == 0) {
-    unsigned* f = a.flag + (int64_t)b * kFlagStride;
+    unsigned* f = SV_AT(a, flag, (int64_t)b * kFlagStride);
     const unsigned expect = (unsigned)a.nt * ((a.saguaro && a.eps > 0.f) ? 2u : 1u) + 1u;
     unsigned polls = 0;
     while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < expect &&
@@ -1022,7 +1031,7 @@ __device__ __forceinline__ void final_item(const VerifyArgs& a, int b, FinalLds&
     if (refine)   // refine_item reads the record, then clears it and the pending word
       __hip_atomic_store(f + kPendingWord, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     else
-      clear_rec(a.seq + b);
+      clear_rec(SV_AT(a, seq, b));
   }
   if constexpr (INLINE) {
     if (refine) {
@@ -1038,23 +1047,23 @@ __device__ __forceinline__ void final_item(const VerifyArgs& a, int b, FinalLds&
 // refinement return at once.
 template <int DT, bool CUT>
 __device__ __forceinline__ void refine_item(const VerifyArgs& a, int b, DrawLds& sh) {
-  unsigned* f = a.flag + (int64_t)b * kFlagStride;
+  unsigned* f = SV_AT(a, flag, (int64_t)b * kFlagStride);
   if (ld_dev_u32(f + kPendingWord) == 0u) return;
   bool lost;
   const SeqRec rec = wait_rec<false>(a, b, lost);
   if (!lost && rec.valid && rec.k < a.gamma) {
     refine_draw<DT, CUT>(a, b, rec, sh);
     if (threadIdx.x == 0) {
-      a.out_tokens[(int64_t)b * (a.gamma + 1) + rec.k] = sh.y;
-      if (a.diag.resid_mass) a.diag.resid_mass[b] = sh.n_rm;
-      if (a.diag.token_prob) a.diag.token_prob[b] = sh.n_tp;
-      if (a.diag.cdf_lo) a.diag.cdf_lo[b] = sh.n_lo;
-      if (a.diag.cdf_hi) a.diag.cdf_hi[b] = sh.n_hi;
+      *SV_AT(a, out_tokens, ((int64_t)b * (a.gamma + 1) + rec.k)) = sh.y;
+      if (a.diag.resid_mass) a.diag.resid_mass[SV_IDX(a, b, a.B)] = sh.n_rm;
+      if (a.diag.token_prob) a.diag.token_prob[SV_IDX(a, b, a.B)] = sh.n_tp;
+      if (a.diag.cdf_lo) a.diag.cdf_lo[SV_IDX(a, b, a.B)] = sh.n_lo;
+      if (a.diag.cdf_hi) a.diag.cdf_hi[SV_IDX(a, b, a.B)] = sh.n_hi;
     }
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    clear_rec(a.seq + b);
+    clear_rec(SV_AT(a, seq, b));
     slot_clear32(f + kPendingWord);
   }
 }

@@ -2,6 +2,9 @@
 #pragma once
 #include "verify_args.h"
 
+#undef SV_FILE
+#define SV_FILE 2
+
 namespace sv {
 
 // ---------------------------------------------------------------------------
@@ -80,6 +83,7 @@ __device__ __forceinline__ void store_leaders(const StreamLds& sh, bool nan, Top
 // leaders in cpart.
 template <int DT, bool VEC, int U, bool LEAD = false>
 __device__ __forceinline__ void stream_item(const VerifyArgs& a, int b, int r, int c, StreamLds& sh) {
+  c = (int)SV_IDX(a, c, a.nc);
   const void* row = row_ptr<DT>(a, b, r);
   const int64_t begin = (int64_t)c * a.chunk;
   const int64_t end = min<int64_t>(begin + a.chunk, a.V);
@@ -150,9 +154,9 @@ __device__ __forceinline__ void stream_item(const VerifyArgs& a, int b, int r, i
     // log2 of the chunk's normaliser; -inf for an all -inf chunk.
     const double v = sb > 0.0 ? (double)mb + log2(sb) : (sb == 0.0 ? -INFINITY : sb);
     const int64_t idx = ((int64_t)b * (2 * a.gamma + 1) + r) * a.nc + c;
-    slot_put32(a.mraw + idx, mr);
-    slot_put(a.part + idx, v);
-    if constexpr (LEAD) store_leaders(sh, v != v, a.cpart + ((int64_t)b * (a.gamma + 1) + r) * a.nc + c);
+    slot_put32(SV_AT(a, mraw, idx), mr);
+    slot_put(SV_AT(a, part, idx), v);
+    if constexpr (LEAD) store_leaders(sh, v != v, SV_AT(a, cpart, ((int64_t)b * (a.gamma + 1) + r) * a.nc + c));
   }
 }
 
@@ -161,6 +165,10 @@ __device__ __forceinline__ void stream_item(const VerifyArgs& a, int b, int r, i
 template <int DT, bool VEC, int U>
 __device__ __forceinline__ void leader_item(const VerifyArgs& a, int b, int c, StreamLds& sh) {
   constexpr int kEs = DT == kBF16 ? 2 : 4;
+#if SV_CHECKS
+  b = (int)SV_IDX(a, b, a.B);
+  c = (int)SV_IDX(a, c, a.nc);
+#endif
   const int64_t ridx = (int64_t)b * (a.gamma + 1) + a.gamma;
   const void* row = static_cast<const char*>(a.draft) + ridx * a.V * kEs;
   const int64_t begin = (int64_t)c * a.chunk;
@@ -219,19 +227,19 @@ __device__ __forceinline__ void leader_item(const VerifyArgs& a, int b, int c, S
   if (threadIdx.x == 0) {
     int any = 0;
     for (int i = 0; i < kWaves; ++i) any |= sh.nan[i];
-    store_leaders(sh, any != 0, a.cpart + ridx * a.nc + c);
+    store_leaders(sh, any != 0, SV_AT(a, cpart, ridx * a.nc + c));
   }
 }
 
 // The outputs of an invalid sequence (threads 0..gamma).
 __device__ __forceinline__ void write_invalid(const VerifyArgs& a, int b, int tid) {
   const int g = a.gamma;
-  if (tid <= g) a.out_tokens[(int64_t)b * (g + 1) + tid] = -1;
+  if (tid <= g) *SV_AT(a, out_tokens, ((int64_t)b * (g + 1) + tid)) = -1;
   if (tid == 0) {
-    a.out_acc[b] = -1;
-    if (a.out_first_reject) a.out_first_reject[b] = -1;
-    if (a.out_mask) a.out_mask[b] = 0;
-    if (a.out_len) a.out_len[b] = a.in_len ? a.in_len[b] : 0;
+    *SV_AT(a, out_acc, b) = -1;
+    if (a.out_first_reject) *SV_AT(a, out_first_reject, b) = -1;
+    if (a.out_mask) *SV_AT(a, out_mask, b) = 0;
+    if (a.out_len) *SV_AT(a, out_len, b) = a.in_len ? *SV_AT(a, in_len, b) : 0;
   }
 }
 

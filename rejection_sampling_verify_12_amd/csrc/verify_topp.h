@@ -2,6 +2,9 @@
 #pragma once
 #include "verify_kernels.h"
 
+#undef SV_FILE
+#define SV_FILE 5
+
 namespace sv {
 
 // ---------------------------------------------------------------------------
@@ -33,7 +36,7 @@ __device__ __forceinline__ float key_logit(uint32_t k) {
 __global__ __launch_bounds__(64) void topp_init_kernel(VerifyArgs a) {
   const int64_t row = blockIdx.x;
   const int lane = threadIdx.x;
-  const uint64_t* p = a.part + row * a.nc;
+  const uint64_t* p = SV_AT(a, part, row * a.nc);
   double M = -INFINITY;
   for (int c = lane; c < a.nc; c += 64) M = fmax(M, slot_value(ld_dev_u64(p + c)));
 #pragma unroll
@@ -54,7 +57,7 @@ __global__ __launch_bounds__(64) void topp_init_kernel(VerifyArgs a) {
     t.P = 1.0;
     t.prefix = 0u;
     t.L = -INFINITY;
-    a.topp[row] = t;
+    *SV_AT(a, topp, row) = t;
   }
 }
 
@@ -71,8 +74,8 @@ __global__ __launch_bounds__(kThreads) void topp_hist_kernel(VerifyArgs a, int p
   const int c = (int)(id - row * a.nc);
   const int b = (int)(row / R), r = (int)(row - (int64_t)b * R);
   const TCoef tc = temp_coef(a, b);
-  const float Mf = (float)uni(a.topp[row].M);
-  const uint32_t prefix = (uint32_t)uni((int)a.topp[row].prefix);
+  const float Mf = (float)uni(SV_AT(a, topp, row)->M);
+  const uint32_t prefix = (uint32_t)uni((int)SV_AT(a, topp, row)->prefix);
   constexpr int KB = DT == kBF16 ? 16 : 32;
   const int shift = KB - 8 * (pass + 1);
   const int wave = threadIdx.x >> 6;
@@ -117,7 +120,7 @@ __global__ __launch_bounds__(kThreads) void topp_hist_kernel(VerifyArgs a, int p
   }
   if (cur >= 0) atomicAdd(&h[wave][cur], acc);
   __syncthreads();
-  double* g = a.hist + row * kDigits;
+  double* g = SV_AT(a, hist, row * kDigits);
   for (int i = threadIdx.x; i < kDigits; i += kThreads) {
     double t = 0.0;
 #pragma unroll
@@ -136,8 +139,8 @@ template <int DT>
 __global__ __launch_bounds__(64) void topp_select_kernel(VerifyArgs a, int pass, int npass) {
   const int64_t row = blockIdx.x;
   const int lane = threadIdx.x;
-  TopPRow t = a.topp[row];
-  double* g = a.hist + row * kDigits;
+  TopPRow t = *SV_AT(a, topp, row);
+  double* g = SV_AT(a, hist, row * kDigits);
   double m[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) m[q] = g[4 * lane + q];
@@ -201,7 +204,7 @@ __global__ __launch_bounds__(64) void topp_select_kernel(VerifyArgs a, int pass,
       t.L = key_logit<DT>(t.prefix);
       t.P = (t.above + s_h) / t.Z;
     }
-    a.topp[row] = t;
+    *SV_AT(a, topp, row) = t;
   }
 }
 
@@ -390,8 +393,8 @@ __device__ __forceinline__ void count_outputs(const VerifyArgs& a, int64_t row, 
       else if (kmax >= 0) v = (double)mref + log2(Z);
       mr = (flags & 2) ? INFINITY : vmax;
     }
-    slot_put32(a.mraw + p0 + i, mr);
-    slot_put(a.part + p0 + i, v);
+    slot_put32(SV_AT(a, mraw, p0 + i), mr);
+    slot_put(SV_AT(a, part, p0 + i), v);
   }
   if (tid == 0) {
     TopPRow tr;
@@ -403,7 +406,7 @@ __device__ __forceinline__ void count_outputs(const VerifyArgs& a, int64_t row, 
     tr.P = cut ? P : 1.0;
     tr.prefix = cut ? (uint32_t)sel : 0u;
     tr.L = cut ? key_logit<kBF16>((uint32_t)sel) : -INFINITY;
-    a.topp[row] = tr;
+    *SV_AT(a, topp, row) = tr;
   }
 }
 
@@ -771,9 +774,9 @@ __global__ __launch_bounds__(kCountThreads) void topp_count_kernel(VerifyArgs a,
       E = (int)tot;
     } else {   // left to topp_redo_kernel
       if (t == 0) {
-        const unsigned i = __hip_atomic_fetch_add(a.redo, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const unsigned i = __hip_atomic_fetch_add(SV_AT(a, redo, 0), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const unsigned wrapped = (int64_t)tsum != a.V ? kRedoWrapped : 0u;
-        __hip_atomic_store(a.redo + 2 + i, ((unsigned)row + 1u) | wrapped, __ATOMIC_RELAXED,
+        __hip_atomic_store(SV_AT(a, redo, 2 + i), ((unsigned)row + 1u) | wrapped, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
       }
       for (int i = t; i < kCountWords / 4; i += kCountThreads) c4[i] = make_uint4(0u, 0u, 0u, 0u);
@@ -793,11 +796,11 @@ template <bool VEC>
 __global__ __launch_bounds__(kCountThreads) void topp_redo_kernel(VerifyArgs a) {
   __shared__ CountLds sh;
   const int t = threadIdx.x;
-  const unsigned n = __hip_atomic_load(a.redo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const unsigned n = __hip_atomic_load(SV_AT(a, redo, 0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   uint4* c4 = reinterpret_cast<uint4*>(sh.cnt);
   for (unsigned i = blockIdx.x; i < n; i += gridDim.x) {
-    const unsigned e = __hip_atomic_load(a.redo + 2 + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int64_t row = (int64_t)(e & ~kRedoWrapped) - 1;
+    const unsigned e = __hip_atomic_load(SV_AT(a, redo, 2 + i), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int64_t row = SV_IDX(a, (int64_t)(e & ~kRedoWrapped) - 1, (int64_t)a.B * (2 * a.gamma + 1));
     const bool wrapped = (e & kRedoWrapped) != 0u;
     for (int j = t; j < kCountWords / 4; j += kCountThreads) c4[j] = make_uint4(0u, 0u, 0u, 0u);
     if (t == 0) sh.nev = 0u;
@@ -810,13 +813,13 @@ __global__ __launch_bounds__(kCountThreads) void topp_redo_kernel(VerifyArgs a) 
     __syncthreads();
     finish_inplace<VEC>(a, row, sh, wrapped);
     __syncthreads();
-    if (t == 0) __hip_atomic_store(a.redo + 2 + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (t == 0) __hip_atomic_store(SV_AT(a, redo, 2 + i), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   if (t == 0) {
-    const unsigned d = __hip_atomic_fetch_add(a.redo + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned d = __hip_atomic_fetch_add(SV_AT(a, redo, 1), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (d == gridDim.x - 1) {
-      __hip_atomic_store(a.redo, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(a.redo + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(SV_AT(a, redo, 0), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(SV_AT(a, redo, 1), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }

@@ -31,6 +31,20 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, n), n
 
 
+def test_checks_build_exports_the_same_abi():
+    """The checks build (when built) exports every declared function and its
+    marker; the default library has no marker."""
+    from rejection_sampling_verify_12_amd import build as BLD
+    assert not hasattr(R.load_library(), "spec_checks_build")
+    if not os.path.exists(BLD.CHECKS_LIB):
+        pytest.skip("checks build not built")
+    lib = ctypes.CDLL(BLD.CHECKS_LIB)
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    lib.spec_checks_build.restype = ctypes.c_int
+    assert lib.spec_checks_build() == 1
+
+
 def test_status_strings():
     for st in (R.SPEC_OK, R.SPEC_EINVAL, R.SPEC_EDTYPE, R.SPEC_EWORKSPACE, R.SPEC_ELAUNCH):
         assert R.spec_status_str(st) and R.spec_status_str(st) != "unknown status"
