@@ -66,6 +66,14 @@ constexpr int kMinChunk = SV_STREAM_UNROLL * kThreads * kUnit;
 constexpr int64_t kSmallCallItems = 512;
 static_assert(kChunk % kMinChunk == 0 && (kChunk / kMinChunk & (kChunk / kMinChunk - 1)) == 0,
               "chunks halve down to the batch stride");
+// The shortest chunk of a small call (its chunks halve down to it): one tile.
+#ifndef SV_SMALL_CHUNK
+#define SV_SMALL_CHUNK 2048
+#endif
+constexpr int kSmallChunk = SV_SMALL_CHUNK;
+static_assert(kSmallChunk % kTile == 0 && kChunk % kSmallChunk == 0 &&
+                  (kChunk / kSmallChunk & (kChunk / kSmallChunk - 1)) == 0,
+              "small-call chunks are whole tiles and halve down from the default chunk");
 static_assert(kChunk % (SV_STREAM_UNROLL * kThreads * kUnit) == 0,
               "a stream chunk must hold whole batches");
 constexpr unsigned kMaxPolls = 1u << 22;   // bounded waits: about a quarter of a second
