@@ -152,61 +152,6 @@ static hipError_t resident_groups(int& slots) {
   return hipSuccess;
 }
 
-// NSm stream items per sequence for the rows the accept tests read, NL for
-// target row gamma, NM residual-mass and NB sampling items.
-static Sched make_sched(int B, int NSm, int NL, int NM, int NB, int slots) {
-  Sched s;
-  for (int i = 0; i < kKinds; ++i) s.count[i] = B;
-  s.lag[kItemTest] = 0;
-  s.size[kItemTest] = 0;
-  const double spr = (double)slots / (double)(NSm + NL);   // sequences streamed per round
-  auto steps = [&](int milli) { return (int)std::lround(spr * milli / 1000.0); };
-  s.lag[kItemStream] = 0;
-  s.lag[kItemDecide] = steps(SV_LAG_DECIDE);
-  s.lag[kItemMass] = s.lag[kItemDecide] + (NM > 0 ? steps(SV_LAG_MASS) : 0);
-  s.lag[kItemSample] = s.lag[kItemMass] + steps(SV_LAG_SAMPLE);
-  s.lag[kItemDraw] = s.lag[kItemSample] + steps(SV_LAG_DRAW);
-  s.lag[kItemLast] = std::max(B, s.lag[kItemDraw]);
-  s.lag[kItemFinal] = s.lag[kItemLast] + steps(SV_LAG_FINAL);
-  s.size[kItemStream] = NSm;
-  s.size[kItemDecide] = 1;
-  s.size[kItemMass] = NM;
-  s.size[kItemSample] = NB;
-  s.size[kItemDraw] = 1;
-  s.size[kItemLast] = NL;
-  s.size[kItemFinal] = 1;
-  sched_finish(s);
-  return s;
-}
-
-// Early exit: G positions, NC chunks per row.
-static Sched make_sched_early(int B, int G, int NC, int NM, int NB, int slots) {
-  Sched s;
-  const double spr = (double)slots / (double)(2 * NC + 1);   // position-steps per round
-  auto steps = [&](int milli) { return (int)std::lround(spr * milli / 1000.0); };
-  for (int i = 0; i < kKinds; ++i) s.count[i] = B;
-  s.count[kItemStream] = s.count[kItemTest] = G * B;
-  s.lag[kItemStream] = 0;
-  s.lag[kItemTest] = std::min(steps(SV_LAG_TEST), std::max(B - 1, 0));
-  const int base = (G - 1) * B + s.lag[kItemTest] + 1;   // after the test of the last position
-  s.lag[kItemDecide] = 0;
-  s.lag[kItemMass] = base;
-  s.lag[kItemSample] = base + (NM > 0 ? steps(SV_LAG_SAMPLE) : 0);
-  s.lag[kItemDraw] = s.lag[kItemSample] + steps(SV_LAG_DRAW);
-  s.lag[kItemLast] = std::max(G * B, s.lag[kItemDraw]);
-  s.lag[kItemFinal] = s.lag[kItemLast] + steps(SV_LAG_FINAL);
-  s.size[kItemStream] = 2 * NC;
-  s.size[kItemTest] = 1;
-  s.size[kItemDecide] = 0;
-  s.size[kItemMass] = NM;
-  s.size[kItemSample] = NB;
-  s.size[kItemDraw] = 1;
-  s.size[kItemLast] = NC;
-  s.size[kItemFinal] = 1;
-  sched_finish(s);
-  return s;
-}
-
 template <int DT, bool VEC>
 static hipError_t launch_kernels(const VerifyArgs& a, hipStream_t st);
 

@@ -95,10 +95,66 @@ static void sched_finish(Sched& s) {
   }
 }
 
+// NSm stream items per sequence for the rows the accept tests read, NL for
+// target row gamma, NM residual-mass and NB sampling items.
+static Sched make_sched(int B, int NSm, int NL, int NM, int NB, int slots) {
+  Sched s;
+  for (int i = 0; i < kKinds; ++i) s.count[i] = B;
+  s.lag[kItemTest] = 0;
+  s.size[kItemTest] = 0;
+  const double spr = (double)slots / (double)(NSm + NL);   // sequences streamed per round
+  auto steps = [&](int milli) { return (int)std::lround(spr * milli / 1000.0); };
+  s.lag[kItemStream] = 0;
+  s.lag[kItemDecide] = steps(SV_LAG_DECIDE);
+  s.lag[kItemMass] = s.lag[kItemDecide] + (NM > 0 ? steps(SV_LAG_MASS) : 0);
+  s.lag[kItemSample] = s.lag[kItemMass] + steps(SV_LAG_SAMPLE);
+  s.lag[kItemDraw] = s.lag[kItemSample] + steps(SV_LAG_DRAW);
+  s.lag[kItemLast] = std::max(B, s.lag[kItemDraw]);
+  s.lag[kItemFinal] = s.lag[kItemLast] + steps(SV_LAG_FINAL);
+  s.size[kItemStream] = NSm;
+  s.size[kItemDecide] = 1;
+  s.size[kItemMass] = NM;
+  s.size[kItemSample] = NB;
+  s.size[kItemDraw] = 1;
+  s.size[kItemLast] = NL;
+  s.size[kItemFinal] = 1;
+  sched_finish(s);
+  return s;
+}
+
+// Early exit: G positions, NC chunks per row.
+static Sched make_sched_early(int B, int G, int NC, int NM, int NB, int slots) {
+  Sched s;
+  const double spr = (double)slots / (double)(2 * NC + 1);   // position-steps per round
+  auto steps = [&](int milli) { return (int)std::lround(spr * milli / 1000.0); };
+  for (int i = 0; i < kKinds; ++i) s.count[i] = B;
+  s.count[kItemStream] = s.count[kItemTest] = G * B;
+  s.lag[kItemStream] = 0;
+  s.lag[kItemTest] = std::min(steps(SV_LAG_TEST), std::max(B - 1, 0));
+  const int base = (G - 1) * B + s.lag[kItemTest] + 1;   // after the test of the last position
+  s.lag[kItemDecide] = 0;
+  s.lag[kItemMass] = base;
+  s.lag[kItemSample] = base + (NM > 0 ? steps(SV_LAG_SAMPLE) : 0);
+  s.lag[kItemDraw] = s.lag[kItemSample] + steps(SV_LAG_DRAW);
+  s.lag[kItemLast] = std::max(G * B, s.lag[kItemDraw]);
+  s.lag[kItemFinal] = s.lag[kItemLast] + steps(SV_LAG_FINAL);
+  s.size[kItemStream] = 2 * NC;
+  s.size[kItemTest] = 1;
+  s.size[kItemDecide] = 0;
+  s.size[kItemMass] = NM;
+  s.size[kItemSample] = NB;
+  s.size[kItemDraw] = 1;
+  s.size[kItemLast] = NC;
+  s.size[kItemFinal] = 1;
+  sched_finish(s);
+  return s;
+}
+
 // Two decoders of a block number: a binary search over the steps (the
 // default order measures faster with it) and the segment table (the
 // early-exit order, whose many short items gain from the shorter decode).
-__device__ inline int64_t sched_offset_dev(const Sched& s, int t) {
+// Host code too, so that a host test can walk every block of an order.
+__host__ __device__ inline int64_t sched_offset_dev(const Sched& s, int t) {
   int64_t o = 0;
 #pragma unroll
   for (int i = 0; i < kKinds; ++i) {
@@ -108,7 +164,7 @@ __device__ inline int64_t sched_offset_dev(const Sched& s, int t) {
   }
   return o;
 }
-__device__ inline void sched_decode_search(const Sched& s, int j, int& kind, int& b, int& sub) {
+__host__ __device__ inline void sched_decode_search(const Sched& s, int j, int& kind, int& b, int& sub) {
   int lo = 0, hi = s.steps;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
@@ -134,7 +190,7 @@ __device__ inline void sched_decode_search(const Sched& s, int j, int& kind, int
 }
 // Every index into the table is a constant (unrolled loops and selects), so
 // the table is read straight from the kernel arguments.
-__device__ inline void sched_decode_table(const Sched& s, int j, int& kind, int& b, int& sub) {
+__host__ __device__ inline void sched_decode_table(const Sched& s, int j, int& kind, int& b, int& sub) {
   int step = s.seg_step[0], first = s.seg_first[0], per = s.seg_per[0];
   unsigned mask = s.seg_mask[0];
 #pragma unroll

@@ -245,6 +245,29 @@ def test_lost_decision_record_decodes_without_indices(tmp_path):
     assert run.returncode == 0, run.stdout + run.stderr
 
 
+def test_launch_orders_only_wait_on_earlier_blocks(tmp_path):
+    """The single kernel's launch orders (tests/host/sched_check.hip, the real
+    header compiled host-only): over a sweep of sizes and slot counts every
+    block decodes to one in-range item with both decoders, every item is
+    dispatched exactly once, and every item a block waits for has a smaller
+    block number (blocks start in order, so every wait ends)."""
+    import shutil
+    import subprocess
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc not available")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    exe = str(tmp_path / "sched_check")
+    build = subprocess.run([hipcc, "--offload-host-only", "-std=c++17", "-O2", "-x", "hip",
+                            "-I", os.path.join(root, "include"),
+                            "-I", os.path.join(root, "rejection_sampling_verify_12_amd", "csrc"),
+                            os.path.join(root, "tests", "host", "sched_check.hip"), "-o", exe],
+                           capture_output=True, text=True)
+    assert build.returncode == 0, build.stderr[-2000:]
+    run = subprocess.run([exe], capture_output=True, text=True)
+    assert run.returncode == 0 and run.stdout.startswith("ok"), run.stdout[-3000:] + run.stderr[-2000:]
+
+
 def test_noalloc_rejects_sizes_beyond_its_scratch():
     """spec_verify_noalloc checks sizes against its 16 MiB static scratch (and
     the usual arguments) before anything is enqueued or any device is used."""
