@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <limits.h>
 #include <stdint.h>
 
 namespace sv {
@@ -243,26 +244,150 @@ __device__ __forceinline__ void wait_mem() {
 }
 
 // ---------------------------------------------------------------------------
-// Work-group reductions and scans (256 threads, 4 waves).  `lds` must hold
-// kWaves entries of the reduced type; each call ends with a barrier so the
-// scratch can be reused.
+// Cross-lane steps through DPP: a VALU move whose source lane is permuted
+// within a row of 16 lanes, shifted, or broadcast from one row to the next -
+// a few cycles, against the LDS round trip of a lane permute (a 64-bit value
+// takes two moves either way).  Controls in the GFX9 encoding.
+#ifndef SV_DPP
+#define SV_DPP 1
+#endif
+enum : int {
+  kDppQuad1032 = 0xB1,       // quad_perm [1,0,3,2]: lane ^ 1
+  kDppQuad2301 = 0x4E,       // quad_perm [2,3,0,1]: lane ^ 2
+  kDppRowShr = 0x110,        // + n: lane - n within the row
+  kDppWaveShr1 = 0x138,      // lane - 1 across the wave
+  kDppRowMirror = 0x140,     // lane 15 - i of the row
+  kDppRowHalfMirror = 0x141, // lane 7 - i of the half-row
+  kDppRowBcast15 = 0x142,    // lane 15 of each row into the next row
+  kDppRowBcast31 = 0x143,    // lane 31 into rows 2 and 3
+};
+// Lanes the controls, the row mask or the bank mask leave out take `old`
+// (or 0 with BC, for a source outside the row or wave).
+template <int CTRL, int ROWS = 0xF, int BANKS = 0xF, bool BC = false>
+__device__ __forceinline__ int dpp(int v, int old) {
+  return __builtin_amdgcn_update_dpp(old, v, CTRL, ROWS, BANKS, BC);
+}
+template <int CTRL, int ROWS = 0xF, int BANKS = 0xF, bool BC = false>
+__device__ __forceinline__ float dpp(float v, float old) {
+  return __int_as_float(dpp<CTRL, ROWS, BANKS, BC>(__float_as_int(v), __float_as_int(old)));
+}
+template <int CTRL, int ROWS = 0xF, int BANKS = 0xF, bool BC = false>
+__device__ __forceinline__ double dpp(double v, double old) {
+  const uint64_t x = (uint64_t)__double_as_longlong(v), o = (uint64_t)__double_as_longlong(old);
+  const uint32_t lo = (uint32_t)dpp<CTRL, ROWS, BANKS, BC>((int)(uint32_t)x, (int)(uint32_t)o);
+  const uint32_t hi = (uint32_t)dpp<CTRL, ROWS, BANKS, BC>((int)(uint32_t)(x >> 32), (int)(uint32_t)(o >> 32));
+  return __longlong_as_double((long long)((uint64_t)hi << 32 | lo));
+}
+// op over each row of 16 lanes, in every lane of the row (the row's lanes
+// all active).
+template <class T, class Op>
+__device__ __forceinline__ T row16_reduce(T v, Op op) {
+  v = op(v, dpp<kDppQuad1032>(v, v));
+  v = op(v, dpp<kDppQuad2301>(v, v));
+  v = op(v, dpp<kDppRowHalfMirror>(v, v));
+  return op(v, dpp<kDppRowMirror>(v, v));
+}
+// Pair each lane with its lane in the other row of its 32-lane half
+// (SWAP 16) or in the other half (SWAP 32): both lanes of a pair get the
+// pair's two values, the lower row's (half's) first, so they combine the same
+// values in the same order.
+template <int SWAP>
+__device__ __forceinline__ int2 swap_pair(int v) {
+  const auto r = SWAP == 16 ? __builtin_amdgcn_permlane16_swap(v, v, false, false)
+                            : __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return make_int2((int)r[0], (int)r[1]);
+}
+template <int SWAP, class Op>
+__device__ __forceinline__ float swap_combine(float v, Op op) {
+  const int2 p = swap_pair<SWAP>(__float_as_int(v));
+  return op(__int_as_float(p.x), __int_as_float(p.y));
+}
+template <int SWAP, class Op>
+__device__ __forceinline__ int swap_combine(int v, Op op) {
+  const int2 p = swap_pair<SWAP>(v);
+  return op(p.x, p.y);
+}
+template <int SWAP, class Op>
+__device__ __forceinline__ double swap_combine(double v, Op op) {
+  const uint64_t x = (uint64_t)__double_as_longlong(v);
+  const int2 lo = swap_pair<SWAP>((int)(uint32_t)x), hi = swap_pair<SWAP>((int)(uint32_t)(x >> 32));
+  const double a = __longlong_as_double((long long)((uint64_t)(uint32_t)hi.x << 32 | (uint32_t)lo.x));
+  const double b = __longlong_as_double((long long)((uint64_t)(uint32_t)hi.y << 32 | (uint32_t)lo.y));
+  return op(a, b);
+}
+// op over the wave (every lane active), the same value in every lane, kept in
+// vector registers: rows of 16 by DPP, then the row pairs and the halves by
+// the gfx950 lane swaps.
+template <class T, class Op>
+__device__ __forceinline__ T wave_reduce(T v, Op op) {
+  v = row16_reduce(v, op);
+  v = swap_combine<16>(v, op);
+  return swap_combine<32>(v, op);
+}
 
-__device__ __forceinline__ double wave_sum(double v) {
+// Wave reductions through LDS lane permutes.
+__device__ __forceinline__ double wave_sum_lds(double v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
 }
-
-__device__ __forceinline__ float wave_max(float v) {
+__device__ __forceinline__ float wave_max_lds(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
   return v;
 }
 
+// ---------------------------------------------------------------------------
+// Work-group reductions and scans (256 threads, 4 waves).  `lds` must hold
+// kWaves entries of the reduced type; each call ends with a barrier so the
+// scratch can be reused.
+
+__device__ __forceinline__ double wave_sum(double v) {
+#if SV_DPP
+  return wave_reduce(v, [](double x, double y) { return x + y; });
+#else
+  return wave_sum_lds(v);
+#endif
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#if SV_DPP
+  return wave_reduce(v, [](float x, float y) { return fmaxf(x, y); });
+#else
+  return wave_max_lds(v);
+#endif
+}
+
 __device__ __forceinline__ int wave_min_int(int v) {
+#if SV_DPP
+  return wave_reduce(v, [](int x, int y) { return min(x, y); });
+#else
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, 64));
   return v;
+#endif
+}
+
+// Inclusive prefix sum over the wave (every lane active).
+__device__ __forceinline__ double wave_inclusive_scan(double v) {
+#if SV_DPP
+  double s = v + dpp<kDppRowShr + 1, 0xF, 0xF, true>(v, 0.0);
+  s += dpp<kDppRowShr + 2, 0xF, 0xF, true>(v, 0.0);
+  s += dpp<kDppRowShr + 3, 0xF, 0xF, true>(v, 0.0);          // rows: sums of 4
+  s += dpp<kDppRowShr + 4, 0xF, 0xE>(s, 0.0);                // lanes 4..15 of a row
+  s += dpp<kDppRowShr + 8, 0xF, 0xC>(s, 0.0);                // lanes 8..15
+  s += dpp<kDppRowBcast15, 0xA>(s, 0.0);                     // rows 1, 3
+  s += dpp<kDppRowBcast31, 0xC>(s, 0.0);                     // rows 2, 3
+  return s;
+#else
+  const int l = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const double t = __shfl_up(v, o, 64);
+    if (l >= o) v += t;
+  }
+  return v;
+#endif
 }
 
 __device__ __forceinline__ double block_sum(double v, double* lds) {
@@ -352,12 +477,7 @@ __device__ __forceinline__ int block_min_int(int v, int* lds) {
 // thread's offset and writes the total.
 __device__ __forceinline__ double block_exclusive_scan(double v, double* lds, double& total) {
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-  double incl = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const double t = __shfl_up(incl, o, 64);
-    if (l >= o) incl += t;
-  }
+  const double incl = wave_inclusive_scan(v);
   __syncthreads();
   if (l == 63) lds[w] = incl;
   __syncthreads();
@@ -369,7 +489,11 @@ __device__ __forceinline__ double block_exclusive_scan(double v, double* lds, do
   }
   __syncthreads();
   total = all;
+#if SV_DPP
+  const double excl = dpp<kDppWaveShr1, 0xF, 0xF, true>(incl, 0.0);
+#else
   const double excl = __shfl_up(incl, 1, 64);
+#endif
   return before + (l == 0 ? 0.0 : excl);
 }
 

@@ -34,11 +34,16 @@ __device__ __forceinline__ void merge_row(const VerifyArgs& a, int b, int r, int
     if (c == sub) v0 = v;
     M = fmax(M, v);
   }
+#if SV_DPP
+  M = row16_reduce(M, [](double x, double y) { return fmax(x, y); });
+  mr = row16_reduce(mr, [](float x, float y) { return fmaxf(x, y); });
+#else
 #pragma unroll
   for (int o = 8; o > 0; o >>= 1) {
     M = fmax(M, __shfl_xor(M, o, 16));
     mr = fmaxf(mr, __shfl_xor(mr, o, 16));
   }
+#endif
   M = ceil(M);
   for (int c = sub; c < a.nc; c += 16) {
     const double v = c == sub ? v0 : slot_value(ld_dev_u64(SV_AT(a, part, p0 + c)));
@@ -46,8 +51,12 @@ __device__ __forceinline__ void merge_row(const VerifyArgs& a, int b, int r, int
     slot_clear(SV_AT(a, part, p0 + c));
     slot_clear32(SV_AT(a, mraw, p0 + c));
   }
+#if SV_DPP
+  z = row16_reduce(z, [](double x, double y) { return x + y; });
+#else
 #pragma unroll
   for (int o = 8; o > 0; o >>= 1) z += __shfl_xor(z, o, 16);
+#endif
 }
 
 // An all -inf row (M = -inf), a +inf logit (M = +inf) or a NaN logit (z =
