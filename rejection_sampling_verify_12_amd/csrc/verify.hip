@@ -185,7 +185,7 @@ static hipError_t launch_short(const VerifyArgs& a, hipStream_t st) {
   b.nt = (a.ntile + kShortTiles - 1) / kShortTiles;
   const Sched sc = make_sched(b.B, 2 * b.gamma * b.nc, b.nc, 0, b.nt, slots);
   hipLaunchKernelGGL((fused_kernel<DT, VEC, SV_STREAM_UNROLL, false, false, kShortTiles>),
-                     dim3((unsigned)sc.total), dim3(kThreads), 0, st, b, sc);
+                     dim3((unsigned)sc.total), dim3(kThreads), 0, st, FusedArgs{b, sc});
   return hipGetLastError();
 }
 
@@ -209,7 +209,7 @@ static hipError_t launch_all(const VerifyArgs& a, const PredictArgs* pa, hipStre
         b.nc = (int)(((int64_t)a.V + b.chunk - 1) / b.chunk);
         const Sched sc = make_sched_early(b.B, b.gamma, b.nc, eps_mode ? b.nt : 0, b.nt, slots);
         hipLaunchKernelGGL((fused_kernel<DT, VEC, SV_STREAM_UNROLL, false, true>), dim3((unsigned)sc.total),
-                           dim3(kThreads), 0, st, b, sc);
+                           dim3(kThreads), 0, st, FusedArgs{b, sc});
         return launch_refine<DT, false>(b, st);
       }
       hipError_t e = pa ? resident_groups<DT, VEC, true, false>(slots) : resident_groups<DT, VEC, false, false>(slots);
@@ -224,13 +224,13 @@ static hipError_t launch_all(const VerifyArgs& a, const PredictArgs* pa, hipStre
       const Sched sc = make_sched(a.B, 2 * a.gamma * a.nc, (pa ? 2 : 1) * a.nc, eps_mode ? a.nt : 0, a.nt, slots);
       if (pa) {
         hipLaunchKernelGGL((fused_kernel<DT, VEC, SV_STREAM_UNROLL, true, false>), dim3((unsigned)sc.total),
-                           dim3(kThreads), 0, st, a, sc);
+                           dim3(kThreads), 0, st, FusedArgs{a, sc});
         e = launch_refine<DT, false>(a, st);
         if (e != hipSuccess) return e;
         return predict_launch_leaders(*pa, SPEC_BF16, st);
       }
       hipLaunchKernelGGL((fused_kernel<DT, VEC, SV_STREAM_UNROLL, false, false>), dim3((unsigned)sc.total),
-                         dim3(kThreads), 0, st, a, sc);
+                         dim3(kThreads), 0, st, FusedArgs{a, sc});
       return launch_refine<DT, false>(a, st);
     }
   }
@@ -245,7 +245,7 @@ static hipError_t launch_all(const VerifyArgs& a, const PredictArgs* pa, hipStre
       if (short_sampling(a, slots)) return launch_short<DT, VEC>(a, st);   // refines in place too
       const Sched sc = make_sched(a.B, 2 * a.gamma * a.nc, a.nc, 0, a.nt, slots);
       hipLaunchKernelGGL((fused_kernel<DT, VEC, SV_STREAM_UNROLL, false, false>), dim3((unsigned)sc.total),
-                         dim3(kThreads), 0, st, a, sc);
+                         dim3(kThreads), 0, st, FusedArgs{a, sc});
       return hipGetLastError();   // its final items refine in place (registers to spare)
     }
   }

@@ -57,9 +57,16 @@ constexpr int kFusedWaves = DT == kBF16 && VEC ? 8 : 4;
 // items of target row gamma are followed by leader items of draft row gamma).
 // EARLY: the early-exit order (position-major stream items, position tests).
 // N: tiles per sampling item.
+// The single kernel's one argument: the call and its launch order.
+struct FusedArgs {
+  VerifyArgs a;
+  Sched sc;
+};
+
 template <int DT, bool VEC, int U, bool PRED, bool EARLY, int N = kTilesPerItem>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kFusedWaves<DT, VEC>, 8)))
-void fused_kernel(VerifyArgs a, Sched sc) {
+void fused_kernel(FusedArgs fa) {
+  const VerifyArgs& a = fa.a;
   __shared__ ItemLds sh;
   __shared__ int item[4];
 #if SV_TIMELINE
@@ -69,8 +76,10 @@ void fused_kernel(VerifyArgs a, Sched sc) {
   // the CU's waves share) and hands the item to the others.
   if (threadIdx.x < 64) {
     int kind, b, sub;
-    if constexpr (EARLY) sched_decode_table(sc, (int)blockIdx.x, kind, b, sub);
-    else sched_decode_search(sc, (int)blockIdx.x, kind, b, sub);
+    // The order is read where the argument segment holds it (FusedArgs is
+    // the kernel's only argument, at the segment's start).
+    const FusedArgs* ka = (const FusedArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+    sched_decode_mem(ka->sc, (int)blockIdx.x, kind, b, sub);
     if (threadIdx.x == 0) {
       item[0] = kind;
       item[1] = b;
@@ -89,8 +98,8 @@ void fused_kernel(VerifyArgs a, Sched sc) {
   // The decoded item: a kind with instances, instance and part in range.
   if (threadIdx.x == 0) {
     const int kd = (int)SV_IDX(a, kind, kKinds);
-    SV_IDX(a, b, sc.count[kd]);
-    SV_IDX(a, sub, sc.size[kd]);
+    SV_IDX(a, b, fa.sc.count[kd]);
+    SV_IDX(a, sub, fa.sc.size[kd]);
   }
 #endif
   switch (kind) {

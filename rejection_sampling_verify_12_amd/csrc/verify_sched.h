@@ -188,6 +188,40 @@ __host__ __device__ inline void sched_decode_search(const Sched& s, int j, int& 
     w -= s.size[i];
   }
 }
+// The segment of block j by a binary search over the segments' first items,
+// then the kinds of its steps: every index is dynamic, so `s` must be memory
+// the scalar unit reads directly (the kernel argument segment, see
+// FusedArgs) - a few dependent scalar loads instead of the whole table held
+// in scalar registers.
+__host__ __device__ inline void sched_decode_mem(const Sched& s, int j, int& kind, int& b, int& sub) {
+  int lo = 0, hi = s.nseg;   // the last segment starting at or before j (an empty
+  while (hi - lo > 1) {      // one shares its start with the next)
+    const int mid = (lo + hi) >> 1;
+    if (s.seg_first[mid] <= j) lo = mid;
+    else hi = mid;
+  }
+  const int per = s.seg_per[lo];
+  const unsigned mask = s.seg_mask[lo];
+  const int rel = j - s.seg_first[lo];
+  const int dt = rel / per;
+  const int t = s.seg_step[lo] + dt;
+  int w = rel - dt * per;
+  kind = kItemFinal;
+  b = 0;
+  sub = 0;
+  for (int i = 0; i < kKinds; ++i) {
+    if ((mask >> i) & 1u) {
+      const int size = s.size[i];
+      if (w < size) {
+        kind = i;
+        b = t - s.lag[i];
+        sub = w;
+        return;
+      }
+      w -= size;
+    }
+  }
+}
 // Every index into the table is a constant (unrolled loops and selects), so
 // the table is read straight from the kernel arguments.
 __host__ __device__ inline void sched_decode_table(const Sched& s, int j, int& kind, int& b, int& sub) {

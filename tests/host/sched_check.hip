@@ -3,8 +3,8 @@
 // the default sequence-major order (with and without residual-mass items and
 // prediction's leader items) and the early-exit position-major order - over
 // a sweep of batch sizes, gamma, chunk and sampling-item counts and slot
-// counts, every block number is decoded with both decoders, and:
-//   * both decoders give the same item, whose kind, instance and part are in
+// counts, every block number is decoded with the three decoders, and:
+//   * they give the same item, whose kind, instance and part are in
 //     range, and every item of every kind appears exactly once;
 //   * every item a block waits for has a smaller block number.  Blocks are
 //     dispatched in increasing order, so a block only ever waits for blocks
@@ -55,11 +55,13 @@ static bool walk(Order& o, const char* what) {
   CHECK(total == s.total, "%s: %lld items listed, %lld in the order", what, (long long)total, (long long)s.total);
   if (total != s.total) return false;
   for (int64_t j = 0; j < s.total; ++j) {
-    int k1, b1, p1, k2, b2, p2;
+    int k1, b1, p1, k2, b2, p2, k3, b3, p3;
     sched_decode_search(s, (int)j, k1, b1, p1);
     sched_decode_table(s, (int)j, k2, b2, p2);
-    CHECK(k1 == k2 && b1 == b2 && p1 == p2, "%s: block %lld: search (%d,%d,%d) table (%d,%d,%d)", what,
-          (long long)j, k1, b1, p1, k2, b2, p2);
+    sched_decode_mem(s, (int)j, k3, b3, p3);
+    CHECK(k1 == k2 && b1 == b2 && p1 == p2 && k1 == k3 && b1 == b3 && p1 == p3,
+          "%s: block %lld: search (%d,%d,%d) table (%d,%d,%d) mem (%d,%d,%d)", what, (long long)j, k1, b1, p1,
+          k2, b2, p2, k3, b3, p3);
     const bool ok = k1 >= 0 && k1 < kKinds && b1 >= 0 && b1 < s.count[k1] && p1 >= 0 && p1 < s.size[k1];
     CHECK(ok, "%s: block %lld decodes to kind %d instance %d part %d", what, (long long)j, k1, b1, p1);
     if (!ok) return false;
