@@ -71,6 +71,16 @@ __device__ __forceinline__ int64_t check_index(unsigned* chk, int64_t i, int64_t
 #define SV_AT(a, f, i) ((a).f + i)
 #endif
 
+// A kernel's first argument, read where the argument segment holds it
+// (explicit arguments start the segment): each field is loaded where it is
+// used.  Taken by value, every field a kernel uses is loaded at its entry
+// into scalar registers, which then spill to vector lanes on every
+// work-group.
+template <class T>
+__device__ __forceinline__ const T& kernel_arg0() {
+  return *(const T*)__builtin_amdgcn_kernarg_segment_ptr();
+}
+
 // ---------------------------------------------------------------------------
 // Logit loads.  A row is `const void*`; element j is float32 or bfloat16.
 

@@ -245,7 +245,8 @@ __device__ __forceinline__ void greedy_decode(const GreedyArgs& a, int64_t j, bo
 }
 
 template <int DT, bool VEC>
-__global__ __launch_bounds__(kThreads) void greedy_kernel(GreedyArgs a) {
+__global__ __launch_bounds__(kThreads) void greedy_kernel(GreedyArgs) {
+  const GreedyArgs& a = kernel_arg0<GreedyArgs>();
   __shared__ GreedyLds sh;
   __shared__ int item[3];
   if (threadIdx.x < 64) {

@@ -65,7 +65,8 @@ struct FusedArgs {
 
 template <int DT, bool VEC, int U, bool PRED, bool EARLY, int N = kTilesPerItem>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kFusedWaves<DT, VEC>, 8)))
-void fused_kernel(FusedArgs fa) {
+void fused_kernel(FusedArgs) {
+  const FusedArgs& fa = kernel_arg0<FusedArgs>();
   const VerifyArgs& a = fa.a;
   __shared__ ItemLds sh;
   __shared__ int item[4];
@@ -76,10 +77,9 @@ void fused_kernel(FusedArgs fa) {
   // the CU's waves share) and hands the item to the others.
   if (threadIdx.x < 64) {
     int kind, b, sub;
-    // The order is read where the argument segment holds it (FusedArgs is
-    // the kernel's only argument, at the segment's start).
-    const FusedArgs* ka = (const FusedArgs*)__builtin_amdgcn_kernarg_segment_ptr();
-    sched_decode_mem(ka->sc, (int)blockIdx.x, kind, b, sub);
+    // The order is read where the argument segment holds it, with dynamic
+    // indices (scalar loads).
+    sched_decode_mem(fa.sc, (int)blockIdx.x, kind, b, sub);
     if (threadIdx.x == 0) {
       item[0] = kind;
       item[1] = b;
@@ -147,7 +147,8 @@ void fused_kernel(FusedArgs fa) {
 }
 
 template <int DT, bool VEC, int U>
-__global__ __launch_bounds__(kThreads) void stream_kernel(VerifyArgs a) {
+__global__ __launch_bounds__(kThreads) void stream_kernel(VerifyArgs) {
+  const VerifyArgs& a = kernel_arg0<VerifyArgs>();
   __shared__ StreamLds sh;
   const int R = 2 * a.gamma + 1;
   const int64_t id = blockIdx.x;
@@ -159,20 +160,23 @@ __global__ __launch_bounds__(kThreads) void stream_kernel(VerifyArgs a) {
 }
 
 template <int DT, bool CUT>
-__global__ __launch_bounds__(kThreads) void decide_kernel(VerifyArgs a) {
+__global__ __launch_bounds__(kThreads) void decide_kernel(VerifyArgs) {
+  const VerifyArgs& a = kernel_arg0<VerifyArgs>();
   __shared__ DecideLds sh;
   decide_item<DT, CUT>(a, blockIdx.x, sh);
 }
 
 template <int DT>
-__global__ __launch_bounds__(kThreads) void test_kernel(VerifyArgs a) {
+__global__ __launch_bounds__(kThreads) void test_kernel(VerifyArgs) {
+  const VerifyArgs& a = kernel_arg0<VerifyArgs>();
   __shared__ TestLds sh;
   const int i = blockIdx.x / a.B;
   test_item<DT>(a, blockIdx.x - i * a.B, i, sh);
 }
 
 template <int DT, bool VEC, bool CUT>
-__global__ __launch_bounds__(kThreads) void mass_kernel(VerifyArgs a) {
+__global__ __launch_bounds__(kThreads) void mass_kernel(VerifyArgs) {
+  const VerifyArgs& a = kernel_arg0<VerifyArgs>();
   __shared__ double lds_d[kWaves * (kTilesPerItem + 1)];
   const int b = blockIdx.x / a.nt, s = blockIdx.x - b * a.nt;
   mass_item<DT, VEC, CUT>(a, b, s, lds_d);
@@ -180,14 +184,16 @@ __global__ __launch_bounds__(kThreads) void mass_kernel(VerifyArgs a) {
 
 // EPS: the call may use the Saguaro eps mode (its weights need more registers).
 template <int DT, bool VEC, bool CUT, bool EPS>
-__global__ __launch_bounds__(kThreads) void sample_kernel(VerifyArgs a) {
+__global__ __launch_bounds__(kThreads) void sample_kernel(VerifyArgs) {
+  const VerifyArgs& a = kernel_arg0<VerifyArgs>();
   __shared__ double lds_d[kWaves * (kTilesPerItem + 1)];
   const int b = blockIdx.x / a.nt, s = blockIdx.x - b * a.nt;
   sample_item<DT, VEC, CUT, EPS>(a, b, s, lds_d);
 }
 
 template <int DT, bool VEC, bool CUT>
-__global__ __launch_bounds__(kThreads) void draw_kernel(VerifyArgs a) {
+__global__ __launch_bounds__(kThreads) void draw_kernel(VerifyArgs) {
+  const VerifyArgs& a = kernel_arg0<VerifyArgs>();
   __shared__ DrawLds sh;
   draw_item<DT, VEC, CUT>(a, blockIdx.x, sh);
 }
@@ -200,7 +206,8 @@ __global__ __launch_bounds__(kThreads) void zero_kernel(uint4* p, size_t n) {
 }
 
 template <int DT>
-__global__ __launch_bounds__(kThreads) void final_kernel(VerifyArgs a) {
+__global__ __launch_bounds__(kThreads) void final_kernel(VerifyArgs) {
+  const VerifyArgs& a = kernel_arg0<VerifyArgs>();
   __shared__ FinalLds sh;
   final_item<DT>(a, blockIdx.x, sh);
 }
@@ -208,7 +215,8 @@ __global__ __launch_bounds__(kThreads) void final_kernel(VerifyArgs a) {
 // The refined residual draws, after every other kernel of the call (and
 // before the outcome prediction, which reads the drawn tokens).
 template <int DT, bool CUT>
-__global__ __launch_bounds__(kThreads) void refine_kernel(VerifyArgs a) {
+__global__ __launch_bounds__(kThreads) void refine_kernel(VerifyArgs) {
+  const VerifyArgs& a = kernel_arg0<VerifyArgs>();
   __shared__ DrawLds sh;
   refine_item<DT, CUT>(a, blockIdx.x, sh);
 }

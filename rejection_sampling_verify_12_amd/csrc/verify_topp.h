@@ -33,7 +33,8 @@ __device__ __forceinline__ float key_logit(uint32_t k) {
 
 // One wave per row: the row's offset and normaliser from its pieces (left in
 // place for the decision), and the selection's start.
-__global__ __launch_bounds__(64) void topp_init_kernel(VerifyArgs a) {
+__global__ __launch_bounds__(64) void topp_init_kernel(VerifyArgs) {
+  const VerifyArgs& a = kernel_arg0<VerifyArgs>();
   const int64_t row = blockIdx.x;
   const int lane = threadIdx.x;
   const uint64_t* p = SV_AT(a, part, row * a.nc);
@@ -66,7 +67,8 @@ __global__ __launch_bounds__(64) void topp_init_kernel(VerifyArgs a) {
 // has its own LDS histogram (fewer colliding atomics); a lane sums runs of
 // one digit before adding.  Loads: four units in flight per lane.
 template <int DT, bool VEC>
-__global__ __launch_bounds__(kThreads) void topp_hist_kernel(VerifyArgs a, int pass) {
+__global__ __launch_bounds__(kThreads) void topp_hist_kernel(VerifyArgs, int pass) {
+  const VerifyArgs& a = kernel_arg0<VerifyArgs>();
   __shared__ double h[kWaves][kDigits];
   const int R = 2 * a.gamma + 1;
   const int64_t id = blockIdx.x;
@@ -136,7 +138,8 @@ __global__ __launch_bounds__(kThreads) void topp_hist_kernel(VerifyArgs a, int p
 // lowest digit with mass is selected).  After the last pass, the threshold
 // logit and the nucleus mass.
 template <int DT>
-__global__ __launch_bounds__(64) void topp_select_kernel(VerifyArgs a, int pass, int npass) {
+__global__ __launch_bounds__(64) void topp_select_kernel(VerifyArgs, int pass, int npass) {
+  const VerifyArgs& a = kernel_arg0<VerifyArgs>();
   const int64_t row = blockIdx.x;
   const int lane = threadIdx.x;
   TopPRow t = *SV_AT(a, topp, row);
@@ -699,7 +702,8 @@ __device__ void finish_list(const VerifyArgs& a, int64_t row, const CountLds& sh
 // wrapped, or whose words do not fit the list, is left to topp_redo_kernel
 // (keeping the in-place finish out of this kernel keeps its registers).
 template <bool VEC>
-__global__ __launch_bounds__(kCountThreads) void topp_count_kernel(VerifyArgs a, int64_t nrows) {
+__global__ __launch_bounds__(kCountThreads) void topp_count_kernel(VerifyArgs, int64_t nrows) {
+  const VerifyArgs& a = kernel_arg0<VerifyArgs>();
   __shared__ CountLds sh;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int R = 2 * a.gamma + 1;
@@ -793,7 +797,8 @@ __global__ __launch_bounds__(kCountThreads) void topp_count_kernel(VerifyArgs a,
 // work-group to finish clears the two counters.  Launched after the
 // counting kernel on the same stream, so the list is complete.
 template <bool VEC>
-__global__ __launch_bounds__(kCountThreads) void topp_redo_kernel(VerifyArgs a) {
+__global__ __launch_bounds__(kCountThreads) void topp_redo_kernel(VerifyArgs) {
+  const VerifyArgs& a = kernel_arg0<VerifyArgs>();
   __shared__ CountLds sh;
   const int t = threadIdx.x;
   const unsigned n = __hip_atomic_load(SV_AT(a, redo, 0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
