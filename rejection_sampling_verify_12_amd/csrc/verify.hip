@@ -210,28 +210,22 @@ static hipError_t launch_all(const VerifyArgs& a, const PredictArgs* pa, hipStre
         const Sched sc = make_sched_early(b.B, b.gamma, b.nc, eps_mode ? b.nt : 0, b.nt, slots);
         hipLaunchKernelGGL((fused_kernel<DT, VEC, SV_STREAM_UNROLL, false, true>), dim3((unsigned)sc.total),
                            dim3(kThreads), 0, st, FusedArgs{b, sc});
-        return launch_refine<DT, false>(b, st);
+        return hipGetLastError();   // the single kernel's final items refine in place
       }
       hipError_t e = pa ? resident_groups<DT, VEC, true, false>(slots) : resident_groups<DT, VEC, false, false>(slots);
       if (e != hipSuccess) return e;
-      if (!pa && short_sampling(a, slots)) {
-        e = launch_short<DT, VEC>(a, st);
-        if (e != hipSuccess) return e;
-        VerifyArgs b = a;
-        b.nt = (a.ntile + kShortTiles - 1) / kShortTiles;
-        return launch_refine<DT, false>(b, st);
-      }
+      if (!pa && short_sampling(a, slots)) return launch_short<DT, VEC>(a, st);
       const Sched sc = make_sched(a.B, 2 * a.gamma * a.nc, (pa ? 2 : 1) * a.nc, eps_mode ? a.nt : 0, a.nt, slots);
       if (pa) {
         hipLaunchKernelGGL((fused_kernel<DT, VEC, SV_STREAM_UNROLL, true, false>), dim3((unsigned)sc.total),
                            dim3(kThreads), 0, st, FusedArgs{a, sc});
-        e = launch_refine<DT, false>(a, st);
+        e = hipGetLastError();
         if (e != hipSuccess) return e;
         return predict_launch_leaders(*pa, SPEC_BF16, st);
       }
       hipLaunchKernelGGL((fused_kernel<DT, VEC, SV_STREAM_UNROLL, false, false>), dim3((unsigned)sc.total),
                          dim3(kThreads), 0, st, FusedArgs{a, sc});
-      return launch_refine<DT, false>(a, st);
+      return hipGetLastError();
     }
   }
   if constexpr (SV_FUSED && !(DT == kBF16 && VEC)) {

@@ -131,7 +131,7 @@ void fused_kernel(FusedArgs) {
       if (!PRED || sub < a.nc) stream_item<DT, VEC, U>(a, b, 2 * a.gamma, sub, sh.s);
       else leader_item<DT, VEC, U>(a, b, sub - a.nc, sh.s);
       break;
-    default: final_item<DT, !(DT == kBF16 && VEC)>(a, b, sh.f); break;
+    default: final_item<DT, true>(a, b, sh.f); break;
   }
 #if SV_TIMELINE
   if (threadIdx.x == 0 && blockIdx.x < kTimelineBlocks) {

@@ -552,12 +552,14 @@ __device__ __forceinline__ void recompute_tiles(const VerifyArgs& a, int b, int 
 // configured workloads); normalised by the residual mass S that error grows
 // by 1/S.  Down to S = kRefineMass of q_k's mass it stays below 7e-7, inside
 // the 1e-6 window a draw's uniform must clear to be decided; a smaller
-// residual (zero included) is refined: the final item leaves the sequence's
-// token at k to refine_kernel, which runs after the call's other kernels and
-// takes the draw again in fp64 from the logits - both rows' normalisers,
-// every tile's residual sum and the chosen tile's running sums.  That code
-// lives in its own kernel: inside the single kernel its registers would
-// slow every stream item.
+// residual (zero included) is refined: the draw is taken again in fp64 from
+// the logits - both rows' normalisers, every tile's residual sum and the
+// chosen tile's running sums - by the sequence's final item in the single
+// kernel, or after the call's other kernels by refine_kernel where the
+// kernels are separate.  In the bf16 single kernel that path needs more than
+// its 64 registers and spills 92 bytes a lane to scratch, on that path only
+// (no spill in the stream, sampling or draw code); a second launch would cost
+// every call ~2-4 us.
 constexpr double kRefineMass = 0.0625;           // refined below this fraction of q_k's mass
 constexpr uint32_t kRefineToken = 0xFFFFFFFEu;   // drawn slot: the draw is refined (never a token id)
 constexpr int kPendingWord = 8;                  // flag line: 1 = a refinement is pending
@@ -956,7 +958,8 @@ template <int DT, bool CUT>
 __device__ __forceinline__ void refine_item(const VerifyArgs& a, int b, DrawLds& sh);
 
 // INLINE: a refined draw is taken here, by this work-group, instead of by
-// refine_kernel (kernels with registers to spare for it).
+// refine_kernel (the single kernel: its refined draws spill a few registers
+// to scratch, on that path only, and save the call a second launch).
 template <int DT, bool INLINE = false>
 __device__ __forceinline__ void final_item(const VerifyArgs& a, int b, FinalLds& sh) {
   const int tid = threadIdx.x;
