@@ -47,22 +47,22 @@ __device__ __forceinline__ void early_skip(const VerifyArgs& a, int b, int r, in
 }
 
 // Packed bf16 rows: compiled for 8 waves per SIMD (64 VGPRs), which the
-// stream items need and every other path fits without spilling.  float32
-// and unaligned rows hold twice the registers per logit in flight, and their
-// sampling paths need more: 4 waves per SIMD (128 VGPRs).
+// stream items need; only the refined draw spills (a few registers, on its
+// own path).  float32 and unaligned rows hold twice the registers per logit
+// in flight, and their sampling paths need more: 4 waves per SIMD (128 VGPRs).
 template <int DT, bool VEC>
 constexpr int kFusedWaves = DT == kBF16 && VEC ? 8 : 4;
 
-// PRED: outcome prediction too (draft-row items record lane leaders; the
-// items of target row gamma are followed by leader items of draft row gamma).
-// EARLY: the early-exit order (position-major stream items, position tests).
-// N: tiles per sampling item.
 // The single kernel's one argument: the call and its launch order.
 struct FusedArgs {
   VerifyArgs a;
   Sched sc;
 };
 
+// PRED: outcome prediction too (draft-row items record lane leaders; the
+// items of target row gamma are followed by leader items of draft row gamma).
+// EARLY: the early-exit order (position-major stream items, position tests).
+// N: tiles per sampling item.
 template <int DT, bool VEC, int U, bool PRED, bool EARLY, int N = kTilesPerItem>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kFusedWaves<DT, VEC>, 8)))
 void fused_kernel(FusedArgs) {
