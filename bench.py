@@ -591,7 +591,10 @@ def main():
                      "p50": float(np.percentile(per_call_ms, 50)),
                      "p90": float(np.percentile(per_call_ms, 90)),
                      "region_per_step": region_ms / args.steps},
-        "clocks": {"end_of_warmup": clk0, "during_timed_calls": clk1 if busy_at_clk1 else None},
+        # Identical readings at both points mean the SMI tables did not refresh
+        # between them: then neither is the clock the timed calls ran at.
+        "clocks": {"end_of_warmup": clk0, "during_timed_calls": clk1 if busy_at_clk1 else None,
+                   "refreshed_between_reads": clk0 != clk1},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic_record(
                          args.workload, args.mode + ("_predict" if args.predict and not sep else "")
