@@ -249,13 +249,27 @@ constexpr uint32_t kKeyNegInf = 0x007Fu, kKeyNegZero = 0x7FFFu, kKeyPosZero = 0x
 // The counted row's words with a count, compacted in ascending order (word,
 // low count | high count << 16) for the wave that finishes the row while the
 // next one is counted; a row with more is left to topp_redo_kernel.
-constexpr int kListCap = 3328;
+constexpr int kListCap = 1792;
+// The band: the 64 keys from a row's origin key up (set just below the
+// median of a sample of the row, where its logits crowd) are counted in
+// per-lane copies, so the lanes of one add reach 64 different words and
+// banks.  Word 64 i + l holds key origin + i for lane l of every counting
+// wave, in the half its counter takes; a copy takes at most
+// (V / 960 + 9) * 15 < 65536 counts for rows up to kBandMaxV.  After the row
+// the copies are summed into the counters.
+#ifndef SV_COUNT_PIPE
+#define SV_COUNT_PIPE 2
+#endif
+constexpr int kBandKeys = 64;
+constexpr int kBandWords = kBandKeys * 64;
+constexpr int64_t kBandMaxV = (int64_t)1 << 21;
+constexpr uint32_t kBandOff = 0x10000u;   // an origin no key reaches: no band
 constexpr unsigned kRedoWrapped = 0x80000000u;   // a redo entry's flag: the row's counters wrapped
 constexpr int kCountingWaves = kCountWaves - 1;
 constexpr int kCountingThreads = 64 * kCountingWaves;
 
 struct CountLds {
-  uint32_t cnt[kCountWords];
+  uint32_t cnt[kCountWords + kBandWords];   // the counters, then the band's copies
   uint2 list[kListCap];
   uint32_t ev[kCountEvents];   // keys whose counter wrapped (checked pass)
   uint32_t nev;
@@ -264,6 +278,7 @@ struct CountLds {
   double tot[2][kCountWaves];
   int sel;
   double P;
+  uint32_t org[2];   // band origins: row n of the work-group counts with org[n & 1]
 };
 
 // The keys of the two bfloat16 logits in w (its halves), in the halves of
@@ -304,11 +319,32 @@ __device__ __forceinline__ void count_pair(CountLds& sh, uint32_t w) {
   count_key<CHECK>(sh, kp >> 16);
 }
 
+// The counting kernel's layout counts raw bfloat16 bits x (no key
+// transform on the hot path): word x & 0x7FFF, the low half for a
+// non-negative value, the high half for a negative one.  Raw word w then
+// holds key w + 32768 (low) and key 32767 - w (high), and the compaction
+// turns the counters back into key words.  One add for x: into this lane's
+// band copy when x - org < kBandKeys (org a raw origin), else into its
+// counter.  blane = 4 (kCountWords + lane): byte offsets.
+__device__ __forceinline__ void count_raw(CountLds& sh, uint32_t x, uint32_t org, uint32_t blane) {
+  const uint32_t d = x - org;
+  const bool in = d < (uint32_t)kBandKeys;
+  const uint32_t o = in ? (d << 8) + blane : ((x << 2) & 0x1FFFCu);
+  uint32_t* w = static_cast<uint32_t*>(__builtin_assume_aligned(reinterpret_cast<char*>(sh.cnt) + o, 4));
+  __hip_atomic_fetch_add(w, ((x >> 15) & 1u) * 0xFFFFu + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ void count_pair_raw(CountLds& sh, uint32_t w, uint32_t org, uint32_t blane) {
+  count_raw(sh, w & 0xFFFFu, org, blane);
+  count_raw(sh, w >> 16, org, blane);
+}
+
 // Every logit of the row, once, by threads 0 .. NT - 1.  Lane t takes
 // 8-logit units t, t + NT, ... (eight in flight; one in the rarely run
 // checked pass, whose code stays small), then one of the last V mod 8.
-template <bool VEC, bool CHECK, int NT>
-__device__ void count_row(const uint16_t* row, int64_t V, CountLds& sh) {
+// RAW: the raw-bit layout of the counting kernel, whose values from the raw
+// origin org up go to the band's copies.
+template <bool VEC, bool CHECK, int NT, bool RAW = false>
+__device__ void count_row(const uint16_t* row, int64_t V, CountLds& sh, uint32_t org = kBandOff) {
   const int t = threadIdx.x;
   const int64_t units = V >> 3;
   int64_t u = t;
@@ -318,34 +354,126 @@ __device__ void count_row(const uint16_t* row, int64_t V, CountLds& sh) {
     const __amdgpu_buffer_rsrc_t rs = chunk_rsrc(row, (int)(units * 16));
     const int voff = t * 16;
     const int64_t nb = units / kBatch;
-    for (int64_t i = 0; i < nb; ++i) {
-      u32x4 w[U];
-#pragma unroll
-      for (int q = 0; q < U; ++q)
-        w[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, (int)((i * kBatch + q * NT) * 16), 2);
-#pragma unroll
-      for (int q = 0; q < U; ++q) {
-        count_pair<CHECK>(sh, w[q].x);
-        count_pair<CHECK>(sh, w[q].y);
-        count_pair<CHECK>(sh, w[q].z);
-        count_pair<CHECK>(sh, w[q].w);
+    const uint32_t blane = 4u * ((uint32_t)kCountWords + (uint32_t)(t & 63));
+    auto count4 = [&](const u32x4& w) {
+      if constexpr (RAW) {
+        count_pair_raw(sh, w.x, org, blane);
+        count_pair_raw(sh, w.y, org, blane);
+        count_pair_raw(sh, w.z, org, blane);
+        count_pair_raw(sh, w.w, org, blane);
+      } else {
+        count_pair<CHECK>(sh, w.x);
+        count_pair<CHECK>(sh, w.y);
+        count_pair<CHECK>(sh, w.z);
+        count_pair<CHECK>(sh, w.w);
       }
+    };
+    if constexpr (RAW) {
+      // Batches of P loads, the next one in flight while this one is
+      // counted (the last batch is loaded twice rather than branch).
+      constexpr int P = SV_COUNT_PIPE;
+      constexpr int64_t kB = (int64_t)P * NT;
+      const int64_t np = units / kB;
+      // Two register sets taken in turn, so no copy ties a batch's wait to
+      // the previous batch's counting.
+      auto load = [&](u32x4* w, int64_t i) {
+        i = i < np ? i : np - 1;
+#pragma unroll
+        for (int q = 0; q < P; ++q)
+          w[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, (int)((i * kB + q * NT) * 16), 2);
+      };
+      if (np > 0) {
+        u32x4 wa[P], wb[P];
+        load(wa, 0);
+        // The scheduling barriers keep the compiler from interleaving one
+        // set's counting with the other's, which would wait for loads just
+        // issued.
+        for (int64_t i = 0; i + 1 < np; i += 2) {
+          load(wb, i + 1);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int q = 0; q < P; ++q) count4(wa[q]);
+          __builtin_amdgcn_sched_barrier(0);
+          load(wa, i + 2);   // batch np - 1 again after the last pair of an even count
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int q = 0; q < P; ++q) count4(wb[q]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (np & 1) {
+#pragma unroll
+          for (int q = 0; q < P; ++q) count4(wa[q]);
+        }
+      }
+      u = np * kB + t;
+    } else {
+      for (int64_t i = 0; i < nb; ++i) {
+        u32x4 w[U];
+#pragma unroll
+        for (int q = 0; q < U; ++q)
+          w[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, (int)((i * kBatch + q * NT) * 16), 2);
+#pragma unroll
+        for (int q = 0; q < U; ++q) count4(w[q]);
+      }
+      u = nb * kBatch + t;
     }
-    for (u = nb * kBatch + t; u < units; u += NT) {
-      const u32x4 w = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, (int)((u - t) * 16), 2);
-      count_pair<CHECK>(sh, w.x);
-      count_pair<CHECK>(sh, w.y);
-      count_pair<CHECK>(sh, w.z);
-      count_pair<CHECK>(sh, w.w);
-    }
+    for (; u < units; u += NT)
+      count4(__builtin_amdgcn_raw_buffer_load_b128(rs, voff, (int)((u - t) * 16), 2));
   } else {
+    const uint32_t blane = 4u * ((uint32_t)kCountWords + (uint32_t)(t & 63));
     for (; u < units; u += NT) {
 #pragma unroll
-      for (int e = 0; e < 8; e += 2)
-        count_pair<CHECK>(sh, (uint32_t)row[u * 8 + e] | ((uint32_t)row[u * 8 + e + 1] << 16));
+      for (int e = 0; e < 8; e += 2) {
+        const uint32_t w = (uint32_t)row[u * 8 + e] | ((uint32_t)row[u * 8 + e + 1] << 16);
+        if constexpr (RAW) count_pair_raw(sh, w, org, blane);
+        else count_pair<CHECK>(sh, w);
+      }
     }
   }
-  if (t < V - units * 8) count_key<CHECK>(sh, bf16_key_pair(row[units * 8 + t]) & 0xFFFFu);
+  if (t < V - units * 8) {
+    const uint32_t x = row[units * 8 + t];
+    if constexpr (RAW) count_raw(sh, x, kBandOff, 0u);
+    else count_key<CHECK>(sh, bf16_key_pair(x) & 0xFFFFu);
+  }
+}
+
+// The band's origin for a row of V logits (one wave): a 16-byte load at each
+// of 64 evenly spaced places (band_sample), then the 64 values from 32 below
+// the lower median of those 512 up, found by a binary search over the key
+// range and moved, if they straddle zero, to the median's side (band_origin,
+// the same value in every lane).  It returns the band's lowest raw bits:
+// keys k .. k + 63 below 32768 (negative values) are raw bits
+// 65472 - k .. 65535 - k, keys from 32768 up raw bits k - 32768 on.  Any
+// origin counts the row exactly; a good one puts most of its logits in the
+// band.  kBandOff for rows shorter than 64 loads or longer than kBandMaxV.
+__device__ __forceinline__ bool band_rows(int64_t V) { return V >= 512 && V <= kBandMaxV; }
+__device__ __forceinline__ u32x4 band_sample(const uint16_t* row, int64_t V) {
+  const int64_t units = V >> 3;
+  const int lane = threadIdx.x & 63;
+  const __amdgpu_buffer_rsrc_t rs = chunk_rsrc(row, (int)(units * 16));
+  return __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(units * lane / 64) * 16, 0, 2);
+}
+__device__ __forceinline__ uint32_t band_origin(const u32x4& w) {
+  uint32_t k[8];
+  const uint32_t x[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t kp = bf16_key_pair(x[i]);
+    k[2 * i] = kp & 0xFFFFu;
+    k[2 * i + 1] = kp >> 16;
+  }
+  uint32_t lo = 0u, hi = 0xFFFFu;   // the smallest m with at least 256 keys <= m
+  while (lo < hi) {
+    const uint32_t mid = (lo + hi) >> 1;
+    int c = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) c += __popcll(__ballot(k[e] <= mid));
+    if (c >= 256) hi = mid;
+    else lo = mid + 1u;
+  }
+  uint32_t ko = min(lo - min(lo, 32u), 0x10000u - (uint32_t)kBandKeys);
+  if (ko < 0x8000u && ko + kBandKeys > 0x8000u) ko = lo < 0x8000u ? 0x8000u - kBandKeys : 0x8000u;
+  return ko < 0x8000u ? 0xFFC0u - ko : ko - 0x8000u;
 }
 
 __device__ __forceinline__ bool key_finite(uint32_t k) { return k > kKeyNegInf && k < kKeyPosInf; }
@@ -612,10 +740,12 @@ __device__ void finish_inplace(const VerifyArgs& a, int64_t row, CountLds& sh, b
   count_outputs(a, row, flags, kmax, mref, Z, sh.sel, sh.P, t, kCountThreads);
 }
 
-// The previous row's finish from its compacted words (one wave, while the
-// other waves count the next row).  Lane l takes a run of consecutive
-// entries; from the top key down the order is the high halves of entries
-// E-1..0, then the low halves of entries E-1..0.  -0 has been counted with
+// The previous row's finish from its compacted raw words (one wave, while
+// the other waves count the next row).  Lane l takes a run of consecutive
+// entries.  Entry x holds raw value x (non-negative, key x + 32768) in its
+// low half and raw value 0x8000 + x (negative, key 32767 - x) in its high
+// half, so from the top key down the order is the low halves of entries
+// E-1..0, then the high halves of entries 0..E-1.  -0 has been counted with
 // +0 already and no counter wrapped.
 __device__ void finish_list(const VerifyArgs& a, int64_t row, const CountLds& sh, int E) {
   const int lane = threadIdx.x & 63;
@@ -624,12 +754,13 @@ __device__ void finish_list(const VerifyArgs& a, int64_t row, const CountLds& sh
   const TCoef tc = temp_coef(a, b);
   const int per = (E + 63) >> 6;
   const int e0 = min(lane * per, E), e1 = min(e0 + per, E);
+  auto key = [](uint32_t x, int h) -> uint32_t { return h ? 0x7FFFu - x : x + 0x8000u; };
   int kmax = -1, flags = 0;
   for (int e = e0; e < e1; ++e) {
     const uint2 en = sh.list[e];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const uint32_t k = en.x + 32768u * h, n = (en.y >> (16 * h)) & 0xFFFFu;
+      const uint32_t k = key(en.x, h), n = (en.y >> (16 * h)) & 0xFFFFu;
       if (n == 0u) continue;
       if (key_finite(k)) kmax = max(kmax, (int)k);
       else flags |= nonfinite_flag(k);
@@ -648,33 +779,38 @@ __device__ void finish_list(const VerifyArgs& a, int64_t row, const CountLds& sh
     const float m = (float)n * exp2_fast(fmaf(v, tc.c_lo, fmaf(v, tc.c_hi, -mref)));
     return (n != 0u && key_finite(k)) ? m : 0.f;
   };
-  double sm[2] = {0.0, 0.0};
+  double sm[2] = {0.0, 0.0};   // this lane's masses: non-negative values, negative values
   if (!bad) {
     for (int e = e0; e < e1; ++e) {
       const uint2 en = sh.list[e];
-      sm[0] += (double)mass(en.x, en.y & 0xFFFFu);
-      sm[1] += (double)mass(en.x + 32768u, en.y >> 16);
+      sm[0] += (double)mass(key(en.x, 0), en.y & 0xFFFFu);
+      sm[1] += (double)mass(key(en.x, 1), en.y >> 16);
     }
   }
-  // Suffix sums over the lanes, the high halves first; a lane's `above` is
-  // the next lane's `incl`, the same value, so the intervals tile (0, Z].
-  const double s1 = wave_suffix_sum(sm[1], lane), s0 = wave_suffix_sum(sm[0], lane);
-  const double H = __shfl(s1, 0, 64);
-  const double d1 = __shfl_down(s1, 1, 64), d0 = __shfl_down(s0, 1, 64);
-  const double incl1 = s1, above1 = lane == 63 ? 0.0 : d1;
-  const double incl0 = s0 + H, above0 = (lane == 63 ? 0.0 : d0) + H;
-  const double Z = __shfl(incl0, 0, 64);
+  // Running masses from the top: a suffix sum over the lanes for the
+  // non-negative values (lane 63 holds the largest), then, below their total
+  // H, a prefix sum for the negative ones (lane 0 holds the largest).  A
+  // lane's `above` is the running mass before its entries, the value the
+  // lane before it in that order ends on, so the intervals tile (0, Z].
+  const double s0 = wave_suffix_sum(sm[0], lane);
+  const double p1 = wave_inclusive_scan(sm[1]);
+  const double H = __shfl(s0, 0, 64);
+  const double d0 = __shfl_down(s0, 1, 64);
+  const double incl0 = s0, above0 = lane == 63 ? 0.0 : d0;
+  const double incl1 = p1 + H, above1 = (p1 - sm[1]) + H;
+  const double Z = __shfl(incl1, 63, 64);
   const double tgt = (double)a.top_p * Z;
-  const bool c1 = !bad && above1 < tgt && tgt <= incl1, c0 = !bad && above0 < tgt && tgt <= incl0;
+  const bool c0 = !bad && above0 < tgt && tgt <= incl0, c1 = !bad && above1 < tgt && tgt <= incl1;
   int sel = -1;
   double P = 1.0;
-  if (c1 || c0) {   // this lane's entries hold the threshold: walk them from the top
-    const int h = c1 ? 1 : 0;
-    double run = c1 ? above1 : above0, Pl = run;
+  if (c0 || c1) {   // this lane's entries hold the threshold: walk them from the top
+    const int h = c0 ? 0 : 1;
+    double run = c0 ? above0 : above1, Pl = run;
     int low = -1;
-    for (int e = e1 - 1; e >= e0; --e) {
+    for (int i = 0; i < e1 - e0; ++i) {
+      const int e = h ? e0 + i : e1 - 1 - i;
       const uint2 en = sh.list[e];
-      const uint32_t k = en.x + 32768u * h;
+      const uint32_t k = key(en.x, h);
       const float m = mass(k, (en.y >> (16 * h)) & 0xFFFFu);
       if (m == 0.f) continue;
       run += (double)m;
@@ -708,38 +844,65 @@ __global__ __launch_bounds__(kCountThreads) void topp_count_kernel(VerifyArgs, i
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int R = 2 * a.gamma + 1;
   uint4* c4 = reinterpret_cast<uint4*>(sh.cnt);
-  for (int i = t; i < kCountWords / 4; i += kCountThreads) c4[i] = make_uint4(0u, 0u, 0u, 0u);
+  for (int i = t; i < (kCountWords + kBandWords) / 4; i += kCountThreads) c4[i] = make_uint4(0u, 0u, 0u, 0u);
+  const bool banded = VEC && band_rows(a.V);
+  auto rowp = [&](int64_t row) {
+    const int b = (int)(row / R), r = (int)(row - (int64_t)b * R);
+    return static_cast<const uint16_t*>(row_ptr<kBF16>(a, b, r));
+  };
+  if (wave == kCountingWaves) {
+    const uint32_t o = banded && (int64_t)blockIdx.x < nrows ? band_origin(band_sample(rowp(blockIdx.x), a.V))
+                                                             : kBandOff;
+    if (lane == 0) sh.org[0] = o;
+  }
   __syncthreads();
   int64_t prev = -1;
   int E = 0;
-  for (int64_t row = blockIdx.x;; row += gridDim.x) {
+  for (int64_t row = blockIdx.x, n = 0;; row += gridDim.x, ++n) {
     const bool have = row < nrows;
+    const uint32_t org = sh.org[n & 1];
     if (wave < kCountingWaves) {
-      if (have) {
-        const int b = (int)(row / R), r = (int)(row - (int64_t)b * R);
-        count_row<VEC, false, kCountingThreads>(static_cast<const uint16_t*>(row_ptr<kBF16>(a, b, r)), a.V, sh);
-      }
-    } else if (prev >= 0) {
-      finish_list(a, prev, sh, E);
+      if (have) count_row<VEC, false, kCountingThreads, true>(rowp(row), a.V, sh, org);
+    } else {
+      // The next row's sample flies while the previous row is finished.
+      const int64_t next = row + gridDim.x;
+      const bool s = banded && next < nrows;
+      const u32x4 w = s ? band_sample(rowp(next), a.V) : u32x4{0u, 0u, 0u, 0u};
+      if (prev >= 0) finish_list(a, prev, sh, E);
+      const uint32_t o = s ? band_origin(w) : kBandOff;
+      if (lane == 0) sh.org[(n + 1) & 1] = o;
     }
     __syncthreads();
     if (!have) break;
 
-    // Compaction.  -0 (the low half of word 32767) moves to +0 (the high
-    // half of word 0); the sum of the counters checks for a wrap.  Words
-    // are read from LDS as needed (registers stay free for the counting);
-    // word of row j: wbase + 64 j.
+    // The band's copies into the counters: thread t sums copies
+    // 4 (t & 15) .. 4 (t & 15) + 3 of raw value org + (t >> 4), clears them,
+    // and the value's 16 threads add up; a count that overflows its 16-bit
+    // counter leaves the counters' sum short of V, as any wrap does.
+    if (org != kBandOff) {
+      const uint32_t k = org + (uint32_t)(t >> 4), sh16 = 16u * (k >> 15);
+      uint4* bw = reinterpret_cast<uint4*>(sh.cnt + kCountWords) + t;
+      const uint4 w = *bw;
+      *bw = make_uint4(0u, 0u, 0u, 0u);
+      int c = (int)((w.x >> sh16) + (w.y >> sh16) + (w.z >> sh16) + (w.w >> sh16));
+      c = row16_reduce(c, [](int x, int y) { return x + y; });
+      if ((t & 15) == 0) sh.cnt[k & 0x7FFFu] += (uint32_t)c << sh16;
+      __syncthreads();
+    }
+
+    // Compaction of the raw words.  -0 (raw 0x8000, the high half of word
+    // 0) moves to +0 (raw 0, its low half); the sum of the counters checks
+    // for a wrap.  Words are read from LDS as needed (registers stay free
+    // for the counting); word of row j: wbase + 64 j.
     uint32_t wbase = 2048u * (uint32_t)wave + (uint32_t)lane;
     asm volatile("" : "+v"(wbase));
-    const uint32_t nzero = sh.cnt[kKeyNegZero] & 0xFFFFu;
     auto word = [&](int j) -> uint32_t {
       uint32_t w = sh.cnt[wbase + 64u * j];
-      if (t == kCountThreads - 1 && j == 31) w &= 0xFFFF0000u;
-      if (t == 0 && j == 0) w += nzero << 16;   // checked against overflow below
+      if (t == 0 && j == 0) w = (w & 0xFFFFu) + (w >> 16);   // checked against overflow below
       return w;
     };
     uint32_t sum = 0, nzc = 0;
-    int over = t == 0 && (sh.cnt[0] >> 16) + nzero > 0xFFFFu;
+    int over = t == 0 && (sh.cnt[0] & 0xFFFFu) + (sh.cnt[0] >> 16) > 0xFFFFu;
 #pragma unroll 8
     for (int j = 0; j < 32; ++j) {
       const uint32_t w = sh.cnt[wbase + 64u * j];
@@ -763,8 +926,8 @@ __global__ __launch_bounds__(kCountThreads) void topp_count_kernel(VerifyArgs, i
       over |= sh.flags[i];
     }
     if ((int64_t)tsum == a.V && tot <= (uint32_t)kListCap && !over) {
-      // Each thread reads only its own words here (-0's counter was read
-      // before the barrier above), so it clears each once read.
+      // Each thread reads only its own words here, so it clears each once
+      // read.
       const uint64_t lt = (1ull << lane) - 1ull;
 #pragma unroll 8
       for (int j = 0; j < 32; ++j) {

@@ -305,6 +305,26 @@ def test_top_p_longest_rows(V):
     rep.check()
 
 
+@pytest.mark.parametrize("V", [1 << 21, (1 << 21) + 8])
+def test_top_p_band_limits(V):
+    """bfloat16 rows at the longest the counting path takes with its band of
+    per-lane copies (2^21 logits) and just past it (no band).  In the draft
+    rows one value fills every other logit, so it is the rows' median and
+    falls in the band, whose copies then sum past a 16-bit counter; in the
+    target rows one value fills every 16th logit, away from the median."""
+    batch = random_batch(1, 1, V, "bf16", 1.0, seed=6900 + V % 7, scale=2.0, sigma=0.4)
+    d, t = batch.draft.copy(), batch.target.copy()
+    d[..., ::2] = np.uint16(0xBF80)    # -1.0, 2^20 times a row
+    t[..., ::16] = np.uint16(0xC040)   # -3.0, 2^17 times a row
+    batch = W.Batch(**{**batch.__dict__, "draft": d, "target": t, "name": f"band_V{V}"})
+    for top_p in (0.3, 0.9):
+        gpu = run_ex(batch, 1.0, top_p=top_p)
+        ref = oracle_per_seq(batch, np.full(batch.B, 1.0), top_p=top_p)
+        rep = H.compare(batch, gpu, ref)
+        H.say(f"[options]   {rep}")
+        rep.check()
+
+
 @pytest.mark.parametrize("V", [2, 8, 33])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("mode,eps", [("residual", 0.0), ("saguaro", 1e-8)])
