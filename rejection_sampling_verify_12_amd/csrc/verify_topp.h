@@ -370,17 +370,18 @@ __device__ void count_row(const uint16_t* row, int64_t V, CountLds& sh, uint32_t
     };
     if constexpr (RAW) {
       // Batches of P loads, the next one in flight while this one is
-      // counted (the last batch is loaded twice rather than branch).
+      // counted.  Past the last batch the loads take an offset outside the
+      // buffer's range, which the hardware answers with zeros and no memory
+      // access (rather than a branch around them).
       constexpr int P = SV_COUNT_PIPE;
       constexpr int64_t kB = (int64_t)P * NT;
       const int64_t np = units / kB;
       // Two register sets taken in turn, so no copy ties a batch's wait to
       // the previous batch's counting.
       auto load = [&](u32x4* w, int64_t i) {
-        i = i < np ? i : np - 1;
 #pragma unroll
         for (int q = 0; q < P; ++q)
-          w[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, (int)((i * kB + q * NT) * 16), 2);
+          w[q] = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, i < np ? (int)((i * kB + q * NT) * 16) : (int)(units * 16), 2);
       };
       if (np > 0) {
         u32x4 wa[P], wb[P];
@@ -394,7 +395,7 @@ __device__ void count_row(const uint16_t* row, int64_t V, CountLds& sh, uint32_t
 #pragma unroll
           for (int q = 0; q < P; ++q) count4(wa[q]);
           __builtin_amdgcn_sched_barrier(0);
-          load(wa, i + 2);   // batch np - 1 again after the last pair of an even count
+          load(wa, i + 2);   // nothing read after the last pair of an even count
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int q = 0; q < P; ++q) count4(wb[q]);
