@@ -155,15 +155,6 @@ static hipError_t resident_groups(int& slots) {
 template <int DT, bool VEC>
 static hipError_t launch_kernels(const VerifyArgs& a, hipStream_t st);
 
-// After the call's other kernels: the refined residual draws (a.refine).
-template <int DT, bool CUT>
-static hipError_t launch_refine(const VerifyArgs& a, hipStream_t st) {
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || !a.refine) return e;
-  hipLaunchKernelGGL((refine_kernel<DT, CUT>), dim3((unsigned)a.B), dim3(kThreads), 0, st, a);
-  return hipGetLastError();
-}
-
 // Short calls - stream items at most 1.5 times the fused kernel's slots -
 // take sampling items of kShortTiles tiles: twice as many, each reading half
 // as much, so the last sequences' sampling ends sooner.  Longer calls keep
@@ -285,9 +276,8 @@ static hipError_t launch_kernels_cut(const VerifyArgs& a, hipStream_t st) {
   if (eps_mode) hipLaunchKernelGGL((mass_kernel<DT, VEC, CUT>), dim3(nsample), dim3(kThreads), 0, st, a);
   if (eps_mode) hipLaunchKernelGGL((sample_kernel<DT, VEC, CUT, true>), dim3(nsample), dim3(kThreads), 0, st, a);
   else hipLaunchKernelGGL((sample_kernel<DT, VEC, CUT, false>), dim3(nsample), dim3(kThreads), 0, st, a);
-  hipLaunchKernelGGL((draw_kernel<DT, VEC, CUT>), dim3((unsigned)a.B), dim3(kThreads), 0, st, a);
-  hipLaunchKernelGGL((final_kernel<DT>), dim3((unsigned)a.B), dim3(kThreads), 0, st, a);
-  return launch_refine<DT, CUT>(a, st);
+  hipLaunchKernelGGL((draw_final_kernel<DT, VEC, CUT>), dim3((unsigned)a.B), dim3(kThreads), 0, st, a);
+  return hipGetLastError();
 }
 
 template <int DT, bool VEC>

@@ -172,7 +172,7 @@ struct VerifyArgs {
   uint64_t* rsum;    // [B][nt] slots: residual sums of the sampling items (Saguaro)
   Top3* cpart;       // [B][gamma+1][nc] lane leaders of the draft rows (outcome prediction)
   uint64_t* ref;     // [B][ntile][4] slots: fp64 tile sums of a refined residual draw
-  int refine;        // 1: refine_kernel follows the call's kernels (small residual masses are refined)
+  int refine;        // 1: small residual masses are refined (by the final items)
   int B, gamma, V;
   int nc, chunk;     // stream chunks per row and their length
   int ntile, nt;     // sampling tiles per row; sampling items per sequence

@@ -191,11 +191,16 @@ __global__ __launch_bounds__(kThreads) void sample_kernel(VerifyArgs) {
   sample_item<DT, VEC, CUT, EPS>(a, b, s, lds_d);
 }
 
+// The draw and the final item of sequence blockIdx.x, which refines a
+// small-residual draw in place: one launch where three would follow the
+// sampling.
 template <int DT, bool VEC, bool CUT>
-__global__ __launch_bounds__(kThreads) void draw_kernel(VerifyArgs) {
+__global__ __launch_bounds__(kThreads) void draw_final_kernel(VerifyArgs) {
   const VerifyArgs& a = kernel_arg0<VerifyArgs>();
-  __shared__ DrawLds sh;
-  draw_item<DT, VEC, CUT>(a, blockIdx.x, sh);
+  __shared__ FinalLds sh;
+  draw_item<DT, VEC, CUT>(a, blockIdx.x, sh.r);
+  __syncthreads();
+  final_item<DT, true, CUT>(a, blockIdx.x, sh);
 }
 
 // Zero n 16-byte words (a kernel, not a memset, so a captured call records
@@ -203,22 +208,6 @@ __global__ __launch_bounds__(kThreads) void draw_kernel(VerifyArgs) {
 __global__ __launch_bounds__(kThreads) void zero_kernel(uint4* p, size_t n) {
   const uint4 z = make_uint4(0u, 0u, 0u, 0u);
   for (size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x; i < n; i += (size_t)gridDim.x * kThreads) p[i] = z;
-}
-
-template <int DT>
-__global__ __launch_bounds__(kThreads) void final_kernel(VerifyArgs) {
-  const VerifyArgs& a = kernel_arg0<VerifyArgs>();
-  __shared__ FinalLds sh;
-  final_item<DT>(a, blockIdx.x, sh);
-}
-
-// The refined residual draws, after every other kernel of the call (and
-// before the outcome prediction, which reads the drawn tokens).
-template <int DT, bool CUT>
-__global__ __launch_bounds__(kThreads) void refine_kernel(VerifyArgs) {
-  const VerifyArgs& a = kernel_arg0<VerifyArgs>();
-  __shared__ DrawLds sh;
-  refine_item<DT, CUT>(a, blockIdx.x, sh);
 }
 
 }  // namespace sv

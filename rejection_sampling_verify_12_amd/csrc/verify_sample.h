@@ -554,12 +554,12 @@ __device__ __forceinline__ void recompute_tiles(const VerifyArgs& a, int b, int 
 // the 1e-6 window a draw's uniform must clear to be decided; a smaller
 // residual (zero included) is refined: the draw is taken again in fp64 from
 // the logits - both rows' normalisers, every tile's residual sum and the
-// chosen tile's running sums - by the sequence's final item in the single
-// kernel, or after the call's other kernels by refine_kernel where the
-// kernels are separate.  In the bf16 single kernel that path needs more than
-// its 64 registers and spills 92 bytes a lane to scratch, on that path only
-// (no spill in the stream, sampling or draw code); a second launch would cost
-// every call ~2-4 us.
+// chosen tile's running sums - by the sequence's final item, in the single
+// kernel or in the draw-and-final kernel where the kernels are separate.  In
+// the bf16 single kernel that path needs more than its 64 registers and
+// spills 92 bytes a lane to scratch, on that path only (no spill in the
+// stream, sampling or draw code); a launch of its own would cost every call
+// ~2-5 us.
 constexpr double kRefineMass = 0.0625;           // refined below this fraction of q_k's mass
 constexpr uint32_t kRefineToken = 0xFFFFFFFEu;   // drawn slot: the draw is refined (never a token id)
 constexpr int kPendingWord = 8;                  // flag line: 1 = a refinement is pending
@@ -957,10 +957,10 @@ struct FinalLds {
 template <int DT, bool CUT>
 __device__ __forceinline__ void refine_item(const VerifyArgs& a, int b, DrawLds& sh);
 
-// INLINE: a refined draw is taken here, by this work-group, instead of by
-// refine_kernel (the single kernel: its refined draws spill a few registers
-// to scratch, on that path only, and save the call a second launch).
-template <int DT, bool INLINE = false>
+// INLINE: a refined draw is taken here, by this work-group, after the
+// outputs (in the single kernel its refined draws spill a few registers to
+// scratch, on that path only); CUT: the rows are cut to their nuclei.
+template <int DT, bool INLINE = false, bool CUT = false>
 __device__ __forceinline__ void final_item(const VerifyArgs& a, int b, FinalLds& sh) {
   const int tid = threadIdx.x;
   const int g = a.gamma, R = 2 * g + 1, r = 2 * g;
@@ -991,7 +991,7 @@ __device__ __forceinline__ void final_item(const VerifyArgs& a, int b, FinalLds&
     }
   }
   __syncthreads();
-  const bool refine = uni(sh.refine) != 0;   // the token at k comes from refine_kernel
+  const bool refine = uni(sh.refine) != 0;   // the token at k comes from the refined draw
   if (lost_rec) {   // no decision arrived: nothing can be reported but an invalid sequence
     write_invalid(a, b, tid);
   } else if (rec.valid) {   // an invalid decision wrote its outputs already
@@ -1039,15 +1039,15 @@ __device__ __forceinline__ void final_item(const VerifyArgs& a, int b, FinalLds&
   if constexpr (INLINE) {
     if (refine) {
       __syncthreads();
-      refine_item<DT, false>(a, b, sh.r);
+      refine_item<DT, CUT>(a, b, sh.r);
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Refinement: the refined residual draws of a call (see kRefineMass), after
-// its other kernels.  One work-group per sequence; those with no pending
-// refinement return at once.
+// Refinement: a refined residual draw (see kRefineMass), taken by the
+// sequence's final item once its outputs are written; with no pending
+// refinement it returns at once.
 template <int DT, bool CUT>
 __device__ __forceinline__ void refine_item(const VerifyArgs& a, int b, DrawLds& sh) {
   unsigned* f = SV_AT(a, flag, (int64_t)b * kFlagStride);
