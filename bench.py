@@ -89,12 +89,39 @@ def parse():
     return ap.parse_args()
 
 
+def _code_only(text: str) -> str:
+    """C++ source without its comments, trailing blanks and empty lines:
+    what the compiler sees of it, so that a comment edit keeps the digest."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":   # a string or character literal, escapes included
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    lines = (line.rstrip() for line in "".join(out).splitlines())
+    return "\n".join(line for line in lines if line)
+
+
 def source_digest() -> str:
+    """sha256 prefix of the kernel sources (rejection_sampling_verify_12_amd/
+    csrc/*) without their comments."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "rejection_sampling_verify_12_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
+            h.update(f.encode() + b"\0" + _code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -217,15 +217,19 @@ __global__ __launch_bounds__(64) void topp_select_kernel(VerifyArgs, int pass, i
 // row's masses in value order follow exactly from how often each value
 // occurs.  For each row a 1024-thread work-group (all 128 KB of counters
 // fill its CU's LDS):
-//   * counts the row's values by their 16-bit order-preserving keys in LDS,
-//     two 16-bit counters per 32-bit word: word w counts key w (a negative
-//     value) in its low half and key w + 32768 (a non-negative one) in its
-//     high half, so neighbouring values, which a row's logits crowd, fall in
-//     different words.  A counter wraps only where one value occurs 65536
-//     times or more; the counters then sum to less than V, and the row is
-//     counted again (topp_redo_kernel) with returning atomics that record
-//     every wrap, so only such rows are read a second time;
-//   * from the counts, from the top key down: the largest finite value (the
+//   * counts the row's values in LDS, two 16-bit counters per 32-bit word,
+//     so that neighbouring values, which a row's logits crowd, fall in
+//     different words: topp_count_kernel by the raw bits x (word x & 0x7FFF,
+//     the low half for a non-negative value, the high half for a negative
+//     one; the crowded values in per-lane copies, the band, below), and
+//     topp_redo_kernel by the 16-bit order-preserving keys (word w counts
+//     key w, a negative value, in its low half and key w + 32768, a
+//     non-negative one, in its high half).  A counter wraps only where one
+//     value occurs 65536 times or more; the counters then sum to less than
+//     V, and the row is counted again (topp_redo_kernel) with returning
+//     atomics that record every wrap, so only such rows are read a second
+//     time;
+//   * from the counts, from the top value down: the largest finite value (the
 //     row offset), the row normaliser in fp64, and the nucleus threshold (the
 //     first value at whose end the running mass reaches top_p times the
 //     normaliser; each value is one run of equal logits);
@@ -246,17 +250,19 @@ constexpr int kCountEvents = 288;
 constexpr uint32_t kKeyNegInf = 0x007Fu, kKeyNegZero = 0x7FFFu, kKeyPosZero = 0x8000u,
                    kKeyPosInf = 0xFF80u;
 
-// The counted row's words with a count, compacted in ascending order (word,
-// low count | high count << 16) for the wave that finishes the row while the
-// next one is counted; a row with more is left to topp_redo_kernel.
+// The counted row's raw words with a count, compacted in ascending order
+// (word, low count | high count << 16) for the wave that finishes the row
+// while the next one is counted; a row with more is left to
+// topp_redo_kernel.
 constexpr int kListCap = 1792;
-// The band: the 64 keys from a row's origin key up (set just below the
+// The band: the 64 raw values from a row's origin up (set just below the
 // median of a sample of the row, where its logits crowd) are counted in
 // per-lane copies, so the lanes of one add reach 64 different words and
-// banks.  Word 64 i + l holds key origin + i for lane l of every counting
-// wave, in the half its counter takes; a copy takes at most
-// (V / 960 + 9) * 15 < 65536 counts for rows up to kBandMaxV.  After the row
-// the copies are summed into the counters.
+// banks (an LDS atomic add takes two clocks for each lane on its most loaded
+// bank, lanes on one word included).  Word 64 i + l holds value origin + i
+// for lane l of every counting wave, in the half its counter takes; a copy
+// takes at most (V / 960 + 9) * 15 < 65536 counts for rows up to kBandMaxV.
+// After the row the copies are summed into the counters.
 #ifndef SV_COUNT_PIPE
 #define SV_COUNT_PIPE 2
 #endif
