@@ -86,7 +86,36 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device copy of this many bytes (counter calibration)")
+    ap.add_argument("--lds-probe", action="store_true",
+                    help="only time LDS atomic adds by lane-to-word pattern (spec_lds_atomic_probe)")
     return ap.parse_args()
+
+
+LDS_PATTERNS = ("64 words, 64 banks", "8 words, 8 lanes each", "one word", "32 words on one bank")
+
+
+def lds_probe(R, dev, iters: int = 2048, reps: int = 5) -> dict:
+    """Clocks per wave-wide LDS atomic add per CU, by the lane-to-word
+    pattern of spec_lds_atomic_probe: the kernel's event time (best of reps)
+    times the 2.4 GHz peak engine clock over the 16 waves x 8 x iters adds
+    each CU issues."""
+    import torch
+    sink = torch.zeros(1, dtype=torch.int64, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    out = {}
+    for pat, name in enumerate(LDS_PATTERNS):
+        for _ in range(2):
+            R.spec_lds_atomic_probe(pat, iters, sink, stream=stream)
+        best = float("inf")
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            R.spec_lds_atomic_probe(pat, iters, sink, stream=stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1))
+        out[name] = {"us": best * 1e3, "clocks_per_add": best * 1e-3 * 2.4e9 / (16 * 8 * iters)}
+    return out
 
 
 def _code_only(text: str) -> str:
@@ -457,6 +486,10 @@ def main():
 
     import torch
     dev = torch.device("cuda:0")
+    if args.lds_probe:
+        print(json.dumps({"lds_atomic_probe": lds_probe(R, dev), "iters": 2048, "waves_per_cu": 16,
+                          "clock_ghz": 2.4, "source_digest": source_digest()}))
+        return
     if args.copy_bytes:
         src = torch.empty(args.copy_bytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)

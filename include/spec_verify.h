@@ -410,6 +410,20 @@ int spec_verify_noalloc(const void* draft_logits, const void* target_logits, int
  */
 int spec_read_bandwidth(const void* buf, size_t bytes, uint64_t* sink, void* stream);
 
+/*
+ * A measurement aid, not part of the verification: the cost of an LDS atomic
+ * add by how a wave's lanes fall on words and banks, which the top-p
+ * counting kernel's counter layout is designed around.  One 1024-thread
+ * work-group per CU; each wave adds 1 to words of its own 2048-word region,
+ * 8 x iters wave-wide adds, lane l to word: pattern 0: l (64 words, 64
+ * banks); 1: l / 8 (8 words, 8 lanes each); 2: 0 (one word); 3: 64 (l mod 32)
+ * (32 words on one bank).  The caller times the launch on `stream`.  `sink`
+ * is a device word written only if a count equals an impossible value.
+ * pattern outside 0..3, iters outside 1..2^20 or a null sink: SPEC_EINVAL.
+ * Enqueues only.
+ */
+int spec_lds_atomic_probe(int pattern, int iters, uint64_t* sink, void* stream);
+
 /* A static, human-readable description of a status code. */
 const char* spec_status_str(int status);
 

@@ -22,6 +22,7 @@ EXPORTED = ("spec_workspace_bytes", "spec_verify", "spec_verify_saguaro",
             "spec_predict_workspace_bytes", "spec_predict_outcomes", "spec_verify_predict",
             "spec_greedy_workspace_bytes", "spec_verify_greedy", "spec_verify_early",
             "spec_verify_ex", "spec_synthetic_busy", "spec_verify_noalloc", "spec_read_bandwidth",
+            "spec_lds_atomic_probe",
             "spec_synth_draft", "spec_synth_rows", "spec_ssd_prespeculate", "spec_ssd_advance",
             "spec_status_str")
 
@@ -93,6 +94,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.spec_verify_greedy.restype = i32
     lib.spec_read_bandwidth.argtypes = [vp, sz, vp, vp]
     lib.spec_read_bandwidth.restype = i32
+    lib.spec_lds_atomic_probe.argtypes = [i32, i32, vp, vp]
+    lib.spec_lds_atomic_probe.restype = i32
     lib.spec_verify_noalloc.argtypes = verify_args[:-3] + [vp]
     lib.spec_verify_noalloc.restype = i32
     lib.spec_status_str.argtypes = [i32]
@@ -432,6 +435,17 @@ def spec_read_bandwidth(buf, sink, nbytes=None, stream=None):
     n = buf.numel() * buf.element_size() if nbytes is None else int(nbytes)
     st = load_library().spec_read_bandwidth(buf.data_ptr(), n, sink.data_ptr(),
                                             _stream_handle(stream, buf.device))
+    if st != SPEC_OK:
+        raise SpecError(st)
+
+
+def spec_lds_atomic_probe(pattern: int, iters: int, sink, stream=None):
+    """LDS atomic adds in a fixed lane-to-word pattern, one work-group per CU
+    (a measurement aid, see spec_verify.h); ``sink`` is a device int64
+    tensor of at least one element."""
+    _check_dev(sink)
+    st = load_library().spec_lds_atomic_probe(int(pattern), int(iters), sink.data_ptr(),
+                                              _stream_handle(stream, sink.device))
     if st != SPEC_OK:
         raise SpecError(st)
 

@@ -28,6 +28,10 @@ TIMELINE_LIB = os.path.join(PKG, "libspecverify_timeline.so")
 # workspace's second word instead of trapping (tests/test_gpu_checks.py).
 CHECKS_LIB = os.path.join(PKG, "libspecverify_checks.so")
 SOURCES = ["verify.hip", "predict.hip", "greedy.hip", "synthetic.hip", "readbw.hip"]
+# Measurement aids outside the kernel sources (whose digest ties the
+# committed traffic records to the code they were taken on).
+MEASURE = os.path.join(PKG, "measure")
+MEASURE_SOURCES = ["lds_probe.hip"]
 
 
 def hipcc() -> str:
@@ -39,6 +43,7 @@ def hipcc() -> str:
 
 def command(out: str = LIB, extra=()) -> list[str]:
     srcs = [os.path.join(CSRC, s) for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
+    srcs += [os.path.join(MEASURE, s) for s in MEASURE_SOURCES if os.path.exists(os.path.join(MEASURE, s))]
     return [hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-Wall", "-Wno-unused-function",
