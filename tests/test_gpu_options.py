@@ -325,6 +325,33 @@ def test_top_p_band_limits(V):
         rep.check()
 
 
+@pytest.mark.parametrize("kind", ["near", "past"])
+def test_top_p_list_capacity(kind):
+    """bfloat16 rows of V = 152064 whose distinct raw words (a value and its
+    negation share one) come near the counting kernel's list of 1792 words
+    (Gaussian logits, ~1550) or pass it (magnitudes over 11 binades, ~2000:
+    the redo kernel finishes those rows)."""
+    B, g, V = 2, 2, 152064
+    batch = random_batch(B, g, V, "bf16", 1.0, seed=7100, scale=3.0, sigma=0.5)
+    if kind == "past":
+        rng = W.philox(7101, 1)
+        mag = np.exp(rng.uniform(-8.0, 3.0, (B, g + 1, V)))
+        d64 = np.sign(rng.standard_normal((B, g + 1, V))) * mag
+        t64 = d64 * np.exp(0.1 * rng.standard_normal((B, g + 1, V)))
+        d, t = W.encode(d64, "bf16"), W.encode(t64, "bf16")
+        x = W.gumbel_argmax(W.decode_f64(d, "bf16")[:, :g], 1.0, W.philox(7101, 2))
+        batch = W.Batch(**{**batch.__dict__, "draft": d, "target": t, "draft_tokens": x,
+                           "name": f"list_past_V{V}"})
+    words = [len(np.unique(r.view(np.uint16) & 0x7FFF)) for r in batch.draft.reshape(-1, V)]
+    assert all(1000 < w <= 1792 for w in words) if kind == "near" else all(w > 1792 for w in words), words
+    for top_p in (0.5, 0.95):
+        gpu = run_ex(batch, 1.0, top_p=top_p)
+        ref = oracle_per_seq(batch, np.full(batch.B, 1.0), top_p=top_p)
+        rep = H.compare(batch, gpu, ref)
+        H.say(f"[options]   {rep}")
+        rep.check()
+
+
 @pytest.mark.parametrize("V", [2, 8, 33])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 @pytest.mark.parametrize("mode,eps", [("residual", 0.0), ("saguaro", 1e-8)])
