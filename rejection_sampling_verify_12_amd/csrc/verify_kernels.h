@@ -174,21 +174,23 @@ __global__ __launch_bounds__(kThreads) void test_kernel(VerifyArgs) {
   test_item<DT>(a, blockIdx.x - i * a.B, i, sh);
 }
 
-template <int DT, bool VEC, bool CUT>
+// N tiles per item (a.nt items per sequence).
+template <int DT, bool VEC, bool CUT, int N = kTilesPerItem>
 __global__ __launch_bounds__(kThreads) void mass_kernel(VerifyArgs) {
   const VerifyArgs& a = kernel_arg0<VerifyArgs>();
   __shared__ double lds_d[kWaves * (kTilesPerItem + 1)];
   const int b = blockIdx.x / a.nt, s = blockIdx.x - b * a.nt;
-  mass_item<DT, VEC, CUT>(a, b, s, lds_d);
+  mass_item<DT, VEC, CUT, N>(a, b, s, lds_d);
 }
 
-// EPS: the call may use the Saguaro eps mode (its weights need more registers).
-template <int DT, bool VEC, bool CUT, bool EPS>
+// EPS: the call may use the Saguaro eps mode (its weights need more
+// registers); N tiles per item (a.nt items per sequence).
+template <int DT, bool VEC, bool CUT, bool EPS, int N = kTilesPerItem>
 __global__ __launch_bounds__(kThreads) void sample_kernel(VerifyArgs) {
   const VerifyArgs& a = kernel_arg0<VerifyArgs>();
   __shared__ double lds_d[kWaves * (kTilesPerItem + 1)];
   const int b = blockIdx.x / a.nt, s = blockIdx.x - b * a.nt;
-  sample_item<DT, VEC, CUT, EPS>(a, b, s, lds_d);
+  sample_item<DT, VEC, CUT, EPS, N>(a, b, s, lds_d);
 }
 
 // The draw and the final item of sequence blockIdx.x, which refines a

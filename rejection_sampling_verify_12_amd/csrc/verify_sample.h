@@ -251,14 +251,15 @@ __device__ float eps_clamp(const VerifyArgs& a, int b, double* lds_d) {
 // ---------------------------------------------------------------------------
 // Residual-mass and sampling items.
 
-template <int DT, bool VEC, bool CUT = false>
+// N tiles per item, as the call's sampling items take.
+template <int DT, bool VEC, bool CUT = false, int N = kTilesPerItem>
 __device__ __forceinline__ void mass_item(const VerifyArgs& a, int b, int s, double* lds_d) {
   const SeqRec rec = wait_rec<true>(a, b);
   if (!rec.valid || rec.mode != kModeSaguaroEps) return;
-  double tw[kTilesPerItem + 1];
-  float mt[kTilesPerItem];
-  tile_sums<DT, VEC, kModeResidual, CUT>(a, b, coef_of<CUT>(a, b, rec, 0.f), rec.k, s * kTilesPerItem, tw, mt, lds_d);
-  if (threadIdx.x == 0) slot_put(SV_AT(a, mass, (int64_t)b * a.nt + s), tw[kTilesPerItem]);
+  double tw[N + 1];
+  float mt[N];
+  tile_sums<DT, VEC, kModeResidual, CUT, N>(a, b, coef_of<CUT>(a, b, rec, 0.f), rec.k, s * N, tw, mt, lds_d);
+  if (threadIdx.x == 0) slot_put(SV_AT(a, mass, (int64_t)b * a.nt + s), tw[N]);
 }
 
 // N tiles per item (kTilesPerItem, or fewer for short calls: see
