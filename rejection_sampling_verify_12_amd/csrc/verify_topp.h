@@ -328,8 +328,8 @@ __device__ __forceinline__ void count_pair(CountLds& sh, uint32_t w) {
 // The counting kernel's layout counts raw bfloat16 bits x (no key
 // transform on the hot path): word x & 0x7FFF, the low half for a
 // non-negative value, the high half for a negative one.  Raw word w then
-// holds key w + 32768 (low) and key 32767 - w (high), and the compaction
-// turns the counters back into key words.  One add for x: into this lane's
+// holds key w + 32768 (low) and key 32767 - w (high), which is how the
+// finish (finish_list) reads the compacted words.  One add for x: into this lane's
 // band copy when x - org < kBandKeys (org a raw origin), else into its
 // counter.  blane = 4 (kCountWords + lane): byte offsets.
 __device__ __forceinline__ void count_raw(CountLds& sh, uint32_t x, uint32_t org, uint32_t blane) {
@@ -345,7 +345,8 @@ __device__ __forceinline__ void count_pair_raw(CountLds& sh, uint32_t w, uint32_
 }
 
 // Every logit of the row, once, by threads 0 .. NT - 1.  Lane t takes
-// 8-logit units t, t + NT, ... (eight in flight; one in the rarely run
+// 8-logit units t, t + NT, ... (eight in flight; in the raw layout, batches
+// of SV_COUNT_PIPE with the next batch in flight; one in the rarely run
 // checked pass, whose code stays small), then one of the last V mod 8.
 // RAW: the raw-bit layout of the counting kernel, whose values from the raw
 // origin org up go to the band's copies.
@@ -797,14 +798,17 @@ __device__ void finish_list(const VerifyArgs& a, int64_t row, const CountLds& sh
   // Running masses from the top: a suffix sum over the lanes for the
   // non-negative values (lane 63 holds the largest), then, below their total
   // H, a prefix sum for the negative ones (lane 0 holds the largest).  A
-  // lane's `above` is the running mass before its entries, the value the
-  // lane before it in that order ends on, so the intervals tile (0, Z].
+  // lane's `above` is the `incl` of the lane before it in that order, taken
+  // from that lane (lane 0's negative part starts at H, lane 0's `incl` of
+  // the non-negative part), so the intervals tile (0, Z] exactly.
   const double s0 = wave_suffix_sum(sm[0], lane);
   const double p1 = wave_inclusive_scan(sm[1]);
   const double H = __shfl(s0, 0, 64);
   const double d0 = __shfl_down(s0, 1, 64);
   const double incl0 = s0, above0 = lane == 63 ? 0.0 : d0;
-  const double incl1 = p1 + H, above1 = (p1 - sm[1]) + H;
+  const double incl1 = p1 + H;
+  const double u1 = __shfl_up(incl1, 1, 64);
+  const double above1 = lane == 0 ? H : u1;
   const double Z = __shfl(incl1, 63, 64);
   const double tgt = (double)a.top_p * Z;
   const bool c0 = !bad && above0 < tgt && tgt <= incl0, c1 = !bad && above1 < tgt && tgt <= incl1;
