@@ -325,6 +325,30 @@ def test_top_p_band_limits(V):
         rep.check()
 
 
+@pytest.mark.parametrize("V", [40000, 40003])   # the band (16-byte rows) and without it
+@pytest.mark.parametrize("mu,sd,T", [(-8.0, 2.0, 0.7), (0.0, 0.5, 1.3), (3.0, 6.0, 1.0), (-1.0, 12.0, 0.8)])
+def test_top_p_row_shapes(V, mu, sd, T):
+    """bfloat16 rows whose logits centre on different values with different
+    spreads, so the counting kernel's band lands on negative values, on
+    both sides of zero (moved to one side) and on positive ones, and a wide
+    spread leaves most logits outside it."""
+    B, g = 4, 2
+    rng = W.philox(7200 + int(10 * sd), 1)
+    d64 = mu + sd * rng.standard_normal((B, g + 1, V))
+    t64 = d64 + 0.4 * rng.standard_normal((B, g + 1, V))
+    base = random_batch(B, g, 8, "bf16", T, seed=7201)
+    d, t = W.encode(d64, "bf16"), W.encode(t64, "bf16")
+    x = W.gumbel_argmax(W.decode_f64(d, "bf16")[:, :g], T, W.philox(7202, 2))
+    batch = W.Batch(**{**base.__dict__, "V": V, "T": T, "draft": d, "target": t, "draft_tokens": x,
+                       "name": f"shape_mu{mu}_sd{sd}_V{V}"})
+    for top_p in (0.5, 0.95):
+        gpu = run_ex(batch, T, top_p=top_p)
+        ref = oracle_per_seq(batch, np.full(batch.B, T), top_p=top_p)
+        rep = H.compare(batch, gpu, ref)
+        H.say(f"[options]   {rep}")
+        rep.check()
+
+
 @pytest.mark.parametrize("kind", ["near", "past"])
 def test_top_p_list_capacity(kind):
     """bfloat16 rows of V = 152064 whose distinct raw words (a value and its
